@@ -1,0 +1,146 @@
+// C ABI of the MXFP4 routed-expert FFN: argument validation, then enqueue.
+// Every check here runs before any HIP call, so a rejected call touches
+// neither the device nor the stream.
+#include <stdint.h>
+
+#include "../../include/moe_fp4.h"
+#include "kernels.h"
+
+namespace {
+
+inline bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+moe_status check_store(const moe_fp4_experts* w) {
+  if (!w) return MOE_ERR_NULL;
+  if (!w->w_gate || !w->s_gate || !w->w_up || !w->s_up || !w->w_down || !w->s_down) return MOE_ERR_NULL;
+  if (w->num_slots < 1 || w->hidden < 256 || w->inter < 128) return MOE_ERR_SHAPE;
+  if (w->hidden % 256 != 0 || w->inter % 128 != 0) return MOE_ERR_SHAPE;
+  if (w->hidden > 16384 || w->inter > 8192) return MOE_ERR_UNSUPPORTED;
+  if (misaligned(w->w_gate, 16) || misaligned(w->w_up, 16) || misaligned(w->w_down, 16)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+moe::ExpertStore to_store(const moe_fp4_experts* w) {
+  return moe::ExpertStore{w->num_slots, w->hidden, w->inter, w->w_gate, w->s_gate,
+                          w->w_up,      w->s_up,   w->w_down, w->s_down};
+}
+
+moe_status check_ffn_common(const uint16_t* x, int32_t T, int32_t k, int32_t E, const moe_fp4_experts* w,
+                            const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
+                            float* y_pair, void* ws, size_t ws_bytes, size_t need) {
+  moe_status st = check_store(w);
+  if (st != MOE_OK) return st;
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS || k > E) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !offsets || !sorted_pair || !y_pair) return MOE_ERR_NULL;
+  if (!e2s && w->num_slots < E) return MOE_ERR_SHAPE;
+  if (misaligned(x, 16) || misaligned(y_pair, 16)) return MOE_ERR_ALIGN;
+  if (need > 0) {
+    if (!ws) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    if (misaligned(ws, 256)) return MOE_ERR_ALIGN;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+MOE_FP4_API const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case MOE_ERR_ALIGN: return "a pointer misses its required alignment";
+    case MOE_ERR_UNSUPPORTED: return "shape not supported by this build";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+MOE_FP4_API moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
+                                 const int32_t* expert_to_slot, int32_t* topk_ids, float* topk_w,
+                                 hipStream_t stream) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E) return MOE_ERR_SHAPE;
+  if ((int64_t)T * E > INT32_MAX) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w) return MOE_ERR_NULL;
+  return launched(moe::launch_route(logits, T, E, k, expert_to_slot, topk_ids, topk_w, stream));
+}
+
+MOE_FP4_API moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                                   int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_to_row,
+                                   hipStream_t stream) {
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+  if ((int64_t)T * k > (1 << 24)) return MOE_ERR_SHAPE;
+  if (!expert_offsets) return MOE_ERR_NULL;
+  if (T > 0 && (!topk_ids || !sorted_pair || !pair_to_row)) return MOE_ERR_NULL;
+  // T == 0 still enqueues: the offsets of an empty batch are all zero.
+  return launched(moe::launch_permute(topk_ids, T * k, E, expert_offsets, sorted_pair, pair_to_row, stream));
+}
+
+MOE_FP4_API size_t moe_ffn_fp4_decode_workspace_bytes(int32_t T, int32_t k, int32_t inter) {
+  if (T < 0 || k < 1 || inter < 1) return 0;
+  return moe::decode_workspace_bytes(T, k, inter);
+}
+
+MOE_FP4_API moe_status moe_ffn_fp4_decode(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                          const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                          const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                          float* y_pair, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (T > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+  const size_t need = (T > 0 && k > 0 && w) ? moe::decode_workspace_bytes(T, k, w->inter) : 0;
+  moe_status st = check_ffn_common(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, y_pair,
+                                   ws, ws_bytes, need);
+  if (st != MOE_OK || T == 0) return st;
+  return launched(moe::launch_decode(x_bf16, T, k, E, to_store(w), expert_to_slot, expert_offsets,
+                                     sorted_pair, y_pair, ws, stream));
+}
+
+MOE_FP4_API size_t moe_ffn_fp4_prefill_workspace_bytes(int32_t T, int32_t k, int32_t hidden, int32_t inter) {
+  if (T < 0 || k < 1 || hidden < 1 || inter < 1) return 0;
+  return moe::prefill_workspace_bytes(T, k, hidden, inter);
+}
+
+MOE_FP4_API moe_status moe_ffn_fp4_prefill(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                           const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                           const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                           moe_act_fmt act, float* y_pair, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  if (act != MOE_ACT_MXFP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * k > (1 << 22)) return MOE_ERR_SHAPE;
+  const size_t need = (T > 0 && k > 0 && w) ? moe::prefill_workspace_bytes(T, k, w->hidden, w->inter) : 0;
+  moe_status st = check_ffn_common(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, y_pair,
+                                   ws, ws_bytes, need);
+  if (st != MOE_OK || T == 0) return st;
+  return launched(moe::launch_prefill(x_bf16, T, k, E, to_store(w), expert_to_slot, expert_offsets,
+                                      sorted_pair, y_pair, ws, stream));
+}
+
+MOE_FP4_API moe_status moe_combine(const float* y_pair, const float* topk_w, int32_t T, int32_t k, int32_t H,
+                                   const uint16_t* residual_bf16, moe_out_dtype od, void* out,
+                                   hipStream_t stream) {
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
+  if (od != MOE_OUT_BF16 && od != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y_pair || !topk_w || !out) return MOE_ERR_NULL;
+  if (misaligned(y_pair, 16) || misaligned(out, 16) || (residual_bf16 && misaligned(residual_bf16, 16)))
+    return MOE_ERR_ALIGN;
+  if (T > 65535) return MOE_ERR_UNSUPPORTED;
+  return launched(moe::launch_combine(y_pair, topk_w, T, k, H, residual_bf16, od == MOE_OUT_BF16, out, stream));
+}
+
+MOE_FP4_API moe_status moe_rmsnorm_bf16(const uint16_t* x_bf16, int32_t T, int32_t H, float eps,
+                                        uint16_t* out_bf16, hipStream_t stream) {
+  if (T < 0 || H < 8 || H % 8 != 0 || H > 65536 || !(eps >= 0.0f)) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !out_bf16) return MOE_ERR_NULL;
+  if (misaligned(x_bf16, 16) || misaligned(out_bf16, 16)) return MOE_ERR_ALIGN;
+  return launched(moe::launch_rmsnorm(x_bf16, T, H, eps, out_bf16, stream));
+}
+
+}  // extern "C"

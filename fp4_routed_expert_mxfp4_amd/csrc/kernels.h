@@ -1,0 +1,42 @@
+// Internal launchers of the gfx950 kernels; the C ABI in api.cpp validates
+// arguments and then calls these.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+
+struct ExpertStore {
+  int num_slots, H, I;
+  const uint8_t *wg, *sg, *wu, *su, *wd, *sd;
+};
+
+hipError_t launch_route(const float* logits, int T, int E, int k, const int32_t* e2s, int32_t* ids,
+                        float* w, hipStream_t s);
+
+hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pair,
+                          int32_t* pair_to_row, hipStream_t s);
+
+// Decode FFN: gate/up + SwiGLU into h (fp32, sorted-row order), then down.
+size_t decode_workspace_bytes(int T, int k, int I);
+hipError_t launch_decode(const uint16_t* x, int T, int k, int E, const ExpertStore& w,
+                         const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
+                         float* y_pair, void* ws, hipStream_t s);
+
+// Prefill FFN on block-scaled MFMA with MXFP8 activations.
+size_t prefill_workspace_bytes(int T, int k, int H, int I);
+hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertStore& w,
+                          const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
+                          float* y_pair, void* ws, hipStream_t s);
+
+hipError_t launch_combine(const float* y_pair, const float* w, int T, int k, int H,
+                          const uint16_t* residual, bool bf16_out, void* out, hipStream_t s);
+
+hipError_t launch_rmsnorm(const uint16_t* x, int T, int H, float eps, uint16_t* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,255 @@
+"""Python binding of the C ABI in include/moe_fp4.h (ctypes).
+
+Argument marshalling only: every step of the routed MoE FFN runs in the HIP
+kernels of libmoe_fp4.so.  torch supplies device memory and the current
+stream.  The functions carry the C names; outputs that are not passed in are
+allocated with torch on the input's device.  If the library has not been
+built, every call raises -- there is no other implementation to fall back on.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_fp4.so")
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN = 0, 1, 2, 3
+MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
+MOE_OUT_BF16, MOE_OUT_F32 = 0, 1
+MOE_ACT_MXFP8_E4M3 = 0
+EXPORTED = ("moe_route", "moe_permute", "moe_ffn_fp4_decode_workspace_bytes", "moe_ffn_fp4_decode",
+            "moe_ffn_fp4_prefill_workspace_bytes", "moe_ffn_fp4_prefill", "moe_combine",
+            "moe_rmsnorm_bf16", "moe_status_string")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: status {status} ({text})")
+        self.status = status
+
+
+class CExperts(ctypes.Structure):
+    _fields_ = [("num_slots", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("w_gate", ctypes.c_void_p), ("s_gate", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("s_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe_fp4.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python fp4_routed_expert_mxfp4_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+        sig = {
+            "moe_route": [vp, i32, i32, i32, vp, vp, vp, vp],
+            "moe_permute": [vp, i32, i32, i32, vp, vp, vp, vp],
+            "moe_ffn_fp4_decode_workspace_bytes": [i32, i32, i32],
+            "moe_ffn_fp4_decode": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp, vp, sz, vp],
+            "moe_ffn_fp4_prefill_workspace_bytes": [i32, i32, i32, i32],
+            "moe_ffn_fp4_prefill": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, ctypes.c_int,
+                                    vp, vp, sz, vp],
+            "moe_combine": [vp, vp, i32, i32, i32, vp, ctypes.c_int, vp, vp],
+            "moe_rmsnorm_bf16": [vp, i32, i32, f32, vp, vp],
+            "moe_status_string": [ctypes.c_int],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.moe_ffn_fp4_decode_workspace_bytes.restype = sz
+        L.moe_ffn_fp4_prefill_workspace_bytes.restype = sz
+        L.moe_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(fn, status, status_string(status))
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _want(t: torch.Tensor, dtypes, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+@dataclass
+class ExpertStore:
+    """One layer's experts in the checkpoint layout, as device tensors (uint8).
+
+    w_gate, w_up [S][I][H/2]; s_gate, s_up [S][I][H/32];
+    w_down [S][H][I/2]; s_down [S][H][I/32].
+    """
+    w_gate: torch.Tensor
+    s_gate: torch.Tensor
+    w_up: torch.Tensor
+    s_up: torch.Tensor
+    w_down: torch.Tensor
+    s_down: torch.Tensor
+
+    @property
+    def num_slots(self) -> int:
+        return self.w_gate.shape[0]
+
+    @property
+    def inter(self) -> int:
+        return self.w_gate.shape[1]
+
+    @property
+    def hidden(self) -> int:
+        return self.w_down.shape[1]
+
+    def cstruct(self) -> CExperts:
+        for n in ("w_gate", "s_gate", "w_up", "s_up", "w_down", "s_down"):
+            _want(getattr(self, n), (torch.uint8,), n)
+        return CExperts(self.num_slots, self.hidden, self.inter,
+                        _ptr(self.w_gate), _ptr(self.s_gate), _ptr(self.w_up), _ptr(self.s_up),
+                        _ptr(self.w_down), _ptr(self.s_down))
+
+
+def moe_route(logits: torch.Tensor, k: int, expert_to_slot: torch.Tensor | None = None,
+              topk_ids: torch.Tensor | None = None, topk_w: torch.Tensor | None = None):
+    _want(logits, (torch.float32,), "logits")
+    T, E = logits.shape
+    dev = logits.device
+    if expert_to_slot is not None:
+        _want(expert_to_slot, (torch.int32,), "expert_to_slot")
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _want(topk_ids, (torch.int32,), "topk_ids")
+    _want(topk_w, (torch.float32,), "topk_w")
+    _check("moe_route", lib().moe_route(_ptr(logits), T, E, k, _ptr(expert_to_slot), _ptr(topk_ids),
+                                        _ptr(topk_w), _stream(dev)))
+    return topk_ids, topk_w
+
+
+def moe_permute(topk_ids: torch.Tensor, E: int, expert_offsets: torch.Tensor | None = None,
+                sorted_pair: torch.Tensor | None = None, pair_to_row: torch.Tensor | None = None):
+    _want(topk_ids, (torch.int32,), "topk_ids")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    if expert_offsets is None:
+        expert_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if sorted_pair is None:
+        sorted_pair = torch.empty(T * k, dtype=torch.int32, device=dev)
+    if pair_to_row is None:
+        pair_to_row = torch.empty(T * k, dtype=torch.int32, device=dev)
+    for n, t in (("expert_offsets", expert_offsets), ("sorted_pair", sorted_pair), ("pair_to_row", pair_to_row)):
+        _want(t, (torch.int32,), n)
+    _check("moe_permute", lib().moe_permute(_ptr(topk_ids), T, k, E, _ptr(expert_offsets), _ptr(sorted_pair),
+                                            _ptr(pair_to_row), _stream(dev)))
+    return expert_offsets, sorted_pair, pair_to_row
+
+
+def decode_workspace_bytes(T: int, k: int, inter: int) -> int:
+    return int(lib().moe_ffn_fp4_decode_workspace_bytes(T, k, inter))
+
+
+def prefill_workspace_bytes(T: int, k: int, hidden: int, inter: int) -> int:
+    return int(lib().moe_ffn_fp4_prefill_workspace_bytes(T, k, hidden, inter))
+
+
+def _ffn_args(x, k, store, expert_to_slot, expert_offsets, sorted_pair, y_pair):
+    _want(x, _BF16, "x")
+    _want(expert_offsets, (torch.int32,), "expert_offsets")
+    _want(sorted_pair, (torch.int32,), "sorted_pair")
+    if expert_to_slot is not None:
+        _want(expert_to_slot, (torch.int32,), "expert_to_slot")
+    T, H = x.shape
+    if y_pair is None:
+        y_pair = torch.empty((T * k, H), dtype=torch.float32, device=x.device)
+    _want(y_pair, (torch.float32,), "y_pair")
+    return T, y_pair
+
+
+def moe_ffn_fp4_decode(x: torch.Tensor, k: int, E: int, store: ExpertStore,
+                       expert_to_slot: torch.Tensor | None, expert_offsets: torch.Tensor,
+                       sorted_pair: torch.Tensor, y_pair: torch.Tensor | None = None,
+                       ws: torch.Tensor | None = None) -> torch.Tensor:
+    T, y_pair = _ffn_args(x, k, store, expert_to_slot, expert_offsets, sorted_pair, y_pair)
+    need = decode_workspace_bytes(T, k, store.inter)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _want(ws, (torch.uint8,), "ws")
+    cs = store.cstruct()
+    _check("moe_ffn_fp4_decode", lib().moe_ffn_fp4_decode(
+        _ptr(x), T, k, E, ctypes.byref(cs), _ptr(expert_to_slot), _ptr(expert_offsets), _ptr(sorted_pair),
+        _ptr(y_pair), _ptr(ws), ws.numel(), _stream(x.device)))
+    return y_pair
+
+
+def moe_ffn_fp4_prefill(x: torch.Tensor, k: int, E: int, store: ExpertStore,
+                        expert_to_slot: torch.Tensor | None, expert_offsets: torch.Tensor,
+                        sorted_pair: torch.Tensor, y_pair: torch.Tensor | None = None,
+                        ws: torch.Tensor | None = None, act: int = MOE_ACT_MXFP8_E4M3) -> torch.Tensor:
+    T, y_pair = _ffn_args(x, k, store, expert_to_slot, expert_offsets, sorted_pair, y_pair)
+    need = prefill_workspace_bytes(T, k, store.hidden, store.inter)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _want(ws, (torch.uint8,), "ws")
+    cs = store.cstruct()
+    _check("moe_ffn_fp4_prefill", lib().moe_ffn_fp4_prefill(
+        _ptr(x), T, k, E, ctypes.byref(cs), _ptr(expert_to_slot), _ptr(expert_offsets), _ptr(sorted_pair),
+        act, _ptr(y_pair), _ptr(ws), ws.numel(), _stream(x.device)))
+    return y_pair
+
+
+def moe_combine(y_pair: torch.Tensor, topk_w: torch.Tensor, residual: torch.Tensor | None = None,
+                out_dtype: int = MOE_OUT_BF16, out: torch.Tensor | None = None) -> torch.Tensor:
+    _want(y_pair, (torch.float32,), "y_pair")
+    _want(topk_w, (torch.float32,), "topk_w")
+    T, k = topk_w.shape
+    H = y_pair.shape[1]
+    if residual is not None:
+        _want(residual, _BF16, "residual")
+    if out is None:
+        dt = torch.bfloat16 if out_dtype == MOE_OUT_BF16 else torch.float32
+        out = torch.empty((T, H), dtype=dt, device=y_pair.device)
+    _want(out, _BF16 if out_dtype == MOE_OUT_BF16 else (torch.float32,), "out")
+    _check("moe_combine", lib().moe_combine(_ptr(y_pair), _ptr(topk_w), T, k, H, _ptr(residual), out_dtype,
+                                            _ptr(out), _stream(y_pair.device)))
+    return out
+
+
+def moe_rmsnorm_bf16(x: torch.Tensor, eps: float = 1e-6, out: torch.Tensor | None = None) -> torch.Tensor:
+    _want(x, _BF16, "x")
+    T, H = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _want(out, _BF16, "out")
+    _check("moe_rmsnorm_bf16", lib().moe_rmsnorm_bf16(_ptr(x), T, H, eps, _ptr(out), _stream(x.device)))
+    return out

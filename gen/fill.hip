@@ -63,7 +63,7 @@ int grid_x(int64_t n, int nslots) {
 extern "C" {
 
 // Returns 0 on success, 1 on bad arguments, 2 on a launch error.
-int gen_fill_codes(void* dst, int64_t bytes_per_slot, const int32_t* slot_expert_dev, int nslots,
+__attribute__((visibility("default"))) int gen_fill_codes(void* dst, int64_t bytes_per_slot, const int32_t* slot_expert_dev, int nslots,
                    uint32_t seed, int layer, int matrix, hipStream_t stream) {
   if (!dst || !slot_expert_dev || nslots <= 0 || nslots > 65535 || bytes_per_slot <= 0 ||
       bytes_per_slot % 8 != 0 || ((uintptr_t)dst & 7u) != 0)
@@ -75,7 +75,7 @@ int gen_fill_codes(void* dst, int64_t bytes_per_slot, const int32_t* slot_expert
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
-int gen_fill_scales(void* dst, int64_t bytes_per_slot, const int32_t* slot_expert_dev, int nslots,
+__attribute__((visibility("default"))) int gen_fill_scales(void* dst, int64_t bytes_per_slot, const int32_t* slot_expert_dev, int nslots,
                     uint32_t seed, int layer, int matrix, int emin, hipStream_t stream) {
   if (!dst || !slot_expert_dev || nslots <= 0 || nslots > 65535 || bytes_per_slot <= 0 ||
       emin > 0 || emin < -127)

@@ -1,0 +1,216 @@
+/*
+ * moe_fp4.h -- C ABI of the routed Mixture-of-Experts FFN over MXFP4 experts
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the routed-expert FFN of a DeepSeek-V4.1-Flash-class model as
+ * the pages describe it:
+ *   - every routed expert is three matrices (gate, up: [I][H]; down: [H][I])
+ *     stored as e2m1 codes with one UE8M0 scale per 32 weights -- "DeepSeek-
+ *     V4.1-Flash on a single NVIDIA DGX Spark", "Why it is built this way"
+ *     (15,360 experts x 3 x 2304 x 5120 weights at FP4 + UE8M0/32) and its
+ *     intro (the checkpoint's own e2m1 experts, never requantised);
+ *   - only a kept subset of the experts may be routable -- same page, "The
+ *     numbers" (the top ~40 % of experts stay routable and resident);
+ *   - every (token, slot) row is written once and the slot sum is a separate
+ *     fixed-order step -- "DeepSeek V4.1 Flash Q4 / 27 September 2026",
+ *     "30 September follow-up: prefill";
+ *   - prefill and decode are separate arithmetic paths, each judged against
+ *     its own reference -- "Fast single-box DeepSeek v4.1 Flash runtime",
+ *     "Conventions".
+ *
+ * Conventions shared by every call
+ * ---------------------------------
+ *  - Array arguments are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees, synchronises or reads device memory back on the
+ *    host.  The one exception is `const moe_fp4_experts* w`, a HOST pointer to
+ *    a small struct that itself holds device pointers; it is read during the
+ *    call only.
+ *  - Each call validates its arguments synchronously.  On failure it returns
+ *    a status and enqueues nothing.  On success it enqueues its kernels on
+ *    `stream` and returns at once; a launch failure is reported as
+ *    MOE_ERR_LAUNCH.  No call prints, throws or keeps global mutable state.
+ *  - No call records a memset, so every call may be captured into a HIP graph.
+ *  - Element layouts are row-major.  e2m1 codes are packed two per byte,
+ *    element 2c in the low nibble of byte c.  A scale byte e stands for
+ *    2^(e-127); byte 255 (NaN) must not occur (not checked on the device).
+ *  - bf16 values are passed as uint16_t bit patterns.
+ *  - Device data are not inspected on the host.  Preconditions on their
+ *    contents (finite logits, expert ids in range, at least k routable
+ *    experts) are documented per call; when they are violated the kernels
+ *    still stay inside every buffer, but the values written are unspecified.
+ *  - T == 0 is valid everywhere and enqueues nothing.
+ */
+#ifndef MOE_FP4_H
+#define MOE_FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_FP4_API __attribute__((visibility("default")))
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,         /* a required pointer is NULL                         */
+  MOE_ERR_SHAPE = 2,        /* a size is out of range or inconsistent             */
+  MOE_ERR_ALIGN = 3,        /* a pointer misses the alignment stated for it       */
+  MOE_ERR_UNSUPPORTED = 4,  /* a valid shape this build has no kernel for         */
+  MOE_ERR_WORKSPACE = 5,    /* workspace missing or smaller than the query says   */
+  MOE_ERR_LAUNCH = 6        /* the HIP runtime rejected a kernel launch           */
+} moe_status;
+
+typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out_dtype;
+
+/* Activation encoding of the prefill path (MX block format, 32 per scale). */
+typedef enum { MOE_ACT_MXFP8_E4M3 = 0 } moe_act_fmt;
+
+/* One layer's expert store, the checkpoint's own layout, indexed by slot.
+ * Slot s holds one expert; expert_to_slot tables map expert ids to slots.
+ *   w_gate, w_up : [num_slots][inter][hidden/2]  e2m1 codes  (16-byte aligned)
+ *   s_gate, s_up : [num_slots][inter][hidden/32] UE8M0 bytes
+ *   w_down       : [num_slots][hidden][inter/2]  e2m1 codes  (16-byte aligned)
+ *   s_down       : [num_slots][hidden][inter/32] UE8M0 bytes
+ * Rows are the output features; K (the reduction index) is contiguous.
+ * Requirements: hidden % 256 == 0, inter % 128 == 0, hidden <= 16384,
+ * inter <= 8192, num_slots >= 1.  One expert occupies
+ * 3*hidden*inter/2 + 3*hidden*inter/32 bytes (18,800,640 B at 5120 x 2304,
+ * the "18.8 MB" per-expert read of the DGX Spark page, "Open WebUI"). */
+typedef struct {
+  int32_t num_slots, hidden, inter;
+  const uint8_t *w_gate, *s_gate;
+  const uint8_t *w_up, *s_up;
+  const uint8_t *w_down, *s_down;
+} moe_fp4_experts;
+
+/* Limits of this build. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+#define MOE_DECODE_MAX_TOKENS 256
+
+/* ---------------------------------------------------------------------------
+ * moe_route -- top-k router.
+ * The pages give no scoring function; the reading implemented is: for token
+ * t, the candidates are the experts e with expert_to_slot[e] >= 0 (all
+ * experts when expert_to_slot is NULL) -- the kept/routable subset of the DGX
+ * Spark page, "The numbers".  Candidates are ordered by (logit descending,
+ * expert index ascending); slot j receives rank j; weights are the softmax of
+ * the k selected logits, w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), in fp32.
+ *   logits         [T][E] fp32, finite (NaN is treated as -inf)
+ *   expert_to_slot [E] int32 or NULL
+ *   topk_ids       [T][k] int32 out: expert ids
+ *   topk_w         [T][k] fp32  out
+ * 1 <= k <= MOE_MAX_TOPK, k <= E <= MOE_MAX_EXPERTS.  If fewer than k experts
+ * are routable, the remaining slots get non-routable experts with weight 0.
+ * ------------------------------------------------------------------------- */
+MOE_FP4_API moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
+                                 const int32_t* expert_to_slot, int32_t* topk_ids,
+                                 float* topk_w, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_permute -- token-to-expert bucketing of the (token, slot) rows.
+ * Pair p = t*k + j.  expert_offsets[e] = number of pairs routed to experts
+ * below e (exclusive prefix sum of the per-expert counts; expert_offsets[E] =
+ * T*k).  sorted_pair lists every p ordered by (expert ascending, p ascending)
+ * -- a stable, order-independent bucketing, so the expert FFN can run the
+ * experts in any order ("30 September follow-up: prefill" of the 27 September
+ * argonautlabs report).  pair_to_row is the inverse permutation.
+ *   topk_ids       [T*k] int32, each in [0, E)
+ *   expert_offsets [E+1] int32 out
+ *   sorted_pair    [T*k] int32 out
+ *   pair_to_row    [T*k] int32 out
+ * T*k <= 2^24.  Ids outside [0, E) are left out of every bucket (their
+ * pair_to_row entry is -1 and expert_offsets[E] counts only valid pairs).
+ * ------------------------------------------------------------------------- */
+MOE_FP4_API moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                                   int32_t* expert_offsets, int32_t* sorted_pair,
+                                   int32_t* pair_to_row, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_ffn_fp4_decode -- expert FFN of the decode path (fp32 accumulation).
+ * For every pair p = sorted_pair[r] = t*k + j with expert e (bucket of r):
+ *   g = W_gate[e] . x_t,  u = W_up[e] . x_t,  h = silu(g) * u  (fp32),
+ *   y_pair[p] = W_down[e] . h                                  (fp32)
+ * where W = e2m1(code) * 2^(scale-127) is decoded in registers.  x is used as
+ * given (bf16, exact in fp32) and h stays fp32: this is the decode reference
+ * arithmetic, judged against unquantised activations.
+ *   x_bf16         [T][hidden] bf16 bits (16-byte aligned)
+ *   expert_to_slot [E] int32 (NULL: slot = expert id, needs num_slots >= E);
+ *                  a bucket whose expert has no slot (-1 or >= num_slots)
+ *                  writes zero rows
+ *   expert_offsets [E+1], sorted_pair [T*k]: outputs of moe_permute
+ *   y_pair         [T*k][hidden] fp32 out, row p (token-slot order)
+ *   ws             device workspace of at least
+ *                  moe_ffn_fp4_decode_workspace_bytes(T, k, inter) bytes,
+ *                  256-byte aligned; contents on entry do not matter
+ * 1 <= T <= MOE_DECODE_MAX_TOKENS.
+ * ------------------------------------------------------------------------- */
+MOE_FP4_API size_t moe_ffn_fp4_decode_workspace_bytes(int32_t T, int32_t k, int32_t inter);
+MOE_FP4_API moe_status moe_ffn_fp4_decode(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                          const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                          const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                          float* y_pair, void* ws, size_t ws_bytes,
+                                          hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_ffn_fp4_prefill -- expert FFN of the prefill path on block-scaled MFMA.
+ * Same contract as moe_ffn_fp4_decode except for the activation arithmetic,
+ * which follows the activation-quantisation switch of the DGX Spark page
+ * ("Reproduce the checks"): with MOE_ACT_MXFP8_E4M3, x is quantised to MXFP8
+ * (e4m3 codes, one UE8M0 scale per 32 along hidden) before gate/up, and h to
+ * MXFP8 along inter before down.  Block exponent X = floor(log2 amax) - 8,
+ * plus 1 when the significand of amax exceeds 1.75 (never saturates),
+ * clamped to [-127, 127]; elements are rounded to nearest even.  The GEMMs
+ * run on gfx950 V_MFMA_SCALE_F32_*_F8F6F4 (e4m3 x e2m1, fp32 accumulation).
+ *   ws: at least moe_ffn_fp4_prefill_workspace_bytes(T, k, hidden, inter)
+ *       bytes, 256-byte aligned
+ * T >= 1, T*k <= 2^22.
+ * ------------------------------------------------------------------------- */
+MOE_FP4_API size_t moe_ffn_fp4_prefill_workspace_bytes(int32_t T, int32_t k, int32_t hidden,
+                                                       int32_t inter);
+MOE_FP4_API moe_status moe_ffn_fp4_prefill(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                           const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                           const int32_t* expert_offsets,
+                                           const int32_t* sorted_pair, moe_act_fmt act,
+                                           float* y_pair, void* ws, size_t ws_bytes,
+                                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_combine -- fixed-order weighted slot sum ("30 September follow-up").
+ *   out[t] = sum_{j=0..k-1} topk_w[t][j] * y_pair[t*k+j]   (ascending j, fp32)
+ *            + residual[t]                                 (if not NULL)
+ * stored as bf16 (round to nearest even) or fp32.
+ *   y_pair   [T*k][H] fp32 (16-byte aligned)
+ *   topk_w   [T][k] fp32
+ *   residual [T][H] bf16 bits or NULL
+ *   out      [T][H] bf16 bits or fp32 (16-byte aligned; may not alias y_pair)
+ * H % 8 == 0.
+ * ------------------------------------------------------------------------- */
+MOE_FP4_API moe_status moe_combine(const float* y_pair, const float* topk_w, int32_t T, int32_t k,
+                                   int32_t H, const uint16_t* residual_bf16, moe_out_dtype od,
+                                   void* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_rmsnorm_bf16 -- weightless RMS norm of a bf16 residual stream,
+ *   out[t] = bf16( x[t] / sqrt(mean(x[t]^2) + eps) )   (fp32 arithmetic).
+ * Harness step of the chained multi-layer decode: the pages never restate
+ * the architecture ("Fast single-box DeepSeek v4.1 Flash runtime", "Who this
+ * is for"), and without a norm x <- x + MoE(x) overflows within a few layers.
+ *   x, out [T][H] bf16 bits (16-byte aligned; out may alias x)
+ * H % 8 == 0, H <= 65536.
+ * ------------------------------------------------------------------------- */
+MOE_FP4_API moe_status moe_rmsnorm_bf16(const uint16_t* x_bf16, int32_t T, int32_t H, float eps,
+                                        uint16_t* out_bf16, hipStream_t stream);
+
+/* Static description of a status code. */
+MOE_FP4_API const char* moe_status_string(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP4_H */

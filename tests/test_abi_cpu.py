@@ -1,0 +1,138 @@
+"""The C-ABI library loads without a GPU, exports every symbol the header
+declares, and rejects bad arguments with status codes before touching HIP.
+No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_fp4.h")
+
+
+def _lib():
+    from fp4_routed_expert_mxfp4_amd import moe
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.skip("libmoe_fp4.so not built")
+    return moe
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"MOE_FP4_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
+
+
+def test_header_declares_the_five_calls():
+    names = set(declared_functions())
+    for n in ("moe_route", "moe_permute", "moe_ffn_fp4_decode", "moe_ffn_fp4_prefill", "moe_combine"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    m = _lib()
+    L = ctypes.CDLL(m.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(m.EXPORTED)
+
+
+def test_gen_library_exports():
+    from gen import device as gd
+    if not os.path.exists(gd.LIB_PATH):
+        pytest.skip("libmoe_gen.so not built")
+    L = ctypes.CDLL(gd.LIB_PATH)
+    assert hasattr(L, "gen_fill_codes") and hasattr(L, "gen_fill_scales")
+
+
+def test_status_strings():
+    m = _lib()
+    for s in range(7):
+        assert m.status_string(s)
+    assert m.status_string(99) == "unknown status"
+
+
+FAKE = 0x10000          # a 256-aligned address that is never dereferenced by validation
+MIS = 0x10001
+
+
+def _store(m, **over):
+    d = dict(num_slots=8, hidden=256, inter=128, w_gate=FAKE, s_gate=FAKE, w_up=FAKE, s_up=FAKE,
+             w_down=FAKE, s_down=FAKE)
+    d.update(over)
+    return m.CExperts(d["num_slots"], d["hidden"], d["inter"], d["w_gate"], d["s_gate"], d["w_up"],
+                      d["s_up"], d["w_down"], d["s_down"])
+
+
+def test_route_validation():
+    m = _lib()
+    L = m.lib()
+    assert L.moe_route(None, 1, 8, 2, None, FAKE, FAKE, None) == m.MOE_ERR_NULL
+    assert L.moe_route(FAKE, 1, 8, 9, None, FAKE, FAKE, None) == m.MOE_ERR_SHAPE       # k > E
+    assert L.moe_route(FAKE, 1, 8, 0, None, FAKE, FAKE, None) == m.MOE_ERR_SHAPE       # k = 0
+    assert L.moe_route(FAKE, 1, 8, 17, None, FAKE, FAKE, None) == m.MOE_ERR_SHAPE      # k > 16
+    assert L.moe_route(FAKE, 1, 1025, 2, None, FAKE, FAKE, None) == m.MOE_ERR_SHAPE    # E > 1024
+    assert L.moe_route(FAKE, -1, 8, 2, None, FAKE, FAKE, None) == m.MOE_ERR_SHAPE
+    assert L.moe_route(None, 0, 8, 2, None, None, None, None) == m.MOE_OK              # empty batch
+
+
+def test_permute_validation():
+    m = _lib()
+    L = m.lib()
+    assert L.moe_permute(FAKE, 1, 2, 8, None, FAKE, FAKE, None) == m.MOE_ERR_NULL
+    assert L.moe_permute(None, 1, 2, 8, FAKE, FAKE, FAKE, None) == m.MOE_ERR_NULL
+    assert L.moe_permute(FAKE, 1, 2, 2000, FAKE, FAKE, FAKE, None) == m.MOE_ERR_SHAPE
+    assert L.moe_permute(FAKE, 1 << 22, 8, 8, FAKE, FAKE, FAKE, None) == m.MOE_ERR_SHAPE
+
+
+def _decode(m, x=FAKE, T=1, k=2, E=8, store=None, e2s=None, off=FAKE, sp=FAKE, y=FAKE, ws=FAKE, ws_bytes=1 << 20):
+    st = _store(m) if store is None else store
+    return m.lib().moe_ffn_fp4_decode(x, T, k, E, ctypes.byref(st), e2s, off, sp, y, ws, ws_bytes, None)
+
+
+def test_decode_validation():
+    m = _lib()
+    assert _decode(m, x=None) == m.MOE_ERR_NULL
+    assert _decode(m, store=_store(m, w_up=None)) == m.MOE_ERR_NULL
+    assert _decode(m, store=_store(m, hidden=200)) == m.MOE_ERR_SHAPE
+    assert _decode(m, store=_store(m, inter=100)) == m.MOE_ERR_SHAPE
+    assert _decode(m, store=_store(m, hidden=32768)) == m.MOE_ERR_UNSUPPORTED
+    assert _decode(m, store=_store(m, num_slots=4)) == m.MOE_ERR_SHAPE          # identity needs S >= E
+    assert _decode(m, x=MIS) == m.MOE_ERR_ALIGN
+    assert _decode(m, store=_store(m, w_down=MIS)) == m.MOE_ERR_ALIGN
+    assert _decode(m, ws=None) == m.MOE_ERR_WORKSPACE
+    assert _decode(m, ws_bytes=16) == m.MOE_ERR_WORKSPACE
+    assert _decode(m, ws=FAKE + 16) == m.MOE_ERR_ALIGN
+    assert _decode(m, T=300) == m.MOE_ERR_UNSUPPORTED
+    assert _decode(m, k=9) == m.MOE_ERR_SHAPE
+    assert _decode(m, T=0) == m.MOE_OK
+    assert m.decode_workspace_bytes(1, 8, 2304) == 8 * 2304 * 4
+
+
+def test_prefill_and_combine_validation():
+    m = _lib()
+    L = m.lib()
+    st = _store(m)
+    assert L.moe_ffn_fp4_prefill(FAKE, 4, 2, 8, ctypes.byref(st), None, FAKE, FAKE, 7, FAKE, FAKE, 1 << 30,
+                                 None) == m.MOE_ERR_UNSUPPORTED                      # unknown activation format
+    assert L.moe_ffn_fp4_prefill(None, 4, 2, 8, ctypes.byref(st), None, FAKE, FAKE, 0, FAKE, FAKE, 1 << 30,
+                                 None) == m.MOE_ERR_NULL
+    assert L.moe_ffn_fp4_prefill(FAKE, 4, 2, 8, ctypes.byref(st), None, FAKE, FAKE, 0, FAKE, FAKE, 0,
+                                 None) == m.MOE_ERR_WORKSPACE
+    assert L.moe_combine(None, FAKE, 1, 2, 256, None, 0, FAKE, None) == m.MOE_ERR_NULL
+    assert L.moe_combine(FAKE, FAKE, 1, 2, 250, None, 0, FAKE, None) == m.MOE_ERR_SHAPE
+    assert L.moe_combine(FAKE, FAKE, 1, 2, 256, None, 5, FAKE, None) == m.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(MIS, FAKE, 1, 2, 256, None, 0, FAKE, None) == m.MOE_ERR_ALIGN
+    assert L.moe_combine(FAKE, FAKE, 1, 2, 256, MIS, 0, FAKE, None) == m.MOE_ERR_ALIGN
+    assert L.moe_rmsnorm_bf16(None, 1, 256, 1e-6, FAKE, None) == m.MOE_ERR_NULL
+    assert L.moe_rmsnorm_bf16(FAKE, 1, 250, 1e-6, FAKE, None) == m.MOE_ERR_SHAPE
+    assert L.moe_rmsnorm_bf16(FAKE, 1, 256, -1.0, FAKE, None) == m.MOE_ERR_SHAPE
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    m = _lib()
+    with pytest.raises(ValueError):
+        m.moe_route(torch.zeros((1, 8)), 2)
