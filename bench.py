@@ -1,0 +1,386 @@
+#!/usr/bin/env python3
+"""Throughput of the routed MoE FFN over MXFP4 experts on one MI355X.
+
+Headline (value): single-layer decode at batch 1 -- hidden 5120, expert width
+2304, 384 experts all resident, top-8 -- as achieved HBM GB/s of the whole
+step (router, bucketing, decode FFN, combine), counting the algorithmic bytes
+(the 8 routed experts' codes and scales, x, logits, output).  Each step uses
+one of 64 logit sets in turn, so consecutive steps touch different experts
+and the 256 MB last-level cache cannot hold the weights between them.
+
+Also reported: the gate/up kernel against the HBM roofline (HIP events on its
+stream), the 4096-token prefill chunk (tokens/s of one layer) and the 40-layer
+chained decode (154 of 384 experts resident per layer), and the fp64 CPU
+oracle timed on a bounded sample on the host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-FFN decode achieved HBM GB/s (% of peak); prefill tokens/s at 4096"
+PEAK_HBM = 8.0e12          # bytes/s, MI355X published HBM3E bandwidth
+PEAK_MXFP4 = 10.1e15       # FLOP/s, MI355X published dense MXFP4
+PEAK_MXFP8 = 5.0e15        # FLOP/s, MI355X published dense FP8
+NSETS = 64
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--chain-steps", type=int, default=30)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-chain", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only time torch's plain copy of 4 GiB (the HBM-bytes calibration kernel)")
+    return ap.parse_args()
+
+
+def layer_bytes(cfg, experts: int, T: int, out_bytes: int = 2) -> int:
+    """Algorithmic bytes of one layer call: touched experts + x + logits + output."""
+    return experts * cfg.expert_bytes + T * cfg.H * 2 + T * cfg.E * 4 + T * cfg.H * out_bytes
+
+
+class DecodeBench:
+    """Device state of the single-layer decode workload with 64 rotating routings."""
+
+    def __init__(self, cfg, torch, m, gd, gi):
+        self.cfg, self.torch, self.m = cfg, torch, m
+        hi = gi.host_inputs(cfg)
+        self.hi = hi
+        self.store = m.ExpertStore(*gd.fill_layer(cfg, 0, hi.resident[0]))
+        dev = torch.device("cuda")
+        self.x, _, _ = gd.upload(hi, 0)
+        sets = gi.logit_sets(cfg, hi.bias, NSETS)
+        self.logit_sets = sets
+        self.logits = torch.from_numpy(sets).to(dev)                  # [S][T][E]
+        T, k, E = cfg.T, cfg.k, cfg.E
+        i32, f32 = torch.int32, torch.float32
+        self.ids = torch.empty((NSETS, T, k), dtype=i32, device=dev)
+        self.w = torch.empty((NSETS, T, k), dtype=f32, device=dev)
+        self.off = torch.empty((NSETS, E + 1), dtype=i32, device=dev)
+        self.sp = torch.empty((NSETS, T * k), dtype=i32, device=dev)
+        self.p2r = torch.empty((NSETS, T * k), dtype=i32, device=dev)
+        self.y = torch.empty((T * k, cfg.H), dtype=f32, device=dev)
+        self.ws = torch.empty(m.decode_workspace_bytes(T, k, cfg.I), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+
+    def step(self, s: int) -> None:
+        m, c = self.m, self.cfg
+        m.moe_route(self.logits[s], c.k, None, self.ids[s], self.w[s])
+        m.moe_permute(self.ids[s], c.E, self.off[s], self.sp[s], self.p2r[s])
+        m.moe_ffn_fp4_decode(self.x, c.k, c.E, self.store, None, self.off[s], self.sp[s], self.y, self.ws)
+        m.moe_combine(self.y, self.w[s], None, m.MOE_OUT_BF16, self.out)
+
+    def gateup(self, s: int) -> None:
+        c = self.cfg
+        self.m.moe_ffn_fp4_decode_gateup(self.x, c.k, c.E, self.store, None, self.off[s], self.sp[s], self.y,
+                                         self.ws)
+
+    def down(self, s: int) -> None:
+        c = self.cfg
+        self.m.moe_ffn_fp4_decode_down(self.x, c.k, c.E, self.store, None, self.off[s], self.sp[s], self.y,
+                                       self.ws)
+
+    def touched(self) -> list[int]:
+        """Distinct experts routed per set (host copy of the device routing)."""
+        ids = self.ids.cpu().numpy()
+        return [len(set(ids[s].reshape(-1).tolist())) for s in range(NSETS)]
+
+
+def capture(torch, fn, count: int):
+    """HIP graph holding fn(0..count-1) in order (one graph per call index)."""
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(count):
+            fn(i)  # warm the launch path outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i in range(count):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def capture_many(torch, fn, count: int):
+    """One HIP graph holding fn(0), fn(1), ..., fn(count-1) back to back."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(count):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(torch, graphs, steps: int, pick=lambda i, n: i % n) -> float:
+    """Seconds for `steps` replays, HIP events on the replay stream."""
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(steps):
+        graphs[pick(i, len(graphs))].replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3
+
+
+def decode_section(args, torch, m, gd, gi):
+    cfg = gi.CONFIGS["decode1"]
+    log(f"decode1: filling {cfg.E} experts ({cfg.E * cfg.expert_bytes / 1e9:.2f} GB)")
+    db = DecodeBench(cfg, torch, m, gd, gi)
+    for s in range(NSETS):
+        db.step(s)
+    torch.cuda.synchronize()
+    touched = db.touched()
+    step_graphs = capture(torch, db.step, NSETS)
+    log("decode1: warmup")
+    time_graphs(torch, step_graphs, args.warmup)
+    log(f"decode1: timing {args.steps} steps")
+    t = time_graphs(torch, step_graphs, args.steps)
+    per_step_bytes = [layer_bytes(cfg, touched[i % NSETS], cfg.T) for i in range(args.steps)]
+    gbps = sum(per_step_bytes) / t / 1e9
+    # the gate/up kernel alone, then the down kernel alone: one graph of 64
+    # back-to-back launches over the 64 routings, replayed; HIP events on the
+    # replay stream bracket the whole timed region
+    gu_graph = capture_many(torch, db.gateup, NSETS)
+    dn_graph = capture_many(torch, db.down, NSETS)
+    reps = max(1, max(args.steps, 256) // NSETS)
+    time_graphs(torch, [gu_graph], 2)
+    t_gu = time_graphs(torch, [gu_graph], reps) / (reps * NSETS)
+    time_graphs(torch, [dn_graph], 2)
+    t_dn = time_graphs(torch, [dn_graph], reps) / (reps * NSETS)
+    gu_bytes = cfg.k * (2 * cfg.I * (cfg.H // 2 + cfg.H // 32)) + cfg.H * 2 + cfg.k * cfg.I * 4
+    dn_bytes = cfg.k * (cfg.H * (cfg.I // 2 + cfg.I // 32)) + cfg.k * cfg.I * 4 + cfg.k * cfg.H * 4
+    res = dict(seconds=t, gbps=gbps, ms_per_step=t / args.steps * 1e3, touched_mean=sum(touched) / NSETS,
+               gateup_us=t_gu * 1e6, gateup_bytes=gu_bytes, down_us=t_dn * 1e6, down_bytes=dn_bytes,
+               db=db)
+    log(f"decode1: {res['ms_per_step'] * 1e3:.1f} us/step, {gbps:.0f} GB/s; gate/up {t_gu * 1e6:.1f} us "
+        f"({gu_bytes / t_gu / 1e9:.0f} GB/s), down {t_dn * 1e6:.1f} us ({dn_bytes / t_dn / 1e9:.0f} GB/s)")
+    return res
+
+
+def prefill_section(args, torch, m, gd, gi):
+    cfg = gi.CONFIGS["prefill4096"]
+    hi = gi.host_inputs(cfg)
+    log("prefill4096: filling experts")
+    store = m.ExpertStore(*gd.fill_layer(cfg, 0, hi.resident[0]))
+    x, logits, _ = gd.upload(hi, 0)
+    dev = torch.device("cuda")
+    T, k, E = cfg.T, cfg.k, cfg.E
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sp = torch.empty(T * k, dtype=torch.int32, device=dev)
+    p2r = torch.empty(T * k, dtype=torch.int32, device=dev)
+    y = torch.empty((T * k, cfg.H), dtype=torch.float32, device=dev)
+    ws = torch.empty(m.prefill_workspace_bytes(T, k, cfg.H, cfg.I), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+
+    def step(_i):
+        m.moe_route(logits, k, None, ids, w)
+        m.moe_permute(ids, E, off, sp, p2r)
+        m.moe_ffn_fp4_prefill(x, k, E, store, None, off, sp, y, ws)
+        m.moe_combine(y, w, None, m.MOE_OUT_BF16, out)
+
+    try:
+        step(0)
+        torch.cuda.synchronize()
+    except m.MoeError as exc:
+        log(f"prefill4096 skipped: {exc}")
+        return None
+    graphs = capture(torch, step, 1)
+    time_graphs(torch, graphs, 3)
+    t = time_graphs(torch, graphs, args.prefill_steps)
+    per = t / args.prefill_steps
+    flops = 6.0 * cfg.H * cfg.I * T * k
+    touched = int((torch.diff(off) > 0).sum().item())
+    log(f"prefill4096: {per * 1e3:.3f} ms/layer, {T / per / 1e6:.2f} M tok/s, {touched} experts")
+    return dict(ms_per_layer=per * 1e3, tokens_per_s=T / per, tflops=flops / per / 1e12,
+                frac_of_mxfp4_peak=flops / per / PEAK_MXFP4, frac_of_fp8_peak=flops / per / PEAK_MXFP8,
+                experts_touched=touched, weight_bytes=touched * cfg.expert_bytes)
+
+
+def chain_section(args, torch, m, gd, gi):
+    cfg = gi.CONFIGS["chain40"]
+    hi = gi.host_inputs(cfg)
+    dev = torch.device("cuda")
+    log(f"chain40: filling {cfg.layers} x {cfg.resident} experts "
+        f"({cfg.layers * cfg.resident * cfg.expert_bytes / 1e9:.1f} GB)")
+    stores, logits, e2s = [], [], []
+    for layer in range(cfg.layers):
+        stores.append(m.ExpertStore(*gd.fill_layer(cfg, layer, hi.resident[layer])))
+        logits.append(torch.from_numpy(hi.logits[layer]).to(dev))
+        e2s.append(torch.from_numpy(hi.expert_to_slot[layer]).to(dev))
+    T, k, E, H = cfg.T, cfg.k, cfg.E, cfg.H
+    import numpy as np
+    xs = [torch.from_numpy(hi.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)]
+    xs += [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(cfg.layers)]
+    n = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ids = torch.empty((cfg.layers, T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((cfg.layers, T, k), dtype=torch.float32, device=dev)
+    off = torch.empty((cfg.layers, E + 1), dtype=torch.int32, device=dev)
+    sp = torch.empty((cfg.layers, T * k), dtype=torch.int32, device=dev)
+    p2r = torch.empty((cfg.layers, T * k), dtype=torch.int32, device=dev)
+    y = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(m.decode_workspace_bytes(T, k, cfg.I), dtype=torch.uint8, device=dev)
+
+    def token(_i):
+        for layer in range(cfg.layers):
+            m.moe_rmsnorm_bf16(xs[layer], 1e-6, n)
+            m.moe_route(logits[layer], k, e2s[layer], ids[layer], w[layer])
+            m.moe_permute(ids[layer], E, off[layer], sp[layer], p2r[layer])
+            m.moe_ffn_fp4_decode(n, k, E, stores[layer], e2s[layer], off[layer], sp[layer], y, ws)
+            m.moe_combine(y, w[layer], xs[layer], m.MOE_OUT_BF16, xs[layer + 1])
+
+    graphs = capture(torch, token, 1)
+    time_graphs(torch, graphs, 3)
+    t = time_graphs(torch, graphs, args.chain_steps)
+    per = t / args.chain_steps
+    idn = ids.cpu().numpy()
+    nbytes = sum(layer_bytes(cfg, len(set(idn[layer].reshape(-1).tolist())), T) + T * H * 2 * 2
+                 for layer in range(cfg.layers))
+    fin = xs[-1].float()
+    finite = bool(torch.isfinite(fin).all().item())
+    log(f"chain40: {per * 1e3:.3f} ms/token, {nbytes / per / 1e9:.0f} GB/s, finite={finite}")
+    return dict(ms_per_token=per * 1e3, tokens_per_s=1.0 / per, gbps=nbytes / per / 1e9,
+                frac_of_peak_hbm=nbytes / per / PEAK_HBM, bytes_per_token=nbytes, output_finite=finite)
+
+
+def cpu_baseline(db, gi) -> dict:
+    """The fp64 oracle on a bounded sample of the decode workload (3 routings)."""
+    import numpy as np
+    from oracle import moe_oracle as o
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cfg = db.cfg
+    hw = gi.HostWeights(cfg)
+    n_tok, total_bytes, total_t = 3, 0, 0.0
+    for s in range(n_tok):
+        ids, _ = o.route(db.logit_sets[s], cfg.k)
+        for e in set(ids.reshape(-1).tolist()):
+            for mat in range(3):
+                hw.matrix(int(e), mat)      # generate the inputs outside the timed region
+        t0 = time.perf_counter()
+        o.moe_layer(db.hi.x_bf16, db.logit_sets[s], hw.matrix, cfg.k, cfg.H)
+        total_t += time.perf_counter() - t0
+        total_bytes += layer_bytes(cfg, len(set(ids.reshape(-1).tolist())), cfg.T)
+        hw.drop()
+    log(f"cpu oracle: {total_t:.1f} s for {n_tok} decode tokens")
+    return dict(value=total_bytes / total_t / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"{n_tok} single-token decode layers of the same workload (logit sets 0-{n_tok - 1}), "
+                       f"fp64 numpy oracle, weight generation excluded; {total_t:.1f} s",
+                tokens_per_s=n_tok / total_t)
+
+
+def calibrate(torch) -> dict:
+    """Plain device copy of 4 GiB (torch's copy kernel): a measured streaming
+    ceiling and the known-size kernel the HBM byte counters are scaled by."""
+    n = 4 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / reps
+    res = dict(bytes_read=n, bytes_written=n, us=t * 1e6, copy_GBps=2 * n / t / 1e9)
+    log(f"calibration copy: {t * 1e6:.0f} us per 4 GiB copy, {2 * n / t / 1e9:.0f} GB/s read+write")
+    return res
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print("bench.py: only --gpus 1 is supported (the path is built and measured on one GPU)",
+              file=sys.stderr)
+        return 2
+    import torch
+    import fp4_routed_expert_mxfp4_amd as m
+    from gen import device as gd
+    from gen import inputs as gi
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    m.lib()
+    if args.calibrate:
+        print(json.dumps({"calibration": calibrate(torch)}), flush=True)
+        return 0
+
+    dec = decode_section(args, torch, m, gd, gi)
+    cfg = gi.CONFIGS["decode1"]
+    prefill = None if args.no_prefill else prefill_section(args, torch, m, gd, gi)
+    chain = None if args.no_chain else chain_section(args, torch, m, gd, gi)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(dec["db"], gi)
+
+    gu_achieved = dec["gateup_bytes"] / (dec["gateup_us"] * 1e-6)
+    result = {
+        "metric": METRIC,
+        "value": round(dec["gbps"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": "decode1: single-layer MoE FFN decode, batch 1, hidden 5120, expert width 2304, "
+                               "384 MXFP4 experts resident, top-8, 64 rotating routings",
+                   "hidden": cfg.H, "expert_width": cfg.I, "experts": cfg.E, "top_k": cfg.k, "tokens": cfg.T,
+                   "weights": "e2m1 + UE8M0/32", "activations": "bf16"},
+        "frac_of_peak_hbm": round(dec["gbps"] * 1e9 / PEAK_HBM, 4),
+        "roofline": {"kernel": "decode gate/up + SwiGLU (moe_ffn_fp4_decode_gateup)", "bound": "hbm",
+                     "achieved": round(gu_achieved / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": round(gu_achieved / PEAK_HBM, 4), "traffic": None,
+                     "avg_us": round(dec["gateup_us"], 2), "bytes_per_launch": dec["gateup_bytes"]},
+        "down_kernel": {"avg_us": round(dec["down_us"], 2), "bytes_per_launch": dec["down_bytes"],
+                        "achieved_GBps": round(dec["down_bytes"] / dec["down_us"] / 1e3, 1)},
+        "cpu_baseline": cpu,
+        "prefill4096": prefill,
+        "chain40": chain,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -88,17 +88,41 @@ MOE_FP4_API size_t moe_ffn_fp4_decode_workspace_bytes(int32_t T, int32_t k, int3
   return moe::decode_workspace_bytes(T, k, inter);
 }
 
-MOE_FP4_API moe_status moe_ffn_fp4_decode(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
-                                          const moe_fp4_experts* w, const int32_t* expert_to_slot,
-                                          const int32_t* expert_offsets, const int32_t* sorted_pair,
-                                          float* y_pair, void* ws, size_t ws_bytes, hipStream_t stream) {
+static moe_status decode_phase(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E, const moe_fp4_experts* w,
+                               const int32_t* expert_to_slot, const int32_t* expert_offsets,
+                               const int32_t* sorted_pair, float* y_pair, void* ws, size_t ws_bytes, int phase,
+                               hipStream_t stream) {
   if (T > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
   const size_t need = (T > 0 && k > 0 && w) ? moe::decode_workspace_bytes(T, k, w->inter) : 0;
   moe_status st = check_ffn_common(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, y_pair,
                                    ws, ws_bytes, need);
   if (st != MOE_OK || T == 0) return st;
   return launched(moe::launch_decode(x_bf16, T, k, E, to_store(w), expert_to_slot, expert_offsets,
-                                     sorted_pair, y_pair, ws, stream));
+                                     sorted_pair, y_pair, ws, phase, stream));
+}
+
+MOE_FP4_API moe_status moe_ffn_fp4_decode(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                          const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                          const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                          float* y_pair, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_phase(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, y_pair, ws, ws_bytes, 0,
+                      stream);
+}
+
+MOE_FP4_API moe_status moe_ffn_fp4_decode_gateup(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                                 const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                                 const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                                 float* y_pair, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_phase(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, y_pair, ws, ws_bytes, 1,
+                      stream);
+}
+
+MOE_FP4_API moe_status moe_ffn_fp4_decode_down(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                               const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                               const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                               float* y_pair, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_phase(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, y_pair, ws, ws_bytes, 2,
+                      stream);
 }
 
 MOE_FP4_API size_t moe_ffn_fp4_prefill_workspace_bytes(int32_t T, int32_t k, int32_t hidden, int32_t inter) {

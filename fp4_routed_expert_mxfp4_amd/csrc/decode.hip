@@ -279,6 +279,263 @@ __global__ __launch_bounds__(kThreads) void down_kernel(int k, int E, ExpertStor
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fast paths for the model's shapes.
+//
+// Gate/up at H = 1024*J: the gate row n and the up row n together hold 2*H/32
+// = 64*J blocks, so a row pair is exactly J full-wave 16-byte loads (lane l
+// takes blocks l + 64*j of the concatenated pair) and no lane idles.  The
+// blocks a lane touches are the same for every row, so its slice of x stays
+// in registers.  R row pairs form a batch; the next batch's loads are issued
+// before the current one is reduced (two register buffers), and the 2R
+// partial sums of a batch are reduced with permlane swaps and DPP only.
+//
+// Down at I = 2048*M + 256*TAIL: a row has 64*M main blocks plus 8 tail
+// blocks.  A batch is 8 rows: M full-wave loads per row for the main blocks,
+// and one full-wave load for the 8 tails (lane l takes tail block l%8 of row
+// l/8).  h stays in registers for a one-token bucket.
+// ---------------------------------------------------------------------------
+
+template <int J, int R>
+struct GateUpBatch {
+  uint4 c[R][J];
+  uint32_t s[R][J];  // raw UE8M0 bytes, decoded when the batch is reduced
+};
+
+// Issue the loads of R row pairs starting at n0 (the caller guarantees n0 + R <= I).
+template <int J, int R>
+__device__ __forceinline__ void gu_load(GateUpBatch<J, R>& B, const uint8_t* const (&cp)[J],
+                                        const uint8_t* const (&sp)[J], int n0, size_t rowbytes, int NB) {
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const size_t n = (size_t)(n0 + i);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      B.c[i][j] = ld16(cp[j] + n * rowbytes);
+      B.s[i][j] = sp[j][n * NB];
+    }
+  }
+}
+
+// Reduce the batch for one token and store h for its R rows.
+template <int J, int R>
+__device__ __forceinline__ void gu_finish(const GateUpBatch<J, R>& B, const uint4 (&xr)[J][4], int lane,
+                                          float* hrow, int n0) {
+  constexpr int NB = 32 * J;
+  float g[R], u[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    g[i] = 0.f;
+    u[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const float d = block_dot_bf16(B.c[i][j], xr[j]) * ue8m0_to_f32(B.s[i][j]);
+      if (64 * (j + 1) <= NB) {
+        g[i] += d;                                  // all lanes in the gate row
+      } else if (64 * j >= NB) {
+        u[i] += d;                                  // all lanes in the up row
+      } else {
+        const bool gate = lane + 64 * j < NB;       // the load straddles the two rows
+        g[i] += gate ? d : 0.f;
+        u[i] += gate ? 0.f : d;
+      }
+    }
+  }
+  float gv[R], uv[R];
+  if constexpr (R == 1) {
+    float a = sum16(tswap32(g[0], u[0]));           // lanes 0-31: g, 32-63: u (16-lane partials)
+    a = tswap16(a, a);
+    gv[0] = lane_value(a, 0);
+    uv[0] = lane_value(a, 32);
+  } else {
+    static_assert(R == 2, "gate/up batches of 1 or 2 row pairs");
+    const float a0 = tswap32(g[0], g[1]);
+    const float a1 = tswap32(u[0], u[1]);
+    const float b = sum16(tswap16(a0, a1));         // rows: g0, u0, g1, u1
+    gv[0] = lane_value(b, 0);
+    uv[0] = lane_value(b, 16);
+    gv[1] = lane_value(b, 32);
+    uv[1] = lane_value(b, 48);
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (lane == i) hrow[n0 + i] = swiglu_f32(gv[i], uv[i]);
+}
+
+template <int J, int R>
+__global__ __launch_bounds__(kThreads, 2) void gateup_fast_kernel(
+    const uint16_t* __restrict__ x, int k, int E, ExpertStore w, const int32_t* __restrict__ e2s,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, float* __restrict__ h) {
+  constexpr int NB = 32 * J;
+  __shared__ Buckets bk;
+  build_buckets(offsets, E, bk);
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int total_waves = gridDim.x * kWaves;
+  const int I = w.I;
+  const size_t rowbytes = (size_t)16 * NB;
+  const int nbat = I / R;                 // I % R == 0 is checked at launch
+  const int nbk = bk.n;
+  int C = nbk > 0 ? total_waves / nbk : 1;
+  if (C < 1) C = 1;
+  const int cs = (nbat + C - 1) / C;
+  const int units = nbk * C;
+  for (int unit = gw; unit < units; unit += total_waves) {
+    const int b = unit / C, c = unit - b * C;
+    const int bat0 = c * cs, bat1 = min(bat0 + cs, nbat);
+    if (bat0 >= bat1) continue;
+    const int expert = bk.expert[b], row0 = bk.row0[b];
+    const int slot = e2s ? e2s[expert] : expert;
+    if (slot < 0 || slot >= w.num_slots) continue;  // the down kernel writes zero rows
+    const uint8_t* cb[2] = {w.wg + (size_t)slot * I * rowbytes, w.wu + (size_t)slot * I * rowbytes};
+    const uint8_t* sb[2] = {w.sg + (size_t)slot * I * NB, w.su + (size_t)slot * I * NB};
+    const uint8_t* cp[J];
+    const uint8_t* sp[J];
+    int xblk[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int f = lane + 64 * j, mat = f >= NB ? 1 : 0, blk = f - mat * NB;
+      cp[j] = cb[mat] + blk * 16;
+      sp[j] = sb[mat] + blk;
+      xblk[j] = blk;
+    }
+    uint4 xr[J][4];
+    auto load_x = [&](int t) {
+      const uint16_t* xt = x + (size_t)t * NB * 32;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const uint4* p = reinterpret_cast<const uint4*>(xt + xblk[j] * 32);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xr[j][q] = p[q];
+      }
+    };
+    // one token per bucket: x stays in registers, two batches in flight
+    load_x(sorted_pair[row0] / k);
+    float* hrow = h + (size_t)row0 * I;
+    GateUpBatch<J, R> A, Bn;
+    gu_load(A, cp, sp, bat0 * R, rowbytes, NB);
+    for (int bat = bat0; bat < bat1; bat += 2) {
+      const bool has1 = bat + 1 < bat1;
+      if (has1) gu_load(Bn, cp, sp, (bat + 1) * R, rowbytes, NB);
+      gu_finish(A, xr, lane, hrow, bat * R);
+      if (bat + 2 < bat1) gu_load(A, cp, sp, (bat + 2) * R, rowbytes, NB);
+      if (has1) gu_finish(Bn, xr, lane, hrow, (bat + 1) * R);
+    }
+
+  }
+}
+
+template <int M, bool TAIL>
+struct DownBatch {
+  uint4 c[8][M > 0 ? M : 1];
+  uint32_t s[8][M > 0 ? M : 1];  // raw UE8M0 bytes
+  uint4 ct;
+  uint32_t st;
+};
+
+template <int M, bool TAIL>
+__device__ __forceinline__ void dn_load(DownBatch<M, TAIL>& B, const uint8_t* dc, const uint8_t* ds, int m0,
+                                        int lane, size_t rowbytes, int NB) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int mm = 0; mm < M; ++mm) {
+      const size_t row = (size_t)(m0 + i);
+      B.c[i][mm] = ld16(dc + row * rowbytes + (size_t)(64 * mm + lane) * 16);
+      B.s[i][mm] = ds[row * NB + 64 * mm + lane];
+    }
+  }
+  if (TAIL) {
+    const size_t row = (size_t)(m0 + (lane >> 3));
+    const int blk = 64 * M + (lane & 7);
+    B.ct = ld16(dc + row * rowbytes + (size_t)blk * 16);
+    B.st = ds[row * NB + blk];
+  }
+}
+
+template <int M, bool TAIL>
+__device__ __forceinline__ void dn_finish(const DownBatch<M, TAIL>& B, const float4_t (&hm)[M > 0 ? M : 1][8],
+                                          const float4_t (&ht)[8], int lane, float* yrow, int m0) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = 0.f;
+#pragma unroll
+    for (int mm = 0; mm < M; ++mm) v[i] = fmaf(block_dot_f32(B.c[i][mm], hm[mm]), ue8m0_to_f32(B.s[i][mm]), v[i]);
+  }
+  // 8 row partials -> lanes 8g..8g+7 hold partials of row g
+  const float a0 = tswap32(v[0], v[4]), a1 = tswap32(v[1], v[5]);
+  const float a2 = tswap32(v[2], v[6]), a3 = tswap32(v[3], v[7]);
+  const float b0 = tswap16(a0, a2), b1 = tswap16(a1, a3);
+  float c = tswap8(b0, b1, lane);
+  if (TAIL) c += block_dot_f32(B.ct, ht) * ue8m0_to_f32(B.st);  // this lane's tail block is in row lane/8
+  c = sum8(c);
+  if ((lane & 7) == 0) yrow[m0 + (lane >> 3)] = c;
+}
+
+template <int M, bool TAIL>
+__global__ __launch_bounds__(kThreads, 2) void down_fast_kernel(
+    int k, int E, ExpertStore w, const int32_t* __restrict__ e2s, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pair, const float* __restrict__ h, float* __restrict__ y) {
+  constexpr int NB = 64 * M + (TAIL ? 8 : 0);
+  constexpr int MM = M > 0 ? M : 1;
+  __shared__ Buckets bk;
+  build_buckets(offsets, E, bk);
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int total_waves = gridDim.x * kWaves;
+  const int H = w.H, I = w.I;
+  const size_t rowbytes = (size_t)16 * NB;
+  const int nbat = H / 8;
+  const int nbk = bk.n;
+  int C = nbk > 0 ? total_waves / nbk : 1;
+  if (C < 1) C = 1;
+  const int cs = (nbat + C - 1) / C;
+  const int units = nbk * C;
+  for (int unit = gw; unit < units; unit += total_waves) {
+    const int b = unit / C, c = unit - b * C;
+    const int bat0 = c * cs, bat1 = min(bat0 + cs, nbat);
+    if (bat0 >= bat1) continue;
+    const int expert = bk.expert[b], row0 = bk.row0[b];
+    const int slot = e2s ? e2s[expert] : expert;
+    if (slot < 0 || slot >= w.num_slots) {
+      float* yr = y + (size_t)sorted_pair[row0] * H;
+      for (int m = bat0 * 8 + lane; m < bat1 * 8; m += 64) yr[m] = 0.f;
+      continue;
+    }
+    const uint8_t* dc = w.wd + (size_t)slot * H * rowbytes;
+    const uint8_t* ds = w.sd + (size_t)slot * H * NB;
+    float4_t hm[MM][8], ht[8];
+    auto load_h = [&](int row) {
+      const float* hr = h + (size_t)row * I;
+#pragma unroll
+      for (int mm = 0; mm < M; ++mm) {
+        const float4_t* p = reinterpret_cast<const float4_t*>(hr + (64 * mm + lane) * 32);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) hm[mm][q] = p[q];
+      }
+      if (TAIL) {
+        const float4_t* p = reinterpret_cast<const float4_t*>(hr + (64 * M + (lane & 7)) * 32);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ht[q] = p[q];
+      }
+    };
+    // one token per bucket: h stays in registers, two batches in flight
+    load_h(row0);
+    float* yrow = y + (size_t)sorted_pair[row0] * H;
+    DownBatch<M, TAIL> A, Bn;
+    dn_load(A, dc, ds, bat0 * 8, lane, rowbytes, NB);
+    for (int bat = bat0; bat < bat1; bat += 2) {
+      const bool has1 = bat + 1 < bat1;
+      if (has1) dn_load(Bn, dc, ds, (bat + 1) * 8, lane, rowbytes, NB);
+      dn_finish(A, hm, ht, lane, yrow, bat * 8);
+      if (bat + 2 < bat1) dn_load(A, dc, ds, (bat + 2) * 8, lane, rowbytes, NB);
+      if (has1) dn_finish(Bn, hm, ht, lane, yrow, (bat + 1) * 8);
+    }
+
+  }
+}
+
 template <int JB>
 hipError_t launch_gateup_jb(dim3 grid, const uint16_t* x, int k, int E, const ExpertStore& w,
                             const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
@@ -312,35 +569,64 @@ size_t decode_workspace_bytes(int T, int k, int I) {
 
 hipError_t launch_decode(const uint16_t* x, int T, int k, int E, const ExpertStore& w,
                          const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
-                         float* y_pair, void* ws, hipStream_t s) {
+                         float* y_pair, void* ws, int phase, hipStream_t s) {
   const int P = T * k;
   const int nb_max = P < E ? P : E;
   float* h = reinterpret_cast<float*>(ws);
   const int target = 2048;  // wavefronts: ~8 per CU on 256 CUs
-  const int jb1 = (w.H / 32 + 63) / 64, jb2 = (w.I / 32 + 63) / 64;
+  const dim3 fast_grid(512);
+  hipError_t err = hipSuccess;
 
-  int rpw = pick_rows_per_wave(w.I, nb_max, target);
-  int tiles = (w.I + kWaves * rpw - 1) / (kWaves * rpw);
-  long items = (long)tiles * nb_max;
-  dim3 grid((unsigned)(items < 4096 ? items : 4096));
-  hipError_t err;
-  switch (jb1) {
-    case 1: err = launch_gateup_jb<1>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-    case 2: err = launch_gateup_jb<2>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-    case 3: err = launch_gateup_jb<3>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-    case 4: err = launch_gateup_jb<4>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-    case 5: err = launch_gateup_jb<5>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-    case 6: err = launch_gateup_jb<6>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-    case 7: err = launch_gateup_jb<7>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-    case 8: err = launch_gateup_jb<8>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-    default: return hipErrorInvalidValue;
+  if (phase != 2) {
+    const int J = w.H / 1024;
+    if (T == 1 && w.H % 1024 == 0 && J >= 1 && J <= 6 && w.I % 2 == 0) {
+#define MOE_GU(JJ)                                                                                 \
+  case JJ:                                                                                         \
+    hipLaunchKernelGGL((gateup_fast_kernel<JJ, 2>), fast_grid, dim3(kThreads), 0, s, x, k, E, w, e2s, \
+                       offsets, sorted_pair, h);                                                   \
+    break;
+      switch (J) { MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5) MOE_GU(6) }
+#undef MOE_GU
+      err = hipGetLastError();
+    } else {
+      const int jb1 = (w.H / 32 + 63) / 64;
+      const int rpw = pick_rows_per_wave(w.I, nb_max, target);
+      const int tiles = (w.I + kWaves * rpw - 1) / (kWaves * rpw);
+      const long items = (long)tiles * nb_max;
+      const dim3 grid((unsigned)(items < 4096 ? items : 4096));
+      switch (jb1) {
+        case 1: err = launch_gateup_jb<1>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
+        case 2: err = launch_gateup_jb<2>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
+        case 3: err = launch_gateup_jb<3>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
+        case 4: err = launch_gateup_jb<4>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
+        case 5: err = launch_gateup_jb<5>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
+        case 6: err = launch_gateup_jb<6>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
+        case 7: err = launch_gateup_jb<7>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
+        case 8: err = launch_gateup_jb<8>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
+        default: return hipErrorInvalidValue;
+      }
+    }
   }
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || phase == 1) return err;
 
-  rpw = pick_rows_per_wave(w.H, nb_max, target);
-  tiles = (w.H + kWaves * rpw - 1) / (kWaves * rpw);
-  items = (long)tiles * nb_max;
-  grid = dim3((unsigned)(items < 4096 ? items : 4096));
+  const int NB2 = w.I / 32, M = NB2 / 64, tail = NB2 % 64;
+  if (T == 1 && (tail == 0 || tail == 8) && M <= 1 && (M > 0 || tail == 8)) {
+#define MOE_DN(MM, TT)                                                                                  \
+  hipLaunchKernelGGL((down_fast_kernel<MM, TT>), fast_grid, dim3(kThreads), 0, s, k, E, w, e2s, offsets, \
+                     sorted_pair, h, y_pair)
+    if (tail == 8) {
+      if (M == 0) { MOE_DN(0, true); } else { MOE_DN(1, true); }
+    } else {
+      MOE_DN(1, false);
+    }
+#undef MOE_DN
+    return hipGetLastError();
+  }
+  const int jb2 = (NB2 + 63) / 64;
+  const int rpw = pick_rows_per_wave(w.H, nb_max, target);
+  const int tiles = (w.H + kWaves * rpw - 1) / (kWaves * rpw);
+  const long items = (long)tiles * nb_max;
+  const dim3 grid((unsigned)(items < 4096 ? items : 4096));
   switch (jb2) {
     case 1: return launch_down_jb<1>(grid, k, E, w, e2s, offsets, sorted_pair, h, y_pair, rpw, tiles, s);
     case 2: return launch_down_jb<2>(grid, k, E, w, e2s, offsets, sorted_pair, h, y_pair, rpw, tiles, s);

@@ -24,9 +24,10 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* offsets, in
 
 // Decode FFN: gate/up + SwiGLU into h (fp32, sorted-row order), then down.
 size_t decode_workspace_bytes(int T, int k, int I);
+// phase: 0 both kernels, 1 gate/up only, 2 down only.
 hipError_t launch_decode(const uint16_t* x, int T, int k, int E, const ExpertStore& w,
                          const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
-                         float* y_pair, void* ws, hipStream_t s);
+                         float* y_pair, void* ws, int phase, hipStream_t s);
 
 // Prefill FFN on block-scaled MFMA with MXFP8 activations.
 size_t prefill_workspace_bytes(int T, int k, int H, int I);

@@ -21,16 +21,21 @@ namespace moe {
 
 namespace {
 
-struct Pick {
-  int cls;   // 2 routable, 1 not routable, 0 absent / already taken
-  float v;
-  int e;
-};
+// Selection key: routable class, then logit, then lower expert index, packed
+// so that a larger unsigned key is the better candidate:
+//   bits 42-43 class (2 routable, 1 not routable, 0 absent or taken),
+//   bits 10-41 the logit mapped to an order-preserving unsigned integer
+//              (-0 folded onto +0, NaN read as -inf),
+//   bits  0-9  1023 - expert.
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+  if (v != v) v = -INFINITY;
+  v += 0.0f;                                      // -0 -> +0
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
-__device__ __forceinline__ bool better(const Pick& a, const Pick& b) {
-  if (a.cls != b.cls) return a.cls > b.cls;
-  if (a.v != b.v) return a.v > b.v;
-  return a.e < b.e;
+__device__ __forceinline__ float from_ordered_bits(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
 template <int NPL>
@@ -41,45 +46,38 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wavefront leaves together
   const float* row = logits + (size_t)t * E;
-  float v[NPL];
-  int cls[NPL];
+  uint64_t key[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
-      float x = row[e];
-      v[i] = (x != x) ? -INFINITY : x;
-      cls[i] = (e2s == nullptr || e2s[e] >= 0) ? 2 : 1;
+      const uint64_t cls = (e2s == nullptr || e2s[e] >= 0) ? 2 : 1;
+      key[i] = (cls << 42) | ((uint64_t)ordered_bits(row[e]) << 10) | (uint64_t)(1023 - e);
     } else {
-      v[i] = -INFINITY;
-      cls[i] = 0;
+      key[i] = 0;
     }
   }
-  Pick mine{0, -INFINITY, 0x7FFFFFFF};  // lane j keeps pick j
+  uint64_t mine = 0;  // lane j keeps pick j
   for (int j = 0; j < k; ++j) {
-    Pick best{0, -INFINITY, 0x7FFFFFFF};
+    uint64_t best = key[0];
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      Pick c{cls[i], v[i], lane + 64 * i};
-      if (c.cls > 0 && better(c, best)) best = c;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      Pick o{__shfl_xor(best.cls, off, 64), __shfl_xor(best.v, off, 64), __shfl_xor(best.e, off, 64)};
-      if (better(o, best)) best = o;
-    }
+    for (int i = 1; i < NPL; ++i) best = umax64(best, key[i]);
+    best = wave_max_u64(best);
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
-      if (lane + 64 * i == best.e) cls[i] = 0;
+      if (key[i] == best) key[i] = 0;              // keys are unique: only the winner matches
     if (lane == j) mine = best;
   }
-  const float v0 = __shfl(mine.v, 0, 64);
-  float d = mine.v - v0;
+  const int cls = (int)(mine >> 42);
+  const int e = 1023 - (int)(mine & 1023u);
+  const float v = from_ordered_bits((uint32_t)(mine >> 10));
+  const float v0 = __shfl(v, 0, 64);
+  float d = v - v0;
   if (d != d) d = 0.0f;
-  const float ex = (lane < k && mine.cls == 2) ? expf(d) : 0.0f;
-  const float s = wave_sum(ex);
+  const float ex = (lane < k && cls == 2) ? expf(d) : 0.0f;
+  const float s = wave_sum_dpp(ex);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = mine.e < E ? mine.e : 0;
+    ids[(size_t)t * k + lane] = (cls > 0 && e < E) ? e : 0;
     w[(size_t)t * k + lane] = s > 0.0f ? ex / s : 0.0f;
   }
 }

@@ -22,6 +22,7 @@ MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
 MOE_OUT_BF16, MOE_OUT_F32 = 0, 1
 MOE_ACT_MXFP8_E4M3 = 0
 EXPORTED = ("moe_route", "moe_permute", "moe_ffn_fp4_decode_workspace_bytes", "moe_ffn_fp4_decode",
+            "moe_ffn_fp4_decode_gateup", "moe_ffn_fp4_decode_down",
             "moe_ffn_fp4_prefill_workspace_bytes", "moe_ffn_fp4_prefill", "moe_combine",
             "moe_rmsnorm_bf16", "moe_status_string")
 
@@ -56,6 +57,8 @@ def lib() -> ctypes.CDLL:
             "moe_permute": [vp, i32, i32, i32, vp, vp, vp, vp],
             "moe_ffn_fp4_decode_workspace_bytes": [i32, i32, i32],
             "moe_ffn_fp4_decode": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp, vp, sz, vp],
+            "moe_ffn_fp4_decode_gateup": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp, vp, sz, vp],
+            "moe_ffn_fp4_decode_down": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp, vp, sz, vp],
             "moe_ffn_fp4_prefill_workspace_bytes": [i32, i32, i32, i32],
             "moe_ffn_fp4_prefill": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, ctypes.c_int,
                                     vp, vp, sz, vp],
@@ -196,20 +199,39 @@ def _ffn_args(x, k, store, expert_to_slot, expert_offsets, sorted_pair, y_pair):
     return T, y_pair
 
 
-def moe_ffn_fp4_decode(x: torch.Tensor, k: int, E: int, store: ExpertStore,
-                       expert_to_slot: torch.Tensor | None, expert_offsets: torch.Tensor,
-                       sorted_pair: torch.Tensor, y_pair: torch.Tensor | None = None,
-                       ws: torch.Tensor | None = None) -> torch.Tensor:
+def _decode_call(name, x, k, E, store, expert_to_slot, expert_offsets, sorted_pair, y_pair, ws):
     T, y_pair = _ffn_args(x, k, store, expert_to_slot, expert_offsets, sorted_pair, y_pair)
     need = decode_workspace_bytes(T, k, store.inter)
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     _want(ws, (torch.uint8,), "ws")
     cs = store.cstruct()
-    _check("moe_ffn_fp4_decode", lib().moe_ffn_fp4_decode(
+    _check(name, getattr(lib(), name)(
         _ptr(x), T, k, E, ctypes.byref(cs), _ptr(expert_to_slot), _ptr(expert_offsets), _ptr(sorted_pair),
         _ptr(y_pair), _ptr(ws), ws.numel(), _stream(x.device)))
     return y_pair
+
+
+def moe_ffn_fp4_decode(x: torch.Tensor, k: int, E: int, store: ExpertStore,
+                       expert_to_slot: torch.Tensor | None, expert_offsets: torch.Tensor,
+                       sorted_pair: torch.Tensor, y_pair: torch.Tensor | None = None,
+                       ws: torch.Tensor | None = None) -> torch.Tensor:
+    return _decode_call("moe_ffn_fp4_decode", x, k, E, store, expert_to_slot, expert_offsets, sorted_pair,
+                        y_pair, ws)
+
+
+def moe_ffn_fp4_decode_gateup(x, k, E, store, expert_to_slot, expert_offsets, sorted_pair, y_pair=None,
+                              ws=None) -> torch.Tensor:
+    """First kernel of the decode FFN: writes h into ``ws`` (y_pair untouched)."""
+    return _decode_call("moe_ffn_fp4_decode_gateup", x, k, E, store, expert_to_slot, expert_offsets,
+                        sorted_pair, y_pair, ws)
+
+
+def moe_ffn_fp4_decode_down(x, k, E, store, expert_to_slot, expert_offsets, sorted_pair, y_pair=None,
+                            ws=None) -> torch.Tensor:
+    """Second kernel of the decode FFN: reads h from ``ws``, writes y_pair."""
+    return _decode_call("moe_ffn_fp4_decode_down", x, k, E, store, expert_to_slot, expert_offsets,
+                        sorted_pair, y_pair, ws)
 
 
 def moe_ffn_fp4_prefill(x: torch.Tensor, k: int, E: int, store: ExpertStore,

@@ -38,7 +38,8 @@
  *    contents (finite logits, expert ids in range, at least k routable
  *    experts) are documented per call; when they are violated the kernels
  *    still stay inside every buffer, but the values written are unspecified.
- *  - T == 0 is valid everywhere and enqueues nothing.
+ *  - T == 0 is valid everywhere; it enqueues nothing, except moe_permute,
+ *    which still writes the E+1 zero offsets of the empty batch.
  */
 #ifndef MOE_FP4_H
 #define MOE_FP4_H
@@ -155,6 +156,23 @@ MOE_FP4_API moe_status moe_ffn_fp4_decode(const uint16_t* x_bf16, int32_t T, int
                                           const int32_t* expert_offsets, const int32_t* sorted_pair,
                                           float* y_pair, void* ws, size_t ws_bytes,
                                           hipStream_t stream);
+
+/* moe_ffn_fp4_decode_gateup, moe_ffn_fp4_decode_down -- the two kernels of
+ * moe_ffn_fp4_decode as separate calls with the same arguments: gateup writes
+ * h (fp32, sorted-row order) into the workspace, down reads it from there
+ * and writes y_pair.  gateup followed by down on one stream, with the same
+ * workspace, is exactly moe_ffn_fp4_decode.  They let a caller time or
+ * schedule the two weight streams separately. */
+MOE_FP4_API moe_status moe_ffn_fp4_decode_gateup(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                                 const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                                 const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                                 float* y_pair, void* ws, size_t ws_bytes,
+                                                 hipStream_t stream);
+MOE_FP4_API moe_status moe_ffn_fp4_decode_down(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                               const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                               const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                               float* y_pair, void* ws, size_t ws_bytes,
+                                               hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_ffn_fp4_prefill -- expert FFN of the prefill path on block-scaled MFMA.
