@@ -29,7 +29,6 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-FFN decode achieved HBM GB/s (% of peak); prefill tokens/s at 4096"
 PEAK_HBM = 8.0e12          # bytes/s, MI355X published HBM3E bandwidth
 PEAK_MXFP4 = 10.1e15       # FLOP/s, MI355X published dense MXFP4
-PEAK_MXFP8 = 5.0e15        # FLOP/s, MI355X published dense FP8
 NSETS = 64
 
 
@@ -225,7 +224,7 @@ def prefill_section(args, torch, m, gd, gi):
     touched = int((torch.diff(off) > 0).sum().item())
     log(f"prefill4096: {per * 1e3:.3f} ms/layer, {T / per / 1e6:.2f} M tok/s, {touched} experts")
     return dict(ms_per_layer=per * 1e3, tokens_per_s=T / per, tflops=flops / per / 1e12,
-                frac_of_mxfp4_peak=flops / per / PEAK_MXFP4, frac_of_fp8_peak=flops / per / PEAK_MXFP8,
+                frac_of_mxfp4_peak=flops / per / PEAK_MXFP4,
                 experts_touched=touched, weight_bytes=touched * cfg.expert_bytes)
 
 

@@ -29,7 +29,7 @@ hipError_t launch_decode(const uint16_t* x, int T, int k, int E, const ExpertSto
                          const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
                          float* y_pair, void* ws, int phase, hipStream_t s);
 
-// Prefill FFN on block-scaled MFMA with MXFP8 activations.
+// Prefill FFN on block-scaled MFMA with MXFP6 activations.
 size_t prefill_workspace_bytes(int T, int k, int H, int I);
 hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertStore& w,
                           const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,

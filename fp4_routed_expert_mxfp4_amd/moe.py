@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_fp4.so")
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN = 0, 1, 2, 3
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
 MOE_OUT_BF16, MOE_OUT_F32 = 0, 1
-MOE_ACT_MXFP8_E4M3 = 0
+MOE_ACT_MXFP6_E2M3 = 0
 EXPORTED = ("moe_route", "moe_permute", "moe_ffn_fp4_decode_workspace_bytes", "moe_ffn_fp4_decode",
             "moe_ffn_fp4_decode_gateup", "moe_ffn_fp4_decode_down",
             "moe_ffn_fp4_prefill_workspace_bytes", "moe_ffn_fp4_prefill", "moe_combine",
@@ -237,7 +237,7 @@ def moe_ffn_fp4_decode_down(x, k, E, store, expert_to_slot, expert_offsets, sort
 def moe_ffn_fp4_prefill(x: torch.Tensor, k: int, E: int, store: ExpertStore,
                         expert_to_slot: torch.Tensor | None, expert_offsets: torch.Tensor,
                         sorted_pair: torch.Tensor, y_pair: torch.Tensor | None = None,
-                        ws: torch.Tensor | None = None, act: int = MOE_ACT_MXFP8_E4M3) -> torch.Tensor:
+                        ws: torch.Tensor | None = None, act: int = MOE_ACT_MXFP6_E2M3) -> torch.Tensor:
     T, y_pair = _ffn_args(x, k, store, expert_to_slot, expert_offsets, sorted_pair, y_pair)
     need = prefill_workspace_bytes(T, k, store.hidden, store.inter)
     if ws is None:

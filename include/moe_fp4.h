@@ -68,7 +68,7 @@ typedef enum {
 typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out_dtype;
 
 /* Activation encoding of the prefill path (MX block format, 32 per scale). */
-typedef enum { MOE_ACT_MXFP8_E4M3 = 0 } moe_act_fmt;
+typedef enum { MOE_ACT_MXFP6_E2M3 = 0 } moe_act_fmt;
 
 /* One layer's expert store, the checkpoint's own layout, indexed by slot.
  * Slot s holds one expert; expert_to_slot tables map expert ids to slots.
@@ -178,12 +178,15 @@ MOE_FP4_API moe_status moe_ffn_fp4_decode_down(const uint16_t* x_bf16, int32_t T
  * moe_ffn_fp4_prefill -- expert FFN of the prefill path on block-scaled MFMA.
  * Same contract as moe_ffn_fp4_decode except for the activation arithmetic,
  * which follows the activation-quantisation switch of the DGX Spark page
- * ("Reproduce the checks"): with MOE_ACT_MXFP8_E4M3, x is quantised to MXFP8
- * (e4m3 codes, one UE8M0 scale per 32 along hidden) before gate/up, and h to
- * MXFP8 along inter before down.  Block exponent X = floor(log2 amax) - 8,
- * plus 1 when the significand of amax exceeds 1.75 (never saturates),
- * clamped to [-127, 127]; elements are rounded to nearest even.  The GEMMs
- * run on gfx950 V_MFMA_SCALE_F32_*_F8F6F4 (e4m3 x e2m1, fp32 accumulation).
+ * ("Reproduce the checks"; prefill and decode are separate arithmetic paths,
+ * "Fast single-box DeepSeek v4.1 Flash runtime", "Conventions"): with
+ * MOE_ACT_MXFP6_E2M3, x is quantised to MXFP6 (e2m3 codes, one UE8M0 scale
+ * per 32 along hidden) before gate/up, and h (fp32) to MXFP6 along inter
+ * before down.  Block exponent X = floor(log2 amax) - 2, plus 1 when the
+ * significand of amax exceeds 1.875 (never saturates), clamped to
+ * [-127, 127]; elements are rounded to nearest even.  Both GEMMs run on
+ * gfx950 V_MFMA_SCALE_F32_32X32X64_F8F6F4 with e2m3 x e2m1 operands, whose
+ * 32-term block sums are exact, accumulated in fp32.
  *   ws: at least moe_ffn_fp4_prefill_workspace_bytes(T, k, hidden, inter)
  *       bytes, 256-byte aligned
  * T >= 1, T*k <= 2^22.

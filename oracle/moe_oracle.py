@@ -20,7 +20,7 @@ Sources.  The pages describe the system this path belongs to:
           The numbers (a kept subset of experts stays routable), Reproduce the
           checks (engine checked against a pure-torch reference with
           activation quantisation on).
-  [OCP]   OCP Microscaling Formats (MX) Specification v1.0: the e2m1, e4m3 and
+  [OCP]   OCP Microscaling Formats (MX) Specification v1.0: the e2m1, e2m3 and
           E8M0 element/scale encodings.
 The pages print no formula for routing, SwiGLU or dequantisation; where they
 are silent the reading taken is stated at the function (R-... tags).
@@ -161,7 +161,7 @@ def permute(ids: np.ndarray, E: int):
 
 
 # --------------------------------------------------------------------------
-# Activation encodings used by the prefill path (R-ACT)
+# Activation encoding of the prefill path (R-ACT): MXFP6 E2M3
 # --------------------------------------------------------------------------
 
 
@@ -171,52 +171,54 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def e4m3_value(code: int) -> float:
-    """[OCP] FP8 E4M3: bias 7, subnormals m*2^-9, S.1111.111 is NaN, max 448."""
-    s, e, m = code >> 7, (code >> 3) & 15, code & 7
-    if e == 15 and m == 7:
-        return math.nan
-    mag = math.ldexp(1.0 + m / 8.0, e - 7) if e > 0 else math.ldexp(m / 8.0, -6)
+def e2m3_value(code: int) -> float:
+    """[OCP] FP6 E2M3: bits s e1 e0 m2 m1 m0, exponent bias 1, no inf/NaN.
+
+    E > 0: (-1)^s * 2^(E-1) * (1 + m/8);  E == 0: (-1)^s * m/8.  Max 7.5.
+    """
+    if not 0 <= code < 64:
+        raise ValueError("e2m3 code out of range")
+    s, e, m = code >> 5, (code >> 3) & 3, code & 7
+    mag = (2.0 ** (e - 1)) * (1.0 + m / 8.0) if e > 0 else m / 8.0
     return -mag if s else mag
 
 
-E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+E2M3_TABLE = np.array([e2m3_value(c) for c in range(64)], dtype=np.float64)
+E2M3_MAX = 7.5
 
 
-def e4m3_encode(t: np.ndarray) -> np.ndarray:
-    """Round t (already divided by the block scale) to the e4m3 grid, RNE.
+def e2m3_encode(t: np.ndarray) -> np.ndarray:
+    """Round t (already divided by the block scale) to the e2m3 grid, RNE.
 
-    Normal binades keep 3 mantissa bits; below 2^-6 the step is 2^-9.
-    Magnitudes above 448 saturate to 448 (only reachable when the shared
-    exponent was clamped at -127).  The sign bit is the sign of t, so a
-    negative value that rounds to zero encodes as 0x80.
+    Binades [1,2), [2,4), [4,8) keep 3 mantissa bits; below 1 the step is 1/8.
+    Magnitudes above 7.5 saturate to 7.5 (only reachable when the shared
+    exponent was clamped at -127).  The sign bit is the sign of t.
     """
     t = np.asarray(t, dtype=np.float64)
-    sign = np.where(np.signbit(t), 0x80, 0).astype(np.int64)
+    sign = np.where(np.signbit(t), 0x20, 0).astype(np.int64)
     a = np.abs(t)
-    e = np.frexp(a)[1] - 1                                 # a in [2^e, 2^(e+1)) for a > 0
-    quantum = np.ldexp(1.0, np.maximum(e - 3, -9))
-    q = np.minimum(np.rint(a / quantum) * quantum, 448.0)  # rint rounds half to even
+    e = np.frexp(a)[1] - 1                                  # a in [2^e, 2^(e+1)) for a > 0
+    quantum = np.ldexp(1.0, np.maximum(e - 3, -3))
+    q = np.minimum(np.rint(a / quantum) * quantum, E2M3_MAX)  # rint rounds half to even
     qe = np.frexp(q)[1] - 1
-    normal = q >= 2.0 ** -6
+    normal = q >= 1.0
     m_norm = np.where(normal, (np.ldexp(q, -np.where(normal, qe, 0)) - 1.0) * 8.0, 0.0)
-    code_norm = ((qe + 7) << 3) + m_norm.astype(np.int64)
-    code_sub = (q / 2.0 ** -9).astype(np.int64)
-    code = np.where(normal, code_norm, code_sub)
-    return (sign | code).astype(np.uint8)
+    code_norm = ((qe + 1) << 3) + m_norm.astype(np.int64)
+    code_sub = (q * 8.0).astype(np.int64)
+    return (sign | np.where(normal, code_norm, code_sub)).astype(np.uint8)
 
 
-def q8_rows(a: np.ndarray):
-    """MXFP8 (e4m3) quantisation along the last axis in 32-blocks.  R-ACT.
+def q6_rows(a: np.ndarray):
+    """MXFP6 (e2m3) quantisation along the last axis in 32-blocks.  R-ACT.
 
-    Per block: shared exponent X = floor(log2 amax) - 8, plus one when the
-    significand of amax exceeds 1.75 (so amax * 2^-X <= 448 and nothing
-    saturates); X is clamped to [-127, 127]; scale byte = X + 127.  A block
-    with amax == 0 gets scale byte 0 and all-zero codes.  Elements are
-    v * 2^-X rounded to nearest even on the e4m3 grid.  [OCP] defines the
-    encodings; the pages only show an activation-quantisation switch
-    ([SPARK] "Reproduce the checks").  Returns (codes uint8 [rows][K],
-    scale bytes uint8 [rows][K/32]).
+    Per block: shared exponent X = floor(log2 amax) - 2, plus one when the
+    significand of amax exceeds 1.875 -- the smallest power-of-two scale
+    under which no element exceeds 7.5, so nothing saturates; X is clamped
+    to [-127, 127]; scale byte = X + 127.  A block with amax == 0 gets scale
+    byte 0 and all-zero codes.  Elements are v * 2^-X rounded to nearest
+    even on the e2m3 grid.  [OCP] defines the encodings; the pages only show
+    an activation-quantisation switch ([SPARK] "Reproduce the checks").
+    Returns (codes uint8 [rows][K], scale bytes uint8 [rows][K/32]).
     """
     a = np.asarray(a, dtype=np.float64)
     rows, K = a.shape
@@ -224,23 +226,23 @@ def q8_rows(a: np.ndarray):
     amax = np.max(np.abs(blocks), axis=2)
     frac, ex = np.frexp(amax)                  # amax = frac * 2^ex, frac in [0.5, 1)
     E, M = ex - 1, 2.0 * frac                  # amax = M * 2^E, M in [1, 2)
-    X = np.clip(E - 8 + (M > 1.75), -127, 127)
+    X = np.clip(E - 2 + (M > 1.875), -127, 127)
     zero = amax == 0.0
     X = np.where(zero, -127, X)
-    codes = e4m3_encode(np.ldexp(blocks, -X[..., None]))
+    codes = e2m3_encode(np.ldexp(blocks, -X[..., None]))
     codes[zero] = 0
     return codes.reshape(rows, K), (X + 127).astype(np.uint8)
 
 
-def q8_block(v: np.ndarray):
-    """Q8 of a single 32-element block: (codes uint8[32], scale byte)."""
-    c, s = q8_rows(np.asarray(v, dtype=np.float64).reshape(1, 32))
+def q6_block(v: np.ndarray):
+    """Q6 of a single 32-element block: (codes uint8[32], scale byte)."""
+    c, s = q6_rows(np.asarray(v, dtype=np.float64).reshape(1, 32))
     return c[0], int(s[0, 0])
 
 
-def q8_dequant(codes: np.ndarray, sb: np.ndarray) -> np.ndarray:
+def q6_dequant(codes: np.ndarray, sb: np.ndarray) -> np.ndarray:
     rows, K = codes.shape
-    v = E4M3_TABLE[codes].reshape(rows, K // 32, 32)
+    v = E2M3_TABLE[codes].reshape(rows, K // 32, 32)
     return (v * np.ldexp(1.0, sb.astype(np.int64) - 127)[..., None]).reshape(rows, K)
 
 
@@ -265,21 +267,22 @@ def expert_ffn(x: np.ndarray, weights, expert: int, mode: str = "a16") -> np.nda
 
     weights(expert, matrix) -> (codes, scales) with matrix 0 gate, 1 up,
     2 down.  mode "a16": x as given, no intermediate rounding (the decode
-    reference).  mode "a8" (R-ACT, the prefill reference): x is replaced by
-    Q8(x) before gate/up, and h by Q8(h) before down, h being rounded to
+    reference).  mode "a6" (R-ACT, the prefill reference): x is replaced by
+    Q6(x) before gate/up, and h by Q6(h) before down, h being rounded to
     float32 first so the quantiser decides on the same precision the kernel
-    holds h in.
+    holds h in.  Prefill and decode are separate arithmetic paths judged
+    against their own references ([DS4] "Conventions").
     """
     wg = dequant(*weights(expert, 0))
     wu = dequant(*weights(expert, 1))
     wd = dequant(*weights(expert, 2))
-    if mode == "a8":
-        x = q8_dequant(*q8_rows(x))
+    if mode == "a6":
+        x = q6_dequant(*q6_rows(x))
     elif mode != "a16":
         raise ValueError(mode)
     h = swiglu(x @ wg.T, x @ wu.T)
-    if mode == "a8":
-        h = q8_dequant(*q8_rows(round_f32(h)))
+    if mode == "a6":
+        h = q6_dequant(*q6_rows(round_f32(h)))
     return h @ wd.T
 
 

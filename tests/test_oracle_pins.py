@@ -258,55 +258,89 @@ def test_combine_closed_form():
 
 # ---------------------------------------------------------------- quantiser and bf16
 
-def test_q8_hand_cases(golden_dir):
-    for case in load(golden_dir, "q8_hand.json")["cases"]:
+def test_e2m3_table():
+    tab = o.E2M3_TABLE
+    assert tab.sum() == 0.0
+    mags = sorted(set(abs(v) for v in tab))
+    assert mags == [i / 8 for i in range(8)] + [1 + i / 8 for i in range(8)] + \
+        [2 + i / 4 for i in range(8)] + [4 + i / 2 for i in range(8)]
+    assert tab.max() == 7.5 and tab[0x1F] == 7.5 and tab[0x3F] == -7.5
+
+
+def test_q6_hand_cases(golden_dir):
+    for case in load(golden_dir, "q6_hand.json")["cases"]:
         v = np.zeros(32)
         v[:len(case["elements"])] = case["elements"]
-        codes, sb = o.q8_block(v)
+        codes, sb = o.q6_block(v)
         assert sb == case["scale_byte"], case
         assert codes[:len(case["codes"])].tolist() == case["codes"], case
         assert np.all(codes[len(case["codes"]):] == 0)
 
 
-def test_e4m3_table_against_torch():
-    # torch's float8_e4m3fn is an independent implementation of the same OCP encoding
-    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
-    tv = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
-    ours = o.E4M3_TABLE
-    finite = ~np.isnan(tv)
-    assert np.array_equal(np.isnan(ours), np.isnan(tv))
-    np.testing.assert_array_equal(ours[finite], tv[finite])
+def _brute_e2m3(t):
+    """Nearest e2m3 code by exhaustive search over the 32 magnitudes; ties to the even code."""
+    mags = o.E2M3_TABLE[:32]
+    a = np.abs(t)[..., None]
+    d = np.abs(mags[None, :] - a)
+    best = d.min(axis=-1, keepdims=True)
+    cand = np.where(d == best, np.arange(32), 99)
+    even = np.where(cand % 2 == 0, cand, 99).min(axis=-1)
+    code = np.where(even < 99, even, cand.min(axis=-1))
+    code = np.where(np.abs(t) > 7.5, 31, code)
+    return (code | np.where(np.signbit(t), 0x20, 0)).astype(np.uint8)
 
 
-def test_q8_rounding_against_torch_random():
-    # For a block whose scale is fixed, the element codes are RNE float -> e4m3,
-    # which torch implements independently (saturation never triggers here).
-    rng = np.random.default_rng(3)
-    a = (rng.standard_normal((64, 256)) * np.exp(rng.uniform(-8, 8, (64, 1)))).astype(np.float32).astype(np.float64)
-    codes, sb = o.q8_rows(a)
+def test_e2m3_rounding_against_brute_force():
+    rng = np.random.default_rng(6)
+    t = np.concatenate([rng.uniform(-7.5, 7.5, 20000), np.arange(-60, 61) / 8.0, np.arange(-60, 61) / 16.0,
+                        np.arange(8, 16) / 2 + 0.25, [0.0, -0.0, 1e-9, -1e-9]])
+    np.testing.assert_array_equal(o.e2m3_encode(t), _brute_e2m3(t))
+
+
+def test_q6_scale_is_smallest_non_saturating():
+    rng = np.random.default_rng(7)
+    a = (rng.standard_normal((200, 64)) * np.exp(rng.uniform(-20, 20, (200, 1)))).astype(np.float32)
+    a = a.astype(np.float64)
+    codes, sb = o.q6_rows(a)
+    amax = np.abs(a.reshape(200, 2, 32)).max(-1)
     X = sb.astype(np.int64) - 127
-    t = torch.from_numpy(np.ldexp(a.reshape(64, 8, 32), -X[..., None]).reshape(64, 256))
-    tc = t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    np.testing.assert_array_equal(codes, tc)
-    # non-saturating: every block's amax fits under 448 after scaling
-    assert np.all(np.abs(t.numpy()) <= 448)
-    # and the scale is the smallest that fits: one step smaller would overflow 448 (up to rounding)
-    assert np.all(np.abs(t.numpy()).reshape(64, 8, 32).max(-1) * 2 > 448 * (1 - 1 / 16))
+    # brute force: the smallest integer X with amax * 2^-X <= 7.5
+    for i in range(200):
+        for b in range(2):
+            x = -140
+            while np.ldexp(amax[i, b], -x) > 7.5:
+                x += 1
+            assert X[i, b] == x
+    # and the codes are the nearest grid points of v * 2^-X
+    t = np.ldexp(a.reshape(200, 2, 32), -X[..., None]).reshape(200, 64)
+    np.testing.assert_array_equal(codes, _brute_e2m3(t))
 
 
-def test_q8_exhaustive_bf16_against_torch():
-    # every finite bf16 value, 32 per block in pattern order; codes vs torch RNE at the same scale
+def test_q6_exhaustive_bf16_against_brute_force():
     bits = np.arange(65536, dtype=np.uint32)
     with np.errstate(invalid="ignore"):
         vals = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
     vals = vals[np.isfinite(vals)]
     vals = vals[: len(vals) // 32 * 32].reshape(-1, 32)
-    codes, sb = o.q8_rows(vals)
+    codes, sb = o.q6_rows(vals)
     X = sb.astype(np.int64) - 127
     t = np.ldexp(vals.reshape(-1, 1, 32), -X[..., None]).reshape(vals.shape)
-    tc = torch.from_numpy(t).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     zero_blocks = np.max(np.abs(vals), axis=1) == 0
-    np.testing.assert_array_equal(codes[~zero_blocks], tc[~zero_blocks])
+    np.testing.assert_array_equal(codes[~zero_blocks], _brute_e2m3(t[~zero_blocks]))
+    assert np.all(codes[zero_blocks] == 0) and np.all(sb[zero_blocks] == 0)
+
+
+def test_q6_dequant_error_bound():
+    # every element is within half a step of its grid: 2^-4 relative in the normal
+    # binades, 1/16 absolute (times the block scale) below 1
+    rng = np.random.default_rng(8)
+    a = rng.standard_normal((64, 256))
+    codes, sb = o.q6_rows(a)
+    back = o.q6_dequant(codes, sb)
+    scale = np.repeat(np.ldexp(1.0, sb.astype(np.int64) - 127), 32, axis=1)
+    t = np.abs(a) / scale
+    bound = np.where(t >= 1, np.ldexp(1.0, np.frexp(t)[1] - 1 - 4), 1 / 16) * scale
+    assert np.all(np.abs(back - a) <= bound * (1 + 1e-12))
 
 
 def test_bf16_rne_against_torch():
