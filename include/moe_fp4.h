@@ -189,6 +189,7 @@ MOE_FP4_API moe_status moe_ffn_fp4_decode_down(const uint16_t* x_bf16, int32_t T
  * 32-term block sums are exact, accumulated in fp32.
  *   ws: at least moe_ffn_fp4_prefill_workspace_bytes(T, k, hidden, inter)
  *       bytes, 256-byte aligned
+ *   the scale arrays of w must be 4-byte aligned on this path
  * T >= 1, T*k <= 2^22.
  * ------------------------------------------------------------------------- */
 MOE_FP4_API size_t moe_ffn_fp4_prefill_workspace_bytes(int32_t T, int32_t k, int32_t hidden,
