@@ -32,6 +32,28 @@ PEAK_MXFP4 = 10.1e15       # FLOP/s, MI355X published dense MXFP4
 NSETS = 64
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode1_gateup_traffic.md")
+DECODE_SRC = os.path.join(ROOT, "fp4_routed_expert_mxfp4_amd", "csrc", "decode.hip")
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter summary,
+    or None when that summary was taken on a different kernel source."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE).read()
+        src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines() if line.startswith(("source_sha256:", "traffic_bytes_per_launch:")))
+    if fields.get("source_sha256", "").strip() != src:
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -46,6 +68,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-chain", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=("decode", "prefill", "chain"), default=None,
+                    help="run one section only (for profiling); prints that section's numbers")
     ap.add_argument("--calibrate", action="store_true",
                     help="only time torch's plain copy of 4 GiB (the HBM-bytes calibration kernel)")
     return ap.parse_args()
@@ -202,11 +226,12 @@ def prefill_section(args, torch, m, gd, gi):
     p2r = torch.empty(T * k, dtype=torch.int32, device=dev)
     y = torch.empty((T * k, cfg.H), dtype=torch.float32, device=dev)
     ws = torch.empty(m.prefill_workspace_bytes(T, k, cfg.H, cfg.I), dtype=torch.uint8, device=dev)
+    pws = torch.empty(max(m.permute_workspace_bytes(T, k, E), 256), dtype=torch.uint8, device=dev)
     out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
 
     def step(_i):
         m.moe_route(logits, k, None, ids, w)
-        m.moe_permute(ids, E, off, sp, p2r)
+        m.moe_permute(ids, E, off, sp, p2r, pws)
         m.moe_ffn_fp4_prefill(x, k, E, store, None, off, sp, y, ws)
         m.moe_combine(y, w, None, m.MOE_OUT_BF16, out)
 
@@ -342,6 +367,14 @@ def main() -> int:
         print(json.dumps({"calibration": calibrate(torch)}), flush=True)
         return 0
 
+    if args.only:
+        fn = {"decode": decode_section, "prefill": prefill_section, "chain": chain_section}[args.only]
+        res = fn(args, torch, m, gd, gi)
+        if isinstance(res, dict):
+            res.pop("db", None)
+        print(json.dumps({"section": args.only, "result": res}), flush=True)
+        return 0
+
     dec = decode_section(args, torch, m, gd, gi)
     cfg = gi.CONFIGS["decode1"]
     prefill = None if args.no_prefill else prefill_section(args, torch, m, gd, gi)
@@ -369,7 +402,7 @@ def main() -> int:
         "frac_of_peak_hbm": round(dec["gbps"] * 1e9 / PEAK_HBM, 4),
         "roofline": {"kernel": "decode gate/up + SwiGLU (moe_ffn_fp4_decode_gateup)", "bound": "hbm",
                      "achieved": round(gu_achieved / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                     "frac": round(gu_achieved / PEAK_HBM, 4), "traffic": None,
+                     "frac": round(gu_achieved / PEAK_HBM, 4), "traffic": measured_traffic(),
                      "avg_us": round(dec["gateup_us"], 2), "bytes_per_launch": dec["gateup_bytes"]},
         "down_kernel": {"avg_us": round(dec["down_us"], 2), "bytes_per_launch": dec["down_bytes"],
                         "achieved_GBps": round(dec["down_bytes"] / dec["down_us"] / 1e3, 1)},

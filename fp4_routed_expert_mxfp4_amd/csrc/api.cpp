@@ -72,15 +72,23 @@ MOE_FP4_API moe_status moe_route(const float* logits, int32_t T, int32_t E, int3
   return launched(moe::launch_route(logits, T, E, k, expert_to_slot, topk_ids, topk_w, stream));
 }
 
+MOE_FP4_API size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || E < 1) return 0;
+  return moe::permute_workspace_bytes(T * k, E);
+}
+
 MOE_FP4_API moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                                    int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_to_row,
-                                   hipStream_t stream) {
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
   if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
   if ((int64_t)T * k > (1 << 24)) return MOE_ERR_SHAPE;
   if (!expert_offsets) return MOE_ERR_NULL;
   if (T > 0 && (!topk_ids || !sorted_pair || !pair_to_row)) return MOE_ERR_NULL;
+  const size_t need = moe::permute_workspace_bytes(T * k, E);
+  if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (need > 0 && misaligned(ws, 256)) return MOE_ERR_ALIGN;
   // T == 0 still enqueues: the offsets of an empty batch are all zero.
-  return launched(moe::launch_permute(topk_ids, T * k, E, expert_offsets, sorted_pair, pair_to_row, stream));
+  return launched(moe::launch_permute(topk_ids, T * k, E, expert_offsets, sorted_pair, pair_to_row, ws, stream));
 }
 
 MOE_FP4_API size_t moe_ffn_fp4_decode_workspace_bytes(int32_t T, int32_t k, int32_t inter) {

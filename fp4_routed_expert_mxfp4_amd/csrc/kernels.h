@@ -19,8 +19,9 @@ struct ExpertStore {
 hipError_t launch_route(const float* logits, int T, int E, int k, const int32_t* e2s, int32_t* ids,
                         float* w, hipStream_t s);
 
+size_t permute_workspace_bytes(int P, int E);
 hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pair,
-                          int32_t* pair_to_row, hipStream_t s);
+                          int32_t* pair_to_row, void* ws, hipStream_t s);
 
 // Decode FFN: gate/up + SwiGLU into h (fp32, sorted-row order), then down.
 size_t decode_workspace_bytes(int T, int k, int I);

@@ -278,6 +278,31 @@ __device__ __forceinline__ void mma_chunk(const GemmBuf& d, f16v (&acc)[2][2], i
   }
 }
 
+// The K loop: two LDS buffers and a ring of three register sets, so the
+// global loads of chunk c+3 are in flight while chunk c is multiplied and
+// chunk c+1 is moved into LDS.
+template <typename Load>
+__device__ __forceinline__ void k_loop(GemmSmem& sm, f16v (&acc)[2][2], Load& load, int nchunks, int tid, int lane,
+                                       int arow0, int brow0, int bstep) {
+  ChunkRegs r0, r1, r2;
+  load(0, r0);
+  if (nchunks > 1) load(1, r1);
+  if (nchunks > 2) load(2, r2);
+  store_chunk(sm.buf[0], r0, tid);
+  __syncthreads();
+  auto step = [&](int c, ChunkRegs& next, ChunkRegs& spare) {
+    if (c + 3 < nchunks) load(c + 3, spare);
+    mma_chunk(sm.buf[c & 1], acc, arow0, brow0, bstep, lane);
+    if (c + 1 < nchunks) store_chunk(sm.buf[(c + 1) & 1], next, tid);
+    __syncthreads();
+  };
+  for (int c = 0; c < nchunks; c += 3) {
+    step(c, r1, r0);
+    if (c + 1 < nchunks) step(c + 1, r2, r1);
+    if (c + 2 < nchunks) step(c + 2, r0, r2);
+  }
+}
+
 // ---- P1: gate/up GEMM, SwiGLU and MXFP6 of h ----------------------------------
 
 __global__ __launch_bounds__(kPT, 2) void gateup_mfma_kernel(
@@ -337,17 +362,7 @@ __global__ __launch_bounds__(kPT, 2) void gateup_mfma_kernel(
     for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int g = 0; g < 2; ++g) acc[f][g] = f16v{};
-    ChunkRegs r;
-    load(0, r);
-    store_chunk(sm.buf[0], r, tid);
-    __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-      const bool more = c + 1 < nchunks;
-      if (more) load(c + 1, r);
-      mma_chunk(sm.buf[c & 1], acc, 64 * wm, 32 * wn, 64, lane);  // B: gate rows 32wn.., up rows 64+32wn..
-      if (more) store_chunk(sm.buf[(c + 1) & 1], r, tid);
-      __syncthreads();
-    }
+    k_loop(sm, acc, load, nchunks, tid, lane, 64 * wm, 32 * wn, 64);  // B: gate rows 32wn.., up 64+32wn..
     // h = silu(g) * u into the staging buffer, then MXFP6 per (row, 32-block)
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
@@ -440,17 +455,7 @@ __global__ __launch_bounds__(kPT, 2) void down_mfma_kernel(
     for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int g = 0; g < 2; ++g) acc[f][g] = f16v{};
-    ChunkRegs r;
-    load(0, r);
-    store_chunk(sm.buf[0], r, tid);
-    __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-      const bool more = c + 1 < nchunks;
-      if (more) load(c + 1, r);
-      mma_chunk(sm.buf[c & 1], acc, 64 * wm, 64 * wn, 32, lane);
-      if (more) store_chunk(sm.buf[(c + 1) & 1], r, tid);
-      __syncthreads();
-    }
+    k_loop(sm, acc, load, nchunks, tid, lane, 64 * wm, 64 * wn, 32);
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
 #pragma unroll

@@ -85,84 +85,163 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ ids, int P,
-                                                               int E, int32_t* __restrict__ offsets,
-                                                               int32_t* __restrict__ sorted_pair,
-                                                               int32_t* __restrict__ pair_to_row) {
-  __shared__ int cursor[kMaxExperts];
-  __shared__ int hist[kPermWaves][kMaxExperts];
-  __shared__ int wave_tot[kPermWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+struct PermSmem {
+  int cursor[kMaxExperts];
+  int hist[kPermWaves][kMaxExperts];
+  int wave_tot[kPermWaves];
+};
 
-  for (int e = tid; e < kMaxExperts; e += kPermThreads) {
-    cursor[e] = 0;
+__device__ void zero_hist(PermSmem& sm) {
+  for (int e = threadIdx.x; e < kMaxExperts; e += kPermThreads) {
+    sm.cursor[e] = 0;
 #pragma unroll
-    for (int w = 0; w < kPermWaves; ++w) hist[w][e] = 0;
+    for (int w = 0; w < kPermWaves; ++w) sm.hist[w][e] = 0;
   }
-  __syncthreads();
-  for (int p = tid; p < P; p += kPermThreads) {
-    const int e = ids[p];
-    if (e >= 0 && e < E) atomicAdd(&cursor[e], 1);
-  }
-  __syncthreads();
+}
 
-  // exclusive scan of the counts (E <= 1024: one expert per thread)
-  const int c = tid < E ? cursor[tid] : 0;
+// Exclusive scan of c (one value per thread, E <= 1024 threads); returns the
+// exclusive prefix of this thread and, in *total, the sum.
+__device__ int block_exclusive_scan(PermSmem& sm, int c, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int incl = c;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int o = __shfl_up(incl, off, 64);
     if (lane >= off) incl += o;
   }
-  if (lane == 63) wave_tot[wave] = incl;
+  if (lane == 63) sm.wave_tot[wave] = incl;
   __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wave_tot[w];
-  const int excl = before + incl - c;
+  int before = 0, all = 0;
+  for (int w = 0; w < kPermWaves; ++w) {
+    const int v = sm.wave_tot[w];
+    before += w < wave ? v : 0;
+    all += v;
+  }
+  *total = all;
+  return before + incl - c;
+}
+
+// Stable scatter of the pairs [base, base+1024) given cursor[e] = first row
+// of expert e still free.  Within a wavefront equal experts are ranked with
+// ballots; the per-wave histograms give the rows taken by earlier wavefronts.
+__device__ void scatter_round(PermSmem& sm, const int32_t* __restrict__ ids, int P, int E, int base,
+                              int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_to_row) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int p = base + tid;
+  const int e = p < P ? ids[p] : -1;
+  const bool valid = (e >= 0 && e < E);
+  if (p < P && !valid) pair_to_row[p] = -1;
+  uint64_t active = __ballot(valid);
+  int my_rank = 0, my_cnt = 0;
+  bool leader = false;
+  while (active) {
+    const int ll = __ffsll((unsigned long long)active) - 1;
+    const int ev = __shfl(e, ll, 64);
+    const bool match = valid && e == ev;
+    const uint64_t m = __ballot(match);
+    if (match) {
+      my_rank = __popcll(m & lt_mask);
+      my_cnt = __popcll(m);
+      leader = (lane == ll);
+    }
+    active &= ~m;
+  }
+  if (leader) sm.hist[wave][e] = my_cnt;
+  __syncthreads();
+  if (valid) {
+    int pre = 0;
+    for (int w = 0; w < wave; ++w) pre += sm.hist[w][e];
+    const int pos = sm.cursor[e] + pre + my_rank;
+    sorted_pair[pos] = p;
+    pair_to_row[p] = pos;
+  }
+  __syncthreads();
+  if (leader) {
+    atomicAdd(&sm.cursor[e], my_cnt);
+    sm.hist[wave][e] = 0;
+  }
+  __syncthreads();
+}
+
+// Whole bucketing in one workgroup (used when all pairs fit in one round).
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                               int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ sorted_pair,
+                                                               int32_t* __restrict__ pair_to_row) {
+  __shared__ PermSmem sm;
+  const int tid = threadIdx.x;
+  zero_hist(sm);
+  __syncthreads();
+  for (int p = tid; p < P; p += kPermThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&sm.cursor[e], 1);
+  }
+  __syncthreads();
+  const int c = tid < E ? sm.cursor[tid] : 0;
+  int total;
+  const int excl = block_exclusive_scan(sm, c, &total);
   if (tid < E) {
     offsets[tid] = excl;
-    cursor[tid] = excl;
-    if (tid == E - 1) offsets[E] = excl + c;
+    sm.cursor[tid] = excl;
+  }
+  if (tid == 0) offsets[E] = total;
+  __syncthreads();
+  for (int base = 0; base < P; base += kPermThreads)
+    scatter_round(sm, ids, P, E, base, sorted_pair, pair_to_row);
+}
+
+// Multi-workgroup bucketing: workgroup b owns pairs [1024b, 1024b+1024).
+// (1) per-chunk histograms -> ws[b][e]; (2) one workgroup turns them into the
+// first free row of expert e for chunk b and writes the offsets; (3) each
+// chunk scatters its pairs from those rows.  The order is the same stable
+// (expert, pair) order as the single-workgroup kernel.
+__global__ __launch_bounds__(kPermThreads) void permute_count_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                                     int32_t* __restrict__ ws) {
+  __shared__ int cnt[kMaxExperts];
+  const int tid = threadIdx.x;
+  cnt[tid] = 0;
+  __syncthreads();
+  const int p = blockIdx.x * kPermThreads + tid;
+  if (p < P) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
+  if (tid < E) ws[(size_t)blockIdx.x * E + tid] = cnt[tid];
+}
 
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < P; base += kPermThreads) {
-    const int p = base + tid;
-    const int e = p < P ? ids[p] : -1;
-    const bool valid = (e >= 0 && e < E);
-    if (p < P && !valid) pair_to_row[p] = -1;
-    uint64_t active = __ballot(valid);
-    int my_rank = 0, my_cnt = 0;
-    bool leader = false;
-    while (active) {
-      const int ll = __ffsll((unsigned long long)active) - 1;
-      const int ev = __shfl(e, ll, 64);
-      const bool match = valid && e == ev;
-      const uint64_t m = __ballot(match);
-      if (match) {
-        my_rank = __popcll(m & lt_mask);
-        my_cnt = __popcll(m);
-        leader = (lane == ll);
-      }
-      active &= ~m;
+__global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(int nchunks, int E, int32_t* __restrict__ ws,
+                                                                    int32_t* __restrict__ offsets) {
+  __shared__ PermSmem sm;
+  const int tid = threadIdx.x;
+  int tot = 0;
+  if (tid < E)
+    for (int b = 0; b < nchunks; ++b) tot += ws[(size_t)b * E + tid];
+  int total;
+  const int excl = block_exclusive_scan(sm, tid < E ? tot : 0, &total);
+  if (tid < E) {
+    offsets[tid] = excl;
+    int acc = excl;
+    for (int b = 0; b < nchunks; ++b) {
+      const int t = ws[(size_t)b * E + tid];
+      ws[(size_t)b * E + tid] = acc;
+      acc += t;
     }
-    if (leader) hist[wave][e] = my_cnt;
-    __syncthreads();
-    if (valid) {
-      int pre = 0;
-      for (int w = 0; w < wave; ++w) pre += hist[w][e];
-      const int pos = cursor[e] + pre + my_rank;
-      sorted_pair[pos] = p;
-      pair_to_row[p] = pos;
-    }
-    __syncthreads();
-    if (leader) {
-      atomicAdd(&cursor[e], my_cnt);
-      hist[wave][e] = 0;
-    }
-    __syncthreads();
   }
+  if (tid == 0) offsets[E] = total;
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                                       const int32_t* __restrict__ ws,
+                                                                       int32_t* __restrict__ sorted_pair,
+                                                                       int32_t* __restrict__ pair_to_row) {
+  __shared__ PermSmem sm;
+  zero_hist(sm);
+  __syncthreads();
+  if (threadIdx.x < E) sm.cursor[threadIdx.x] = ws[(size_t)blockIdx.x * E + threadIdx.x];
+  __syncthreads();
+  scatter_round(sm, ids, P, E, blockIdx.x * kPermThreads, sorted_pair, pair_to_row);
 }
 
 }  // namespace
@@ -184,10 +263,29 @@ hipError_t launch_route(const float* logits, int T, int E, int k, const int32_t*
   return hipGetLastError();
 }
 
+size_t permute_workspace_bytes(int P, int E) {
+  if (P <= kPermThreads) return 0;
+  const size_t chunks = ((size_t)P + kPermThreads - 1) / kPermThreads;
+  return (chunks * E * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
 hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pair,
-                          int32_t* pair_to_row, hipStream_t s) {
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, ids, P, E, offsets,
-                     sorted_pair, pair_to_row);
+                          int32_t* pair_to_row, void* ws, hipStream_t s) {
+  if (P <= kPermThreads) {
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, ids, P, E, offsets, sorted_pair,
+                       pair_to_row);
+    return hipGetLastError();
+  }
+  const int chunks = (P + kPermThreads - 1) / kPermThreads;
+  int32_t* w = reinterpret_cast<int32_t*>(ws);
+  hipLaunchKernelGGL(permute_count_kernel, dim3(chunks), dim3(kPermThreads), 0, s, ids, P, E, w);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kPermThreads), 0, s, chunks, E, w, offsets);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(chunks), dim3(kPermThreads), 0, s, ids, P, E, w, sorted_pair,
+                     pair_to_row);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN = 0, 1, 2, 3
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
 MOE_OUT_BF16, MOE_OUT_F32 = 0, 1
 MOE_ACT_MXFP6_E2M3 = 0
-EXPORTED = ("moe_route", "moe_permute", "moe_ffn_fp4_decode_workspace_bytes", "moe_ffn_fp4_decode",
+EXPORTED = ("moe_route", "moe_permute_workspace_bytes", "moe_permute", "moe_ffn_fp4_decode_workspace_bytes", "moe_ffn_fp4_decode",
             "moe_ffn_fp4_decode_gateup", "moe_ffn_fp4_decode_down",
             "moe_ffn_fp4_prefill_workspace_bytes", "moe_ffn_fp4_prefill", "moe_combine",
             "moe_rmsnorm_bf16", "moe_status_string")
@@ -54,7 +54,8 @@ def lib() -> ctypes.CDLL:
         vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
         sig = {
             "moe_route": [vp, i32, i32, i32, vp, vp, vp, vp],
-            "moe_permute": [vp, i32, i32, i32, vp, vp, vp, vp],
+            "moe_permute_workspace_bytes": [i32, i32, i32],
+            "moe_permute": [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp],
             "moe_ffn_fp4_decode_workspace_bytes": [i32, i32, i32],
             "moe_ffn_fp4_decode": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp, vp, sz, vp],
             "moe_ffn_fp4_decode_gateup": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp, vp, sz, vp],
@@ -70,6 +71,7 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        L.moe_permute_workspace_bytes.restype = sz
         L.moe_ffn_fp4_decode_workspace_bytes.restype = sz
         L.moe_ffn_fp4_prefill_workspace_bytes.restype = sz
         L.moe_status_string.restype = ctypes.c_char_p
@@ -160,8 +162,13 @@ def moe_route(logits: torch.Tensor, k: int, expert_to_slot: torch.Tensor | None 
     return topk_ids, topk_w
 
 
+def permute_workspace_bytes(T: int, k: int, E: int) -> int:
+    return int(lib().moe_permute_workspace_bytes(T, k, E))
+
+
 def moe_permute(topk_ids: torch.Tensor, E: int, expert_offsets: torch.Tensor | None = None,
-                sorted_pair: torch.Tensor | None = None, pair_to_row: torch.Tensor | None = None):
+                sorted_pair: torch.Tensor | None = None, pair_to_row: torch.Tensor | None = None,
+                ws: torch.Tensor | None = None):
     _want(topk_ids, (torch.int32,), "topk_ids")
     T, k = topk_ids.shape
     dev = topk_ids.device
@@ -173,8 +180,14 @@ def moe_permute(topk_ids: torch.Tensor, E: int, expert_offsets: torch.Tensor | N
         pair_to_row = torch.empty(T * k, dtype=torch.int32, device=dev)
     for n, t in (("expert_offsets", expert_offsets), ("sorted_pair", sorted_pair), ("pair_to_row", pair_to_row)):
         _want(t, (torch.int32,), n)
+    need = permute_workspace_bytes(T, k, E)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    if ws is not None:
+        _want(ws, (torch.uint8,), "ws")
     _check("moe_permute", lib().moe_permute(_ptr(topk_ids), T, k, E, _ptr(expert_offsets), _ptr(sorted_pair),
-                                            _ptr(pair_to_row), _stream(dev)))
+                                            _ptr(pair_to_row), _ptr(ws), 0 if ws is None else ws.numel(),
+                                            _stream(dev)))
     return expert_offsets, sorted_pair, pair_to_row
 
 

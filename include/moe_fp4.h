@@ -124,12 +124,17 @@ MOE_FP4_API moe_status moe_route(const float* logits, int32_t T, int32_t E, int3
  *   expert_offsets [E+1] int32 out
  *   sorted_pair    [T*k] int32 out
  *   pair_to_row    [T*k] int32 out
+ *   ws             device workspace of moe_permute_workspace_bytes(T, k, E)
+ *                  bytes, 256-byte aligned (may be NULL when that is 0, which
+ *                  it is for T*k <= 1024)
  * T*k <= 2^24.  Ids outside [0, E) are left out of every bucket (their
  * pair_to_row entry is -1 and expert_offsets[E] counts only valid pairs).
  * ------------------------------------------------------------------------- */
+MOE_FP4_API size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E);
 MOE_FP4_API moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                                    int32_t* expert_offsets, int32_t* sorted_pair,
-                                   int32_t* pair_to_row, hipStream_t stream);
+                                   int32_t* pair_to_row, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_ffn_fp4_decode -- expert FFN of the decode path (fp32 accumulation).

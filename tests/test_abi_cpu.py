@@ -81,10 +81,17 @@ def test_route_validation():
 def test_permute_validation():
     m = _lib()
     L = m.lib()
-    assert L.moe_permute(FAKE, 1, 2, 8, None, FAKE, FAKE, None) == m.MOE_ERR_NULL
-    assert L.moe_permute(None, 1, 2, 8, FAKE, FAKE, FAKE, None) == m.MOE_ERR_NULL
-    assert L.moe_permute(FAKE, 1, 2, 2000, FAKE, FAKE, FAKE, None) == m.MOE_ERR_SHAPE
-    assert L.moe_permute(FAKE, 1 << 22, 8, 8, FAKE, FAKE, FAKE, None) == m.MOE_ERR_SHAPE
+    assert L.moe_permute(FAKE, 1, 2, 8, None, FAKE, FAKE, None, 0, None) == m.MOE_ERR_NULL
+    assert L.moe_permute(None, 1, 2, 8, FAKE, FAKE, FAKE, None, 0, None) == m.MOE_ERR_NULL
+    assert L.moe_permute(FAKE, 1, 2, 2000, FAKE, FAKE, FAKE, None, 0, None) == m.MOE_ERR_SHAPE
+    assert L.moe_permute(FAKE, 1 << 22, 8, 8, FAKE, FAKE, FAKE, None, 0, None) == m.MOE_ERR_SHAPE
+    # more than one 1024-pair chunk needs the workspace
+    need = m.permute_workspace_bytes(4096, 8, 384)
+    assert need == 32 * 384 * 4
+    assert m.permute_workspace_bytes(128, 8, 384) == 0
+    assert L.moe_permute(FAKE, 4096, 8, 384, FAKE, FAKE, FAKE, None, 0, None) == m.MOE_ERR_WORKSPACE
+    assert L.moe_permute(FAKE, 4096, 8, 384, FAKE, FAKE, FAKE, FAKE, need - 1, None) == m.MOE_ERR_WORKSPACE
+    assert L.moe_permute(FAKE, 4096, 8, 384, FAKE, FAKE, FAKE, FAKE + 16, need, None) == m.MOE_ERR_ALIGN
 
 
 def _decode(m, x=FAKE, T=1, k=2, E=8, store=None, e2s=None, off=FAKE, sp=FAKE, y=FAKE, ws=FAKE, ws_bytes=1 << 20):
