@@ -102,24 +102,29 @@ class DecodeBench:
         self.p2r = torch.empty((NSETS, T * k), dtype=i32, device=dev)
         self.y = torch.empty((T * k, cfg.H), dtype=f32, device=dev)
         self.ws = torch.empty(m.decode_workspace_bytes(T, k, cfg.I), dtype=torch.uint8, device=dev)
+        self.lws = torch.empty(m.decode_layer_workspace_bytes(T, k, E, cfg.H, cfg.I), dtype=torch.uint8,
+                               device=dev)
         self.out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
 
-    def step(self, s: int) -> None:
+    def step(self, s: int, phase: int = 0) -> None:
+        """One decode layer in one call (two kernels at this shape)."""
+        m, c = self.m, self.cfg
+        m.moe_decode_layer(self.logits[s], self.x, c.k, self.store, None, None, m.MOE_OUT_BF16, self.out,
+                           self.ids[s], self.w[s], self.lws, phase=phase)
+
+    def gateup(self, s: int) -> None:
+        self.step(s, 1)
+
+    def down(self, s: int) -> None:
+        self.step(s, 2)
+
+    def step_separate(self, s: int) -> None:
+        """The same layer as four separate calls (five kernels)."""
         m, c = self.m, self.cfg
         m.moe_route(self.logits[s], c.k, None, self.ids[s], self.w[s])
         m.moe_permute(self.ids[s], c.E, self.off[s], self.sp[s], self.p2r[s])
         m.moe_ffn_fp4_decode(self.x, c.k, c.E, self.store, None, self.off[s], self.sp[s], self.y, self.ws)
         m.moe_combine(self.y, self.w[s], None, m.MOE_OUT_BF16, self.out)
-
-    def gateup(self, s: int) -> None:
-        c = self.cfg
-        self.m.moe_ffn_fp4_decode_gateup(self.x, c.k, c.E, self.store, None, self.off[s], self.sp[s], self.y,
-                                         self.ws)
-
-    def down(self, s: int) -> None:
-        c = self.cfg
-        self.m.moe_ffn_fp4_decode_down(self.x, c.k, c.E, self.store, None, self.off[s], self.sp[s], self.y,
-                                       self.ws)
 
     def touched(self) -> list[int]:
         """Distinct experts routed per set (host copy of the device routing)."""
@@ -191,6 +196,11 @@ def decode_section(args, torch, m, gd, gi):
     t = time_graphs(torch, step_graphs, args.steps)
     per_step_bytes = [layer_bytes(cfg, touched[i % NSETS], cfg.T) for i in range(args.steps)]
     gbps = sum(per_step_bytes) / t / 1e9
+    # for comparison: the four separate calls
+    sep_graphs = capture(torch, db.step_separate, NSETS)
+    time_graphs(torch, sep_graphs, 16)
+    sep_steps = min(args.steps, 512)
+    t_sep = time_graphs(torch, sep_graphs, sep_steps) / sep_steps
     # the gate/up kernel alone, then the down kernel alone: one graph of 64
     # back-to-back launches over the 64 routings, replayed; HIP events on the
     # replay stream bracket the whole timed region
@@ -201,13 +211,16 @@ def decode_section(args, torch, m, gd, gi):
     t_gu = time_graphs(torch, [gu_graph], reps) / (reps * NSETS)
     time_graphs(torch, [dn_graph], 2)
     t_dn = time_graphs(torch, [dn_graph], reps) / (reps * NSETS)
-    gu_bytes = cfg.k * (2 * cfg.I * (cfg.H // 2 + cfg.H // 32)) + cfg.H * 2 + cfg.k * cfg.I * 4
-    dn_bytes = cfg.k * (cfg.H * (cfg.I // 2 + cfg.I // 32)) + cfg.k * cfg.I * 4 + cfg.k * cfg.H * 4
+    # algorithmic bytes of each half: the k experts' weights, x or h, the logits, h, and the output
+    gu_bytes = (cfg.k * (2 * cfg.I * (cfg.H // 2 + cfg.H // 32)) + cfg.H * 2 + cfg.E * 4
+                + cfg.k * cfg.I * 4)
+    dn_bytes = cfg.k * (cfg.H * (cfg.I // 2 + cfg.I // 32)) + cfg.k * cfg.I * 4 + cfg.H * 2
     res = dict(seconds=t, gbps=gbps, ms_per_step=t / args.steps * 1e3, touched_mean=sum(touched) / NSETS,
                gateup_us=t_gu * 1e6, gateup_bytes=gu_bytes, down_us=t_dn * 1e6, down_bytes=dn_bytes,
-               db=db)
-    log(f"decode1: {res['ms_per_step'] * 1e3:.1f} us/step, {gbps:.0f} GB/s; gate/up {t_gu * 1e6:.1f} us "
-        f"({gu_bytes / t_gu / 1e9:.0f} GB/s), down {t_dn * 1e6:.1f} us ({dn_bytes / t_dn / 1e9:.0f} GB/s)")
+               separate_us=t_sep * 1e6, db=db)
+    log(f"decode1: {res['ms_per_step'] * 1e3:.1f} us/step, {gbps:.0f} GB/s (separate calls: {t_sep * 1e6:.1f} us); "
+        f"route+gate/up {t_gu * 1e6:.1f} us ({gu_bytes / t_gu / 1e9:.0f} GB/s), down+combine {t_dn * 1e6:.1f} us "
+        f"({dn_bytes / t_dn / 1e9:.0f} GB/s)")
     return res
 
 
@@ -273,17 +286,13 @@ def chain_section(args, torch, m, gd, gi):
     w = torch.empty((cfg.layers, T, k), dtype=torch.float32, device=dev)
     off = torch.empty((cfg.layers, E + 1), dtype=torch.int32, device=dev)
     sp = torch.empty((cfg.layers, T * k), dtype=torch.int32, device=dev)
-    p2r = torch.empty((cfg.layers, T * k), dtype=torch.int32, device=dev)
-    y = torch.empty((T * k, H), dtype=torch.float32, device=dev)
-    ws = torch.empty(m.decode_workspace_bytes(T, k, cfg.I), dtype=torch.uint8, device=dev)
+    ws = torch.empty(m.decode_layer_workspace_bytes(T, k, E, H, cfg.I), dtype=torch.uint8, device=dev)
 
     def token(_i):
         for layer in range(cfg.layers):
             m.moe_rmsnorm_bf16(xs[layer], 1e-6, n)
-            m.moe_route(logits[layer], k, e2s[layer], ids[layer], w[layer])
-            m.moe_permute(ids[layer], E, off[layer], sp[layer], p2r[layer])
-            m.moe_ffn_fp4_decode(n, k, E, stores[layer], e2s[layer], off[layer], sp[layer], y, ws)
-            m.moe_combine(y, w[layer], xs[layer], m.MOE_OUT_BF16, xs[layer + 1])
+            m.moe_decode_layer(logits[layer], n, k, stores[layer], e2s[layer], xs[layer], m.MOE_OUT_BF16,
+                               xs[layer + 1], ids[layer], w[layer], ws)
 
     graphs = capture(torch, token, 1)
     time_graphs(torch, graphs, 3)
@@ -400,11 +409,14 @@ def main() -> int:
                    "hidden": cfg.H, "expert_width": cfg.I, "experts": cfg.E, "top_k": cfg.k, "tokens": cfg.T,
                    "weights": "e2m1 + UE8M0/32", "activations": "bf16"},
         "frac_of_peak_hbm": round(dec["gbps"] * 1e9 / PEAK_HBM, 4),
-        "roofline": {"kernel": "decode gate/up + SwiGLU (moe_ffn_fp4_decode_gateup)", "bound": "hbm",
+        "separate_calls_us_per_step": round(dec["separate_us"], 2),
+        "roofline": {"kernel": "decode route + gate/up + SwiGLU (fused_gateup_kernel, moe_decode_layer_gateup)",
+                     "bound": "hbm",
                      "achieved": round(gu_achieved / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                      "frac": round(gu_achieved / PEAK_HBM, 4), "traffic": measured_traffic(),
                      "avg_us": round(dec["gateup_us"], 2), "bytes_per_launch": dec["gateup_bytes"]},
-        "down_kernel": {"avg_us": round(dec["down_us"], 2), "bytes_per_launch": dec["down_bytes"],
+        "down_kernel": {"kernel": "decode down + combine (fused_down_combine_kernel, moe_decode_layer_down)",
+                        "avg_us": round(dec["down_us"], 2), "bytes_per_launch": dec["down_bytes"],
                         "achieved_GBps": round(dec["down_bytes"] / dec["down_us"] / 1e3, 1)},
         "cpu_baseline": cpu,
         "prefill4096": prefill,

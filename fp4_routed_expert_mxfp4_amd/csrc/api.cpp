@@ -133,6 +133,113 @@ MOE_FP4_API moe_status moe_ffn_fp4_decode_down(const uint16_t* x_bf16, int32_t T
                       stream);
 }
 
+namespace {
+
+struct LayerWs {
+  int32_t *offsets, *sorted_pair, *pair_to_row;
+  void* pws;
+  void* hws;
+  float* y;
+  size_t total;
+};
+
+size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+LayerWs layer_ws_layout(int T, int k, int E, int H, int I, void* base) {
+  const size_t P = (size_t)T * k;
+  uint8_t* p = reinterpret_cast<uint8_t*>(base);
+  LayerWs l;
+  size_t off = 0;
+  l.offsets = reinterpret_cast<int32_t*>(p + off);
+  off += up256((size_t)(E + 1) * 4);
+  l.sorted_pair = reinterpret_cast<int32_t*>(p + off);
+  off += up256(P * 4);
+  l.pair_to_row = reinterpret_cast<int32_t*>(p + off);
+  off += up256(P * 4);
+  l.pws = p + off;
+  off += up256(moe::permute_workspace_bytes((int)P, E));
+  l.hws = p + off;
+  off += up256(moe::decode_workspace_bytes(T, k, I));
+  l.y = reinterpret_cast<float*>(p + off);
+  off += up256(P * H * 4);
+  l.total = off;
+  return l;
+}
+
+}  // namespace
+
+MOE_FP4_API size_t moe_decode_layer_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t hidden, int32_t inter) {
+  if (T < 1 || k < 1 || E < 1 || hidden < 1 || inter < 1) return 0;
+  if (moe::fused_decode_supported(T, k, E, hidden, inter)) return moe::fused_decode_workspace_bytes(k, inter);
+  return layer_ws_layout(T, k, E, hidden, inter, nullptr).total;
+}
+
+static moe_status decode_layer(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E, int32_t k,
+                               const int32_t* expert_to_slot, const moe_fp4_experts* w, const uint16_t* residual_bf16,
+                               moe_out_dtype od, void* out, int32_t* topk_ids, float* topk_w, void* ws,
+                               size_t ws_bytes, int phase, hipStream_t stream) {
+  if (T > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+  if (od != MOE_OUT_BF16 && od != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
+  moe_status st = check_store(w);
+  if (st != MOE_OK) return st;
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS || k > E) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!logits || !x_bf16 || !out || !topk_ids || !topk_w) return MOE_ERR_NULL;
+  if (!expert_to_slot && w->num_slots < E) return MOE_ERR_SHAPE;
+  if (misaligned(x_bf16, 16) || misaligned(out, 16) || (residual_bf16 && misaligned(residual_bf16, 16)))
+    return MOE_ERR_ALIGN;
+  const size_t need = moe_decode_layer_workspace_bytes(T, k, E, w->hidden, w->inter);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (misaligned(ws, 256)) return MOE_ERR_ALIGN;
+  const moe::ExpertStore store = to_store(w);
+  const bool bf16 = od == MOE_OUT_BF16;
+  if (moe::fused_decode_supported(T, k, E, w->hidden, w->inter))
+    return launched(moe::launch_decode_fused(logits, x_bf16, E, k, expert_to_slot, store, residual_bf16, bf16, out,
+                                             topk_ids, topk_w, ws, phase, stream));
+  const LayerWs l = layer_ws_layout(T, k, E, w->hidden, w->inter, ws);
+  hipError_t e = hipSuccess;
+  if (phase != 2) {
+    e = moe::launch_route(logits, T, E, k, expert_to_slot, topk_ids, topk_w, stream);
+    if (e == hipSuccess)
+      e = moe::launch_permute(topk_ids, T * k, E, l.offsets, l.sorted_pair, l.pair_to_row, l.pws, stream);
+    if (e == hipSuccess)
+      e = moe::launch_decode(x_bf16, T, k, E, store, expert_to_slot, l.offsets, l.sorted_pair, l.y, l.hws, 1, stream);
+  }
+  if (phase != 1) {
+    if (e == hipSuccess)
+      e = moe::launch_decode(x_bf16, T, k, E, store, expert_to_slot, l.offsets, l.sorted_pair, l.y, l.hws, 2, stream);
+    if (e == hipSuccess) e = moe::launch_combine(l.y, topk_w, T, k, w->hidden, residual_bf16, bf16, out, stream);
+  }
+  return launched(e);
+}
+
+MOE_FP4_API moe_status moe_decode_layer(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E, int32_t k,
+                                        const int32_t* expert_to_slot, const moe_fp4_experts* w,
+                                        const uint16_t* residual_bf16, moe_out_dtype od, void* out,
+                                        int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out, topk_ids, topk_w, ws,
+                      ws_bytes, 0, stream);
+}
+
+MOE_FP4_API moe_status moe_decode_layer_gateup(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E,
+                                               int32_t k, const int32_t* expert_to_slot, const moe_fp4_experts* w,
+                                               const uint16_t* residual_bf16, moe_out_dtype od, void* out,
+                                               int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                                               hipStream_t stream) {
+  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out, topk_ids, topk_w, ws,
+                      ws_bytes, 1, stream);
+}
+
+MOE_FP4_API moe_status moe_decode_layer_down(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E,
+                                             int32_t k, const int32_t* expert_to_slot, const moe_fp4_experts* w,
+                                             const uint16_t* residual_bf16, moe_out_dtype od, void* out,
+                                             int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                                             hipStream_t stream) {
+  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out, topk_ids, topk_w, ws,
+                      ws_bytes, 2, stream);
+}
+
 MOE_FP4_API size_t moe_ffn_fp4_prefill_workspace_bytes(int32_t T, int32_t k, int32_t hidden, int32_t inter) {
   if (T < 0 || k < 1 || hidden < 1 || inter < 1) return 0;
   return moe::prefill_workspace_bytes(T, k, hidden, inter);

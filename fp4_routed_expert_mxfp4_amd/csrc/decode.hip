@@ -25,6 +25,7 @@
 // activations in registers for the whole row walk.
 #include "common.cuh"
 #include "kernels.h"
+#include "route_core.cuh"
 
 namespace moe {
 
@@ -536,6 +537,184 @@ __global__ __launch_bounds__(kThreads, 2) void down_fast_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused one-token decode layer: two launches instead of five.
+//
+// K1 (route + gate/up): every workgroup routes the token itself (one
+//   wavefront, the router of route_core.cuh), so no workgroup waits for
+//   another; the buckets of a one-token batch are its k experts in ascending
+//   id.  Then the same gate/up row walk as gateup_fast_kernel writes h.
+//   Workgroup 0 also publishes the routing for K2 and the caller.
+// K2 (down + combine): one wavefront per routed expert over a slice of 24
+//   output rows (three 8-row batches of down_fast_kernel's walk); the k rows
+//   meet in LDS and are summed in ascending slot order exactly as
+//   combine_kernel does, plus the residual, straight into the output.
+// Per-row arithmetic is that of the separate kernels, so the result is
+// bit-identical to route -> permute -> decode -> combine.
+// ---------------------------------------------------------------------------
+
+constexpr int kFusedMaxK = 8;
+constexpr int kFusedRows = 24;
+
+struct FusedRoute {
+  int expert[kMaxTopK];       // bucket order: ascending expert id
+  int slot[kMaxTopK];         // storage slot of each bucket's expert (-1: none)
+  int row_of_pair[kMaxTopK];  // bucket row of slot j
+  float w[kMaxTopK];          // weight of slot j
+};
+
+template <int NPL>
+__device__ void fused_route(const float* __restrict__ logits, int E, int k, const int32_t* __restrict__ e2s,
+                            int num_slots, FusedRoute& fr, FusedRoute* __restrict__ pub,
+                            int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const RoutePick pick = route_token<NPL>(logits, E, k, e2s, lane);
+    // rank of this slot's expert among the k picks (ties broken by slot)
+    int r = 0;
+    for (int i = 0; i < k; ++i) {
+      const int ei = __shfl(pick.expert, i, 64);
+      r += (ei < pick.expert || (ei == pick.expert && i < lane)) ? 1 : 0;
+    }
+    if (lane < k) {
+      int sl = e2s ? e2s[pick.expert] : pick.expert;
+      if (sl >= num_slots) sl = -1;
+      fr.expert[r] = pick.expert;
+      fr.slot[r] = sl;
+      fr.row_of_pair[lane] = r;
+      fr.w[lane] = pick.weight;
+      if (blockIdx.x == 0) {
+        topk_ids[lane] = pick.expert;
+        topk_w[lane] = pick.weight;
+        pub->expert[r] = pick.expert;
+        pub->slot[r] = sl;
+        pub->row_of_pair[lane] = r;
+        pub->w[lane] = pick.weight;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <int NPL, int J>
+__global__ __launch_bounds__(kThreads, 2) void fused_gateup_kernel(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x, int E, int k, const int32_t* __restrict__ e2s,
+    ExpertStore w, FusedRoute* __restrict__ pub, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+    float* __restrict__ h) {
+  constexpr int R = 2;
+  constexpr int NB = 32 * J;
+  __shared__ FusedRoute fr;
+  fused_route<NPL>(logits, E, k, e2s, w.num_slots, fr, pub, topk_ids, topk_w);
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int total_waves = gridDim.x * kWaves;
+  const int I = w.I;
+  const size_t rowbytes = (size_t)16 * NB;
+  const int nbat = I / R;
+  int C = total_waves / k;
+  if (C < 1) C = 1;
+  const int cs = (nbat + C - 1) / C;
+  const int units = k * C;
+  // the token's x: lane l owns blocks (l + 64j) mod NB of the concatenated gate/up row
+  uint4 xr[J][4];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int f = lane + 64 * j, blk = f >= NB ? f - NB : f;
+    const uint4* px = reinterpret_cast<const uint4*>(x + blk * 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xr[j][q] = px[q];
+  }
+  for (int unit = gw; unit < units; unit += total_waves) {
+    const int b = unit / C, c = unit - b * C;
+    const int bat0 = c * cs, bat1 = min(bat0 + cs, nbat);
+    if (bat0 >= bat1) continue;
+    const int slot = fr.slot[b];
+    if (slot < 0) continue;  // no stored expert: K2 contributes zero rows
+    const uint8_t* cb[2] = {w.wg + (size_t)slot * I * rowbytes, w.wu + (size_t)slot * I * rowbytes};
+    const uint8_t* sb[2] = {w.sg + (size_t)slot * I * NB, w.su + (size_t)slot * I * NB};
+    const uint8_t* cp[J];
+    const uint8_t* sp[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int f = lane + 64 * j, mat = f >= NB ? 1 : 0, blk = f - mat * NB;
+      cp[j] = cb[mat] + blk * 16;
+      sp[j] = sb[mat] + blk;
+    }
+    float* hrow = h + (size_t)b * I;
+    GateUpBatch<J, R> A, Bn;
+    gu_load(A, cp, sp, bat0 * R, rowbytes, NB);
+    for (int bat = bat0; bat < bat1; bat += 2) {
+      const bool has1 = bat + 1 < bat1;
+      if (has1) gu_load(Bn, cp, sp, (bat + 1) * R, rowbytes, NB);
+      gu_finish(A, xr, lane, hrow, bat * R);
+      if (bat + 2 < bat1) gu_load(A, cp, sp, (bat + 2) * R, rowbytes, NB);
+      if (has1) gu_finish(Bn, xr, lane, hrow, (bat + 1) * R);
+    }
+  }
+}
+
+template <int M, bool TAIL, bool kBf16Out>
+__global__ __launch_bounds__(kFusedMaxK * 64) void fused_down_combine_kernel(
+    int k, ExpertStore w, const FusedRoute* __restrict__ pub, const float* __restrict__ h,
+    const uint16_t* __restrict__ residual, void* __restrict__ out) {
+  constexpr int NB = 64 * M + (TAIL ? 8 : 0);
+  constexpr int MM = M > 0 ? M : 1;
+  __shared__ FusedRoute fr;
+  __shared__ float ybuf[kFusedMaxK][kFusedRows];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < kMaxTopK) {
+    fr.expert[tid] = pub->expert[tid];
+    fr.slot[tid] = pub->slot[tid];
+    fr.row_of_pair[tid] = pub->row_of_pair[tid];
+    fr.w[tid] = pub->w[tid];
+  }
+  __syncthreads();
+  const int H = w.H, I = w.I;
+  const int m0 = blockIdx.x * kFusedRows;
+  const int nb = min(kFusedRows, H - m0) / 8;  // 8-row batches in this slice
+  const int slot = fr.slot[wave];
+  if (slot < 0) {
+    if (lane < kFusedRows) ybuf[wave][lane] = 0.f;
+  } else {
+    const size_t rowbytes = (size_t)16 * NB;
+    const uint8_t* dc = w.wd + (size_t)slot * H * rowbytes;
+    const uint8_t* ds = w.sd + (size_t)slot * H * NB;
+    float4_t hm[MM][8], ht[8];
+    const float* hr = h + (size_t)wave * I;
+#pragma unroll
+    for (int mm = 0; mm < M; ++mm) {
+      const float4_t* p = reinterpret_cast<const float4_t*>(hr + (64 * mm + lane) * 32);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) hm[mm][q] = p[q];
+    }
+    if (TAIL) {
+      const float4_t* p = reinterpret_cast<const float4_t*>(hr + (64 * M + (lane & 7)) * 32);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ht[q] = p[q];
+    }
+    DownBatch<M, TAIL> A, Bn;
+    dn_load(A, dc, ds, m0, lane, rowbytes, NB);
+    for (int bat = 0; bat < nb; bat += 2) {
+      const bool has1 = bat + 1 < nb;
+      if (has1) dn_load(Bn, dc, ds, m0 + (bat + 1) * 8, lane, rowbytes, NB);
+      dn_finish(A, hm, ht, lane, ybuf[wave], bat * 8);
+      if (bat + 2 < nb) dn_load(A, dc, ds, m0 + (bat + 2) * 8, lane, rowbytes, NB);
+      if (has1) dn_finish(Bn, hm, ht, lane, ybuf[wave], (bat + 1) * 8);
+    }
+  }
+  __syncthreads();
+  if (tid < nb * 8) {
+    const int m = m0 + tid;
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) acc = fmaf(fr.w[j], ybuf[fr.row_of_pair[j]][tid], acc);
+    if (residual) acc += bf16_bits_to_f32(residual[m]);
+    if (kBf16Out)
+      reinterpret_cast<uint16_t*>(out)[m] = f32_to_bf16_rne(acc);
+    else
+      reinterpret_cast<float*>(out)[m] = acc;
+  }
+}
+
 template <int JB>
 hipError_t launch_gateup_jb(dim3 grid, const uint16_t* x, int k, int E, const ExpertStore& w,
                             const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
@@ -561,6 +740,50 @@ int pick_rows_per_wave(int rows, int nb_max, int target_waves) {
 }
 
 }  // namespace
+
+bool fused_decode_supported(int T, int k, int E, int H, int I) {
+  const int NB2 = I / 32, tail = NB2 % 64, M = NB2 / 64;
+  return T == 1 && k <= kFusedMaxK && E <= kMaxExperts && H % 1024 == 0 && H / 1024 <= 6 &&
+         (tail == 0 || tail == 8) && M <= 1 && (M > 0 || tail == 8);
+}
+
+size_t fused_decode_workspace_bytes(int k, int I) {
+  return 512 + (((size_t)k * I * sizeof(float) + 255) & ~(size_t)255);
+}
+
+hipError_t launch_decode_fused(const float* logits, const uint16_t* x, int E, int k, const int32_t* e2s,
+                               const ExpertStore& w, const uint16_t* residual, bool bf16_out, void* out,
+                               int32_t* topk_ids, float* topk_w, void* ws, int phase, hipStream_t s) {
+  FusedRoute* pub = reinterpret_cast<FusedRoute*>(ws);
+  float* h = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + 512);
+  const int J = w.H / 1024, npl = (E + 63) / 64;
+  const dim3 g1(512), b1(kThreads);
+  if (phase != 2) {
+#define MOE_FGU(NP, JJ)                                                                                      \
+  hipLaunchKernelGGL((fused_gateup_kernel<NP, JJ>), g1, b1, 0, s, logits, x, E, k, e2s, w, pub, topk_ids, topk_w, h)
+#define MOE_FGU_J(NP)                                                                                        \
+  switch (J) { case 1: MOE_FGU(NP, 1); break; case 2: MOE_FGU(NP, 2); break; case 3: MOE_FGU(NP, 3); break;  \
+               case 4: MOE_FGU(NP, 4); break; case 5: MOE_FGU(NP, 5); break; default: MOE_FGU(NP, 6); break; }
+  if (npl <= 1) { MOE_FGU_J(1) } else if (npl <= 2) { MOE_FGU_J(2) } else if (npl <= 4) { MOE_FGU_J(4) }
+  else if (npl <= 8) { MOE_FGU_J(8) } else { MOE_FGU_J(16) }
+#undef MOE_FGU_J
+#undef MOE_FGU
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || phase == 1) return err;
+  }
+  const int NB2 = w.I / 32, M = NB2 / 64, tail = NB2 % 64;
+  const dim3 g2((w.H + kFusedRows - 1) / kFusedRows), b2(k * 64);
+#define MOE_FDC(MM, TT, BF)                                                                                  \
+  hipLaunchKernelGGL((fused_down_combine_kernel<MM, TT, BF>), g2, b2, 0, s, k, w, pub, h, residual, out)
+  if (tail == 8) {
+    if (M == 0) { if (bf16_out) MOE_FDC(0, true, true); else MOE_FDC(0, true, false); }
+    else { if (bf16_out) MOE_FDC(1, true, true); else MOE_FDC(1, true, false); }
+  } else {
+    if (bf16_out) MOE_FDC(1, false, true); else MOE_FDC(1, false, false);
+  }
+#undef MOE_FDC
+  return hipGetLastError();
+}
 
 size_t decode_workspace_bytes(int T, int k, int I) {
   size_t b = (size_t)T * k * I * sizeof(float);

@@ -180,6 +180,50 @@ MOE_FP4_API moe_status moe_ffn_fp4_decode_down(const uint16_t* x_bf16, int32_t T
                                                hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_decode_layer -- one whole decode layer: moe_route, moe_permute,
+ * moe_ffn_fp4_decode and moe_combine in one call, with the same results bit
+ * for bit.  Kernel boundaries cost a measurable share of a decode token
+ * ("DeepSeek V4.1 Flash Q4 / 27 September 2026", "28 September follow-up":
+ * 3-5 ms of command-buffer boundaries in a 43 ms token); for one token
+ * (T == 1, k <= 8, hidden a multiple of 1024 up to 6144, inter = 2048*M or
+ * 2048*M + 256 with M <= 1) the layer runs as two kernels: route + gate/up,
+ * then down + the fixed-order slot sum written straight to `out`.  Other
+ * shapes run the four steps with their intermediates in the workspace.
+ *   logits [T][E] fp32, x_bf16 [T][hidden] bf16 (16-byte aligned),
+ *   expert_to_slot, w: as for moe_route and moe_ffn_fp4_decode
+ *   residual_bf16 [T][hidden] or NULL; od, out [T][hidden]: as moe_combine
+ *   topk_ids [T][k], topk_w [T][k]: the routing (outputs, as moe_route)
+ *   ws: moe_decode_layer_workspace_bytes(T, k, E, hidden, inter) bytes,
+ *       256-byte aligned; contents on entry do not matter
+ * 1 <= T <= MOE_DECODE_MAX_TOKENS.
+ * ------------------------------------------------------------------------- */
+MOE_FP4_API size_t moe_decode_layer_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t hidden,
+                                                    int32_t inter);
+MOE_FP4_API moe_status moe_decode_layer(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E,
+                                        int32_t k, const int32_t* expert_to_slot,
+                                        const moe_fp4_experts* w, const uint16_t* residual_bf16,
+                                        moe_out_dtype od, void* out, int32_t* topk_ids, float* topk_w,
+                                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_decode_layer_gateup, moe_decode_layer_down -- the two halves of
+ * moe_decode_layer with the same arguments: gateup routes (writing topk_ids,
+ * topk_w and the routing state in ws) and runs the gate/up + SwiGLU weight
+ * stream (h into ws); down runs the down-projection stream and the combine
+ * into out.  gateup then down on one stream, with the same workspace, is
+ * exactly moe_decode_layer.  They let a caller time or schedule the two
+ * weight streams apart. */
+MOE_FP4_API moe_status moe_decode_layer_gateup(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E,
+                                               int32_t k, const int32_t* expert_to_slot,
+                                               const moe_fp4_experts* w, const uint16_t* residual_bf16,
+                                               moe_out_dtype od, void* out, int32_t* topk_ids, float* topk_w,
+                                               void* ws, size_t ws_bytes, hipStream_t stream);
+MOE_FP4_API moe_status moe_decode_layer_down(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E,
+                                             int32_t k, const int32_t* expert_to_slot,
+                                             const moe_fp4_experts* w, const uint16_t* residual_bf16,
+                                             moe_out_dtype od, void* out, int32_t* topk_ids, float* topk_w,
+                                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_ffn_fp4_prefill -- expert FFN of the prefill path on block-scaled MFMA.
  * Same contract as moe_ffn_fp4_decode except for the activation arithmetic,
  * which follows the activation-quantisation switch of the DGX Spark page

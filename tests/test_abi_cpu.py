@@ -143,3 +143,37 @@ def test_python_binding_refuses_cpu_tensors():
     m = _lib()
     with pytest.raises(ValueError):
         m.moe_route(torch.zeros((1, 8)), 2)
+
+
+def _layer_call(m, logits=FAKE, x=FAKE, T=1, E=8, k=2, e2s=None, store=None, res=None, od=0, out=FAKE,
+                ids=FAKE, tw=FAKE, ws=FAKE, ws_bytes=1 << 20):
+    st = _store(m, hidden=1024, inter=256) if store is None else store
+    return m.lib().moe_decode_layer(logits, x, T, E, k, e2s, ctypes.byref(st), res, od, out, ids, tw, ws,
+                                    ws_bytes, None)
+
+
+def test_decode_layer_validation():
+    m = _lib()
+    # one token at a fused shape: the routing record plus h in [k][inter] fp32
+    assert m.decode_layer_workspace_bytes(1, 8, 384, 5120, 2304) == 512 + 8 * 2304 * 4
+    assert m.decode_layer_workspace_bytes(1, 2, 8, 1024, 256) == 512 + 2 * 256 * 4
+    # other shapes: offsets, the two pair maps, the permute and h workspaces and y_pair
+    assert m.decode_layer_workspace_bytes(16, 8, 384, 5120, 2304) >= 16 * 8 * (5120 + 2304) * 4
+    assert m.decode_layer_workspace_bytes(1, 2, 8, 256, 128) >= 2 * (256 + 128) * 4
+    assert m.decode_layer_workspace_bytes(0, 2, 8, 256, 128) == 0
+    assert _layer_call(m, logits=None) == m.MOE_ERR_NULL
+    assert _layer_call(m, out=None) == m.MOE_ERR_NULL
+    assert _layer_call(m, ids=None) == m.MOE_ERR_NULL
+    assert _layer_call(m, k=9, E=8) == m.MOE_ERR_SHAPE
+    assert _layer_call(m, k=0) == m.MOE_ERR_SHAPE
+    assert _layer_call(m, E=2000) == m.MOE_ERR_SHAPE
+    assert _layer_call(m, store=_store(m, hidden=1000, inter=256)) == m.MOE_ERR_SHAPE
+    assert _layer_call(m, store=_store(m, num_slots=4, hidden=1024, inter=256)) == m.MOE_ERR_SHAPE
+    assert _layer_call(m, T=300) == m.MOE_ERR_UNSUPPORTED
+    assert _layer_call(m, od=5) == m.MOE_ERR_UNSUPPORTED
+    assert _layer_call(m, x=MIS) == m.MOE_ERR_ALIGN
+    assert _layer_call(m, res=MIS) == m.MOE_ERR_ALIGN
+    assert _layer_call(m, ws=None) == m.MOE_ERR_WORKSPACE
+    assert _layer_call(m, ws_bytes=512) == m.MOE_ERR_WORKSPACE
+    assert _layer_call(m, ws=FAKE + 16) == m.MOE_ERR_ALIGN
+    assert _layer_call(m, T=0, logits=None, x=None, out=None, ids=None, tw=None, ws=None) == m.MOE_OK
