@@ -10,16 +10,19 @@
 // the FP4/FP6 rate.
 //
 //   P0  quant_x:  x bf16 [T][H] -> xq [T][H/32][24 B] + xs [T][H/32]
-//   P1  gateup:   per bucket tile: g = W_gate.x, u = W_up.x (MFMA, fp32),
+//   plan:         bucket offsets -> flat tile lists of both GEMMs
+//   P1  gateup:   per tile: g = W_gate.x, u = W_up.x (MFMA, fp32),
 //                 h = silu(g)*u, h -> MXFP6 into hq/hs (sorted-row order)
-//   P2  down:     per bucket tile: y = W_down.h (MFMA, fp32) -> y_pair row p
+//   P2  down:     per tile: y = W_down.h (MFMA, fp32) -> y_pair row p
 //
-// GEMM tiles are 128 (bucket rows) x 128 (weight rows) with K chunks of 128
-// (four 32-blocks) double-buffered through LDS; four wavefronts each own a
-// 64 x 64 sub-tile as 2 x 2 MFMA 32x32x64 fragments.  Workgroups are
-// persistent: the tile list (bucket, weight tile, row tile -- row tiles of
-// one weight tile adjacent, so they share that weight tile in L2) is split
-// into eight contiguous ranges, one per XCD.
+// A GEMM tile is 128 bucket rows x 256 weight rows over all of K, in chunks of
+// 256 (eight 32-blocks, four MFMA K-steps).  The weights, the large operand,
+// stream from memory straight into the registers of the one wavefront that
+// uses them; the activations are staged once per chunk through LDS and read
+// by all four wavefronts.  Workgroups are persistent: the tile list (bucket,
+// weight tile, row tile -- row tiles of one weight tile adjacent, so they
+// share that weight tile in L2) is split into eight contiguous ranges, one
+// per XCD.
 #include "common.cuh"
 #include "kernels.h"
 
@@ -27,13 +30,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kPT = 256;           // threads per workgroup
-constexpr int BM = 128;            // bucket rows per tile
-constexpr int BK = 128;            // K per chunk (4 blocks)
-constexpr int A_STRIDE = 104;      // LDS bytes per A row: 4 x 24 B blocks + 8 pad
-constexpr int B_STRIDE = 80;       // LDS bytes per B row: 4 x 16 B blocks + 16 pad
-constexpr int H_STRIDE = 65;       // fp32 words per row of the h staging buffer
-constexpr int kGrid = 512;         // persistent workgroups (2 per CU)
+constexpr int kPT = 256;  // threads per workgroup
 
 typedef int i8v __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
@@ -120,270 +117,385 @@ __global__ __launch_bounds__(kPT) void quant_x_kernel(const uint16_t* __restrict
   xs[g] = (uint8_t)sb;
 }
 
-// ---- tile table --------------------------------------------------------------
+// ---- tile plan -----------------------------------------------------------------
+//
+// One small kernel turns the bucket offsets into two flat tile lists, one per
+// GEMM, ordered expert by expert, then by weight tile, then by row tile, so
+// the row tiles that share a weight tile are neighbours (and run at the same
+// time on one XCD, sharing that weight tile in its L2).
 
-struct TileTable {
-  int nb;
-  int total;
-  int expert[kMaxExperts];
-  int row0[kMaxExperts];
-  int cnt[kMaxExperts];
-  int tstart[kMaxExperts + 1];
+constexpr int BM = 128;            // bucket rows per tile
+constexpr int KC = 128;            // K per chunk (4 scale blocks, 2 MFMA K-steps)
+constexpr int GU_N = 128;          // gate/up tile: 128 h columns = 128 gate + 128 up weight rows
+constexpr int DN_N = 256;          // down tile: 256 output columns
+constexpr int STAGE_S = GU_N + 1;  // fp32 words per row of the h staging buffer
+constexpr int kGrid = 512;         // persistent workgroups (2 per CU)
+
+struct TileDesc {
+  int32_t row0;   // first sorted row of the tile
+  int32_t mrows;  // rows in the tile (1..BM)
+  int32_t slot;   // storage slot of the expert, -1 if it has none
+  int32_t ntile;  // weight tile
 };
 
-// Non-empty buckets and the first tile index of each (tiles = ceil(cnt/BM) * ntw).
-__device__ void build_tiles(const int32_t* __restrict__ offsets, int E, int ntw, TileTable& tt) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    constexpr int CH = kMaxExperts / 64;
-    int off[CH + 1];
+__global__ __launch_bounds__(kPT) void plan_kernel(const int32_t* __restrict__ offsets, int E,
+                                                   const int32_t* __restrict__ e2s, int num_slots, int ntw_gu,
+                                                   int ntw_dn, TileDesc* __restrict__ gu, TileDesc* __restrict__ dn,
+                                                   int32_t* __restrict__ counts) {
+  __shared__ int mstart[kMaxExperts + 1];
+  __shared__ int part[kPT / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  constexpr int PER = kMaxExperts / kPT;  // experts per thread
+  int mt[PER];
+  int sum = 0;
 #pragma unroll
-    for (int i = 0; i <= CH; ++i) {
-      const int e = lane * CH + i;
-      off[i] = offsets[e < E ? e : E];
-    }
-    int n = 0, nt = 0;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = (lane * CH + i < E) ? off[i + 1] - off[i] : 0;
-      if (c > 0) {
-        ++n;
-        nt += (c + BM - 1) / BM * ntw;
-      }
-    }
-    int incl = n, tincl = nt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d, 64), ot = __shfl_up(tincl, d, 64);
-      if (lane >= d) {
-        incl += o;
-        tincl += ot;
-      }
-    }
-    int pos = incl - n, tpos = tincl - nt;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int e = lane * CH + i;
-      const int c = (e < E) ? off[i + 1] - off[i] : 0;
-      if (c > 0) {
-        tt.expert[pos] = e;
-        tt.row0[pos] = off[i];
-        tt.cnt[pos] = c;
-        tt.tstart[pos] = tpos;
-        tpos += (c + BM - 1) / BM * ntw;
-        ++pos;
-      }
-    }
-    if (lane == 63) {
-      tt.nb = incl;
-      tt.total = tincl;
-      tt.tstart[incl] = tincl;
-    }
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid * PER + i;
+    const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+    mt[i] = (c + BM - 1) / BM;
+    sum += mt[i];
   }
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) part[wid] = incl;
   __syncthreads();
-}
-
-__device__ __forceinline__ int find_bucket(const TileTable& tt, int t) {
-  int lo = 0, hi = tt.nb - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tt.tstart[mid] <= t) lo = mid; else hi = mid - 1;
+  int base = 0;
+  for (int w = 0; w < wid; ++w) base += part[w];
+  int run = base + incl - sum;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    mstart[tid * PER + i] = run;
+    run += mt[i];
   }
-  return lo;
+  if (tid == kPT - 1) mstart[kMaxExperts] = run;
+  __syncthreads();
+  const int nm = mstart[kMaxExperts];
+  for (int pass = 0; pass < 2; ++pass) {
+    const int ntw = pass ? ntw_dn : ntw_gu;
+    TileDesc* out = pass ? dn : gu;
+    const int total = nm * ntw;
+    for (int t = tid; t < total; t += kPT) {
+      // expert e with mstart[e]*ntw <= t < mstart[e+1]*ntw (empty experts have equal bounds)
+      int lo = 0, hi = kMaxExperts - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (mstart[mid] * ntw <= t) lo = mid; else hi = mid - 1;
+      }
+      const int e = lo;
+      const int mtiles = mstart[e + 1] - mstart[e];
+      const int local = t - mstart[e] * ntw;
+      const int ntile = local / mtiles, mtile = local - ntile * mtiles;
+      const int c = offsets[e + 1] - offsets[e];
+      int slot = e2s ? e2s[e] : e;
+      if (slot >= num_slots) slot = -1;
+      TileDesc d;
+      d.row0 = offsets[e] + mtile * BM;
+      d.mrows = min(BM, c - mtile * BM);
+      d.slot = slot < 0 ? -1 : slot;
+      d.ntile = ntile;
+      out[t] = d;
+    }
+  }
+  if (tid == 0) {
+    counts[0] = nm * ntw_gu;
+    counts[1] = nm * ntw_dn;
+  }
 }
 
 // XCD-aware walk: the tile list is cut into 8 contiguous ranges, and the
-// workgroups on XCD x (blockIdx.x % 8 == x) take range x.
+// workgroups on XCD x (blockIdx.x % 8 == x) take range x in turn.
 struct TileWalk {
   int next, end, step;
   __device__ TileWalk(int total) {
     const int xcd = blockIdx.x & 7, per = gridDim.x >> 3;
-    const int lo = (int)((long)total * xcd / 8), hi = (int)((long)total * (xcd + 1) / 8);
-    next = lo + (int)(blockIdx.x >> 3);
-    end = hi;
+    next = (int)((long)total * xcd / 8) + (int)(blockIdx.x >> 3);
+    end = (int)((long)total * (xcd + 1) / 8);
     step = per;
   }
 };
 
-// ---- LDS buffers of the GEMMs -------------------------------------------------
+// ---- buffer-resource loads ---------------------------------------------------------
+//
+// A wave-uniform base and byte range; an offset past the range reads zeros.
+// Rows beyond a bucket's end get such an offset, so every load of the K loop
+// is issued unconditionally and the compiler can count the loads in flight
+// exactly (a load behind a branch makes it wait for all of them).
 
-struct GemmBuf {
-  uint8_t a[BM * A_STRIDE];
-  uint8_t b[128 * B_STRIDE];
-  uint32_t as[BM];
-  uint32_t bs[128];
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw 32-bit access, range-checked
+constexpr uint32_t kOob = 0x80000000u;         // an offset past every range used here
+constexpr uint32_t kOpenRange = 0x7FFFFFF0u;   // range of the activation buffers (offsets < 2^31)
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), (int)kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4_t bload16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// ---- the grouped GEMM core ---------------------------------------------------------
+//
+// A workgroup computes a tile of BM bucket rows x 256 weight rows over all of
+// K, in chunks of 128 (four 32-blocks, two MFMA 32x32x64 K-steps).  Each
+// wavefront owns 64 weight rows (two 32-row B fragments) and all BM rows (four
+// A fragments): 8 MFMAs per K-step.  The weight rows are not shared between
+// wavefronts, so they go straight from memory into the wavefront's registers
+// in MFMA order, one chunk ahead.  The MXFP6 activations are shared: staged
+// once per chunk through LDS (double-buffered, one barrier per chunk).  Two
+// workgroups share a CU, so one's loads, barriers and epilogue overlap the
+// other's MFMAs.
+//
+// LDS layout of one A chunk: for each K-half h a region of BM rows x 48 B --
+// blocks h and 2+h of the chunk, i.e. the lane's A operand for K-steps 0 and 1
+// -- read as three 16-B loads per lane (lanes 48 B apart touch every bank
+// once); then one scale word (4 bytes) per row.
+
+constexpr int A_HS = BM * 48 + 64;  // LDS bytes per K-half region of an A chunk
+
+struct ABuf {
+  uint8_t codes[2 * A_HS];
+  uint32_t scales[2 * BM];  // rows 0..BM-1; the upper half takes the stores of threads tid >= BM
+  uint2 spill[64];          // the stores of lanes that carry no codes
 };
 
 struct GemmSmem {
   union {
-    GemmBuf buf[2];
-    float hbuf[BM * H_STRIDE];
+    ABuf a[2];
+    float stage[BM * STAGE_S];
   };
   int rowtok[BM];
 };
 
-// Registers holding one K chunk between its global loads and its LDS store.
-struct ChunkRegs {
-  uint4 a[3];   // 48 B: two 24-B blocks of one A row
-  uint4 b[2];   // 32 B: two 16-B blocks of one B row
-  uint32_t s;   // four scale bytes of one A row (tid < 128) or one B row (tid >= 128)
+// Registers of one A chunk between its global loads and its LDS store.  The
+// loads are row-contiguous: 8 lanes per row, 6 of them carrying its 96 B of
+// codes (lane p: bytes 16p..16p+15), 8 rows per wavefront load.  Threads
+// tid < BM also load the scale word of row tid.
+struct ARegs {
+  uint4_t q[BM / 32];  // rows 32w + 8i + lane/8, i = 0..3
+  uint32_t s;
 };
 
-__device__ __forceinline__ void store_chunk(GemmBuf& d, const ChunkRegs& r, int tid) {
-  const int row = tid >> 1, part = tid & 1;
-  uint2* pa = reinterpret_cast<uint2*>(d.a + row * A_STRIDE + part * 48);
-  pa[0] = make_uint2(r.a[0].x, r.a[0].y);
-  pa[1] = make_uint2(r.a[0].z, r.a[0].w);
-  pa[2] = make_uint2(r.a[1].x, r.a[1].y);
-  pa[3] = make_uint2(r.a[1].z, r.a[1].w);
-  pa[4] = make_uint2(r.a[2].x, r.a[2].y);
-  pa[5] = make_uint2(r.a[2].z, r.a[2].w);
-  uint4* pb = reinterpret_cast<uint4*>(d.b + row * B_STRIDE + part * 32);
-  pb[0] = r.b[0];
-  pb[1] = r.b[1];
-  if (tid < 128) d.as[tid] = r.s; else d.bs[tid - 128] = r.s;
+struct ASrc {
+  rsrc_t rc, rs;
+  uint32_t vc[BM / 32];  // row offsets + 16p (kOob for rows past the bucket and for lanes p >= 6)
+  uint32_t vs;           // scale offset of row tid (kOob past the bucket, or for tid >= BM)
+  __device__ __forceinline__ void load(int c, ARegs& r) const {
+#pragma unroll
+    for (int i = 0; i < BM / 32; ++i) r.q[i] = bload16(rc, vc[i] + (uint32_t)c * 96u);
+    r.s = bload4(rs, vs + (uint32_t)c * 4u);
+  }
+};
+
+// Every thread stores unconditionally (lanes without codes into d.spill,
+// threads tid >= BM into the upper scale half), so no store of the K loop sits
+// behind a branch.
+__device__ __forceinline__ void store_a(ABuf& d, const ARegs& r, int tid) {
+  const int lane = tid & 63, p = lane & 7;
+  const bool codes = p < 6;
+  // 8-byte units U = 2p, 2p+1 of the row's 96 B: part U%3 of block b = U/3,
+  // which goes to K-half b&1 at offset (b>>1)*24 + (U%3)*8
+  int o[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int U = 2 * p + k, b = U / 3;
+    o[k] = (b & 1) * A_HS + (b >> 1) * 24 + (U % 3) * 8;
+  }
+  uint8_t* const sp = reinterpret_cast<uint8_t*>(d.spill) + 8 * lane;
+#pragma unroll
+  for (int i = 0; i < BM / 32; ++i) {
+    const int row = 32 * (tid >> 6) + 8 * i + (lane >> 3);
+    uint8_t* d0 = codes ? d.codes + o[0] + row * 48 : sp;
+    uint8_t* d1 = codes ? d.codes + o[1] + row * 48 : sp;
+    *reinterpret_cast<uint2*>(d0) = make_uint2(r.q[i].x, r.q[i].y);
+    *reinterpret_cast<uint2*>(d1) = make_uint2(r.q[i].z, r.q[i].w);
+  }
+  d.scales[tid] = r.s;
 }
 
-// 2 x 2 MFMA fragments of one wavefront over one K chunk: A fragments at LDS
-// rows arow0 + 32f, B fragments at rows brow0 + bstep*g.
-__device__ __forceinline__ void mma_chunk(const GemmBuf& d, f16v (&acc)[2][2], int arow0, int brow0, int bstep,
-                                          int lane) {
-  const int r32 = lane & 31, h = lane >> 5;
+// Row offsets of this thread's A loads; row_off(r) gives the byte offset of
+// bucket row r's codes (or kOob when the row is past the bucket's end).
+template <typename RowOff>
+__device__ __forceinline__ void a_offsets(ASrc& as, int tid, RowOff row_off) {
+  const int lane = tid & 63, p = lane & 7;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int blk = 2 * s + h;
-    i8v a[2], b[2];
-    int sa[2], sb[2];
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int row = arow0 + 32 * f + r32;
-      const uint2* p = reinterpret_cast<const uint2*>(d.a + row * A_STRIDE + blk * 24);
-      const uint2 q0 = p[0], q1 = p[1], q2 = p[2];
-      a[f] = i8v{(int)q0.x, (int)q0.y, (int)q1.x, (int)q1.y, (int)q2.x, (int)q2.y, 0, 0};
-      sa[f] = (int)((d.as[row] >> (8 * blk)) & 0xFFu);
-    }
+  for (int i = 0; i < BM / 32; ++i) {
+    const uint32_t o = row_off(32 * (tid >> 6) + 8 * i + (lane >> 3));
+    as.vc[i] = (p < 6 && o != kOob) ? o + 16u * p : kOob;
+  }
+}
+
+// One wavefront's B operand for one chunk, loaded in MFMA order: lane l holds
+// row l%32 of fragment g, block 2s + l/32 (K-step s); plus the row's scale
+// word (blocks 0..3 of the chunk).
+struct BRegs {
+  uint4_t q[2][2];  // [fragment][K-step]
+  uint32_t s[2];
+};
+
+struct BSrc {
+  rsrc_t rc[2], rs[2];  // codes and scales of fragment 0 and 1
+  uint32_t vc[2], vs[2];  // this lane's row offsets (codes: + 16 * K-half)
+  __device__ __forceinline__ void load(int c, BRegs& r) const {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const int row = brow0 + bstep * g + r32;
-      const uint4 q = *reinterpret_cast<const uint4*>(d.b + row * B_STRIDE + blk * 16);
-      b[g] = i8v{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-      sb[g] = (int)((d.bs[row] >> (8 * blk)) & 0xFFu);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) r.q[g][s] = bload16(rc[g], vc[g] + (uint32_t)c * 64u + 32u * s);
+      r.s[g] = bload4(rs[g], vs[g] + (uint32_t)c * 4u);
     }
+  }
+};
+
+// One chunk of MFMAs: A fragments from LDS (48 B per lane = both K-steps),
+// B from registers.  With an empty chunk (nks == 0) nothing is multiplied.
+__device__ __forceinline__ void mma_chunk(const ABuf& cur, const BRegs& b, f16v (&acc)[4][2], int nks, int lane) {
+  const int r32 = lane & 31, h = lane >> 5;
+  if (nks == 0) return;
+  uint4_t av[4][3];
+  uint32_t asw[4];
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < 4; ++f) {
+    const uint4_t* p = reinterpret_cast<const uint4_t*>(cur.codes + h * A_HS + (32 * f + r32) * 48);
+    av[f][0] = p[0];
+    av[f][1] = p[1];
+    av[f][2] = p[2];
+    asw[f] = cur.scales[32 * f + r32] >> (8 * h);
+  }
+  uint32_t bsw[2];
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
-        acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[f], b[g], acc[f][g], 2, 4, 0, sa[f], 0,
-                                                                    sb[g]);
+  for (int g = 0; g < 2; ++g) bsw[g] = b.s[g] >> (8 * h);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      // dwords 6s..6s+5 of the lane's 48 B are its block at K-step s
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(av[f]) + 6 * s;
+      const i8v a = i8v{(int)w[0], (int)w[1], (int)w[2], (int)w[3], (int)w[4], (int)w[5], 0, 0};
+      const int sa = (int)(asw[f] >> (16 * s));  // low byte: block 2s+h
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const uint4_t q = b.q[g][s];
+        const i8v bb = i8v{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+        const int sb = (int)(bsw[g] >> (16 * s));
+        acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bb, acc[f][g], 2, 4, 0, sa, 0, sb);
+      }
+    }
   }
 }
 
-// The K loop: two LDS buffers and a ring of three register sets, so the
-// global loads of chunk c+3 are in flight while chunk c is multiplied and
-// chunk c+1 is moved into LDS.
-template <typename Load>
-__device__ __forceinline__ void k_loop(GemmSmem& sm, f16v (&acc)[2][2], Load& load, int nchunks, int tid, int lane,
-                                       int arow0, int brow0, int bstep) {
-  ChunkRegs r0, r1, r2;
-  load(0, r0);
-  if (nchunks > 1) load(1, r1);
-  if (nchunks > 2) load(2, r2);
-  store_chunk(sm.buf[0], r0, tid);
+// The K loop over all chunks of one tile.  The A chunk c+1 is loaded during
+// chunk c-1 and stored to LDS at the end of chunk c; the B registers of chunk
+// c+1 are loaded at the start of chunk c.  Chunks run in pairs (the B register
+// sets alternate); with an odd chunk count the last step multiplies nothing.
+// Loads past the last chunk re-read it, and stores past it write a stage that
+// nothing reads again, so no load or store of the loop sits behind a branch.
+__device__ __forceinline__ void gemm_k_loop(GemmSmem& sm, f16v (&acc)[4][2], const ASrc& as, const BSrc& bs,
+                                            int K, int tid, int lane) {
+  const int nchunks = K / KC, last = nchunks - 1;
+  ARegs an;
+  BRegs b0, b1;
+  as.load(0, an);
+  bs.load(0, b0);
+  store_a(sm.a[0], an, tid);
+  as.load(min(1, last), an);
   __syncthreads();
-  auto step = [&](int c, ChunkRegs& next, ChunkRegs& spare) {
-    if (c + 3 < nchunks) load(c + 3, spare);
-    mma_chunk(sm.buf[c & 1], acc, arow0, brow0, bstep, lane);
-    if (c + 1 < nchunks) store_chunk(sm.buf[(c + 1) & 1], next, tid);
+  auto step = [&](int c, const BRegs& cur, BRegs& nxt) {
+    bs.load(min(c + 1, last), nxt);
+    mma_chunk(sm.a[c & 1], cur, acc, c > last ? 0 : 2, lane);
+    store_a(sm.a[(c + 1) & 1], an, tid);
+    as.load(min(c + 2, last), an);
     __syncthreads();
   };
-  for (int c = 0; c < nchunks; c += 3) {
-    step(c, r1, r0);
-    if (c + 1 < nchunks) step(c + 1, r2, r1);
-    if (c + 2 < nchunks) step(c + 2, r0, r2);
+  for (int c = 0; c < nchunks; c += 2) {
+    step(c, b0, b1);
+    step(c + 1, b1, b0);
   }
 }
 
-// ---- P1: gate/up GEMM, SwiGLU and MXFP6 of h ----------------------------------
+// ---- P1: gate/up GEMM, SwiGLU and MXFP6 of h -----------------------------------------
+//
+// Wavefront w's fragments are gate rows j0+32w.. and the up rows with the same
+// index, so h = silu(g)*u is formed in its registers; its 32 h columns are
+// exactly one MXFP6 block per row.
 
 __global__ __launch_bounds__(kPT, 2) void gateup_mfma_kernel(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int k, int E, ExpertStore w,
-    const int32_t* __restrict__ e2s, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair,
-    uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
-  __shared__ TileTable tt;
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, uint32_t xq_bytes, uint32_t xs_bytes, int k,
+    ExpertStore w, const int32_t* __restrict__ sorted_pair, const TileDesc* __restrict__ tiles,
+    const int32_t* __restrict__ counts, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
   __shared__ GemmSmem sm;
   const int H = w.H, I = w.I, NBH = H / 32, NBI = I / 32;
-  const int ntw = I / 64;  // weight tiles: 64 gate rows + the same 64 up rows
-  build_tiles(offsets, E, ntw, tt);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, wm = wid >> 1, wn = wid & 1;
-  const size_t arow_bytes = (size_t)NBH * 24, wrow_bytes = (size_t)H / 2;
-  const int nchunks = H / BK;
-  for (TileWalk tw(tt.total); tw.next < tw.end; tw.next += tw.step) {
-    const int t = tw.next;
-    const int b = find_bucket(tt, t);
-    const int expert = tt.expert[b], row0 = tt.row0[b], cnt = tt.cnt[b];
-    const int mtiles = (cnt + BM - 1) / BM, local = t - tt.tstart[b];
-    const int ntile = local / mtiles, mtile = local - ntile * mtiles;
-    const int slot = e2s ? e2s[expert] : expert;
-    if (slot < 0 || slot >= w.num_slots) continue;  // the down GEMM writes zero rows
-    const int m0 = mtile * BM, n0 = ntile * 64;
-    const int mrows = min(BM, cnt - m0);
-    if (tid < BM) sm.rowtok[tid] = tid < mrows ? sorted_pair[row0 + m0 + tid] / k : -1;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
+  const uint32_t arow = (uint32_t)NBH * 24u, wrow = (uint32_t)H / 2u;
+  const size_t mat = (size_t)I * wrow, smat = (size_t)I * NBH;
+  const int total = counts[0];
+  for (TileWalk tw(total); tw.next < tw.end; tw.next += tw.step) {
+    const TileDesc d = tiles[tw.next];
+    if (d.slot < 0) continue;  // no stored expert: the down GEMM writes its rows as zeros
+    __syncthreads();           // the previous tile's epilogue is done with the LDS
+    if (tid < BM) sm.rowtok[tid] = tid < d.mrows ? sorted_pair[d.row0 + tid] / k : -1;
     __syncthreads();
-    // this thread's load sources
-    const int lrow = tid >> 1, part = tid & 1;
-    const int tok = sm.rowtok[lrow];
-    const uint8_t* asrc = tok >= 0 ? xq + (size_t)tok * arow_bytes + part * 48 : nullptr;
-    const int wmat = lrow >> 6, wn_row = n0 + (lrow & 63);
-    const uint8_t* bsrc = (wmat ? w.wu : w.wg) + ((size_t)slot * I + wn_row) * wrow_bytes + part * 32;
-    const uint8_t* ssrc;
-    if (tid < BM) {
-      const int st = sm.rowtok[tid];
-      ssrc = st >= 0 ? xs + (size_t)st * NBH : nullptr;
-    } else {
-      const int r = tid - BM;
-      ssrc = (r >> 6 ? w.su : w.sg) + ((size_t)slot * I + n0 + (r & 63)) * NBH;
+    const int j0 = d.ntile * GU_N;
+    ASrc as;
+    as.rc = make_rsrc(xq, xq_bytes);
+    as.rs = make_rsrc(xs, xs_bytes);
+    a_offsets(as, tid, [&](int r) {
+      const int tok = sm.rowtok[r];
+      return tok >= 0 ? (uint32_t)tok * arow : kOob;
+    });
+    {
+      const int tok = tid < BM ? sm.rowtok[tid] : -1;
+      as.vs = tok >= 0 ? (uint32_t)tok * NBH : kOob;
     }
-    auto load = [&](int c, ChunkRegs& r) {
-      if (asrc) {
-        const uint4* p = reinterpret_cast<const uint4*>(asrc + (size_t)c * 96);
-        r.a[0] = p[0];
-        r.a[1] = p[1];
-        r.a[2] = p[2];
-      } else {
-        r.a[0] = r.a[1] = r.a[2] = make_uint4(0, 0, 0, 0);
-      }
-      const uint4* q = reinterpret_cast<const uint4*>(bsrc + (size_t)c * 64);
-      r.b[0] = q[0];
-      r.b[1] = q[1];
-      r.s = ssrc ? *reinterpret_cast<const uint32_t*>(ssrc + c * 4) : 0x7F7F7F7Fu;
-    };
-    f16v acc[2][2];
+    BSrc bs;
+    {
+      // wavefront wid: gate rows j0+32*wid.. (fragment 0) and the same up rows (fragment 1)
+      const uint32_t jr = (uint32_t)(j0 + 32 * wid + r32);
+      bs.rc[0] = make_rsrc(w.wg + (size_t)d.slot * mat, (uint32_t)mat);
+      bs.rc[1] = make_rsrc(w.wu + (size_t)d.slot * mat, (uint32_t)mat);
+      bs.rs[0] = make_rsrc(w.sg + (size_t)d.slot * smat, (uint32_t)smat);
+      bs.rs[1] = make_rsrc(w.su + (size_t)d.slot * smat, (uint32_t)smat);
+      bs.vc[0] = bs.vc[1] = jr * wrow + 16u * h;
+      bs.vs[0] = bs.vs[1] = jr * NBH;
+    }
+    f16v acc[4][2];
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int g = 0; g < 2; ++g) acc[f][g] = f16v{};
-    k_loop(sm, acc, load, nchunks, tid, lane, 64 * wm, 32 * wn, 64);  // B: gate rows 32wn.., up 64+32wn..
-    // h = silu(g) * u into the staging buffer, then MXFP6 per (row, 32-block)
+    gemm_k_loop(sm, acc, as, bs, H, tid, lane);
+    // h = silu(g) * u into the staging buffer (the K loop ended on a barrier)
+    const int wcol = 32 * wid + r32;
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int row = 64 * wm + 32 * f + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-        const int col = 32 * wn + (lane & 31);
-        sm.hbuf[row * H_STRIDE + col] = swiglu_f32(acc[f][0][i], acc[f][1][i]);
+        const int row = 32 * f + (i >> 2) * 8 + h * 4 + (i & 3);
+        sm.stage[row * STAGE_S + wcol] = swiglu_f32(acc[f][0][i], acc[f][1][i]);
       }
-    }
     __syncthreads();
-    {
-      const int row = tid >> 1, blk = tid & 1;
-      if (row < mrows) {
+    // MXFP6 of each (row, 32-block) of the tile, written in sorted-row order
+    for (int item = tid; item < BM * (GU_N / 32); item += kPT) {
+      const int row = item % BM, blk = item / BM;
+      if (row < d.mrows) {
         float v[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = sm.hbuf[row * H_STRIDE + 32 * blk + i];
+        for (int i = 0; i < 32; ++i) v[i] = sm.stage[row * STAGE_S + 32 * blk + i];
         uint32_t pk[6], sb;
         q6_block(v, pk, sb);
-        const size_t grow = (size_t)(row0 + m0 + row);
-        const int gblk = n0 / 32 + blk;
+        const size_t grow = (size_t)(d.row0 + row);
+        const int gblk = j0 / 32 + blk;
         uint2* dst = reinterpret_cast<uint2*>(hq + grow * NBI * 24 + (size_t)gblk * 24);
         dst[0] = make_uint2(pk[0], pk[1]);
         dst[1] = make_uint2(pk[2], pk[3]);
@@ -391,120 +503,122 @@ __global__ __launch_bounds__(kPT, 2) void gateup_mfma_kernel(
         hs[grow * NBI + gblk] = (uint8_t)sb;
       }
     }
-    __syncthreads();
   }
 }
 
-// ---- P2: down GEMM -> y_pair ---------------------------------------------------
+// ---- P2: down GEMM -> y_pair ---------------------------------------------------------
 
 __global__ __launch_bounds__(kPT, 2) void down_mfma_kernel(
-    const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, int E, ExpertStore w,
-    const int32_t* __restrict__ e2s, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair,
-    float* __restrict__ y) {
-  __shared__ TileTable tt;
+    const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, uint32_t hq_bytes, uint32_t hs_bytes,
+    ExpertStore w, const int32_t* __restrict__ sorted_pair, const TileDesc* __restrict__ tiles,
+    const int32_t* __restrict__ counts, float* __restrict__ y) {
   __shared__ GemmSmem sm;
   const int H = w.H, I = w.I, NBI = I / 32;
-  const int ntw = H / 128;
-  build_tiles(offsets, E, ntw, tt);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, wm = wid >> 1, wn = wid & 1;
-  const size_t arow_bytes = (size_t)NBI * 24, wrow_bytes = (size_t)I / 2;
-  const int nchunks = I / BK;
-  for (TileWalk tw(tt.total); tw.next < tw.end; tw.next += tw.step) {
-    const int t = tw.next;
-    const int b = find_bucket(tt, t);
-    const int expert = tt.expert[b], row0 = tt.row0[b], cnt = tt.cnt[b];
-    const int mtiles = (cnt + BM - 1) / BM, local = t - tt.tstart[b];
-    const int ntile = local / mtiles, mtile = local - ntile * mtiles;
-    const int slot = e2s ? e2s[expert] : expert;
-    const int m0 = mtile * BM, n0 = ntile * 128;
-    const int mrows = min(BM, cnt - m0);
-    if (tid < BM) sm.rowtok[tid] = tid < mrows ? sorted_pair[row0 + m0 + tid] : -1;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
+  const uint32_t arow = (uint32_t)NBI * 24u, wrow = (uint32_t)I / 2u;
+  const size_t mat = (size_t)H * wrow, smat = (size_t)H * NBI;
+  const int total = counts[1];
+  for (TileWalk tw(total); tw.next < tw.end; tw.next += tw.step) {
+    const TileDesc d = tiles[tw.next];
     __syncthreads();
-    if (slot < 0 || slot >= w.num_slots) {
-      for (int i = tid; i < mrows * 128; i += kPT) {
-        const int row = i >> 7, col = i & 127;
+    if (tid < BM) sm.rowtok[tid] = tid < d.mrows ? sorted_pair[d.row0 + tid] : -1;
+    __syncthreads();
+    const int n0 = d.ntile * DN_N;
+    if (d.slot < 0) {
+      for (int i = tid; i < d.mrows * DN_N; i += kPT) {
+        const int row = i / DN_N, col = i % DN_N;
         y[(size_t)sm.rowtok[row] * H + n0 + col] = 0.f;
       }
-      __syncthreads();
       continue;
     }
-    const int lrow = tid >> 1, part = tid & 1;
-    const uint8_t* asrc = lrow < mrows ? hq + (size_t)(row0 + m0 + lrow) * arow_bytes + part * 48 : nullptr;
-    const uint8_t* bsrc = w.wd + ((size_t)slot * H + n0 + lrow) * wrow_bytes + part * 32;
-    const uint8_t* ssrc;
-    if (tid < BM)
-      ssrc = tid < mrows ? hs + (size_t)(row0 + m0 + tid) * NBI : nullptr;
-    else
-      ssrc = w.sd + ((size_t)slot * H + n0 + (tid - BM)) * NBI;
-    auto load = [&](int c, ChunkRegs& r) {
-      if (asrc) {
-        const uint4* p = reinterpret_cast<const uint4*>(asrc + (size_t)c * 96);
-        r.a[0] = p[0];
-        r.a[1] = p[1];
-        r.a[2] = p[2];
-      } else {
-        r.a[0] = r.a[1] = r.a[2] = make_uint4(0, 0, 0, 0);
-      }
-      const uint4* q = reinterpret_cast<const uint4*>(bsrc + (size_t)c * 64);
-      r.b[0] = q[0];
-      r.b[1] = q[1];
-      r.s = ssrc ? *reinterpret_cast<const uint32_t*>(ssrc + c * 4) : 0x7F7F7F7Fu;
-    };
-    f16v acc[2][2];
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int g = 0; g < 2; ++g) acc[f][g] = f16v{};
-    k_loop(sm, acc, load, nchunks, tid, lane, 64 * wm, 64 * wn, 32);
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    ASrc as;
+    as.rc = make_rsrc(hq, hq_bytes);
+    as.rs = make_rsrc(hs, hs_bytes);
+    a_offsets(as, tid, [&](int r) { return r < d.mrows ? (uint32_t)(d.row0 + r) * arow : kOob; });
+    as.vs = tid < d.mrows ? (uint32_t)(d.row0 + tid) * NBI : kOob;
+    BSrc bs;
+    {
+      // wavefront wid: output rows n0+64*wid+32g.. (fragment g)
+      const rsrc_t rc = make_rsrc(w.wd + (size_t)d.slot * mat, (uint32_t)mat);
+      const rsrc_t rs = make_rsrc(w.sd + (size_t)d.slot * smat, (uint32_t)smat);
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
+        const uint32_t nr = (uint32_t)(n0 + 64 * wid + 32 * g + r32);
+        bs.rc[g] = rc;
+        bs.rs[g] = rs;
+        bs.vc[g] = nr * wrow + 16u * h;
+        bs.vs[g] = nr * NBI;
+      }
+    }
+    f16v acc[4][2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = 64 * wm + 32 * f + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-          if (row < mrows) {
-            const int col = n0 + 64 * wn + 32 * g + (lane & 31);
-            y[(size_t)sm.rowtok[row] * H + col] = acc[f][g][i];
-          }
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) acc[f][g] = f16v{};
+    gemm_k_loop(sm, acc, as, bs, I, tid, lane);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      __builtin_amdgcn_sched_barrier(0);  // one fragment's stores at a time (register pressure)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 32 * f + (i >> 2) * 8 + h * 4 + (i & 3);
+        if (row < d.mrows) {
+          float* yr = y + (size_t)sm.rowtok[row] * H + n0 + 64 * wid + r32;
+          yr[0] = acc[f][0][i];
+          yr[32] = acc[f][1][i];
         }
       }
     }
-    __syncthreads();
   }
 }
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Upper bound of the row tiles of a call: one ragged tile per non-empty bucket.
+size_t max_mtiles(size_t P) { return (P + BM - 1) / BM + (P < (size_t)kMaxExperts ? P : (size_t)kMaxExperts); }
+
 }  // namespace
 
 size_t prefill_workspace_bytes(int T, int k, int H, int I) {
-  const size_t P = (size_t)T * k;
+  const size_t P = (size_t)T * k, nm = max_mtiles(P);
   return align256((size_t)T * H / 32 * 24) + align256((size_t)T * H / 32) + align256(P * I / 32 * 24) +
-         align256(P * I / 32);
+         align256(P * I / 32) + align256(nm * (I / GU_N) * sizeof(TileDesc)) +
+         align256(nm * (H / DN_N) * sizeof(TileDesc)) + 256;
 }
 
 hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertStore& w, const int32_t* e2s,
                           const int32_t* offsets, const int32_t* sorted_pair, float* y_pair, void* ws,
                           hipStream_t s) {
   const int H = w.H, I = w.I;
-  if (H % 128 != 0 || I % 128 != 0) return hipErrorInvalidValue;
-  const size_t P = (size_t)T * k;
+  if (H % DN_N != 0 || I % GU_N != 0) return hipErrorInvalidValue;
+  const size_t P = (size_t)T * k, nm = max_mtiles(P);
+  const size_t xq_b = (size_t)T * H / 32 * 24, xs_b = (size_t)T * H / 32;
+  const size_t hq_b = P * I / 32 * 24, hs_b = P * I / 32;
+  if (xq_b >= kOob || hq_b >= kOob) return hipErrorInvalidValue;
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   uint8_t* xq = base;
-  uint8_t* xs = xq + align256((size_t)T * H / 32 * 24);
-  uint8_t* hq = xs + align256((size_t)T * H / 32);
-  uint8_t* hs = hq + align256(P * I / 32 * 24);
+  uint8_t* xs = xq + align256(xq_b);
+  uint8_t* hq = xs + align256(xs_b);
+  uint8_t* hs = hq + align256(hq_b);
+  TileDesc* gu = reinterpret_cast<TileDesc*>(hs + align256(hs_b));
+  TileDesc* dn = reinterpret_cast<TileDesc*>(reinterpret_cast<uint8_t*>(gu) +
+                                             align256(nm * (I / GU_N) * sizeof(TileDesc)));
+  int32_t* counts = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(dn) +
+                                               align256(nm * (H / DN_N) * sizeof(TileDesc)));
   const int nblk = T * (H / 32);
   hipLaunchKernelGGL(quant_x_kernel, dim3((nblk + kPT - 1) / kPT), dim3(kPT), 0, s, x, nblk, xq, xs);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(gateup_mfma_kernel, dim3(kGrid), dim3(kPT), 0, s, xq, xs, k, E, w, e2s, offsets, sorted_pair,
-                     hq, hs);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPT), 0, s, offsets, E, e2s, w.num_slots, I / GU_N, H / DN_N, gu,
+                     dn, counts);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(down_mfma_kernel, dim3(kGrid), dim3(kPT), 0, s, hq, hs, E, w, e2s, offsets, sorted_pair,
-                     y_pair);
+  hipLaunchKernelGGL(gateup_mfma_kernel, dim3(kGrid), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, k, w,
+                     sorted_pair, gu, counts, hq, hs);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(down_mfma_kernel, dim3(kGrid), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, w,
+                     sorted_pair, dn, counts, y_pair);
   return hipGetLastError();
 }
 
