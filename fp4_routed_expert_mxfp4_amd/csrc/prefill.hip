@@ -131,6 +131,15 @@ constexpr int DN_N = 256;          // down tile: 256 output columns
 constexpr int STAGE_S = GU_N + 1;  // fp32 words per row of the h staging buffer
 constexpr int kGrid = 512;         // persistent workgroups (2 per CU)
 
+constexpr int SK_MAX = 32;  // buckets with at most this many rows take the streaming kernels
+
+struct SkBucket {
+  int32_t row0;  // first sorted row
+  int32_t cnt;   // rows (1..SK_MAX)
+  int32_t slot;  // storage slot of the expert, -1 if it has none
+  int32_t pad;
+};
+
 struct TileDesc {
   int32_t row0;   // first sorted row of the tile
   int32_t mrows;  // rows in the tile (1..BM)
@@ -138,48 +147,73 @@ struct TileDesc {
   int32_t ntile;  // weight tile
 };
 
-__global__ __launch_bounds__(kPT) void plan_kernel(const int32_t* __restrict__ offsets, int E,
-                                                   const int32_t* __restrict__ e2s, int num_slots, int ntw_gu,
-                                                   int ntw_dn, TileDesc* __restrict__ gu, TileDesc* __restrict__ dn,
-                                                   int32_t* __restrict__ counts) {
-  __shared__ int mstart[kMaxExperts + 1];
-  __shared__ int part[kPT / 64];
+// Exclusive prefix sum over the workgroup of one value per thread; *total gets the sum.
+__device__ int block_exclusive_sum(int v, int* part, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  constexpr int PER = kMaxExperts / kPT;  // experts per thread
-  int mt[PER];
-  int sum = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = tid * PER + i;
-    const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-    mt[i] = (c + BM - 1) / BM;
-    sum += mt[i];
-  }
-  int incl = sum;
+  int incl = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int o = __shfl_up(incl, d, 64);
     if (lane >= d) incl += o;
   }
+  __syncthreads();
   if (lane == 63) part[wid] = incl;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wid; ++w) base += part[w];
-  int run = base + incl - sum;
+  int base = 0, sum = 0;
+  for (int w = 0; w < kPT / 64; ++w) {
+    if (w < wid) base += part[w];
+    sum += part[w];
+  }
+  *total = sum;
+  return base + incl - v;
+}
+
+__global__ __launch_bounds__(kPT) void plan_kernel(const int32_t* __restrict__ offsets, int E,
+                                                   const int32_t* __restrict__ e2s, int num_slots, int ntw_gu,
+                                                   int ntw_dn, TileDesc* __restrict__ gu, TileDesc* __restrict__ dn,
+                                                   SkBucket* __restrict__ sbk, int32_t* __restrict__ counts) {
+  __shared__ int mstart[kMaxExperts + 1];
+  __shared__ int part[kPT / 64];
+  const int tid = threadIdx.x;
+  constexpr int PER = kMaxExperts / kPT;  // experts per thread
+  int mt[PER], small[PER];
+  int msum = 0, ssum = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    mstart[tid * PER + i] = run;
-    run += mt[i];
+    const int e = tid * PER + i;
+    const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+    small[i] = (c >= 1 && c <= SK_MAX) ? 1 : 0;
+    mt[i] = small[i] ? 0 : (c + BM - 1) / BM;
+    msum += mt[i];
+    ssum += small[i];
   }
-  if (tid == kPT - 1) mstart[kMaxExperts] = run;
+  int nm, ns;
+  int mrun = block_exclusive_sum(msum, part, &nm);
+  int srun = block_exclusive_sum(ssum, part, &ns);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid * PER + i;
+    mstart[e] = mrun;
+    mrun += mt[i];
+    if (small[i]) {
+      int slot = e2s ? e2s[e] : e;
+      if (slot >= num_slots) slot = -1;
+      SkBucket b;
+      b.row0 = offsets[e];
+      b.cnt = offsets[e + 1] - offsets[e];
+      b.slot = slot < 0 ? -1 : slot;
+      b.pad = 0;
+      sbk[srun++] = b;
+    }
+  }
+  if (tid == kPT - 1) mstart[kMaxExperts] = mrun;
   __syncthreads();
-  const int nm = mstart[kMaxExperts];
   for (int pass = 0; pass < 2; ++pass) {
     const int ntw = pass ? ntw_dn : ntw_gu;
     TileDesc* out = pass ? dn : gu;
     const int total = nm * ntw;
     for (int t = tid; t < total; t += kPT) {
-      // expert e with mstart[e]*ntw <= t < mstart[e+1]*ntw (empty experts have equal bounds)
+      // expert e with mstart[e]*ntw <= t < mstart[e+1]*ntw (experts without row tiles have equal bounds)
       int lo = 0, hi = kMaxExperts - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -203,6 +237,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(const int32_t* __restrict__ o
   if (tid == 0) {
     counts[0] = nm * ntw_gu;
     counts[1] = nm * ntw_dn;
+    counts[2] = ns;
   }
 }
 
@@ -337,26 +372,47 @@ __device__ __forceinline__ void a_offsets(ASrc& as, int tid, RowOff row_off) {
   }
 }
 
-// One wavefront's B operand for one chunk, loaded in MFMA order: lane l holds
-// row l%32 of fragment g, block 2s + l/32 (K-step s); plus the row's scale
-// word (blocks 0..3 of the chunk).
+// One wavefront's B operand for one chunk.  Each fragment's 32 rows are
+// loaded as two halves of 16 rows x 64 contiguous bytes (lane l: row 16j +
+// l%16, block l/16 of the chunk), which touches half the cache lines of the
+// MFMA order (32 rows x 32 B); b_operands() moves them into MFMA order with two
+// lane swaps per dword when they are used.  Plus the row's scale word (blocks
+// 0..3 of the chunk) in MFMA order (lane l: row l%32).
 struct BRegs {
-  uint4_t q[2][2];  // [fragment][K-step]
+  uint4_t q[2][2];  // [fragment][row half], as loaded
   uint32_t s[2];
 };
 
 struct BSrc {
-  rsrc_t rc[2], rs[2];  // codes and scales of fragment 0 and 1
-  uint32_t vc[2], vs[2];  // this lane's row offsets (codes: + 16 * K-half)
+  rsrc_t rc[2], rs[2];    // codes and scales of fragment 0 and 1
+  uint32_t vc[2], vs[2];  // codes: row (lane%16) offset + 16 * (lane/16); scales: row (lane%32) offset
+  uint32_t half;          // byte distance of row 16 from row 0
   __device__ __forceinline__ void load(int c, BRegs& r) const {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) r.q[g][s] = bload16(rc[g], vc[g] + (uint32_t)c * 64u + 32u * s);
+      for (int j = 0; j < 2; ++j) r.q[g][j] = bload16(rc[g], vc[g] + half * j + (uint32_t)c * 64u);
       r.s[g] = bload4(rs[g], vs[g] + (uint32_t)c * 4u);
     }
   }
 };
+
+// Rows 0-15 (P) and 16-31 (Q) as loaded, 16-lane groups [b0 b1 b2 b3] of 16
+// rows each  ->  K-step 0 = [P.b0 Q.b0 P.b1 Q.b1], K-step 1 = [P.b2 Q.b2 P.b3 Q.b3]
+// (lane l: row l%32, block 2s + l/32).
+__device__ __forceinline__ void b_operands(const uint4_t& P, const uint4_t& Q, i8v& s0, i8v& s1) {
+  uint32_t o0[4], o1[4];
+  const uint32_t p[4] = {P.x, P.y, P.z, P.w}, q[4] = {Q.x, Q.y, Q.z, Q.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const auto t = __builtin_amdgcn_permlane16_swap(p[d], q[d], false, false);   // [P0 Q0 P2 Q2], [P1 Q1 P3 Q3]
+    const auto u = __builtin_amdgcn_permlane32_swap(t[0], t[1], false, false);   // [P0 Q0 P1 Q1], [P2 Q2 P3 Q3]
+    o0[d] = u[0];
+    o1[d] = u[1];
+  }
+  s0 = i8v{(int)o0[0], (int)o0[1], (int)o0[2], (int)o0[3], 0, 0, 0, 0};
+  s1 = i8v{(int)o1[0], (int)o1[1], (int)o1[2], (int)o1[3], 0, 0, 0, 0};
+}
 
 // One chunk of MFMAs: A fragments from LDS (48 B per lane = both K-steps),
 // B from registers.  With an empty chunk (nks == 0) nothing is multiplied.
@@ -376,6 +432,9 @@ __device__ __forceinline__ void mma_chunk(const ABuf& cur, const BRegs& b, f16v 
   uint32_t bsw[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) bsw[g] = b.s[g] >> (8 * h);
+  i8v bop[2][2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) b_operands(b.q[g][0], b.q[g][1], bop[g][0], bop[g][1]);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -386,8 +445,7 @@ __device__ __forceinline__ void mma_chunk(const ABuf& cur, const BRegs& b, f16v 
       const int sa = (int)(asw[f] >> (16 * s));  // low byte: block 2s+h
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const uint4_t q = b.q[g][s];
-        const i8v bb = i8v{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+        const i8v bb = bop[g][s];
         const int sb = (int)(bsw[g] >> (16 * s));
         acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bb, acc[f][g], 2, 4, 0, sa, 0, sb);
       }
@@ -395,32 +453,223 @@ __device__ __forceinline__ void mma_chunk(const ABuf& cur, const BRegs& b, f16v 
   }
 }
 
-// The K loop over all chunks of one tile.  The A chunk c+1 is loaded during
-// chunk c-1 and stored to LDS at the end of chunk c; the B registers of chunk
-// c+1 are loaded at the start of chunk c.  Chunks run in pairs (the B register
-// sets alternate); with an odd chunk count the last step multiplies nothing.
-// Loads past the last chunk re-read it, and stores past it write a stage that
-// nothing reads again, so no load or store of the loop sits behind a branch.
+// The K loop over all chunks of one tile.  A ring of PF register sets keeps
+// the loads of chunks c+1..c+PF-1 in flight while chunk c is multiplied (the
+// gathered activation rows come from the last-level cache, a long round
+// trip); A chunk c+1 moves from its registers to LDS at the end of chunk c.
+// The loop runs in rounds of PF steps; steps past the last chunk multiply
+// nothing, loads past it re-read it and stores past it write a stage nothing
+// reads again, so no load or store of the loop sits behind a branch.
+constexpr int PF = 4;
+
+struct ChunkRegs {
+  ARegs a;
+  BRegs b;
+};
+
 __device__ __forceinline__ void gemm_k_loop(GemmSmem& sm, f16v (&acc)[4][2], const ASrc& as, const BSrc& bs,
                                             int K, int tid, int lane) {
   const int nchunks = K / KC, last = nchunks - 1;
-  ARegs an;
-  BRegs b0, b1;
-  as.load(0, an);
-  bs.load(0, b0);
-  store_a(sm.a[0], an, tid);
-  as.load(min(1, last), an);
+  ChunkRegs r[PF];
+#pragma unroll
+  for (int j = 0; j < PF - 1; ++j) {
+    as.load(min(j, last), r[j].a);
+    bs.load(min(j, last), r[j].b);
+  }
+  store_a(sm.a[0], r[0].a, tid);
   __syncthreads();
-  auto step = [&](int c, const BRegs& cur, BRegs& nxt) {
-    bs.load(min(c + 1, last), nxt);
-    mma_chunk(sm.a[c & 1], cur, acc, c > last ? 0 : 2, lane);
-    store_a(sm.a[(c + 1) & 1], an, tid);
-    as.load(min(c + 2, last), an);
-    __syncthreads();
-  };
-  for (int c = 0; c < nchunks; c += 2) {
-    step(c, b0, b1);
-    step(c + 1, b1, b0);
+  for (int c0 = 0; c0 < nchunks; c0 += PF) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int c = c0 + j;
+      ChunkRegs& ahead = r[(j + PF - 1) % PF];
+      as.load(min(c + PF - 1, last), ahead.a);
+      bs.load(min(c + PF - 1, last), ahead.b);
+      mma_chunk(sm.a[c & 1], r[j].b, acc, c > last ? 0 : 2, lane);
+      store_a(sm.a[(c + 1) & 1], r[(j + 1) % PF].a, tid);
+      __syncthreads();
+    }
+  }
+}
+
+// ---- streaming path for small buckets ----------------------------------------------
+//
+// A bucket of at most SK_MAX rows (most experts of a prefill chunk: tokens
+// spread thinly over the routed experts) is a weight stream, not a GEMM: its
+// expert is read once for a handful of rows.  One wavefront per (bucket, 32
+// weight rows of each of two matrices): its A fragment (the bucket's rows,
+// rows past the end read as zeros) and its two B fragments come straight from
+// memory into registers in MFMA order, in batches of four K-steps with the next
+// batch in flight, and many wavefronts per CU keep the HBM stream full.
+
+__device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v[0], v[1]);
+}
+
+// Four K-steps of one wavefront: A block 2s+h of row r32 (24 B), B block 2s+h
+// of fragment rows (16 B each), and the scale words of those 8 blocks.
+struct SkRegs {
+  uint2 a[4][3];
+  uint4_t b[4][2];
+  uint32_t as[2];
+  uint32_t bs[2][2];
+};
+
+struct SkSrc {
+  rsrc_t ra, ras, rb[2], rbs[2];
+  uint32_t va, vas, vb[2], vbs[2];  // va: + 24 * K-half; vb: + 16 * K-half
+  __device__ __forceinline__ void load(int n, SkRegs& r) const {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t ks = (uint32_t)(4 * n + s);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) r.a[s][j] = bload8(ra, va + ks * 48u + 8u * j);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) r.b[s][g] = bload16(rb[g], vb[g] + ks * 32u);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      r.as[j] = bload4(ras, vas + (uint32_t)n * 8u + 4u * j);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) r.bs[g][j] = bload4(rbs[g], vbs[g] + (uint32_t)n * 8u + 4u * j);
+    }
+  }
+};
+
+__device__ __forceinline__ void sk_mma(const SkRegs& r, f16v (&acc)[2], int nks, int h) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (s < nks) {
+      const i8v a = i8v{(int)r.a[s][0].x, (int)r.a[s][0].y, (int)r.a[s][1].x, (int)r.a[s][1].y,
+                        (int)r.a[s][2].x, (int)r.a[s][2].y, 0, 0};
+      // low byte: the scale of block 2s+h
+      const int sa = (int)((r.as[s >> 1] >> (8 * h)) >> (16 * (s & 1)));
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const i8v b = i8v{(int)r.b[s][g].x, (int)r.b[s][g].y, (int)r.b[s][g].z, (int)r.b[s][g].w, 0, 0, 0, 0};
+        const int sb = (int)((r.bs[g][s >> 1] >> (8 * h)) >> (16 * (s & 1)));
+        acc[g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[g], 2, 4, 0, sa, 0, sb);
+      }
+    }
+  }
+}
+
+// All K of one unit: batches of four K-steps, the next batch's loads in flight
+// while one is multiplied; pairs of batches alternate the two register sets.
+// Loads past the last batch re-read it (never used): no load behind a branch.
+__device__ __forceinline__ void sk_k_loop(const SkSrc& src, f16v (&acc)[2], int K, int h) {
+  const int nks_total = K / 64, nbat = (nks_total + 3) / 4, last = nbat - 1;
+  SkRegs r0, r1;
+  src.load(0, r0);
+  for (int n = 0; n < nbat; n += 2) {
+    src.load(min(n + 1, last), r1);
+    sk_mma(r0, acc, min(4, nks_total - 4 * n), h);
+    src.load(min(n + 2, last), r0);
+    sk_mma(r1, acc, n + 1 > last ? 0 : min(4, nks_total - 4 * (n + 1)), h);
+  }
+}
+
+constexpr int SK_GRID = 1024;  // workgroups of the streaming kernels (4 wavefronts each)
+
+__global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, uint32_t xq_bytes, uint32_t xs_bytes, int k,
+    ExpertStore w, const int32_t* __restrict__ sorted_pair, const SkBucket* __restrict__ sbk,
+    const int32_t* __restrict__ counts, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
+  __shared__ float stage[4][32 * 33];
+  const int H = w.H, I = w.I, NBH = H / 32, NBI = I / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
+  const uint32_t arow = (uint32_t)NBH * 24u, wrow = (uint32_t)H / 2u;
+  const size_t mat = (size_t)I * wrow, smat = (size_t)I * NBH;
+  const int groups = I / 32, units = counts[2] * groups;
+  float* st = stage[wid];
+  for (int u = blockIdx.x * 4 + wid; u < units; u += gridDim.x * 4) {
+    const SkBucket bk = sbk[u / groups];
+    const int q = u % groups;
+    if (bk.slot < 0) continue;
+    const int tok = r32 < bk.cnt ? sorted_pair[bk.row0 + r32] / k : -1;
+    SkSrc src;
+    src.ra = make_rsrc(xq, xq_bytes);
+    src.ras = make_rsrc(xs, xs_bytes);
+    src.va = tok >= 0 ? (uint32_t)tok * arow + 24u * h : kOob;
+    src.vas = tok >= 0 ? (uint32_t)tok * NBH : kOob;
+    const uint32_t jr = (uint32_t)(32 * q + r32);
+    src.rb[0] = make_rsrc(w.wg + (size_t)bk.slot * mat, (uint32_t)mat);
+    src.rb[1] = make_rsrc(w.wu + (size_t)bk.slot * mat, (uint32_t)mat);
+    src.rbs[0] = make_rsrc(w.sg + (size_t)bk.slot * smat, (uint32_t)smat);
+    src.rbs[1] = make_rsrc(w.su + (size_t)bk.slot * smat, (uint32_t)smat);
+    src.vb[0] = src.vb[1] = jr * wrow + 16u * h;
+    src.vbs[0] = src.vbs[1] = jr * NBH;
+    f16v acc[2] = {f16v{}, f16v{}};
+    sk_k_loop(src, acc, H, h);
+    // h = silu(g) * u: rows of the bucket x this unit's 32 h columns (one MXFP6 block per row)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = (i >> 2) * 8 + h * 4 + (i & 3);
+      st[row * 33 + r32] = swiglu_f32(acc[0][i], acc[1][i]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (h == 0 && r32 < bk.cnt) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = st[r32 * 33 + i];
+      uint32_t pk[6], sb;
+      q6_block(v, pk, sb);
+      const size_t grow = (size_t)(bk.row0 + r32);
+      uint2* dst = reinterpret_cast<uint2*>(hq + grow * NBI * 24 + (size_t)q * 24);
+      dst[0] = make_uint2(pk[0], pk[1]);
+      dst[1] = make_uint2(pk[2], pk[3]);
+      dst[2] = make_uint2(pk[4], pk[5]);
+      hs[grow * NBI + q] = (uint8_t)sb;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+__global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
+    const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, uint32_t hq_bytes, uint32_t hs_bytes,
+    ExpertStore w, const int32_t* __restrict__ sorted_pair, const SkBucket* __restrict__ sbk,
+    const int32_t* __restrict__ counts, float* __restrict__ y) {
+  const int H = w.H, I = w.I, NBI = I / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
+  const uint32_t arow = (uint32_t)NBI * 24u, wrow = (uint32_t)I / 2u;
+  const size_t mat = (size_t)H * wrow, smat = (size_t)H * NBI;
+  const int groups = H / 64, units = counts[2] * groups;
+  for (int u = blockIdx.x * 4 + wid; u < units; u += gridDim.x * 4) {
+    const SkBucket bk = sbk[u / groups];
+    const int n0 = 64 * (u % groups);
+    if (bk.slot < 0) {
+      // no stored expert: its rows are zero
+      for (int r = 0; r < bk.cnt; ++r) y[(size_t)sorted_pair[bk.row0 + r] * H + n0 + lane] = 0.f;
+      continue;
+    }
+    SkSrc src;
+    src.ra = make_rsrc(hq, hq_bytes);
+    src.ras = make_rsrc(hs, hs_bytes);
+    const uint32_t arow_i = (uint32_t)(bk.row0 + r32);
+    src.va = r32 < bk.cnt ? arow_i * arow + 24u * h : kOob;
+    src.vas = r32 < bk.cnt ? arow_i * NBI : kOob;
+    const rsrc_t rc = make_rsrc(w.wd + (size_t)bk.slot * mat, (uint32_t)mat);
+    const rsrc_t rs = make_rsrc(w.sd + (size_t)bk.slot * smat, (uint32_t)smat);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const uint32_t nr = (uint32_t)(n0 + 32 * g + r32);
+      src.rb[g] = rc;
+      src.rbs[g] = rs;
+      src.vb[g] = nr * wrow + 16u * h;
+      src.vbs[g] = nr * NBI;
+    }
+    f16v acc[2] = {f16v{}, f16v{}};
+    sk_k_loop(src, acc, I, h);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = (i >> 2) * 8 + h * 4 + (i & 3);
+      if (row < bk.cnt) {
+        float* yr = y + (size_t)sorted_pair[bk.row0 + row] * H + n0 + r32;
+        yr[0] = acc[0][i];
+        yr[32] = acc[1][i];
+      }
+    }
   }
 }
 
@@ -430,7 +679,7 @@ __device__ __forceinline__ void gemm_k_loop(GemmSmem& sm, f16v (&acc)[4][2], con
 // index, so h = silu(g)*u is formed in its registers; its 32 h columns are
 // exactly one MXFP6 block per row.
 
-__global__ __launch_bounds__(kPT, 2) void gateup_mfma_kernel(
+__global__ __launch_bounds__(kPT, 1) void gateup_mfma_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, uint32_t xq_bytes, uint32_t xs_bytes, int k,
     ExpertStore w, const int32_t* __restrict__ sorted_pair, const TileDesc* __restrict__ tiles,
     const int32_t* __restrict__ counts, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
@@ -466,7 +715,9 @@ __global__ __launch_bounds__(kPT, 2) void gateup_mfma_kernel(
       bs.rc[1] = make_rsrc(w.wu + (size_t)d.slot * mat, (uint32_t)mat);
       bs.rs[0] = make_rsrc(w.sg + (size_t)d.slot * smat, (uint32_t)smat);
       bs.rs[1] = make_rsrc(w.su + (size_t)d.slot * smat, (uint32_t)smat);
-      bs.vc[0] = bs.vc[1] = jr * wrow + 16u * h;
+      const uint32_t jl = (uint32_t)(j0 + 32 * wid + (lane & 15));
+      bs.vc[0] = bs.vc[1] = jl * wrow + 16u * (uint32_t)(lane >> 4);
+      bs.half = 16u * wrow;
       bs.vs[0] = bs.vs[1] = jr * NBH;
     }
     f16v acc[4][2];
@@ -508,7 +759,7 @@ __global__ __launch_bounds__(kPT, 2) void gateup_mfma_kernel(
 
 // ---- P2: down GEMM -> y_pair ---------------------------------------------------------
 
-__global__ __launch_bounds__(kPT, 2) void down_mfma_kernel(
+__global__ __launch_bounds__(kPT, 1) void down_mfma_kernel(
     const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, uint32_t hq_bytes, uint32_t hs_bytes,
     ExpertStore w, const int32_t* __restrict__ sorted_pair, const TileDesc* __restrict__ tiles,
     const int32_t* __restrict__ counts, float* __restrict__ y) {
@@ -543,12 +794,13 @@ __global__ __launch_bounds__(kPT, 2) void down_mfma_kernel(
       const rsrc_t rs = make_rsrc(w.sd + (size_t)d.slot * smat, (uint32_t)smat);
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const uint32_t nr = (uint32_t)(n0 + 64 * wid + 32 * g + r32);
+        const uint32_t nr = (uint32_t)(n0 + 64 * wid + 32 * g);
         bs.rc[g] = rc;
         bs.rs[g] = rs;
-        bs.vc[g] = nr * wrow + 16u * h;
-        bs.vs[g] = nr * NBI;
+        bs.vc[g] = (nr + (uint32_t)(lane & 15)) * wrow + 16u * (uint32_t)(lane >> 4);
+        bs.vs[g] = (nr + (uint32_t)r32) * NBI;
       }
+      bs.half = 16u * wrow;
     }
     f16v acc[4][2];
 #pragma unroll
@@ -583,7 +835,7 @@ size_t prefill_workspace_bytes(int T, int k, int H, int I) {
   const size_t P = (size_t)T * k, nm = max_mtiles(P);
   return align256((size_t)T * H / 32 * 24) + align256((size_t)T * H / 32) + align256(P * I / 32 * 24) +
          align256(P * I / 32) + align256(nm * (I / GU_N) * sizeof(TileDesc)) +
-         align256(nm * (H / DN_N) * sizeof(TileDesc)) + 256;
+         align256(nm * (H / DN_N) * sizeof(TileDesc)) + align256(kMaxExperts * sizeof(SkBucket)) + 256;
 }
 
 hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertStore& w, const int32_t* e2s,
@@ -603,18 +855,28 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
   TileDesc* gu = reinterpret_cast<TileDesc*>(hs + align256(hs_b));
   TileDesc* dn = reinterpret_cast<TileDesc*>(reinterpret_cast<uint8_t*>(gu) +
                                              align256(nm * (I / GU_N) * sizeof(TileDesc)));
-  int32_t* counts = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(dn) +
-                                               align256(nm * (H / DN_N) * sizeof(TileDesc)));
+  SkBucket* sbk = reinterpret_cast<SkBucket*>(reinterpret_cast<uint8_t*>(dn) +
+                                             align256(nm * (H / DN_N) * sizeof(TileDesc)));
+  int32_t* counts = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(sbk) +
+                                               align256(kMaxExperts * sizeof(SkBucket)));
   const int nblk = T * (H / 32);
   hipLaunchKernelGGL(quant_x_kernel, dim3((nblk + kPT - 1) / kPT), dim3(kPT), 0, s, x, nblk, xq, xs);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPT), 0, s, offsets, E, e2s, w.num_slots, I / GU_N, H / DN_N, gu,
-                     dn, counts);
+                     dn, sbk, counts);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(gateup_skinny_kernel, dim3(SK_GRID), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, k,
+                     w, sorted_pair, sbk, counts, hq, hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(gateup_mfma_kernel, dim3(kGrid), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, k, w,
                      sorted_pair, gu, counts, hq, hs);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(down_skinny_kernel, dim3(SK_GRID), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, w,
+                     sorted_pair, sbk, counts, y_pair);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(down_mfma_kernel, dim3(kGrid), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, w,
