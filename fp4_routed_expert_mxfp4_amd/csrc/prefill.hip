@@ -302,16 +302,61 @@ constexpr int A_HS = BM * 48 + 64;  // LDS bytes per K-half region of an A chunk
 
 struct ABuf {
   uint8_t codes[2 * A_HS];
-  uint32_t scales[2 * BM];  // rows 0..BM-1; the upper half takes the stores of threads tid >= BM
-  uint2 spill[64];          // the stores of lanes that carry no codes
+  uint2 spill[64];  // the stores of lanes that carry no codes
 };
+
+// Scale bytes are read once per tile into LDS tables (a scale word -- the 4
+// blocks of one chunk -- per row and chunk, for a window of SCWIN chunks):
+// per-chunk loads of 4 bytes from every row would each cost a cache-line
+// request.  The rows of a wavefront's weight fragment are consecutive, so
+// their table loads read contiguous memory.
+constexpr int SCWIN = 40;       // largest scale window in chunks (160 blocks)
+constexpr int SCW = SCWIN + 1;  // words per table row (odd: a fragment's 32 rows hit 32 banks)
 
 struct GemmSmem {
   union {
     ABuf a[2];
     float stage[BM * STAGE_S];
   };
+  uint32_t sca[BM * SCW];      // A scale words of the tile's rows
+  uint32_t scb[4][64 * SCW];   // B scale words of each wavefront's 64 weight rows
   int rowtok[BM];
+};
+
+// Words [cw0, cw0 + SCWIN) of ROWS table rows, in two steps so that their
+// latency overlaps the first chunk loads of the K loop: issue() loads into
+// registers, store() writes the table.  row_off(r) is the byte offset of row
+// r's scale bytes (kOob for rows past the bucket).
+template <int ROWS, int NT, int WIN>
+struct ScaleRows {
+  static constexpr int N = ROWS * WIN / NT;
+  static_assert(ROWS * WIN % NT == 0 && WIN <= SCWIN, "table split");
+  uint32_t v[N];
+  template <typename RowOff>
+  __device__ __forceinline__ void issue(rsrc_t r, int cw0, int t, RowOff row_off) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = t + NT * i, row = idx / WIN, wd = idx - row * WIN;
+      const uint32_t o = row_off(row);
+      v[i] = bload4(r, o == kOob ? kOob : o + 4u * (uint32_t)(cw0 + wd));
+    }
+  }
+  __device__ __forceinline__ void store(uint32_t* tab, int t) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = t + NT * i, row = idx / WIN, wd = idx - row * WIN;
+      tab[row * SCW + wd] = v[i];
+    }
+  }
+};
+
+// The scale tables of one tile for a window of WIN chunks: A rows (all
+// threads) and each wavefront's two 32-row weight fragments.
+template <int WIN>
+struct TileScales {
+  static constexpr int kWin = WIN;
+  ScaleRows<BM, kPT, WIN> a;
+  ScaleRows<32, 64, WIN> b[2];
 };
 
 // Registers of one A chunk between its global loads and its LDS store.  The
@@ -320,17 +365,14 @@ struct GemmSmem {
 // tid < BM also load the scale word of row tid.
 struct ARegs {
   uint4_t q[BM / 32];  // rows 32w + 8i + lane/8, i = 0..3
-  uint32_t s;
 };
 
 struct ASrc {
-  rsrc_t rc, rs;
+  rsrc_t rc;
   uint32_t vc[BM / 32];  // row offsets + 16p (kOob for rows past the bucket and for lanes p >= 6)
-  uint32_t vs;           // scale offset of row tid (kOob past the bucket, or for tid >= BM)
   __device__ __forceinline__ void load(int c, ARegs& r) const {
 #pragma unroll
     for (int i = 0; i < BM / 32; ++i) r.q[i] = bload16(rc, vc[i] + (uint32_t)c * 96u);
-    r.s = bload4(rs, vs + (uint32_t)c * 4u);
   }
 };
 
@@ -357,7 +399,6 @@ __device__ __forceinline__ void store_a(ABuf& d, const ARegs& r, int tid) {
     *reinterpret_cast<uint2*>(d0) = make_uint2(r.q[i].x, r.q[i].y);
     *reinterpret_cast<uint2*>(d1) = make_uint2(r.q[i].z, r.q[i].w);
   }
-  d.scales[tid] = r.s;
 }
 
 // Row offsets of this thread's A loads; row_off(r) gives the byte offset of
@@ -376,24 +417,20 @@ __device__ __forceinline__ void a_offsets(ASrc& as, int tid, RowOff row_off) {
 // loaded as two halves of 16 rows x 64 contiguous bytes (lane l: row 16j +
 // l%16, block l/16 of the chunk), which touches half the cache lines of the
 // MFMA order (32 rows x 32 B); b_operands() moves them into MFMA order with two
-// lane swaps per dword when they are used.  Plus the row's scale word (blocks
-// 0..3 of the chunk) in MFMA order (lane l: row l%32).
+// lane swaps per dword when they are used.
 struct BRegs {
   uint4_t q[2][2];  // [fragment][row half], as loaded
-  uint32_t s[2];
 };
 
 struct BSrc {
-  rsrc_t rc[2], rs[2];    // codes and scales of fragment 0 and 1
-  uint32_t vc[2], vs[2];  // codes: row (lane%16) offset + 16 * (lane/16); scales: row (lane%32) offset
-  uint32_t half;          // byte distance of row 16 from row 0
+  rsrc_t rc[2];     // codes of fragment 0 and 1
+  uint32_t vc[2];   // row (lane%16) offset + 16 * (lane/16)
+  uint32_t half;    // byte distance of row 16 from row 0
   __device__ __forceinline__ void load(int c, BRegs& r) const {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int j = 0; j < 2; ++j) r.q[g][j] = bload16(rc[g], vc[g] + half * j + (uint32_t)c * 64u);
-      r.s[g] = bload4(rs[g], vs[g] + (uint32_t)c * 4u);
-    }
   }
 };
 
@@ -416,7 +453,8 @@ __device__ __forceinline__ void b_operands(const uint4_t& P, const uint4_t& Q, i
 
 // One chunk of MFMAs: A fragments from LDS (48 B per lane = both K-steps),
 // B from registers.  With an empty chunk (nks == 0) nothing is multiplied.
-__device__ __forceinline__ void mma_chunk(const ABuf& cur, const BRegs& b, f16v (&acc)[4][2], int nks, int lane) {
+__device__ __forceinline__ void mma_chunk(const ABuf& cur, const BRegs& b, const uint32_t* sca, const uint32_t* scb,
+                                          int cw, f16v (&acc)[4][2], int nks, int lane) {
   const int r32 = lane & 31, h = lane >> 5;
   if (nks == 0) return;
   uint4_t av[4][3];
@@ -427,11 +465,11 @@ __device__ __forceinline__ void mma_chunk(const ABuf& cur, const BRegs& b, f16v 
     av[f][0] = p[0];
     av[f][1] = p[1];
     av[f][2] = p[2];
-    asw[f] = cur.scales[32 * f + r32] >> (8 * h);
+    asw[f] = sca[(32 * f + r32) * SCW + cw] >> (8 * h);
   }
   uint32_t bsw[2];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) bsw[g] = b.s[g] >> (8 * h);
+  for (int g = 0; g < 2; ++g) bsw[g] = scb[(32 * g + r32) * SCW + cw] >> (8 * h);
   i8v bop[2][2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) b_operands(b.q[g][0], b.q[g][1], bop[g][0], bop[g][1]);
@@ -467,27 +505,37 @@ struct ChunkRegs {
   BRegs b;
 };
 
+template <int WIN, typename Tables>
 __device__ __forceinline__ void gemm_k_loop(GemmSmem& sm, f16v (&acc)[4][2], const ASrc& as, const BSrc& bs,
-                                            int K, int tid, int lane) {
-  const int nchunks = K / KC, last = nchunks - 1;
-  ChunkRegs r[PF];
+                                            int K, int tid, int lane, Tables tables) {
+  const int nchunks = K / KC, wid = tid >> 6;
+  for (int cw0 = 0; cw0 < nchunks; cw0 += WIN) {
+    const int last = min(cw0 + WIN, nchunks) - 1;
+    TileScales<WIN> ts;
+    tables(cw0, ts);
+    ChunkRegs r[PF];
 #pragma unroll
-  for (int j = 0; j < PF - 1; ++j) {
-    as.load(min(j, last), r[j].a);
-    bs.load(min(j, last), r[j].b);
-  }
-  store_a(sm.a[0], r[0].a, tid);
-  __syncthreads();
-  for (int c0 = 0; c0 < nchunks; c0 += PF) {
+    for (int j = 0; j < PF - 1; ++j) {
+      as.load(min(cw0 + j, last), r[j].a);
+      bs.load(min(cw0 + j, last), r[j].b);
+    }
+    // the tables and A chunk 0, made visible by the barrier below
+    ts.a.store(sm.sca, tid);
+    ts.b[0].store(sm.scb[wid], lane);
+    ts.b[1].store(sm.scb[wid] + 32 * SCW, lane);
+    store_a(sm.a[0], r[0].a, tid);
+    __syncthreads();
+    for (int c0 = cw0; c0 <= last; c0 += PF) {
 #pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int c = c0 + j;
-      ChunkRegs& ahead = r[(j + PF - 1) % PF];
-      as.load(min(c + PF - 1, last), ahead.a);
-      bs.load(min(c + PF - 1, last), ahead.b);
-      mma_chunk(sm.a[c & 1], r[j].b, acc, c > last ? 0 : 2, lane);
-      store_a(sm.a[(c + 1) & 1], r[(j + 1) % PF].a, tid);
-      __syncthreads();
+      for (int j = 0; j < PF; ++j) {
+        const int c = c0 + j;
+        ChunkRegs& ahead = r[(j + PF - 1) % PF];
+        as.load(min(c + PF - 1, last), ahead.a);
+        bs.load(min(c + PF - 1, last), ahead.b);
+        mma_chunk(sm.a[(c - cw0) & 1], r[j].b, sm.sca, sm.scb[wid], c - cw0, acc, c > last ? 0 : 2, lane);
+        store_a(sm.a[(c - cw0 + 1) & 1], r[(j + 1) % PF].a, tid);
+        __syncthreads();
+      }
     }
   }
 }
@@ -698,34 +746,38 @@ __global__ __launch_bounds__(kPT, 1) void gateup_mfma_kernel(
     const int j0 = d.ntile * GU_N;
     ASrc as;
     as.rc = make_rsrc(xq, xq_bytes);
-    as.rs = make_rsrc(xs, xs_bytes);
     a_offsets(as, tid, [&](int r) {
       const int tok = sm.rowtok[r];
       return tok >= 0 ? (uint32_t)tok * arow : kOob;
     });
-    {
-      const int tok = tid < BM ? sm.rowtok[tid] : -1;
-      as.vs = tok >= 0 ? (uint32_t)tok * NBH : kOob;
-    }
     BSrc bs;
     {
       // wavefront wid: gate rows j0+32*wid.. (fragment 0) and the same up rows (fragment 1)
       const uint32_t jr = (uint32_t)(j0 + 32 * wid + r32);
       bs.rc[0] = make_rsrc(w.wg + (size_t)d.slot * mat, (uint32_t)mat);
       bs.rc[1] = make_rsrc(w.wu + (size_t)d.slot * mat, (uint32_t)mat);
-      bs.rs[0] = make_rsrc(w.sg + (size_t)d.slot * smat, (uint32_t)smat);
-      bs.rs[1] = make_rsrc(w.su + (size_t)d.slot * smat, (uint32_t)smat);
       const uint32_t jl = (uint32_t)(j0 + 32 * wid + (lane & 15));
       bs.vc[0] = bs.vc[1] = jl * wrow + 16u * (uint32_t)(lane >> 4);
       bs.half = 16u * wrow;
-      bs.vs[0] = bs.vs[1] = jr * NBH;
     }
+    const rsrc_t xsr = make_rsrc(xs, xs_bytes);
+    const rsrc_t sgr = make_rsrc(w.sg + (size_t)d.slot * smat, (uint32_t)smat);
+    const rsrc_t sur = make_rsrc(w.su + (size_t)d.slot * smat, (uint32_t)smat);
+    const uint32_t jr0 = (uint32_t)(j0 + 32 * wid);
+    auto tables = [&](int cw0, TileScales<40>& ts) {
+      ts.a.issue(xsr, cw0, tid, [&](int r) {
+        const int tok = sm.rowtok[r];
+        return tok >= 0 ? (uint32_t)tok * NBH : kOob;
+      });
+      ts.b[0].issue(sgr, cw0, lane, [&](int r) { return (jr0 + (uint32_t)r) * NBH; });
+      ts.b[1].issue(sur, cw0, lane, [&](int r) { return (jr0 + (uint32_t)r) * NBH; });
+    };
     f16v acc[4][2];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int g = 0; g < 2; ++g) acc[f][g] = f16v{};
-    gemm_k_loop(sm, acc, as, bs, H, tid, lane);
+    gemm_k_loop<40>(sm, acc, as, bs, H, tid, lane, tables);
     // h = silu(g) * u into the staging buffer (the K loop ended on a barrier)
     const int wcol = 32 * wid + r32;
 #pragma unroll
@@ -784,9 +836,7 @@ __global__ __launch_bounds__(kPT, 1) void down_mfma_kernel(
     }
     ASrc as;
     as.rc = make_rsrc(hq, hq_bytes);
-    as.rs = make_rsrc(hs, hs_bytes);
     a_offsets(as, tid, [&](int r) { return r < d.mrows ? (uint32_t)(d.row0 + r) * arow : kOob; });
-    as.vs = tid < d.mrows ? (uint32_t)(d.row0 + tid) * NBI : kOob;
     BSrc bs;
     {
       // wavefront wid: output rows n0+64*wid+32g.. (fragment g)
@@ -796,18 +846,26 @@ __global__ __launch_bounds__(kPT, 1) void down_mfma_kernel(
       for (int g = 0; g < 2; ++g) {
         const uint32_t nr = (uint32_t)(n0 + 64 * wid + 32 * g);
         bs.rc[g] = rc;
-        bs.rs[g] = rs;
         bs.vc[g] = (nr + (uint32_t)(lane & 15)) * wrow + 16u * (uint32_t)(lane >> 4);
-        bs.vs[g] = (nr + (uint32_t)r32) * NBI;
       }
       bs.half = 16u * wrow;
+      (void)rs;
     }
+    const rsrc_t hsr = make_rsrc(hs, hs_bytes);
+    const rsrc_t sdr = make_rsrc(w.sd + (size_t)d.slot * smat, (uint32_t)smat);
+    const uint32_t nr0 = (uint32_t)(n0 + 64 * wid);
+    auto tables = [&](int cw0, TileScales<20>& ts) {
+      ts.a.issue(hsr, cw0, tid, [&](int r) { return r < d.mrows ? (uint32_t)(d.row0 + r) * NBI : kOob; });
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        ts.b[g].issue(sdr, cw0, lane, [&](int r) { return (nr0 + 32u * g + (uint32_t)r) * NBI; });
+    };
     f16v acc[4][2];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int g = 0; g < 2; ++g) acc[f][g] = f16v{};
-    gemm_k_loop(sm, acc, as, bs, I, tid, lane);
+    gemm_k_loop<20>(sm, acc, as, bs, I, tid, lane, tables);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       __builtin_amdgcn_sched_barrier(0);  // one fragment's stores at a time (register pressure)

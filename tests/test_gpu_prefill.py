@@ -16,6 +16,8 @@ PREFILL_CASES = {
     "mid_zipf": gi.custom("mid_zipf_p", 1024, 384, 24, 4, 300, seed=31, zipf=1.1),
     # masked routable subset, k = 6
     "mid_resident": gi.custom("mid_resident_p", 512, 256, 40, 6, 77, seed=32, resident=10),
+    # hidden 6144: the gate/up K loop spans two scale windows; buckets of ~100 rows (tiled path)
+    "wide_hidden": gi.custom("wide_hidden_p", 6144, 256, 4, 2, 200, seed=33),
 }
 
 
