@@ -555,27 +555,34 @@ __device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t off) {
   return make_uint2(v[0], v[1]);
 }
 
-// Four K-steps of one wavefront: A block 2s+h of row r32 (24 B), B block 2s+h
-// of fragment rows (16 B each), and the scale words of those 8 blocks.
+// Four K-steps (two 128-K chunks) of one wavefront: A block 2s+h of row r32
+// (24 B); each B fragment's rows as two halves of 16 rows x 64 B per chunk
+// (moved into MFMA order by b_operands when used); and the scale words of
+// those 8 blocks.
 struct SkRegs {
   uint2 a[4][3];
-  uint4_t b[4][2];
+  uint4_t b[2][2][2];  // [chunk][fragment][row half]
   uint32_t as[2];
   uint32_t bs[2][2];
 };
 
 struct SkSrc {
   rsrc_t ra, ras, rb[2], rbs[2];
-  uint32_t va, vas, vb[2], vbs[2];  // va: + 24 * K-half; vb: + 16 * K-half
+  uint32_t va, vas, vb[2], vbs[2];  // va: + 24 * K-half; vb: row (lane%16) + 16 * (lane/16)
+  uint32_t half;                    // byte distance of fragment row 16 from row 0
   __device__ __forceinline__ void load(int n, SkRegs& r) const {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const uint32_t ks = (uint32_t)(4 * n + s);
 #pragma unroll
       for (int j = 0; j < 3; ++j) r.a[s][j] = bload8(ra, va + ks * 48u + 8u * j);
-#pragma unroll
-      for (int g = 0; g < 2; ++g) r.b[s][g] = bload16(rb[g], vb[g] + ks * 32u);
     }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) r.b[m][g][j] = bload16(rb[g], vb[g] + half * j + (uint32_t)(2 * n + m) * 64u);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       r.as[j] = bload4(ras, vas + (uint32_t)n * 8u + 4u * j);
@@ -586,6 +593,11 @@ struct SkSrc {
 };
 
 __device__ __forceinline__ void sk_mma(const SkRegs& r, f16v (&acc)[2], int nks, int h) {
+  i8v bop[2][4];  // [fragment][K-step]
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) b_operands(r.b[m][g][0], r.b[m][g][1], bop[g][2 * m], bop[g][2 * m + 1]);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     if (s < nks) {
@@ -595,9 +607,8 @@ __device__ __forceinline__ void sk_mma(const SkRegs& r, f16v (&acc)[2], int nks,
       const int sa = (int)((r.as[s >> 1] >> (8 * h)) >> (16 * (s & 1)));
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const i8v b = i8v{(int)r.b[s][g].x, (int)r.b[s][g].y, (int)r.b[s][g].z, (int)r.b[s][g].w, 0, 0, 0, 0};
         const int sb = (int)((r.bs[g][s >> 1] >> (8 * h)) >> (16 * (s & 1)));
-        acc[g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[g], 2, 4, 0, sa, 0, sb);
+        acc[g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop[g][s], acc[g], 2, 4, 0, sa, 0, sb);
       }
     }
   }
@@ -646,7 +657,8 @@ __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
     src.rb[1] = make_rsrc(w.wu + (size_t)bk.slot * mat, (uint32_t)mat);
     src.rbs[0] = make_rsrc(w.sg + (size_t)bk.slot * smat, (uint32_t)smat);
     src.rbs[1] = make_rsrc(w.su + (size_t)bk.slot * smat, (uint32_t)smat);
-    src.vb[0] = src.vb[1] = jr * wrow + 16u * h;
+    src.vb[0] = src.vb[1] = (uint32_t)(32 * q + (lane & 15)) * wrow + 16u * (uint32_t)(lane >> 4);
+    src.half = 16u * wrow;
     src.vbs[0] = src.vbs[1] = jr * NBH;
     f16v acc[2] = {f16v{}, f16v{}};
     sk_k_loop(src, acc, H, h);
@@ -701,12 +713,13 @@ __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
     const rsrc_t rs = make_rsrc(w.sd + (size_t)bk.slot * smat, (uint32_t)smat);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const uint32_t nr = (uint32_t)(n0 + 32 * g + r32);
+      const uint32_t nr = (uint32_t)(n0 + 32 * g);
       src.rb[g] = rc;
       src.rbs[g] = rs;
-      src.vb[g] = nr * wrow + 16u * h;
-      src.vbs[g] = nr * NBI;
+      src.vb[g] = (nr + (uint32_t)(lane & 15)) * wrow + 16u * (uint32_t)(lane >> 4);
+      src.vbs[g] = (nr + (uint32_t)r32) * NBI;
     }
+    src.half = 16u * wrow;
     f16v acc[2] = {f16v{}, f16v{}};
     sk_k_loop(src, acc, I, h);
 #pragma unroll
