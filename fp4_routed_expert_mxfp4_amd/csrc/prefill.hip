@@ -327,7 +327,7 @@ struct GemmSmem {
 // latency overlaps the first chunk loads of the K loop: issue() loads into
 // registers, store() writes the table.  row_off(r) is the byte offset of row
 // r's scale bytes (kOob for rows past the bucket).
-template <int ROWS, int NT, int WIN>
+template <int ROWS, int NT, int WIN, int STRIDE = SCW>  // STRIDE: words per table row
 struct ScaleRows {
   static constexpr int N = ROWS * WIN / NT;
   static_assert(ROWS * WIN % NT == 0 && WIN <= SCWIN, "table split");
@@ -345,7 +345,7 @@ struct ScaleRows {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int idx = t + NT * i, row = idx / WIN, wd = idx - row * WIN;
-      tab[row * SCW + wd] = v[i];
+      tab[row * STRIDE + wd] = v[i];
     }
   }
 };
@@ -562,14 +562,18 @@ __device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t off) {
 struct SkRegs {
   uint2 a[4][3];
   uint4_t b[2][2][2];  // [chunk][fragment][row half]
-  uint32_t as[2];
-  uint32_t bs[2][2];
 };
 
+// Scale words come from a per-wavefront LDS table read once per window of
+// SKWIN chunks: rows 0-31 the unit's A rows, 32-63 and 64-95 its two weight
+// fragments (whose scale bytes are contiguous).
+constexpr int SKWIN = 20;
+constexpr int SKW = SKWIN + 1;  // words per table row (odd: 32 rows hit 32 banks)
+
 struct SkSrc {
-  rsrc_t ra, ras, rb[2], rbs[2];
-  uint32_t va, vas, vb[2], vbs[2];  // va: + 24 * K-half; vb: row (lane%16) + 16 * (lane/16)
-  uint32_t half;                    // byte distance of fragment row 16 from row 0
+  rsrc_t ra, rb[2];
+  uint32_t va, vb[2];  // va: + 24 * K-half; vb: row (lane%16) + 16 * (lane/16)
+  uint32_t half;       // byte distance of fragment row 16 from row 0
   __device__ __forceinline__ void load(int n, SkRegs& r) const {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -583,16 +587,12 @@ struct SkSrc {
       for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int j = 0; j < 2; ++j) r.b[m][g][j] = bload16(rb[g], vb[g] + half * j + (uint32_t)(2 * n + m) * 64u);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      r.as[j] = bload4(ras, vas + (uint32_t)n * 8u + 4u * j);
-#pragma unroll
-      for (int g = 0; g < 2; ++g) r.bs[g][j] = bload4(rbs[g], vbs[g] + (uint32_t)n * 8u + 4u * j);
-    }
   }
 };
 
-__device__ __forceinline__ void sk_mma(const SkRegs& r, f16v (&acc)[2], int nks, int h) {
+__device__ __forceinline__ void sk_mma(const SkRegs& r, f16v (&acc)[2], int nks, int h, const uint32_t* tab,
+                                       int cw) {  // cw: the batch's first chunk within the window
+  const int r32 = __lane_id() & 31;
   i8v bop[2][4];  // [fragment][K-step]
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -604,10 +604,10 @@ __device__ __forceinline__ void sk_mma(const SkRegs& r, f16v (&acc)[2], int nks,
       const i8v a = i8v{(int)r.a[s][0].x, (int)r.a[s][0].y, (int)r.a[s][1].x, (int)r.a[s][1].y,
                         (int)r.a[s][2].x, (int)r.a[s][2].y, 0, 0};
       // low byte: the scale of block 2s+h
-      const int sa = (int)((r.as[s >> 1] >> (8 * h)) >> (16 * (s & 1)));
+      const int sa = (int)((tab[r32 * SKW + cw + (s >> 1)] >> (8 * h)) >> (16 * (s & 1)));
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const int sb = (int)((r.bs[g][s >> 1] >> (8 * h)) >> (16 * (s & 1)));
+        const int sb = (int)((tab[(32 + 32 * g + r32) * SKW + cw + (s >> 1)] >> (8 * h)) >> (16 * (s & 1)));
         acc[g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop[g][s], acc[g], 2, 4, 0, sa, 0, sb);
       }
     }
@@ -617,15 +617,28 @@ __device__ __forceinline__ void sk_mma(const SkRegs& r, f16v (&acc)[2], int nks,
 // All K of one unit: batches of four K-steps, the next batch's loads in flight
 // while one is multiplied; pairs of batches alternate the two register sets.
 // Loads past the last batch re-read it (never used): no load behind a branch.
-__device__ __forceinline__ void sk_k_loop(const SkSrc& src, f16v (&acc)[2], int K, int h) {
-  const int nks_total = K / 64, nbat = (nks_total + 3) / 4, last = nbat - 1;
-  SkRegs r0, r1;
-  src.load(0, r0);
-  for (int n = 0; n < nbat; n += 2) {
-    src.load(min(n + 1, last), r1);
-    sk_mma(r0, acc, min(4, nks_total - 4 * n), h);
-    src.load(min(n + 2, last), r0);
-    sk_mma(r1, acc, n + 1 > last ? 0 : min(4, nks_total - 4 * (n + 1)), h);
+// tables(cw0, ts) issues the scale-table loads of the window starting at chunk cw0.
+template <typename Tables>
+__device__ __forceinline__ void sk_k_loop(const SkSrc& src, f16v (&acc)[2], int K, int h, uint32_t* tab,
+                                          Tables tables) {
+  const int nks_total = K / 64, nchunks = K / KC;
+  const int lane = __lane_id();
+  for (int cw0 = 0; cw0 < nchunks; cw0 += SKWIN) {
+    const int b0 = cw0 / 2, last = (min(cw0 + SKWIN, nchunks) + 1) / 2 - 1;  // batches of this window
+    ScaleRows<32, 64, SKWIN, SKW> ts[3];
+    tables(cw0, ts);
+    SkRegs r0, r1;
+    src.load(b0, r0);
+#pragma unroll
+    for (int t = 0; t < 3; ++t) ts[t].store(tab + 32 * t * SKW, lane);
+    __builtin_amdgcn_wave_barrier();  // a wavefront's LDS accesses complete in order
+    for (int n = b0; n <= last; n += 2) {
+      src.load(min(n + 1, last), r1);
+      sk_mma(r0, acc, min(4, nks_total - 4 * n), h, tab, 2 * (n - b0));
+      src.load(min(n + 2, last), r0);
+      sk_mma(r1, acc, n + 1 > last ? 0 : min(4, nks_total - 4 * (n + 1)), h, tab, 2 * (n + 1 - b0));
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -636,6 +649,7 @@ __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
     ExpertStore w, const int32_t* __restrict__ sorted_pair, const SkBucket* __restrict__ sbk,
     const int32_t* __restrict__ counts, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
   __shared__ float stage[4][32 * 33];
+  __shared__ uint32_t sktab[4][96 * SKW];
   const int H = w.H, I = w.I, NBH = H / 32, NBI = I / 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
   const uint32_t arow = (uint32_t)NBH * 24u, wrow = (uint32_t)H / 2u;
@@ -649,19 +663,24 @@ __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
     const int tok = r32 < bk.cnt ? sorted_pair[bk.row0 + r32] / k : -1;
     SkSrc src;
     src.ra = make_rsrc(xq, xq_bytes);
-    src.ras = make_rsrc(xs, xs_bytes);
     src.va = tok >= 0 ? (uint32_t)tok * arow + 24u * h : kOob;
-    src.vas = tok >= 0 ? (uint32_t)tok * NBH : kOob;
-    const uint32_t jr = (uint32_t)(32 * q + r32);
     src.rb[0] = make_rsrc(w.wg + (size_t)bk.slot * mat, (uint32_t)mat);
     src.rb[1] = make_rsrc(w.wu + (size_t)bk.slot * mat, (uint32_t)mat);
-    src.rbs[0] = make_rsrc(w.sg + (size_t)bk.slot * smat, (uint32_t)smat);
-    src.rbs[1] = make_rsrc(w.su + (size_t)bk.slot * smat, (uint32_t)smat);
     src.vb[0] = src.vb[1] = (uint32_t)(32 * q + (lane & 15)) * wrow + 16u * (uint32_t)(lane >> 4);
     src.half = 16u * wrow;
-    src.vbs[0] = src.vbs[1] = jr * NBH;
+    const rsrc_t xsr = make_rsrc(xs, xs_bytes);
+    const rsrc_t sgr = make_rsrc(w.sg + (size_t)bk.slot * smat, (uint32_t)smat);
+    const rsrc_t sur = make_rsrc(w.su + (size_t)bk.slot * smat, (uint32_t)smat);
+    auto tables = [&](int cw0, ScaleRows<32, 64, SKWIN, SKW> (&ts)[3]) {
+      ts[0].issue(xsr, cw0, lane, [&](int r) {
+        const int t = __shfl(tok, r, 64);
+        return t >= 0 ? (uint32_t)t * NBH : kOob;
+      });
+      ts[1].issue(sgr, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NBH; });
+      ts[2].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NBH; });
+    };
     f16v acc[2] = {f16v{}, f16v{}};
-    sk_k_loop(src, acc, H, h);
+    sk_k_loop(src, acc, H, h, sktab[wid], tables);
     // h = silu(g) * u: rows of the bucket x this unit's 32 h columns (one MXFP6 block per row)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -690,6 +709,7 @@ __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
     const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, uint32_t hq_bytes, uint32_t hs_bytes,
     ExpertStore w, const int32_t* __restrict__ sorted_pair, const SkBucket* __restrict__ sbk,
     const int32_t* __restrict__ counts, float* __restrict__ y) {
+  __shared__ uint32_t sktab[4][96 * SKW];
   const int H = w.H, I = w.I, NBI = I / 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
   const uint32_t arow = (uint32_t)NBI * 24u, wrow = (uint32_t)I / 2u;
@@ -705,23 +725,25 @@ __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
     }
     SkSrc src;
     src.ra = make_rsrc(hq, hq_bytes);
-    src.ras = make_rsrc(hs, hs_bytes);
     const uint32_t arow_i = (uint32_t)(bk.row0 + r32);
     src.va = r32 < bk.cnt ? arow_i * arow + 24u * h : kOob;
-    src.vas = r32 < bk.cnt ? arow_i * NBI : kOob;
     const rsrc_t rc = make_rsrc(w.wd + (size_t)bk.slot * mat, (uint32_t)mat);
-    const rsrc_t rs = make_rsrc(w.sd + (size_t)bk.slot * smat, (uint32_t)smat);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const uint32_t nr = (uint32_t)(n0 + 32 * g);
       src.rb[g] = rc;
-      src.rbs[g] = rs;
-      src.vb[g] = (nr + (uint32_t)(lane & 15)) * wrow + 16u * (uint32_t)(lane >> 4);
-      src.vbs[g] = (nr + (uint32_t)r32) * NBI;
+      src.vb[g] = (uint32_t)(n0 + 32 * g + (lane & 15)) * wrow + 16u * (uint32_t)(lane >> 4);
     }
     src.half = 16u * wrow;
+    const rsrc_t hsr = make_rsrc(hs, hs_bytes);
+    const rsrc_t sdr = make_rsrc(w.sd + (size_t)bk.slot * smat, (uint32_t)smat);
+    auto tables = [&](int cw0, ScaleRows<32, 64, SKWIN, SKW> (&ts)[3]) {
+      ts[0].issue(hsr, cw0, lane,
+                  [&](int r) { return r < bk.cnt ? (uint32_t)(bk.row0 + r) * NBI : kOob; });
+      ts[1].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + r) * NBI; });
+      ts[2].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + 32 + r) * NBI; });
+    };
     f16v acc[2] = {f16v{}, f16v{}};
-    sk_k_loop(src, acc, I, h);
+    sk_k_loop(src, acc, I, h, sktab[wid], tables);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = (i >> 2) * 8 + h * 4 + (i & 3);
