@@ -260,10 +260,13 @@ def prefill_section(args, torch, m, gd, gi):
     per = t / args.prefill_steps
     flops = 6.0 * cfg.H * cfg.I * T * k
     touched = int((torch.diff(off) > 0).sum().item())
-    log(f"prefill4096: {per * 1e3:.3f} ms/layer, {T / per / 1e6:.2f} M tok/s, {touched} experts")
+    wbytes = touched * cfg.expert_bytes
+    log(f"prefill4096: {per * 1e3:.3f} ms/layer, {T / per / 1e6:.2f} M tok/s, {touched} experts, "
+        f"{wbytes / per / 1e9:.0f} GB/s of expert weights")
     return dict(ms_per_layer=per * 1e3, tokens_per_s=T / per, tflops=flops / per / 1e12,
                 frac_of_mxfp4_peak=flops / per / PEAK_MXFP4,
-                experts_touched=touched, weight_bytes=touched * cfg.expert_bytes)
+                experts_touched=touched, weight_bytes=wbytes,
+                weight_GBps=wbytes / per / 1e9, frac_of_peak_hbm_weights=wbytes / per / PEAK_HBM)
 
 
 def chain_section(args, torch, m, gd, gi):
@@ -319,7 +322,7 @@ def cpu_baseline(db, gi) -> dict:
         threads = os.cpu_count() or 1
     cfg = db.cfg
     hw = gi.HostWeights(cfg)
-    n_tok, total_bytes, total_t = 3, 0, 0.0
+    n_tok, total_bytes, total_t = 10, 0, 0.0
     for s in range(n_tok):
         ids, _ = o.route(db.logit_sets[s], cfg.k)
         for e in set(ids.reshape(-1).tolist()):
