@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-FFN decode achieved HBM GB/s (% of peak); prefill tokens/s at 4096"
 PEAK_HBM = 8.0e12          # bytes/s, MI355X published HBM3E bandwidth
 PEAK_MXFP4 = 10.1e15       # FLOP/s, MI355X published dense MXFP4
+MFMA_MEASURED = 8.4e15     # FLOP/s, the block-scaled e2m3 x e2m1 MFMA measured alone on one MI355X
 NSETS = 64
 
 
@@ -67,8 +68,9 @@ def parse():
     ap.add_argument("--chain-steps", type=int, default=30)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-chain", action="store_true")
+    ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("decode", "prefill", "chain"), default=None,
+    ap.add_argument("--only", choices=("decode", "prefill", "chain", "verify"), default=None,
                     help="run one section only (for profiling); prints that section's numbers")
     ap.add_argument("--calibrate", action="store_true",
                     help="only time torch's plain copy of 4 GiB (the HBM-bytes calibration kernel)")
@@ -224,6 +226,48 @@ def decode_section(args, torch, m, gd, gi):
     return res
 
 
+def verify_section(args, torch, m, gd, gi):
+    """The 16-token decode batch (Zipf-skewed routing: experts shared across
+    tokens) through moe_decode_layer, over 64 rotating routings."""
+    cfg = gi.CONFIGS["verify16"]
+    log(f"verify16: filling {cfg.E} experts")
+    db = DecodeBench(cfg, torch, m, gd, gi)
+    for s in range(NSETS):
+        db.step(s)
+    torch.cuda.synchronize()
+    touched = db.touched()
+    graphs = capture(torch, db.step, NSETS)
+    time_graphs(torch, graphs, 16)
+    steps = max(NSETS, min(args.steps, 512))
+    t = time_graphs(torch, graphs, steps)
+    nbytes = sum(layer_bytes(cfg, touched[i % NSETS], cfg.T) for i in range(steps))
+    per = t / steps
+    log(f"verify16: {per * 1e6:.1f} us/step, {nbytes / t / 1e9:.0f} GB/s, {sum(touched) / NSETS:.1f} experts/step")
+    return dict(us_per_step=per * 1e6, tokens_per_s=cfg.T / per, gbps=nbytes / t / 1e9,
+                frac_of_peak_hbm=nbytes / t / PEAK_HBM, experts_touched_mean=sum(touched) / NSETS)
+
+
+def read_ceiling(torch) -> dict:
+    """A measured streaming-read ceiling: torch's sum over 4 GiB resident in HBM."""
+    n = 4 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1).view(torch.float32)
+    for _ in range(2):
+        a.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        a.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / reps
+    del a
+    torch.cuda.empty_cache()
+    log(f"read ceiling: {n / t / 1e9:.0f} GB/s (sum over 4 GiB)")
+    return dict(bytes=n, us=t * 1e6, read_GBps=n / t / 1e9)
+
+
 def prefill_section(args, torch, m, gd, gi):
     cfg = gi.CONFIGS["prefill4096"]
     hi = gi.host_inputs(cfg)
@@ -261,12 +305,14 @@ def prefill_section(args, torch, m, gd, gi):
     flops = 6.0 * cfg.H * cfg.I * T * k
     touched = int((torch.diff(off) > 0).sum().item())
     wbytes = touched * cfg.expert_bytes
+    binding = max(flops / PEAK_MXFP4, wbytes / PEAK_HBM)  # seconds at the binding roofline
     log(f"prefill4096: {per * 1e3:.3f} ms/layer, {T / per / 1e6:.2f} M tok/s, {touched} experts, "
         f"{wbytes / per / 1e9:.0f} GB/s of expert weights")
     return dict(ms_per_layer=per * 1e3, tokens_per_s=T / per, tflops=flops / per / 1e12,
                 frac_of_mxfp4_peak=flops / per / PEAK_MXFP4,
                 experts_touched=touched, weight_bytes=wbytes,
-                weight_GBps=wbytes / per / 1e9, frac_of_peak_hbm_weights=wbytes / per / PEAK_HBM)
+                weight_GBps=wbytes / per / 1e9, frac_of_peak_hbm_weights=wbytes / per / PEAK_HBM,
+                frac_of_binding_roofline=binding / per, frac_of_measured_mfma=flops / per / MFMA_MEASURED)
 
 
 def chain_section(args, torch, m, gd, gi):
@@ -380,15 +426,18 @@ def main() -> int:
         return 0
 
     if args.only:
-        fn = {"decode": decode_section, "prefill": prefill_section, "chain": chain_section}[args.only]
+        fn = {"decode": decode_section, "prefill": prefill_section, "chain": chain_section,
+              "verify": verify_section}[args.only]
         res = fn(args, torch, m, gd, gi)
         if isinstance(res, dict):
             res.pop("db", None)
         print(json.dumps({"section": args.only, "result": res}), flush=True)
         return 0
 
+    ceiling = read_ceiling(torch)
     dec = decode_section(args, torch, m, gd, gi)
     cfg = gi.CONFIGS["decode1"]
+    verify = None if args.no_verify else verify_section(args, torch, m, gd, gi)
     prefill = None if args.no_prefill else prefill_section(args, torch, m, gd, gi)
     chain = None if args.no_chain else chain_section(args, torch, m, gd, gi)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec["db"], gi)
@@ -422,6 +471,8 @@ def main() -> int:
                         "avg_us": round(dec["down_us"], 2), "bytes_per_launch": dec["down_bytes"],
                         "achieved_GBps": round(dec["down_bytes"] / dec["down_us"] / 1e3, 1)},
         "cpu_baseline": cpu,
+        "measured_read_ceiling_GBps": round(ceiling["read_GBps"], 1),
+        "verify16": verify,
         "prefill4096": prefill,
         "chain40": chain,
     }
