@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace moe {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -12,6 +14,8 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef int int4_t __attribute__((ext_vector_type(4)));
 typedef int int8_t_v __attribute__((ext_vector_type(8)));
 typedef unsigned uint4_t __attribute__((ext_vector_type(4)));
+typedef int i8v __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 
@@ -130,6 +134,125 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 __device__ __forceinline__ float lane_value(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// ---- buffer-resource loads ---------------------------------------------------------
+//
+// A wave-uniform base and byte range; an offset past the range reads zeros.
+// Rows beyond a bucket's end get such an offset, so every load of the K loop
+// is issued unconditionally and the compiler can count the loads in flight
+// exactly (a load behind a branch makes it wait for all of them).
+
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw 32-bit access, range-checked
+constexpr uint32_t kOob = 0x80000000u;         // an offset past every range used here
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), (int)kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4_t bload16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+__device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v[0], v[1]);
+}
+
+// Rows 0-15 (P) and 16-31 (Q) as loaded, 16-lane groups [b0 b1 b2 b3] of 16
+// rows each  ->  K-step 0 = [P.b0 Q.b0 P.b1 Q.b1], K-step 1 = [P.b2 Q.b2 P.b3 Q.b3]
+// (lane l: row l%32, block 2s + l/32).
+__device__ __forceinline__ void b_operands(const uint4_t& P, const uint4_t& Q, i8v& s0, i8v& s1) {
+  uint32_t o0[4], o1[4];
+  const uint32_t p[4] = {P.x, P.y, P.z, P.w}, q[4] = {Q.x, Q.y, Q.z, Q.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const auto t = __builtin_amdgcn_permlane16_swap(p[d], q[d], false, false);   // [P0 Q0 P2 Q2], [P1 Q1 P3 Q3]
+    const auto u = __builtin_amdgcn_permlane32_swap(t[0], t[1], false, false);   // [P0 Q0 P1 Q1], [P2 Q2 P3 Q3]
+    o0[d] = u[0];
+    o1[d] = u[1];
+  }
+  s0 = i8v{(int)o0[0], (int)o0[1], (int)o0[2], (int)o0[3], 0, 0, 0, 0};
+  s1 = i8v{(int)o1[0], (int)o1[1], (int)o1[2], (int)o1[3], 0, 0, 0, 0};
+}
+
+// Words [cw0, cw0 + WIN) of ROWS scale-table rows, in two steps so that their
+// latency overlaps the first chunk loads of the K loop: issue() loads into
+// registers, store() writes the table.  row_off(r) is the byte offset of row
+// r's scale bytes (kOob for rows past the bucket).
+template <int ROWS, int NT, int WIN, int STRIDE>  // STRIDE: words per table row
+struct ScaleRows {
+  static constexpr int N = ROWS * WIN / NT;
+  static_assert(ROWS * WIN % NT == 0 && WIN < STRIDE, "table split");
+  uint32_t v[N];
+  template <typename RowOff>
+  __device__ __forceinline__ void issue(rsrc_t r, int cw0, int t, RowOff row_off) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = t + NT * i, row = idx / WIN, wd = idx - row * WIN;
+      const uint32_t o = row_off(row);
+      v[i] = bload4(r, o == kOob ? kOob : o + 4u * (uint32_t)(cw0 + wd));
+    }
+  }
+  __device__ __forceinline__ void store(uint32_t* tab, int t) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = t + NT * i, row = idx / WIN, wd = idx - row * WIN;
+      tab[row * STRIDE + wd] = v[i];
+    }
+  }
+};
+
+// Compact list of the non-empty buckets, built by wavefront 0 into LDS.
+struct Buckets {
+  int n;
+  int expert[kMaxExperts];
+  int row0[kMaxExperts];
+  int cnt[kMaxExperts];
+};
+
+__device__ inline void build_buckets(const int32_t* __restrict__ offsets, int E, Buckets& b) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    constexpr int CH = kMaxExperts / 64;
+    int off[CH + 1];
+#pragma unroll
+    for (int i = 0; i <= CH; ++i) {
+      const int e = lane * CH + i;
+      off[i] = offsets[e < E ? e : E];
+    }
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) n += (lane * CH + i < E && off[i + 1] > off[i]) ? 1 : 0;
+    int incl = n;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    int pos = incl - n;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int e = lane * CH + i;
+      if (e < E && off[i + 1] > off[i]) {
+        b.expert[pos] = e;
+        b.row0[pos] = off[i];
+        b.cnt[pos] = off[i + 1] - off[i];
+        ++pos;
+      }
+    }
+    if (lane == 63) b.n = incl;
+  }
+  __syncthreads();
 }
 
 }  // namespace moe

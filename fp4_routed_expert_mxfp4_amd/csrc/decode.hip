@@ -1,4 +1,4 @@
-// Decode expert FFN over MXFP4 experts (gfx950): memory-bound GEMV pair.
+// One-token decode FFN over MXFP4 experts (gfx950): memory-bound GEMV pair.
 //
 // The weight rows of the routed experts -- e2m1 codes with one UE8M0 scale
 // per 32 weights, the checkpoint's own layout ("DeepSeek-V4.1-Flash on a
@@ -8,21 +8,16 @@
 // single-box DeepSeek v4.1 Flash runtime", "Conventions": prefill and decode
 // are separate arithmetic paths), so x stays bf16 and h stays fp32.
 //
-// Kernel 1 (gate/up + SwiGLU): one wavefront per weight row n of the bucket's
-//   expert; lane l owns K-blocks l, l+64, ... (32 weights = 16 code bytes =
-//   one scale each).  A block is decoded with v_cvt_scalef32_pk_bf16_fp4
-//   (exact: e2m1 has two significant bits) and reduced against x with
-//   v_dot2_f32_bf16 (bf16 x bf16 products are exact in fp32); the block sum
-//   is multiplied by its scale 2^(e-127) in fp32.  g and u of row n are then
-//   wave-reduced and h = silu(g) * u is written in fp32.
-// Kernel 2 (down): the same row walk over W_down with h in fp32; the e2m1
-//   codes are decoded to fp32 with v_cvt_scalef32_pk_f32_fp4 and the block
-//   sums use fp32 FMAs.  y_pair row p = t*k + j is written once.
+// A block of 32 codes is decoded with v_cvt_scalef32_pk_bf16_fp4 (exact:
+// e2m1 has two significant bits) and reduced against x with v_dot2_f32_bf16
+// (bf16 x bf16 products are exact in fp32); the block sum is multiplied by
+// its scale 2^(e-127) in fp32.  The down projection decodes to fp32
+// (v_cvt_scalef32_pk_f32_fp4) and sums with fp32 FMAs against h.
 //
-// Work items are (bucket, row tile); the workgroups walk them grid-stride so
-// a launch sized for the largest bucket count also serves fewer buckets.  A
-// bucket's tokens reuse the weight registers; a one-token bucket keeps its
-// activations in registers for the whole row walk.
+// These kernels serve one token (each bucket one row) at the model's shapes;
+// launch_decode sends every other shape and every batch of two or more tokens
+// to the bf16 MFMA kernels of decode_mt.hip.  The fused layer kernels below
+// also route in-kernel and combine in the down kernel.
 #include "common.cuh"
 #include "kernels.h"
 #include "route_core.cuh"
@@ -34,48 +29,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-// Compact list of the non-empty buckets, built by wavefront 0 into LDS.
-struct Buckets {
-  int n;
-  int expert[kMaxExperts];
-  int row0[kMaxExperts];
-  int cnt[kMaxExperts];
-};
-
-__device__ void build_buckets(const int32_t* __restrict__ offsets, int E, Buckets& b) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    constexpr int CH = kMaxExperts / 64;
-    int off[CH + 1];
-#pragma unroll
-    for (int i = 0; i <= CH; ++i) {
-      const int e = lane * CH + i;
-      off[i] = offsets[e < E ? e : E];
-    }
-    int n = 0;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) n += (lane * CH + i < E && off[i + 1] > off[i]) ? 1 : 0;
-    int incl = n;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
-    }
-    int pos = incl - n;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int e = lane * CH + i;
-      if (e < E && off[i + 1] > off[i]) {
-        b.expert[pos] = e;
-        b.row0[pos] = off[i];
-        b.cnt[pos] = off[i + 1] - off[i];
-        ++pos;
-      }
-    }
-    if (lane == 63) b.n = incl;
-  }
-  __syncthreads();
-}
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
@@ -123,161 +76,6 @@ __device__ __forceinline__ float block_dot_f32(const uint4& c, const float4_t (&
     acc = fmaf(w3.y, hb.w, acc);
   }
   return acc;
-}
-
-__device__ __forceinline__ void load_x_blocks(const uint16_t* xt, int NB, int lane, int jb,
-                                              uint4 (&xr)[4]) {
-  const int kb = lane + 64 * jb;
-  if (kb < NB) {
-    const uint4* p = reinterpret_cast<const uint4*>(xt + kb * 32);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xr[q] = p[q];
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xr[q] = make_uint4(0, 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void load_h_blocks(const float* hr, int NB, int lane, int jb, float4_t (&hv)[8]) {
-  const int kb = lane + 64 * jb;
-  if (kb < NB) {
-    const float4_t* p = reinterpret_cast<const float4_t*>(hr + kb * 32);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) hv[q] = p[q];
-  } else {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) hv[q] = float4_t{0.f, 0.f, 0.f, 0.f};
-  }
-}
-
-template <int JB>
-__global__ __launch_bounds__(kThreads) void gateup_kernel(const uint16_t* __restrict__ x, int k, int E,
-                                                          ExpertStore w, const int32_t* __restrict__ e2s,
-                                                          const int32_t* __restrict__ offsets,
-                                                          const int32_t* __restrict__ sorted_pair,
-                                                          float* __restrict__ h, int rows_per_wave,
-                                                          int tiles) {
-  __shared__ Buckets bk;
-  build_buckets(offsets, E, bk);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int H = w.H, I = w.I, NB = H / 32;
-  const size_t rowbytes = (size_t)H / 2;
-  const int nitems = bk.n * tiles;
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int b = item / tiles, tile = item - b * tiles;
-    const int expert = bk.expert[b], row0 = bk.row0[b], cnt = bk.cnt[b];
-    const int slot = e2s ? e2s[expert] : expert;
-    if (slot < 0 || slot >= w.num_slots) continue;  // the down kernel writes zero rows
-    const uint8_t* gc = w.wg + (size_t)slot * I * rowbytes;
-    const uint8_t* uc = w.wu + (size_t)slot * I * rowbytes;
-    const uint8_t* gs = w.sg + (size_t)slot * I * NB;
-    const uint8_t* us = w.su + (size_t)slot * I * NB;
-    const int n0 = (tile * kWaves + wave) * rows_per_wave;
-    const int n1 = min(n0 + rows_per_wave, I);
-    uint4 xr[JB][4];
-    const bool single = (cnt == 1);
-    if (single) {
-      const int t = sorted_pair[row0] / k;
-#pragma unroll
-      for (int j = 0; j < JB; ++j) load_x_blocks(x + (size_t)t * H, NB, lane, j, xr[j]);
-    }
-    for (int n = n0; n < n1; ++n) {
-      uint4 cg[JB], cu[JB];
-      float sg[JB], su[JB];
-#pragma unroll
-      for (int j = 0; j < JB; ++j) {
-        const int kb = lane + 64 * j;
-        if (kb < NB) {
-          cg[j] = ld16(gc + n * rowbytes + kb * 16);
-          cu[j] = ld16(uc + n * rowbytes + kb * 16);
-          sg[j] = ue8m0_to_f32(gs[(size_t)n * NB + kb]);
-          su[j] = ue8m0_to_f32(us[(size_t)n * NB + kb]);
-        } else {
-          cg[j] = cu[j] = make_uint4(0, 0, 0, 0);
-          sg[j] = su[j] = 0.f;
-        }
-      }
-      for (int r = 0; r < cnt; ++r) {
-        if (!single) {
-          const int t = sorted_pair[row0 + r] / k;
-#pragma unroll
-          for (int j = 0; j < JB; ++j) load_x_blocks(x + (size_t)t * H, NB, lane, j, xr[j]);
-        }
-        float ag = 0.f, au = 0.f;
-#pragma unroll
-        for (int j = 0; j < JB; ++j) {
-          ag = fmaf(block_dot_bf16(cg[j], xr[j]), sg[j], ag);
-          au = fmaf(block_dot_bf16(cu[j], xr[j]), su[j], au);
-        }
-        ag = wave_sum(ag);
-        au = wave_sum(au);
-        if (lane == 0) h[(size_t)(row0 + r) * I + n] = swiglu_f32(ag, au);
-      }
-    }
-  }
-}
-
-template <int JB>
-__global__ __launch_bounds__(kThreads) void down_kernel(int k, int E, ExpertStore w,
-                                                        const int32_t* __restrict__ e2s,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ sorted_pair,
-                                                        const float* __restrict__ h, float* __restrict__ y,
-                                                        int rows_per_wave, int tiles) {
-  __shared__ Buckets bk;
-  build_buckets(offsets, E, bk);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int H = w.H, I = w.I, NB = I / 32;
-  const size_t rowbytes = (size_t)I / 2;
-  const int nitems = bk.n * tiles;
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int b = item / tiles, tile = item - b * tiles;
-    const int expert = bk.expert[b], row0 = bk.row0[b], cnt = bk.cnt[b];
-    const int slot = e2s ? e2s[expert] : expert;
-    const int m0 = (tile * kWaves + wave) * rows_per_wave;
-    const int m1 = min(m0 + rows_per_wave, H);
-    if (slot < 0 || slot >= w.num_slots) {
-      for (int r = 0; r < cnt; ++r) {
-        const int p = sorted_pair[row0 + r];
-        for (int m = m0 + lane; m < m1; m += 64) y[(size_t)p * H + m] = 0.f;
-      }
-      continue;
-    }
-    const uint8_t* dc = w.wd + (size_t)slot * H * rowbytes;
-    const uint8_t* ds = w.sd + (size_t)slot * H * NB;
-    float4_t hv[JB][8];
-    const bool single = (cnt == 1);
-    if (single) {
-#pragma unroll
-      for (int j = 0; j < JB; ++j) load_h_blocks(h + (size_t)row0 * I, NB, lane, j, hv[j]);
-    }
-    for (int m = m0; m < m1; ++m) {
-      uint4 c[JB];
-      float s[JB];
-#pragma unroll
-      for (int j = 0; j < JB; ++j) {
-        const int kb = lane + 64 * j;
-        if (kb < NB) {
-          c[j] = ld16(dc + m * rowbytes + kb * 16);
-          s[j] = ue8m0_to_f32(ds[(size_t)m * NB + kb]);
-        } else {
-          c[j] = make_uint4(0, 0, 0, 0);
-          s[j] = 0.f;
-        }
-      }
-      for (int r = 0; r < cnt; ++r) {
-        if (!single) {
-#pragma unroll
-          for (int j = 0; j < JB; ++j) load_h_blocks(h + (size_t)(row0 + r) * I, NB, lane, j, hv[j]);
-        }
-        float acc = 0.f;
-#pragma unroll
-        for (int j = 0; j < JB; ++j) acc = fmaf(block_dot_f32(c[j], hv[j]), s[j], acc);
-        acc = wave_sum(acc);
-        if (lane == 0) y[(size_t)sorted_pair[row0 + r] * H + m] = acc;
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -715,30 +513,6 @@ __global__ __launch_bounds__(kFusedMaxK * 64) void fused_down_combine_kernel(
   }
 }
 
-template <int JB>
-hipError_t launch_gateup_jb(dim3 grid, const uint16_t* x, int k, int E, const ExpertStore& w,
-                            const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
-                            float* h, int rpw, int tiles, hipStream_t s) {
-  hipLaunchKernelGGL(gateup_kernel<JB>, grid, dim3(kThreads), 0, s, x, k, E, w, e2s, offsets,
-                     sorted_pair, h, rpw, tiles);
-  return hipGetLastError();
-}
-
-template <int JB>
-hipError_t launch_down_jb(dim3 grid, int k, int E, const ExpertStore& w, const int32_t* e2s,
-                          const int32_t* offsets, const int32_t* sorted_pair, const float* h, float* y,
-                          int rpw, int tiles, hipStream_t s) {
-  hipLaunchKernelGGL(down_kernel<JB>, grid, dim3(kThreads), 0, s, k, E, w, e2s, offsets, sorted_pair, h,
-                     y, rpw, tiles);
-  return hipGetLastError();
-}
-
-int pick_rows_per_wave(int rows, int nb_max, int target_waves) {
-  long total = (long)rows * nb_max;
-  int rpw = (int)((total + target_waves - 1) / target_waves);
-  return rpw < 1 ? 1 : (rpw > 64 ? 64 : rpw);
-}
-
 }  // namespace
 
 bool fused_decode_supported(int T, int k, int E, int H, int I) {
@@ -793,70 +567,34 @@ size_t decode_workspace_bytes(int T, int k, int I) {
 hipError_t launch_decode(const uint16_t* x, int T, int k, int E, const ExpertStore& w,
                          const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
                          float* y_pair, void* ws, int phase, hipStream_t s) {
-  const int P = T * k;
-  const int nb_max = P < E ? P : E;
+  const int J = w.H / 1024, NB2 = w.I / 32, M = NB2 / 64, tail = NB2 % 64;
+  const bool one_token_shape = T == 1 && w.H % 1024 == 0 && J >= 1 && J <= 6 && (tail == 0 || tail == 8) &&
+                               M <= 1 && (M > 0 || tail == 8);
+  if (!one_token_shape)  // both halves on the multi-token kernels (their h layout differs)
+    return launch_decode_mt(x, T, k, E, w, e2s, offsets, sorted_pair, y_pair, ws, phase, s);
   float* h = reinterpret_cast<float*>(ws);
-  const int target = 2048;  // wavefronts: ~8 per CU on 256 CUs
   const dim3 fast_grid(512);
-  hipError_t err = hipSuccess;
-
   if (phase != 2) {
-    const int J = w.H / 1024;
-    if (T == 1 && w.H % 1024 == 0 && J >= 1 && J <= 6 && w.I % 2 == 0) {
-#define MOE_GU(JJ)                                                                                 \
-  case JJ:                                                                                         \
+#define MOE_GU(JJ)                                                                                    \
+  case JJ:                                                                                            \
     hipLaunchKernelGGL((gateup_fast_kernel<JJ, 2>), fast_grid, dim3(kThreads), 0, s, x, k, E, w, e2s, \
-                       offsets, sorted_pair, h);                                                   \
+                       offsets, sorted_pair, h);                                                      \
     break;
-      switch (J) { MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5) MOE_GU(6) }
+    switch (J) { MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5) MOE_GU(6) }
 #undef MOE_GU
-      err = hipGetLastError();
-    } else {
-      const int jb1 = (w.H / 32 + 63) / 64;
-      const int rpw = pick_rows_per_wave(w.I, nb_max, target);
-      const int tiles = (w.I + kWaves * rpw - 1) / (kWaves * rpw);
-      const long items = (long)tiles * nb_max;
-      const dim3 grid((unsigned)(items < 4096 ? items : 4096));
-      switch (jb1) {
-        case 1: err = launch_gateup_jb<1>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-        case 2: err = launch_gateup_jb<2>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-        case 3: err = launch_gateup_jb<3>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-        case 4: err = launch_gateup_jb<4>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-        case 5: err = launch_gateup_jb<5>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-        case 6: err = launch_gateup_jb<6>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-        case 7: err = launch_gateup_jb<7>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-        case 8: err = launch_gateup_jb<8>(grid, x, k, E, w, e2s, offsets, sorted_pair, h, rpw, tiles, s); break;
-        default: return hipErrorInvalidValue;
-      }
-    }
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess || phase == 1) return err;
   }
-  if (err != hipSuccess || phase == 1) return err;
-
-  const int NB2 = w.I / 32, M = NB2 / 64, tail = NB2 % 64;
-  if (T == 1 && (tail == 0 || tail == 8) && M <= 1 && (M > 0 || tail == 8)) {
 #define MOE_DN(MM, TT)                                                                                  \
   hipLaunchKernelGGL((down_fast_kernel<MM, TT>), fast_grid, dim3(kThreads), 0, s, k, E, w, e2s, offsets, \
                      sorted_pair, h, y_pair)
-    if (tail == 8) {
-      if (M == 0) { MOE_DN(0, true); } else { MOE_DN(1, true); }
-    } else {
-      MOE_DN(1, false);
-    }
+  if (tail == 8) {
+    if (M == 0) { MOE_DN(0, true); } else { MOE_DN(1, true); }
+  } else {
+    MOE_DN(1, false);
+  }
 #undef MOE_DN
-    return hipGetLastError();
-  }
-  const int jb2 = (NB2 + 63) / 64;
-  const int rpw = pick_rows_per_wave(w.H, nb_max, target);
-  const int tiles = (w.H + kWaves * rpw - 1) / (kWaves * rpw);
-  const long items = (long)tiles * nb_max;
-  const dim3 grid((unsigned)(items < 4096 ? items : 4096));
-  switch (jb2) {
-    case 1: return launch_down_jb<1>(grid, k, E, w, e2s, offsets, sorted_pair, h, y_pair, rpw, tiles, s);
-    case 2: return launch_down_jb<2>(grid, k, E, w, e2s, offsets, sorted_pair, h, y_pair, rpw, tiles, s);
-    case 3: return launch_down_jb<3>(grid, k, E, w, e2s, offsets, sorted_pair, h, y_pair, rpw, tiles, s);
-    case 4: return launch_down_jb<4>(grid, k, E, w, e2s, offsets, sorted_pair, h, y_pair, rpw, tiles, s);
-    default: return hipErrorInvalidValue;
-  }
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -1,0 +1,365 @@
+// Multi-token decode FFN over MXFP4 experts on gfx950 bf16 MFMA.
+//
+// Decode with more than one token (a small decode batch, the draft tokens a
+// speculative step verifies) keeps the decode arithmetic: x stays bf16 and h
+// keeps the precision of fp32, as the one-token kernels do ("Fast single-box
+// DeepSeek v4.1 Flash runtime", "Conventions": decode is judged against
+// unquantised activations).  A bucket -- the rows routed to one expert, at
+// most one per token -- is a skinny GEMM, so groups of 16 of its rows are the
+// M dimension of V_MFMA_F32_16X16X32_BF16 and 16 weight rows its N dimension:
+//
+//  * weights: e2m1 codes decoded to bf16 with the block's UE8M0 scale folded
+//    in (v_cvt_scalef32_pk_bf16_fp4).  Exact while the scaled value is a
+//    normal bf16 (block scales of 2^-125 and up): an e2m1 value has two
+//    significant bits and the scale is a power of two.
+//  * x: bf16 as given; every product is exact in fp32 and the MFMA sums in fp32.
+//  * h: silu(g) * u is stored as two bf16 planes, hi = rne(h) and
+//    lo = rne(h - hi); the down projection multiplies both (two MFMAs per
+//    K-step), so h enters it with a relative error of at most 2^-18.
+//
+// Kernel G (gate/up): a unit is (bucket, group of 16 bucket rows, 32 h
+//   columns): one A fragment (the rows' x, rows past the bucket's end read as
+//   zeros) against four B fragments (16 gate rows, 16 more, and the same rows
+//   of W_up).
+// Kernel D (down): a unit is (bucket, group of 16 rows, 64 output columns):
+//   A = the rows' h planes, B = four fragments of 16 W_down rows; y_pair rows
+//   are written once.
+//
+// A unit belongs to one workgroup; its four wavefronts take fixed quarters of
+// K and add their partial sums in LDS in wavefront order.  A row's result is
+// therefore one fixed fp32 expression of its own inputs: bit-identical
+// whichever other rows share its bucket and batch.
+//
+// K runs in chunks of 128 (four 32-blocks).  A B fragment is one 16-byte load
+// per lane -- lane l: block 4c + l/16 of row l%16, so 16 rows x 64 contiguous
+// bytes -- which is already the MFMA's operand order: K-step t takes dword t
+// (codes 8t..8t+7) of that block, and A's lane the same 8 values of x (or h)
+// of its row.  The scale bytes of a window of chunks are read once per
+// wavefront into an LDS table (contiguous row reads); the next chunk's loads
+// are in flight while one is multiplied.  The workgroups are persistent and
+// walk the units grid-stride.
+#include "common.cuh"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+constexpr int kMtThreads = 256;   // four wavefronts: the four quarters of a unit's K
+constexpr int kMtGridGU = 768;    // persistent workgroups of the gate/up kernel (three per CU)
+constexpr int kMtGridDN = 512;    // and of the down kernel (two per CU)
+constexpr int kMtWin = 20;        // chunks per scale window (80 blocks)
+constexpr int kMtW = kMtWin + 1;  // words per table row (odd: 16 rows hit 16 banks)
+constexpr int kMtRows = 16;       // bucket rows per unit (the MFMA's M)
+constexpr int kMtFrags = 4;       // 16-row weight fragments per unit
+
+// The bucket list and, per bucket, the prefix of its groups of kMtRows rows: bucket b
+// owns units [tiles * G[b], tiles * G[b+1]), its groups of one column tile
+// adjacent (they read the same weights).
+struct MtPlan {
+  Buckets bk;
+  int G[kMaxExperts + 1];
+
+  __device__ void build(const int32_t* __restrict__ offsets, int E) {
+    build_buckets(offsets, E, bk);
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x, n = bk.n;
+      constexpr int CH = kMaxExperts / 64;
+      int v[CH], s = 0;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int b = lane * CH + i;
+        v[i] = b < n ? (bk.cnt[b] + kMtRows - 1) / kMtRows : 0;
+        s += v[i];
+      }
+      int incl = s;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+      }
+      int pos = incl - s;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        G[lane * CH + i] = pos;
+        pos += v[i];
+      }
+      if (lane == 63) G[kMaxExperts] = incl;
+    }
+    __syncthreads();
+  }
+
+  __device__ int groups() const { return G[kMaxExperts]; }
+
+  // unit u -> bucket b, row group mg, column tile q
+  __device__ void locate(int u, int tiles, int& b, int& mg, int& q) const {
+    const int gi = u / tiles;
+    int lo = 0, hi = bk.n;  // G[lo] <= gi < G[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (G[mid] <= gi) lo = mid; else hi = mid;
+    }
+    b = lo;
+    const int ng = G[b + 1] - G[b], local = u - tiles * G[b];
+    q = local / ng;
+    mg = local - q * ng;
+  }
+};
+
+// Eight e2m1 codes (one dword, code 2i in the low nibble of byte i) times the
+// block scale, as eight bf16.
+__device__ __forceinline__ bf16x8_t dq8(uint32_t w, float s) {
+  const uint4_t u = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3))};
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// One chunk of one unit: A (per plane the lane's 64 B of block 4c+g) and the
+// four B fragments (lane: 16 B = block 4c+g of row l%16).
+template <int PLANES>
+struct MtRegs {
+  uint4_t a[PLANES][4];  // [plane][K-step]
+  uint4_t b[kMtFrags];   // [fragment]
+};
+
+template <int PLANES>
+struct MtSrc {
+  rsrc_t ra, rb[kMtFrags];
+  uint32_t va;              // the lane's A row + 64 * g (kOob past the bucket's end)
+  uint32_t plane;           // byte distance of the A planes
+  uint32_t vb[kMtFrags];    // fragment row (lane%16) + 16 * g
+  // chunk c; with ok false every offset is past its range and the registers read zeros
+  __device__ __forceinline__ void load(int c, bool ok, MtRegs<PLANES>& r) const {
+    const uint32_t off = ok ? 0u : kOob;  // real offsets stay below 2^31
+#pragma unroll
+    for (int p = 0; p < PLANES; ++p)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) r.a[p][t] = bload16(ra, (va + p * plane + (uint32_t)c * 256u + 16u * t) | off);
+#pragma unroll
+    for (int f = 0; f < kMtFrags; ++f) r.b[f] = bload16(rb[f], (vb[f] + (uint32_t)c * 64u) | off);
+  }
+};
+
+// One chunk of MFMAs: 4 K-steps x 4 fragments x PLANES.  The lane's scale is
+// byte g of its row's table word for the chunk.
+template <int PLANES>
+__device__ __forceinline__ void mt_mma(const MtRegs<PLANES>& r, f4v (&acc)[kMtFrags], const uint32_t* tab, int cw,
+                                       int q16, int g) {
+  float sc[kMtFrags];
+#pragma unroll
+  for (int f = 0; f < kMtFrags; ++f) sc[f] = ue8m0_to_f32((tab[(16 * f + q16) * kMtW + cw] >> (8 * g)) & 0xFFu);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int f = 0; f < kMtFrags; ++f) {
+      const bf16x8_t bw = dq8(r.b[f][t], sc[f]);
+#pragma unroll
+      for (int p = 0; p < PLANES; ++p)
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.a[p][t]), bw, acc[f], 0, 0, 0);
+    }
+}
+
+// The chunks [cb, ce) of one unit: windows of kMtWin chunks; in a window the
+// next chunk's loads are in flight while one is multiplied, the two register
+// sets alternating.  A load past the window's last chunk reads zeros (its
+// offsets are out of range) and is multiplied like any other, so neither the
+// loads nor the MFMAs sit behind a branch.  tables(cw0, ts) issues the scale
+// loads of the window starting at chunk cw0 (table row 16f + r: row r of
+// fragment f).
+template <int PLANES, typename Tables>
+__device__ __forceinline__ void mt_k_loop(const MtSrc<PLANES>& src, f4v (&acc)[kMtFrags], int cb, int ce,
+                                          uint32_t* tab, Tables tables) {
+  const int lane = __lane_id(), q16 = lane & 15, g = lane >> 4;
+  for (int cw0 = cb; cw0 < ce; cw0 += kMtWin) {
+    const int last = min(cw0 + kMtWin, ce) - 1;
+    ScaleRows<32, 64, kMtWin, kMtW> ts[2];
+    tables(cw0, ts);
+    MtRegs<PLANES> r0, r1;
+    src.load(cw0, true, r0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) ts[t].store(tab + 32 * t * kMtW, lane);
+    __builtin_amdgcn_wave_barrier();  // a wavefront's LDS accesses complete in order
+    for (int c = cw0; c <= last; c += 2) {
+      src.load(min(c + 1, last), c + 1 <= last, r1);
+      __builtin_amdgcn_sched_barrier(0);  // all of the next chunk's loads go out before these MFMAs
+      mt_mma(r0, acc, tab, c - cw0, q16, g);
+      src.load(min(c + 2, last), c + 2 <= last, r0);
+      __builtin_amdgcn_sched_barrier(0);
+      mt_mma(r1, acc, tab, min(c + 1, last) - cw0, q16, g);  // zeros past the window's end
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// The four wavefronts of a workgroup take fixed quarters of a unit's K
+// (chunks [w*nch/4, (w+1)*nch/4)); their partial sums meet in LDS and are
+// added in wavefront order, so every output is the same fp32 expression
+// whatever the batch around it.  part: the wavefront's own table area, free
+// once its K loop is done.
+__device__ __forceinline__ void mt_part_store(float* part, const f4v (&acc)[kMtFrags], int lane) {
+#pragma unroll
+  for (int f = 0; f < kMtFrags; ++f)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) part[(4 * f + v) * 64 + lane] = acc[f][v];
+}
+
+// fragment f, accumulator v of the whole unit: partial 0 + 1 + 2 + 3
+__device__ __forceinline__ float mt_part_sum(const uint32_t (*tabs)[64 * kMtW], int f, int v, int lane) {
+  const int i = (4 * f + v) * 64 + lane;
+  float s = __uint_as_float(tabs[0][i]);
+#pragma unroll
+  for (int w = 1; w < 4; ++w) s += __uint_as_float(tabs[w][i]);
+  return s;
+}
+
+__device__ __forceinline__ uint16_t bf16_lo_part(float v, uint16_t hi) {
+  const float hf = bf16_bits_to_f32(hi);
+  return fabsf(hf) <= 3.4028234663852886e38f ? f32_to_bf16_rne(v - hf) : (uint16_t)0;
+}
+
+__global__ __launch_bounds__(kMtThreads, 3) void gateup_mt_kernel(
+    const uint16_t* __restrict__ x, uint32_t x_bytes, int k, int E, ExpertStore w, const int32_t* __restrict__ e2s,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, uint16_t* __restrict__ hpl,
+    int P) {
+  __shared__ MtPlan pl;
+  __shared__ uint32_t tabs[4][64 * kMtW];
+  pl.build(offsets, E);
+  const int H = w.H, I = w.I, NB = H / 32, tiles = I / 32, nch = H / 128;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, q16 = lane & 15, g = lane >> 4;
+  const int cb = wid * nch / 4, ce = (wid + 1) * nch / 4;
+  const uint32_t wrow = (uint32_t)H / 2u;
+  const size_t mat = (size_t)I * wrow, smat = (size_t)I * NB, lo_plane = (size_t)P * I;
+  const int units = tiles * pl.groups();
+  uint32_t* tab = tabs[wid];
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    int b, mg, q;
+    pl.locate(u, tiles, b, mg, q);
+    const int expert = pl.bk.expert[b], row0 = pl.bk.row0[b], cnt = pl.bk.cnt[b];
+    const int slot = e2s ? e2s[expert] : expert;
+    if (slot < 0 || slot >= w.num_slots) continue;  // the down kernel writes zero rows
+    const int rr = kMtRows * mg + q16;
+    const int tok = rr < cnt ? sorted_pair[row0 + rr] / k : -1;
+    MtSrc<1> src;
+    src.ra = make_rsrc(x, x_bytes);
+    src.va = tok >= 0 ? (uint32_t)tok * (uint32_t)H * 2u + 64u * g : kOob;
+    src.plane = 0;
+    const rsrc_t gr = make_rsrc(w.wg + (size_t)slot * mat, (uint32_t)mat);
+    const rsrc_t ur = make_rsrc(w.wu + (size_t)slot * mat, (uint32_t)mat);
+#pragma unroll
+    for (int f = 0; f < kMtFrags; ++f) {  // fragments 0, 1: gate rows; 2, 3: the same up rows
+      src.rb[f] = f < 2 ? gr : ur;
+      src.vb[f] = (uint32_t)(32 * q + 16 * (f & 1) + q16) * wrow + 16u * (uint32_t)g;
+    }
+    const rsrc_t sgr = make_rsrc(w.sg + (size_t)slot * smat, (uint32_t)smat);
+    const rsrc_t sur = make_rsrc(w.su + (size_t)slot * smat, (uint32_t)smat);
+    auto tables = [&](int cw0, ScaleRows<32, 64, kMtWin, kMtW> (&ts)[2]) {
+      ts[0].issue(sgr, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NB; });
+      ts[1].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NB; });
+    };
+    f4v acc[kMtFrags] = {};
+    mt_k_loop(src, acc, cb, ce, tab, tables);
+    __builtin_amdgcn_wave_barrier();
+    mt_part_store(reinterpret_cast<float*>(tab), acc, lane);
+    __syncthreads();
+    // wavefront f < 2: h columns 32q + 16f + q16 (gate fragment f, up fragment f + 2);
+    // accumulator v: bucket row 16mg + 4g + v
+    if (wid < 2) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = kMtRows * mg + 4 * g + v;
+        const float gv = mt_part_sum(tabs, wid, v, lane), uv = mt_part_sum(tabs, wid + 2, v, lane);
+        if (row < cnt) {
+          const float hv = swiglu_f32(gv, uv);
+          const uint16_t hi = f32_to_bf16_rne(hv);
+          const size_t o = (size_t)(row0 + row) * I + 32 * q + 16 * wid + q16;
+          hpl[o] = hi;
+          hpl[lo_plane + o] = bf16_lo_part(hv, hi);
+        }
+      }
+    }
+    __syncthreads();  // the partials are read before the next unit's tables overwrite them
+  }
+}
+
+__global__ __launch_bounds__(kMtThreads, 2) void down_mt_kernel(
+    const uint16_t* __restrict__ hpl, int P, int E, ExpertStore w, const int32_t* __restrict__ e2s,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, float* __restrict__ y) {
+  __shared__ MtPlan pl;
+  __shared__ uint32_t tabs[4][64 * kMtW];
+  pl.build(offsets, E);
+  const int H = w.H, I = w.I, NB = I / 32, tiles = H / 64, nch = I / 128;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, q16 = lane & 15, g = lane >> 4;
+  const int cb = wid * nch / 4, ce = (wid + 1) * nch / 4;
+  const uint32_t wrow = (uint32_t)I / 2u;
+  const size_t mat = (size_t)H * wrow, smat = (size_t)H * NB;
+  const int units = tiles * pl.groups();
+  uint32_t* tab = tabs[wid];
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    int b, mg, q;
+    pl.locate(u, tiles, b, mg, q);
+    const int expert = pl.bk.expert[b], row0 = pl.bk.row0[b], cnt = pl.bk.cnt[b];
+    const int slot = e2s ? e2s[expert] : expert;
+    const int n0 = 64 * q;
+    if (slot < 0 || slot >= w.num_slots) {  // no stored expert: its rows are zero
+      for (int r = kMtRows * mg + wid; r < min(cnt, kMtRows * (mg + 1)); r += 4)
+        y[(size_t)sorted_pair[row0 + r] * H + n0 + lane] = 0.f;
+      continue;
+    }
+    const int rr = kMtRows * mg + q16;
+    MtSrc<2> src;
+    src.ra = make_rsrc(hpl, (uint32_t)((size_t)P * I * 4));
+    src.va = rr < cnt ? (uint32_t)(row0 + rr) * (uint32_t)I * 2u + 64u * g : kOob;
+    src.plane = (uint32_t)((size_t)P * I * 2);
+    const rsrc_t rc = make_rsrc(w.wd + (size_t)slot * mat, (uint32_t)mat);
+#pragma unroll
+    for (int f = 0; f < kMtFrags; ++f) {
+      src.rb[f] = rc;
+      src.vb[f] = (uint32_t)(n0 + 16 * f + q16) * wrow + 16u * (uint32_t)g;
+    }
+    const rsrc_t sdr = make_rsrc(w.sd + (size_t)slot * smat, (uint32_t)smat);
+    auto tables = [&](int cw0, ScaleRows<32, 64, kMtWin, kMtW> (&ts)[2]) {
+      ts[0].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + r) * NB; });
+      ts[1].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + 32 + r) * NB; });
+    };
+    f4v acc[kMtFrags] = {};
+    mt_k_loop(src, acc, cb, ce, tab, tables);
+    __builtin_amdgcn_wave_barrier();
+    mt_part_store(reinterpret_cast<float*>(tab), acc, lane);
+    __syncthreads();
+    // wavefront f: output columns n0 + 16f + q16; accumulator v: bucket row 16mg + 4g + v
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = kMtRows * mg + 4 * g + v;
+      const float yv = mt_part_sum(tabs, wid, v, lane);
+      if (row < cnt) y[(size_t)sorted_pair[row0 + row] * H + n0 + 16 * wid + q16] = yv;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_mt(const uint16_t* x, int T, int k, int E, const ExpertStore& w, const int32_t* e2s,
+                            const int32_t* offsets, const int32_t* sorted_pair, float* y_pair, void* ws, int phase,
+                            hipStream_t s) {
+  const int P = T * k;
+  uint16_t* hpl = reinterpret_cast<uint16_t*>(ws);
+  if (phase != 2) {
+    hipLaunchKernelGGL(gateup_mt_kernel, dim3(kMtGridGU), dim3(kMtThreads), 0, s, x,
+                       (uint32_t)((size_t)T * w.H * 2), k, E, w, e2s, offsets, sorted_pair, hpl, P);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess || phase == 1) return err;
+  }
+  hipLaunchKernelGGL(down_mt_kernel, dim3(kMtGridDN), dim3(kMtThreads), 0, s, hpl, P, E, w, e2s, offsets,
+                     sorted_pair, y_pair);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -23,12 +23,18 @@ size_t permute_workspace_bytes(int P, int E);
 hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pair,
                           int32_t* pair_to_row, void* ws, hipStream_t s);
 
-// Decode FFN: gate/up + SwiGLU into h (fp32, sorted-row order), then down.
+// Decode FFN: gate/up + SwiGLU into h (sorted-row order, in ws), then down.
 size_t decode_workspace_bytes(int T, int k, int I);
 // phase: 0 both kernels, 1 gate/up only, 2 down only.
 hipError_t launch_decode(const uint16_t* x, int T, int k, int E, const ExpertStore& w,
                          const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
                          float* y_pair, void* ws, int phase, hipStream_t s);
+
+// Multi-token decode FFN (bf16 MFMA); launch_decode uses it for every shape
+// the one-token kernels do not cover.  ws holds h as bf16 hi and lo planes.
+hipError_t launch_decode_mt(const uint16_t* x, int T, int k, int E, const ExpertStore& w, const int32_t* e2s,
+                            const int32_t* offsets, const int32_t* sorted_pair, float* y_pair, void* ws, int phase,
+                            hipStream_t s);
 
 // Fused one-token decode layer (route + gate/up, then down + combine).
 bool fused_decode_supported(int T, int k, int E, int H, int I);

@@ -32,8 +32,6 @@ namespace {
 
 constexpr int kPT = 256;  // threads per workgroup
 
-typedef int i8v __attribute__((ext_vector_type(8)));
-typedef float f16v __attribute__((ext_vector_type(16)));
 
 // ---- MXFP6 (e2m3) quantiser, exact arithmetic -------------------------------
 
@@ -253,33 +251,8 @@ struct TileWalk {
   }
 };
 
-// ---- buffer-resource loads ---------------------------------------------------------
-//
-// A wave-uniform base and byte range; an offset past the range reads zeros.
-// Rows beyond a bucket's end get such an offset, so every load of the K loop
-// is issued unconditionally and the compiler can count the loads in flight
-// exactly (a load behind a branch makes it wait for all of them).
 
-constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw 32-bit access, range-checked
-constexpr uint32_t kOob = 0x80000000u;         // an offset past every range used here
-constexpr uint32_t kOpenRange = 0x7FFFFFF0u;   // range of the activation buffers (offsets < 2^31)
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
-                                           (int)__builtin_amdgcn_readfirstlane(bytes), (int)kRsrcWord3);
-}
-
-__device__ __forceinline__ uint4_t bload16(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
+constexpr uint32_t kOpenRange = 0x7FFFFFF0u;  // range of the activation buffers (offsets < 2^31)
 
 // ---- the grouped GEMM core ---------------------------------------------------------
 //
@@ -323,40 +296,15 @@ struct GemmSmem {
   int rowtok[BM];
 };
 
-// Words [cw0, cw0 + SCWIN) of ROWS table rows, in two steps so that their
-// latency overlaps the first chunk loads of the K loop: issue() loads into
-// registers, store() writes the table.  row_off(r) is the byte offset of row
-// r's scale bytes (kOob for rows past the bucket).
-template <int ROWS, int NT, int WIN, int STRIDE = SCW>  // STRIDE: words per table row
-struct ScaleRows {
-  static constexpr int N = ROWS * WIN / NT;
-  static_assert(ROWS * WIN % NT == 0 && WIN <= SCWIN, "table split");
-  uint32_t v[N];
-  template <typename RowOff>
-  __device__ __forceinline__ void issue(rsrc_t r, int cw0, int t, RowOff row_off) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = t + NT * i, row = idx / WIN, wd = idx - row * WIN;
-      const uint32_t o = row_off(row);
-      v[i] = bload4(r, o == kOob ? kOob : o + 4u * (uint32_t)(cw0 + wd));
-    }
-  }
-  __device__ __forceinline__ void store(uint32_t* tab, int t) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = t + NT * i, row = idx / WIN, wd = idx - row * WIN;
-      tab[row * STRIDE + wd] = v[i];
-    }
-  }
-};
 
 // The scale tables of one tile for a window of WIN chunks: A rows (all
 // threads) and each wavefront's two 32-row weight fragments.
 template <int WIN>
 struct TileScales {
   static constexpr int kWin = WIN;
-  ScaleRows<BM, kPT, WIN> a;
-  ScaleRows<32, 64, WIN> b[2];
+  static_assert(WIN <= SCWIN, "scale window");
+  ScaleRows<BM, kPT, WIN, SCW> a;
+  ScaleRows<32, 64, WIN, SCW> b[2];
 };
 
 // Registers of one A chunk between its global loads and its LDS store.  The
@@ -434,22 +382,6 @@ struct BSrc {
   }
 };
 
-// Rows 0-15 (P) and 16-31 (Q) as loaded, 16-lane groups [b0 b1 b2 b3] of 16
-// rows each  ->  K-step 0 = [P.b0 Q.b0 P.b1 Q.b1], K-step 1 = [P.b2 Q.b2 P.b3 Q.b3]
-// (lane l: row l%32, block 2s + l/32).
-__device__ __forceinline__ void b_operands(const uint4_t& P, const uint4_t& Q, i8v& s0, i8v& s1) {
-  uint32_t o0[4], o1[4];
-  const uint32_t p[4] = {P.x, P.y, P.z, P.w}, q[4] = {Q.x, Q.y, Q.z, Q.w};
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const auto t = __builtin_amdgcn_permlane16_swap(p[d], q[d], false, false);   // [P0 Q0 P2 Q2], [P1 Q1 P3 Q3]
-    const auto u = __builtin_amdgcn_permlane32_swap(t[0], t[1], false, false);   // [P0 Q0 P1 Q1], [P2 Q2 P3 Q3]
-    o0[d] = u[0];
-    o1[d] = u[1];
-  }
-  s0 = i8v{(int)o0[0], (int)o0[1], (int)o0[2], (int)o0[3], 0, 0, 0, 0};
-  s1 = i8v{(int)o1[0], (int)o1[1], (int)o1[2], (int)o1[3], 0, 0, 0, 0};
-}
 
 // One chunk of MFMAs: A fragments from LDS (48 B per lane = both K-steps),
 // B from registers.  With an empty chunk (nks == 0) nothing is multiplied.
@@ -550,10 +482,6 @@ __device__ __forceinline__ void gemm_k_loop(GemmSmem& sm, f16v (&acc)[4][2], con
 // memory into registers in MFMA order, in batches of four K-steps with the next
 // batch in flight, and many wavefronts per CU keep the HBM stream full.
 
-__device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-  return make_uint2(v[0], v[1]);
-}
 
 // Four K-steps (two 128-K chunks) of one wavefront: A block 2s+h of row r32
 // (24 B); each B fragment's rows as two halves of 16 rows x 64 B per chunk

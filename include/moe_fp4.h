@@ -142,8 +142,12 @@ MOE_FP4_API moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k
  *   g = W_gate[e] . x_t,  u = W_up[e] . x_t,  h = silu(g) * u  (fp32),
  *   y_pair[p] = W_down[e] . h                                  (fp32)
  * where W = e2m1(code) * 2^(scale-127) is decoded in registers.  x is used as
- * given (bf16, exact in fp32) and h stays fp32: this is the decode reference
- * arithmetic, judged against unquantised activations.
+ * given (bf16, exact in fp32) and h keeps fp32 precision: this is the decode
+ * reference arithmetic, judged against unquantised activations.  One token at
+ * hidden = 1024*J (J <= 6) with inter/32 = 64*M + 8*tail (M <= 1) runs on VALU
+ * dot products; every other call (two or more tokens, other shapes) on bf16
+ * MFMA with h carried as bf16 hi + lo (relative error <= 2^-18), where a
+ * token's rows are bit-identical whichever tokens share the batch.
  *   x_bf16         [T][hidden] bf16 bits (16-byte aligned)
  *   expert_to_slot [E] int32 (NULL: slot = expert id, needs num_slots >= E);
  *                  a bucket whose expert has no slot (-1 or >= num_slots)
@@ -164,7 +168,7 @@ MOE_FP4_API moe_status moe_ffn_fp4_decode(const uint16_t* x_bf16, int32_t T, int
 
 /* moe_ffn_fp4_decode_gateup, moe_ffn_fp4_decode_down -- the two kernels of
  * moe_ffn_fp4_decode as separate calls with the same arguments: gateup writes
- * h (fp32, sorted-row order) into the workspace, down reads it from there
+ * h (sorted-row order) into the workspace, down reads it from there
  * and writes y_pair.  gateup followed by down on one stream, with the same
  * workspace, is exactly moe_ffn_fp4_decode.  They let a caller time or
  * schedule the two weight streams separately. */

@@ -18,6 +18,10 @@ DECODE_CASES = {
     "mid_resident": gi.custom("mid_resident", 768, 256, 40, 3, 9, seed=22, resident=12),
     "decode1": gi.CONFIGS["decode1"],
     "verify16": gi.CONFIGS["verify16"],
+    # buckets of more than 16 rows (several row groups), 3 chunks of K in the down projection
+    "groups40": gi.custom("groups40", 512, 384, 16, 4, 40, seed=23, zipf=1.1),
+    # the largest decode batch: 256 tokens, buckets of up to 256 rows
+    "batch256": gi.custom("batch256", 1024, 256, 8, 2, 256, seed=24),
 }
 
 
@@ -63,8 +67,12 @@ def test_decode_rotated_logits_full_size():
 
 
 def test_decode_deterministic_and_batch_consistent():
-    """Byte-identical reruns; a token's rows alone and inside a 16-token batch agree
-    (to fp32 rounding: the one-token kernels sum in a different order)."""
+    """Byte-identical reruns; a token's rows alone (the one-token kernels: VALU dot
+    products in fp32) and inside the 16-token batch (the multi-token kernels: bf16
+    MFMA with h as bf16 hi + lo) agree to 1e-5 of max|y|.  The two paths round
+    differently, so they are not bit-identical: against the fp64 oracle the MFMA
+    path measures <= 3.5e-6 and the one-token path <= 2e-7 of max|y| on every
+    decode case, and 1e-5 leaves a margin of about three over their sum."""
     cfg = gi.CONFIGS["verify16"]
     gl = GpuLayer(cfg)
     a, b = gl.run("decode"), gl.run("decode")
@@ -77,7 +85,28 @@ def test_decode_deterministic_and_batch_consistent():
         y1 = m.moe_ffn_fp4_decode(gl.x[t:t + 1].contiguous(), cfg.k, cfg.E, gl.store, None, off, sp)
         torch.cuda.synchronize()
         ref = a["y_pair"][t * cfg.k:(t + 1) * cfg.k]
-        assert rel_err(to_np(y1), to_np(ref).astype(np.float64)) <= 1e-6, t
+        e = rel_err(to_np(y1), to_np(ref).astype(np.float64))
+        print(f"token {t}: alone vs in the batch {e:.2e}", flush=True)
+        assert e <= 1e-5, t
+
+
+def test_multi_token_batch_invariant_bit_exact():
+    """With two or more tokens every row is one MFMA dot-product chain over the same
+    K order, and the workgroup's K quarters are added in a fixed order: a token's
+    y_pair rows are bit-identical whichever other tokens share its batch."""
+    import fp4_routed_expert_mxfp4_amd as m
+    cfg = gi.CONFIGS["verify16"]
+    gl = GpuLayer(cfg)
+    full = gl.run("decode")["y_pair"]
+    k = cfg.k
+    for sel in ([0, 1], [15, 3], list(range(8)), [5, 9, 12, 2, 14]):
+        idx = torch.tensor(sel, device="cuda")
+        ids, w = m.moe_route(gl.logits[idx].contiguous(), k)
+        off, sp, _ = m.moe_permute(ids, cfg.E)
+        y = m.moe_ffn_fp4_decode(gl.x[idx].contiguous(), k, cfg.E, gl.store, None, off, sp)
+        torch.cuda.synchronize()
+        for i, t in enumerate(sel):
+            assert torch.equal(y[i * k:(i + 1) * k], full[t * k:(t + 1) * k]), (sel, t)
 
 
 def test_integer_exact_case_bit_identical():
