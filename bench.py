@@ -6,7 +6,9 @@ Headline (value): single-layer decode at batch 1 -- hidden 5120, expert width
 step (router, bucketing, decode FFN, combine), counting the algorithmic bytes
 (the 8 routed experts' codes and scales, x, logits, output).  Each step uses
 one of 64 logit sets in turn, so consecutive steps touch different experts
-and the 256 MB last-level cache cannot hold the weights between them.
+and the 256 MB last-level cache cannot hold the weights between them.  The
+timed steps are one HIP graph of back-to-back layer calls, as a decode token
+runs its layers; the same steps launched as one graph each are also reported.
 
 Also reported: the gate/up kernel against the HBM roofline (HIP events on its
 stream), the 4096-token prefill chunk (tokens/s of one layer) and the 40-layer
@@ -191,18 +193,30 @@ def decode_section(args, torch, m, gd, gi):
         db.step(s)
     torch.cuda.synchronize()
     touched = db.touched()
-    step_graphs = capture(torch, db.step, NSETS)
+    # the timed steps are one HIP graph of back-to-back layer calls, as a decode
+    # token runs its layers; step i uses routing i mod 64
     log("decode1: warmup")
-    time_graphs(torch, step_graphs, args.warmup)
+    warm = capture_many(torch, lambda i: db.step(i % NSETS), max(args.warmup, 1))
+    time_graphs(torch, [warm], 1)
+    del warm
     log(f"decode1: timing {args.steps} steps")
-    t = time_graphs(torch, step_graphs, args.steps)
+    timed = capture_many(torch, lambda i: db.step(i % NSETS), args.steps)
+    t = time_graphs(torch, [timed], 1)
+    del timed
     per_step_bytes = [layer_bytes(cfg, touched[i % NSETS], cfg.T) for i in range(args.steps)]
     gbps = sum(per_step_bytes) / t / 1e9
-    # for comparison: the four separate calls
-    sep_graphs = capture(torch, db.step_separate, NSETS)
-    time_graphs(torch, sep_graphs, 16)
-    sep_steps = min(args.steps, 512)
-    t_sep = time_graphs(torch, sep_graphs, sep_steps) / sep_steps
+    # for comparison: each step as its own graph launch (adds the launch gap)
+    step_graphs = capture(torch, db.step, NSETS)
+    time_graphs(torch, step_graphs, 16)
+    per_launch_steps = min(args.steps, 512)
+    t_launch = time_graphs(torch, step_graphs, per_launch_steps) / per_launch_steps
+    del step_graphs
+    # for comparison: the four separate calls, back to back in one graph
+    sep_graph = capture_many(torch, lambda i: db.step_separate(i % NSETS), NSETS)
+    time_graphs(torch, [sep_graph], 2)
+    sep_reps = max(1, min(args.steps, 512) // NSETS)
+    t_sep = time_graphs(torch, [sep_graph], sep_reps) / (sep_reps * NSETS)
+    del sep_graph
     # the gate/up kernel alone, then the down kernel alone: one graph of 64
     # back-to-back launches over the 64 routings, replayed; HIP events on the
     # replay stream bracket the whole timed region
@@ -219,8 +233,9 @@ def decode_section(args, torch, m, gd, gi):
     dn_bytes = cfg.k * (cfg.H * (cfg.I // 2 + cfg.I // 32)) + cfg.k * cfg.I * 4 + cfg.H * 2
     res = dict(seconds=t, gbps=gbps, ms_per_step=t / args.steps * 1e3, touched_mean=sum(touched) / NSETS,
                gateup_us=t_gu * 1e6, gateup_bytes=gu_bytes, down_us=t_dn * 1e6, down_bytes=dn_bytes,
-               separate_us=t_sep * 1e6, db=db)
-    log(f"decode1: {res['ms_per_step'] * 1e3:.1f} us/step, {gbps:.0f} GB/s (separate calls: {t_sep * 1e6:.1f} us); "
+               separate_us=t_sep * 1e6, graph_per_step_us=t_launch * 1e6, db=db)
+    log(f"decode1: {res['ms_per_step'] * 1e3:.1f} us/step, {gbps:.0f} GB/s (separate calls: {t_sep * 1e6:.1f} us; "
+        f"one graph launch per step: {t_launch * 1e6:.1f} us); "
         f"route+gate/up {t_gu * 1e6:.1f} us ({gu_bytes / t_gu / 1e9:.0f} GB/s), down+combine {t_dn * 1e6:.1f} us "
         f"({dn_bytes / t_dn / 1e9:.0f} GB/s)")
     return res
@@ -236,10 +251,11 @@ def verify_section(args, torch, m, gd, gi):
         db.step(s)
     torch.cuda.synchronize()
     touched = db.touched()
-    graphs = capture(torch, db.step, NSETS)
-    time_graphs(torch, graphs, 16)
     steps = max(NSETS, min(args.steps, 512))
-    t = time_graphs(torch, graphs, steps)
+    g = capture_many(torch, lambda i: db.step(i % NSETS), steps)  # back to back, as in decode1
+    time_graphs(torch, [g], 1)
+    t = time_graphs(torch, [g], 1)
+    del g
     nbytes = sum(layer_bytes(cfg, touched[i % NSETS], cfg.T) for i in range(steps))
     per = t / steps
     log(f"verify16: {per * 1e6:.1f} us/step, {nbytes / t / 1e9:.0f} GB/s, {sum(touched) / NSETS:.1f} experts/step")
@@ -247,24 +263,33 @@ def verify_section(args, torch, m, gd, gi):
                 frac_of_peak_hbm=nbytes / t / PEAK_HBM, experts_touched_mean=sum(touched) / NSETS)
 
 
-def read_ceiling(torch) -> dict:
-    """A measured streaming-read ceiling: torch's sum over 4 GiB resident in HBM."""
+def read_ceiling(torch, gd) -> dict:
+    """The measured streaming-read ceiling: the harness's probe kernel (every
+    wavefront 16 KiB contiguous per step, all loads in flight) over 4 GiB
+    resident in HBM, HIP events on its stream."""
     n = 4 << 30
-    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1).view(torch.float32)
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L = gd.lib()
+    stream = torch.cuda.current_stream()
+
+    def run():
+        assert L.gen_stream_read(a.data_ptr(), n, sink.data_ptr(), stream.cuda_stream) == 0
+
     for _ in range(2):
-        a.sum()
+        run()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 5
-    e0.record()
+    e0.record(stream)
     for _ in range(reps):
-        a.sum()
-    e1.record()
+        run()
+    e1.record(stream)
     torch.cuda.synchronize()
     t = e0.elapsed_time(e1) / 1e3 / reps
     del a
     torch.cuda.empty_cache()
-    log(f"read ceiling: {n / t / 1e9:.0f} GB/s (sum over 4 GiB)")
+    log(f"read ceiling: {n / t / 1e9:.0f} GB/s (streaming-read probe over 4 GiB)")
     return dict(bytes=n, us=t * 1e6, read_GBps=n / t / 1e9)
 
 
@@ -434,7 +459,7 @@ def main() -> int:
         print(json.dumps({"section": args.only, "result": res}), flush=True)
         return 0
 
-    ceiling = read_ceiling(torch)
+    ceiling = read_ceiling(torch, gd)
     dec = decode_section(args, torch, m, gd, gi)
     cfg = gi.CONFIGS["decode1"]
     verify = None if args.no_verify else verify_section(args, torch, m, gd, gi)
@@ -462,6 +487,7 @@ def main() -> int:
                    "weights": "e2m1 + UE8M0/32", "activations": "bf16"},
         "frac_of_peak_hbm": round(dec["gbps"] * 1e9 / PEAK_HBM, 4),
         "separate_calls_us_per_step": round(dec["separate_us"], 2),
+        "graph_launch_per_step_us": round(dec["graph_per_step_us"], 2),
         "roofline": {"kernel": "decode route + gate/up + SwiGLU (fused_gateup_kernel, moe_decode_layer_gateup)",
                      "bound": "hbm",
                      "achieved": round(gu_achieved / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",

@@ -1,7 +1,8 @@
 """Builds the gfx950 shared libraries in-tree with hipcc.
 
   fp4_routed_expert_mxfp4_amd/libmoe_fp4.so  the C-ABI MoE library (include/moe_fp4.h)
-  gen/libmoe_gen.so                          the device filler of the synthetic inputs
+  gen/libmoe_gen.so                          the device filler of the synthetic inputs and the
+                                             benchmark's streaming-read probe
 
 Every HIP translation unit is compiled with packed-fp32 instructions disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops).
@@ -57,7 +58,7 @@ def _link(objs: list[str], out: str) -> None:
 def build(jobs: int = 8) -> list[str]:
     os.makedirs(BUILD, exist_ok=True)
     moe_srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
-    gen_srcs = [os.path.join(ROOT, "gen", "fill.hip")]
+    gen_srcs = [os.path.join(ROOT, "gen", f) for f in ("fill.hip", "probe.hip")]
     units = [(s, os.path.join(BUILD, "moe_" + os.path.basename(s) + ".o")) for s in moe_srcs]
     units += [(s, os.path.join(BUILD, "gen_" + os.path.basename(s) + ".o")) for s in gen_srcs]
     with ThreadPoolExecutor(max_workers=jobs) as ex:

@@ -25,6 +25,8 @@ def lib() -> ctypes.CDLL:
         L.gen_fill_codes.argtypes = [vp, i64, vp, i32, u32, i32, i32, vp]
         L.gen_fill_scales.argtypes = [vp, i64, vp, i32, u32, i32, i32, i32, vp]
         L.gen_fill_codes.restype = L.gen_fill_scales.restype = ctypes.c_int
+        L.gen_stream_read.argtypes = [vp, i64, vp, vp]
+        L.gen_stream_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
