@@ -394,18 +394,15 @@ __device__ void fused_route(const float* __restrict__ logits, int E, int k, cons
   __syncthreads();
 }
 
-template <int NPL, int J>
-__global__ __launch_bounds__(kThreads, 2) void fused_gateup_kernel(
-    const float* __restrict__ logits, const uint16_t* __restrict__ x, int E, int k, const int32_t* __restrict__ e2s,
-    ExpertStore w, FusedRoute* __restrict__ pub, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
-    float* __restrict__ h) {
+// The gate/up work of the one-token layer: wavefront gw of total_waves takes
+// a contiguous range of R-row-pair batches of one bucket's expert and writes
+// h for those rows (bucket-major rows of h, I floats each).
+template <int J>
+__device__ __forceinline__ void fused_gateup_rows(const FusedRoute& fr, const uint16_t* __restrict__ x, int k,
+                                                  const ExpertStore& w, float* __restrict__ h, int gw,
+                                                  int total_waves, int lane) {
   constexpr int R = 2;
   constexpr int NB = 32 * J;
-  __shared__ FusedRoute fr;
-  fused_route<NPL>(logits, E, k, e2s, w.num_slots, fr, pub, topk_ids, topk_w);
-  const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int total_waves = gridDim.x * kWaves;
   const int I = w.I;
   const size_t rowbytes = (size_t)16 * NB;
   const int nbat = I / R;
@@ -427,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_gateup_kernel(
     const int bat0 = c * cs, bat1 = min(bat0 + cs, nbat);
     if (bat0 >= bat1) continue;
     const int slot = fr.slot[b];
-    if (slot < 0) continue;  // no stored expert: K2 contributes zero rows
+    if (slot < 0) continue;  // no stored expert: the down half contributes zero rows
     const uint8_t* cb[2] = {w.wg + (size_t)slot * I * rowbytes, w.wu + (size_t)slot * I * rowbytes};
     const uint8_t* sb[2] = {w.sg + (size_t)slot * I * NB, w.su + (size_t)slot * I * NB};
     const uint8_t* cp[J];
@@ -449,6 +446,17 @@ __global__ __launch_bounds__(kThreads, 2) void fused_gateup_kernel(
       if (has1) gu_finish(Bn, xr, lane, hrow, (bat + 1) * R);
     }
   }
+}
+
+template <int NPL, int J>
+__global__ __launch_bounds__(kThreads, 2) void fused_gateup_kernel(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x, int E, int k, const int32_t* __restrict__ e2s,
+    ExpertStore w, FusedRoute* __restrict__ pub, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+    float* __restrict__ h) {
+  __shared__ FusedRoute fr;
+  fused_route<NPL>(logits, E, k, e2s, w.num_slots, fr, pub, topk_ids, topk_w);
+  fused_gateup_rows<J>(fr, x, k, w, h, blockIdx.x * kWaves + (threadIdx.x >> 6), gridDim.x * kWaves,
+                       threadIdx.x & 63);
 }
 
 template <int M, bool TAIL, bool kBf16Out>

@@ -49,9 +49,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr int kMtThreads = 256;   // four wavefronts: the four quarters of a unit's K
-constexpr int kMtGridGU = 768;    // persistent workgroups of the gate/up kernel (three per CU)
+constexpr int kMtGridGU = 512;    // persistent workgroups of the gate/up kernel (two per CU)
 constexpr int kMtGridDN = 512;    // and of the down kernel (two per CU)
-constexpr int kMtWin = 20;        // chunks per scale window (80 blocks)
+constexpr int kMtWin = 20;        // chunks per scale window (80 blocks; even: whole chunk pairs)
 constexpr int kMtW = kMtWin + 1;  // words per table row (odd: 16 rows hit 16 banks)
 constexpr int kMtRows = 16;       // bucket rows per unit (the MFMA's M)
 constexpr int kMtFrags = 4;       // 16-row weight fragments per unit
@@ -121,12 +121,15 @@ __device__ __forceinline__ bf16x8_t dq8(uint32_t w, float s) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// One chunk of one unit: A (per plane the lane's 64 B of block 4c+g) and the
-// four B fragments (lane: 16 B = block 4c+g of row l%16).
-template <int PLANES>
+// CH consecutive chunks of one unit (one or two): A (per chunk and plane the
+// lane's 64 B of block 4c+g) and the four B fragments (lane: 16 B = block
+// 4c+g of row l%16).  With CH = 2 a fragment row's two chunks are the two
+// halves of one 128-byte line and their loads go out back to back, which
+// keeps the line's two requests together in the memory pipeline.
+template <int PLANES, int CH>
 struct MtRegs {
-  uint4_t a[PLANES][4];  // [plane][K-step]
-  uint4_t b[kMtFrags];   // [fragment]
+  uint4_t a[CH][PLANES][4];  // [chunk][plane][K-step]
+  uint4_t b[CH][kMtFrags];   // [chunk][fragment]
 };
 
 template <int PLANES>
@@ -135,64 +138,80 @@ struct MtSrc {
   uint32_t va;              // the lane's A row + 64 * g (kOob past the bucket's end)
   uint32_t plane;           // byte distance of the A planes
   uint32_t vb[kMtFrags];    // fragment row (lane%16) + 16 * g
-  // chunk c; with ok false every offset is past its range and the registers read zeros
-  __device__ __forceinline__ void load(int c, bool ok, MtRegs<PLANES>& r) const {
-    const uint32_t off = ok ? 0u : kOob;  // real offsets stay below 2^31
+  // chunks c .. c+CH-1, those at or past `end` read as zeros (every offset past its range)
+  template <int CH>
+  __device__ __forceinline__ void load(int c, int end, MtRegs<PLANES, CH>& r) const {
+    uint32_t off[CH];
 #pragma unroll
-    for (int p = 0; p < PLANES; ++p)
+    for (int i = 0; i < CH; ++i) off[i] = c + i < end ? 0u : kOob;  // real offsets stay below 2^31
 #pragma unroll
-      for (int t = 0; t < 4; ++t) r.a[p][t] = bload16(ra, (va + p * plane + (uint32_t)c * 256u + 16u * t) | off);
+    for (int f = 0; f < kMtFrags; ++f)
 #pragma unroll
-    for (int f = 0; f < kMtFrags; ++f) r.b[f] = bload16(rb[f], (vb[f] + (uint32_t)c * 64u) | off);
+      for (int i = 0; i < CH; ++i) r.b[i][f] = bload16(rb[f], (vb[f] + (uint32_t)(c + i) * 64u) | off[i]);
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+#pragma unroll
+      for (int p = 0; p < PLANES; ++p)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          r.a[i][p][t] = bload16(ra, (va + p * plane + (uint32_t)(c + i) * 256u + 16u * t) | off[i]);
   }
 };
 
-// One chunk of MFMAs: 4 K-steps x 4 fragments x PLANES.  The lane's scale is
-// byte g of its row's table word for the chunk.
-template <int PLANES>
-__device__ __forceinline__ void mt_mma(const MtRegs<PLANES>& r, f4v (&acc)[kMtFrags], const uint32_t* tab, int cw,
-                                       int q16, int g) {
-  float sc[kMtFrags];
+// The MFMAs of the CH chunks: per chunk 4 K-steps x 4 fragments x PLANES.  The
+// lane's scale is byte g of its row's table word for the chunk (cw: the first
+// chunk's table column; a chunk past the window's last column cwl reads zeros
+// and takes the scale of column cwl, a loaded one).
+template <int PLANES, int CH>
+__device__ __forceinline__ void mt_mma(const MtRegs<PLANES, CH>& r, f4v (&acc)[kMtFrags], const uint32_t* tab,
+                                       int cw, int cwl, int q16, int g) {
 #pragma unroll
-  for (int f = 0; f < kMtFrags; ++f) sc[f] = ue8m0_to_f32((tab[(16 * f + q16) * kMtW + cw] >> (8 * g)) & 0xFFu);
+  for (int i = 0; i < CH; ++i) {
+    const int col = min(cw + i, cwl);
+    float sc[kMtFrags];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int f = 0; f < kMtFrags; ++f)
+      sc[f] = ue8m0_to_f32((tab[(16 * f + q16) * kMtW + col] >> (8 * g)) & 0xFFu);
 #pragma unroll
-    for (int f = 0; f < kMtFrags; ++f) {
-      const bf16x8_t bw = dq8(r.b[f][t], sc[f]);
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int p = 0; p < PLANES; ++p)
-        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.a[p][t]), bw, acc[f], 0, 0, 0);
-    }
+      for (int f = 0; f < kMtFrags; ++f) {
+        const bf16x8_t bw = dq8(r.b[i][f][t], sc[f]);
+#pragma unroll
+        for (int p = 0; p < PLANES; ++p)
+          acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.a[i][p][t]), bw, acc[f], 0, 0, 0);
+      }
+  }
 }
 
 // The chunks [cb, ce) of one unit: windows of kMtWin chunks; in a window the
-// next chunk's loads are in flight while one is multiplied, the two register
-// sets alternating.  A load past the window's last chunk reads zeros (its
-// offsets are out of range) and is multiplied like any other, so neither the
-// loads nor the MFMAs sit behind a branch.  tables(cw0, ts) issues the scale
-// loads of the window starting at chunk cw0 (table row 16f + r: row r of
-// fragment f).
-template <int PLANES, typename Tables>
+// next CH chunks' loads are in flight while CH chunks are multiplied, the two
+// register sets alternating.  A chunk past the window's end reads zeros and
+// is multiplied like the others (a set wholly past the end is skipped); the
+// loads are unconditional and pinned ahead of the MFMAs they overlap.
+// tables(cw0, ts) issues the scale loads of the window starting at chunk cw0
+// (table row 16f + r: row r of fragment f).
+template <int CH, int PLANES, typename Tables>
 __device__ __forceinline__ void mt_k_loop(const MtSrc<PLANES>& src, f4v (&acc)[kMtFrags], int cb, int ce,
                                           uint32_t* tab, Tables tables) {
+  static_assert(kMtWin % CH == 0, "whole chunk sets per window");
   const int lane = __lane_id(), q16 = lane & 15, g = lane >> 4;
   for (int cw0 = cb; cw0 < ce; cw0 += kMtWin) {
-    const int last = min(cw0 + kMtWin, ce) - 1;
+    const int end = min(cw0 + kMtWin, ce), last = end - 1;
     ScaleRows<32, 64, kMtWin, kMtW> ts[2];
     tables(cw0, ts);
-    MtRegs<PLANES> r0, r1;
-    src.load(cw0, true, r0);
+    MtRegs<PLANES, CH> r0, r1;
+    src.load(cw0, end, r0);
 #pragma unroll
     for (int t = 0; t < 2; ++t) ts[t].store(tab + 32 * t * kMtW, lane);
     __builtin_amdgcn_wave_barrier();  // a wavefront's LDS accesses complete in order
-    for (int c = cw0; c <= last; c += 2) {
-      src.load(min(c + 1, last), c + 1 <= last, r1);
-      __builtin_amdgcn_sched_barrier(0);  // all of the next chunk's loads go out before these MFMAs
-      mt_mma(r0, acc, tab, c - cw0, q16, g);
-      src.load(min(c + 2, last), c + 2 <= last, r0);
+    for (int c = cw0; c < end; c += 2 * CH) {
+      src.load(min(c + CH, last), c + CH < end ? end : 0, r1);
+      __builtin_amdgcn_sched_barrier(0);  // the next set's loads go out before these MFMAs
+      mt_mma(r0, acc, tab, c - cw0, last - cw0, q16, g);
+      src.load(min(c + 2 * CH, last), c + 2 * CH < end ? end : 0, r0);
       __builtin_amdgcn_sched_barrier(0);
-      mt_mma(r1, acc, tab, min(c + 1, last) - cw0, q16, g);  // zeros past the window's end
+      if (c + CH < end) mt_mma(r1, acc, tab, c + CH - cw0, last - cw0, q16, g);
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -224,7 +243,7 @@ __device__ __forceinline__ uint16_t bf16_lo_part(float v, uint16_t hi) {
   return fabsf(hf) <= 3.4028234663852886e38f ? f32_to_bf16_rne(v - hf) : (uint16_t)0;
 }
 
-__global__ __launch_bounds__(kMtThreads, 3) void gateup_mt_kernel(
+__global__ __launch_bounds__(kMtThreads, 2) void gateup_mt_kernel(
     const uint16_t* __restrict__ x, uint32_t x_bytes, int k, int E, ExpertStore w, const int32_t* __restrict__ e2s,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, uint16_t* __restrict__ hpl,
     int P) {
@@ -264,7 +283,7 @@ __global__ __launch_bounds__(kMtThreads, 3) void gateup_mt_kernel(
       ts[1].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NB; });
     };
     f4v acc[kMtFrags] = {};
-    mt_k_loop(src, acc, cb, ce, tab, tables);
+    mt_k_loop<2>(src, acc, cb, ce, tab, tables);
     __builtin_amdgcn_wave_barrier();
     mt_part_store(reinterpret_cast<float*>(tab), acc, lane);
     __syncthreads();
@@ -329,7 +348,7 @@ __global__ __launch_bounds__(kMtThreads, 2) void down_mt_kernel(
       ts[1].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + 32 + r) * NB; });
     };
     f4v acc[kMtFrags] = {};
-    mt_k_loop(src, acc, cb, ce, tab, tables);
+    mt_k_loop<1>(src, acc, cb, ce, tab, tables);
     __builtin_amdgcn_wave_barrier();
     mt_part_store(reinterpret_cast<float*>(tab), acc, lane);
     __syncthreads();
