@@ -252,9 +252,9 @@ MOE_FP4_API moe_status moe_ffn_fp4_prefill(const uint16_t* x_bf16, int32_t T, in
                                            hipStream_t stream) {
   if (act != MOE_ACT_MXFP6_E2M3) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)T * k > (1 << 22)) return MOE_ERR_SHAPE;
-  // the MXFP6 activations are addressed with 31-bit buffer offsets
+  // the MXFP6 activations (x once per sorted row, and h) are addressed with 31-bit buffer offsets
   if (w && T > 0 && k > 0 &&
-      ((int64_t)T * (w->hidden / 32) * 24 >= ((int64_t)1 << 31) ||
+      ((int64_t)T * k * (w->hidden / 32) * 24 >= ((int64_t)1 << 31) ||
        (int64_t)T * k * (w->inter / 32) * 24 >= ((int64_t)1 << 31)))
     return MOE_ERR_UNSUPPORTED;
   if (w && (misaligned(w->s_gate, 4) || misaligned(w->s_up, 4) || misaligned(w->s_down, 4))) return MOE_ERR_ALIGN;

@@ -9,7 +9,9 @@
 // most 10 bits, inside the instruction's block fixed point), and e2m3 runs at
 // the FP4/FP6 rate.
 //
-//   P0  quant_x:  x bf16 [T][H] -> xq [T][H/32][24 B] + xs [T][H/32]
+//   P0  quant_x:  x bf16 [T][H] -> MXFP6 blocks per token (scratch)
+//       sort_x:   -> xq, xs in bucket-sorted rows, chunk-major (one 48-B record per
+//                 row, 128-K chunk and K-half; see q6_offset)
 //   plan:         bucket offsets -> flat tile lists of both GEMMs
 //   P1  gateup:   per tile: g = W_gate.x, u = W_up.x (MFMA, fp32),
 //                 h = silu(g)*u, h -> MXFP6 into hq/hs (sorted-row order)
@@ -90,6 +92,21 @@ __device__ __forceinline__ void q6_block(const float (&v)[32], uint32_t (&pk)[6]
   sbyte = (uint32_t)(X + 127);
 }
 
+// MXFP6 rows in the layout the GEMMs read.  Row p is a sorted (bucket-order)
+// row; K runs in chunks of 128 (blocks 4c..4c+3).  For chunk c and K-half
+// h (blocks h and 2+h: the lane's operand for the chunk's two MFMA K-steps)
+// the rows' 48-byte records are contiguous:
+//   codes: [c][h][p][48 B] (block h, then block 2+h, 24 B each)
+//   x scales: [c][p] words (the scale bytes of blocks 4c..4c+3)
+// so a tile's chunk is two contiguous runs of 48-byte records, in the order
+// the LDS stage holds them.
+__device__ __forceinline__ size_t q6_offset(int p, int b, int P) {
+  const int c = b >> 2, bb = b & 3;
+  return ((size_t)(2 * c + (bb & 1)) * P + p) * 48 + (size_t)(bb >> 1) * 24;
+}
+
+// Each token's x once: one thread per 32-block, token-major codes [T][H/32][24 B]
+// and scale bytes [T][H/32].
 __global__ __launch_bounds__(kPT) void quant_x_kernel(const uint16_t* __restrict__ x, int nblk,
                                                       uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
   const int g = blockIdx.x * kPT + threadIdx.x;
@@ -113,6 +130,35 @@ __global__ __launch_bounds__(kPT) void quant_x_kernel(const uint16_t* __restrict
   dst[1] = make_uint2(pk[2], pk[3]);
   dst[2] = make_uint2(pk[4], pk[5]);
   xs[g] = (uint8_t)sb;
+}
+
+// The token-major blocks copied into the sorted chunk-major layout: one
+// thread per (chunk c, sorted row p) reads its token's 96 B and scale word of
+// the chunk and writes the two 48-byte records (consecutive threads write
+// consecutive records) and the chunk's scale word.
+__global__ __launch_bounds__(kPT) void sort_x_kernel(const uint8_t* __restrict__ xq_t,
+                                                     const uint8_t* __restrict__ xs_t, int H, int k, int P,
+                                                     const int32_t* __restrict__ sorted_pair,
+                                                     uint8_t* __restrict__ xq, uint32_t* __restrict__ xs) {
+  const int g = blockIdx.x * kPT + threadIdx.x;
+  const int nch = H / 128;
+  if (g >= P * nch) return;
+  const int c = g / P, p = g - c * P;
+  const size_t t = (size_t)(sorted_pair[p] / k);
+  const uint2* src = reinterpret_cast<const uint2*>(xq_t + (t * (H / 32) + 4 * c) * 24);
+  uint2 w[12];  // block b of the chunk = w[3b .. 3b+2]
+#pragma unroll
+  for (int i = 0; i < 12; ++i) w[i] = src[i];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {  // record of K-half h: block h, then block 2+h
+    uint2* dst = reinterpret_cast<uint2*>(xq + q6_offset(p, 4 * c + h, P));
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      dst[i] = w[3 * h + i];
+      dst[3 + i] = w[3 * (2 + h) + i];
+    }
+  }
+  xs[(size_t)c * P + p] = *reinterpret_cast<const uint32_t*>(xs_t + t * (H / 32) + 4 * c);
 }
 
 // ---- tile plan -----------------------------------------------------------------
@@ -171,15 +217,25 @@ __global__ __launch_bounds__(kPT) void plan_kernel(const int32_t* __restrict__ o
                                                    int ntw_dn, TileDesc* __restrict__ gu, TileDesc* __restrict__ dn,
                                                    SkBucket* __restrict__ sbk, int32_t* __restrict__ counts) {
   __shared__ int mstart[kMaxExperts + 1];
+  __shared__ int offs[kMaxExperts + 1];  // the bucket offsets and slots, read once: the tile loop
+  __shared__ int slots[kMaxExperts];     // below touches them once per tile
   __shared__ int part[kPT / 64];
   const int tid = threadIdx.x;
+  for (int e = tid; e <= kMaxExperts; e += kPT) {
+    offs[e] = offsets[e < E ? e : E];
+    if (e < kMaxExperts) {
+      int slot = e < E ? (e2s ? e2s[e] : e) : -1;
+      slots[e] = (slot < 0 || slot >= num_slots) ? -1 : slot;
+    }
+  }
+  __syncthreads();
   constexpr int PER = kMaxExperts / kPT;  // experts per thread
   int mt[PER], small[PER];
   int msum = 0, ssum = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = tid * PER + i;
-    const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+    const int c = e < E ? offs[e + 1] - offs[e] : 0;
     small[i] = (c >= 1 && c <= SK_MAX) ? 1 : 0;
     mt[i] = small[i] ? 0 : (c + BM - 1) / BM;
     msum += mt[i];
@@ -194,12 +250,10 @@ __global__ __launch_bounds__(kPT) void plan_kernel(const int32_t* __restrict__ o
     mstart[e] = mrun;
     mrun += mt[i];
     if (small[i]) {
-      int slot = e2s ? e2s[e] : e;
-      if (slot >= num_slots) slot = -1;
       SkBucket b;
-      b.row0 = offsets[e];
-      b.cnt = offsets[e + 1] - offsets[e];
-      b.slot = slot < 0 ? -1 : slot;
+      b.row0 = offs[e];
+      b.cnt = offs[e + 1] - offs[e];
+      b.slot = slots[e];
       b.pad = 0;
       sbk[srun++] = b;
     }
@@ -221,13 +275,11 @@ __global__ __launch_bounds__(kPT) void plan_kernel(const int32_t* __restrict__ o
       const int mtiles = mstart[e + 1] - mstart[e];
       const int local = t - mstart[e] * ntw;
       const int ntile = local / mtiles, mtile = local - ntile * mtiles;
-      const int c = offsets[e + 1] - offsets[e];
-      int slot = e2s ? e2s[e] : e;
-      if (slot >= num_slots) slot = -1;
+      const int c = offs[e + 1] - offs[e];
       TileDesc d;
-      d.row0 = offsets[e] + mtile * BM;
+      d.row0 = offs[e] + mtile * BM;
       d.mrows = min(BM, c - mtile * BM);
-      d.slot = slot < 0 ? -1 : slot;
+      d.slot = slots[e];
       d.ntile = ntile;
       out[t] = d;
     }
@@ -275,7 +327,6 @@ constexpr int A_HS = BM * 48 + 64;  // LDS bytes per K-half region of an A chunk
 
 struct ABuf {
   uint8_t codes[2 * A_HS];
-  uint2 spill[64];  // the stores of lanes that carry no codes
 };
 
 // Scale bytes are read once per tile into LDS tables (a scale word -- the 4
@@ -297,67 +348,76 @@ struct GemmSmem {
 };
 
 
+// Words [cw0, cw0 + WIN) of ROWS table rows from a chunk-major word array
+// ([chunk][row], row stride 1 word, P rows per chunk): consecutive threads
+// read consecutive rows of one chunk.  Rows at or past nrows read zeros.
+template <int ROWS, int NT, int WIN, int STRIDE>
+struct ScaleCols {
+  static constexpr int N = ROWS * WIN / NT;
+  static_assert(ROWS * WIN % NT == 0 && WIN < STRIDE, "table split");
+  uint32_t v[N];
+  __device__ __forceinline__ void issue(rsrc_t r, int cw0, int t, int row0, int nrows, int P) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = t + NT * i, wd = idx / ROWS, row = idx - wd * ROWS;
+      v[i] = bload4(r, row < nrows ? ((uint32_t)(cw0 + wd) * (uint32_t)P + (uint32_t)(row0 + row)) * 4u : kOob);
+    }
+  }
+  __device__ __forceinline__ void store(uint32_t* tab, int t) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = t + NT * i, wd = idx / ROWS, row = idx - wd * ROWS;
+      tab[row * STRIDE + wd] = v[i];
+    }
+  }
+};
+
 // The scale tables of one tile for a window of WIN chunks: A rows (all
-// threads) and each wavefront's two 32-row weight fragments.
-template <int WIN>
+// threads; AS is the loader of the A scale layout) and each wavefront's two
+// 32-row weight fragments.
+template <int WIN, typename AS>
 struct TileScales {
   static constexpr int kWin = WIN;
   static_assert(WIN <= SCWIN, "scale window");
-  ScaleRows<BM, kPT, WIN, SCW> a;
+  AS a;
   ScaleRows<32, 64, WIN, SCW> b[2];
 };
 
-// Registers of one A chunk between its global loads and its LDS store.  The
-// loads are row-contiguous: 8 lanes per row, 6 of them carrying its 96 B of
-// codes (lane p: bytes 16p..16p+15), 8 rows per wavefront load.  Threads
-// tid < BM also load the scale word of row tid.
+// Registers of one A chunk between its global loads and its LDS store: the
+// tile's two records runs (K-half 0, then 1; 128 rows x 48 B each) as 768
+// pieces of 16 B, piece t + 256j in thread t.  Memory and LDS hold the runs
+// in the same order, so the store is a plain copy.
 struct ARegs {
-  uint4_t q[BM / 32];  // rows 32w + 8i + lane/8, i = 0..3
+  uint4_t q[3];
 };
 
 struct ASrc {
   rsrc_t rc;
-  uint32_t vc[BM / 32];  // row offsets + 16p (kOob for rows past the bucket and for lanes p >= 6)
+  uint32_t vc[3];     // this thread's pieces of chunk 0
+  uint32_t cstride;   // bytes per chunk: both K-halves of all P rows
   __device__ __forceinline__ void load(int c, ARegs& r) const {
 #pragma unroll
-    for (int i = 0; i < BM / 32; ++i) r.q[i] = bload16(rc, vc[i] + (uint32_t)c * 96u);
+    for (int j = 0; j < 3; ++j) r.q[j] = bload16(rc, vc[j] + (uint32_t)c * cstride);
   }
 };
 
-// Every thread stores unconditionally (lanes without codes into d.spill,
-// threads tid >= BM into the upper scale half), so no store of the K loop sits
-// behind a branch.
 __device__ __forceinline__ void store_a(ABuf& d, const ARegs& r, int tid) {
-  const int lane = tid & 63, p = lane & 7;
-  const bool codes = p < 6;
-  // 8-byte units U = 2p, 2p+1 of the row's 96 B: part U%3 of block b = U/3,
-  // which goes to K-half b&1 at offset (b>>1)*24 + (U%3)*8
-  int o[2];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int U = 2 * p + k, b = U / 3;
-    o[k] = (b & 1) * A_HS + (b >> 1) * 24 + (U % 3) * 8;
-  }
-  uint8_t* const sp = reinterpret_cast<uint8_t*>(d.spill) + 8 * lane;
-#pragma unroll
-  for (int i = 0; i < BM / 32; ++i) {
-    const int row = 32 * (tid >> 6) + 8 * i + (lane >> 3);
-    uint8_t* d0 = codes ? d.codes + o[0] + row * 48 : sp;
-    uint8_t* d1 = codes ? d.codes + o[1] + row * 48 : sp;
-    *reinterpret_cast<uint2*>(d0) = make_uint2(r.q[i].x, r.q[i].y);
-    *reinterpret_cast<uint2*>(d1) = make_uint2(r.q[i].z, r.q[i].w);
+  for (int j = 0; j < 3; ++j) {
+    const int i = tid + kPT * j, h = i / (BM * 3);
+    *reinterpret_cast<uint4_t*>(d.codes + h * A_HS + (i - h * BM * 3) * 16) = r.q[j];
   }
 }
 
-// Row offsets of this thread's A loads; row_off(r) gives the byte offset of
-// bucket row r's codes (or kOob when the row is past the bucket's end).
-template <typename RowOff>
-__device__ __forceinline__ void a_offsets(ASrc& as, int tid, RowOff row_off) {
-  const int lane = tid & 63, p = lane & 7;
+// A offsets of a tile whose rows are sorted rows row0.. of P.  Rows past the
+// bucket read other buckets' records (their outputs are never stored, and
+// their scale words are zero); past the array's end they read zeros.
+__device__ __forceinline__ void a_offsets(ASrc& as, int tid, int row0, int P) {
+  as.cstride = 96u * (uint32_t)P;
 #pragma unroll
-  for (int i = 0; i < BM / 32; ++i) {
-    const uint32_t o = row_off(32 * (tid >> 6) + 8 * i + (lane >> 3));
-    as.vc[i] = (p < 6 && o != kOob) ? o + 16u * p : kOob;
+  for (int j = 0; j < 3; ++j) {
+    const int i = tid + kPT * j, h = i / (BM * 3);
+    as.vc[j] = ((uint32_t)h * (uint32_t)P + (uint32_t)row0) * 48u + (uint32_t)(i - h * BM * 3) * 16u;
   }
 }
 
@@ -437,13 +497,14 @@ struct ChunkRegs {
   BRegs b;
 };
 
-template <int WIN, typename Tables>
+template <typename TS, typename Tables>
 __device__ __forceinline__ void gemm_k_loop(GemmSmem& sm, f16v (&acc)[4][2], const ASrc& as, const BSrc& bs,
                                             int K, int tid, int lane, Tables tables) {
+  constexpr int WIN = TS::kWin;
   const int nchunks = K / KC, wid = tid >> 6;
   for (int cw0 = 0; cw0 < nchunks; cw0 += WIN) {
     const int last = min(cw0 + WIN, nchunks) - 1;
-    TileScales<WIN> ts;
+    TS ts;
     tables(cw0, ts);
     ChunkRegs r[PF];
 #pragma unroll
@@ -500,14 +561,15 @@ constexpr int SKW = SKWIN + 1;  // words per table row (odd: 32 rows hit 32 bank
 
 struct SkSrc {
   rsrc_t ra, rb[2];
-  uint32_t va, vb[2];  // va: + 24 * K-half; vb: row (lane%16) + 16 * (lane/16)
+  uint32_t va, vb[2];  // va: the lane's record (row r32, K-half h) in chunk 0; vb: row (lane%16) + 16 * (lane/16)
+  uint32_t cstride;    // bytes per chunk of the A records
   uint32_t half;       // byte distance of fragment row 16 from row 0
   __device__ __forceinline__ void load(int n, SkRegs& r) const {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint32_t ks = (uint32_t)(4 * n + s);
+    for (int s = 0; s < 4; ++s) {  // K-step s: chunk 2n + s/2, block 2(s%2) + h = bytes 24(s%2).. of the record
+      const uint32_t o = va + (uint32_t)(2 * n + (s >> 1)) * cstride + 24u * (uint32_t)(s & 1);
 #pragma unroll
-      for (int j = 0; j < 3; ++j) r.a[s][j] = bload8(ra, va + ks * 48u + 8u * j);
+      for (int j = 0; j < 3; ++j) r.a[s][j] = bload8(ra, o + 8u * j);
     }
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -542,23 +604,32 @@ __device__ __forceinline__ void sk_mma(const SkRegs& r, f16v (&acc)[2], int nks,
   }
 }
 
+// The scale tables of a unit's window: its A rows (loader AS) and its two
+// weight fragments.
+template <typename AS>
+struct SkTables {
+  AS a;
+  ScaleRows<32, 64, SKWIN, SKW> b[2];
+};
+
 // All K of one unit: batches of four K-steps, the next batch's loads in flight
 // while one is multiplied; pairs of batches alternate the two register sets.
 // Loads past the last batch re-read it (never used): no load behind a branch.
 // tables(cw0, ts) issues the scale-table loads of the window starting at chunk cw0.
-template <typename Tables>
+template <typename TS, typename Tables>
 __device__ __forceinline__ void sk_k_loop(const SkSrc& src, f16v (&acc)[2], int K, int h, uint32_t* tab,
                                           Tables tables) {
   const int nks_total = K / 64, nchunks = K / KC;
   const int lane = __lane_id();
   for (int cw0 = 0; cw0 < nchunks; cw0 += SKWIN) {
     const int b0 = cw0 / 2, last = (min(cw0 + SKWIN, nchunks) + 1) / 2 - 1;  // batches of this window
-    ScaleRows<32, 64, SKWIN, SKW> ts[3];
+    TS ts;
     tables(cw0, ts);
     SkRegs r0, r1;
     src.load(b0, r0);
-#pragma unroll
-    for (int t = 0; t < 3; ++t) ts[t].store(tab + 32 * t * SKW, lane);
+    ts.a.store(tab, lane);
+    ts.b[0].store(tab + 32 * SKW, lane);
+    ts.b[1].store(tab + 64 * SKW, lane);
     __builtin_amdgcn_wave_barrier();  // a wavefront's LDS accesses complete in order
     for (int n = b0; n <= last; n += 2) {
       src.load(min(n + 1, last), r1);
@@ -573,14 +644,14 @@ __device__ __forceinline__ void sk_k_loop(const SkSrc& src, f16v (&acc)[2], int 
 constexpr int SK_GRID = 1024;  // workgroups of the streaming kernels (4 wavefronts each)
 
 __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, uint32_t xq_bytes, uint32_t xs_bytes, int k,
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, uint32_t xq_bytes, uint32_t xs_bytes, int P,
     ExpertStore w, const int32_t* __restrict__ sorted_pair, const SkBucket* __restrict__ sbk,
     const int32_t* __restrict__ counts, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
   __shared__ float stage[4][32 * 33];
   __shared__ uint32_t sktab[4][96 * SKW];
   const int H = w.H, I = w.I, NBH = H / 32, NBI = I / 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
-  const uint32_t arow = (uint32_t)NBH * 24u, wrow = (uint32_t)H / 2u;
+  const uint32_t wrow = (uint32_t)H / 2u;
   const size_t mat = (size_t)I * wrow, smat = (size_t)I * NBH;
   const int groups = I / 32, units = counts[2] * groups;
   float* st = stage[wid];
@@ -588,10 +659,10 @@ __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
     const SkBucket bk = sbk[u / groups];
     const int q = u % groups;
     if (bk.slot < 0) continue;
-    const int tok = r32 < bk.cnt ? sorted_pair[bk.row0 + r32] / k : -1;
     SkSrc src;
     src.ra = make_rsrc(xq, xq_bytes);
-    src.va = tok >= 0 ? (uint32_t)tok * arow + 24u * h : kOob;
+    src.va = r32 < bk.cnt ? ((uint32_t)h * (uint32_t)P + (uint32_t)(bk.row0 + r32)) * 48u : kOob;
+    src.cstride = 96u * (uint32_t)P;
     src.rb[0] = make_rsrc(w.wg + (size_t)bk.slot * mat, (uint32_t)mat);
     src.rb[1] = make_rsrc(w.wu + (size_t)bk.slot * mat, (uint32_t)mat);
     src.vb[0] = src.vb[1] = (uint32_t)(32 * q + (lane & 15)) * wrow + 16u * (uint32_t)(lane >> 4);
@@ -599,16 +670,14 @@ __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
     const rsrc_t xsr = make_rsrc(xs, xs_bytes);
     const rsrc_t sgr = make_rsrc(w.sg + (size_t)bk.slot * smat, (uint32_t)smat);
     const rsrc_t sur = make_rsrc(w.su + (size_t)bk.slot * smat, (uint32_t)smat);
-    auto tables = [&](int cw0, ScaleRows<32, 64, SKWIN, SKW> (&ts)[3]) {
-      ts[0].issue(xsr, cw0, lane, [&](int r) {
-        const int t = __shfl(tok, r, 64);
-        return t >= 0 ? (uint32_t)t * NBH : kOob;
-      });
-      ts[1].issue(sgr, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NBH; });
-      ts[2].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NBH; });
+    using TS = SkTables<ScaleCols<32, 64, SKWIN, SKW>>;
+    auto tables = [&](int cw0, TS& ts) {
+      ts.a.issue(xsr, cw0, lane, bk.row0, bk.cnt, P);
+      ts.b[0].issue(sgr, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NBH; });
+      ts.b[1].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NBH; });
     };
     f16v acc[2] = {f16v{}, f16v{}};
-    sk_k_loop(src, acc, H, h, sktab[wid], tables);
+    sk_k_loop<TS>(src, acc, H, h, sktab[wid], tables);
     // h = silu(g) * u: rows of the bucket x this unit's 32 h columns (one MXFP6 block per row)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -623,7 +692,7 @@ __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
       uint32_t pk[6], sb;
       q6_block(v, pk, sb);
       const size_t grow = (size_t)(bk.row0 + r32);
-      uint2* dst = reinterpret_cast<uint2*>(hq + grow * NBI * 24 + (size_t)q * 24);
+      uint2* dst = reinterpret_cast<uint2*>(hq + q6_offset(bk.row0 + r32, q, P));
       dst[0] = make_uint2(pk[0], pk[1]);
       dst[1] = make_uint2(pk[2], pk[3]);
       dst[2] = make_uint2(pk[4], pk[5]);
@@ -634,13 +703,13 @@ __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
 }
 
 __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
-    const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, uint32_t hq_bytes, uint32_t hs_bytes,
+    const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, uint32_t hq_bytes, uint32_t hs_bytes, int P,
     ExpertStore w, const int32_t* __restrict__ sorted_pair, const SkBucket* __restrict__ sbk,
     const int32_t* __restrict__ counts, float* __restrict__ y) {
   __shared__ uint32_t sktab[4][96 * SKW];
   const int H = w.H, I = w.I, NBI = I / 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
-  const uint32_t arow = (uint32_t)NBI * 24u, wrow = (uint32_t)I / 2u;
+  const uint32_t wrow = (uint32_t)I / 2u;
   const size_t mat = (size_t)H * wrow, smat = (size_t)H * NBI;
   const int groups = H / 64, units = counts[2] * groups;
   for (int u = blockIdx.x * 4 + wid; u < units; u += gridDim.x * 4) {
@@ -653,8 +722,8 @@ __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
     }
     SkSrc src;
     src.ra = make_rsrc(hq, hq_bytes);
-    const uint32_t arow_i = (uint32_t)(bk.row0 + r32);
-    src.va = r32 < bk.cnt ? arow_i * arow + 24u * h : kOob;
+    src.va = r32 < bk.cnt ? ((uint32_t)h * (uint32_t)P + (uint32_t)(bk.row0 + r32)) * 48u : kOob;
+    src.cstride = 96u * (uint32_t)P;
     const rsrc_t rc = make_rsrc(w.wd + (size_t)bk.slot * mat, (uint32_t)mat);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
@@ -664,14 +733,14 @@ __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
     src.half = 16u * wrow;
     const rsrc_t hsr = make_rsrc(hs, hs_bytes);
     const rsrc_t sdr = make_rsrc(w.sd + (size_t)bk.slot * smat, (uint32_t)smat);
-    auto tables = [&](int cw0, ScaleRows<32, 64, SKWIN, SKW> (&ts)[3]) {
-      ts[0].issue(hsr, cw0, lane,
-                  [&](int r) { return r < bk.cnt ? (uint32_t)(bk.row0 + r) * NBI : kOob; });
-      ts[1].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + r) * NBI; });
-      ts[2].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + 32 + r) * NBI; });
+    using TS = SkTables<ScaleRows<32, 64, SKWIN, SKW>>;
+    auto tables = [&](int cw0, TS& ts) {
+      ts.a.issue(hsr, cw0, lane, [&](int r) { return r < bk.cnt ? (uint32_t)(bk.row0 + r) * NBI : kOob; });
+      ts.b[0].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + r) * NBI; });
+      ts.b[1].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + 32 + r) * NBI; });
     };
     f16v acc[2] = {f16v{}, f16v{}};
-    sk_k_loop(src, acc, I, h, sktab[wid], tables);
+    sk_k_loop<TS>(src, acc, I, h, sktab[wid], tables);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = (i >> 2) * 8 + h * 4 + (i & 3);
@@ -691,28 +760,23 @@ __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
 // exactly one MXFP6 block per row.
 
 __global__ __launch_bounds__(kPT, 1) void gateup_mfma_kernel(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, uint32_t xq_bytes, uint32_t xs_bytes, int k,
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, uint32_t xq_bytes, uint32_t xs_bytes, int P,
     ExpertStore w, const int32_t* __restrict__ sorted_pair, const TileDesc* __restrict__ tiles,
     const int32_t* __restrict__ counts, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
   __shared__ GemmSmem sm;
   const int H = w.H, I = w.I, NBH = H / 32, NBI = I / 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
-  const uint32_t arow = (uint32_t)NBH * 24u, wrow = (uint32_t)H / 2u;
+  const uint32_t wrow = (uint32_t)H / 2u;
   const size_t mat = (size_t)I * wrow, smat = (size_t)I * NBH;
   const int total = counts[0];
   for (TileWalk tw(total); tw.next < tw.end; tw.next += tw.step) {
     const TileDesc d = tiles[tw.next];
     if (d.slot < 0) continue;  // no stored expert: the down GEMM writes its rows as zeros
     __syncthreads();           // the previous tile's epilogue is done with the LDS
-    if (tid < BM) sm.rowtok[tid] = tid < d.mrows ? sorted_pair[d.row0 + tid] / k : -1;
-    __syncthreads();
     const int j0 = d.ntile * GU_N;
     ASrc as;
     as.rc = make_rsrc(xq, xq_bytes);
-    a_offsets(as, tid, [&](int r) {
-      const int tok = sm.rowtok[r];
-      return tok >= 0 ? (uint32_t)tok * arow : kOob;
-    });
+    a_offsets(as, tid, d.row0, P);
     BSrc bs;
     {
       // wavefront wid: gate rows j0+32*wid.. (fragment 0) and the same up rows (fragment 1)
@@ -727,11 +791,9 @@ __global__ __launch_bounds__(kPT, 1) void gateup_mfma_kernel(
     const rsrc_t sgr = make_rsrc(w.sg + (size_t)d.slot * smat, (uint32_t)smat);
     const rsrc_t sur = make_rsrc(w.su + (size_t)d.slot * smat, (uint32_t)smat);
     const uint32_t jr0 = (uint32_t)(j0 + 32 * wid);
-    auto tables = [&](int cw0, TileScales<40>& ts) {
-      ts.a.issue(xsr, cw0, tid, [&](int r) {
-        const int tok = sm.rowtok[r];
-        return tok >= 0 ? (uint32_t)tok * NBH : kOob;
-      });
+    using TS = TileScales<40, ScaleCols<BM, kPT, 40, SCW>>;
+    auto tables = [&](int cw0, TS& ts) {
+      ts.a.issue(xsr, cw0, tid, d.row0, d.mrows, P);
       ts.b[0].issue(sgr, cw0, lane, [&](int r) { return (jr0 + (uint32_t)r) * NBH; });
       ts.b[1].issue(sur, cw0, lane, [&](int r) { return (jr0 + (uint32_t)r) * NBH; });
     };
@@ -740,7 +802,7 @@ __global__ __launch_bounds__(kPT, 1) void gateup_mfma_kernel(
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int g = 0; g < 2; ++g) acc[f][g] = f16v{};
-    gemm_k_loop<40>(sm, acc, as, bs, H, tid, lane, tables);
+    gemm_k_loop<TS>(sm, acc, as, bs, H, tid, lane, tables);
     // h = silu(g) * u into the staging buffer (the K loop ended on a barrier)
     const int wcol = 32 * wid + r32;
 #pragma unroll
@@ -762,7 +824,7 @@ __global__ __launch_bounds__(kPT, 1) void gateup_mfma_kernel(
         q6_block(v, pk, sb);
         const size_t grow = (size_t)(d.row0 + row);
         const int gblk = j0 / 32 + blk;
-        uint2* dst = reinterpret_cast<uint2*>(hq + grow * NBI * 24 + (size_t)gblk * 24);
+        uint2* dst = reinterpret_cast<uint2*>(hq + q6_offset(d.row0 + row, gblk, P));
         dst[0] = make_uint2(pk[0], pk[1]);
         dst[1] = make_uint2(pk[2], pk[3]);
         dst[2] = make_uint2(pk[4], pk[5]);
@@ -775,13 +837,13 @@ __global__ __launch_bounds__(kPT, 1) void gateup_mfma_kernel(
 // ---- P2: down GEMM -> y_pair ---------------------------------------------------------
 
 __global__ __launch_bounds__(kPT, 1) void down_mfma_kernel(
-    const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, uint32_t hq_bytes, uint32_t hs_bytes,
+    const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, uint32_t hq_bytes, uint32_t hs_bytes, int P,
     ExpertStore w, const int32_t* __restrict__ sorted_pair, const TileDesc* __restrict__ tiles,
     const int32_t* __restrict__ counts, float* __restrict__ y) {
   __shared__ GemmSmem sm;
   const int H = w.H, I = w.I, NBI = I / 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
-  const uint32_t arow = (uint32_t)NBI * 24u, wrow = (uint32_t)I / 2u;
+  const uint32_t wrow = (uint32_t)I / 2u;
   const size_t mat = (size_t)H * wrow, smat = (size_t)H * NBI;
   const int total = counts[1];
   for (TileWalk tw(total); tw.next < tw.end; tw.next += tw.step) {
@@ -799,7 +861,7 @@ __global__ __launch_bounds__(kPT, 1) void down_mfma_kernel(
     }
     ASrc as;
     as.rc = make_rsrc(hq, hq_bytes);
-    a_offsets(as, tid, [&](int r) { return r < d.mrows ? (uint32_t)(d.row0 + r) * arow : kOob; });
+    a_offsets(as, tid, d.row0, P);
     BSrc bs;
     {
       // wavefront wid: output rows n0+64*wid+32g.. (fragment g)
@@ -817,7 +879,8 @@ __global__ __launch_bounds__(kPT, 1) void down_mfma_kernel(
     const rsrc_t hsr = make_rsrc(hs, hs_bytes);
     const rsrc_t sdr = make_rsrc(w.sd + (size_t)d.slot * smat, (uint32_t)smat);
     const uint32_t nr0 = (uint32_t)(n0 + 64 * wid);
-    auto tables = [&](int cw0, TileScales<20>& ts) {
+    using TS = TileScales<20, ScaleRows<BM, kPT, 20, SCW>>;
+    auto tables = [&](int cw0, TS& ts) {
       ts.a.issue(hsr, cw0, tid, [&](int r) { return r < d.mrows ? (uint32_t)(d.row0 + r) * NBI : kOob; });
 #pragma unroll
       for (int g = 0; g < 2; ++g)
@@ -828,7 +891,7 @@ __global__ __launch_bounds__(kPT, 1) void down_mfma_kernel(
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int g = 0; g < 2; ++g) acc[f][g] = f16v{};
-    gemm_k_loop<20>(sm, acc, as, bs, I, tid, lane, tables);
+    gemm_k_loop<TS>(sm, acc, as, bs, I, tid, lane, tables);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       __builtin_amdgcn_sched_barrier(0);  // one fragment's stores at a time (register pressure)
@@ -854,9 +917,10 @@ size_t max_mtiles(size_t P) { return (P + BM - 1) / BM + (P < (size_t)kMaxExpert
 
 size_t prefill_workspace_bytes(int T, int k, int H, int I) {
   const size_t P = (size_t)T * k, nm = max_mtiles(P);
-  return align256((size_t)T * H / 32 * 24) + align256((size_t)T * H / 32) + align256(P * I / 32 * 24) +
+  return align256(P * H / 32 * 24) + align256(P * H / 32) + align256(P * I / 32 * 24) +
          align256(P * I / 32) + align256(nm * (I / GU_N) * sizeof(TileDesc)) +
-         align256(nm * (H / DN_N) * sizeof(TileDesc)) + align256(kMaxExperts * sizeof(SkBucket)) + 256;
+         align256(nm * (H / DN_N) * sizeof(TileDesc)) + align256(kMaxExperts * sizeof(SkBucket)) + 256 +
+         align256((size_t)T * H / 32 * 24) + align256((size_t)T * H / 32);
 }
 
 hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertStore& w, const int32_t* e2s,
@@ -865,7 +929,7 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
   const int H = w.H, I = w.I;
   if (H % DN_N != 0 || I % GU_N != 0) return hipErrorInvalidValue;
   const size_t P = (size_t)T * k, nm = max_mtiles(P);
-  const size_t xq_b = (size_t)T * H / 32 * 24, xs_b = (size_t)T * H / 32;
+  const size_t xq_b = P * H / 32 * 24, xs_b = P * H / 32;  // per sorted row (each token k times)
   const size_t hq_b = P * I / 32 * 24, hs_b = P * I / 32;
   if (xq_b >= kOob || hq_b >= kOob) return hipErrorInvalidValue;
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
@@ -880,27 +944,33 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
                                              align256(nm * (H / DN_N) * sizeof(TileDesc)));
   int32_t* counts = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(sbk) +
                                                align256(kMaxExperts * sizeof(SkBucket)));
-  const int nblk = T * (H / 32);
-  hipLaunchKernelGGL(quant_x_kernel, dim3((nblk + kPT - 1) / kPT), dim3(kPT), 0, s, x, nblk, xq, xs);
+  uint8_t* xq_t = reinterpret_cast<uint8_t*>(counts) + 256;  // token-major x blocks, then their scales
+  uint8_t* xs_t = xq_t + align256((size_t)T * H / 32 * 24);
+  const int nblk = T * (H / 32), nq = (int)P * (H / 128);
+  hipLaunchKernelGGL(quant_x_kernel, dim3((nblk + kPT - 1) / kPT), dim3(kPT), 0, s, x, nblk, xq_t, xs_t);
   hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(sort_x_kernel, dim3((nq + kPT - 1) / kPT), dim3(kPT), 0, s, xq_t, xs_t, H, k, (int)P,
+                     sorted_pair, xq, reinterpret_cast<uint32_t*>(xs));
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPT), 0, s, offsets, E, e2s, w.num_slots, I / GU_N, H / DN_N, gu,
                      dn, sbk, counts);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(gateup_skinny_kernel, dim3(SK_GRID), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, k,
+  hipLaunchKernelGGL(gateup_skinny_kernel, dim3(SK_GRID), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, (int)P,
                      w, sorted_pair, sbk, counts, hq, hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(gateup_mfma_kernel, dim3(kGrid), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, k, w,
+  hipLaunchKernelGGL(gateup_mfma_kernel, dim3(kGrid), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, (int)P, w,
                      sorted_pair, gu, counts, hq, hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(down_skinny_kernel, dim3(SK_GRID), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, w,
+  hipLaunchKernelGGL(down_skinny_kernel, dim3(SK_GRID), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, (int)P, w,
                      sorted_pair, sbk, counts, y_pair);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(down_mfma_kernel, dim3(kGrid), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, w,
+  hipLaunchKernelGGL(down_mfma_kernel, dim3(kGrid), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, (int)P, w,
                      sorted_pair, dn, counts, y_pair);
   return hipGetLastError();
 }

@@ -243,8 +243,9 @@ MOE_FP4_API moe_status moe_decode_layer_down(const float* logits, const uint16_t
  *   ws: at least moe_ffn_fp4_prefill_workspace_bytes(T, k, hidden, inter)
  *       bytes, 256-byte aligned
  *   the scale arrays of w must be 4-byte aligned on this path
- * T >= 1, T*k <= 2^22; the MXFP6 activations must each stay under 2 GiB
- * (T*hidden*3/4 < 2^31 and T*k*inter*3/4 < 2^31), else MOE_ERR_UNSUPPORTED.
+ * T >= 1, T*k <= 2^22; the MXFP6 activations (x once per routed row, in
+ * bucket order, and h) must each stay under 2 GiB (T*k*hidden*3/4 < 2^31 and
+ * T*k*inter*3/4 < 2^31), else MOE_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 MOE_FP4_API size_t moe_ffn_fp4_prefill_workspace_bytes(int32_t T, int32_t k, int32_t hidden,
                                                        int32_t inter);

@@ -132,6 +132,9 @@ def test_prefill_and_combine_validation():
     # 200,000 tokens at hidden 16384: 2.46 GB of MXFP6 x, past 31-bit offsets
     assert L.moe_ffn_fp4_prefill(FAKE, 200000, 1, 8, ctypes.byref(big), None, FAKE, FAKE, 0, FAKE, FAKE, 1 << 40,
                                  None) == m.MOE_ERR_UNSUPPORTED
+    # x is quantised once per routed row: 40,000 tokens x top-8 at hidden 16384 is 3.9 GB
+    assert L.moe_ffn_fp4_prefill(FAKE, 40000, 8, 8, ctypes.byref(big), None, FAKE, FAKE, 0, FAKE, FAKE, 1 << 40,
+                                 None) == m.MOE_ERR_UNSUPPORTED
     assert L.moe_combine(None, FAKE, 1, 2, 256, None, 0, FAKE, None) == m.MOE_ERR_NULL
     assert L.moe_combine(FAKE, FAKE, 1, 2, 250, None, 0, FAKE, None) == m.MOE_ERR_SHAPE
     assert L.moe_combine(FAKE, FAKE, 1, 2, 256, None, 5, FAKE, None) == m.MOE_ERR_UNSUPPORTED

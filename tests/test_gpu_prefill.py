@@ -60,8 +60,11 @@ def test_prefill_layer_matches_oracle(name):
 
 def test_prefill_quantiser_bit_exact_all_bf16():
     """The x quantiser (first stage of the prefill call) against the oracle's
-    Q6 on every finite bf16 value; read back from the documented workspace
-    layout (xq [T][H/32][24 B] at offset 0, then xs [T][H/32])."""
+    Q6 on every finite bf16 value, read back from the workspace layout: codes
+    [H/128][2][T*k][48 B] at offset 0 (per 128-K chunk c and K-half h, each
+    sorted row's blocks 4c+h then 4c+2+h, 24 B each), then scale words
+    [H/128][T*k] (the bytes of blocks 4c..4c+3).  With k = 1 and one expert
+    the sorted rows are the tokens in order."""
     import fp4_routed_expert_mxfp4_amd as m
     H = 256
     bits = np.arange(65536, dtype=np.uint32)
@@ -76,14 +79,20 @@ def test_prefill_quantiser_bit_exact_all_bf16():
     x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
     ids = torch.zeros((T, 1), dtype=torch.int32, device="cuda")
     off, sp, _ = m.moe_permute(ids, cfg.E)
+    np.testing.assert_array_equal(to_np(sp), np.arange(T))
     ws = torch.empty(m.prefill_workspace_bytes(T, 1, cfg.H, cfg.I), dtype=torch.uint8, device="cuda")
     m.moe_ffn_fp4_prefill(x, 1, cfg.E, gl.store, None, off, sp, ws=ws)
     torch.cuda.synchronize()
     wsn = ws.cpu().numpy()
+    nch = H // 128
     nq = T * H // 32 * 24
-    xq = wsn[:nq].reshape(T, H // 32 * 24)
+    rec = wsn[:nq].reshape(nch, 2, T, 48)
+    blocks = np.empty((T, H // 32, 24), np.uint8)
+    for bb in range(4):  # block 4c + bb: record of K-half bb % 2, bytes 24 (bb // 2) ..
+        blocks[:, bb::4, :] = rec[:, bb % 2, :, 24 * (bb // 2):24 * (bb // 2) + 24].transpose(1, 0, 2)
+    xq = blocks.reshape(T, H // 32 * 24)
     xs_off = (nq + 255) // 256 * 256
-    xs = wsn[xs_off:xs_off + T * H // 32].reshape(T, H // 32)
+    xs = wsn[xs_off:xs_off + T * H // 32].reshape(nch, T, 4).transpose(1, 0, 2).reshape(T, H // 32)
     codes, sb = o.q6_rows(o.bf16_bits_to_f64(xb))
     np.testing.assert_array_equal(xs, sb)
     np.testing.assert_array_equal(xq, pack6(codes))
