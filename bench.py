@@ -355,18 +355,16 @@ def chain_section(args, torch, m, gd, gi):
     import numpy as np
     xs = [torch.from_numpy(hi.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)]
     xs += [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(cfg.layers)]
-    n = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     ids = torch.empty((cfg.layers, T, k), dtype=torch.int32, device=dev)
     w = torch.empty((cfg.layers, T, k), dtype=torch.float32, device=dev)
     off = torch.empty((cfg.layers, E + 1), dtype=torch.int32, device=dev)
     sp = torch.empty((cfg.layers, T * k), dtype=torch.int32, device=dev)
-    ws = torch.empty(m.decode_layer_workspace_bytes(T, k, E, H, cfg.I), dtype=torch.uint8, device=dev)
+    ws = torch.empty(m.decode_layer_rmsnorm_workspace_bytes(T, k, E, H, cfg.I), dtype=torch.uint8, device=dev)
 
-    def token(_i):
+    def token(_i):  # each layer: RMS norm (inside the layer's first kernel) -> MoE -> + residual
         for layer in range(cfg.layers):
-            m.moe_rmsnorm_bf16(xs[layer], 1e-6, n)
-            m.moe_decode_layer(logits[layer], n, k, stores[layer], e2s[layer], xs[layer], m.MOE_OUT_BF16,
-                               xs[layer + 1], ids[layer], w[layer], ws)
+            m.moe_decode_layer_rmsnorm(logits[layer], xs[layer], k, stores[layer], 1e-6, e2s[layer], m.MOE_OUT_BF16,
+                                       xs[layer + 1], ids[layer], w[layer], ws)
 
     graphs = capture(torch, token, 1)
     time_graphs(torch, graphs, 3)

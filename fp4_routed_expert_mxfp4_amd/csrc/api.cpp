@@ -174,10 +174,12 @@ MOE_FP4_API size_t moe_decode_layer_workspace_bytes(int32_t T, int32_t k, int32_
   return layer_ws_layout(T, k, E, hidden, inter, nullptr).total;
 }
 
+// norm: x_bf16 is the raw residual row; it is normalised first (as moe_rmsnorm_bf16, eps) and is
+// itself the residual (residual_bf16 is then ignored).
 static moe_status decode_layer(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E, int32_t k,
                                const int32_t* expert_to_slot, const moe_fp4_experts* w, const uint16_t* residual_bf16,
                                moe_out_dtype od, void* out, int32_t* topk_ids, float* topk_w, void* ws,
-                               size_t ws_bytes, int phase, hipStream_t stream) {
+                               size_t ws_bytes, int phase, hipStream_t stream, bool norm = false, float eps = 0.f) {
   if (T > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
   if (od != MOE_OUT_BF16 && od != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
   moe_status st = check_store(w);
@@ -188,16 +190,24 @@ static moe_status decode_layer(const float* logits, const uint16_t* x_bf16, int3
   if (!expert_to_slot && w->num_slots < E) return MOE_ERR_SHAPE;
   if (misaligned(x_bf16, 16) || misaligned(out, 16) || (residual_bf16 && misaligned(residual_bf16, 16)))
     return MOE_ERR_ALIGN;
-  const size_t need = moe_decode_layer_workspace_bytes(T, k, E, w->hidden, w->inter);
+  if (norm && !(eps >= 0.0f)) return MOE_ERR_SHAPE;
+  const size_t lbytes = moe_decode_layer_workspace_bytes(T, k, E, w->hidden, w->inter);
+  const size_t need = norm ? up256(lbytes) + up256((size_t)T * w->hidden * 2) : lbytes;
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
   if (misaligned(ws, 256)) return MOE_ERR_ALIGN;
   const moe::ExpertStore store = to_store(w);
   const bool bf16 = od == MOE_OUT_BF16;
+  if (norm) residual_bf16 = x_bf16;
   if (moe::fused_decode_supported(T, k, E, w->hidden, w->inter))
     return launched(moe::launch_decode_fused(logits, x_bf16, E, k, expert_to_slot, store, residual_bf16, bf16, out,
-                                             topk_ids, topk_w, ws, phase, stream));
+                                             topk_ids, topk_w, ws, phase, stream, norm, eps));
   const LayerWs l = layer_ws_layout(T, k, E, w->hidden, w->inter, ws);
   hipError_t e = hipSuccess;
+  if (norm) {  // the normalised rows after the layer's own workspace
+    uint16_t* n = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(ws) + up256(lbytes));
+    if (phase != 2) e = moe::launch_rmsnorm(x_bf16, T, w->hidden, eps, n, stream);
+    x_bf16 = n;
+  }
   if (phase != 2) {
     e = moe::launch_route(logits, T, E, k, expert_to_slot, topk_ids, topk_w, stream);
     if (e == hipSuccess)
@@ -238,6 +248,21 @@ MOE_FP4_API moe_status moe_decode_layer_down(const float* logits, const uint16_t
                                              hipStream_t stream) {
   return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out, topk_ids, topk_w, ws,
                       ws_bytes, 2, stream);
+}
+
+MOE_FP4_API size_t moe_decode_layer_rmsnorm_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t hidden,
+                                                            int32_t inter) {
+  if (T <= 0 || k <= 0 || hidden <= 0) return 0;
+  return up256(moe_decode_layer_workspace_bytes(T, k, E, hidden, inter)) + up256((size_t)T * hidden * 2);
+}
+
+MOE_FP4_API moe_status moe_decode_layer_rmsnorm(const float* logits, const uint16_t* x_bf16, float eps, int32_t T,
+                                                int32_t E, int32_t k, const int32_t* expert_to_slot,
+                                                const moe_fp4_experts* w, moe_out_dtype od, void* out,
+                                                int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                                                hipStream_t stream) {
+  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, nullptr, od, out, topk_ids, topk_w, ws, ws_bytes,
+                      0, stream, true, eps);
 }
 
 MOE_FP4_API size_t moe_ffn_fp4_prefill_workspace_bytes(int32_t T, int32_t k, int32_t hidden, int32_t inter) {

@@ -448,15 +448,66 @@ __device__ __forceinline__ void fused_gateup_rows(const FusedRoute& fr, const ui
   }
 }
 
-template <int NPL, int J>
+// The chain's weightless RMS norm of the token, folded into K1 (NORM): the
+// sum of squares is taken exactly as rmsnorm_kernel takes it for one row --
+// thread t of 256 accumulates elements 8t + 2048i in element order with fmaf,
+// each wave's 64 partials are summed by the xor butterfly, and the four wave
+// sums are added as (p0 + p1) + (p2 + p3) -- and every element is divided by
+// the same r, so the normalised row is bit-identical to moe_rmsnorm_bf16's.
+// Wavefront 0 routes meanwhile; wavefront 1 also takes wavefront 0's partials.
+constexpr int kNormMaxH = 6144;  // the largest hidden of the one-token layer
+
+__device__ __forceinline__ float norm_thread_sum(const uint16_t* __restrict__ x, int H, int t) {
+  float ss = 0.f;
+  for (int h = t * 8; h < H; h += 256 * 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(x + h);
+    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = bf16_bits_to_f32(q[i] & 0xFFFFu), b = bf16_bits_to_f32(q[i] >> 16);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+    }
+  }
+  return ss;
+}
+
+template <int NPL, int J, bool NORM>
 __global__ __launch_bounds__(kThreads, 2) void fused_gateup_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ x, int E, int k, const int32_t* __restrict__ e2s,
     ExpertStore w, FusedRoute* __restrict__ pub, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
-    float* __restrict__ h) {
+    float* __restrict__ h, float eps) {
   __shared__ FusedRoute fr;
-  fused_route<NPL>(logits, E, k, e2s, w.num_slots, fr, pub, topk_ids, topk_w);
-  fused_gateup_rows<J>(fr, x, k, w, h, blockIdx.x * kWaves + (threadIdx.x >> 6), gridDim.x * kWaves,
-                       threadIdx.x & 63);
+  __shared__ __attribute__((aligned(16))) uint16_t xn[NORM ? kNormMaxH : 8];
+  __shared__ float npart[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, H = w.H;
+  if (NORM && wave > 0) {
+    const float ss = wave_sum(norm_thread_sum(x, H, tid));
+    if (lane == 0) npart[wave] = ss;
+    if (wave == 1) {
+      const float s0 = wave_sum(norm_thread_sum(x, H, lane));
+      if (lane == 0) npart[0] = s0;
+    }
+  }
+  fused_route<NPL>(logits, E, k, e2s, w.num_slots, fr, pub, topk_ids, topk_w);  // ends on a barrier
+  const uint16_t* xs = x;
+  if (NORM) {
+    const float r = sqrtf(((npart[0] + npart[1]) + (npart[2] + npart[3])) / (float)H + eps);
+    for (int e = tid * 8; e < H; e += 256 * 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(x + e);
+      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = bf16_bits_to_f32(q[i] & 0xFFFFu) / r, b = bf16_bits_to_f32(q[i] >> 16) / r;
+        o[i] = (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+      }
+      *reinterpret_cast<uint4*>(xn + e) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    __syncthreads();
+    xs = xn;
+  }
+  fused_gateup_rows<J>(fr, xs, k, w, h, blockIdx.x * kWaves + wave, gridDim.x * kWaves, lane);
 }
 
 template <int M, bool TAIL, bool kBf16Out>
@@ -535,14 +586,20 @@ size_t fused_decode_workspace_bytes(int k, int I) {
 
 hipError_t launch_decode_fused(const float* logits, const uint16_t* x, int E, int k, const int32_t* e2s,
                                const ExpertStore& w, const uint16_t* residual, bool bf16_out, void* out,
-                               int32_t* topk_ids, float* topk_w, void* ws, int phase, hipStream_t s) {
+                               int32_t* topk_ids, float* topk_w, void* ws, int phase, hipStream_t s, bool norm,
+                               float eps) {
   FusedRoute* pub = reinterpret_cast<FusedRoute*>(ws);
   float* h = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + 512);
   const int J = w.H / 1024, npl = (E + 63) / 64;
   const dim3 g1(512), b1(kThreads);
   if (phase != 2) {
 #define MOE_FGU(NP, JJ)                                                                                      \
-  hipLaunchKernelGGL((fused_gateup_kernel<NP, JJ>), g1, b1, 0, s, logits, x, E, k, e2s, w, pub, topk_ids, topk_w, h)
+  if (norm)                                                                                                  \
+    hipLaunchKernelGGL((fused_gateup_kernel<NP, JJ, true>), g1, b1, 0, s, logits, x, E, k, e2s, w, pub, topk_ids, \
+                       topk_w, h, eps);                                                                      \
+  else                                                                                                       \
+    hipLaunchKernelGGL((fused_gateup_kernel<NP, JJ, false>), g1, b1, 0, s, logits, x, E, k, e2s, w, pub, topk_ids, \
+                       topk_w, h, eps)
 #define MOE_FGU_J(NP)                                                                                        \
   switch (J) { case 1: MOE_FGU(NP, 1); break; case 2: MOE_FGU(NP, 2); break; case 3: MOE_FGU(NP, 3); break;  \
                case 4: MOE_FGU(NP, 4); break; case 5: MOE_FGU(NP, 5); break; default: MOE_FGU(NP, 6); break; }

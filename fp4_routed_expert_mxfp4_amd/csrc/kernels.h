@@ -39,9 +39,12 @@ hipError_t launch_decode_mt(const uint16_t* x, int T, int k, int E, const Expert
 // Fused one-token decode layer (route + gate/up, then down + combine).
 bool fused_decode_supported(int T, int k, int E, int H, int I);
 size_t fused_decode_workspace_bytes(int k, int I);
+// norm: x is the raw residual row; K1 normalises it (as launch_rmsnorm does, bit
+// for bit) before the gate/up projection.
 hipError_t launch_decode_fused(const float* logits, const uint16_t* x, int E, int k, const int32_t* e2s,
                                const ExpertStore& w, const uint16_t* residual, bool bf16_out, void* out,
-                               int32_t* topk_ids, float* topk_w, void* ws, int phase, hipStream_t s);
+                               int32_t* topk_ids, float* topk_w, void* ws, int phase, hipStream_t s,
+                               bool norm = false, float eps = 0.f);
 
 // Prefill FFN on block-scaled MFMA with MXFP6 activations.
 size_t prefill_workspace_bytes(int T, int k, int H, int I);

@@ -227,6 +227,26 @@ MOE_FP4_API moe_status moe_decode_layer_down(const float* logits, const uint16_t
                                              moe_out_dtype od, void* out, int32_t* topk_ids, float* topk_w,
                                              void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_decode_layer_rmsnorm -- one layer of a chained decode: the weightless
+ * RMS norm of the bf16 residual rows x (exactly moe_rmsnorm_bf16 with eps),
+ * then moe_decode_layer on the normalised rows with x itself as the
+ * residual: out = x + sum_j w_j * FFN_j(rmsnorm(x)).  Bit-identical to
+ * moe_rmsnorm_bf16 followed by moe_decode_layer: the harness layer of the
+ * chained decode (the norm is the weightless one of moe_rmsnorm_bf16).  For
+ * one token at the one-token shapes of moe_decode_layer the norm runs inside
+ * its first kernel, which saves the norm kernel and its launch.
+ *   arguments as moe_decode_layer; eps >= 0 (else MOE_ERR_SHAPE)
+ *   ws: moe_decode_layer_rmsnorm_workspace_bytes(T, k, E, hidden, inter)
+ *       bytes, 256-byte aligned; contents on entry do not matter
+ * ------------------------------------------------------------------------- */
+MOE_FP4_API size_t moe_decode_layer_rmsnorm_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t hidden,
+                                                            int32_t inter);
+MOE_FP4_API moe_status moe_decode_layer_rmsnorm(const float* logits, const uint16_t* x_bf16, float eps, int32_t T,
+                                                int32_t E, int32_t k, const int32_t* expert_to_slot,
+                                                const moe_fp4_experts* w, moe_out_dtype od, void* out,
+                                                int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                                                hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * moe_ffn_fp4_prefill -- expert FFN of the prefill path on block-scaled MFMA.
  * Same contract as moe_ffn_fp4_decode except for the activation arithmetic,

@@ -159,6 +159,28 @@ def _layer_call(m, logits=FAKE, x=FAKE, T=1, E=8, k=2, e2s=None, store=None, res
                                     ws_bytes, None)
 
 
+def _norm_layer_call(m, logits=FAKE, x=FAKE, eps=1e-6, T=1, E=8, k=2, od=0, out=FAKE, ws=FAKE, ws_bytes=1 << 20):
+    st = _store(m, hidden=1024, inter=256)
+    return m.lib().moe_decode_layer_rmsnorm(logits, x, eps, T, E, k, None, ctypes.byref(st), od, out, FAKE, FAKE, ws,
+                                            ws_bytes, None)
+
+
+def test_decode_layer_rmsnorm_validation():
+    m = _lib()
+    # the layer's own workspace, then T x hidden bf16 for the normalised rows
+    assert m.decode_layer_rmsnorm_workspace_bytes(1, 8, 384, 5120, 2304) == 512 + 8 * 2304 * 4 + 5120 * 2
+    lb = m.decode_layer_workspace_bytes(16, 8, 384, 5120, 2304)
+    assert m.decode_layer_rmsnorm_workspace_bytes(16, 8, 384, 5120, 2304) == (lb + 255) // 256 * 256 + 16 * 5120 * 2
+    assert m.decode_layer_rmsnorm_workspace_bytes(0, 8, 384, 5120, 2304) == 0
+    assert _norm_layer_call(m, eps=-1.0) == m.MOE_ERR_SHAPE
+    assert _norm_layer_call(m, eps=float("nan")) == m.MOE_ERR_SHAPE
+    assert _norm_layer_call(m, x=None) == m.MOE_ERR_NULL
+    assert _norm_layer_call(m, x=MIS) == m.MOE_ERR_ALIGN
+    need = m.decode_layer_rmsnorm_workspace_bytes(1, 2, 8, 1024, 256)
+    assert _norm_layer_call(m, ws_bytes=need - 1) == m.MOE_ERR_WORKSPACE
+    assert _norm_layer_call(m, T=0, logits=None, x=None, out=None, ws=None) == m.MOE_OK
+
+
 def test_decode_layer_validation():
     m = _lib()
     # one token at a fused shape: the routing record plus h in [k][inter] fp32

@@ -5,8 +5,9 @@ fp64 oracle.
 * Every layer is one decode step: rmsnorm -> route over the layer's resident
   experts -> bucketing -> decode FFN -> combine with the residual.  Sampled
   layers are checked one by one on seeded inputs against the oracle's layer.
-* The whole 40-layer chain runs as one captured HIP graph (the launch the
-  benchmark times).  Its first layers are compared with the oracle's own
+* The whole 40-layer chain runs as one captured HIP graph of
+  moe_decode_layer_rmsnorm calls (the launch the benchmark times), bit-identical
+  to the chain of separate calls.  Its first layers are compared with the oracle's own
   chain; over all 40 layers the routing must equal the oracle's exactly and
   the stream must stay finite and unit-normalised.
 """
@@ -93,18 +94,21 @@ def test_chain_layer_matches_oracle(chain, layer):
 
 
 def test_chain_40_layers_graph(chain):
-    """The whole chain in one HIP graph, as the benchmark launches it."""
+    """The whole chain in one HIP graph, as the benchmark launches it (each layer one
+    moe_decode_layer_rmsnorm call); eager, it equals the chain of separate calls bit for bit."""
     import fp4_routed_expert_mxfp4_amd as m
     hi, stores, logits, e2s = chain
     L = CFG.layers
     b = buffers(m, L)
     xs = [torch.from_numpy(hi.x_bf16.view(np.int16)).cuda().view(torch.bfloat16)]
     xs += [torch.empty((CFG.T, CFG.H), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    lws = torch.empty(m.decode_layer_rmsnorm_workspace_bytes(CFG.T, CFG.k, CFG.E, CFG.H, CFG.I), dtype=torch.uint8,
+                      device="cuda")
 
     def token():
         for layer in range(L):
-            layer_step(m, xs[layer], stores[layer], logits[layer], e2s[layer], b["ids"][layer], b["w"][layer],
-                       b["off"][layer], b["sp"][layer], b["p2r"][layer], b["y"], b["ws"], b["n"], xs[layer + 1])
+            m.moe_decode_layer_rmsnorm(logits[layer], xs[layer], CFG.k, stores[layer], 1e-6, e2s[layer],
+                                       m.MOE_OUT_BF16, xs[layer + 1], b["ids"][layer], b["w"][layer], lws)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -113,6 +117,14 @@ def test_chain_40_layers_graph(chain):
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     eager = [to_np(x) for x in xs]
+    # the same chain as five separate calls per layer
+    sep = [xs[0].clone()] + [torch.empty_like(xs[0]) for _ in range(L)]
+    for layer in range(L):
+        layer_step(m, sep[layer], stores[layer], logits[layer], e2s[layer], b["ids"][layer], b["w"][layer],
+                   b["off"][layer], b["sp"][layer], b["p2r"][layer], b["y"], b["ws"], b["n"], sep[layer + 1])
+    torch.cuda.synchronize()
+    for layer in range(L + 1):
+        assert np.array_equal(to_np(sep[layer]), eager[layer]), layer
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         token()

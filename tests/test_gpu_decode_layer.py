@@ -170,3 +170,48 @@ def test_fused_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager[i][0]) and torch.equal(ids, eager[i][1]) and torch.equal(w, eager[i][2]), rep
+
+
+NORM_SHAPES = {
+    "decode1": gi.CONFIGS["decode1"],                                  # the norm inside K1, hidden 5120
+    "h6144_i2048_k1": FUSED_SHAPES["h6144_i2048_k1"],                  # the largest one-token hidden (6144)
+    "h1024_i256": FUSED_SHAPES["h1024_i256"],
+    "verify16": gi.CONFIGS["verify16"],                                # 16 rows: norm kernel + the layer
+    "tiny": gi.CONFIGS["tiny"],
+}
+
+
+@pytest.mark.parametrize("name", list(NORM_SHAPES))
+def test_rmsnorm_layer_bit_identical(name):
+    """moe_decode_layer_rmsnorm against moe_rmsnorm_bf16 then moe_decode_layer with x as
+    the residual: the same bits, for residual streams of chain-like magnitude."""
+    import fp4_routed_expert_mxfp4_amd as m
+    cfg = NORM_SHAPES[name]
+    print(f"case {name}", flush=True)
+    gl = GpuLayer(cfg)
+    rng = np.random.default_rng(17)
+    for scale in (3e5, 1.0):
+        x_np = gi.f32_to_bf16_bits((rng.standard_normal((cfg.T, cfg.H)) * scale).astype(np.float32))
+        x = _bf16(x_np)
+        n = m.moe_rmsnorm_bf16(x, 1e-6)
+        for od in (m.MOE_OUT_BF16, m.MOE_OUT_F32):
+            ref, ids_r, w_r = m.moe_decode_layer(gl.logits, n, cfg.k, gl.store, gl.e2s, x, od)
+            got, ids, w = m.moe_decode_layer_rmsnorm(gl.logits, x, cfg.k, gl.store, 1e-6, gl.e2s, od)
+            torch.cuda.synchronize()
+            assert torch.equal(ids, ids_r) and torch.equal(w, w_r)
+            assert torch.equal(got, ref), (name, scale, od)
+
+
+def test_rmsnorm_chain_layer_masked():
+    """A chain layer (154 of 384 experts, masked routing) through the norm-folded call."""
+    import fp4_routed_expert_mxfp4_amd as m
+    cfg = gi.CONFIGS["chain40"]
+    hi = gi.host_inputs(cfg)
+    gl = GpuLayer(cfg, layer=11, hi=hi)
+    rng = np.random.default_rng(11)
+    x = _bf16(gi.f32_to_bf16_bits((rng.standard_normal((1, cfg.H)) * 3e5).astype(np.float32)))
+    n = m.moe_rmsnorm_bf16(x, 1e-6)
+    ref, ids_r, _ = m.moe_decode_layer(gl.logits, n, cfg.k, gl.store, gl.e2s, x, m.MOE_OUT_BF16)
+    got, ids, _ = m.moe_decode_layer_rmsnorm(gl.logits, x, cfg.k, gl.store, 1e-6, gl.e2s, m.MOE_OUT_BF16)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids_r) and torch.equal(got, ref)
