@@ -173,7 +173,7 @@ constexpr int KC = 128;            // K per chunk (4 scale blocks, 2 MFMA K-step
 constexpr int GU_N = 128;          // gate/up tile: 128 h columns = 128 gate + 128 up weight rows
 constexpr int DN_N = 256;          // down tile: 256 output columns
 constexpr int STAGE_S = GU_N + 1;  // fp32 words per row of the h staging buffer
-constexpr int kGrid = 512;         // persistent workgroups (2 per CU)
+constexpr int kGrid = 256;         // persistent workgroups (one per CU: the LDS holds one)
 
 constexpr int SK_MAX = 32;  // buckets with at most this many rows take the streaming kernels
 
@@ -313,10 +313,10 @@ constexpr uint32_t kOpenRange = 0x7FFFFFF0u;  // range of the activation buffers
 // wavefront owns 64 weight rows (two 32-row B fragments) and all BM rows (four
 // A fragments): 8 MFMAs per K-step.  The weight rows are not shared between
 // wavefronts, so they go straight from memory into the wavefront's registers
-// in MFMA order, one chunk ahead.  The MXFP6 activations are shared: staged
-// once per chunk through LDS (double-buffered, one barrier per chunk).  Two
-// workgroups share a CU, so one's loads, barriers and epilogue overlap the
-// other's MFMAs.
+// in MFMA order, three chunks ahead.  The MXFP6 activations are shared: staged
+// once per chunk through LDS (double-buffered, one barrier per chunk).  The
+// scale tables and the h staging buffer fill most of the LDS, so one
+// workgroup runs per CU (one wavefront per SIMD).
 //
 // LDS layout of one A chunk: for each K-half h a region of BM rows x 48 B --
 // blocks h and 2+h of the chunk, i.e. the lane's A operand for K-steps 0 and 1
@@ -571,12 +571,13 @@ struct SkSrc {
 #pragma unroll
       for (int j = 0; j < 3; ++j) r.a[s][j] = bload8(ra, o + 8u * j);
     }
+    // the two chunks' 64-B halves of each row's 128-B line back to back
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) r.b[m][g][j] = bload16(rb[g], vb[g] + half * j + (uint32_t)(2 * n + m) * 64u);
+        for (int m = 0; m < 2; ++m) r.b[m][g][j] = bload16(rb[g], vb[g] + half * j + (uint32_t)(2 * n + m) * 64u);
   }
 };
 
@@ -641,7 +642,9 @@ __device__ __forceinline__ void sk_k_loop(const SkSrc& src, f16v (&acc)[2], int 
   }
 }
 
-constexpr int SK_GRID = 1024;  // workgroups of the streaming kernels (4 wavefronts each)
+// The streaming kernels launch one wavefront per possible unit (four per
+// workgroup); those past the plan's unit count exit at once, and the hardware
+// dispatcher balances the rest.
 
 __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, uint32_t xq_bytes, uint32_t xs_bytes, int P,
@@ -958,7 +961,9 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
                      dn, sbk, counts);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(gateup_skinny_kernel, dim3(SK_GRID), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, (int)P,
+  const size_t nsk = min((size_t)E, P);  // small buckets at most
+  const int gu_grid = (int)((nsk * (size_t)(I / 32) + 3) / 4), dn_grid = (int)((nsk * (size_t)(H / 64) + 3) / 4);
+  hipLaunchKernelGGL(gateup_skinny_kernel, dim3(gu_grid), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, (int)P,
                      w, sorted_pair, sbk, counts, hq, hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -966,7 +971,7 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
                      sorted_pair, gu, counts, hq, hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(down_skinny_kernel, dim3(SK_GRID), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, (int)P, w,
+  hipLaunchKernelGGL(down_skinny_kernel, dim3(dn_grid), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, (int)P, w,
                      sorted_pair, sbk, counts, y_pair);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
