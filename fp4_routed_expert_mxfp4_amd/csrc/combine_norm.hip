@@ -4,7 +4,9 @@
 // once each ("DeepSeek V4.1 Flash Q4 / 27 September 2026", "30 September
 // follow-up"), so the result does not depend on the order the experts ran in.
 // Each thread owns four consecutive outputs of one token and accumulates the
-// k slots in ascending j with fp32 FMAs; loads are 16-byte and coalesced.
+// k slots in ascending j with fp32 FMAs; loads are 16-byte and coalesced, and
+// eight slots' loads are in flight at once (slots past k re-read slot k-1 and
+// are not added).
 #include "common.cuh"
 #include "kernels.h"
 
@@ -22,13 +24,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
   const float* wt = w + (size_t)t * k;
   const float* yt = y + (size_t)t * k * H + h;
-  for (int j = 0; j < k; ++j) {
-    const float wj = wt[j];
-    const float4_t v = *reinterpret_cast<const float4_t*>(yt + (size_t)j * H);
-    acc.x = fmaf(wj, v.x, acc.x);
-    acc.y = fmaf(wj, v.y, acc.y);
-    acc.z = fmaf(wj, v.z, acc.z);
-    acc.w = fmaf(wj, v.w, acc.w);
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    float4_t v[8];
+    float wj[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = min(j0 + i, k - 1);
+      v[i] = *reinterpret_cast<const float4_t*>(yt + (size_t)j * H);
+      wj[i] = wt[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (j0 + i < k) {
+        acc.x = fmaf(wj[i], v[i].x, acc.x);
+        acc.y = fmaf(wj[i], v[i].y, acc.y);
+        acc.z = fmaf(wj[i], v[i].z, acc.z);
+        acc.w = fmaf(wj[i], v[i].w, acc.w);
+      }
+    }
   }
   if (kResidual) {
     const uint2 r = *reinterpret_cast<const uint2*>(res + (size_t)t * H + h);

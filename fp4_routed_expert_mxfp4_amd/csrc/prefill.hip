@@ -166,7 +166,10 @@ __global__ __launch_bounds__(kPT) void sort_x_kernel(const uint8_t* __restrict__
 // One small kernel turns the bucket offsets into two flat tile lists, one per
 // GEMM, ordered expert by expert, then by weight tile, then by row tile, so
 // the row tiles that share a weight tile are neighbours (and run at the same
-// time on one XCD, sharing that weight tile in its L2).
+// time on one XCD, sharing that weight tile in its L2).  Every workgroup
+// computes the per-expert tile prefix (a few thousand LDS operations) and
+// writes its grid-stride share of the tiles; workgroup 0 writes the
+// small-bucket list and the counts.
 
 constexpr int BM = 128;            // bucket rows per tile
 constexpr int KC = 128;            // K per chunk (4 scale blocks, 2 MFMA K-steps)
@@ -176,6 +179,7 @@ constexpr int STAGE_S = GU_N + 1;  // fp32 words per row of the h staging buffer
 constexpr int kGrid = 256;         // persistent workgroups (one per CU: the LDS holds one)
 
 constexpr int SK_MAX = 32;  // buckets with at most this many rows take the streaming kernels
+constexpr int kPlanGrid = 32;  // workgroups of the plan kernel
 
 struct SkBucket {
   int32_t row0;  // first sorted row
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(const int32_t* __restrict__ o
     const int e = tid * PER + i;
     mstart[e] = mrun;
     mrun += mt[i];
-    if (small[i]) {
+    if (small[i] && blockIdx.x == 0) {
       SkBucket b;
       b.row0 = offs[e];
       b.cnt = offs[e + 1] - offs[e];
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(const int32_t* __restrict__ o
     const int ntw = pass ? ntw_dn : ntw_gu;
     TileDesc* out = pass ? dn : gu;
     const int total = nm * ntw;
-    for (int t = tid; t < total; t += kPT) {
+    for (int t = blockIdx.x * kPT + tid; t < total; t += gridDim.x * kPT) {
       // expert e with mstart[e]*ntw <= t < mstart[e+1]*ntw (experts without row tiles have equal bounds)
       int lo = 0, hi = kMaxExperts - 1;
       while (lo < hi) {
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(const int32_t* __restrict__ o
       out[t] = d;
     }
   }
-  if (tid == 0) {
+  if (blockIdx.x == 0 && tid == 0) {
     counts[0] = nm * ntw_gu;
     counts[1] = nm * ntw_dn;
     counts[2] = ns;
@@ -957,7 +961,7 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
                      sorted_pair, xq, reinterpret_cast<uint32_t*>(xs));
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPT), 0, s, offsets, E, e2s, w.num_slots, I / GU_N, H / DN_N, gu,
+  hipLaunchKernelGGL(plan_kernel, dim3(kPlanGrid), dim3(kPT), 0, s, offsets, E, e2s, w.num_slots, I / GU_N, H / DN_N, gu,
                      dn, sbk, counts);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
