@@ -109,6 +109,9 @@ class DecodeBench:
         self.lws = torch.empty(m.decode_layer_workspace_bytes(T, k, E, cfg.H, cfg.I), dtype=torch.uint8,
                                device=dev)
         self.out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+        # the two waves of the expert-subset runs: even expert ids, then odd ones
+        even = (torch.arange(E, device=dev) % 2 == 0).to(torch.uint8)
+        self.waves = (even, 1 - even)
 
     def step(self, s: int, phase: int = 0) -> None:
         """One decode layer in one call (two kernels at this shape)."""
@@ -128,6 +131,17 @@ class DecodeBench:
         m.moe_route(self.logits[s], c.k, None, self.ids[s], self.w[s])
         m.moe_permute(self.ids[s], c.E, self.off[s], self.sp[s], self.p2r[s])
         m.moe_ffn_fp4_decode(self.x, c.k, c.E, self.store, None, self.off[s], self.sp[s], self.y, self.ws)
+        m.moe_combine(self.y, self.w[s], None, m.MOE_OUT_BF16, self.out)
+
+    def step_two_wave(self, s: int) -> None:
+        """The same layer with the expert FFN in two waves over complementary expert
+        subsets (every expert's weights read once, y_pair bit-identical)."""
+        m, c = self.m, self.cfg
+        m.moe_route(self.logits[s], c.k, None, self.ids[s], self.w[s])
+        m.moe_permute(self.ids[s], c.E, self.off[s], self.sp[s], self.p2r[s])
+        for run in self.waves:
+            m.moe_ffn_fp4_decode_subset(self.x, c.k, c.E, self.store, None, self.off[s], self.sp[s], run, self.y,
+                                        self.ws)
         m.moe_combine(self.y, self.w[s], None, m.MOE_OUT_BF16, self.out)
 
     def touched(self) -> list[int]:
@@ -259,8 +273,17 @@ def verify_section(args, torch, m, gd, gi):
     nbytes = sum(layer_bytes(cfg, touched[i % NSETS], cfg.T) for i in range(steps))
     per = t / steps
     log(f"verify16: {per * 1e6:.1f} us/step, {nbytes / t / 1e9:.0f} GB/s, {sum(touched) / NSETS:.1f} experts/step")
+    # the same steps as separate calls, and with the expert FFN in two waves (even, then odd expert ids)
+    extra = {}
+    for key, fn in (("separate_calls_us_per_step", db.step_separate), ("two_wave_us_per_step", db.step_two_wave)):
+        g = capture_many(torch, lambda i: fn(i % NSETS), NSETS)
+        time_graphs(torch, [g], 1)
+        extra[key] = time_graphs(torch, [g], 2) / (2 * NSETS) * 1e6
+        del g
+    log(f"verify16: separate calls {extra['separate_calls_us_per_step']:.1f} us/step, expert FFN in two waves "
+        f"{extra['two_wave_us_per_step']:.1f} us/step (same bytes)")
     return dict(us_per_step=per * 1e6, tokens_per_s=cfg.T / per, gbps=nbytes / t / 1e9,
-                frac_of_peak_hbm=nbytes / t / PEAK_HBM, experts_touched_mean=sum(touched) / NSETS)
+                frac_of_peak_hbm=nbytes / t / PEAK_HBM, experts_touched_mean=sum(touched) / NSETS, **extra)
 
 
 def read_ceiling(torch, gd) -> dict:

@@ -99,14 +99,14 @@ MOE_FP4_API size_t moe_ffn_fp4_decode_workspace_bytes(int32_t T, int32_t k, int3
 static moe_status decode_phase(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E, const moe_fp4_experts* w,
                                const int32_t* expert_to_slot, const int32_t* expert_offsets,
                                const int32_t* sorted_pair, float* y_pair, void* ws, size_t ws_bytes, int phase,
-                               hipStream_t stream) {
+                               hipStream_t stream, const uint8_t* run = nullptr) {
   if (T > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
   const size_t need = (T > 0 && k > 0 && w) ? moe::decode_workspace_bytes(T, k, w->inter) : 0;
   moe_status st = check_ffn_common(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, y_pair,
                                    ws, ws_bytes, need);
   if (st != MOE_OK || T == 0) return st;
   return launched(moe::launch_decode(x_bf16, T, k, E, to_store(w), expert_to_slot, expert_offsets,
-                                     sorted_pair, y_pair, ws, phase, stream));
+                                     sorted_pair, y_pair, ws, phase, stream, run));
 }
 
 MOE_FP4_API moe_status moe_ffn_fp4_decode(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
@@ -115,6 +115,16 @@ MOE_FP4_API moe_status moe_ffn_fp4_decode(const uint16_t* x_bf16, int32_t T, int
                                           float* y_pair, void* ws, size_t ws_bytes, hipStream_t stream) {
   return decode_phase(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, y_pair, ws, ws_bytes, 0,
                       stream);
+}
+
+MOE_FP4_API moe_status moe_ffn_fp4_decode_subset(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                                 const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                                 const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                                 const uint8_t* run_mask, float* y_pair, void* ws, size_t ws_bytes,
+                                                 hipStream_t stream) {
+  if (!run_mask && T > 0) return MOE_ERR_NULL;
+  return decode_phase(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, y_pair, ws, ws_bytes, 0,
+                      stream, run_mask);
 }
 
 MOE_FP4_API moe_status moe_ffn_fp4_decode_gateup(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
@@ -270,11 +280,10 @@ MOE_FP4_API size_t moe_ffn_fp4_prefill_workspace_bytes(int32_t T, int32_t k, int
   return moe::prefill_workspace_bytes(T, k, hidden, inter);
 }
 
-MOE_FP4_API moe_status moe_ffn_fp4_prefill(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
-                                           const moe_fp4_experts* w, const int32_t* expert_to_slot,
-                                           const int32_t* expert_offsets, const int32_t* sorted_pair,
-                                           moe_act_fmt act, float* y_pair, void* ws, size_t ws_bytes,
-                                           hipStream_t stream) {
+static moe_status prefill_call(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E, const moe_fp4_experts* w,
+                               const int32_t* expert_to_slot, const int32_t* expert_offsets,
+                               const int32_t* sorted_pair, moe_act_fmt act, float* y_pair, void* ws,
+                               size_t ws_bytes, hipStream_t stream, const uint8_t* run) {
   if (act != MOE_ACT_MXFP6_E2M3) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)T * k > (1 << 22)) return MOE_ERR_SHAPE;
   // the MXFP6 activations (x once per sorted row, and h) are addressed with 31-bit buffer offsets
@@ -288,7 +297,26 @@ MOE_FP4_API moe_status moe_ffn_fp4_prefill(const uint16_t* x_bf16, int32_t T, in
                                    ws, ws_bytes, need);
   if (st != MOE_OK || T == 0) return st;
   return launched(moe::launch_prefill(x_bf16, T, k, E, to_store(w), expert_to_slot, expert_offsets,
-                                      sorted_pair, y_pair, ws, stream));
+                                      sorted_pair, y_pair, ws, stream, run));
+}
+
+MOE_FP4_API moe_status moe_ffn_fp4_prefill(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                           const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                           const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                           moe_act_fmt act, float* y_pair, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  return prefill_call(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, act, y_pair, ws, ws_bytes,
+                      stream, nullptr);
+}
+
+MOE_FP4_API moe_status moe_ffn_fp4_prefill_subset(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                                  const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                                  const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                                  const uint8_t* run_mask, moe_act_fmt act, float* y_pair, void* ws,
+                                                  size_t ws_bytes, hipStream_t stream) {
+  if (!run_mask && T > 0) return MOE_ERR_NULL;
+  return prefill_call(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, act, y_pair, ws, ws_bytes,
+                      stream, run_mask);
 }
 
 MOE_FP4_API moe_status moe_combine(const float* y_pair, const float* topk_w, int32_t T, int32_t k, int32_t H,

@@ -212,7 +212,9 @@ struct ScaleRows {
   }
 };
 
-// Compact list of the non-empty buckets, built by wavefront 0 into LDS.
+// Compact list of the non-empty buckets, built by wavefront 0 into LDS.  With
+// a run mask ([E] bytes, nonzero: run now) only the buckets of masked-in
+// experts are listed, so every other bucket's rows are left untouched.
 struct Buckets {
   int n;
   int expert[kMaxExperts];
@@ -220,19 +222,26 @@ struct Buckets {
   int cnt[kMaxExperts];
 };
 
-__device__ inline void build_buckets(const int32_t* __restrict__ offsets, int E, Buckets& b) {
+__device__ inline void build_buckets(const int32_t* __restrict__ offsets, int E, Buckets& b,
+                                     const uint8_t* __restrict__ run) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     constexpr int CH = kMaxExperts / 64;
     int off[CH + 1];
+    bool on[CH];
 #pragma unroll
     for (int i = 0; i <= CH; ++i) {
       const int e = lane * CH + i;
       off[i] = offsets[e < E ? e : E];
     }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int e = lane * CH + i;
+      on[i] = e < E && off[i + 1] > off[i] && (run == nullptr || run[e] != 0);
+    }
     int n = 0;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) n += (lane * CH + i < E && off[i + 1] > off[i]) ? 1 : 0;
+    for (int i = 0; i < CH; ++i) n += on[i] ? 1 : 0;
     int incl = n;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -243,7 +252,7 @@ __device__ inline void build_buckets(const int32_t* __restrict__ offsets, int E,
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int e = lane * CH + i;
-      if (e < E && off[i + 1] > off[i]) {
+      if (on[i]) {
         b.expert[pos] = e;
         b.row0[pos] = off[i];
         b.cnt[pos] = off[i + 1] - off[i];

@@ -164,10 +164,11 @@ __device__ __forceinline__ void gu_finish(const GateUpBatch<J, R>& B, const uint
 template <int J, int R>
 __global__ __launch_bounds__(kThreads, 2) void gateup_fast_kernel(
     const uint16_t* __restrict__ x, int k, int E, ExpertStore w, const int32_t* __restrict__ e2s,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, float* __restrict__ h) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, const uint8_t* __restrict__ run,
+    float* __restrict__ h) {
   constexpr int NB = 32 * J;
   __shared__ Buckets bk;
-  build_buckets(offsets, E, bk);
+  build_buckets(offsets, E, bk, run);
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int total_waves = gridDim.x * kWaves;
@@ -275,11 +276,12 @@ __device__ __forceinline__ void dn_finish(const DownBatch<M, TAIL>& B, const flo
 template <int M, bool TAIL>
 __global__ __launch_bounds__(kThreads, 2) void down_fast_kernel(
     int k, int E, ExpertStore w, const int32_t* __restrict__ e2s, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_pair, const float* __restrict__ h, float* __restrict__ y) {
+    const int32_t* __restrict__ sorted_pair, const uint8_t* __restrict__ run, const float* __restrict__ h,
+    float* __restrict__ y) {
   constexpr int NB = 64 * M + (TAIL ? 8 : 0);
   constexpr int MM = M > 0 ? M : 1;
   __shared__ Buckets bk;
-  build_buckets(offsets, E, bk);
+  build_buckets(offsets, E, bk, run);
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int total_waves = gridDim.x * kWaves;
@@ -631,19 +633,19 @@ size_t decode_workspace_bytes(int T, int k, int I) {
 
 hipError_t launch_decode(const uint16_t* x, int T, int k, int E, const ExpertStore& w,
                          const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
-                         float* y_pair, void* ws, int phase, hipStream_t s) {
+                         float* y_pair, void* ws, int phase, hipStream_t s, const uint8_t* run) {
   const int J = w.H / 1024, NB2 = w.I / 32, M = NB2 / 64, tail = NB2 % 64;
   const bool one_token_shape = T == 1 && w.H % 1024 == 0 && J >= 1 && J <= 6 && (tail == 0 || tail == 8) &&
                                M <= 1 && (M > 0 || tail == 8);
   if (!one_token_shape)  // both halves on the multi-token kernels (their h layout differs)
-    return launch_decode_mt(x, T, k, E, w, e2s, offsets, sorted_pair, y_pair, ws, phase, s);
+    return launch_decode_mt(x, T, k, E, w, e2s, offsets, sorted_pair, y_pair, ws, phase, s, run);
   float* h = reinterpret_cast<float*>(ws);
   const dim3 fast_grid(512);
   if (phase != 2) {
 #define MOE_GU(JJ)                                                                                    \
   case JJ:                                                                                            \
     hipLaunchKernelGGL((gateup_fast_kernel<JJ, 2>), fast_grid, dim3(kThreads), 0, s, x, k, E, w, e2s, \
-                       offsets, sorted_pair, h);                                                      \
+                       offsets, sorted_pair, run, h);                                                 \
     break;
     switch (J) { MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5) MOE_GU(6) }
 #undef MOE_GU
@@ -652,7 +654,7 @@ hipError_t launch_decode(const uint16_t* x, int T, int k, int E, const ExpertSto
   }
 #define MOE_DN(MM, TT)                                                                                  \
   hipLaunchKernelGGL((down_fast_kernel<MM, TT>), fast_grid, dim3(kThreads), 0, s, k, E, w, e2s, offsets, \
-                     sorted_pair, h, y_pair)
+                     sorted_pair, run, h, y_pair)
   if (tail == 8) {
     if (M == 0) { MOE_DN(0, true); } else { MOE_DN(1, true); }
   } else {

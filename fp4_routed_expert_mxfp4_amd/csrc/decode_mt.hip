@@ -63,8 +63,8 @@ struct MtPlan {
   Buckets bk;
   int G[kMaxExperts + 1];
 
-  __device__ void build(const int32_t* __restrict__ offsets, int E) {
-    build_buckets(offsets, E, bk);
+  __device__ void build(const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ run) {
+    build_buckets(offsets, E, bk, run);
     if (threadIdx.x < 64) {
       const int lane = threadIdx.x, n = bk.n;
       constexpr int CH = kMaxExperts / 64;
@@ -245,11 +245,11 @@ __device__ __forceinline__ uint16_t bf16_lo_part(float v, uint16_t hi) {
 
 __global__ __launch_bounds__(kMtThreads, 2) void gateup_mt_kernel(
     const uint16_t* __restrict__ x, uint32_t x_bytes, int k, int E, ExpertStore w, const int32_t* __restrict__ e2s,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, uint16_t* __restrict__ hpl,
-    int P) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, const uint8_t* __restrict__ run,
+    uint16_t* __restrict__ hpl, int P) {
   __shared__ MtPlan pl;
   __shared__ uint32_t tabs[4][64 * kMtW];
-  pl.build(offsets, E);
+  pl.build(offsets, E, run);
   const int H = w.H, I = w.I, NB = H / 32, tiles = I / 32, nch = H / 128;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, q16 = lane & 15, g = lane >> 4;
   const int cb = wid * nch / 4, ce = (wid + 1) * nch / 4;
@@ -309,10 +309,11 @@ __global__ __launch_bounds__(kMtThreads, 2) void gateup_mt_kernel(
 
 __global__ __launch_bounds__(kMtThreads, 2) void down_mt_kernel(
     const uint16_t* __restrict__ hpl, int P, int E, ExpertStore w, const int32_t* __restrict__ e2s,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, float* __restrict__ y) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, const uint8_t* __restrict__ run,
+    float* __restrict__ y) {
   __shared__ MtPlan pl;
   __shared__ uint32_t tabs[4][64 * kMtW];
-  pl.build(offsets, E);
+  pl.build(offsets, E, run);
   const int H = w.H, I = w.I, NB = I / 32, tiles = H / 64, nch = I / 128;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, q16 = lane & 15, g = lane >> 4;
   const int cb = wid * nch / 4, ce = (wid + 1) * nch / 4;
@@ -367,17 +368,17 @@ __global__ __launch_bounds__(kMtThreads, 2) void down_mt_kernel(
 
 hipError_t launch_decode_mt(const uint16_t* x, int T, int k, int E, const ExpertStore& w, const int32_t* e2s,
                             const int32_t* offsets, const int32_t* sorted_pair, float* y_pair, void* ws, int phase,
-                            hipStream_t s) {
+                            hipStream_t s, const uint8_t* run) {
   const int P = T * k;
   uint16_t* hpl = reinterpret_cast<uint16_t*>(ws);
   if (phase != 2) {
     hipLaunchKernelGGL(gateup_mt_kernel, dim3(kMtGridGU), dim3(kMtThreads), 0, s, x,
-                       (uint32_t)((size_t)T * w.H * 2), k, E, w, e2s, offsets, sorted_pair, hpl, P);
+                       (uint32_t)((size_t)T * w.H * 2), k, E, w, e2s, offsets, sorted_pair, run, hpl, P);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess || phase == 1) return err;
   }
   hipLaunchKernelGGL(down_mt_kernel, dim3(kMtGridDN), dim3(kMtThreads), 0, s, hpl, P, E, w, e2s, offsets,
-                     sorted_pair, y_pair);
+                     sorted_pair, run, y_pair);
   return hipGetLastError();
 }
 

@@ -25,16 +25,18 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* offsets, in
 
 // Decode FFN: gate/up + SwiGLU into h (sorted-row order, in ws), then down.
 size_t decode_workspace_bytes(int T, int k, int I);
-// phase: 0 both kernels, 1 gate/up only, 2 down only.
+// phase: 0 both kernels, 1 gate/up only, 2 down only.  run: [E] bytes, or NULL
+// for every expert; the buckets of experts whose byte is 0 are skipped and
+// their y rows left as they are.
 hipError_t launch_decode(const uint16_t* x, int T, int k, int E, const ExpertStore& w,
                          const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
-                         float* y_pair, void* ws, int phase, hipStream_t s);
+                         float* y_pair, void* ws, int phase, hipStream_t s, const uint8_t* run = nullptr);
 
 // Multi-token decode FFN (bf16 MFMA); launch_decode uses it for every shape
 // the one-token kernels do not cover.  ws holds h as bf16 hi and lo planes.
 hipError_t launch_decode_mt(const uint16_t* x, int T, int k, int E, const ExpertStore& w, const int32_t* e2s,
                             const int32_t* offsets, const int32_t* sorted_pair, float* y_pair, void* ws, int phase,
-                            hipStream_t s);
+                            hipStream_t s, const uint8_t* run = nullptr);
 
 // Fused one-token decode layer (route + gate/up, then down + combine).
 bool fused_decode_supported(int T, int k, int E, int H, int I);
@@ -50,7 +52,7 @@ hipError_t launch_decode_fused(const float* logits, const uint16_t* x, int E, in
 size_t prefill_workspace_bytes(int T, int k, int H, int I);
 hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertStore& w,
                           const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
-                          float* y_pair, void* ws, hipStream_t s);
+                          float* y_pair, void* ws, hipStream_t s, const uint8_t* run = nullptr);
 
 hipError_t launch_combine(const float* y_pair, const float* w, int T, int k, int H,
                           const uint16_t* residual, bool bf16_out, void* out, hipStream_t s);

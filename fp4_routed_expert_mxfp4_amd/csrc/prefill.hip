@@ -218,7 +218,8 @@ __device__ int block_exclusive_sum(int v, int* part, int* total) {
 
 __global__ __launch_bounds__(kPT) void plan_kernel(const int32_t* __restrict__ offsets, int E,
                                                    const int32_t* __restrict__ e2s, int num_slots, int ntw_gu,
-                                                   int ntw_dn, TileDesc* __restrict__ gu, TileDesc* __restrict__ dn,
+                                                   int ntw_dn, const uint8_t* __restrict__ run,
+                                                   TileDesc* __restrict__ gu, TileDesc* __restrict__ dn,
                                                    SkBucket* __restrict__ sbk, int32_t* __restrict__ counts) {
   __shared__ int mstart[kMaxExperts + 1];
   __shared__ int offs[kMaxExperts + 1];  // the bucket offsets and slots, read once: the tile loop
@@ -239,7 +240,8 @@ __global__ __launch_bounds__(kPT) void plan_kernel(const int32_t* __restrict__ o
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = tid * PER + i;
-    const int c = e < E ? offs[e + 1] - offs[e] : 0;
+    // experts outside the run mask get no work: their rows are left untouched
+    const int c = (e < E && (run == nullptr || run[e] != 0)) ? offs[e + 1] - offs[e] : 0;
     small[i] = (c >= 1 && c <= SK_MAX) ? 1 : 0;
     mt[i] = small[i] ? 0 : (c + BM - 1) / BM;
     msum += mt[i];
@@ -932,7 +934,7 @@ size_t prefill_workspace_bytes(int T, int k, int H, int I) {
 
 hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertStore& w, const int32_t* e2s,
                           const int32_t* offsets, const int32_t* sorted_pair, float* y_pair, void* ws,
-                          hipStream_t s) {
+                          hipStream_t s, const uint8_t* run) {
   const int H = w.H, I = w.I;
   if (H % DN_N != 0 || I % GU_N != 0) return hipErrorInvalidValue;
   const size_t P = (size_t)T * k, nm = max_mtiles(P);
@@ -961,8 +963,8 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
                      sorted_pair, xq, reinterpret_cast<uint32_t*>(xs));
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(plan_kernel, dim3(kPlanGrid), dim3(kPT), 0, s, offsets, E, e2s, w.num_slots, I / GU_N, H / DN_N, gu,
-                     dn, sbk, counts);
+  hipLaunchKernelGGL(plan_kernel, dim3(kPlanGrid), dim3(kPT), 0, s, offsets, E, e2s, w.num_slots, I / GU_N, H / DN_N, run,
+                     gu, dn, sbk, counts);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const size_t nsk = min((size_t)E, P);  // small buckets at most

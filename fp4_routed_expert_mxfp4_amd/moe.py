@@ -22,10 +22,10 @@ MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
 MOE_OUT_BF16, MOE_OUT_F32 = 0, 1
 MOE_ACT_MXFP6_E2M3 = 0
 EXPORTED = ("moe_route", "moe_permute_workspace_bytes", "moe_permute", "moe_ffn_fp4_decode_workspace_bytes", "moe_ffn_fp4_decode",
-            "moe_ffn_fp4_decode_gateup", "moe_ffn_fp4_decode_down",
+            "moe_ffn_fp4_decode_gateup", "moe_ffn_fp4_decode_down", "moe_ffn_fp4_decode_subset",
             "moe_decode_layer_workspace_bytes", "moe_decode_layer", "moe_decode_layer_gateup",
             "moe_decode_layer_down", "moe_decode_layer_rmsnorm_workspace_bytes", "moe_decode_layer_rmsnorm",
-            "moe_ffn_fp4_prefill_workspace_bytes", "moe_ffn_fp4_prefill", "moe_combine",
+            "moe_ffn_fp4_prefill_workspace_bytes", "moe_ffn_fp4_prefill", "moe_ffn_fp4_prefill_subset", "moe_combine",
             "moe_rmsnorm_bf16", "moe_status_string")
 
 
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
             "moe_ffn_fp4_decode": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp, vp, sz, vp],
             "moe_ffn_fp4_decode_gateup": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp, vp, sz, vp],
             "moe_ffn_fp4_decode_down": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp, vp, sz, vp],
+            "moe_ffn_fp4_decode_subset": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp, vp, vp, sz,
+                                          vp],
             "moe_decode_layer_workspace_bytes": [i32, i32, i32, i32, i32],
             "moe_decode_layer": _LAYER_ARGS,
             "moe_decode_layer_gateup": _LAYER_ARGS,
@@ -73,6 +75,8 @@ def lib() -> ctypes.CDLL:
             "moe_ffn_fp4_prefill_workspace_bytes": [i32, i32, i32, i32],
             "moe_ffn_fp4_prefill": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, ctypes.c_int,
                                     vp, vp, sz, vp],
+            "moe_ffn_fp4_prefill_subset": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp,
+                                           ctypes.c_int, vp, vp, sz, vp],
             "moe_combine": [vp, vp, i32, i32, i32, vp, ctypes.c_int, vp, vp],
             "moe_rmsnorm_bf16": [vp, i32, i32, f32, vp, vp],
             "moe_status_string": [ctypes.c_int],
@@ -245,6 +249,25 @@ def moe_ffn_fp4_decode(x: torch.Tensor, k: int, E: int, store: ExpertStore,
                         y_pair, ws)
 
 
+def moe_ffn_fp4_decode_subset(x: torch.Tensor, k: int, E: int, store: ExpertStore,
+                              expert_to_slot: torch.Tensor | None, expert_offsets: torch.Tensor,
+                              sorted_pair: torch.Tensor, run_mask: torch.Tensor, y_pair: torch.Tensor | None = None,
+                              ws: torch.Tensor | None = None) -> torch.Tensor:
+    """The decode FFN over the experts whose ``run_mask`` byte ([E] uint8) is nonzero; the other
+    experts' rows of ``y_pair`` are left as they are."""
+    T, y_pair = _ffn_args(x, k, store, expert_to_slot, expert_offsets, sorted_pair, y_pair)
+    _want(run_mask, (torch.uint8,), "run_mask")
+    need = decode_workspace_bytes(T, k, store.inter)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _want(ws, (torch.uint8,), "ws")
+    cs = store.cstruct()
+    _check("moe_ffn_fp4_decode_subset", lib().moe_ffn_fp4_decode_subset(
+        _ptr(x), T, k, E, ctypes.byref(cs), _ptr(expert_to_slot), _ptr(expert_offsets), _ptr(sorted_pair),
+        _ptr(run_mask), _ptr(y_pair), _ptr(ws), ws.numel(), _stream(x.device)))
+    return y_pair
+
+
 def moe_ffn_fp4_decode_gateup(x, k, E, store, expert_to_slot, expert_offsets, sorted_pair, y_pair=None,
                               ws=None) -> torch.Tensor:
     """First kernel of the decode FFN: writes h into ``ws`` (y_pair untouched)."""
@@ -348,6 +371,25 @@ def moe_ffn_fp4_prefill(x: torch.Tensor, k: int, E: int, store: ExpertStore,
     _check("moe_ffn_fp4_prefill", lib().moe_ffn_fp4_prefill(
         _ptr(x), T, k, E, ctypes.byref(cs), _ptr(expert_to_slot), _ptr(expert_offsets), _ptr(sorted_pair),
         act, _ptr(y_pair), _ptr(ws), ws.numel(), _stream(x.device)))
+    return y_pair
+
+
+def moe_ffn_fp4_prefill_subset(x: torch.Tensor, k: int, E: int, store: ExpertStore,
+                               expert_to_slot: torch.Tensor | None, expert_offsets: torch.Tensor,
+                               sorted_pair: torch.Tensor, run_mask: torch.Tensor,
+                               y_pair: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                               act: int = MOE_ACT_MXFP6_E2M3) -> torch.Tensor:
+    """The prefill FFN over the experts whose ``run_mask`` byte is nonzero (see the decode form)."""
+    T, y_pair = _ffn_args(x, k, store, expert_to_slot, expert_offsets, sorted_pair, y_pair)
+    _want(run_mask, (torch.uint8,), "run_mask")
+    need = prefill_workspace_bytes(T, k, store.hidden, store.inter)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _want(ws, (torch.uint8,), "ws")
+    cs = store.cstruct()
+    _check("moe_ffn_fp4_prefill_subset", lib().moe_ffn_fp4_prefill_subset(
+        _ptr(x), T, k, E, ctypes.byref(cs), _ptr(expert_to_slot), _ptr(expert_offsets), _ptr(sorted_pair),
+        _ptr(run_mask), act, _ptr(y_pair), _ptr(ws), ws.numel(), _stream(x.device)))
     return y_pair
 
 

@@ -277,6 +277,33 @@ MOE_FP4_API moe_status moe_ffn_fp4_prefill(const uint16_t* x_bf16, int32_t T, in
                                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_ffn_fp4_decode_subset, moe_ffn_fp4_prefill_subset -- the expert FFN
+ * over a subset of the experts: the two-wave routed MoE of the M5 Max page
+ * ("DeepSeek V4.1 Flash Q4 / 27 September 2026", "30 September follow-up:
+ * prefill"), which computes the experts already on hand first and the rest
+ * once they arrive.  It is exact because every (token, slot) row is written
+ * once and the slot sum is a separate fixed-order kernel.
+ *   run_mask [E] uint8 on the device: nonzero = run this expert's bucket now
+ *   other arguments: as moe_ffn_fp4_decode / moe_ffn_fp4_prefill
+ * Rows of the buckets whose mask byte is 0 are not written (their y_pair
+ * rows keep whatever they held); every other row is exactly what the call
+ * without a mask writes.  So calls whose masks cover each expert once, on
+ * one stream (with one workspace, or one each), leave y_pair bit-identical
+ * to one call over all experts, and each expert's weights are read by one
+ * of them only.  A NULL run_mask with T >= 1 is MOE_ERR_NULL.
+ * ------------------------------------------------------------------------- */
+MOE_FP4_API moe_status moe_ffn_fp4_decode_subset(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                                 const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                                 const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                                 const uint8_t* run_mask, float* y_pair, void* ws,
+                                                 size_t ws_bytes, hipStream_t stream);
+MOE_FP4_API moe_status moe_ffn_fp4_prefill_subset(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                                  const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                                  const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                                  const uint8_t* run_mask, moe_act_fmt act, float* y_pair,
+                                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_combine -- fixed-order weighted slot sum ("30 September follow-up").
  *   out[t] = sum_{j=0..k-1} topk_w[t][j] * y_pair[t*k+j]   (ascending j, fp32)
  *            + residual[t]                                 (if not NULL)

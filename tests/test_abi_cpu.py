@@ -118,6 +118,27 @@ def test_decode_validation():
     assert m.decode_workspace_bytes(1, 8, 2304) == 8 * 2304 * 4
 
 
+def test_subset_validation():
+    """The expert-subset FFN calls need a run mask and otherwise validate as the calls without one."""
+    m = _lib()
+    L = m.lib()
+    st = _store(m)
+    dec = lambda x=FAKE, T=1, mask=FAKE, ws_bytes=1 << 20: L.moe_ffn_fp4_decode_subset(
+        x, T, 2, 8, ctypes.byref(st), None, FAKE, FAKE, mask, FAKE, FAKE, ws_bytes, None)
+    pre = lambda x=FAKE, T=4, mask=FAKE, act=0, ws_bytes=1 << 30: L.moe_ffn_fp4_prefill_subset(
+        x, T, 2, 8, ctypes.byref(st), None, FAKE, FAKE, mask, act, FAKE, FAKE, ws_bytes, None)
+    assert dec(mask=None) == m.MOE_ERR_NULL
+    assert dec(x=None) == m.MOE_ERR_NULL
+    assert dec(ws_bytes=16) == m.MOE_ERR_WORKSPACE
+    assert dec(T=300) == m.MOE_ERR_UNSUPPORTED
+    assert dec(T=0, mask=None) == m.MOE_OK
+    assert pre(mask=None) == m.MOE_ERR_NULL
+    assert pre(x=None) == m.MOE_ERR_NULL
+    assert pre(act=7) == m.MOE_ERR_UNSUPPORTED
+    assert pre(ws_bytes=0) == m.MOE_ERR_WORKSPACE
+    assert pre(T=0, mask=None) == m.MOE_OK
+
+
 def test_prefill_and_combine_validation():
     m = _lib()
     L = m.lib()
