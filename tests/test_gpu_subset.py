@@ -8,7 +8,8 @@ import pytest
 import torch
 
 from gen import inputs as gi
-from tests.harness import GpuLayer, to_np
+from oracle import moe_oracle as o
+from tests.harness import REL_TOL, GpuLayer, rel_err, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -67,6 +68,27 @@ def test_two_waves_equal_one_pass(name):
     _ffn(m, path, gl, off, sp, torch.from_numpy((~on).astype(np.uint8)).cuda(), y)
     torch.cuda.synchronize()
     assert np.array_equal(_bits(to_np(y)), _bits(full))
+
+
+@pytest.mark.parametrize("name", ["mid_resident", "prefill_mid_zipf", "prefill_tiny"])
+def test_first_wave_matches_oracle(name):
+    """The rows one wave writes against the oracle's rows of the same pairs (decode: the
+    unquantised reading; prefill: the MXFP6 reading)."""
+    m, path, cfg, gl, off, sp, pair_expert, _ = _setup(name)
+    on = np.zeros(cfg.E, dtype=bool)
+    on[::3] = True
+    on[pair_expert[0]] = True
+    y = torch.full((cfg.T * cfg.k, cfg.H), SENTINEL, dtype=torch.float32, device="cuda")
+    _ffn(m, path, gl, off, sp, torch.from_numpy(on.astype(np.uint8)).cuda(), y)
+    torch.cuda.synchronize()
+    ref = o.moe_layer(gl.hi.x_bf16, gl.hi.logits[gl.layer], gl.weights.matrix, cfg.k, cfg.H,
+                      "a16" if path == "decode" else "a6", gl.e2s_np)["y_pair"]
+    first = on[pair_expert]
+    got = to_np(y)
+    e = rel_err(got[first], ref[first])
+    print(f"[{name}] {int(first.sum())} of {first.size} rows, rel {e:.3e}", flush=True)
+    assert e <= REL_TOL
+    assert np.all(got[~first] == SENTINEL)
 
 
 @pytest.mark.parametrize("name", ["verify16", "prefill_tiny"])
