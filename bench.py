@@ -133,6 +133,16 @@ class DecodeBench:
         m.moe_ffn_fp4_decode(self.x, c.k, c.E, self.store, None, self.off[s], self.sp[s], self.y, self.ws)
         m.moe_combine(self.y, self.w[s], None, m.MOE_OUT_BF16, self.out)
 
+    def step_invariant(self, s: int) -> None:
+        """The same layer as four calls with the batch-invariant decode FFN (a token's
+        rows bit-identical alone or inside a verify batch)."""
+        m, c = self.m, self.cfg
+        m.moe_route(self.logits[s], c.k, None, self.ids[s], self.w[s])
+        m.moe_permute(self.ids[s], c.E, self.off[s], self.sp[s], self.p2r[s])
+        m.moe_ffn_fp4_decode_invariant(self.x, c.k, c.E, self.store, None, self.off[s], self.sp[s], self.y,
+                                       self.ws)
+        m.moe_combine(self.y, self.w[s], None, m.MOE_OUT_BF16, self.out)
+
     def step_two_wave(self, s: int) -> None:
         """The same layer with the expert FFN in two waves over complementary expert
         subsets (every expert's weights read once, y_pair bit-identical)."""
@@ -231,6 +241,11 @@ def decode_section(args, torch, m, gd, gi):
     sep_reps = max(1, min(args.steps, 512) // NSETS)
     t_sep = time_graphs(torch, [sep_graph], sep_reps) / (sep_reps * NSETS)
     del sep_graph
+    # the same four calls with the batch-invariant decode FFN
+    inv_graph = capture_many(torch, lambda i: db.step_invariant(i % NSETS), NSETS)
+    time_graphs(torch, [inv_graph], 2)
+    t_inv = time_graphs(torch, [inv_graph], sep_reps) / (sep_reps * NSETS)
+    del inv_graph
     # the gate/up kernel alone, then the down kernel alone: one graph of 64
     # back-to-back launches over the 64 routings, replayed; HIP events on the
     # replay stream bracket the whole timed region
@@ -247,8 +262,9 @@ def decode_section(args, torch, m, gd, gi):
     dn_bytes = cfg.k * (cfg.H * (cfg.I // 2 + cfg.I // 32)) + cfg.k * cfg.I * 4 + cfg.H * 2
     res = dict(seconds=t, gbps=gbps, ms_per_step=t / args.steps * 1e3, touched_mean=sum(touched) / NSETS,
                gateup_us=t_gu * 1e6, gateup_bytes=gu_bytes, down_us=t_dn * 1e6, down_bytes=dn_bytes,
-               separate_us=t_sep * 1e6, graph_per_step_us=t_launch * 1e6, db=db)
+               separate_us=t_sep * 1e6, invariant_us=t_inv * 1e6, graph_per_step_us=t_launch * 1e6, db=db)
     log(f"decode1: {res['ms_per_step'] * 1e3:.1f} us/step, {gbps:.0f} GB/s (separate calls: {t_sep * 1e6:.1f} us; "
+        f"separate calls, batch-invariant FFN: {t_inv * 1e6:.1f} us; "
         f"one graph launch per step: {t_launch * 1e6:.1f} us); "
         f"route+gate/up {t_gu * 1e6:.1f} us ({gu_bytes / t_gu / 1e9:.0f} GB/s), down+combine {t_dn * 1e6:.1f} us "
         f"({dn_bytes / t_dn / 1e9:.0f} GB/s)")
@@ -508,6 +524,7 @@ def main() -> int:
                    "weights": "e2m1 + UE8M0/32", "activations": "bf16"},
         "frac_of_peak_hbm": round(dec["gbps"] * 1e9 / PEAK_HBM, 4),
         "separate_calls_us_per_step": round(dec["separate_us"], 2),
+        "batch_invariant_separate_calls_us_per_step": round(dec["invariant_us"], 2),
         "graph_launch_per_step_us": round(dec["graph_per_step_us"], 2),
         "roofline": {"kernel": "decode route + gate/up + SwiGLU (fused_gateup_kernel, moe_decode_layer_gateup)",
                      "bound": "hbm",

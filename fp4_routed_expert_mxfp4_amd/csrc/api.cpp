@@ -99,12 +99,15 @@ MOE_FP4_API size_t moe_ffn_fp4_decode_workspace_bytes(int32_t T, int32_t k, int3
 static moe_status decode_phase(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E, const moe_fp4_experts* w,
                                const int32_t* expert_to_slot, const int32_t* expert_offsets,
                                const int32_t* sorted_pair, float* y_pair, void* ws, size_t ws_bytes, int phase,
-                               hipStream_t stream, const uint8_t* run = nullptr) {
+                               hipStream_t stream, const uint8_t* run = nullptr, bool invariant = false) {
   if (T > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
   const size_t need = (T > 0 && k > 0 && w) ? moe::decode_workspace_bytes(T, k, w->inter) : 0;
   moe_status st = check_ffn_common(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, y_pair,
                                    ws, ws_bytes, need);
   if (st != MOE_OK || T == 0) return st;
+  if (invariant)  // every batch size on the multi-token kernels, whose rows do not depend on the batch
+    return launched(moe::launch_decode_mt(x_bf16, T, k, E, to_store(w), expert_to_slot, expert_offsets,
+                                          sorted_pair, y_pair, ws, phase, stream, run));
   return launched(moe::launch_decode(x_bf16, T, k, E, to_store(w), expert_to_slot, expert_offsets,
                                      sorted_pair, y_pair, ws, phase, stream, run));
 }
@@ -115,6 +118,14 @@ MOE_FP4_API moe_status moe_ffn_fp4_decode(const uint16_t* x_bf16, int32_t T, int
                                           float* y_pair, void* ws, size_t ws_bytes, hipStream_t stream) {
   return decode_phase(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, y_pair, ws, ws_bytes, 0,
                       stream);
+}
+
+MOE_FP4_API moe_status moe_ffn_fp4_decode_invariant(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                                    const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                                    const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                                    float* y_pair, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_phase(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, y_pair, ws, ws_bytes, 0,
+                      stream, nullptr, true);
 }
 
 MOE_FP4_API moe_status moe_ffn_fp4_decode_subset(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,

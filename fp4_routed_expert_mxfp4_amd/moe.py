@@ -23,6 +23,7 @@ MOE_OUT_BF16, MOE_OUT_F32 = 0, 1
 MOE_ACT_MXFP6_E2M3 = 0
 EXPORTED = ("moe_route", "moe_permute_workspace_bytes", "moe_permute", "moe_ffn_fp4_decode_workspace_bytes", "moe_ffn_fp4_decode",
             "moe_ffn_fp4_decode_gateup", "moe_ffn_fp4_decode_down", "moe_ffn_fp4_decode_subset",
+            "moe_ffn_fp4_decode_invariant",
             "moe_decode_layer_workspace_bytes", "moe_decode_layer", "moe_decode_layer_gateup",
             "moe_decode_layer_down", "moe_decode_layer_rmsnorm_workspace_bytes", "moe_decode_layer_rmsnorm",
             "moe_ffn_fp4_prefill_workspace_bytes", "moe_ffn_fp4_prefill", "moe_ffn_fp4_prefill_subset", "moe_combine",
@@ -65,6 +66,8 @@ def lib() -> ctypes.CDLL:
             "moe_ffn_fp4_decode_down": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp, vp, sz, vp],
             "moe_ffn_fp4_decode_subset": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp, vp, vp, sz,
                                           vp],
+            "moe_ffn_fp4_decode_invariant": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp, vp, sz,
+                                             vp],
             "moe_decode_layer_workspace_bytes": [i32, i32, i32, i32, i32],
             "moe_decode_layer": _LAYER_ARGS,
             "moe_decode_layer_gateup": _LAYER_ARGS,
@@ -247,6 +250,15 @@ def moe_ffn_fp4_decode(x: torch.Tensor, k: int, E: int, store: ExpertStore,
                        ws: torch.Tensor | None = None) -> torch.Tensor:
     return _decode_call("moe_ffn_fp4_decode", x, k, E, store, expert_to_slot, expert_offsets, sorted_pair,
                         y_pair, ws)
+
+
+def moe_ffn_fp4_decode_invariant(x: torch.Tensor, k: int, E: int, store: ExpertStore,
+                                 expert_to_slot: torch.Tensor | None, expert_offsets: torch.Tensor,
+                                 sorted_pair: torch.Tensor, y_pair: torch.Tensor | None = None,
+                                 ws: torch.Tensor | None = None) -> torch.Tensor:
+    """The decode FFN with a token's rows bit-identical at every batch size (one token included)."""
+    return _decode_call("moe_ffn_fp4_decode_invariant", x, k, E, store, expert_to_slot, expert_offsets,
+                        sorted_pair, y_pair, ws)
 
 
 def moe_ffn_fp4_decode_subset(x: torch.Tensor, k: int, E: int, store: ExpertStore,

@@ -166,6 +166,21 @@ MOE_FP4_API moe_status moe_ffn_fp4_decode(const uint16_t* x_bf16, int32_t T, int
                                           float* y_pair, void* ws, size_t ws_bytes,
                                           hipStream_t stream);
 
+/* moe_ffn_fp4_decode_invariant -- moe_ffn_fp4_decode with every batch size on
+ * the multi-token (bf16 MFMA, h as hi + lo) arithmetic, so that a token's
+ * y_pair rows are bit-identical whether it is decoded alone or inside a batch
+ * (a verify round of speculative decoding): the single-box runtime's
+ * verification reproduces single-token decode bit for bit, and its hardest
+ * bugs were batched-versus-single disagreements ("Fast single-box DeepSeek
+ * v4.1 Flash runtime", "Dependency order and swarm split"; exact multi-row
+ * kernels, "Document map").  Same arguments and workspace as
+ * moe_ffn_fp4_decode; one token costs more than on the one-token kernels. */
+MOE_FP4_API moe_status moe_ffn_fp4_decode_invariant(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                                    const moe_fp4_experts* w, const int32_t* expert_to_slot,
+                                                    const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                                    float* y_pair, void* ws, size_t ws_bytes,
+                                                    hipStream_t stream);
+
 /* moe_ffn_fp4_decode_gateup, moe_ffn_fp4_decode_down -- the two kernels of
  * moe_ffn_fp4_decode as separate calls with the same arguments: gateup writes
  * h (sorted-row order) into the workspace, down reads it from there

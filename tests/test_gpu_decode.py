@@ -109,6 +109,36 @@ def test_multi_token_batch_invariant_bit_exact():
             assert torch.equal(y[i * k:(i + 1) * k], full[t * k:(t + 1) * k]), (sel, t)
 
 
+def test_invariant_decode_one_token_equals_batch_row():
+    """moe_ffn_fp4_decode_invariant: each of the 16 verify tokens decoded alone gives
+    the same y_pair rows, and the same combined output bits, as inside the
+    16-token batch; one full-size token stays within the oracle tolerance."""
+    import fp4_routed_expert_mxfp4_amd as m
+    cfg = gi.CONFIGS["verify16"]
+    gl = GpuLayer(cfg)
+    r = gl.run("decode")
+    k = cfg.k
+    for t in range(cfg.T):
+        ids, w = m.moe_route(gl.logits[t:t + 1].contiguous(), k)
+        off, sp, _ = m.moe_permute(ids, cfg.E)
+        y = m.moe_ffn_fp4_decode_invariant(gl.x[t:t + 1].contiguous(), k, cfg.E, gl.store, None, off, sp)
+        out = m.moe_combine(y, w, None, m.MOE_OUT_BF16)
+        torch.cuda.synchronize()
+        assert torch.equal(y, r["y_pair"][t * k:(t + 1) * k]), t
+        assert torch.equal(out.view(torch.int16), r["out16"][t:t + 1].view(torch.int16)), t
+    c1 = gi.CONFIGS["decode1"]
+    g1 = GpuLayer(c1)
+    ids, w = m.moe_route(g1.logits, c1.k)
+    off, sp, _ = m.moe_permute(ids, c1.E)
+    y = m.moe_ffn_fp4_decode_invariant(g1.x, c1.k, c1.E, g1.store, None, off, sp)
+    out = m.moe_combine(y, w, None, m.MOE_OUT_F32)
+    torch.cuda.synchronize()
+    ref = o.moe_layer(g1.hi.x_bf16, g1.hi.logits[0], g1.weights.matrix, c1.k, c1.H, "a16", None)
+    e = rel_err(to_np(out), ref["out"])
+    print(f"[decode1, invariant arithmetic] out fp32 rel {e:.3e}", flush=True)
+    assert e <= REL_TOL
+
+
 def test_integer_exact_case_bit_identical():
     """Weights +-1 and x = 1 keep every partial sum an integer below 2^24, and
     g >= 40 makes silu(g) == g in fp32 and fp64: the result must be exact."""
