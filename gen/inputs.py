@@ -19,7 +19,9 @@ Host draws (numpy PCG64 seeded with the config's seed), in this order:
 4. for every layer: ``rng.standard_normal((T, E)) + bias`` rounded to float32.
 
 Extra logit sets (used to rotate the experts a timing loop touches) come from
-a second generator PCG64([seed, 1 + layer]) with the same bias.
+a second generator PCG64([seed, 1 + layer]) with the same bias.  The router
+gate rows W_r (the projection upstream of the router) come from a third,
+PCG64([seed, 1000 + layer]), see router_weights.
 
 Weight bytes come from the SplitMix64 streams documented in gen/splitmix.py,
 keyed by expert id (not slot), so an expert's bytes do not depend on which
@@ -124,6 +126,23 @@ def logit_sets(cfg: Config, bias: np.ndarray, n: int, layer: int = 0) -> np.ndar
     """``n`` further logit sets float32 [n][T][E] for rotating a timing loop."""
     rng = np.random.Generator(np.random.PCG64([cfg.seed, 1 + layer]))
     return (rng.standard_normal((n, cfg.T, cfg.E)) + bias).astype(np.float32)
+
+
+def router_weights(cfg: Config, layer: int = 0) -> np.ndarray:
+    """Router gate rows W_r as bf16 bit patterns [E][H].
+
+    Draws ``rng.standard_normal((E, H)) / sqrt(H)`` from PCG64([seed, 1000 +
+    layer]), rounded to float32 and then to bf16 (nearest even).  With x ~
+    N(0,1) the projected logits have unit variance, like the configs' logits.
+    """
+    rng = np.random.Generator(np.random.PCG64([cfg.seed, 1000 + layer]))
+    w = rng.standard_normal((cfg.E, cfg.H)) / np.sqrt(cfg.H)
+    return f32_to_bf16_bits(w.astype(np.float32))
+
+
+def router_bias(hi: "HostInputs") -> np.ndarray | None:
+    """The config's per-expert popularity bias as float32 [E], or None without one."""
+    return hi.bias.astype(np.float32) if hi.cfg.zipf is not None else None
 
 
 class HostWeights:

@@ -133,6 +133,45 @@ def route(logits: np.ndarray, k: int, expert_to_slot: np.ndarray | None = None):
     return ids, w
 
 
+def router_logits(x_bf16: np.ndarray, w_router_bf16: np.ndarray, bias=None) -> np.ndarray:
+    """Router gate projection: logits[t][e] = sum_c x[t][c] * W_r[e][c] + bias[e].
+
+    The router runs before expert selection and the experts' reads cannot
+    start until it has ([M5] "30 September follow-up: prefill"; the split
+    router of "4 October follow-up"), but no page gives its form or
+    precision.  R-GATE: the
+    plain linear gate of a routed MoE layer -- W_r holds one row per expert
+    over the hidden size, in bf16 like the activations; bias (optional, one
+    value per expert, given as float32) is added to the dot product.  Here it
+    carries the per-expert popularity bias of the skewed synthetic routings.
+    x and W_r arrive as bf16 bit patterns; every step is fp64.
+    Returns fp64 [T][E].
+    """
+    x = bf16_bits_to_f64(x_bf16)
+    w = bf16_bits_to_f64(w_router_bf16)
+    if x.ndim != 2 or w.ndim != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("x [T][H] and W_r [E][H] must share H")
+    out = x @ w.T
+    if bias is not None:
+        b = np.asarray(bias, dtype=np.float32).astype(np.float64)
+        if b.shape != (w.shape[0],):
+            raise ValueError("bias must hold one value per expert")
+        out = out + b
+    return out
+
+
+def route_from_x(x_bf16, w_router_bf16, k: int, bias=None, expert_to_slot=None):
+    """Gate projection, then top-k routing (route above).
+
+    The logits are held as float32 (the router's input type), so the
+    selection is taken on the fp64 logits rounded once to float32.
+    Returns (logits fp64 [T][E], ids int32 [T][k], weights fp64 [T][k]).
+    """
+    l = router_logits(x_bf16, w_router_bf16, bias)
+    ids, w = route(l.astype(np.float32), k, expert_to_slot)
+    return l, ids, w
+
+
 # --------------------------------------------------------------------------
 # Token -> expert bucketing
 # --------------------------------------------------------------------------
