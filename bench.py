@@ -72,7 +72,8 @@ def parse():
     ap.add_argument("--no-chain", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("decode", "prefill", "chain", "verify"), default=None,
+    ap.add_argument("--no-router-gate", action="store_true")
+    ap.add_argument("--only", choices=("decode", "prefill", "chain", "verify", "router"), default=None,
                     help="run one section only (for profiling); prints that section's numbers")
     ap.add_argument("--calibrate", action="store_true",
                     help="only time torch's plain copy of 4 GiB (the HBM-bytes calibration kernel)")
@@ -379,6 +380,42 @@ def prefill_section(args, torch, m, gd, gi):
                 frac_of_binding_roofline=binding / per, frac_of_measured_mfma=flops / per / MFMA_MEASURED)
 
 
+def router_gate_section(args, torch, m, gd, gi):
+    """moe_route_x (gate projection + top-k) at one token, the 16-token verify
+    batch and the 4096-token chunk.  Each timed graph holds 40 back-to-back
+    calls over 40 distinct W_r copies (one per layer of the chained decode),
+    so no call finds its gate rows in cache from the previous one."""
+    import numpy as np
+    dev = torch.device("cuda")
+    out = {}
+    for name in ("decode1", "verify16", "prefill4096"):
+        cfg = gi.CONFIGS[name]
+        hi = gi.host_inputs(cfg)
+        T, E, H, k = cfg.T, cfg.E, cfg.H, cfg.k
+        x = torch.from_numpy(hi.x_bf16.view(np.int16)).to(dev)
+        w0 = torch.from_numpy(gi.router_weights(cfg).view(np.int16)).to(dev)
+        b_np = gi.router_bias(hi)
+        b = None if b_np is None else torch.from_numpy(b_np).to(dev)
+        layers = 40
+        wl = [w0.clone() for _ in range(layers)]
+        lg = torch.empty((T, E), dtype=torch.float32, device=dev)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+        g = capture_many(torch, lambda i: m.moe_route_x(x, wl[i], k, b, None, lg, ids, tw), layers)
+        reps = 5 if T > 64 else 50
+        time_graphs(torch, [g], 2)
+        per = time_graphs(torch, [g], reps) / (reps * layers)
+        nbytes = 2 * E * H + 2 * T * H + 4 * T * E + 8 * T * k
+        flops = 2.0 * T * E * H
+        out[name] = dict(us_per_call=per * 1e6, tokens=T, bytes=nbytes, GBps=nbytes / per / 1e9,
+                         frac_of_peak_hbm=nbytes / per / PEAK_HBM, tflops=flops / per / 1e12,
+                         kernels="gemv + router" if T <= 64 else "bf16 MFMA GEMM with in-kernel top-k")
+        log(f"router gate {name}: {per * 1e6:.2f} us/call, {nbytes / per / 1e9:.0f} GB/s, "
+            f"{flops / per / 1e12:.1f} TFLOP/s")
+        del wl
+    return out
+
+
 def chain_section(args, torch, m, gd, gi):
     cfg = gi.CONFIGS["chain40"]
     hi = gi.host_inputs(cfg)
@@ -489,7 +526,7 @@ def main() -> int:
 
     if args.only:
         fn = {"decode": decode_section, "prefill": prefill_section, "chain": chain_section,
-              "verify": verify_section}[args.only]
+              "verify": verify_section, "router": router_gate_section}[args.only]
         res = fn(args, torch, m, gd, gi)
         if isinstance(res, dict):
             res.pop("db", None)
@@ -502,6 +539,7 @@ def main() -> int:
     verify = None if args.no_verify else verify_section(args, torch, m, gd, gi)
     prefill = None if args.no_prefill else prefill_section(args, torch, m, gd, gi)
     chain = None if args.no_chain else chain_section(args, torch, m, gd, gi)
+    router = None if args.no_router_gate else router_gate_section(args, torch, m, gd, gi)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec["db"], gi)
 
     gu_achieved = dec["gateup_bytes"] / (dec["gateup_us"] * 1e-6)
@@ -539,6 +577,7 @@ def main() -> int:
         "verify16": verify,
         "prefill4096": prefill,
         "chain40": chain,
+        "router_gate": router,
     }
     print(json.dumps(result), flush=True)
     return 0

@@ -8,4 +8,4 @@ from .moe import (  # noqa: F401
     decode_layer_workspace_bytes, decode_layer_rmsnorm_workspace_bytes, moe_combine, moe_decode_layer,
     moe_decode_layer_rmsnorm, moe_ffn_fp4_decode, moe_ffn_fp4_decode_down, moe_ffn_fp4_decode_gateup,
     moe_ffn_fp4_decode_invariant, moe_ffn_fp4_decode_subset, moe_ffn_fp4_prefill, moe_ffn_fp4_prefill_subset, moe_permute, moe_rmsnorm_bf16,
-    moe_route, permute_workspace_bytes, prefill_workspace_bytes, status_string)
+    moe_route, moe_route_x, moe_router_logits, permute_workspace_bytes, prefill_workspace_bytes, status_string)

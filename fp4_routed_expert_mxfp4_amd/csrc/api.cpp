@@ -72,6 +72,37 @@ MOE_FP4_API moe_status moe_route(const float* logits, int32_t T, int32_t E, int3
   return launched(moe::launch_route(logits, T, E, k, expert_to_slot, topk_ids, topk_w, stream));
 }
 
+static moe_status check_router_gate(const uint16_t* x_bf16, int32_t T, int32_t hidden, const uint16_t* w_router,
+                                    int32_t E, const float* logits) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+  if (hidden < 256 || hidden % 256 != 0 || hidden > 16384) return MOE_ERR_SHAPE;
+  if ((int64_t)T * E > INT32_MAX) return MOE_ERR_SHAPE;
+  if ((int64_t)T * hidden * 2 >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;  // 31-bit buffer offsets
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !w_router || !logits) return MOE_ERR_NULL;
+  if (misaligned(x_bf16, 16) || misaligned(w_router, 16)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+MOE_FP4_API moe_status moe_router_logits(const uint16_t* x_bf16, int32_t T, int32_t hidden,
+                                         const uint16_t* w_router, int32_t E, const float* bias, float* logits,
+                                         hipStream_t stream) {
+  const moe_status st = check_router_gate(x_bf16, T, hidden, w_router, E, logits);
+  if (st != MOE_OK || T == 0) return st;
+  return launched(moe::launch_router_logits(x_bf16, T, hidden, w_router, E, bias, logits, stream));
+}
+
+MOE_FP4_API moe_status moe_route_x(const uint16_t* x_bf16, int32_t T, int32_t hidden, const uint16_t* w_router,
+                                   int32_t E, const float* bias, int32_t k, const int32_t* expert_to_slot,
+                                   float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  if (k < 1 || k > MOE_MAX_TOPK || k > E) return MOE_ERR_SHAPE;
+  const moe_status st = check_router_gate(x_bf16, T, hidden, w_router, E, logits);
+  if (st != MOE_OK || T == 0) return st;
+  if (!topk_ids || !topk_w) return MOE_ERR_NULL;
+  return launched(moe::launch_route_x(x_bf16, T, hidden, w_router, E, bias, k, expert_to_slot, logits, topk_ids,
+                                      topk_w, stream));
+}
+
 MOE_FP4_API size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E) {
   if (T < 0 || k < 1 || E < 1) return 0;
   return moe::permute_workspace_bytes(T * k, E);

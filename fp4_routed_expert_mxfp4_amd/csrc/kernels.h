@@ -19,6 +19,15 @@ struct ExpertStore {
 hipError_t launch_route(const float* logits, int T, int E, int k, const int32_t* e2s, int32_t* ids,
                         float* w, hipStream_t s);
 
+// Router gate projection logits = x . W_r^T (+ bias): bf16 x and W_r [E][H],
+// fp32 logits [T][E].  launch_route_x also routes (as launch_route), inside
+// the projection kernel when the batch takes the MFMA kernel and E fits its
+// LDS stage, else as a second kernel on the written logits.
+hipError_t launch_router_logits(const uint16_t* x, int T, int H, const uint16_t* wr, int E, const float* bias,
+                                float* logits, hipStream_t s);
+hipError_t launch_route_x(const uint16_t* x, int T, int H, const uint16_t* wr, int E, const float* bias, int k,
+                          const int32_t* e2s, float* logits, int32_t* ids, float* tw, hipStream_t s);
+
 size_t permute_workspace_bytes(int P, int E);
 hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pair,
                           int32_t* pair_to_row, void* ws, hipStream_t s);

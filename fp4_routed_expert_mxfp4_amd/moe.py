@@ -21,7 +21,7 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN = 0, 1, 2, 3
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
 MOE_OUT_BF16, MOE_OUT_F32 = 0, 1
 MOE_ACT_MXFP6_E2M3 = 0
-EXPORTED = ("moe_route", "moe_permute_workspace_bytes", "moe_permute", "moe_ffn_fp4_decode_workspace_bytes", "moe_ffn_fp4_decode",
+EXPORTED = ("moe_route", "moe_router_logits", "moe_route_x", "moe_permute_workspace_bytes", "moe_permute", "moe_ffn_fp4_decode_workspace_bytes", "moe_ffn_fp4_decode",
             "moe_ffn_fp4_decode_gateup", "moe_ffn_fp4_decode_down", "moe_ffn_fp4_decode_subset",
             "moe_ffn_fp4_decode_invariant",
             "moe_decode_layer_workspace_bytes", "moe_decode_layer", "moe_decode_layer_gateup",
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         _LAYER_ARGS = [vp, vp, i32, i32, i32, vp, ctypes.POINTER(CExperts), vp, ctypes.c_int, vp, vp, vp, vp, sz, vp]
         sig = {
             "moe_route": [vp, i32, i32, i32, vp, vp, vp, vp],
+            "moe_router_logits": [vp, i32, i32, vp, i32, vp, vp, vp],
+            "moe_route_x": [vp, i32, i32, vp, i32, vp, i32, vp, vp, vp, vp, vp],
             "moe_permute_workspace_bytes": [i32, i32, i32],
             "moe_permute": [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp],
             "moe_ffn_fp4_decode_workspace_bytes": [i32, i32, i32],
@@ -179,6 +181,50 @@ def moe_route(logits: torch.Tensor, k: int, expert_to_slot: torch.Tensor | None 
     _check("moe_route", lib().moe_route(_ptr(logits), T, E, k, _ptr(expert_to_slot), _ptr(topk_ids),
                                         _ptr(topk_w), _stream(dev)))
     return topk_ids, topk_w
+
+
+def _router_gate_args(x, w_router, bias, logits):
+    _want(x, (torch.bfloat16, torch.int16, torch.uint16), "x")
+    _want(w_router, (torch.bfloat16, torch.int16, torch.uint16), "w_router")
+    T, H = x.shape
+    E, H2 = w_router.shape
+    if H2 != H:
+        raise ValueError("x [T][H] and w_router [E][H] must share H")
+    if bias is not None:
+        _want(bias, (torch.float32,), "bias")
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _want(logits, (torch.float32,), "logits")
+    return T, H, E, logits
+
+
+def moe_router_logits(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor | None = None,
+                      logits: torch.Tensor | None = None) -> torch.Tensor:
+    """logits = x . w_router^T (+ bias): x [T][H], w_router [E][H] bf16 bits; fp32 [T][E]."""
+    T, H, E, logits = _router_gate_args(x, w_router, bias, logits)
+    _check("moe_router_logits", lib().moe_router_logits(_ptr(x), T, H, _ptr(w_router), E, _ptr(bias),
+                                                        _ptr(logits), _stream(x.device)))
+    return logits
+
+
+def moe_route_x(x: torch.Tensor, w_router: torch.Tensor, k: int, bias: torch.Tensor | None = None,
+                expert_to_slot: torch.Tensor | None = None, logits: torch.Tensor | None = None,
+                topk_ids: torch.Tensor | None = None, topk_w: torch.Tensor | None = None):
+    """Gate projection and top-k routing in one call; returns (logits, topk_ids, topk_w)."""
+    T, H, E, logits = _router_gate_args(x, w_router, bias, logits)
+    dev = x.device
+    if expert_to_slot is not None:
+        _want(expert_to_slot, (torch.int32,), "expert_to_slot")
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _want(topk_ids, (torch.int32,), "topk_ids")
+    _want(topk_w, (torch.float32,), "topk_w")
+    _check("moe_route_x", lib().moe_route_x(_ptr(x), T, H, _ptr(w_router), E, _ptr(bias), k,
+                                            _ptr(expert_to_slot), _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+                                            _stream(dev)))
+    return logits, topk_ids, topk_w
 
 
 def permute_workspace_bytes(T: int, k: int, E: int) -> int:

@@ -113,6 +113,40 @@ MOE_FP4_API moe_status moe_route(const float* logits, int32_t T, int32_t E, int3
                                  float* topk_w, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_router_logits -- the router's gate projection, the step before moe_route.
+ * The router runs before any expert can be read: prefill could stage only the
+ * experts "the router selected", which waits on the layer's router ("DeepSeek
+ * V4.1 Flash Q4 / 27 September 2026", "30 September follow-up: prefill"; the
+ * split router of its "4 October follow-up").  The pages give neither its
+ * form nor its precision; the reading implemented is the plain linear gate
+ *   logits[t][e] = sum_c x[t][c] * w_router[e][c] + bias[e]
+ * with bf16 x and W_r (every product exact in fp32) and fp32 sums in a fixed
+ * order, so the logits are run-to-run deterministic.  Up to 64 tokens run as
+ * a GEMV (one workgroup per expert row), larger batches as a bf16 MFMA GEMM.
+ *   x_bf16   [T][hidden] bf16 bits (16-byte aligned)
+ *   w_router [E][hidden] bf16 bits (16-byte aligned), row e = expert e
+ *   bias     [E] fp32 or NULL (added after the dot product)
+ *   logits   [T][E] fp32 out
+ * hidden % 256 == 0, 256 <= hidden <= 16384, 1 <= E <= MOE_MAX_EXPERTS,
+ * T*hidden*2 < 2^31 (else MOE_ERR_UNSUPPORTED).
+ * ------------------------------------------------------------------------- */
+MOE_FP4_API moe_status moe_router_logits(const uint16_t* x_bf16, int32_t T, int32_t hidden,
+                                         const uint16_t* w_router, int32_t E, const float* bias,
+                                         float* logits, hipStream_t stream);
+
+/* moe_route_x -- moe_router_logits followed by moe_route in one call: the
+ * gate projection and the top-k with the routable subset of moe_route.
+ * logits (required, [T][E] fp32) receives the projected logits; topk_ids and
+ * topk_w are exactly what moe_route writes for those logits.  Batches of more
+ * than 64 tokens with E <= 448 route inside the projection kernel (the
+ * logits of its 32 tokens are staged on chip); other calls launch the router
+ * kernel after the projection.  Arguments and limits: as moe_router_logits
+ * and moe_route. */
+MOE_FP4_API moe_status moe_route_x(const uint16_t* x_bf16, int32_t T, int32_t hidden, const uint16_t* w_router,
+                                   int32_t E, const float* bias, int32_t k, const int32_t* expert_to_slot,
+                                   float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_permute -- token-to-expert bucketing of the (token, slot) rows.
  * Pair p = t*k + j.  expert_offsets[e] = number of pairs routed to experts
  * below e (exclusive prefix sum of the per-expert counts; expert_offsets[E] =

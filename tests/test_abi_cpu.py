@@ -227,3 +227,31 @@ def test_decode_layer_validation():
     assert _layer_call(m, ws_bytes=512) == m.MOE_ERR_WORKSPACE
     assert _layer_call(m, ws=FAKE + 16) == m.MOE_ERR_ALIGN
     assert _layer_call(m, T=0, logits=None, x=None, out=None, ids=None, tw=None, ws=None) == m.MOE_OK
+
+
+def test_router_gate_validation():
+    """The gate projection calls check shapes, pointers and alignment before any launch."""
+    m = _lib()
+    L = m.lib()
+    lg = lambda x=FAKE, T=4, H=256, w=FAKE, E=8, out=FAKE: L.moe_router_logits(x, T, H, w, E, None, out, None)
+    assert lg(x=None) == m.MOE_ERR_NULL
+    assert lg(w=None) == m.MOE_ERR_NULL
+    assert lg(out=None) == m.MOE_ERR_NULL
+    assert lg(H=200) == m.MOE_ERR_SHAPE
+    assert lg(H=32768) == m.MOE_ERR_SHAPE
+    assert lg(E=0) == m.MOE_ERR_SHAPE
+    assert lg(E=2000) == m.MOE_ERR_SHAPE
+    assert lg(T=-1) == m.MOE_ERR_SHAPE
+    assert lg(x=MIS) == m.MOE_ERR_ALIGN
+    assert lg(w=MIS) == m.MOE_ERR_ALIGN
+    assert lg(T=1 << 20, H=1024) == m.MOE_ERR_UNSUPPORTED   # x past 31-bit buffer offsets
+    assert lg(T=0, x=None) == m.MOE_OK
+    rx = lambda T=4, k=2, E=8, ids=FAKE, w=FAKE, out=FAKE: L.moe_route_x(
+        FAKE, T, 256, FAKE, E, None, k, None, out, ids, w, None)
+    assert rx(k=0) == m.MOE_ERR_SHAPE
+    assert rx(k=9) == m.MOE_ERR_SHAPE
+    assert rx(k=17, E=64) == m.MOE_ERR_SHAPE
+    assert rx(ids=None) == m.MOE_ERR_NULL
+    assert rx(w=None) == m.MOE_ERR_NULL
+    assert rx(out=None) == m.MOE_ERR_NULL
+    assert rx(T=0, ids=None) == m.MOE_OK
