@@ -20,9 +20,8 @@ hipError_t launch_route(const float* logits, int T, int E, int k, const int32_t*
                         float* w, hipStream_t s);
 
 // Router gate projection logits = x . W_r^T (+ bias): bf16 x and W_r [E][H],
-// fp32 logits [T][E].  launch_route_x also routes (as launch_route), inside
-// the projection kernel when the batch takes the MFMA kernel and E fits its
-// LDS stage, else as a second kernel on the written logits.
+// fp32 logits [T][E].  launch_route_x then routes the written logits
+// (launch_route).
 hipError_t launch_router_logits(const uint16_t* x, int T, int H, const uint16_t* wr, int E, const float* bias,
                                 float* logits, hipStream_t s);
 hipError_t launch_route_x(const uint16_t* x, int T, int H, const uint16_t* wr, int E, const float* bias, int k,

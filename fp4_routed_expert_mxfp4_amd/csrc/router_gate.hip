@@ -13,19 +13,18 @@
 //    four partials are added in wavefront order.  The top-k then runs as the
 //    router kernel on the written logits (a token's k experts need all E
 //    logits, which here come from E different workgroups).
-//  * a chunk of tokens (prefill): a skinny GEMM on V_MFMA_F32_16X16X32_BF16.
-//    A workgroup takes 32 tokens (two 16-row A fragments) against every
-//    expert; each of its eight wavefronts owns every eighth 16-row fragment
-//    of W_r.  K runs in chunks of 64 with a ring of register sets in flight.
-//    With E <= 448 the 32 x E logits are also staged in LDS and the same
-//    workgroup routes its tokens (the router of route_core.cuh), so the
-//    projection and the top-k are one kernel.
+//  * a chunk of tokens (prefill): a GEMM on V_MFMA_F32_16X16X32_BF16 over
+//    64-token x 128-expert tiles.  K runs in chunks of 64: both operands'
+//    chunks are loaded once per workgroup with whole-line loads and shared
+//    through LDS, with a ring of chunks in flight.  Splitting the experts
+//    over workgroups keeps each CU's share of W_r reads to a third of W_r at
+//    384 experts.  The top-k runs as the router kernel on the written
+//    logits.
 // In both, lane (r, g) of a fragment supplies 16 consecutive bf16 of row r at
 // element 64c + 16g of chunk c, two K-steps of eight each; A and B use the
 // same K order, so the MFMA sums the plain dot product.
 #include "common.cuh"
 #include "kernels.h"
-#include "route_core.cuh"
 
 namespace moe {
 
@@ -107,109 +106,114 @@ __global__ __launch_bounds__(kGvThreads) void router_gemv_kernel(const uint16_t*
 }
 
 // ---------------------------------------------------------------------------
-// MFMA: 32 tokens x every expert per workgroup, optional in-kernel top-k
+// MFMA: a 64-token x 128-expert tile per workgroup
 // ---------------------------------------------------------------------------
 
-constexpr int kRmThreads = 512;   // eight wavefronts, two per SIMD
-constexpr int kRmWaves = kRmThreads / 64;
-constexpr int kRmTok = 32;        // tokens per workgroup
-constexpr int kRmFusedMaxE = 448; // 32 x (E + 1) fp32 logits fit the LDS stage
-constexpr int kRmStride = kRmFusedMaxE + 1;
+constexpr int kRmThreads = 512;  // eight wavefronts, two per SIMD
+constexpr int kRmTok = 64;       // tokens per tile: four 16-row A fragments
+constexpr int kRmExp = 128;      // experts per tile: eight 16-row W_r fragments
+constexpr int kRmAStride = 144;  // bytes per staged token row: 128 + 16 (rows land on distinct banks)
 
-template <int NF>
-struct RmChunk {
-  uint4_t a[2][2];   // [token fragment][K-step]
-  uint4_t b[NF][2];  // [expert fragment][K-step]
-};
-
-template <int NF, int RING, bool FUSED>
-__global__ __launch_bounds__(kRmThreads, 1) void router_mfma_kernel(
-    const uint16_t* __restrict__ x, int T, int H, const uint16_t* __restrict__ wr, int E,
-    const float* __restrict__ bias, float* __restrict__ logits, int k, const int32_t* __restrict__ e2s,
-    int32_t* __restrict__ ids, float* __restrict__ tw) {
-  __shared__ float lt[FUSED ? kRmTok * kRmStride : 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q16 = lane & 15, g = lane >> 4;
-  const int t0 = blockIdx.x * kRmTok;
+// Wavefront w = 4*tm + te takes token fragments 2tm, 2tm+1 and expert
+// fragments te, te+4 of the tile.  Per chunk of 64 K, the tile's 64 token
+// rows and 128 W_r rows (128 B each) are loaded once per workgroup -- every
+// load instruction covers eight whole 128-byte lines -- and staged in LDS,
+// from where each wavefront reads its fragments in MFMA order.  Ring slot s
+// holds the thread's pieces of the next chunk = s (mod RING), staged one
+// chunk before it is multiplied; every slot is refilled RING chunks ahead,
+// so the in-order wait for one slot never drains the loads of the others.
+template <int RING>
+__global__ __launch_bounds__(kRmThreads, 1) void router_mfma_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                                    const uint16_t* __restrict__ wr, int E,
+                                                                    const float* __restrict__ bias,
+                                                                    float* __restrict__ logits) {
+  __shared__ uint8_t sa[2][kRmTok * kRmAStride];  // the token rows' chunk, double-buffered
+  __shared__ uint8_t sb[2][kRmExp * kRmAStride];  // the W_r rows' chunk, double-buffered
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q16 = lane & 15, g = lane >> 4;
+  const int tm = wave >> 2, te = wave & 3;
+  const int t0 = blockIdx.x * kRmTok, e0 = blockIdx.y * kRmExp;
   const uint32_t rowb = (uint32_t)H * 2u;
   const rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)T * rowb));
   const rsrc_t wrr = make_rsrc(wr, (uint32_t)((size_t)E * rowb));
-  uint32_t va[2], vb[NF];
+  // staging: thread tid moves 16-byte piece tid%8 of token row tid/8, and of
+  // W_r rows tid/8 and 64 + tid/8; rows past the batch or the experts read zeros
+  const int ar = tid >> 3, ap = tid & 7;
+  const uint32_t vax = (t0 + ar < T) ? (uint32_t)(t0 + ar) * rowb + 16u * ap : kOob;
+  uint32_t vbx[2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int tok = t0 + 16 * m + q16;
-    va[m] = tok < T ? (uint32_t)tok * rowb + 32u * g : kOob;  // rows past the batch read zeros
-  }
-#pragma unroll
-  for (int j = 0; j < NF; ++j) {
-    const int er = 16 * (wave + kRmWaves * j) + q16;
-    vb[j] = er < E ? (uint32_t)er * rowb + 32u * g : kOob;    // rows past the experts read zeros
+  for (int h = 0; h < 2; ++h) {
+    const int er = e0 + 64 * h + ar;
+    vbx[h] = er < E ? (uint32_t)er * rowb + 16u * ap : kOob;
   }
   const int nch = H / 64;  // a multiple of RING (H % 256 == 0, RING <= 4)
-  auto load = [&](RmChunk<NF>& r, int c) {
+  uint4_t aring[RING], bring[RING][2];
+  auto load = [&](int slot, int c) {
     const uint32_t o = 128u * (uint32_t)c;
+    aring[slot] = bload16(xr, vax + o);
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) r.a[m][t] = bload16(xr, va[m] + o + 16u * t);
-#pragma unroll
-    for (int j = 0; j < NF; ++j)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) r.b[j][t] = bload16(wrr, vb[j] + o + 16u * t);
+    for (int h = 0; h < 2; ++h) bring[slot][h] = bload16(wrr, vbx[h] + o);
   };
-  f4v acc[2][NF];
+  auto stage = [&](int slot, int buf) {
+    *reinterpret_cast<uint4_t*>(sa[buf] + ar * kRmAStride + 16 * ap) = aring[slot];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<uint4_t*>(sb[buf] + (64 * h + ar) * kRmAStride + 16 * ap) = bring[slot][h];
+  };
+  f4v acc[2][2];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int j = 0; j < NF; ++j) acc[m][j] = f4v{0.f, 0.f, 0.f, 0.f};
-  RmChunk<NF> ring[RING];
+    for (int j = 0; j < 2; ++j) acc[m][j] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int r = 0; r < RING; ++r) load(ring[r], r);
+  for (int r = 0; r < RING; ++r) load(r, r);  // nch >= 4 >= RING
+  stage(0, 0);
+  load(0, min(RING, nch - 1));
   for (int c0 = 0; c0 < nch; c0 += RING) {
 #pragma unroll
     for (int r = 0; r < RING; ++r) {
+      const int c = c0 + r, s1 = (r + 1) % RING;
+      // chunk c sits in buffers c&1 (c0 is even, so that is r&1); buffers (c+1)&1 are free
+      __syncthreads();
+      stage(s1, (r + 1) & 1);
+      load(s1, min(c + 1 + RING, nch - 1));  // past the end: the last chunk again (in range, never used)
+      __builtin_amdgcn_sched_barrier(0);     // these loads go out before the LDS reads and MFMAs
+      uint4_t af[2][2], bf[2][2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          af[m][t] = *reinterpret_cast<const uint4_t*>(sa[r & 1] + (16 * (2 * tm + m) + q16) * kRmAStride + 32 * g +
+                                                       16 * t);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          bf[j][t] = *reinterpret_cast<const uint4_t*>(sb[r & 1] + (16 * (te + 4 * j) + q16) * kRmAStride + 32 * g +
+                                                       16 * t);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int j = 0; j < NF; ++j)
-            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ring[r].a[m][t]),
-                                                                as_bf16x8(ring[r].b[j][t]), acc[m][j], 0, 0, 0);
-      // refill the set with the chunk RING ahead; past the end, the last chunk
-      // again (in range, never multiplied), so no load sits behind a branch
-      const int cn = c0 + r + RING;
-      load(ring[r], cn < nch ? cn : nch - 1);
+          for (int j = 0; j < 2; ++j)
+            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[m][t]), as_bf16x8(bf[j][t]), acc[m][j],
+                                                                0, 0, 0);
     }
   }
-  // accumulator v of fragment pair (m, j): token t0 + 16m + 4g + v, expert 16(wave + 8j) + q16
+  // accumulator v of fragment pair (m, j): token t0 + 16(2tm + m) + 4g + v,
+  // expert e0 + 16(te + 4j) + q16
 #pragma unroll
-  for (int j = 0; j < NF; ++j) {
-    const int er = 16 * (wave + kRmWaves * j) + q16;
+  for (int j = 0; j < 2; ++j) {
+    const int er = e0 + 16 * (te + 4 * j) + q16;
     if (er >= E) continue;
     const float b = bias ? bias[er] : 0.f;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int r = 16 * m + 4 * g + v;
-        const float l = acc[m][j][v] + b;
-        if (t0 + r < T) logits[(size_t)(t0 + r) * E + er] = l;
-        if (FUSED) lt[r * kRmStride + er] = l;
+        const int t = t0 + 16 * (2 * tm + m) + 4 * g + v;
+        if (t < T) logits[(size_t)t * E + er] = acc[m][j][v] + b;
       }
-  }
-  if (FUSED) {
-    __syncthreads();
-    // wavefront w routes rows 4w .. 4w+3 of the tile from LDS
-#pragma unroll
-    for (int i = 0; i < kRmTok / kRmWaves; ++i) {
-      const int r = (kRmTok / kRmWaves) * wave + i, t = t0 + r;
-      if (t >= T) break;  // whole wavefront leaves together
-      const RoutePick pick = route_token<8>(lt + r * kRmStride, E, k, e2s, lane);
-      if (lane < k) {
-        ids[(size_t)t * k + lane] = pick.expert;
-        tw[(size_t)t * k + lane] = pick.weight;
-      }
-    }
   }
 }
 
@@ -235,33 +239,10 @@ hipError_t launch_gemv(const uint16_t* x, int T, int H, const uint16_t* wr, int 
   return hipGetLastError();
 }
 
-// fused: also route (k, e2s, ids, tw) inside the kernel; needs E <= kRmFusedMaxE
 hipError_t launch_mfma(const uint16_t* x, int T, int H, const uint16_t* wr, int E, const float* bias, float* logits,
-                       bool fused, int k, const int32_t* e2s, int32_t* ids, float* tw, hipStream_t s) {
-  const int nfrag = (E + 15) / 16, need = (nfrag + kRmWaves - 1) / kRmWaves;
-  const dim3 grid((T + kRmTok - 1) / kRmTok), block(kRmThreads);
-#define MOE_RM(NF, RING, FU)                                                                                  \
-  hipLaunchKernelGGL((router_mfma_kernel<NF, RING, FU>), grid, block, 0, s, x, T, H, wr, E, bias, logits, k, \
-                     e2s, ids, tw)
-  if (fused) {
-    switch (need) {
-      case 1: MOE_RM(1, 4, true); break;
-      case 2: MOE_RM(2, 4, true); break;
-      case 3: MOE_RM(3, 4, true); break;
-      default: MOE_RM(4, 4, true); break;
-    }
-  } else {
-    switch (need) {
-      case 1: MOE_RM(1, 4, false); break;
-      case 2: MOE_RM(2, 4, false); break;
-      case 3: MOE_RM(3, 4, false); break;
-      case 4: MOE_RM(4, 4, false); break;
-      case 5:
-      case 6: MOE_RM(6, 2, false); break;
-      default: MOE_RM(8, 2, false); break;
-    }
-  }
-#undef MOE_RM
+                       hipStream_t s) {
+  const dim3 grid((T + kRmTok - 1) / kRmTok, (E + kRmExp - 1) / kRmExp), block(kRmThreads);
+  hipLaunchKernelGGL((router_mfma_kernel<4>), grid, block, 0, s, x, T, H, wr, E, bias, logits);
   return hipGetLastError();
 }
 
@@ -270,13 +251,11 @@ hipError_t launch_mfma(const uint16_t* x, int T, int H, const uint16_t* wr, int 
 hipError_t launch_router_logits(const uint16_t* x, int T, int H, const uint16_t* wr, int E, const float* bias,
                                 float* logits, hipStream_t s) {
   if (T <= kGemvMaxT) return launch_gemv(x, T, H, wr, E, bias, logits, s);
-  return launch_mfma(x, T, H, wr, E, bias, logits, false, 0, nullptr, nullptr, nullptr, s);
+  return launch_mfma(x, T, H, wr, E, bias, logits, s);
 }
 
 hipError_t launch_route_x(const uint16_t* x, int T, int H, const uint16_t* wr, int E, const float* bias, int k,
                           const int32_t* e2s, float* logits, int32_t* ids, float* tw, hipStream_t s) {
-  if (T > kGemvMaxT && E <= kRmFusedMaxE)
-    return launch_mfma(x, T, H, wr, E, bias, logits, true, k, e2s, ids, tw, s);
   const hipError_t err = launch_router_logits(x, T, H, wr, E, bias, logits, s);
   if (err != hipSuccess) return err;
   return launch_route(logits, T, E, k, e2s, ids, tw, s);

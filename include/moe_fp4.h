@@ -137,11 +137,9 @@ MOE_FP4_API moe_status moe_router_logits(const uint16_t* x_bf16, int32_t T, int3
 /* moe_route_x -- moe_router_logits followed by moe_route in one call: the
  * gate projection and the top-k with the routable subset of moe_route.
  * logits (required, [T][E] fp32) receives the projected logits; topk_ids and
- * topk_w are exactly what moe_route writes for those logits.  Batches of more
- * than 64 tokens with E <= 448 route inside the projection kernel (the
- * logits of its 32 tokens are staged on chip); other calls launch the router
- * kernel after the projection.  Arguments and limits: as moe_router_logits
- * and moe_route. */
+ * topk_w are exactly what moe_route writes for those logits (the router
+ * kernel runs on them after the projection).  Arguments and limits: as
+ * moe_router_logits and moe_route. */
 MOE_FP4_API moe_status moe_route_x(const uint16_t* x_bf16, int32_t T, int32_t hidden, const uint16_t* w_router,
                                    int32_t E, const float* bias, int32_t k, const int32_t* expert_to_slot,
                                    float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream);

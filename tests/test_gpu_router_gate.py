@@ -29,11 +29,11 @@ CASES = {
     "decode1": (gi.CONFIGS["decode1"], None),                                 # GEMV, one token
     "verify16": (gi.CONFIGS["verify16"], None),                               # GEMV, Zipf bias
     "gemv64": (gi.custom("gemv64", 1024, 128, 48, 6, 64, seed=31, zipf=1.1), 30),  # largest GEMV batch, masked
-    "mfma65": (gi.custom("mfma65", 512, 128, 384, 8, 65, seed=32, zipf=1.1), None),  # fused MFMA, ragged tile
+    "mfma65": (gi.custom("mfma65", 512, 128, 384, 8, 65, seed=32, zipf=1.1), None),  # MFMA, ragged token tile
     "mfma_e8": (gi.custom("mfma_e8", 256, 128, 8, 2, 100, seed=33), 5),       # one partial expert fragment
     "mfma_e40": (gi.custom("mfma_e40", 768, 128, 40, 4, 200, seed=34, zipf=1.1), None),  # E % 16 != 0
-    "mfma_e500": (gi.custom("mfma_e500", 512, 128, 500, 8, 130, seed=35), None),   # E > 448: unfused top-k
-    "mfma_e1024": (gi.custom("mfma_e1024", 256, 128, 1024, 16, 96, seed=36), 700),  # largest E, ring of 2
+    "mfma_e500": (gi.custom("mfma_e500", 512, 128, 500, 8, 130, seed=35), None),   # four expert tiles
+    "mfma_e1024": (gi.custom("mfma_e1024", 256, 128, 1024, 16, 96, seed=36), 700),  # largest E, eight expert tiles
 }
 
 
