@@ -373,7 +373,7 @@ __device__ void fused_route(const float* __restrict__ logits, int E, int k, cons
     // rank of this slot's expert among the k picks (ties broken by slot)
     int r = 0;
     for (int i = 0; i < k; ++i) {
-      const int ei = __shfl(pick.expert, i, 64);
+      const int ei = __builtin_amdgcn_readlane(pick.expert, i);
       r += (ei < pick.expert || (ei == pick.expert && i < lane)) ? 1 : 0;
     }
     if (lane < k) {

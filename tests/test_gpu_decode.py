@@ -245,6 +245,39 @@ def test_route_masked_and_edge_cases():
             np.testing.assert_array_equal(to_np(a), b)
 
 
+def test_route_all_ties_and_fewer_routable():
+    """Every logit equal (each pick is decided by the lower expert index), and
+    fewer routable experts than k: the routable ones come first in rank order
+    with their softmax weights, then the best non-routable ones with weight 0."""
+    import fp4_routed_expert_mxfp4_amd as m
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(19)
+    for E, k in [(384, 8), (1024, 16), (70, 6)]:
+        logits = np.full((3, E), 0.75, np.float32)
+        logits[1] = np.round(rng.standard_normal(E)).astype(np.float32)  # a few distinct values, many ties
+        ids, w = m.moe_route(torch.from_numpy(logits).to(dev), k)
+        ref_ids, ref_w = o.route(logits, k)
+        np.testing.assert_array_equal(to_np(ids), ref_ids)
+        assert np.max(np.abs(to_np(w) - ref_w)) <= W_TOL
+        np.testing.assert_array_equal(to_np(ids)[0], np.arange(k))
+    for E, k, n_rout in [(40, 8, 5), (384, 8, 0), (1024, 16, 15)]:
+        logits = rng.standard_normal((4, E)).astype(np.float32)
+        e2s = np.full(E, -1, np.int32)
+        rout = np.sort(rng.choice(E, n_rout, replace=False))
+        e2s[rout] = np.arange(n_rout, dtype=np.int32)
+        ids, w = m.moe_route(torch.from_numpy(logits).to(dev), k, torch.from_numpy(e2s).to(dev))
+        ids, w = to_np(ids), to_np(w)
+        nonr = np.nonzero(e2s < 0)[0]
+        for t in range(logits.shape[0]):
+            first = rout[np.lexsort((rout, -logits[t, rout]))]
+            rest = nonr[np.lexsort((nonr, -logits[t, nonr]))][:k - n_rout]
+            np.testing.assert_array_equal(ids[t], np.concatenate([first, rest]))
+            assert np.all(w[t, n_rout:] == 0)
+            if n_rout:
+                _, ref_w = o.route(logits[t:t + 1], n_rout, e2s)
+                assert np.max(np.abs(w[t, :n_rout] - ref_w[0])) <= W_TOL
+
+
 def test_permute_large_and_empty():
     import fp4_routed_expert_mxfp4_amd as m
     dev = torch.device("cuda")
