@@ -409,7 +409,7 @@ def router_gate_section(args, torch, m, gd, gi):
         flops = 2.0 * T * E * H
         out[name] = dict(us_per_call=per * 1e6, tokens=T, bytes=nbytes, GBps=nbytes / per / 1e9,
                          frac_of_peak_hbm=nbytes / per / PEAK_HBM, tflops=flops / per / 1e12,
-                         kernels="gemv + router" if T <= 64 else "bf16 MFMA GEMM with in-kernel top-k")
+                         kernels=("router_skinny_kernel" if T <= 64 else "router_mfma_kernel") + " + route_kernel")
         log(f"router gate {name}: {per * 1e6:.2f} us/call, {nbytes / per / 1e9:.0f} GB/s, "
             f"{flops / per / 1e12:.1f} TFLOP/s")
         del wl

@@ -6,23 +6,20 @@
 // its cost sits in front of the expert streams of every layer.
 //
 // Two kernels, by batch size:
-//  * a few tokens (decode, a verify batch): one workgroup per expert row.  Its
-//    four wavefronts hold interleaved 512-element steps of the row in
-//    registers (one 16-byte load per lane and step) and run the tokens past
-//    them in groups; a wavefront's partial is reduced with DPP/permlane, the
-//    four partials are added in wavefront order.  The top-k then runs as the
-//    router kernel on the written logits (a token's k experts need all E
-//    logits, which here come from E different workgroups).
+//  * a few tokens (decode, a verify batch): one workgroup per 16 expert rows
+//    and every 16 tokens, on the same MFMA; its eight wavefronts take
+//    interleaved K-steps, issue all their loads in one round trip, and add
+//    their 16x16 partial tiles in LDS in wavefront order.
 //  * a chunk of tokens (prefill): a GEMM on V_MFMA_F32_16X16X32_BF16 over
 //    64-token x 128-expert tiles.  K runs in chunks of 64: both operands'
 //    chunks are loaded once per workgroup with whole-line loads and shared
 //    through LDS, with a ring of chunks in flight.  Splitting the experts
 //    over workgroups keeps each CU's share of W_r reads to a third of W_r at
-//    384 experts.  The top-k runs as the router kernel on the written
-//    logits.
-// In both, lane (r, g) of a fragment supplies 16 consecutive bf16 of row r at
-// element 64c + 16g of chunk c, two K-steps of eight each; A and B use the
-// same K order, so the MFMA sums the plain dot product.
+//    384 experts.
+// The top-k then runs as the router kernel on the written logits (a token's
+// k experts need all E logits, which come from several workgroups).
+// A and B fragments always take the same K order, so the MFMA sums the plain
+// dot product.
 #include "common.cuh"
 #include "kernels.h"
 
@@ -36,70 +33,58 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // ---------------------------------------------------------------------------
-// GEMV: one workgroup per expert row
+// Few tokens: one workgroup per 16 expert rows, K split over eight wavefronts
 // ---------------------------------------------------------------------------
 
-constexpr int kGvThreads = 256;
+constexpr int kSkThreads = 512;  // eight wavefronts: K-steps s = w (mod 8)
+constexpr int kSkBlock = 20;     // K-steps (32 elements each) loaded per round trip
 
-// 8 bf16 of W_r times 8 bf16 of x added to acc (products exact, fp32 sums in order).
-__device__ __forceinline__ float dot8_bf16(const uint4& w, const uint4& x, float acc) {
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, x.x), acc,
-                                        false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, x.y), acc,
-                                        false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, x.z), acc,
-                                        false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, x.w), acc,
-                                        false);
-  return acc;
-}
-
-// S: 512-element steps per wavefront (wavefront w takes steps w, w+4, ...),
-// TG: tokens per register group.
-template <int S, int TG>
-__global__ __launch_bounds__(kGvThreads) void router_gemv_kernel(const uint16_t* __restrict__ x, int T, int H,
-                                                                 const uint16_t* __restrict__ wr, int E,
-                                                                 const float* __restrict__ bias,
-                                                                 float* __restrict__ logits) {
-  __shared__ float part[4][TG];
-  const int e = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint16_t* row = wr + (size_t)e * H;
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-  int col[S];
-  uint4 wv[S];
+// A = 16 W_r rows (the expert fragment), B = 16 tokens; lane (r, g) supplies
+// 8 bf16 of row / token r at element 32s + 8g of K-step s.  Every load of a
+// block is issued before the block's MFMAs; steps past the wavefront's share
+// and rows past E or T read zeros (buffer range), so nothing is branched.
+// The eight partial 16x16 tiles meet in LDS and are added in wavefront order.
+__global__ __launch_bounds__(kSkThreads) void router_skinny_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                                   const uint16_t* __restrict__ wr, int E,
+                                                                   const float* __restrict__ bias,
+                                                                   float* __restrict__ logits) {
+  __shared__ float part[8][4 * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q16 = lane & 15, g = lane >> 4;
+  const int e0 = blockIdx.x * 16;
+  const uint32_t rowb = (uint32_t)H * 2u;
+  const rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)T * rowb));
+  const rsrc_t wrr = make_rsrc(wr, (uint32_t)((size_t)E * rowb));
+  const int ks = H / 256;  // K-steps per wavefront (H % 256 == 0)
+  const uint32_t vw = e0 + q16 < E ? (uint32_t)(e0 + q16) * rowb + 16u * g : kOob;
+  for (int t0 = 0; t0 < T; t0 += 16) {
+    const uint32_t vx = t0 + q16 < T ? (uint32_t)(t0 + q16) * rowb + 16u * g : kOob;
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+    for (int b0 = 0; b0 < ks; b0 += kSkBlock) {
+      uint4_t wa[kSkBlock], xb[kSkBlock];
 #pragma unroll
-  for (int i = 0; i < S; ++i) {
-    col[i] = (wave + 4 * i) * 512 + 8 * lane;
-    wv[i] = col[i] < H ? *reinterpret_cast<const uint4*>(row + col[i]) : zero;
-  }
-  const float b = bias ? bias[e] : 0.f;
-  for (int t0 = 0; t0 < T; t0 += TG) {
-    uint4 xv[TG][S];
+      for (int i = 0; i < kSkBlock; ++i) {
+        const int st = wave + 8 * (b0 + i);  // this wavefront's K-step
+        const uint32_t o = 64u * (uint32_t)st;
+        const bool in = b0 + i < ks;
+        wa[i] = bload16(wrr, in ? vw + o : kOob);
+        xb[i] = bload16(xr, in ? vx + o : kOob);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // the whole block's loads go out before its MFMAs
 #pragma unroll
-    for (int j = 0; j < TG; ++j)
-#pragma unroll
-      for (int i = 0; i < S; ++i)
-        xv[j][i] = (t0 + j < T && col[i] < H)
-                       ? *reinterpret_cast<const uint4*>(x + (size_t)(t0 + j) * H + col[i])
-                       : zero;
-    float acc[TG];
-#pragma unroll
-    for (int j = 0; j < TG; ++j) {
-      acc[j] = 0.f;
-#pragma unroll
-      for (int i = 0; i < S; ++i) acc[j] = dot8_bf16(wv[i], xv[j][i], acc[j]);
-      acc[j] = wave_sum_dpp(acc[j]);
+      for (int i = 0; i < kSkBlock; ++i)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[i]), as_bf16x8(xb[i]), acc, 0, 0, 0);
     }
-    if (lane == 0) {
+    // accumulator v: expert e0 + 4g + v, token t0 + q16
 #pragma unroll
-      for (int j = 0; j < TG; ++j) part[wave][j] = acc[j];
-    }
+    for (int v = 0; v < 4; ++v) part[wave][v * 64 + lane] = acc[v];
     __syncthreads();
-    if (threadIdx.x < TG && t0 + (int)threadIdx.x < T) {
-      const int j = threadIdx.x;
-      const float s = (part[0][j] + part[1][j]) + (part[2][j] + part[3][j]);
-      logits[(size_t)(t0 + j) * E + e] = s + b;
+    if (tid < 256) {
+      const int v = tid >> 6, l = tid & 63;
+      const int e = e0 + 4 * (l >> 4) + v, t = t0 + (l & 15);
+      float sum = part[0][tid];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) sum += part[w][tid];
+      if (e < E && t < T) logits[(size_t)t * E + e] = sum + (bias ? bias[e] : 0.f);
     }
     __syncthreads();  // part is rewritten by the next token group
   }
@@ -114,6 +99,8 @@ constexpr int kRmTok = 64;       // tokens per tile: four 16-row A fragments
 constexpr int kRmExp = 128;      // experts per tile: eight 16-row W_r fragments
 constexpr int kRmAStride = 144;  // bytes per staged token row: 128 + 16 (rows land on distinct banks)
 
+// Lane (r, g) of a fragment supplies 16 consecutive bf16 of row r at element
+// 64c + 16g of chunk c, two K-steps of eight each.
 // Wavefront w = 4*tm + te takes token fragments 2tm, 2tm+1 and expert
 // fragments te, te+4 of the tile.  Per chunk of 64 K, the tile's 64 token
 // rows and 128 W_r rows (128 B each) are loaded once per workgroup -- every
@@ -217,25 +204,11 @@ __global__ __launch_bounds__(kRmThreads, 1) void router_mfma_kernel(const uint16
   }
 }
 
-constexpr int kGemvMaxT = 64;  // larger batches take the MFMA kernel
+constexpr int kSkinnyMaxT = 64;  // larger batches take the tiled kernel
 
-hipError_t launch_gemv(const uint16_t* x, int T, int H, const uint16_t* wr, int E, const float* bias, float* logits,
-                       hipStream_t s) {
-  const int S = (H + 2047) / 2048;
-  const dim3 grid(E), block(kGvThreads);
-#define MOE_GV(SS, TG) \
-  hipLaunchKernelGGL((router_gemv_kernel<SS, TG>), grid, block, 0, s, x, T, H, wr, E, bias, logits)
-  switch (S) {
-    case 1: MOE_GV(1, 8); break;
-    case 2: MOE_GV(2, 8); break;
-    case 3: MOE_GV(3, 8); break;
-    case 4: MOE_GV(4, 4); break;
-    case 5: MOE_GV(5, 4); break;
-    case 6: MOE_GV(6, 4); break;
-    case 7: MOE_GV(7, 2); break;
-    default: MOE_GV(8, 2); break;
-  }
-#undef MOE_GV
+hipError_t launch_skinny(const uint16_t* x, int T, int H, const uint16_t* wr, int E, const float* bias,
+                         float* logits, hipStream_t s) {
+  hipLaunchKernelGGL(router_skinny_kernel, dim3((E + 15) / 16), dim3(kSkThreads), 0, s, x, T, H, wr, E, bias, logits);
   return hipGetLastError();
 }
 
@@ -250,7 +223,7 @@ hipError_t launch_mfma(const uint16_t* x, int T, int H, const uint16_t* wr, int 
 
 hipError_t launch_router_logits(const uint16_t* x, int T, int H, const uint16_t* wr, int E, const float* bias,
                                 float* logits, hipStream_t s) {
-  if (T <= kGemvMaxT) return launch_gemv(x, T, H, wr, E, bias, logits, s);
+  if (T <= kSkinnyMaxT) return launch_skinny(x, T, H, wr, E, bias, logits, s);
   return launch_mfma(x, T, H, wr, E, bias, logits, s);
 }
 
