@@ -421,32 +421,60 @@ __device__ __forceinline__ void fused_gateup_rows(const FusedRoute& fr, const ui
 #pragma unroll
     for (int q = 0; q < 4; ++q) xr[j][q] = px[q];
   }
-  for (int unit = gw; unit < units; unit += total_waves) {
-    const int b = unit / C, c = unit - b * C;
-    const int bat0 = c * cs, bat1 = min(bat0 + cs, nbat);
-    if (bat0 >= bat1) continue;
-    const int slot = fr.slot[b];
-    if (slot < 0) continue;  // no stored expert: the down half contributes zero rows
-    const uint8_t* cb[2] = {w.wg + (size_t)slot * I * rowbytes, w.wu + (size_t)slot * I * rowbytes};
-    const uint8_t* sb[2] = {w.sg + (size_t)slot * I * NB, w.su + (size_t)slot * I * NB};
+  // Batch slot q = batch q % nbat of bucket q / nbat.  Wavefront gw takes
+  // slots gw, gw + total_waves, ...: consecutive batches of one wavefront lie
+  // in different experts and rows, so each wavefront samples many regions of
+  // HBM instead of streaming one contiguous range.
+  int matj[J], blkj[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int f = lane + 64 * j;
+    matj[j] = f >= NB ? 1 : 0;
+    blkj[j] = f - matj[j] * NB;
+  }
+  struct Where {
     const uint8_t* cp[J];
     const uint8_t* sp[J];
+    float* hrow;
+    int n0;
+    bool store;
+  };
+  auto where = [&](int q, Where& wh) {
+    const int b = q / nbat, bat = q - b * nbat;
+    const int slot = fr.slot[b];
+    wh.store = slot >= 0;  // no stored expert: the down half contributes zero rows
+    const size_t s0 = (size_t)(slot >= 0 ? slot : 0);
+    const uint8_t* cb[2] = {w.wg + s0 * I * rowbytes, w.wu + s0 * I * rowbytes};
+    const uint8_t* sb[2] = {w.sg + s0 * I * NB, w.su + s0 * I * NB};
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int f = lane + 64 * j, mat = f >= NB ? 1 : 0, blk = f - mat * NB;
-      cp[j] = cb[mat] + blk * 16;
-      sp[j] = sb[mat] + blk;
+      wh.cp[j] = cb[matj[j]] + blkj[j] * 16;
+      wh.sp[j] = sb[matj[j]] + blkj[j];
     }
-    float* hrow = h + (size_t)b * I;
-    GateUpBatch<J, R> A, Bn;
-    gu_load(A, cp, sp, bat0 * R, rowbytes, NB);
-    for (int bat = bat0; bat < bat1; bat += 2) {
-      const bool has1 = bat + 1 < bat1;
-      if (has1) gu_load(Bn, cp, sp, (bat + 1) * R, rowbytes, NB);
-      gu_finish(A, xr, lane, hrow, bat * R);
-      if (bat + 2 < bat1) gu_load(A, cp, sp, (bat + 2) * R, rowbytes, NB);
-      if (has1) gu_finish(Bn, xr, lane, hrow, (bat + 1) * R);
+    wh.hrow = h + (size_t)b * I;
+    wh.n0 = bat * R;
+  };
+  (void)cs;
+  (void)units;
+  const int nslot = k * nbat;
+  if (gw >= nslot) return;
+  Where wa, wb;
+  GateUpBatch<J, R> A, Bn;
+  where(gw, wa);
+  gu_load(A, wa.cp, wa.sp, wa.n0, rowbytes, NB);
+  for (int q = gw; q < nslot; q += 2 * total_waves) {
+    const int q1 = q + total_waves, q2 = q + 2 * total_waves;
+    const bool has1 = q1 < nslot;
+    if (has1) {
+      where(q1, wb);
+      gu_load(Bn, wb.cp, wb.sp, wb.n0, rowbytes, NB);
     }
+    if (wa.store) gu_finish(A, xr, lane, wa.hrow, wa.n0);
+    if (q2 < nslot) {
+      where(q2, wa);
+      gu_load(A, wa.cp, wa.sp, wa.n0, rowbytes, NB);
+    }
+    if (has1 && wb.store) gu_finish(Bn, xr, lane, wb.hrow, wb.n0);
   }
 }
 
