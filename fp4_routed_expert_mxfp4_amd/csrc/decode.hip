@@ -343,7 +343,8 @@ __global__ __launch_bounds__(kThreads, 2) void down_fast_kernel(
 // K1 (route + gate/up): every workgroup routes the token itself (one
 //   wavefront, the router of route_core.cuh), so no workgroup waits for
 //   another; the buckets of a one-token batch are its k experts in ascending
-//   id.  Then the same gate/up row walk as gateup_fast_kernel writes h.
+//   id.  Then gate/up batches of gateup_fast_kernel's arithmetic, dealt out
+//   interleaved over all (expert, batch) pairs, write h.
 //   Workgroup 0 also publishes the routing for K2 and the caller.
 // K2 (down + combine): one wavefront per routed expert over a slice of 24
 //   output rows (three 8-row batches of down_fast_kernel's walk); the k rows
