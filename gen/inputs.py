@@ -145,6 +145,40 @@ def router_bias(hi: "HostInputs") -> np.ndarray | None:
     return hi.bias.astype(np.float32) if hi.cfg.zipf is not None else None
 
 
+# cb3 experts: index bytes from the SplitMix code streams of matrices 8 + m
+# (gate 8, up 9, down 10), codebooks from PCG64([seed, 2000 + layer, expert, m]).
+CB3_MATRIX_BASE = 8
+
+
+def cb3_codebook(cfg: Config, layer: int, expert: int, matrix: int) -> np.ndarray:
+    """One matrix's per-row codebooks as bf16 bits [rows][8]: N(0,1)/8 rounded
+    to float32, then to bf16 (nearest even)."""
+    rows = cfg.I if matrix in (sm.MATRIX_GATE, sm.MATRIX_UP) else cfg.H
+    rng = np.random.Generator(np.random.PCG64([cfg.seed, 2000 + layer, expert, matrix]))
+    return f32_to_bf16_bits((rng.standard_normal((rows, 8)) / 8).astype(np.float32))
+
+
+class HostCb3Weights:
+    """Host copy of one layer's synthetic cb3 experts, generated on demand.
+
+    Layouts (row-major, K contiguous): index bytes gate/up [I][3H/8], down
+    [H][3I/8]; codebooks gate/up [I][8], down [H][8] bf16 bits.
+    """
+
+    def __init__(self, cfg: Config, layer: int = 0):
+        self.cfg, self.layer = cfg, layer
+        self._cache: dict[tuple[int, int], tuple[np.ndarray, np.ndarray]] = {}
+
+    def matrix(self, expert: int, matrix: int) -> tuple[np.ndarray, np.ndarray]:
+        key = (expert, matrix)
+        if key not in self._cache:
+            c = self.cfg
+            rows, K = (c.I, c.H) if matrix in (sm.MATRIX_GATE, sm.MATRIX_UP) else (c.H, c.I)
+            q = sm.code_bytes(c.seed, self.layer, expert, CB3_MATRIX_BASE + matrix, rows * K * 3 // 8)
+            self._cache[key] = (q.reshape(rows, K * 3 // 8), cb3_codebook(c, self.layer, expert, matrix))
+        return self._cache[key]
+
+
 class HostWeights:
     """Host copy of one layer's synthetic expert bytes, generated on demand.
 

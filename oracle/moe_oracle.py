@@ -338,6 +338,60 @@ def ffn(x_bf16: np.ndarray, ids: np.ndarray, weights, H: int, mode: str = "a16")
 
 
 # --------------------------------------------------------------------------
+# Second expert codec: 3-bit per-row codebook (R-CB3)
+# --------------------------------------------------------------------------
+
+
+def cb3_indices(qbytes: np.ndarray, K: int) -> np.ndarray:
+    """Packed 3-bit indices [rows][3K/8] bytes -> int [rows][K].
+
+    R-CB3: the DGX Spark page ("The numbers") keeps the routable experts "in
+    a 3-bit per-row codebook packed from the checkpoint's own FP4 experts"
+    and says no more.  Reading: every group of 8 consecutive indices of a row
+    is one 24-bit little-endian word in 3 bytes; index i of the group sits in
+    bits 3i..3i+2.
+    """
+    q = np.asarray(qbytes, dtype=np.uint8)
+    rows = q.shape[0]
+    if K % 8 or q.shape[1] * 8 != K * 3:
+        raise ValueError("cb3 rows hold 3 bytes per 8 weights")
+    b = q.reshape(rows, K // 8, 3).astype(np.uint32)
+    word = b[..., 0] | (b[..., 1] << np.uint32(8)) | (b[..., 2] << np.uint32(16))
+    idx = (word[..., None] >> (np.uint32(3) * np.arange(8, dtype=np.uint32))) & np.uint32(7)
+    return idx.reshape(rows, K).astype(np.int64)
+
+
+def cb3_dequant(qbytes: np.ndarray, codebook_bf16: np.ndarray) -> np.ndarray:
+    """W[n][c] = codebook[n][index[n][c]] in fp64.  R-CB3: each output row has
+    its own codebook of 8 values, held as bf16 (a value of the FP4 checkpoint,
+    an e2m1 code times a power of two, is exact in bf16)."""
+    cb = bf16_bits_to_f64(np.asarray(codebook_bf16, dtype=np.uint16))
+    if cb.ndim != 2 or cb.shape[1] != 8:
+        raise ValueError("one codebook of 8 entries per row")
+    K = np.asarray(qbytes).shape[1] * 8 // 3
+    idx = cb3_indices(qbytes, K)
+    return np.take_along_axis(cb, idx, axis=1)
+
+
+def ffn_cb3(x_bf16: np.ndarray, ids: np.ndarray, weights, H: int) -> np.ndarray:
+    """y_pair fp64 [T*k][H] for cb3 experts: as ffn (mode "a16", the decode
+    reference) with W from cb3_dequant.  weights(expert, matrix) -> (index
+    bytes, codebook) with matrix 0 gate, 1 up, 2 down."""
+    x = bf16_bits_to_f64(x_bf16)
+    T, k = ids.shape
+    y = np.zeros((T * k, H), dtype=np.float64)
+    flat = ids.reshape(-1)
+    for e in sorted(set(int(v) for v in flat)):
+        pairs = np.nonzero(flat == e)[0]
+        wg = cb3_dequant(*weights(e, 0))
+        wu = cb3_dequant(*weights(e, 1))
+        wd = cb3_dequant(*weights(e, 2))
+        xe = x[pairs // k]
+        y[pairs] = swiglu(xe @ wg.T, xe @ wu.T) @ wd.T
+    return y
+
+
+# --------------------------------------------------------------------------
 # Combine and bf16 store
 # --------------------------------------------------------------------------
 
