@@ -73,7 +73,8 @@ def parse():
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-router-gate", action="store_true")
-    ap.add_argument("--only", choices=("decode", "prefill", "chain", "verify", "router"), default=None,
+    ap.add_argument("--no-cb3", action="store_true")
+    ap.add_argument("--only", choices=("decode", "prefill", "chain", "verify", "router", "cb3"), default=None,
                     help="run one section only (for profiling); prints that section's numbers")
     ap.add_argument("--calibrate", action="store_true",
                     help="only time torch's plain copy of 4 GiB (the HBM-bytes calibration kernel)")
@@ -270,6 +271,37 @@ def decode_section(args, torch, m, gd, gi):
         f"route+gate/up {t_gu * 1e6:.1f} us ({gu_bytes / t_gu / 1e9:.0f} GB/s), down+combine {t_dn * 1e6:.1f} us "
         f"({dn_bytes / t_dn / 1e9:.0f} GB/s)")
     return res
+
+
+def cb3_section(args, torch, m, gd, gi, db=None):
+    """The decode expert FFN over the 3-bit per-row codebook experts at decode1
+    (moe_ffn_cb3_decode), beside moe_ffn_fp4_decode on the same 64 routings:
+    each as one graph of 64 back-to-back FFN calls, replayed."""
+    cfg = gi.CONFIGS["decode1"]
+    if db is None:
+        db = DecodeBench(cfg, torch, m, gd, gi)
+    for s_ in range(NSETS):
+        db.step_separate(s_)  # routing and buckets of every set
+    log(f"cb3: filling {cfg.E} experts")
+    cb = m.Cb3Store(*gd.fill_cb3_layer(cfg, 0, db.hi.resident[0]))
+    k, E = cfg.k, cfg.E
+    g_cb = capture_many(torch, lambda i: m.moe_ffn_cb3_decode(db.x, k, E, cb, None, db.off[i], db.sp[i], db.y,
+                                                              db.ws), NSETS)
+    g_fp = capture_many(torch, lambda i: m.moe_ffn_fp4_decode(db.x, k, E, db.store, None, db.off[i], db.sp[i],
+                                                              db.y, db.ws), NSETS)
+    reps = max(1, min(args.steps, 512) // NSETS)
+    time_graphs(torch, [g_cb], 2)
+    t_cb = time_graphs(torch, [g_cb], reps) / (reps * NSETS)
+    time_graphs(torch, [g_fp], 2)
+    t_fp = time_graphs(torch, [g_fp], reps) / (reps * NSETS)
+    del g_cb, g_fp, cb
+    ebytes = 2 * cfg.I * (cfg.H * 3 // 8 + 16) + cfg.H * (cfg.I * 3 // 8 + 16)
+    nbytes = k * ebytes + cfg.H * 2 + k * cfg.H * 4
+    fbytes = k * cfg.expert_bytes + cfg.H * 2 + k * cfg.H * 4
+    log(f"cb3: FFN {t_cb * 1e6:.1f} us/token ({nbytes / t_cb / 1e9:.0f} GB/s of {nbytes / 1e6:.1f} MB); "
+        f"FP4 FFN on the same routings {t_fp * 1e6:.1f} us ({fbytes / 1e6:.1f} MB)")
+    return dict(ffn_us=t_cb * 1e6, bytes=nbytes, GBps=nbytes / t_cb / 1e9, frac_of_peak_hbm=nbytes / t_cb / PEAK_HBM,
+                expert_bytes=ebytes, fp4_ffn_us_same_routings=t_fp * 1e6, fp4_bytes=fbytes)
 
 
 def verify_section(args, torch, m, gd, gi):
@@ -526,7 +558,7 @@ def main() -> int:
 
     if args.only:
         fn = {"decode": decode_section, "prefill": prefill_section, "chain": chain_section,
-              "verify": verify_section, "router": router_gate_section}[args.only]
+              "verify": verify_section, "router": router_gate_section, "cb3": cb3_section}[args.only]
         res = fn(args, torch, m, gd, gi)
         if isinstance(res, dict):
             res.pop("db", None)
@@ -540,6 +572,7 @@ def main() -> int:
     prefill = None if args.no_prefill else prefill_section(args, torch, m, gd, gi)
     chain = None if args.no_chain else chain_section(args, torch, m, gd, gi)
     router = None if args.no_router_gate else router_gate_section(args, torch, m, gd, gi)
+    cb3 = None if args.no_cb3 else cb3_section(args, torch, m, gd, gi, dec["db"])
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec["db"], gi)
 
     gu_achieved = dec["gateup_bytes"] / (dec["gateup_us"] * 1e-6)
@@ -578,6 +611,7 @@ def main() -> int:
         "prefill4096": prefill,
         "chain40": chain,
         "router_gate": router,
+        "cb3_decode1": cb3,
     }
     print(json.dumps(result), flush=True)
     return 0

@@ -103,6 +103,37 @@ MOE_FP4_API moe_status moe_route_x(const uint16_t* x_bf16, int32_t T, int32_t hi
                                       topk_w, stream));
 }
 
+MOE_FP4_API size_t moe_ffn_cb3_decode_workspace_bytes(int32_t T, int32_t k, int32_t inter) {
+  if (T < 0 || k < 1 || inter < 1) return 0;
+  return moe::decode_workspace_bytes(T, k, inter);
+}
+
+MOE_FP4_API moe_status moe_ffn_cb3_decode(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                          const moe_cb3_experts* w, const int32_t* expert_to_slot,
+                                          const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                          float* y_pair, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!w) return MOE_ERR_NULL;
+  if (!w->q_gate || !w->q_up || !w->q_down || !w->cb_gate || !w->cb_up || !w->cb_down) return MOE_ERR_NULL;
+  if (w->num_slots < 1 || w->hidden < 256 || w->inter < 128) return MOE_ERR_SHAPE;
+  if (w->hidden % 256 != 0 || w->inter % 128 != 0) return MOE_ERR_SHAPE;
+  if (!moe::cb3_decode_supported(w->hidden, w->inter)) return MOE_ERR_UNSUPPORTED;
+  if (misaligned(w->q_gate, 4) || misaligned(w->q_up, 4) || misaligned(w->q_down, 4)) return MOE_ERR_ALIGN;
+  if (misaligned(w->cb_gate, 16) || misaligned(w->cb_up, 16) || misaligned(w->cb_down, 16)) return MOE_ERR_ALIGN;
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS || k > E) return MOE_ERR_SHAPE;
+  if (T > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !expert_offsets || !sorted_pair || !y_pair) return MOE_ERR_NULL;
+  if (!expert_to_slot && w->num_slots < E) return MOE_ERR_SHAPE;
+  if (misaligned(x_bf16, 16) || misaligned(y_pair, 16)) return MOE_ERR_ALIGN;
+  const size_t need = moe::decode_workspace_bytes(T, k, w->inter);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (misaligned(ws, 256)) return MOE_ERR_ALIGN;
+  const moe::Cb3Store st{w->num_slots, w->hidden, w->inter, w->q_gate, w->q_up, w->q_down,
+                         w->cb_gate, w->cb_up, w->cb_down};
+  return launched(moe::launch_decode_cb3(x_bf16, T, k, E, st, expert_to_slot, expert_offsets, sorted_pair, y_pair, ws,
+                                         stream));
+}
+
 MOE_FP4_API size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E) {
   if (T < 0 || k < 1 || E < 1) return 0;
   return moe::permute_workspace_bytes(T * k, E);

@@ -62,6 +62,18 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
                           const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
                           float* y_pair, void* ws, hipStream_t s, const uint8_t* run = nullptr);
 
+// Decode FFN over experts in the 3-bit per-row codebook format: index bytes
+// [S][rows][K*3/8], codebooks [S][rows][8] bf16; h fp32 in ws as for launch_decode.
+struct Cb3Store {
+  int num_slots, H, I;
+  const uint8_t *qg, *qu, *qd;
+  const uint16_t *cg, *cu, *cd;
+};
+bool cb3_decode_supported(int H, int I);
+hipError_t launch_decode_cb3(const uint16_t* x, int T, int k, int E, const Cb3Store& w, const int32_t* e2s,
+                             const int32_t* offsets, const int32_t* sorted_pair, float* y_pair, void* ws,
+                             hipStream_t s);
+
 hipError_t launch_combine(const float* y_pair, const float* w, int T, int k, int H,
                           const uint16_t* residual, bool bf16_out, void* out, hipStream_t s);
 

@@ -21,7 +21,7 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN = 0, 1, 2, 3
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
 MOE_OUT_BF16, MOE_OUT_F32 = 0, 1
 MOE_ACT_MXFP6_E2M3 = 0
-EXPORTED = ("moe_route", "moe_router_logits", "moe_route_x", "moe_permute_workspace_bytes", "moe_permute", "moe_ffn_fp4_decode_workspace_bytes", "moe_ffn_fp4_decode",
+EXPORTED = ("moe_route", "moe_router_logits", "moe_route_x", "moe_ffn_cb3_decode_workspace_bytes", "moe_ffn_cb3_decode", "moe_permute_workspace_bytes", "moe_permute", "moe_ffn_fp4_decode_workspace_bytes", "moe_ffn_fp4_decode",
             "moe_ffn_fp4_decode_gateup", "moe_ffn_fp4_decode_down", "moe_ffn_fp4_decode_subset",
             "moe_ffn_fp4_decode_invariant",
             "moe_decode_layer_workspace_bytes", "moe_decode_layer", "moe_decode_layer_gateup",
@@ -43,6 +43,12 @@ class CExperts(ctypes.Structure):
                 ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
 
 
+class CCb3Experts(ctypes.Structure):
+    _fields_ = [("num_slots", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("q_gate", ctypes.c_void_p), ("q_up", ctypes.c_void_p), ("q_down", ctypes.c_void_p),
+                ("cb_gate", ctypes.c_void_p), ("cb_up", ctypes.c_void_p), ("cb_down", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -60,6 +66,8 @@ def lib() -> ctypes.CDLL:
             "moe_route": [vp, i32, i32, i32, vp, vp, vp, vp],
             "moe_router_logits": [vp, i32, i32, vp, i32, vp, vp, vp],
             "moe_route_x": [vp, i32, i32, vp, i32, vp, i32, vp, vp, vp, vp, vp],
+            "moe_ffn_cb3_decode_workspace_bytes": [i32, i32, i32],
+            "moe_ffn_cb3_decode": [vp, i32, i32, i32, ctypes.POINTER(CCb3Experts), vp, vp, vp, vp, vp, sz, vp],
             "moe_permute_workspace_bytes": [i32, i32, i32],
             "moe_permute": [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp],
             "moe_ffn_fp4_decode_workspace_bytes": [i32, i32, i32],
@@ -91,6 +99,7 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = args
             fn.restype = ctypes.c_int
         L.moe_permute_workspace_bytes.restype = sz
+        L.moe_ffn_cb3_decode_workspace_bytes.restype = sz
         L.moe_ffn_fp4_decode_workspace_bytes.restype = sz
         L.moe_ffn_fp4_prefill_workspace_bytes.restype = sz
         L.moe_decode_layer_workspace_bytes.restype = sz
@@ -285,6 +294,58 @@ def _decode_call(name, x, k, E, store, expert_to_slot, expert_offsets, sorted_pa
     _want(ws, (torch.uint8,), "ws")
     cs = store.cstruct()
     _check(name, getattr(lib(), name)(
+        _ptr(x), T, k, E, ctypes.byref(cs), _ptr(expert_to_slot), _ptr(expert_offsets), _ptr(sorted_pair),
+        _ptr(y_pair), _ptr(ws), ws.numel(), _stream(x.device)))
+    return y_pair
+
+
+@dataclass
+class Cb3Store:
+    """One layer's experts in the 3-bit per-row codebook format, as device tensors.
+
+    q_gate, q_up uint8 [S][I][3H/8]; q_down uint8 [S][H][3I/8];
+    cb_gate, cb_up [S][I][8], cb_down [S][H][8] bf16 bit patterns (int16/uint16/bfloat16).
+    """
+    q_gate: torch.Tensor
+    q_up: torch.Tensor
+    q_down: torch.Tensor
+    cb_gate: torch.Tensor
+    cb_up: torch.Tensor
+    cb_down: torch.Tensor
+
+    @property
+    def num_slots(self) -> int:
+        return self.q_gate.shape[0]
+
+    @property
+    def inter(self) -> int:
+        return self.q_gate.shape[1]
+
+    @property
+    def hidden(self) -> int:
+        return self.q_down.shape[1]
+
+    def cstruct(self) -> CCb3Experts:
+        for n in ("q_gate", "q_up", "q_down"):
+            _want(getattr(self, n), (torch.uint8,), n)
+        for n in ("cb_gate", "cb_up", "cb_down"):
+            _want(getattr(self, n), _BF16, n)
+        return CCb3Experts(self.num_slots, self.hidden, self.inter, _ptr(self.q_gate), _ptr(self.q_up),
+                           _ptr(self.q_down), _ptr(self.cb_gate), _ptr(self.cb_up), _ptr(self.cb_down))
+
+
+def moe_ffn_cb3_decode(x: torch.Tensor, k: int, E: int, store: Cb3Store,
+                       expert_to_slot: torch.Tensor | None, expert_offsets: torch.Tensor,
+                       sorted_pair: torch.Tensor, y_pair: torch.Tensor | None = None,
+                       ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode expert FFN over cb3 experts; y_pair fp32 [T*k][H] in (token, slot) order."""
+    T, y_pair = _ffn_args(x, k, store, expert_to_slot, expert_offsets, sorted_pair, y_pair)
+    need = int(lib().moe_ffn_cb3_decode_workspace_bytes(T, k, store.inter))
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _want(ws, (torch.uint8,), "ws")
+    cs = store.cstruct()
+    _check("moe_ffn_cb3_decode", lib().moe_ffn_cb3_decode(
         _ptr(x), T, k, E, ctypes.byref(cs), _ptr(expert_to_slot), _ptr(expert_offsets), _ptr(sorted_pair),
         _ptr(y_pair), _ptr(ws), ws.numel(), _stream(x.device)))
     return y_pair

@@ -65,3 +65,30 @@ def upload(hi: HostInputs, layer: int = 0, device="cuda"):
     logits = torch.from_numpy(hi.logits[layer]).to(dev)
     e2s = torch.from_numpy(hi.expert_to_slot[layer]).to(dev)
     return x, logits, e2s
+
+
+def fill_cb3_layer(cfg: Config, layer: int, slot_expert: np.ndarray, device="cuda"):
+    """One layer's cb3 expert store: index bytes filled on the device from the
+    SplitMix code streams of matrices 8 + m, codebooks generated on the host.
+
+    Returns (q_gate, q_up, q_down, cb_gate, cb_up, cb_down).
+    """
+    from .inputs import CB3_MATRIX_BASE, cb3_codebook
+    S, H, I = len(slot_expert), cfg.H, cfg.I
+    dev = torch.device(device)
+    se = torch.from_numpy(np.ascontiguousarray(slot_expert, dtype=np.int32)).to(dev)
+    shapes = {sm.MATRIX_GATE: (I, H), sm.MATRIX_UP: (I, H), sm.MATRIX_DOWN: (H, I)}
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    qs, cbs = [], []
+    for m in (sm.MATRIX_GATE, sm.MATRIX_UP, sm.MATRIX_DOWN):
+        rows, K = shapes[m]
+        q = torch.empty((S, rows, K * 3 // 8), dtype=torch.uint8, device=dev)
+        rc = lib().gen_fill_codes(q.data_ptr(), rows * K * 3 // 8, se.data_ptr(), S, cfg.seed, layer,
+                                  CB3_MATRIX_BASE + m, stream)
+        if rc:
+            raise RuntimeError(f"gen_fill_codes failed ({rc})")
+        cb = np.stack([cb3_codebook(cfg, layer, int(e), m) for e in slot_expert])
+        qs.append(q)
+        cbs.append(torch.from_numpy(cb.view(np.int16)).to(dev))
+    torch.cuda.current_stream(dev).synchronize()
+    return tuple(qs + cbs)

@@ -351,6 +351,36 @@ MOE_FP4_API moe_status moe_ffn_fp4_prefill_subset(const uint16_t* x_bf16, int32_
                                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_ffn_cb3_decode -- the decode expert FFN over a second expert codec, the
+ * 3-bit per-row codebook in which the DGX Spark page keeps its routable
+ * experts ("The numbers": a 3-bit per-row codebook packed from the
+ * checkpoint's own FP4 experts).  The page fixes nothing more; the format
+ * read here: every output row has a codebook of 8 bf16 values, and each
+ * weight is a 3-bit index into its row's codebook, 8 indices per 3 bytes
+ * (index i of a group in bits 3i..3i+2 of the little-endian 24-bit word).
+ * W[n][c] = codebook[n][index[n][c]]; everything else -- buckets, arithmetic
+ * (x bf16, fp32 sums, h fp32), y_pair, workspace -- is moe_ffn_fp4_decode's.
+ *   q_gate, q_up : [num_slots][inter][hidden*3/8] index bytes (4-byte aligned)
+ *   q_down       : [num_slots][hidden][inter*3/8]
+ *   cb_gate, cb_up : [num_slots][inter][8] bf16 bits (16-byte aligned)
+ *   cb_down        : [num_slots][hidden][8]
+ * hidden % 256 == 0 and <= 6144, inter % 128 == 0 and <= 4096 (else
+ * MOE_ERR_SHAPE / MOE_ERR_UNSUPPORTED); 1 <= T <= MOE_DECODE_MAX_TOKENS.
+ * The encoder (packing FP4 experts into codebooks) is not part of the library.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t num_slots, hidden, inter;
+  const uint8_t *q_gate, *q_up, *q_down;
+  const uint16_t *cb_gate, *cb_up, *cb_down;
+} moe_cb3_experts;
+
+MOE_FP4_API size_t moe_ffn_cb3_decode_workspace_bytes(int32_t T, int32_t k, int32_t inter);
+MOE_FP4_API moe_status moe_ffn_cb3_decode(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                          const moe_cb3_experts* w, const int32_t* expert_to_slot,
+                                          const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                          float* y_pair, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_combine -- fixed-order weighted slot sum ("30 September follow-up").
  *   out[t] = sum_{j=0..k-1} topk_w[t][j] * y_pair[t*k+j]   (ascending j, fp32)
  *            + residual[t]                                 (if not NULL)

@@ -255,3 +255,38 @@ def test_router_gate_validation():
     assert rx(w=None) == m.MOE_ERR_NULL
     assert rx(out=None) == m.MOE_ERR_NULL
     assert rx(T=0, ids=None) == m.MOE_OK
+
+
+def test_cb3_decode_validation():
+    """The cb3 decode FFN checks its store, shapes, alignment and workspace before any launch."""
+    m = _lib()
+    L = m.lib()
+
+    def st(**kw):
+        f = dict(num_slots=8, hidden=256, inter=128, q_gate=FAKE, q_up=FAKE, q_down=FAKE,
+                 cb_gate=FAKE, cb_up=FAKE, cb_down=FAKE)
+        f.update(kw)
+        return m.CCb3Experts(f["num_slots"], f["hidden"], f["inter"], f["q_gate"], f["q_up"], f["q_down"],
+                                 f["cb_gate"], f["cb_up"], f["cb_down"])
+
+    def call(store=None, x=FAKE, T=1, k=2, E=8, ws=FAKE, ws_bytes=1 << 20):
+        s = st() if store is None else store
+        return L.moe_ffn_cb3_decode(x, T, k, E, ctypes.byref(s), None, FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+    assert L.moe_ffn_cb3_decode(FAKE, 1, 2, 8, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == m.MOE_ERR_NULL
+    assert call(store=st(cb_up=None)) == m.MOE_ERR_NULL
+    assert call(x=None) == m.MOE_ERR_NULL
+    assert call(store=st(hidden=200)) == m.MOE_ERR_SHAPE
+    assert call(store=st(inter=100)) == m.MOE_ERR_SHAPE
+    assert call(store=st(hidden=8192)) == m.MOE_ERR_UNSUPPORTED
+    assert call(store=st(inter=8192)) == m.MOE_ERR_UNSUPPORTED
+    assert call(store=st(q_down=FAKE + 2)) == m.MOE_ERR_ALIGN
+    assert call(store=st(cb_gate=FAKE + 8)) == m.MOE_ERR_ALIGN
+    assert call(store=st(num_slots=4)) == m.MOE_ERR_SHAPE
+    assert call(x=MIS) == m.MOE_ERR_ALIGN
+    assert call(ws=None) == m.MOE_ERR_WORKSPACE
+    assert call(ws_bytes=16) == m.MOE_ERR_WORKSPACE
+    assert call(T=300) == m.MOE_ERR_UNSUPPORTED
+    assert call(k=9) == m.MOE_ERR_SHAPE
+    assert call(T=0, x=None) == m.MOE_OK
+    assert L.moe_ffn_cb3_decode_workspace_bytes(1, 8, 2304) == 8 * 2304 * 4

@@ -1,0 +1,61 @@
+"""GPU parity of the decode FFN over 3-bit per-row codebook experts
+(moe_ffn_cb3_decode) against the fp64 oracle (ffn_cb3), through the C ABI.
+Routing and bucketing come from moe_route / moe_permute (pinned elsewhere);
+y_pair must be within 2e-3 of max|ref| (the decode arithmetic gives ~1e-7)."""
+import numpy as np
+import pytest
+import torch
+
+from gen import device as gd
+from gen import inputs as gi
+from oracle import moe_oracle as o
+from tests.harness import REL_TOL, rel_err, to_np
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny": gi.CONFIGS["tiny"],
+    "decode1": gi.CONFIGS["decode1"],
+    "verify16": gi.CONFIGS["verify16"],
+    # a routable subset smaller than E (expert_to_slot), several tokens per bucket
+    "mid_resident": gi.custom("mid_resident", 768, 256, 40, 3, 9, seed=22, resident=12),
+    # the largest hidden and expert width the kernels take
+    "wide": gi.custom("wide", 6144, 4096, 8, 2, 3, seed=43),
+}
+
+
+def _run(cfg, logits_np=None):
+    import fp4_routed_expert_mxfp4_amd as m
+    hi = gi.host_inputs(cfg)
+    store = m.Cb3Store(*gd.fill_cb3_layer(cfg, 0, hi.resident[0]))
+    x, logits, e2s = gd.upload(hi, 0)
+    e2s_t = None if cfg.resident is None else e2s
+    e2s_np = None if cfg.resident is None else hi.expert_to_slot[0]
+    ids, w = m.moe_route(logits, cfg.k, e2s_t)
+    off, sp, _ = m.moe_permute(ids, cfg.E)
+    y = m.moe_ffn_cb3_decode(x, cfg.k, cfg.E, store, e2s_t, off, sp)
+    torch.cuda.synchronize()
+    ref_ids, _ = o.route(hi.logits[0], cfg.k, e2s_np)
+    np.testing.assert_array_equal(to_np(ids), ref_ids)
+    return hi, to_np(y), ref_ids, (store, x, off, sp, e2s_t)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_cb3_decode_matches_oracle(name):
+    cfg = CASES[name]
+    print(f"case {name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}", flush=True)
+    hi, y, ids, _ = _run(cfg)
+    ref = o.ffn_cb3(hi.x_bf16, ids, gi.HostCb3Weights(cfg).matrix, cfg.H)
+    e = rel_err(y, ref)
+    print(f"[{name}] cb3 y_pair rel err {e:.3e}", flush=True)
+    assert e <= REL_TOL
+    assert e <= 1e-5  # fp32 sums of exact products: far inside the tolerance
+
+
+def test_cb3_decode_deterministic():
+    import fp4_routed_expert_mxfp4_amd as m
+    cfg = CASES["verify16"]
+    _, y1, _, (store, x, off, sp, e2s) = _run(cfg)
+    y2 = to_np(m.moe_ffn_cb3_decode(x, cfg.k, cfg.E, store, e2s, off, sp))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y1.view(np.uint32), y2.view(np.uint32))
