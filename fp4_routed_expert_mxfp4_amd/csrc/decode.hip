@@ -140,22 +140,15 @@ __device__ __forceinline__ void gu_finish(const GateUpBatch<J, R>& B, const uint
       }
     }
   }
+  static_assert(R == 2, "gate/up batches of 2 row pairs");
   float gv[R], uv[R];
-  if constexpr (R == 1) {
-    float a = sum16(tswap32(g[0], u[0]));           // lanes 0-31: g, 32-63: u (16-lane partials)
-    a = tswap16(a, a);
-    gv[0] = lane_value(a, 0);
-    uv[0] = lane_value(a, 32);
-  } else {
-    static_assert(R == 2, "gate/up batches of 1 or 2 row pairs");
-    const float a0 = tswap32(g[0], g[1]);
-    const float a1 = tswap32(u[0], u[1]);
-    const float b = sum16(tswap16(a0, a1));         // rows: g0, u0, g1, u1
-    gv[0] = lane_value(b, 0);
-    uv[0] = lane_value(b, 16);
-    gv[1] = lane_value(b, 32);
-    uv[1] = lane_value(b, 48);
-  }
+  const float a0 = tswap32(g[0], g[1]);
+  const float a1 = tswap32(u[0], u[1]);
+  const float b = sum16(tswap16(a0, a1));           // rows: g0, u0, g1, u1
+  gv[0] = lane_value(b, 0);
+  uv[0] = lane_value(b, 16);
+  gv[1] = lane_value(b, 32);
+  uv[1] = lane_value(b, 48);
 #pragma unroll
   for (int i = 0; i < R; ++i)
     if (lane == i) hrow[n0 + i] = swiglu_f32(gv[i], uv[i]);

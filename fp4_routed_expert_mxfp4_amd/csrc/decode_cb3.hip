@@ -10,13 +10,14 @@
 // Arithmetic is the decode reference's ("Fast single-box DeepSeek v4.1 Flash
 // runtime", "Conventions"): x stays bf16, so W.x uses exact bf16 products
 // summed in fp32 (v_dot2_f32_bf16), and h stays fp32 for the down projection
-// (fp32 FMAs).  Two indices are decoded at once into a bf16x2 word with two
-// v_perm_b32 (entries 0-3 and 4-7 of the codebook held in four registers)
-// and one bit-select on the indices' top bits.
+// (fp32 FMAs).  Two indices are decoded at once: for every row of a unit the
+// wavefront writes a 64-entry table of codebook pairs into its own LDS area
+// (entry a + 8b = entry a in the low half, entry b in the high half; lane l
+// writes entry l), and each pair of weights is one ds_read_b32 of it.
 //
 // Lane l of a wavefront takes the 32-weight groups l, l+64, ... of a row; a
-// gate/up unit is (bucket, two rows of W_gate and the same rows of W_up), a
-// down unit (bucket, eight output rows).  Every bucket row (token) of a unit
+// gate/up unit is (bucket, one row of W_gate and the same row of W_up), a
+// down unit (bucket, four output rows).  Every bucket row (token) of a unit
 // reuses the unit's index words and codebooks, decoding them again.
 #include "common.cuh"
 #include "kernels.h"
@@ -30,26 +31,26 @@ constexpr int kCbGrid = 512;
 constexpr int kCbGU = 3;  // 32-weight groups per lane of a gate/up row: hidden <= 64*32*3 = 6144
 constexpr int kCbDN = 2;  // ... of a down row: inter <= 4096
 
-// Entries a = p & 7 and b = (p >> 3) & 7 of the codebook cb (entry 2i in the
-// low half of word i) as one bf16x2 word, a in the low half.
-__device__ __forceinline__ uint32_t cb3_pair(uint32_t p, const uint4& cb) {
-  const uint32_t a = p & 3u, b = (p >> 3) & 3u;
-  const uint32_t sel = 0x01000100u + a * 0x0202u + b * 0x02020000u;  // bytes 2a, 2a+1, 2b, 2b+1
-  const uint32_t lo = __builtin_amdgcn_perm(cb.y, cb.x, sel);         // from entries 0-3
-  const uint32_t hi = __builtin_amdgcn_perm(cb.w, cb.z, sel);         // from entries 4-7
-  const uint32_t mask = ((p & 4u) ? 0x0000FFFFu : 0u) | ((p & 32u) ? 0xFFFF0000u : 0u);
-  return (hi & mask) | (lo & ~mask);
+// Entry a + 8b of a row's pair table: codebook entries a and b (entry 2i in
+// the low half of word i of cb) as one bf16x2 word, a in the low half.
+__device__ __forceinline__ uint32_t cb3_table_entry(int l, const uint4& cb) {
+  const uint32_t w[4] = {cb.x, cb.y, cb.z, cb.w};
+  const int a = l & 7, b = l >> 3;
+  const uint32_t ea = (w[a >> 1] >> (16 * (a & 1))) & 0xFFFFu;
+  const uint32_t eb = (w[b >> 1] >> (16 * (b & 1))) & 0xFFFFu;
+  return ea | (eb << 16);
 }
 
 // The 16 bf16x2 weight words of one 32-weight group from its 12 index bytes
-// (w.x, w.y, w.z): word 4s + j holds weights 8s + 2j and 8s + 2j + 1.
-__device__ __forceinline__ void cb3_group(const uint3& w, const uint4& cb, uint32_t (&out)[16]) {
+// (w.x, w.y, w.z) and the row's pair table: word 4s + j holds weights 8s + 2j
+// and 8s + 2j + 1 (the 6-bit pair index is the table entry).
+__device__ __forceinline__ void cb3_group(const uint3& w, const uint32_t* tab, uint32_t (&out)[16]) {
   const uint32_t g[4] = {w.x & 0xFFFFFFu, (w.x >> 24) | ((w.y & 0xFFFFu) << 8), (w.y >> 16) | ((w.z & 0xFFu) << 16),
                          w.z >> 8};
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[4 * s + j] = cb3_pair((g[s] >> (6 * j)) & 63u, cb);
+    for (int j = 0; j < 4; ++j) out[4 * s + j] = tab[(g[s] >> (6 * j)) & 63u];
 }
 
 __device__ __forceinline__ uint3 ld12(const uint8_t* p) {
@@ -65,35 +66,39 @@ __global__ __launch_bounds__(kCbThreads, 2) void cb3_gateup_kernel(const uint16_
                                                                    const int32_t* __restrict__ sorted_pair,
                                                                    float* __restrict__ h) {
   __shared__ Buckets bk;
+  __shared__ uint32_t tabs[4][2][64];  // per wavefront: the pair tables of its unit's gate and up rows
   build_buckets(offsets, E, bk, nullptr);
   const int lane = threadIdx.x & 63;
+  uint32_t (*tab)[64] = tabs[threadIdx.x >> 6];
   const int H = w.H, I = w.I, NG = H / 32;
   const size_t qrow = (size_t)H * 3 / 8;
-  const int units = bk.n * (I / 2);
+  const int units = bk.n * I;
   for (int unit = blockIdx.x * 4 + (threadIdx.x >> 6); unit < units; unit += gridDim.x * 4) {
-    const int b = unit / (I / 2), n0 = 2 * (unit - b * (I / 2));
+    const int b = unit / I, n = unit - b * I;
     const int expert = bk.expert[b], row0 = bk.row0[b], cnt = bk.cnt[b];
     const int slot = e2s ? e2s[expert] : expert;
     if (slot < 0 || slot >= w.num_slots) continue;  // the down kernel writes zero rows
-    // rows (n0 + i) of gate (m = 0) and up (m = 1): index words and codebooks
-    uint3 q[2][2][kCbGU];
-    uint4 cb[2][2];
+    // row n of gate (m = 0) and up (m = 1): index words and codebooks
+    const size_t row = (size_t)slot * I + n;
+    uint3 q[2][kCbGU];
+    uint4 cb[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int m = 0; m < 2; ++m) {
+      const uint8_t* qr = (m == 0 ? w.qg : w.qu) + row * qrow;
+      cb[m] = ld_cb((m == 0 ? w.cg : w.cu) + row * 8);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const size_t row = (size_t)slot * I + n0 + i;
-        const uint8_t* qr = (m == 0 ? w.qg : w.qu) + row * qrow;
-        cb[i][m] = ld_cb((m == 0 ? w.cg : w.cu) + row * 8);
-#pragma unroll
-        for (int gi = 0; gi < kCbGU; ++gi) {
-          const int G = lane + 64 * gi;
-          q[i][m][gi] = G < NG ? ld12(qr + 12 * G) : make_uint3(0u, 0u, 0u);
-        }
+      for (int gi = 0; gi < kCbGU; ++gi) {
+        const int G = lane + 64 * gi;
+        q[m][gi] = G < NG ? ld12(qr + 12 * G) : make_uint3(0u, 0u, 0u);
       }
+    }
+    // the previous unit's table reads are done: a wavefront's LDS accesses complete in order
+#pragma unroll
+    for (int m = 0; m < 2; ++m) tab[m][lane] = cb3_table_entry(lane, cb[m]);
+    __builtin_amdgcn_wave_barrier();
     for (int r = 0; r < cnt; ++r) {
       const uint16_t* xt = x + (size_t)(sorted_pair[row0 + r] / k) * H;
-      float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+      float acc[2] = {0.f, 0.f};
 #pragma unroll
       for (int gi = 0; gi < kCbGU; ++gi) {
         const int G = lane + 64 * gi;
@@ -103,27 +108,23 @@ __global__ __launch_bounds__(kCbThreads, 2) void cb3_gateup_kernel(const uint16_
         const uint32_t xw[16] = {xv[0].x, xv[0].y, xv[0].z, xv[0].w, xv[1].x, xv[1].y, xv[1].z, xv[1].w,
                                  xv[2].x, xv[2].y, xv[2].z, xv[2].w, xv[3].x, xv[3].y, xv[3].z, xv[3].w};
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int m = 0; m < 2; ++m) {
+          uint32_t wv[16];
+          cb3_group(q[m][gi], tab[m], wv);
+          float a = acc[m];
 #pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            uint32_t wv[16];
-            cb3_group(q[i][m][gi], cb[i][m], wv);
-            float a = acc[i][m];
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wv[t]),
-                                                  __builtin_bit_cast(bf16x2_t, xw[t]), a, false);
-            acc[i][m] = a;
-          }
+          for (int t = 0; t < 16; ++t)
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wv[t]),
+                                                __builtin_bit_cast(bf16x2_t, xw[t]), a, false);
+          acc[m] = a;
+        }
       }
-      // reduce (gate row 0, up row 0, gate row 1, up row 1) over the wavefront
-      const float a0 = tswap32(acc[0][0], acc[1][0]);
-      const float a1 = tswap32(acc[0][1], acc[1][1]);
-      const float s = sum16(tswap16(a0, a1));  // rows: g0, u0, g1, u1
-      const float g0 = lane_value(s, 0), u0 = lane_value(s, 16), g1 = lane_value(s, 32), u1 = lane_value(s, 48);
-      float* hrow = h + (size_t)(row0 + r) * I + n0;
-      if (lane == 0) hrow[0] = swiglu_f32(g0, u0);
-      if (lane == 1) hrow[1] = swiglu_f32(g1, u1);
+      // reduce (gate, up) over the wavefront: after the swap lanes 0-31 carry
+      // gate partials and 32-63 up partials; the 16-lane sums of rows 0 + 1 and
+      // 2 + 3 are added in that order
+      const float a = sum16(tswap32(acc[0], acc[1]));
+      const float gs = lane_value(a, 0) + lane_value(a, 16), us = lane_value(a, 32) + lane_value(a, 48);
+      if (lane == 0) h[(size_t)(row0 + r) * I + n] = swiglu_f32(gs, us);
     }
   }
 }
@@ -134,24 +135,26 @@ __global__ __launch_bounds__(kCbThreads, 2) void cb3_down_kernel(int k, int E, C
                                                                  const int32_t* __restrict__ sorted_pair,
                                                                  const float* __restrict__ h, float* __restrict__ y) {
   __shared__ Buckets bk;
+  __shared__ uint32_t tabs[4][4][64];  // per wavefront: the pair tables of its unit's four rows
   build_buckets(offsets, E, bk, nullptr);
   const int lane = threadIdx.x & 63;
+  uint32_t (*tab)[64] = tabs[threadIdx.x >> 6];
   const int H = w.H, I = w.I, NG = I / 32;
   const size_t qrow = (size_t)I * 3 / 8;
-  const int units = bk.n * (H / 8);
+  const int units = bk.n * (H / 4);
   for (int unit = blockIdx.x * 4 + (threadIdx.x >> 6); unit < units; unit += gridDim.x * 4) {
-    const int b = unit / (H / 8), m0 = 8 * (unit - b * (H / 8));
+    const int b = unit / (H / 4), m0 = 4 * (unit - b * (H / 4));
     const int expert = bk.expert[b], row0 = bk.row0[b], cnt = bk.cnt[b];
     const int slot = e2s ? e2s[expert] : expert;
     if (slot < 0 || slot >= w.num_slots) {  // no stored expert: its rows are zero
       for (int r = 0; r < cnt; ++r)
-        if (lane < 8) y[(size_t)sorted_pair[row0 + r] * H + m0 + lane] = 0.f;
+        if (lane < 4) y[(size_t)sorted_pair[row0 + r] * H + m0 + lane] = 0.f;
       continue;
     }
-    uint3 q[8][kCbDN];
-    uint4 cb[8];
+    uint3 q[4][kCbDN];
+    uint4 cb[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const size_t row = (size_t)slot * H + m0 + i;
       cb[i] = ld_cb(w.cd + row * 8);
 #pragma unroll
@@ -160,12 +163,13 @@ __global__ __launch_bounds__(kCbThreads, 2) void cb3_down_kernel(int k, int E, C
         q[i][gi] = G < NG ? ld12(w.qd + row * qrow + 12 * G) : make_uint3(0u, 0u, 0u);
       }
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tab[i][lane] = cb3_table_entry(lane, cb[i]);
+    __builtin_amdgcn_wave_barrier();
     for (int r = 0; r < cnt; ++r) {
       const float* hr = h + (size_t)(row0 + r) * I;
-      float v[8];
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
-#pragma unroll 1
       for (int gi = 0; gi < kCbDN; ++gi) {
         const int G = lane + 64 * gi;
         if (G >= NG) break;
@@ -180,9 +184,9 @@ __global__ __launch_bounds__(kCbThreads, 2) void cb3_down_kernel(int k, int E, C
           hv[4 * c + 3] = t.w;
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
           uint32_t wv[16];
-          cb3_group(q[i][gi], cb[i], wv);
+          cb3_group(q[i][gi], tab[i], wv);
           float a = v[i];
 #pragma unroll
           for (int t = 0; t < 16; ++t) {
@@ -190,14 +194,13 @@ __global__ __launch_bounds__(kCbThreads, 2) void cb3_down_kernel(int k, int E, C
             a = fmaf(bf16_bits_to_f32(wv[t] >> 16), hv[2 * t + 1], a);
           }
           v[i] = a;
+          __builtin_amdgcn_sched_barrier(0);  // one row's table reads live at a time
         }
       }
-      // 8 row partials -> lanes 8g..8g+7 hold partials of row g
-      const float a0 = tswap32(v[0], v[4]), a1 = tswap32(v[1], v[5]);
-      const float a2 = tswap32(v[2], v[6]), a3 = tswap32(v[3], v[7]);
-      const float b0 = tswap16(a0, a2), b1 = tswap16(a1, a3);
-      const float c = sum8(tswap8(b0, b1, lane));
-      if ((lane & 7) == 0) y[(size_t)sorted_pair[row0 + r] * H + m0 + (lane >> 3)] = c;
+      // 4 row partials -> lane 16i holds the sum of row i
+      const float a0 = tswap32(v[0], v[2]), a1 = tswap32(v[1], v[3]);
+      const float c = sum16(tswap16(a0, a1));
+      if ((lane & 15) == 0) y[(size_t)sorted_pair[row0 + r] * H + m0 + (lane >> 4)] = c;
     }
   }
 }
