@@ -27,7 +27,8 @@ namespace moe {
 namespace {
 
 constexpr int kCbThreads = 256;
-constexpr int kCbGrid = 512;
+constexpr int kCbGridGU = 768;  // three workgroups per CU: the gate/up kernel fits three wavefronts per SIMD
+constexpr int kCbGridDN = 512;  // the down kernel (four rows per unit) fits two
 constexpr int kCbGU = 3;  // 32-weight groups per lane of a gate/up row: hidden <= 64*32*3 = 6144
 constexpr int kCbDN = 2;  // ... of a down row: inter <= 4096
 
@@ -60,7 +61,7 @@ __device__ __forceinline__ uint3 ld12(const uint8_t* p) {
 
 __device__ __forceinline__ uint4 ld_cb(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__global__ __launch_bounds__(kCbThreads, 2) void cb3_gateup_kernel(const uint16_t* __restrict__ x, int k, int E,
+__global__ __launch_bounds__(kCbThreads, 3) void cb3_gateup_kernel(const uint16_t* __restrict__ x, int k, int E,
                                                                    Cb3Store w, const int32_t* __restrict__ e2s,
                                                                    const int32_t* __restrict__ offsets,
                                                                    const int32_t* __restrict__ sorted_pair,
@@ -216,11 +217,11 @@ hipError_t launch_decode_cb3(const uint16_t* x, int T, int k, int E, const Cb3St
                              hipStream_t s) {
   (void)T;
   float* h = reinterpret_cast<float*>(ws);
-  hipLaunchKernelGGL(cb3_gateup_kernel, dim3(kCbGrid), dim3(kCbThreads), 0, s, x, k, E, w, e2s, offsets,
+  hipLaunchKernelGGL(cb3_gateup_kernel, dim3(kCbGridGU), dim3(kCbThreads), 0, s, x, k, E, w, e2s, offsets,
                      sorted_pair, h);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(cb3_down_kernel, dim3(kCbGrid), dim3(kCbThreads), 0, s, k, E, w, e2s, offsets, sorted_pair, h,
+  hipLaunchKernelGGL(cb3_down_kernel, dim3(kCbGridDN), dim3(kCbThreads), 0, s, k, E, w, e2s, offsets, sorted_pair, h,
                      y_pair);
   return hipGetLastError();
 }
