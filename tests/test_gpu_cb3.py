@@ -59,3 +59,29 @@ def test_cb3_decode_deterministic():
     y2 = to_np(m.moe_ffn_cb3_decode(x, cfg.k, cfg.E, store, e2s, off, sp))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_cb3_decode_graph_replays():
+    """moe_ffn_cb3_decode captured in a HIP graph: three replays, with an eager
+    call on other inputs between them, each bit-identical to the eager result."""
+    import fp4_routed_expert_mxfp4_amd as m
+    cfg = CASES["verify16"]
+    _, y_eager, _, (store, x, off, sp, e2s) = _run(cfg)
+    y = torch.empty((cfg.T * cfg.k, cfg.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(m.decode_workspace_bytes(cfg.T, cfg.k, cfg.I), 256), dtype=torch.uint8, device="cuda")
+    other = torch.flip(x, dims=[0]).contiguous()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        m.moe_ffn_cb3_decode(x, cfg.k, cfg.E, store, e2s, off, sp, y, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.moe_ffn_cb3_decode(x, cfg.k, cfg.E, store, e2s, off, sp, y, ws)
+    for _ in range(3):
+        m.moe_ffn_cb3_decode(other, cfg.k, cfg.E, store, e2s, off, sp, y, ws)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_np(y).view(np.uint32), y_eager.view(np.uint32))

@@ -149,3 +149,34 @@ def test_router_gate_deterministic_and_empty():
     w0 = torch.zeros((8, 256), dtype=torch.int16, device="cuda")
     l0, i0, t0 = m.moe_route_x(x0, w0, 2)
     assert l0.shape == (0, 8) and i0.shape == (0, 2)
+
+
+def test_route_x_graph_replays():
+    """moe_route_x captured in a HIP graph: three replays, with eager calls on
+    other inputs between them, each bit-identical to the eager result."""
+    import fp4_routed_expert_mxfp4_amd as m
+    for name in ("verify16", "mfma65"):
+        cfg, n_res = CASES[name]
+        print(f"case {name} graph", flush=True)
+        _, _, _, _, x, w, b, e2s = _inputs(cfg, n_res)
+        lg = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda")
+        ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+        tw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+        ref = [t.clone() for t in m.moe_route_x(x, w, cfg.k, b, e2s, lg, ids, tw)]
+        other = torch.flip(x, dims=[0]).contiguous()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            m.moe_route_x(x, w, cfg.k, b, e2s, lg, ids, tw)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            m.moe_route_x(x, w, cfg.k, b, e2s, lg, ids, tw)
+        for _ in range(3):
+            m.moe_route_x(other, w, cfg.k, b, e2s, lg, ids, tw)   # eager work that overwrites the outputs
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for got, want in zip((lg, ids, tw), ref):
+                assert torch.equal(got.view(torch.int32), want.view(torch.int32))
