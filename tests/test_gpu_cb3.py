@@ -21,6 +21,9 @@ CASES = {
     "mid_resident": gi.custom("mid_resident", 768, 256, 40, 3, 9, seed=22, resident=12),
     # the largest hidden and expert width the kernels take
     "wide": gi.custom("wide", 6144, 4096, 8, 2, 3, seed=43),
+    # expert width 2944: 92 index groups per down row, 64 in the full pass and
+    # 28 left over, i.e. 4 x 28 = 112 (row, group) items in two passes
+    "tail2": gi.custom("tail2", 512, 2944, 12, 3, 5, seed=44),
 }
 
 
