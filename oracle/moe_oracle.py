@@ -12,8 +12,9 @@ Sources.  The pages describe the system this path belongs to:
           reference-defining); How to use this recipe (keep a correct slow
           baseline as the oracle).
   [M5]    "DeepSeek V4.1 Flash Q4 / 27 September 2026" (argonautlabs): the
-          30 September follow-up (every (token, slot) row is written once and
-          the slot sum is a separate fixed-order kernel).
+          30 September follow-up (each (token, slot) pair has one output row,
+          produced once, and a separate pass adds a token's rows in a fixed
+          order).
   [SPARK] "DeepSeek-V4.1-Flash on a single NVIDIA DGX Spark" (shadowgraph):
           intro (the checkpoint's own e2m1 experts), Why it is built this way
           (15,360 experts x 3 x 2304 x 5120 weights, FP4 + UE8M0 per 32),
@@ -109,27 +110,35 @@ def route(logits: np.ndarray, k: int, expert_to_slot: np.ndarray | None = None):
     w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected.
     R-ROUTE: the pages give no scoring function; this plain reading uses the
     raw fp32 logits, ties go to the lower expert index, -0 == +0.
-    Non-finite logits and fewer than k candidates are rejected.
+    R-ROUTE-FILL: the pages do not say what a token gets when fewer than k of
+    its experts are routable.  Reading: the routable experts come first, in
+    the order above, and the remaining slots take the non-routable experts in
+    the same order with weight 0; the softmax runs over the routable slots
+    only (all weights are 0 when none is routable).  Their rows then hold an
+    expert with no stored weights, whose FFN rows are zero.
+    Non-finite logits and k outside [1, E] are rejected.
     Returns ids int32 [T][k] and weights fp64 [T][k].
     """
     logits = np.asarray(logits, dtype=np.float32)
     T, E = logits.shape
     if not np.all(np.isfinite(logits)):
         raise ValueError("non-finite logit")
-    cand = list(range(E)) if expert_to_slot is None else \
-        [e for e in range(E) if int(expert_to_slot[e]) >= 0]
-    if not 1 <= k <= len(cand):
-        raise ValueError("k exceeds the routable experts")
+    if not 1 <= k <= E:
+        raise ValueError("k must lie in [1, E]")
+    routable = [e for e in range(E) if expert_to_slot is None or int(expert_to_slot[e]) >= 0]
+    others = [e for e in range(E) if expert_to_slot is not None and int(expert_to_slot[e]) < 0]
     ids = np.empty((T, k), dtype=np.int32)
-    w = np.empty((T, k), dtype=np.float64)
+    w = np.zeros((T, k), dtype=np.float64)
     for t in range(T):
         row = [float(v) for v in logits[t]]
-        order = sorted(cand, key=lambda e: (-row[e], e))
-        sel = order[:k]
+        rank = lambda e: (-row[e], e)
+        sel = (sorted(routable, key=rank) + sorted(others, key=rank))[:k]
         ids[t] = sel
-        l = np.array([row[e] for e in sel], dtype=np.float64)
-        ex = np.exp(l - l[0])
-        w[t] = ex / ex.sum()
+        n = min(k, len(routable))              # the routable slots come first
+        if n:
+            l = np.array([row[e] for e in sel[:n]], dtype=np.float64)
+            ex = np.exp(l - l[0])
+            w[t, :n] = ex / ex.sum()
     return ids, w
 
 
@@ -325,13 +334,21 @@ def expert_ffn(x: np.ndarray, weights, expert: int, mode: str = "a16") -> np.nda
     return h @ wd.T
 
 
-def ffn(x_bf16: np.ndarray, ids: np.ndarray, weights, H: int, mode: str = "a16") -> np.ndarray:
-    """y_pair fp64 [T*k][H]: row p = t*k + j is expert ids[t][j] applied to x_t."""
+def ffn(x_bf16: np.ndarray, ids: np.ndarray, weights, H: int, mode: str = "a16",
+        expert_to_slot: np.ndarray | None = None) -> np.ndarray:
+    """y_pair fp64 [T*k][H]: row p = t*k + j is expert ids[t][j] applied to x_t.
+
+    With an expert_to_slot table, an expert without a slot (entry < 0) has no
+    stored weights and its rows are zero (R-ROUTE-FILL: such experts fill the
+    slots of a token with fewer than k routable experts, at weight 0).
+    """
     x = bf16_bits_to_f64(x_bf16)
     T, k = ids.shape
     y = np.zeros((T * k, H), dtype=np.float64)
     flat = ids.reshape(-1)
     for e in sorted(set(int(v) for v in flat)):
+        if expert_to_slot is not None and int(expert_to_slot[e]) < 0:
+            continue
         pairs = np.nonzero(flat == e)[0]
         y[pairs] = expert_ffn(x[pairs // k], weights, e, mode)
     return y
@@ -345,9 +362,9 @@ def ffn(x_bf16: np.ndarray, ids: np.ndarray, weights, H: int, mode: str = "a16")
 def cb3_indices(qbytes: np.ndarray, K: int) -> np.ndarray:
     """Packed 3-bit indices [rows][3K/8] bytes -> int [rows][K].
 
-    R-CB3: the DGX Spark page ("The numbers") keeps the routable experts "in
-    a 3-bit per-row codebook packed from the checkpoint's own FP4 experts"
-    and says no more.  Reading: every group of 8 consecutive indices of a row
+    R-CB3: the DGX Spark page ("The numbers") stores the experts it keeps
+    routable with 3 bits per weight and a codebook per row, derived from the
+    checkpoint's FP4 experts, and gives no further detail.  Reading: every group of 8 consecutive indices of a row
     is one 24-bit little-endian word in 3 bytes; index i of the group sits in
     bits 3i..3i+2.
     """
@@ -435,7 +452,7 @@ def moe_layer(x_bf16, logits, weights, k, H, mode="a16", expert_to_slot=None, re
     E = logits.shape[1]
     ids, w = route(logits, k, expert_to_slot)
     offsets, sorted_pair, pair_to_row = permute(ids, E)
-    y = ffn(x_bf16, ids, weights, H, mode)
+    y = ffn(x_bf16, ids, weights, H, mode, expert_to_slot)
     out = combine(y, w, residual_bf16)
     return dict(ids=ids, w=w, offsets=offsets, sorted_pair=sorted_pair,
                 pair_to_row=pair_to_row, y_pair=y, out=out)

@@ -140,7 +140,32 @@ def test_route_rejects():
     with pytest.raises(ValueError):
         o.route(np.array([[np.nan, 0.0]], np.float32), 1)
     with pytest.raises(ValueError):
-        o.route(np.array([[1.0, 0.0]], np.float32), 2, np.array([0, -1], np.int32))
+        o.route(np.array([[1.0, 0.0]], np.float32), 3)
+    with pytest.raises(ValueError):
+        o.route(np.array([[1.0, 0.0]], np.float32), 0)
+
+
+def test_route_fewer_routable_than_k(golden_dir):
+    """R-ROUTE-FILL hand cases, and the rows of the filled slots are zero."""
+    for case in load(golden_dir, "route_permute_hand.json")["route_fill"]["cases"]:
+        e2s = np.array(case["expert_to_slot"], np.int32)
+        ids, w = o.route(np.array(case["logits"], np.float32), case["k"], e2s)
+        assert ids.tolist() == case["ids"], case
+        if "w" in case:
+            assert w.tolist() == case["w"], case
+    _, w = o.route(np.array([[3.0, 1.0, 4.0, 0.0, 2.0]], np.float32), 4, np.array([0, -1, -1, 1, -1], np.int32))
+    e = math.exp(-3.0)
+    assert w[0, 0] == pytest.approx(1 / (1 + e), abs=1e-15) and w[0, 1] == pytest.approx(e / (1 + e), abs=1e-15)
+    assert w[0, 2] == 0.0 and w[0, 3] == 0.0
+    # the FFN rows of an expert without a slot are zero; the routable rows are untouched
+    H = I = 32
+    mats = {0: (np.full((I, H // 2), 0x22, np.uint8), np.full((I, 1), 127, np.uint8)),
+            1: (np.full((I, H // 2), 0x11, np.uint8), np.full((I, 1), 127, np.uint8)),
+            2: (np.full((H, I // 2), 0x33, np.uint8), np.full((H, 1), 125, np.uint8))}
+    x = _bf16(np.full((1, H), 2.0))
+    e2s = np.array([0, -1], np.int32)
+    y = o.ffn(x, np.array([[0, 1]], np.int32), lambda e, m: mats[m], H, "a16", e2s)
+    assert np.all(y[0] == 24576.0) and np.all(y[1] == 0.0)
 
 
 # ---------------------------------------------------------------- permutation
