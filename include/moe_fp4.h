@@ -11,9 +11,10 @@
  *     intro (the checkpoint's own e2m1 experts, never requantised);
  *   - only a kept subset of the experts may be routable -- same page, "The
  *     numbers" (the top ~40 % of experts stay routable and resident);
- *   - every (token, slot) row is written once and the slot sum is a separate
- *     fixed-order step -- "DeepSeek V4.1 Flash Q4 / 27 September 2026",
- *     "30 September follow-up: prefill";
+ *   - each (token, slot) pair gets its own output row, produced exactly
+ *     once, and adding a token's rows together is its own pass in a fixed
+ *     order -- "DeepSeek V4.1 Flash Q4 / 27 September 2026", "30 September
+ *     follow-up: prefill" (why its two-wave MoE is bit-exact);
  *   - prefill and decode are separate arithmetic paths, each judged against
  *     its own reference -- "Fast single-box DeepSeek v4.1 Flash runtime",
  *     "Conventions".
@@ -32,7 +33,14 @@
  *  - No call records a memset, so every call may be captured into a HIP graph.
  *  - Element layouts are row-major.  e2m1 codes are packed two per byte,
  *    element 2c in the low nibble of byte c.  A scale byte e stands for
- *    2^(e-127); byte 255 (NaN) must not occur (not checked on the device).
+ *    2^(e-127), every byte 0..254 being valid.  Byte 255 (NaN in the OCP MX
+ *    encoding) must not occur; it is not checked on the device, and rows
+ *    that use it come out non-finite (the one-token decode kernels read it
+ *    as +inf, the MFMA kernels as NaN).  The one-token decode kernels scale
+ *    each block sum in fp32 (byte 0 is the fp32 subnormal 2^-127); the
+ *    multi-token decode kernels fold the scale into bf16 weights, exact for
+ *    every weight of magnitude 2^-126 or more, so bytes 0-2 may round their
+ *    smallest weights; the prefill kernels pass the byte to the MFMA.
  *  - bf16 values are passed as uint16_t bit patterns.
  *  - Device data are not inspected on the host.  Preconditions on their
  *    contents (finite logits, expert ids in range, at least k routable
@@ -160,7 +168,10 @@ MOE_FP4_API moe_status moe_route_x(const uint16_t* x_bf16, int32_t T, int32_t hi
  *                  bytes, 256-byte aligned (may be NULL when that is 0, which
  *                  it is for T*k <= 1024)
  * T*k <= 2^24.  Ids outside [0, E) are left out of every bucket (their
- * pair_to_row entry is -1 and expert_offsets[E] counts only valid pairs).
+ * pair_to_row entry is -1 and expert_offsets[E] counts only valid pairs;
+ * sorted rows from expert_offsets[E] on are not written).  The expert FFN
+ * calls read and write nothing for such a pair: its y_pair row keeps what it
+ * held, and moe_combine adds that row like any other.
  * ------------------------------------------------------------------------- */
 MOE_FP4_API size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E);
 MOE_FP4_API moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
@@ -170,6 +181,12 @@ MOE_FP4_API moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k
 
 /* ---------------------------------------------------------------------------
  * moe_ffn_fp4_decode -- expert FFN of the decode path (fp32 accumulation).
+ * Decode is a weight stream: a token reads its k experts once, and the
+ * M5 Max engine's decode kernels run at 69-100 % of its memory roofline
+ * ("DeepSeek V4.1 Flash Q4 / 27 September 2026", "28 September follow-up"),
+ * so every weight byte is loaded once with 16-byte coalesced reads and
+ * decoded in registers.  Decode is judged against unquantised activations
+ * ("Fast single-box DeepSeek v4.1 Flash runtime", "Conventions").
  * For every pair p = sorted_pair[r] = t*k + j with expert e (bucket of r):
  *   g = W_gate[e] . x_t,  u = W_up[e] . x_t,  h = silu(g) * u  (fp32),
  *   y_pair[p] = W_down[e] . h                                  (fp32)
@@ -189,6 +206,8 @@ MOE_FP4_API moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k
  *   ws             device workspace of at least
  *                  moe_ffn_fp4_decode_workspace_bytes(T, k, inter) bytes,
  *                  256-byte aligned; contents on entry do not matter
+ * A token may name one expert in several of its slots (topk_ids from
+ * moe_route never do); every such pair gets its own, equal, y_pair row.
  * 1 <= T <= MOE_DECODE_MAX_TOKENS.
  * ------------------------------------------------------------------------- */
 MOE_FP4_API size_t moe_ffn_fp4_decode_workspace_bytes(int32_t T, int32_t k, int32_t inter);
@@ -328,8 +347,9 @@ MOE_FP4_API moe_status moe_ffn_fp4_prefill(const uint16_t* x_bf16, int32_t T, in
  * over a subset of the experts: the two-wave routed MoE of the M5 Max page
  * ("DeepSeek V4.1 Flash Q4 / 27 September 2026", "30 September follow-up:
  * prefill"), which computes the experts already on hand first and the rest
- * once they arrive.  It is exact because every (token, slot) row is written
- * once and the slot sum is a separate fixed-order kernel.
+ * once they arrive.  Splitting the experts this way changes no bit of the
+ * result, because each (token, slot) row is produced by exactly one call and
+ * the rows are added together afterwards, in a fixed order, by moe_combine.
  *   run_mask [E] uint8 on the device: nonzero = run this expert's bucket now
  *   other arguments: as moe_ffn_fp4_decode / moe_ffn_fp4_prefill
  * Rows of the buckets whose mask byte is 0 are not written (their y_pair
@@ -352,9 +372,9 @@ MOE_FP4_API moe_status moe_ffn_fp4_prefill_subset(const uint16_t* x_bf16, int32_
 
 /* ---------------------------------------------------------------------------
  * moe_ffn_cb3_decode -- the decode expert FFN over a second expert codec, the
- * 3-bit per-row codebook in which the DGX Spark page keeps its routable
- * experts ("The numbers": a 3-bit per-row codebook packed from the
- * checkpoint's own FP4 experts).  The page fixes nothing more; the format
+ * 3-bit per-row codebook in which the DGX Spark page stores the experts it
+ * keeps routable, derived from the checkpoint's FP4 experts ("The
+ * numbers").  The page fixes nothing more; the format
  * read here: every output row has a codebook of 8 bf16 values, and each
  * weight is a 3-bit index into its row's codebook, 8 indices per 3 bytes
  * (index i of a group in bits 3i..3i+2 of the little-endian 24-bit word).
