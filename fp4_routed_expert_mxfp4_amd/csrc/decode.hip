@@ -14,7 +14,8 @@
 // its scale 2^(e-127) in fp32.  The down projection decodes to fp32
 // (v_cvt_scalef32_pk_f32_fp4) and sums with fp32 FMAs against h.
 //
-// These kernels serve one token (each bucket one row) at the model's shapes;
+// These kernels serve one token at the model's shapes (a bucket holds that
+// token once, or several times for a repeated expert id);
 // launch_decode sends every other shape and every batch of two or more tokens
 // to the bf16 MFMA kernels of decode_mt.hip.  The fused layer kernels below
 // also route in-kernel and combine in the down kernel.
@@ -117,9 +118,11 @@ __device__ __forceinline__ void gu_load(GateUpBatch<J, R>& B, const uint8_t* con
 }
 
 // Reduce the batch for one token and store h for its R rows.
+// nrep > 1: the bucket holds the same token nrep times (a repeated expert id
+// of a one-token call); its rows are identical and all of them are stored.
 template <int J, int R>
 __device__ __forceinline__ void gu_finish(const GateUpBatch<J, R>& B, const uint4 (&xr)[J][4], int lane,
-                                          float* hrow, int n0) {
+                                          float* hrow, int n0, int nrep = 1, int I = 0) {
   constexpr int NB = 32 * J;
   float g[R], u[R];
 #pragma unroll
@@ -151,7 +154,11 @@ __device__ __forceinline__ void gu_finish(const GateUpBatch<J, R>& B, const uint
   uv[1] = lane_value(b, 48);
 #pragma unroll
   for (int i = 0; i < R; ++i)
-    if (lane == i) hrow[n0 + i] = swiglu_f32(gv[i], uv[i]);
+    if (lane == i) {
+      const float v = swiglu_f32(gv[i], uv[i]);
+      hrow[n0 + i] = v;
+      for (int r = 1; r < nrep; ++r) hrow[(size_t)r * I + n0 + i] = v;
+    }
 }
 
 template <int J, int R>
@@ -202,17 +209,20 @@ __global__ __launch_bounds__(kThreads, 2) void gateup_fast_kernel(
         for (int q = 0; q < 4; ++q) xr[j][q] = p[q];
       }
     };
-    // one token per bucket: x stays in registers, two batches in flight
+    // one token: x stays in registers, two batches in flight.  Every row of
+    // the bucket is that token (cnt > 1 only for a repeated expert id), so
+    // the rows are computed once and stored cnt times.
     load_x(sorted_pair[row0] / k);
     float* hrow = h + (size_t)row0 * I;
+    const int nrep = bk.cnt[b];
     GateUpBatch<J, R> A, Bn;
     gu_load(A, cp, sp, bat0 * R, rowbytes, NB);
     for (int bat = bat0; bat < bat1; bat += 2) {
       const bool has1 = bat + 1 < bat1;
       if (has1) gu_load(Bn, cp, sp, (bat + 1) * R, rowbytes, NB);
-      gu_finish(A, xr, lane, hrow, bat * R);
+      gu_finish(A, xr, lane, hrow, bat * R, nrep, I);
       if (bat + 2 < bat1) gu_load(A, cp, sp, (bat + 2) * R, rowbytes, NB);
-      if (has1) gu_finish(Bn, xr, lane, hrow, (bat + 1) * R);
+      if (has1) gu_finish(Bn, xr, lane, hrow, (bat + 1) * R, nrep, I);
     }
 
   }
@@ -246,9 +256,14 @@ __device__ __forceinline__ void dn_load(DownBatch<M, TAIL>& B, const uint8_t* dc
   }
 }
 
+// extra, nextra: the further output rows of a bucket that holds one token
+// several times (a repeated expert id of a one-token call), which get the
+// same values as yrow; y is their base and H their row length.
 template <int M, bool TAIL>
 __device__ __forceinline__ void dn_finish(const DownBatch<M, TAIL>& B, const float4_t (&hm)[M > 0 ? M : 1][8],
-                                          const float4_t (&ht)[8], int lane, float* yrow, int m0) {
+                                          const float4_t (&ht)[8], int lane, float* yrow, int m0,
+                                          const int32_t* extra = nullptr, int nextra = 0, float* y = nullptr,
+                                          int H = 0) {
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -263,7 +278,10 @@ __device__ __forceinline__ void dn_finish(const DownBatch<M, TAIL>& B, const flo
   float c = tswap8(b0, b1, lane);
   if (TAIL) c += block_dot_f32(B.ct, ht) * ue8m0_to_f32(B.st);  // this lane's tail block is in row lane/8
   c = sum8(c);
-  if ((lane & 7) == 0) yrow[m0 + (lane >> 3)] = c;
+  if ((lane & 7) == 0) {
+    yrow[m0 + (lane >> 3)] = c;
+    for (int r = 0; r < nextra; ++r) y[(size_t)extra[r] * H + m0 + (lane >> 3)] = c;
+  }
 }
 
 template <int M, bool TAIL>
@@ -292,9 +310,12 @@ __global__ __launch_bounds__(kThreads, 2) void down_fast_kernel(
     if (bat0 >= bat1) continue;
     const int expert = bk.expert[b], row0 = bk.row0[b];
     const int slot = e2s ? e2s[expert] : expert;
+    const int nrep = bk.cnt[b];  // > 1 only for a repeated expert id of the one token
     if (slot < 0 || slot >= w.num_slots) {
-      float* yr = y + (size_t)sorted_pair[row0] * H;
-      for (int m = bat0 * 8 + lane; m < bat1 * 8; m += 64) yr[m] = 0.f;
+      for (int r = 0; r < nrep; ++r) {
+        float* yr = y + (size_t)sorted_pair[row0 + r] * H;
+        for (int m = bat0 * 8 + lane; m < bat1 * 8; m += 64) yr[m] = 0.f;
+      }
       continue;
     }
     const uint8_t* dc = w.wd + (size_t)slot * H * rowbytes;
@@ -314,17 +335,19 @@ __global__ __launch_bounds__(kThreads, 2) void down_fast_kernel(
         for (int q = 0; q < 8; ++q) ht[q] = p[q];
       }
     };
-    // one token per bucket: h stays in registers, two batches in flight
+    // one token: h stays in registers, two batches in flight; the rows of a
+    // repeated expert id are equal and stored once per pair
     load_h(row0);
     float* yrow = y + (size_t)sorted_pair[row0] * H;
+    const int32_t* extra = sorted_pair + row0 + 1;
     DownBatch<M, TAIL> A, Bn;
     dn_load(A, dc, ds, bat0 * 8, lane, rowbytes, NB);
     for (int bat = bat0; bat < bat1; bat += 2) {
       const bool has1 = bat + 1 < bat1;
       if (has1) dn_load(Bn, dc, ds, (bat + 1) * 8, lane, rowbytes, NB);
-      dn_finish(A, hm, ht, lane, yrow, bat * 8);
+      dn_finish(A, hm, ht, lane, yrow, bat * 8, extra, nrep - 1, y, H);
       if (bat + 2 < bat1) dn_load(A, dc, ds, (bat + 2) * 8, lane, rowbytes, NB);
-      if (has1) dn_finish(Bn, hm, ht, lane, yrow, (bat + 1) * 8);
+      if (has1) dn_finish(Bn, hm, ht, lane, yrow, (bat + 1) * 8, extra, nrep - 1, y, H);
     }
 
   }

@@ -135,16 +135,23 @@ __global__ __launch_bounds__(kPT) void quant_x_kernel(const uint16_t* __restrict
 // The token-major blocks copied into the sorted chunk-major layout: one
 // thread per (chunk c, sorted row p) reads its token's 96 B and scale word of
 // the chunk and writes the two 48-byte records (consecutive threads write
-// consecutive records) and the chunk's scale word.
+// consecutive records) and the chunk's scale word.  Only the rows that the
+// bucketing filled are read: sorted rows at or past offsets[E] (pairs whose
+// expert id was out of range are in no bucket) hold no pair index, and a
+// pair index outside [0, T*k) is skipped as well.
 __global__ __launch_bounds__(kPT) void sort_x_kernel(const uint8_t* __restrict__ xq_t,
                                                      const uint8_t* __restrict__ xs_t, int H, int k, int P,
+                                                     const int32_t* __restrict__ offsets, int E,
                                                      const int32_t* __restrict__ sorted_pair,
                                                      uint8_t* __restrict__ xq, uint32_t* __restrict__ xs) {
   const int g = blockIdx.x * kPT + threadIdx.x;
   const int nch = H / 128;
   if (g >= P * nch) return;
   const int c = g / P, p = g - c * P;
-  const size_t t = (size_t)(sorted_pair[p] / k);
+  if (p >= offsets[E]) return;
+  const int pair = sorted_pair[p];
+  if (pair < 0 || pair >= P) return;
+  const size_t t = (size_t)(pair / k);
   const uint2* src = reinterpret_cast<const uint2*>(xq_t + (t * (H / 32) + 4 * c) * 24);
   uint2 w[12];  // block b of the chunk = w[3b .. 3b+2]
 #pragma unroll
@@ -960,7 +967,7 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(sort_x_kernel, dim3((nq + kPT - 1) / kPT), dim3(kPT), 0, s, xq_t, xs_t, H, k, (int)P,
-                     sorted_pair, xq, reinterpret_cast<uint32_t*>(xs));
+                     offsets, E, sorted_pair, xq, reinterpret_cast<uint32_t*>(xs));
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(plan_kernel, dim3(kPlanGrid), dim3(kPT), 0, s, offsets, E, e2s, w.num_slots, I / GU_N, H / DN_N, run,

@@ -22,6 +22,10 @@ DECODE_CASES = {
     "groups40": gi.custom("groups40", 512, 384, 16, 4, 40, seed=23, zipf=1.1),
     # the largest decode batch: 256 tokens, buckets of up to 256 rows
     "batch256": gi.custom("batch256", 1024, 256, 8, 2, 256, seed=24),
+    # fewer routable experts (3) than k (4): the last slot of every token takes a
+    # non-routable expert with weight 0 and a zero row (multi-token and one-token kernels)
+    "few_resident": gi.custom("few_resident", 512, 256, 16, 4, 9, seed=25, resident=3),
+    "few_resident_1": gi.custom("few_resident_1", 1024, 256, 16, 4, 1, seed=26, resident=3),
 }
 
 
@@ -267,15 +271,10 @@ def test_route_all_ties_and_fewer_routable():
         e2s[rout] = np.arange(n_rout, dtype=np.int32)
         ids, w = m.moe_route(torch.from_numpy(logits).to(dev), k, torch.from_numpy(e2s).to(dev))
         ids, w = to_np(ids), to_np(w)
-        nonr = np.nonzero(e2s < 0)[0]
-        for t in range(logits.shape[0]):
-            first = rout[np.lexsort((rout, -logits[t, rout]))]
-            rest = nonr[np.lexsort((nonr, -logits[t, nonr]))][:k - n_rout]
-            np.testing.assert_array_equal(ids[t], np.concatenate([first, rest]))
-            assert np.all(w[t, n_rout:] == 0)
-            if n_rout:
-                _, ref_w = o.route(logits[t:t + 1], n_rout, e2s)
-                assert np.max(np.abs(w[t, :n_rout] - ref_w[0])) <= W_TOL
+        ref_ids, ref_w = o.route(logits, k, e2s)  # the oracle's fill reading (R-ROUTE-FILL)
+        np.testing.assert_array_equal(ids, ref_ids)
+        assert np.max(np.abs(w - ref_w)) <= W_TOL
+        assert np.all(w[:, n_rout:] == 0)
 
 
 def test_permute_large_and_empty():
@@ -298,3 +297,27 @@ def test_permute_large_and_empty():
     # empty batch: offsets all zero
     off0, _, _ = m.moe_permute(torch.empty((0, k), dtype=torch.int32, device=dev), E)
     assert not to_np(off0).any()
+
+
+@pytest.mark.parametrize("H,I", [(1024, 256), (2048, 2304)])
+def test_one_token_repeated_expert_ids(H, I):
+    """One token whose ids repeat an expert ([e, e, f, e]): its bucket holds the
+    token several times, and every one of those rows is written (the one-token
+    kernels compute the row once and store it per pair).  y_pair is checked
+    against the oracle on every row, after filling it with a sentinel."""
+    import fp4_routed_expert_mxfp4_amd as m
+    cfg = gi.custom(f"repeat_{H}_{I}", H, I, 8, 4, 1, seed=27)
+    print(f"case repeated ids H={H} I={I}", flush=True)
+    gl = GpuLayer(cfg)
+    ids = np.array([[5, 5, 2, 5]], np.int32)
+    off, sp, _ = m.moe_permute(torch.from_numpy(ids).cuda(), cfg.E)
+    for call in (m.moe_ffn_fp4_decode, m.moe_ffn_fp4_decode_invariant):
+        y = torch.full((cfg.k, cfg.H), 777.0, dtype=torch.float32, device="cuda")
+        call(gl.x, cfg.k, cfg.E, gl.store, None, off, sp, y_pair=y)
+        torch.cuda.synchronize()
+        y_ref = o.ffn(gl.hi.x_bf16, ids, gl.weights.matrix, cfg.H)
+        e = rel_err(to_np(y), y_ref)
+        print(f"[repeat {H}x{I} {call.__name__}] y_pair rel {e:.3e}", flush=True)
+        assert e <= REL_TOL
+        yn = to_np(y)
+        assert np.array_equal(yn[0], yn[1]) and np.array_equal(yn[0], yn[3])

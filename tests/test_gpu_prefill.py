@@ -6,7 +6,7 @@ import torch
 
 from gen import inputs as gi
 from oracle import moe_oracle as o
-from tests.harness import REL_TOL, W_TOL, GpuLayer, bf16_excess, rel_err, to_np
+from tests.harness import PREFILL_A16_BOUND, REL_TOL, W_TOL, GpuLayer, bf16_excess, rel_err, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -18,6 +18,8 @@ PREFILL_CASES = {
     "mid_resident": gi.custom("mid_resident_p", 512, 256, 40, 6, 77, seed=32, resident=10),
     # hidden 6144: the gate/up K loop spans two scale windows; buckets of ~100 rows (tiled path)
     "wide_hidden": gi.custom("wide_hidden_p", 6144, 256, 4, 2, 200, seed=33),
+    # fewer routable experts (3) than k (4): weight-0 slots with zero rows
+    "few_resident": gi.custom("few_resident_p", 512, 256, 16, 4, 9, seed=34, resident=3),
 }
 
 
@@ -52,10 +54,11 @@ def test_prefill_layer_matches_oracle(name):
     e_32 = rel_err(to_np(r["out32"]), ref["out"])
     e_16 = bf16_excess(to_np(r["out16"]), ref["out"])
     a16 = o.moe_layer(gl.hi.x_bf16, gl.hi.logits[0], gl.weights.matrix, gl.cfg.k, gl.cfg.H, "a16", gl.e2s_np)
-    e_info = rel_err(to_np(r["out32"]), a16["out"])
+    e_a16 = rel_err(to_np(r["out32"]), a16["out"])
     print(f"[{name}] y_pair rel {e_y:.3e}  out fp32 rel {e_32:.3e}  bf16 excess {e_16:.3e}  "
-          f"(vs unquantised reference, for information: {e_info:.3e})", flush=True)
+          f"distance to the unquantised (a16) definition {e_a16:.3e} (bound {PREFILL_A16_BOUND})", flush=True)
     assert e_y <= REL_TOL and e_32 <= REL_TOL and e_16 <= REL_TOL
+    assert e_a16 <= PREFILL_A16_BOUND
 
 
 def test_prefill_quantiser_bit_exact_all_bf16():
@@ -98,23 +101,82 @@ def test_prefill_quantiser_bit_exact_all_bf16():
     np.testing.assert_array_equal(xq, pack6(codes))
 
 
-def test_prefill_full_size_sampled_tokens():
-    """The 4096-token chunk in the launch configuration the benchmark times,
-    checked on a sample of tokens the oracle evaluates one by one."""
+@pytest.fixture(scope="module")
+def full_prefill():
+    """The 4096-token chunk run once through route -> permute -> prefill FFN ->
+    combine, in the launch configuration the benchmark times."""
     cfg = gi.CONFIGS["prefill4096"]
+    print("case prefill4096 (full chunk)", flush=True)
     gl = GpuLayer(cfg)
     r = gl.run("prefill")
     ids_ref, w_ref = o.route(gl.hi.logits[0], cfg.k)
     np.testing.assert_array_equal(to_np(r["ids"]), ids_ref)
-    # sample: tokens whose experts are few and shared, plus the first and last token
+    offsets = to_np(r["offsets"])
+    sp = to_np(r["sorted_pair"])
+    yield dict(cfg=cfg, gl=gl, r=r, ids=ids_ref, w=w_ref, offsets=offsets, sp=sp)
+    gl.weights.drop()
+
+
+def _stratified_rows(offsets):
+    """Rows of every touched expert's bucket to compare: all of a bucket of at
+    most 48 rows (the small-bucket streaming kernels take up to 32), else its
+    first 8 rows, its last 160 (the ragged last row tile and the full tile
+    before it, for row tiles of up to 160) and every 97th row between."""
+    plan = []
+    for e in range(len(offsets) - 1):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        n = b - a
+        if n == 0:
+            continue
+        if n <= 48:
+            rows = list(range(n))
+        else:
+            rows = sorted(set(range(8)) | set(range(max(0, n - 160), n)) | set(range(0, n, 97)))
+        plan.append((e, [a + r for r in rows]))
+    return plan
+
+
+N_PARTS = 4
+
+
+@pytest.mark.parametrize("part", range(N_PARTS))
+def test_prefill_full_size_every_expert(full_prefill, part):
+    """Every touched expert of the 4096-token chunk has rows compared with the
+    oracle: every row of the small buckets, and the first rows, the ragged
+    last tile and a spread of rows of every tiled bucket.  The experts are
+    split over N_PARTS tests (round robin) to keep each under a minute."""
+    f = full_prefill
+    cfg, gl = f["cfg"], f["gl"]
+    plan = _stratified_rows(f["offsets"])[part::N_PARTS]
+    if part == 0:
+        sizes = np.diff(f["offsets"])
+        print(f"prefill4096: {np.count_nonzero(sizes)} experts touched, {np.count_nonzero((sizes > 0) & (sizes <= 32))} "
+              f"small buckets, largest {sizes.max()} rows", flush=True)
+    worst, nrows = 0.0, 0
+    for e, rows in plan:
+        pairs = f["sp"][rows]
+        y_dev = f["r"]["y_pair"][torch.from_numpy(pairs.astype(np.int64)).cuda()]
+        x = o.bf16_bits_to_f64(gl.hi.x_bf16[pairs // cfg.k])
+        y_ref = o.expert_ffn(x, gl.weights.matrix, e, "a6")
+        err = rel_err(to_np(y_dev), y_ref)
+        worst = max(worst, err)
+        nrows += len(rows)
+        gl.weights.drop()
+        assert err <= REL_TOL, f"expert {e}: rel {err:.3e} over {len(rows)} rows"
+    print(f"[prefill4096 part {part}] {len(plan)} experts, {nrows} rows, worst expert rel {worst:.3e}", flush=True)
+
+
+def test_prefill_full_size_sampled_tokens(full_prefill):
+    """Whole tokens of the 4096-token chunk (all k rows and the combine) on a
+    sample the oracle evaluates one by one; byte determinism of a rerun."""
+    f = full_prefill
+    cfg, gl, r = f["cfg"], f["gl"], f["r"]
     rng = np.random.default_rng(0)
-    pop = np.bincount(ids_ref.reshape(-1), minlength=cfg.E)
-    top = set(np.argsort(-pop)[:24].tolist())
-    cands = [t for t in range(cfg.T) if sum(int(e) in top for e in ids_ref[t]) >= 7]
-    sample = sorted(set([0, cfg.T - 1] + list(rng.choice(cands, 10, replace=False))))
+    sample = sorted(set([0, cfg.T - 1] + list(rng.choice(cfg.T, 6, replace=False))))
     x = gl.hi.x_bf16[sample]
-    y_ref = o.ffn(x, ids_ref[sample], gl.weights.matrix, cfg.H, "a6")
-    out_ref = o.combine(y_ref, w_ref[sample])
+    y_ref = o.ffn(x, f["ids"][sample], gl.weights.matrix, cfg.H, "a6")
+    gl.weights.drop()
+    out_ref = o.combine(y_ref, f["w"][sample])
     y = to_np(r["y_pair"]).reshape(cfg.T, cfg.k, cfg.H)[sample].reshape(-1, cfg.H)
     e_y = rel_err(y, y_ref)
     e_32 = rel_err(to_np(r["out32"])[sample], out_ref)
@@ -125,3 +187,47 @@ def test_prefill_full_size_sampled_tokens():
     assert np.isfinite(to_np(r["out32"])).all()
     r2 = gl.run("prefill")
     assert torch.equal(r["y_pair"], r2["y_pair"]) and torch.equal(r["out16"], r2["out16"])
+
+
+@pytest.mark.parametrize("path", ["prefill", "decode"])
+def test_out_of_range_ids_are_left_out(path):
+    """Pairs whose expert id lies outside [0, E) are in no bucket: the FFN
+    reads no row of them and writes no y_pair row for them (the rows keep what
+    they held), and every other row equals the oracle's.  route -> permute ->
+    FFN -> combine, with the ids edited between route and permute."""
+    import fp4_routed_expert_mxfp4_amd as m
+    cfg = gi.custom(f"badids_{path}", 512, 256, 16, 4, 40, seed=35)
+    print(f"case badids {path}", flush=True)
+    gl = GpuLayer(cfg)
+    ids_ref, w_ref = o.route(gl.hi.logits[0], cfg.k)
+    ids = ids_ref.copy()
+    bad = [(3, 1, -1), (7, 0, cfg.E), (20, 3, -5), (39, 2, 1 << 20)]
+    for t, j, v in bad:
+        ids[t, j] = v
+    dev_ids = torch.from_numpy(ids).cuda()
+    off, sp, p2r = m.moe_permute(dev_ids, cfg.E)
+    offn = to_np(off)
+    assert offn[-1] == cfg.T * cfg.k - len(bad)
+    p2rn = to_np(p2r)
+    for t, j, _ in bad:
+        assert p2rn[t * cfg.k + j] == -1
+    sentinel = 12345.0
+    y = torch.full((cfg.T * cfg.k, cfg.H), sentinel, dtype=torch.float32, device="cuda")
+    ffn = m.moe_ffn_fp4_prefill if path == "prefill" else m.moe_ffn_fp4_decode
+    ffn(gl.x, cfg.k, cfg.E, gl.store, None, off, sp, y_pair=y)
+    torch.cuda.synchronize()
+    yn = to_np(y)
+    mode = "a6" if path == "prefill" else "a16"
+    ok = np.ones(cfg.T * cfg.k, bool)
+    for t, j, _ in bad:
+        ok[t * cfg.k + j] = False
+        assert np.all(yn[t * cfg.k + j] == sentinel)
+    y_ref = o.ffn(gl.hi.x_bf16, np.where(ids_ref >= 0, ids_ref, 0), gl.weights.matrix, cfg.H, mode)
+    e = rel_err(yn[ok], y_ref[ok])
+    # the combine of the tokens without an out-of-range id matches the oracle's
+    w_dev = torch.from_numpy(w_ref.astype(np.float32)).cuda()
+    out = to_np(m.moe_combine(y, w_dev, None, m.MOE_OUT_F32))
+    good_t = sorted(set(range(cfg.T)) - {t for t, _, _ in bad})
+    e_out = rel_err(out[good_t], o.combine(y_ref, w_ref)[good_t])
+    print(f"[badids {path}] valid rows rel {e:.3e}, combined rel {e_out:.3e}", flush=True)
+    assert e <= REL_TOL and e_out <= REL_TOL
