@@ -3,6 +3,8 @@
 // neither the device nor the stream.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/moe_fp4.h"
 #include "kernels.h"
 
@@ -43,6 +45,31 @@ moe_status check_ffn_common(const uint16_t* x, int32_t T, int32_t k, int32_t E, 
     if (misaligned(ws, 256)) return MOE_ERR_ALIGN;
   }
   return MOE_OK;
+}
+
+// Scratch of moe_decode_layer_noalloc: a device array of the library, so
+// that call needs no allocation.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per
+// device (with that device current) and only that address is handed to the
+// kernels.  Every call on one device shares that device's copy.
+__device__ __attribute__((aligned(256))) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`; false if the runtime cannot give it.
+bool noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return false;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return true;
 }
 
 }  // namespace
@@ -257,12 +284,14 @@ MOE_FP4_API size_t moe_decode_layer_workspace_bytes(int32_t T, int32_t k, int32_
   return layer_ws_layout(T, k, E, hidden, inter, nullptr).total;
 }
 
-// norm: x_bf16 is the raw residual row; it is normalised first (as moe_rmsnorm_bf16, eps) and is
-// itself the residual (residual_bf16 is then ignored).
-static moe_status decode_layer(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E, int32_t k,
-                               const int32_t* expert_to_slot, const moe_fp4_experts* w, const uint16_t* residual_bf16,
-                               moe_out_dtype od, void* out, int32_t* topk_ids, float* topk_w, void* ws,
-                               size_t ws_bytes, int phase, hipStream_t stream, bool norm = false, float eps = 0.f) {
+// Checks of a decode-layer call other than its workspace; *need receives the
+// workspace bytes the call takes.  MOE_OK with *need == 0 means T == 0 (nothing to do).
+static moe_status check_decode_layer(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E, int32_t k,
+                                     const int32_t* expert_to_slot, const moe_fp4_experts* w,
+                                     const uint16_t* residual_bf16, moe_out_dtype od, const void* out,
+                                     const int32_t* topk_ids, const float* topk_w, bool norm, float eps,
+                                     size_t* need) {
+  *need = 0;
   if (T > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
   if (od != MOE_OUT_BF16 && od != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
   moe_status st = check_store(w);
@@ -275,9 +304,23 @@ static moe_status decode_layer(const float* logits, const uint16_t* x_bf16, int3
     return MOE_ERR_ALIGN;
   if (norm && !(eps >= 0.0f)) return MOE_ERR_SHAPE;
   const size_t lbytes = moe_decode_layer_workspace_bytes(T, k, E, w->hidden, w->inter);
-  const size_t need = norm ? up256(lbytes) + up256((size_t)T * w->hidden * 2) : lbytes;
+  *need = norm ? up256(lbytes) + up256((size_t)T * w->hidden * 2) : lbytes;
+  return MOE_OK;
+}
+
+// norm: x_bf16 is the raw residual row; it is normalised first (as moe_rmsnorm_bf16, eps) and is
+// itself the residual (residual_bf16 is then ignored).
+static moe_status decode_layer(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E, int32_t k,
+                               const int32_t* expert_to_slot, const moe_fp4_experts* w, const uint16_t* residual_bf16,
+                               moe_out_dtype od, void* out, int32_t* topk_ids, float* topk_w, void* ws,
+                               size_t ws_bytes, int phase, hipStream_t stream, bool norm = false, float eps = 0.f) {
+  size_t need = 0;
+  const moe_status st = check_decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out,
+                                           topk_ids, topk_w, norm, eps, &need);
+  if (st != MOE_OK || T == 0) return st;
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
   if (misaligned(ws, 256)) return MOE_ERR_ALIGN;
+  const size_t lbytes = moe_decode_layer_workspace_bytes(T, k, E, w->hidden, w->inter);
   const moe::ExpertStore store = to_store(w);
   const bool bf16 = od == MOE_OUT_BF16;
   if (norm) residual_bf16 = x_bf16;
@@ -313,6 +356,21 @@ MOE_FP4_API moe_status moe_decode_layer(const float* logits, const uint16_t* x_b
                                         hipStream_t stream) {
   return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out, topk_ids, topk_w, ws,
                       ws_bytes, 0, stream);
+}
+
+MOE_FP4_API moe_status moe_decode_layer_noalloc(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E,
+                                                int32_t k, const int32_t* expert_to_slot, const moe_fp4_experts* w,
+                                                const uint16_t* residual_bf16, moe_out_dtype od, void* out,
+                                                int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  size_t need = 0;
+  const moe_status st = check_decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out,
+                                           topk_ids, topk_w, false, 0.f, &need);
+  if (st != MOE_OK || T == 0) return st;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (!noalloc_scratch(&ws)) return MOE_ERR_LAUNCH;
+  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out, topk_ids, topk_w, ws,
+                      MOE_NOALLOC_SCRATCH_BYTES, 0, stream);
 }
 
 MOE_FP4_API moe_status moe_decode_layer_gateup(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E,

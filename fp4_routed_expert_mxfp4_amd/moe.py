@@ -24,7 +24,7 @@ MOE_ACT_MXFP6_E2M3 = 0
 EXPORTED = ("moe_route", "moe_router_logits", "moe_route_x", "moe_ffn_cb3_decode_workspace_bytes", "moe_ffn_cb3_decode", "moe_permute_workspace_bytes", "moe_permute", "moe_ffn_fp4_decode_workspace_bytes", "moe_ffn_fp4_decode",
             "moe_ffn_fp4_decode_gateup", "moe_ffn_fp4_decode_down", "moe_ffn_fp4_decode_subset",
             "moe_ffn_fp4_decode_invariant",
-            "moe_decode_layer_workspace_bytes", "moe_decode_layer", "moe_decode_layer_gateup",
+            "moe_decode_layer_workspace_bytes", "moe_decode_layer", "moe_decode_layer_noalloc", "moe_decode_layer_gateup",
             "moe_decode_layer_down", "moe_decode_layer_rmsnorm_workspace_bytes", "moe_decode_layer_rmsnorm",
             "moe_ffn_fp4_prefill_workspace_bytes", "moe_ffn_fp4_prefill", "moe_ffn_fp4_prefill_subset", "moe_combine",
             "moe_rmsnorm_bf16", "moe_status_string")
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
                                              vp],
             "moe_decode_layer_workspace_bytes": [i32, i32, i32, i32, i32],
             "moe_decode_layer": _LAYER_ARGS,
+            "moe_decode_layer_noalloc": [vp, vp, i32, i32, i32, vp, ctypes.POINTER(CExperts), vp, ctypes.c_int, vp,
+                                         vp, vp, vp],
             "moe_decode_layer_gateup": _LAYER_ARGS,
             "moe_decode_layer_down": _LAYER_ARGS,
             "moe_decode_layer_rmsnorm_workspace_bytes": [i32, i32, i32, i32, i32],
@@ -439,6 +441,41 @@ def moe_decode_layer(logits: torch.Tensor, x: torch.Tensor, k: int, store: Exper
     _check(name, getattr(lib(), name)(
         _ptr(logits), _ptr(x), T, E, k, _ptr(expert_to_slot), ctypes.byref(cs), _ptr(residual), out_dtype,
         _ptr(out), _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(), _stream(dev)))
+    return out, topk_ids, topk_w
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MOE_NOALLOC_SCRATCH_BYTES of the C header
+
+
+def moe_decode_layer_noalloc(logits: torch.Tensor, x: torch.Tensor, k: int, store: ExpertStore,
+                             expert_to_slot: torch.Tensor | None = None, residual: torch.Tensor | None = None,
+                             out_dtype: int = MOE_OUT_BF16, out: torch.Tensor | None = None,
+                             topk_ids: torch.Tensor | None = None, topk_w: torch.Tensor | None = None):
+    """moe_decode_layer on the library's static scratch (no workspace argument).
+    Returns (out, topk_ids, topk_w); out, topk_ids and topk_w are allocated here
+    only when not given."""
+    _want(logits, (torch.float32,), "logits")
+    _want(x, _BF16, "x")
+    T, E = logits.shape
+    H = x.shape[1]
+    dev = x.device
+    if expert_to_slot is not None:
+        _want(expert_to_slot, (torch.int32,), "expert_to_slot")
+    if residual is not None:
+        _want(residual, _BF16, "residual")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16 if out_dtype == MOE_OUT_BF16 else torch.float32, device=dev)
+    _want(out, _BF16 if out_dtype == MOE_OUT_BF16 else (torch.float32,), "out")
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _want(topk_ids, (torch.int32,), "topk_ids")
+    _want(topk_w, (torch.float32,), "topk_w")
+    cs = store.cstruct()
+    _check("moe_decode_layer_noalloc", lib().moe_decode_layer_noalloc(
+        _ptr(logits), _ptr(x), T, E, k, _ptr(expert_to_slot), ctypes.byref(cs), _ptr(residual), out_dtype,
+        _ptr(out), _ptr(topk_ids), _ptr(topk_w), _stream(dev)))
     return out, topk_ids, topk_w
 
 

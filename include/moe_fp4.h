@@ -275,6 +275,29 @@ MOE_FP4_API moe_status moe_decode_layer(const float* logits, const uint16_t* x_b
                                         moe_out_dtype od, void* out, int32_t* topk_ids, float* topk_w,
                                         void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_decode_layer_noalloc -- moe_decode_layer for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments and the same results
+ * bit for bit, without a workspace argument.  The workspace is instead a
+ * static device array of the library, MOE_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the first call on a GPU until the process ends; the call itself
+ * allocates and frees nothing.  Its device address is looked up on the first
+ * call on each GPU (with that GPU current), which should therefore happen
+ * outside graph capture.  A call whose moe_decode_layer_workspace_bytes
+ * exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE (one token at
+ * the 5120 x 2304 shape takes 74 KB, 16 tokens 3.8 MB).  Nothing in the
+ * array needs to start at zero.  All calls on one GPU share its array, so
+ * calls that may overlap in time on one GPU (different streams, threads) race
+ * on it and must be serialised by the caller; calls in stream order do not.
+ * Unlike the other calls it keeps one piece of global state, the per-GPU
+ * address of the array. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+MOE_FP4_API moe_status moe_decode_layer_noalloc(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E,
+                                                int32_t k, const int32_t* expert_to_slot,
+                                                const moe_fp4_experts* w, const uint16_t* residual_bf16,
+                                                moe_out_dtype od, void* out, int32_t* topk_ids, float* topk_w,
+                                                hipStream_t stream);
+
 /* moe_decode_layer_gateup, moe_decode_layer_down -- the two halves of
  * moe_decode_layer with the same arguments: gateup routes (writing topk_ids,
  * topk_w and the routing state in ws) and runs the gate/up + SwiGLU weight

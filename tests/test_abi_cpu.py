@@ -290,3 +290,23 @@ def test_cb3_decode_validation():
     assert call(k=9) == m.MOE_ERR_SHAPE
     assert call(T=0, x=None) == m.MOE_OK
     assert L.moe_ffn_cb3_decode_workspace_bytes(1, 8, 2304) == 8 * 2304 * 4
+
+
+def test_noalloc_layer_validation():
+    """moe_decode_layer_noalloc validates as moe_decode_layer and rejects, before
+    any HIP call, a call whose workspace would not fit the static scratch."""
+    m = _lib()
+    L = m.lib()
+    big = _store(m, hidden=5120, inter=2304, num_slots=384)
+    call = lambda logits=FAKE, x=FAKE, T=1, E=384, k=8, st=big, od=0, out=FAKE: L.moe_decode_layer_noalloc(
+        logits, x, T, E, k, None, ctypes.byref(st), None, od, out, FAKE, FAKE, None)
+    assert call(logits=None) == m.MOE_ERR_NULL
+    assert call(out=MIS) == m.MOE_ERR_ALIGN
+    assert call(od=5) == m.MOE_ERR_UNSUPPORTED
+    assert call(k=17) == m.MOE_ERR_SHAPE
+    assert call(T=257) == m.MOE_ERR_UNSUPPORTED
+    assert call(T=0) == m.MOE_OK
+    # 256 tokens need 58 MiB, 128 tokens 29 MiB: the scratch holds 32 MiB
+    assert m.decode_layer_workspace_bytes(256, 8, 384, 5120, 2304) > m.NOALLOC_SCRATCH_BYTES
+    assert m.decode_layer_workspace_bytes(128, 8, 384, 5120, 2304) <= m.NOALLOC_SCRATCH_BYTES
+    assert call(T=256) == m.MOE_ERR_WORKSPACE
