@@ -180,9 +180,8 @@ __global__ __launch_bounds__(kPT) void sort_x_kernel(const uint8_t* __restrict__
 
 constexpr int BM = 128;            // bucket rows per tile
 constexpr int KC = 128;            // K per chunk (4 scale blocks, 2 MFMA K-steps)
-constexpr int GU_N = 128;          // gate/up tile: 128 h columns = 128 gate + 128 up weight rows
-constexpr int DN_N = 256;          // down tile: 256 output columns
-constexpr int STAGE_S = GU_N + 1;  // fp32 words per row of the h staging buffer
+constexpr int GU_N = 256;          // gate/up tile: 256 h columns = 256 gate + 256 up weight rows
+constexpr int DN_N = 512;          // down tile: 512 output columns
 constexpr int kGrid = 256;         // persistent workgroups (one per CU: the LDS holds one)
 
 constexpr int SK_MAX = 32;  // buckets with at most this many rows take the streaming kernels
@@ -321,45 +320,48 @@ constexpr uint32_t kOpenRange = 0x7FFFFFF0u;  // range of the activation buffers
 
 // ---- the grouped GEMM core ---------------------------------------------------------
 //
-// A workgroup computes a tile of BM bucket rows x 256 weight rows over all of
-// K, in chunks of 128 (four 32-blocks, two MFMA 32x32x64 K-steps).  Each
-// wavefront owns 64 weight rows (two 32-row B fragments) and all BM rows (four
-// A fragments): 8 MFMAs per K-step.  The weight rows are not shared between
-// wavefronts, so they go straight from memory into the wavefront's registers
-// in MFMA order, three chunks ahead.  The MXFP6 activations are shared: staged
-// once per chunk through LDS (double-buffered, one barrier per chunk).  The
-// scale tables and the h staging buffer fill most of the LDS, so one
-// workgroup runs per CU (one wavefront per SIMD).
-//
-// LDS layout of one A chunk: for each K-half h a region of BM rows x 48 B --
-// blocks h and 2+h of the chunk, i.e. the lane's A operand for K-steps 0 and 1
-// -- read as three 16-B loads per lane (lanes 48 B apart touch every bank
-// once); then one scale word (4 bytes) per row.
+// A tile is BM = 128 bucket rows x 4 * WN = 512 weight rows over all of K, in
+// chunks of 128 (four 32-blocks, two K-steps of V_MFMA_SCALE_F32_32X32X64).
+// Each wavefront owns WN = 128 weight rows (four 32-row B fragments) and all
+// 128 bucket rows (four A fragments): 16 MFMAs per K-step into 16 x 16 fp32
+// accumulators per lane.  Its weight rows are used by no other wavefront, so
+// they go from memory straight into its registers; the MXFP6 activations are
+// shared by the four wavefronts and staged once per chunk through a
+// three-stage LDS ring with one barrier per chunk.  With three stages the
+// first K-step of chunk c+1 is read from LDS while chunk c is multiplied (it
+// was stored before the previous barrier), and the stage refilled during
+// chunk c (with chunk c+2) was last read before that barrier.  The scale
+// bytes of the tile are read once per window of TWIN chunks into LDS tables
+// (row-contiguous loads: a per-chunk 4-byte load from every row would cost a
+// cache-line request per row).
 
+// A copy of v that the compiler cannot see through: per-lane index arithmetic
+// derived from it is recomputed where it is used instead of being hoisted out
+// of the persistent tile loop (hoisted, the table and epilogue addresses of a
+// tile would hold well over a hundred registers for the whole kernel).
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+constexpr int WN = 128;             // weight rows per wavefront (four fragments)
+constexpr int NSTAGE = 3;           // A chunks held in LDS
 constexpr int A_HS = BM * 48 + 64;  // LDS bytes per K-half region of an A chunk
+constexpr int A_STAGE = 2 * A_HS;   // LDS bytes per A chunk
+constexpr int TWIN = 40;            // scale-table window in chunks (160 blocks)
+constexpr int TSW = TWIN + 1;       // words per table row (odd: a fragment's 32 rows hit 32 banks)
 
-struct ABuf {
-  uint8_t codes[2 * A_HS];
-};
-
-// Scale bytes are read once per tile into LDS tables (a scale word -- the 4
-// blocks of one chunk -- per row and chunk, for a window of SCWIN chunks):
-// per-chunk loads of 4 bytes from every row would each cost a cache-line
-// request.  The rows of a wavefront's weight fragment are consecutive, so
-// their table loads read contiguous memory.
-constexpr int SCWIN = 40;       // largest scale window in chunks (160 blocks)
-constexpr int SCW = SCWIN + 1;  // words per table row (odd: a fragment's 32 rows hit 32 banks)
-
-struct GemmSmem {
+struct TileSmem {
   union {
-    ABuf a[2];
-    float stage[BM * STAGE_S];
+    struct {
+      uint8_t a[NSTAGE][A_STAGE];
+      uint32_t sca[BM * TSW];     // A scale words of the tile's rows, [row][chunk of the window]
+      uint32_t scb[4][WN * TSW];  // B scale words of each wavefront's 128 weight rows
+    } k;
+    float stage[BM * (GU_N + 1)];  // gate/up epilogue: h of the tile, fp32
   };
-  uint32_t sca[BM * SCW];      // A scale words of the tile's rows
-  uint32_t scb[4][64 * SCW];   // B scale words of each wavefront's 64 weight rows
   int rowtok[BM];
 };
-
 
 // Words [cw0, cw0 + WIN) of ROWS table rows from a chunk-major word array
 // ([chunk][row], row stride 1 word, P rows per chunk): consecutive threads
@@ -385,165 +387,202 @@ struct ScaleCols {
   }
 };
 
-// The scale tables of one tile for a window of WIN chunks: A rows (all
-// threads; AS is the loader of the A scale layout) and each wavefront's two
-// 32-row weight fragments.
-template <int WIN, typename AS>
-struct TileScales {
-  static constexpr int kWin = WIN;
-  static_assert(WIN <= SCWIN, "scale window");
-  AS a;
-  ScaleRows<32, 64, WIN, SCW> b[2];
+// Half (rows 64 HALF .. 64 HALF + 63) of the B scale table of one wavefront:
+// words [cw0, cw0 + TWIN) of those weight rows, read as 8-byte pairs (a row's
+// scale bytes are contiguous and 8-byte aligned: K is a multiple of 256).
+// Words past a row's end belong to the next row or lie past the resource's
+// range (zeros); they are never used.  row_off(r): byte offset of table row r.
+template <int HALF>
+struct BTable {
+  static constexpr int N = (WN / 2) * TWIN / 2 / 64;  // 8-byte loads per lane
+  uint2 v[N];
+  template <typename RowRes, typename RowOff>
+  __device__ __forceinline__ void issue(RowRes res, RowOff row_off, int cw0, int lane) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = lane + 64 * i, row = 64 * HALF + idx / (TWIN / 2), pr = idx % (TWIN / 2);
+      v[i] = bload8(res(row), row_off(row) + 4u * (uint32_t)(cw0 + 2 * pr));
+    }
+  }
+  __device__ __forceinline__ void store(uint32_t* tab, int lane) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = lane + 64 * i, row = 64 * HALF + idx / (TWIN / 2), pr = idx % (TWIN / 2);
+      tab[row * TSW + 2 * pr] = v[i].x;
+      tab[row * TSW + 2 * pr + 1] = v[i].y;
+    }
+  }
 };
 
-// Registers of one A chunk between its global loads and its LDS store: the
-// tile's two records runs (K-half 0, then 1; 128 rows x 48 B each) as 768
-// pieces of 16 B, piece t + 256j in thread t.  Memory and LDS hold the runs
-// in the same order, so the store is a plain copy.
-struct ARegs {
+// One A chunk in registers between its loads and its LDS store: the tile's two
+// record runs (K-half 0, then 1; 128 rows x 48 B each) as 768 pieces of 16 B,
+// piece t + 256 j in thread t.  Memory and LDS hold the runs in the same order.
+struct AStage {
   uint4_t q[3];
 };
 
 struct ASrc {
   rsrc_t rc;
-  uint32_t vc[3];     // this thread's pieces of chunk 0
-  uint32_t cstride;   // bytes per chunk: both K-halves of all P rows
-  __device__ __forceinline__ void load(int c, ARegs& r) const {
+  uint32_t vc[3];    // this thread's pieces of chunk 0
+  uint32_t cstride;  // bytes per chunk: both K-halves of all P rows
+  // Rows past the bucket read other buckets' records (their outputs are never
+  // stored and their scale words are zero); past the array's end they read zeros.
+  __device__ __forceinline__ void init(const uint8_t* base, uint32_t bytes, int tid, int row0, int P) {
+    rc = make_rsrc(base, bytes);
+    cstride = 96u * (uint32_t)P;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int i = tid + kPT * j, h = i / (BM * 3);
+      vc[j] = ((uint32_t)h * (uint32_t)P + (uint32_t)row0) * 48u + (uint32_t)(i - h * BM * 3) * 16u;
+    }
+  }
+  __device__ __forceinline__ void load(int c, AStage& r) const {
 #pragma unroll
     for (int j = 0; j < 3; ++j) r.q[j] = bload16(rc, vc[j] + (uint32_t)c * cstride);
   }
 };
 
-__device__ __forceinline__ void store_a(ABuf& d, const ARegs& r, int tid) {
+__device__ __forceinline__ void store_a(uint8_t* st, const AStage& r, int tid) {
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const int i = tid + kPT * j, h = i / (BM * 3);
-    *reinterpret_cast<uint4_t*>(d.codes + h * A_HS + (i - h * BM * 3) * 16) = r.q[j];
+    *reinterpret_cast<uint4_t*>(st + h * A_HS + (i - h * BM * 3) * 16) = r.q[j];
   }
 }
 
-// A offsets of a tile whose rows are sorted rows row0.. of P.  Rows past the
-// bucket read other buckets' records (their outputs are never stored, and
-// their scale words are zero); past the array's end they read zeros.
-__device__ __forceinline__ void a_offsets(ASrc& as, int tid, int row0, int P) {
-  as.cstride = 96u * (uint32_t)P;
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int i = tid + kPT * j, h = i / (BM * 3);
-    as.vc[j] = ((uint32_t)h * (uint32_t)P + (uint32_t)row0) * 48u + (uint32_t)(i - h * BM * 3) * 16u;
+// The lane's A operand of K-step S of fragment f: 24 bytes at offset 24 S of
+// the 48-byte record of row 32 f + r32 in K-half h (blocks 4c + h and 4c + 2 + h).
+template <int S>
+__device__ __forceinline__ i8v read_afrag(const uint8_t* st, int f, int r32, int h) {
+  const uint8_t* p = st + h * A_HS + (32 * f + r32) * 48 + 24 * S;
+  if (S == 0) {
+    const uint4_t a = *reinterpret_cast<const uint4_t*>(p);
+    const uint2 b = *reinterpret_cast<const uint2*>(p + 16);
+    return i8v{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, 0, 0};
+  } else {
+    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    const uint4_t b = *reinterpret_cast<const uint4_t*>(p + 8);
+    return i8v{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0};
   }
 }
 
-// One wavefront's B operand for one chunk.  Each fragment's 32 rows are
-// loaded as two halves of 16 rows x 64 contiguous bytes (lane l: row 16j +
-// l%16, block l/16 of the chunk), which touches half the cache lines of the
-// MFMA order (32 rows x 32 B); b_operands() moves them into MFMA order with two
-// lane swaps per dword when they are used.
-struct BRegs {
-  uint4_t q[2][2];  // [fragment][row half], as loaded
+// One wavefront's weight rows for one chunk: each fragment's 32 rows as two
+// loads of 16 rows x 64 contiguous bytes (lane l: row 16 j + l % 16, block
+// l / 16 of the chunk); b_operands() moves them into MFMA order.
+struct BChunk {
+  uint4_t q[4][2];  // [fragment][row half]
 };
 
 struct BSrc {
-  rsrc_t rc[2];     // codes of fragment 0 and 1
-  uint32_t vc[2];   // row (lane%16) offset + 16 * (lane/16)
-  uint32_t half;    // byte distance of row 16 from row 0
-  __device__ __forceinline__ void load(int c, BRegs& r) const {
+  rsrc_t rc[4];    // codes of the matrix holding each fragment
+  uint32_t vc[4];  // fragment row (lane % 16) offset + 16 * (lane / 16)
+  uint32_t half;   // byte distance of fragment row 16 from row 0
+  __device__ __forceinline__ void load(int c, BChunk& r) const {
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int j = 0; j < 2; ++j) r.q[g][j] = bload16(rc[g], vc[g] + half * j + (uint32_t)c * 64u);
   }
 };
 
-
-// One chunk of MFMAs: A fragments from LDS (48 B per lane = both K-steps),
-// B from registers.  With an empty chunk (nks == 0) nothing is multiplied.
-__device__ __forceinline__ void mma_chunk(const ABuf& cur, const BRegs& b, const uint32_t* sca, const uint32_t* scb,
-                                          int cw, f16v (&acc)[4][2], int nks, int lane) {
-  const int r32 = lane & 31, h = lane >> 5;
-  if (nks == 0) return;
-  uint4_t av[4][3];
-  uint32_t asw[4];
+// Chunk c of the tile (i = c - cw0 within the window): both K-steps, 32
+// MFMAs.  af holds the chunk's K-step 0 fragments on entry and the next
+// chunk's on return (read from stage nxt).  run == false multiplies nothing
+// (a chunk past the last one of a pair).
+__device__ __forceinline__ void tile_chunk(const TileSmem& sm, const uint8_t* cur, const uint8_t* nxt,
+                                           const BChunk& bc, i8v (&af)[4], f16v (&acc)[4][4], int i, int wid,
+                                           int r32, int h, bool run) {
+  uint32_t sa[4], sb[4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const uint4_t* p = reinterpret_cast<const uint4_t*>(cur.codes + h * A_HS + (32 * f + r32) * 48);
-    av[f][0] = p[0];
-    av[f][1] = p[1];
-    av[f][2] = p[2];
-    asw[f] = sca[(32 * f + r32) * SCW + cw] >> (8 * h);
+  for (int f = 0; f < 4; ++f) sa[f] = sm.k.sca[(32 * f + r32) * TSW + i] >> (8 * h);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) sb[g] = sm.k.scb[wid][(32 * g + r32) * TSW + i] >> (8 * h);
+  i8v bop[4][2];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) b_operands(bc.q[g][0], bc.q[g][1], bop[g][0], bop[g][1]);
+  i8v af1[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) af1[f] = read_afrag<1>(cur, f, r32, h);
+  if (run) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[f], bop[g][0], acc[f][g], 2, 4, 0,
+                                                                     (int)sa[f], 0, (int)sb[g]);
   }
-  uint32_t bsw[2];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) bsw[g] = scb[(32 * g + r32) * SCW + cw] >> (8 * h);
-  i8v bop[2][2];
+  for (int f = 0; f < 4; ++f) af[f] = read_afrag<0>(nxt, f, r32, h);
+  if (run) {
 #pragma unroll
-  for (int g = 0; g < 2; ++g) b_operands(b.q[g][0], b.q[g][1], bop[g][0], bop[g][1]);
+    for (int f = 0; f < 4; ++f)
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+      for (int g = 0; g < 4; ++g)
+        acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af1[f], bop[g][1], acc[f][g], 2, 4, 0,
+                                                                     (int)(sa[f] >> 16), 0, (int)(sb[g] >> 16));
+  }
+}
+
+// All K of one tile.  B chunk c+1 is loaded while chunk c is multiplied (two
+// register sets, so the loop runs in pairs of chunks), A chunk c+2 is loaded
+// into registers at the start of chunk c and stored into its LDS stage at the
+// end.  Loads past the window's last chunk re-read it, so no load sits behind
+// a branch.  tables(cw0) issues and stores the scale tables of a window; the
+// barrier after the first A stages makes them visible.
+template <typename Tables>
+__device__ __forceinline__ void tile_k_loop(TileSmem& sm, f16v (&acc)[4][4], const ASrc& as, const BSrc& bs,
+                                            int nch, int tid, Tables tables) {
+  const int lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
+  for (int cw0 = 0; cw0 < nch; cw0 += TWIN) {
+    const int last = min(cw0 + TWIN, nch) - 1;
+    if (cw0 > 0) __syncthreads();  // every wavefront is done with the previous window
+    AStage a0, a1;
+    as.load(cw0, a0);
+    as.load(min(cw0 + 1, last), a1);
+    BChunk b0, b1;
+    bs.load(cw0, b0);
+    tables(cw0);
+    store_a(sm.k.a[0], a0, tid);
+    store_a(sm.k.a[1], a1, tid);
+    __syncthreads();
+    i8v af[4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      // dwords 6s..6s+5 of the lane's 48 B are its block at K-step s
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(av[f]) + 6 * s;
-      const i8v a = i8v{(int)w[0], (int)w[1], (int)w[2], (int)w[3], (int)w[4], (int)w[5], 0, 0};
-      const int sa = (int)(asw[f] >> (16 * s));  // low byte: block 2s+h
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const i8v bb = bop[g][s];
-        const int sb = (int)(bsw[g] >> (16 * s));
-        acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bb, acc[f][g], 2, 4, 0, sa, 0, sb);
+    for (int f = 0; f < 4; ++f) af[f] = read_afrag<0>(sm.k.a[0], f, r32, h);
+    int s0 = 0;  // LDS stage of chunk c
+    for (int c = cw0; c <= last; c += 2) {
+      const int s1 = s0 == 2 ? 0 : s0 + 1, s2 = s1 == 2 ? 0 : s1 + 1;
+      // The loads of each step are pinned ahead of its MFMAs (sched_barrier):
+      // left to itself the scheduler sinks them next to their first use.
+      {  // chunk c (always present)
+        AStage an;
+        as.load(min(c + 2, last), an);
+        bs.load(min(c + 1, last), b1);
+        __builtin_amdgcn_sched_barrier(0);
+        tile_chunk(sm, sm.k.a[s0], sm.k.a[s1], b0, af, acc, c - cw0, wid, r32, h, true);
+        store_a(sm.k.a[s2], an, tid);
+        __syncthreads();
       }
+      {  // chunk c + 1 (past the last chunk of an odd window: loads and stores only)
+        AStage an;
+        as.load(min(c + 3, last), an);
+        bs.load(min(c + 2, last), b0);
+        __builtin_amdgcn_sched_barrier(0);
+        tile_chunk(sm, sm.k.a[s1], sm.k.a[s2], b1, af, acc, c + 1 - cw0, wid, r32, h, c + 1 <= last);
+        store_a(sm.k.a[s0], an, tid);
+        __syncthreads();
+      }
+      s0 = s2;
     }
   }
 }
 
-// The K loop over all chunks of one tile.  A ring of PF register sets keeps
-// the loads of chunks c+1..c+PF-1 in flight while chunk c is multiplied (the
-// gathered activation rows come from the last-level cache, a long round
-// trip); A chunk c+1 moves from its registers to LDS at the end of chunk c.
-// The loop runs in rounds of PF steps; steps past the last chunk multiply
-// nothing, loads past it re-read it and stores past it write a stage nothing
-// reads again, so no load or store of the loop sits behind a branch.
-constexpr int PF = 4;
-
-struct ChunkRegs {
-  ARegs a;
-  BRegs b;
-};
-
-template <typename TS, typename Tables>
-__device__ __forceinline__ void gemm_k_loop(GemmSmem& sm, f16v (&acc)[4][2], const ASrc& as, const BSrc& bs,
-                                            int K, int tid, int lane, Tables tables) {
-  constexpr int WIN = TS::kWin;
-  const int nchunks = K / KC, wid = tid >> 6;
-  for (int cw0 = 0; cw0 < nchunks; cw0 += WIN) {
-    const int last = min(cw0 + WIN, nchunks) - 1;
-    TS ts;
-    tables(cw0, ts);
-    ChunkRegs r[PF];
-#pragma unroll
-    for (int j = 0; j < PF - 1; ++j) {
-      as.load(min(cw0 + j, last), r[j].a);
-      bs.load(min(cw0 + j, last), r[j].b);
-    }
-    // the tables and A chunk 0, made visible by the barrier below
-    ts.a.store(sm.sca, tid);
-    ts.b[0].store(sm.scb[wid], lane);
-    ts.b[1].store(sm.scb[wid] + 32 * SCW, lane);
-    store_a(sm.a[0], r[0].a, tid);
-    __syncthreads();
-    for (int c0 = cw0; c0 <= last; c0 += PF) {
-#pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        const int c = c0 + j;
-        ChunkRegs& ahead = r[(j + PF - 1) % PF];
-        as.load(min(c + PF - 1, last), ahead.a);
-        bs.load(min(c + PF - 1, last), ahead.b);
-        mma_chunk(sm.a[(c - cw0) & 1], r[j].b, sm.sca, sm.scb[wid], c - cw0, acc, c > last ? 0 : 2, lane);
-        store_a(sm.a[(c - cw0 + 1) & 1], r[(j + 1) % PF].a, tid);
-        __syncthreads();
-      }
-    }
-  }
+// SwiGLU of the GEMM epilogues: silu(g) = g / (1 + 2^(-g log2 e)) on the
+// hardware exp2 and reciprocal (about one ulp each; h then goes to MXFP6, whose
+// step is 2^-3 of the block's scale).  Saturates to 0 for g below about -88 and
+// to g * u above about +17, like the exact form.
+__device__ __forceinline__ float swiglu_fast(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * u * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // ---- streaming path for small buckets ----------------------------------------------
@@ -698,7 +737,7 @@ __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = (i >> 2) * 8 + h * 4 + (i & 3);
-      st[row * 33 + r32] = swiglu_f32(acc[0][i], acc[1][i]);
+      st[row * 33 + r32] = swiglu_fast(acc[0][i], acc[1][i]);
     }
     __builtin_amdgcn_wave_barrier();
     if (h == 0 && r32 < bk.cnt) {
@@ -771,15 +810,18 @@ __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
 
 // ---- P1: gate/up GEMM, SwiGLU and MXFP6 of h -----------------------------------------
 //
-// Wavefront w's fragments are gate rows j0+32w.. and the up rows with the same
-// index, so h = silu(g)*u is formed in its registers; its 32 h columns are
-// exactly one MXFP6 block per row.
+// Wavefront w of a tile owns h columns j0 + 64 w .. j0 + 64 w + 63: its four
+// fragments are those gate rows (two) and the same up rows (two), so
+// h = silu(g) * u is formed in its registers.  The tile's 256 h columns are
+// staged in LDS and quantised per (row, 32-column block) into hq/hs.  In a
+// last tile narrower than 256 columns (inter % 256 == 128) wavefronts 2 and 3
+// load zeros and store nothing.
 
-__global__ __launch_bounds__(kPT, 1) void gateup_mfma_kernel(
+__global__ __launch_bounds__(kPT, 1) void gateup_tile_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, uint32_t xq_bytes, uint32_t xs_bytes, int P,
-    ExpertStore w, const int32_t* __restrict__ sorted_pair, const TileDesc* __restrict__ tiles,
-    const int32_t* __restrict__ counts, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
-  __shared__ GemmSmem sm;
+    ExpertStore w, const TileDesc* __restrict__ tiles, const int32_t* __restrict__ counts,
+    uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
+  __shared__ TileSmem sm;
   const int H = w.H, I = w.I, NBH = H / 32, NBI = I / 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
   const uint32_t wrow = (uint32_t)H / 2u;
@@ -790,52 +832,64 @@ __global__ __launch_bounds__(kPT, 1) void gateup_mfma_kernel(
     if (d.slot < 0) continue;  // no stored expert: the down GEMM writes its rows as zeros
     __syncthreads();           // the previous tile's epilogue is done with the LDS
     const int j0 = d.ntile * GU_N;
+    const int hc0 = j0 + 64 * wid;           // this wavefront's first h column
+    const bool live = hc0 < I;               // inter % 256 == 128: the last tile is half wide
     ASrc as;
-    as.rc = make_rsrc(xq, xq_bytes);
-    a_offsets(as, tid, d.row0, P);
+    as.init(xq, xq_bytes, tid, d.row0, P);
     BSrc bs;
-    {
-      // wavefront wid: gate rows j0+32*wid.. (fragment 0) and the same up rows (fragment 1)
-      const uint32_t jr = (uint32_t)(j0 + 32 * wid + r32);
-      bs.rc[0] = make_rsrc(w.wg + (size_t)d.slot * mat, (uint32_t)mat);
-      bs.rc[1] = make_rsrc(w.wu + (size_t)d.slot * mat, (uint32_t)mat);
-      const uint32_t jl = (uint32_t)(j0 + 32 * wid + (lane & 15));
-      bs.vc[0] = bs.vc[1] = jl * wrow + 16u * (uint32_t)(lane >> 4);
-      bs.half = 16u * wrow;
+    const rsrc_t rg = make_rsrc(w.wg + (size_t)d.slot * mat, (uint32_t)mat);
+    const rsrc_t ru = make_rsrc(w.wu + (size_t)d.slot * mat, (uint32_t)mat);
+    const uint32_t lrow = (uint32_t)(lane & 15) * wrow + 16u * (uint32_t)(lane >> 4);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bs.rc[g] = g < 2 ? rg : ru;
+      bs.vc[g] = live ? (uint32_t)(hc0 + 32 * (g & 1)) * wrow + lrow : kOob;
     }
+    bs.half = 16u * wrow;
     const rsrc_t xsr = make_rsrc(xs, xs_bytes);
     const rsrc_t sgr = make_rsrc(w.sg + (size_t)d.slot * smat, (uint32_t)smat);
     const rsrc_t sur = make_rsrc(w.su + (size_t)d.slot * smat, (uint32_t)smat);
-    const uint32_t jr0 = (uint32_t)(j0 + 32 * wid);
-    using TS = TileScales<40, ScaleCols<BM, kPT, 40, SCW>>;
-    auto tables = [&](int cw0, TS& ts) {
-      ts.a.issue(xsr, cw0, tid, d.row0, d.mrows, P);
-      ts.b[0].issue(sgr, cw0, lane, [&](int r) { return (jr0 + (uint32_t)r) * NBH; });
-      ts.b[1].issue(sur, cw0, lane, [&](int r) { return (jr0 + (uint32_t)r) * NBH; });
+    auto tables = [&](int cw0) {
+      const int t = opaque(tid), l = t & 63;
+      // table rows 0-63: gate rows hc0.., 64-127: the same up rows
+      const auto off = [&](int r) { return live ? (uint32_t)(hc0 + (r & 63)) * (uint32_t)NBH : kOob; };
+      ScaleCols<BM, kPT, TWIN, TSW> ta;
+      BTable<0> t0;
+      BTable<1> t1;
+      ta.issue(xsr, cw0, t, d.row0, d.mrows, P);
+      t0.issue([&](int) { return sgr; }, off, cw0, l);
+      ta.store(sm.k.sca, t);
+      t0.store(sm.k.scb[wid], l);
+      t1.issue([&](int) { return sur; }, off, cw0, l);
+      t1.store(sm.k.scb[wid], l);
     };
-    f16v acc[4][2];
+    f16v acc[4][4];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
-      for (int g = 0; g < 2; ++g) acc[f][g] = f16v{};
-    gemm_k_loop<TS>(sm, acc, as, bs, H, tid, lane, tables);
-    // h = silu(g) * u into the staging buffer (the K loop ended on a barrier)
-    const int wcol = 32 * wid + r32;
+      for (int g = 0; g < 4; ++g) acc[f][g] = f16v{};
+    tile_k_loop(sm, acc, as, bs, H / KC, tid, tables);  // ends on a barrier
+    // h = silu(g) * u into the staging buffer
+    {
+      const int t = opaque(tid), e32 = t & 31, eh = (t >> 5) & 1;
+      float* st = sm.stage + (eh * 4) * (GU_N + 1) + 64 * (t >> 6) + e32;
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+      for (int f = 0; f < 4; ++f)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 32 * f + (i >> 2) * 8 + h * 4 + (i & 3);
-        sm.stage[row * STAGE_S + wcol] = swiglu_f32(acc[f][0][i], acc[f][1][i]);
-      }
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            st[(32 * f + (r >> 2) * 8 + (r & 3)) * (GU_N + 1) + 32 * i] = swiglu_fast(acc[f][i][r], acc[f][2 + i][r]);
+    }
     __syncthreads();
     // MXFP6 of each (row, 32-block) of the tile, written in sorted-row order
-    for (int item = tid; item < BM * (GU_N / 32); item += kPT) {
+    const int nblk = min(GU_N, I - j0) / 32;
+    for (int item = opaque(tid); item < BM * (GU_N / 32); item += kPT) {
       const int row = item % BM, blk = item / BM;
-      if (row < d.mrows) {
+      if (row < d.mrows && blk < nblk) {
         float v[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = sm.stage[row * STAGE_S + 32 * blk + i];
+        for (int i = 0; i < 32; ++i) v[i] = sm.stage[row * (GU_N + 1) + 32 * blk + i];
         uint32_t pk[6], sb;
         q6_block(v, pk, sb);
         const size_t grow = (size_t)(d.row0 + row);
@@ -851,12 +905,18 @@ __global__ __launch_bounds__(kPT, 1) void gateup_mfma_kernel(
 }
 
 // ---- P2: down GEMM -> y_pair ---------------------------------------------------------
+//
+// Wavefront w of a tile owns output columns n0 + 128 w .. + 127 (four
+// fragments of W_down rows); each lane stores its accumulators straight into
+// the y_pair rows of the tile's pairs (32 consecutive columns of two rows per
+// store).  In a last tile narrower than 512 columns (hidden % 512 == 256)
+// wavefronts 2 and 3 load zeros and store nothing.
 
-__global__ __launch_bounds__(kPT, 1) void down_mfma_kernel(
+__global__ __launch_bounds__(kPT, 1) void down_tile_kernel(
     const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, uint32_t hq_bytes, uint32_t hs_bytes, int P,
     ExpertStore w, const int32_t* __restrict__ sorted_pair, const TileDesc* __restrict__ tiles,
     const int32_t* __restrict__ counts, float* __restrict__ y) {
-  __shared__ GemmSmem sm;
+  __shared__ TileSmem sm;
   const int H = w.H, I = w.I, NBI = I / 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
   const uint32_t wrow = (uint32_t)I / 2u;
@@ -868,56 +928,62 @@ __global__ __launch_bounds__(kPT, 1) void down_mfma_kernel(
     if (tid < BM) sm.rowtok[tid] = tid < d.mrows ? sorted_pair[d.row0 + tid] : -1;
     __syncthreads();
     const int n0 = d.ntile * DN_N;
+    const int nc0 = n0 + WN * wid;  // this wavefront's first output column
+    const bool live = nc0 < H;
     if (d.slot < 0) {
       for (int i = tid; i < d.mrows * DN_N; i += kPT) {
         const int row = i / DN_N, col = i % DN_N;
-        y[(size_t)sm.rowtok[row] * H + n0 + col] = 0.f;
+        if (n0 + col < H) y[(size_t)sm.rowtok[row] * H + n0 + col] = 0.f;
       }
       continue;
     }
     ASrc as;
-    as.rc = make_rsrc(hq, hq_bytes);
-    a_offsets(as, tid, d.row0, P);
+    as.init(hq, hq_bytes, tid, d.row0, P);
     BSrc bs;
-    {
-      // wavefront wid: output rows n0+64*wid+32g.. (fragment g)
-      const rsrc_t rc = make_rsrc(w.wd + (size_t)d.slot * mat, (uint32_t)mat);
-      const rsrc_t rs = make_rsrc(w.sd + (size_t)d.slot * smat, (uint32_t)smat);
+    const rsrc_t rd = make_rsrc(w.wd + (size_t)d.slot * mat, (uint32_t)mat);
+    const uint32_t lrow = (uint32_t)(lane & 15) * wrow + 16u * (uint32_t)(lane >> 4);
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const uint32_t nr = (uint32_t)(n0 + 64 * wid + 32 * g);
-        bs.rc[g] = rc;
-        bs.vc[g] = (nr + (uint32_t)(lane & 15)) * wrow + 16u * (uint32_t)(lane >> 4);
-      }
-      bs.half = 16u * wrow;
-      (void)rs;
+    for (int g = 0; g < 4; ++g) {
+      bs.rc[g] = rd;
+      bs.vc[g] = live ? (uint32_t)(nc0 + 32 * g) * wrow + lrow : kOob;
     }
+    bs.half = 16u * wrow;
     const rsrc_t hsr = make_rsrc(hs, hs_bytes);
     const rsrc_t sdr = make_rsrc(w.sd + (size_t)d.slot * smat, (uint32_t)smat);
-    const uint32_t nr0 = (uint32_t)(n0 + 64 * wid);
-    using TS = TileScales<20, ScaleRows<BM, kPT, 20, SCW>>;
-    auto tables = [&](int cw0, TS& ts) {
-      ts.a.issue(hsr, cw0, tid, [&](int r) { return r < d.mrows ? (uint32_t)(d.row0 + r) * NBI : kOob; });
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-        ts.b[g].issue(sdr, cw0, lane, [&](int r) { return (nr0 + 32u * g + (uint32_t)r) * NBI; });
+    auto tables = [&](int cw0) {
+      // A scales: hs is row-major [sorted row][I/32], so its words are read row by row
+      const int t = opaque(tid), l = t & 63;
+      const auto res = [&](int) { return sdr; };
+      const auto off = [&](int r) { return live ? (uint32_t)(nc0 + r) * (uint32_t)NBI : kOob; };
+      ScaleRows<BM, kPT, TWIN, TSW> ta;
+      BTable<0> t0;
+      BTable<1> t1;
+      ta.issue(hsr, cw0, t, [&](int r) { return r < d.mrows ? (uint32_t)(d.row0 + r) * (uint32_t)NBI : kOob; });
+      t0.issue(res, off, cw0, l);
+      ta.store(sm.k.sca, t);
+      t0.store(sm.k.scb[wid], l);
+      t1.issue(res, off, cw0, l);
+      t1.store(sm.k.scb[wid], l);
     };
-    f16v acc[4][2];
+    f16v acc[4][4];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
-      for (int g = 0; g < 2; ++g) acc[f][g] = f16v{};
-    gemm_k_loop<TS>(sm, acc, as, bs, I, tid, lane, tables);
+      for (int g = 0; g < 4; ++g) acc[f][g] = f16v{};
+    tile_k_loop(sm, acc, as, bs, I / KC, tid, tables);
+    if (live) {
+      const int t = opaque(tid), e32 = t & 31, eh = (t >> 5) & 1;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      __builtin_amdgcn_sched_barrier(0);  // one fragment's stores at a time (register pressure)
+      for (int f = 0; f < 4; ++f) {
+        __builtin_amdgcn_sched_barrier(0);  // one fragment's stores at a time (register pressure)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 32 * f + (i >> 2) * 8 + h * 4 + (i & 3);
-        if (row < d.mrows) {
-          float* yr = y + (size_t)sm.rowtok[row] * H + n0 + 64 * wid + r32;
-          yr[0] = acc[f][0][i];
-          yr[32] = acc[f][1][i];
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * f + (r >> 2) * 8 + eh * 4 + (r & 3);
+          if (row < d.mrows) {
+            float* yr = y + (size_t)sm.rowtok[row] * H + nc0 + e32;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) yr[32 * g] = acc[f][g][r];
+          }
         }
       }
     }
@@ -934,8 +1000,8 @@ size_t max_mtiles(size_t P) { return (P + BM - 1) / BM + (P < (size_t)kMaxExpert
 size_t prefill_workspace_bytes(int T, int k, int H, int I) {
   const size_t P = (size_t)T * k, nm = max_mtiles(P);
   return align256(P * H / 32 * 24) + align256(P * H / 32) + align256(P * I / 32 * 24) +
-         align256(P * I / 32) + align256(nm * (I / GU_N) * sizeof(TileDesc)) +
-         align256(nm * (H / DN_N) * sizeof(TileDesc)) + align256(kMaxExperts * sizeof(SkBucket)) + 256 +
+         align256(P * I / 32) + align256(nm * ((I + GU_N - 1) / GU_N) * sizeof(TileDesc)) +
+         align256(nm * ((H + DN_N - 1) / DN_N) * sizeof(TileDesc)) + align256(kMaxExperts * sizeof(SkBucket)) + 256 +
          align256((size_t)T * H / 32 * 24) + align256((size_t)T * H / 32);
 }
 
@@ -943,7 +1009,8 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
                           const int32_t* offsets, const int32_t* sorted_pair, float* y_pair, void* ws,
                           hipStream_t s, const uint8_t* run) {
   const int H = w.H, I = w.I;
-  if (H % DN_N != 0 || I % GU_N != 0) return hipErrorInvalidValue;
+  if (H % 256 != 0 || I % 128 != 0) return hipErrorInvalidValue;
+  const int ntw_gu = (I + GU_N - 1) / GU_N, ntw_dn = (H + DN_N - 1) / DN_N;
   const size_t P = (size_t)T * k, nm = max_mtiles(P);
   const size_t xq_b = P * H / 32 * 24, xs_b = P * H / 32;  // per sorted row (each token k times)
   const size_t hq_b = P * I / 32 * 24, hs_b = P * I / 32;
@@ -955,9 +1022,9 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
   uint8_t* hs = hq + align256(hq_b);
   TileDesc* gu = reinterpret_cast<TileDesc*>(hs + align256(hs_b));
   TileDesc* dn = reinterpret_cast<TileDesc*>(reinterpret_cast<uint8_t*>(gu) +
-                                             align256(nm * (I / GU_N) * sizeof(TileDesc)));
+                                             align256(nm * ntw_gu * sizeof(TileDesc)));
   SkBucket* sbk = reinterpret_cast<SkBucket*>(reinterpret_cast<uint8_t*>(dn) +
-                                             align256(nm * (H / DN_N) * sizeof(TileDesc)));
+                                             align256(nm * ntw_dn * sizeof(TileDesc)));
   int32_t* counts = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(sbk) +
                                                align256(kMaxExperts * sizeof(SkBucket)));
   uint8_t* xq_t = reinterpret_cast<uint8_t*>(counts) + 256;  // token-major x blocks, then their scales
@@ -970,7 +1037,7 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
                      offsets, E, sorted_pair, xq, reinterpret_cast<uint32_t*>(xs));
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(plan_kernel, dim3(kPlanGrid), dim3(kPT), 0, s, offsets, E, e2s, w.num_slots, I / GU_N, H / DN_N, run,
+  hipLaunchKernelGGL(plan_kernel, dim3(kPlanGrid), dim3(kPT), 0, s, offsets, E, e2s, w.num_slots, ntw_gu, ntw_dn, run,
                      gu, dn, sbk, counts);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -980,15 +1047,15 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
                      w, sorted_pair, sbk, counts, hq, hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(gateup_mfma_kernel, dim3(kGrid), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, (int)P, w,
-                     sorted_pair, gu, counts, hq, hs);
+  hipLaunchKernelGGL(gateup_tile_kernel, dim3(kGrid), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, (int)P, w,
+                     gu, counts, hq, hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(down_skinny_kernel, dim3(dn_grid), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, (int)P, w,
                      sorted_pair, sbk, counts, y_pair);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(down_mfma_kernel, dim3(kGrid), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, (int)P, w,
+  hipLaunchKernelGGL(down_tile_kernel, dim3(kGrid), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, (int)P, w,
                      sorted_pair, dn, counts, y_pair);
   return hipGetLastError();
 }
