@@ -163,6 +163,9 @@ __device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
+__device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
 __device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
   return make_uint2(v[0], v[1]);

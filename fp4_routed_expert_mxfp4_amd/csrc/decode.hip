@@ -362,8 +362,8 @@ __global__ __launch_bounds__(kThreads, 2) void down_fast_kernel(
 //   id.  Then gate/up batches of gateup_fast_kernel's arithmetic, dealt out
 //   interleaved over all (expert, batch) pairs, write h.
 //   Workgroup 0 also publishes the routing for K2 and the caller.
-// K2 (down + combine): one wavefront per routed expert over a slice of 24
-//   output rows (three 8-row batches of down_fast_kernel's walk); the k rows
+// K2 (down + combine): one wavefront per routed expert over a slice of 20
+//   output rows (8-row batches of down_fast_kernel's arithmetic); the k rows
 //   meet in LDS and are summed in ascending slot order exactly as
 //   combine_kernel does, plus the residual, straight into the output.
 // Per-row arithmetic is that of the separate kernels, so the result is
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 2) void down_fast_kernel(
 // ---------------------------------------------------------------------------
 
 constexpr int kFusedMaxK = 8;
-constexpr int kFusedRows = 24;
+constexpr int kFusedRows = 20;  // output rows per down workgroup: 256 workgroups at hidden 5120
 
 struct FusedRoute {
   int expert[kMaxTopK];       // bucket order: ascending expert id
@@ -557,15 +557,46 @@ __global__ __launch_bounds__(kThreads, 2) void fused_gateup_kernel(
   fused_gateup_rows<J>(fr, xs, k, w, h, blockIdx.x * kWaves + wave, gridDim.x * kWaves, lane);
 }
 
+__device__ __forceinline__ uint4 as_uint4(const uint4_t& v) { return make_uint4(v[0], v[1], v[2], v[3]); }
+
+// One 8-row batch of the down stream with range-checked loads: rows at or
+// past nvalid (and every row when on is false) read zeros at no memory cost.
+template <int M, bool TAIL>
+__device__ __forceinline__ void dn_load_rows(DownBatch<M, TAIL>& B, rsrc_t rc, rsrc_t rs, int m0, int nvalid,
+                                             bool on, int lane, uint32_t rowbytes, int NB) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool v = on && i < nvalid;
+    const uint32_t oc = v ? (uint32_t)(m0 + i) * rowbytes : kOob, os = v ? (uint32_t)((m0 + i) * NB) : kOob;
+#pragma unroll
+    for (int mm = 0; mm < M; ++mm) {
+      B.c[i][mm] = as_uint4(bload16(rc, oc + (uint32_t)(64 * mm + lane) * 16u));
+      B.s[i][mm] = bload1(rs, os + (uint32_t)(64 * mm + lane));
+    }
+  }
+  if (TAIL) {
+    const int r = lane >> 3, blk = 64 * M + (lane & 7);
+    const bool v = on && r < nvalid;
+    B.ct = as_uint4(bload16(rc, v ? (uint32_t)(m0 + r) * rowbytes + (uint32_t)blk * 16u : kOob));
+    B.st = bload1(rs, v ? (uint32_t)((m0 + r) * NB + blk) : kOob);
+  }
+}
+
+// K2: workgroup g takes output rows 20g .. 20g + 19, wavefront j the bucket j
+// (one routed expert): two full 8-row batches and the first half of a third,
+// all of whose loads are issued at once (no load waits for another), reduced
+// with down_fast_kernel's per-row arithmetic.
 template <int M, bool TAIL, bool kBf16Out>
 __global__ __launch_bounds__(kFusedMaxK * 64) void fused_down_combine_kernel(
     int k, ExpertStore w, const FusedRoute* __restrict__ pub, const float* __restrict__ h,
     const uint16_t* __restrict__ residual, void* __restrict__ out) {
   constexpr int NB = 64 * M + (TAIL ? 8 : 0);
   constexpr int MM = M > 0 ? M : 1;
+  constexpr int NBAT = (kFusedRows + 7) / 8;
   __shared__ FusedRoute fr;
-  __shared__ float ybuf[kFusedMaxK][kFusedRows];
+  __shared__ float ybuf[kFusedMaxK][8 * NBAT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = w.H, I = w.I;
   if (tid < kMaxTopK) {
     fr.expert[tid] = pub->expert[tid];
     fr.slot[tid] = pub->slot[tid];
@@ -573,41 +604,38 @@ __global__ __launch_bounds__(kFusedMaxK * 64) void fused_down_combine_kernel(
     fr.w[tid] = pub->w[tid];
   }
   __syncthreads();
-  const int H = w.H, I = w.I;
   const int m0 = blockIdx.x * kFusedRows;
-  const int nb = min(kFusedRows, H - m0) / 8;  // 8-row batches in this slice
+  const int nrows = min(kFusedRows, H - m0);
   const int slot = fr.slot[wave];
-  if (slot < 0) {
-    if (lane < kFusedRows) ybuf[wave][lane] = 0.f;
-  } else {
-    const size_t rowbytes = (size_t)16 * NB;
-    const uint8_t* dc = w.wd + (size_t)slot * H * rowbytes;
-    const uint8_t* ds = w.sd + (size_t)slot * H * NB;
-    float4_t hm[MM][8], ht[8];
-    const float* hr = h + (size_t)wave * I;
+  const bool on = slot >= 0;
+  const uint32_t rowbytes = 16u * NB;
+  const size_t s0 = (size_t)(on ? slot : 0);
+  const rsrc_t rc = make_rsrc(w.wd + s0 * H * rowbytes, (uint32_t)H * rowbytes);
+  const rsrc_t rs = make_rsrc(w.sd + s0 * H * NB, (uint32_t)(H * NB));
+  // h of this wavefront's bucket and every weight row of the slice, all in flight together
+  float4_t hm[MM][8], ht[8];
+  const float* hr = h + (size_t)wave * I;
 #pragma unroll
-    for (int mm = 0; mm < M; ++mm) {
-      const float4_t* p = reinterpret_cast<const float4_t*>(hr + (64 * mm + lane) * 32);
+  for (int mm = 0; mm < M; ++mm) {
+    const float4_t* p = reinterpret_cast<const float4_t*>(hr + (64 * mm + lane) * 32);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) hm[mm][q] = p[q];
-    }
-    if (TAIL) {
-      const float4_t* p = reinterpret_cast<const float4_t*>(hr + (64 * M + (lane & 7)) * 32);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) ht[q] = p[q];
-    }
-    DownBatch<M, TAIL> A, Bn;
-    dn_load(A, dc, ds, m0, lane, rowbytes, NB);
-    for (int bat = 0; bat < nb; bat += 2) {
-      const bool has1 = bat + 1 < nb;
-      if (has1) dn_load(Bn, dc, ds, m0 + (bat + 1) * 8, lane, rowbytes, NB);
-      dn_finish(A, hm, ht, lane, ybuf[wave], bat * 8);
-      if (bat + 2 < nb) dn_load(A, dc, ds, m0 + (bat + 2) * 8, lane, rowbytes, NB);
-      if (has1) dn_finish(Bn, hm, ht, lane, ybuf[wave], (bat + 1) * 8);
-    }
+    for (int q = 0; q < 8; ++q) hm[mm][q] = p[q];
   }
+  if (TAIL) {
+    const float4_t* p = reinterpret_cast<const float4_t*>(hr + (64 * M + (lane & 7)) * 32);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ht[q] = p[q];
+  }
+  DownBatch<M, TAIL> B[NBAT];
+#pragma unroll
+  for (int t = 0; t < NBAT; ++t) dn_load_rows(B[t], rc, rs, m0 + 8 * t, nrows - 8 * t, on, lane, rowbytes, NB);
+  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first use
+#pragma unroll
+  for (int t = 0; t < NBAT; ++t) dn_finish(B[t], hm, ht, lane, ybuf[wave], 8 * t);
+  // an expert without storage contributes zero rows (its h was never written)
+  if (!on && lane < 8 * NBAT) ybuf[wave][lane] = 0.f;
   __syncthreads();
-  if (tid < nb * 8) {
+  if (tid < nrows) {
     const int m = m0 + tid;
     float acc = 0.f;
     for (int j = 0; j < k; ++j) acc = fmaf(fr.w[j], ybuf[fr.row_of_pair[j]][tid], acc);
