@@ -57,6 +57,31 @@ def measured_traffic():
         return None
 
 
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_utilisation.md")
+PREFILL_SRC = os.path.join(ROOT, "fp4_routed_expert_mxfp4_amd", "csrc", "prefill.hip")
+
+
+def profile_fields(path: str, src: str, keys) -> dict | None:
+    """`key: value` lines of a committed profile summary, or None when the
+    summary was taken on a different kernel source."""
+    import hashlib
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines() if ":" in line and not line.startswith(" "))
+    if fields.get("source_sha256", "").strip() != sha:
+        return None
+    out = {}
+    for k in keys:
+        try:
+            out[k] = float(fields[k])
+        except (KeyError, ValueError):
+            out[k] = None
+    return out
+
+
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -66,7 +91,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=60)
     ap.add_argument("--chain-steps", type=int, default=30)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-chain", action="store_true")
@@ -74,10 +99,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-router-gate", action="store_true")
     ap.add_argument("--no-cb3", action="store_true")
+    ap.add_argument("--no-series", action="store_true",
+                    help="skip the per-replay, cache-flushed and interleaved series (for counter runs)")
     ap.add_argument("--only", choices=("decode", "prefill", "chain", "verify", "router", "cb3"), default=None,
                     help="run one section only (for profiling); prints that section's numbers")
     ap.add_argument("--calibrate", action="store_true",
-                    help="only time torch's plain copy of 4 GiB (the HBM-bytes calibration kernel)")
+                    help="only run the two HBM-bytes calibration kernels (a 4 GiB copy and a 4 GiB read)")
     return ap.parse_args()
 
 
@@ -211,6 +238,106 @@ def time_graphs(torch, graphs, steps: int, pick=lambda i, n: i % n) -> float:
     return a.elapsed_time(b) / 1e3
 
 
+FLUSH_BYTES = 512 << 20    # read before each cold replay: twice the 256 MB last-level cache
+REPLAYS = 60               # replays of each per-replay series (median and min reported)
+
+
+def provenance() -> dict:
+    """Source hash, git commit (when a checkout is present), seeds and versions.
+    Taken before the GPU is touched (the git query runs as a child process)."""
+    import hashlib
+    import platform
+    import subprocess
+    h = hashlib.sha256()
+    for d in (os.path.join("fp4_routed_expert_mxfp4_amd", "csrc"), "include", "gen"):
+        for f in sorted(os.listdir(os.path.join(ROOT, d))):
+            if f.endswith((".hip", ".cuh", ".cpp", ".h", ".py")):
+                h.update(f"{d}/{f}".encode())
+                with open(os.path.join(ROOT, d, f), "rb") as fh:
+                    h.update(fh.read())
+    sha = None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=20)
+        sha = r.stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    from gen import inputs as gi
+    built = None
+    try:
+        with open(os.path.join(ROOT, "fp4_routed_expert_mxfp4_amd", "build_info.json")) as f:
+            built = json.load(f)
+    except (OSError, ValueError):
+        pass
+    return dict(git_sha=sha, source_sha256=h.hexdigest(), libraries_built_from=built, host=platform.node(), python=platform.python_version(),
+                seeds={name: c.seed for name, c in gi.CONFIGS.items()},
+                inputs="gen/inputs.py (PCG64 host draws) + gen/splitmix.py (SplitMix64 weight codes and scales)")
+
+
+def stats_us(per_step_s: list) -> dict:
+    import statistics
+    v = sorted(x * 1e6 for x in per_step_s)
+    return dict(n=len(v), median_us=round(statistics.median(v), 3), min_us=round(v[0], 3), max_us=round(v[-1], 3),
+                mean_us=round(sum(v) / len(v), 3))
+
+
+class Clock:
+    """The shader clock while busy: a probe kernel of 256 one-wavefront
+    workgroups compares the shader cycle counter with the constant 100 MHz
+    counter over ~70 us of dependent arithmetic (no child process: the
+    program has the GPU open)."""
+
+    def __init__(self, torch, gd):
+        self.torch, self.L = torch, gd.lib()
+        self.out = torch.zeros(512, dtype=torch.int64, device="cuda")
+
+    def read(self) -> dict:
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        assert self.L.gen_clock_probe(self.out.data_ptr(), 256, 4000, stream.cuda_stream) == 0
+        torch.cuda.synchronize()
+        v = self.out.view(256, 2).cpu().tolist()
+        mhz = sorted(100.0 * c / r for c, r in v if r > 0)
+        return dict(probe_sclk_mhz_median=round(mhz[len(mhz) // 2], 1), probe_sclk_mhz_min=round(mhz[0], 1))
+
+
+def replay_series(torch, graph, steps_per_replay: int, reps: int, flush=None) -> list:
+    """Seconds per step of each of `reps` replays of `graph`, each bracketed by
+    HIP events on the replay stream; flush() runs before each replay, outside
+    the bracket."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        if flush is not None:
+            flush()
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) / 1e3 / steps_per_replay for a, b in ev]
+
+
+def interleaved(torch, arms: dict, steps_per_replay: int, rounds: int) -> dict:
+    """Replays the arms' graphs in turn (A B C A B C ...), each replay bracketed
+    by HIP events; per-step median and min of each arm."""
+    per = {k: [] for k in arms}
+    for _ in range(rounds):
+        for k, g in arms.items():
+            per[k] += replay_series(torch, g, steps_per_replay, 1)
+    return {k: stats_us(v) for k, v in per.items()}
+
+
+def make_flush(torch, gd):
+    buf = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L = gd.lib()
+
+    def flush():
+        assert L.gen_stream_read(buf.data_ptr(), FLUSH_BYTES, sink.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream) == 0
+    return flush
+
+
 def decode_section(args, torch, m, gd, gi):
     cfg = gi.CONFIGS["decode1"]
     log(f"decode1: filling {cfg.E} experts ({cfg.E * cfg.expert_bytes / 1e9:.2f} GB)")
@@ -219,6 +346,8 @@ def decode_section(args, torch, m, gd, gi):
         db.step(s)
     torch.cuda.synchronize()
     touched = db.touched()
+    clk = Clock(torch, gd)
+    clock_before = clk.read()
     # the timed steps are one HIP graph of back-to-back layer calls, as a decode
     # token runs its layers; step i uses routing i mod 64
     log("decode1: warmup")
@@ -231,23 +360,37 @@ def decode_section(args, torch, m, gd, gi):
     del timed
     per_step_bytes = [layer_bytes(cfg, touched[i % NSETS], cfg.T) for i in range(args.steps)]
     gbps = sum(per_step_bytes) / t / 1e9
-    # for comparison: each step as its own graph launch (adds the launch gap)
+    mean_bytes = sum(layer_bytes(cfg, touched[i], cfg.T) for i in range(NSETS)) / NSETS
+    series = not args.no_series
+    # per-replay series: a graph of the 64 routings back to back, each replay
+    # bracketed by its own events (median and min over the replays)
+    rep = capture_many(torch, lambda i: db.step(i % NSETS), NSETS)
+    replay_series(torch, rep, NSETS, 2)
+    replays = stats_us(replay_series(torch, rep, NSETS, REPLAYS if series else 3))
+    # cold series: one step per replay, after a 512 MiB read that evicts the
+    # last-level cache (routing i mod 64, one graph per routing)
     step_graphs = capture(torch, db.step, NSETS)
+    flush = make_flush(torch, gd)
+    cold_s = []
+    for r in range(REPLAYS if series else 3):
+        cold_s += replay_series(torch, step_graphs[r % NSETS], 1, 1, flush)
+    cold = stats_us(cold_s)
+    # for comparison: each step as its own graph launch (adds the launch gap)
     time_graphs(torch, step_graphs, 16)
     per_launch_steps = min(args.steps, 512)
     t_launch = time_graphs(torch, step_graphs, per_launch_steps) / per_launch_steps
     del step_graphs
-    # for comparison: the four separate calls, back to back in one graph
+    # the four separate calls and the four calls with the batch-invariant FFN,
+    # interleaved with the one-call layer (A B C A B C ...)
     sep_graph = capture_many(torch, lambda i: db.step_separate(i % NSETS), NSETS)
-    time_graphs(torch, [sep_graph], 2)
-    sep_reps = max(1, min(args.steps, 512) // NSETS)
-    t_sep = time_graphs(torch, [sep_graph], sep_reps) / (sep_reps * NSETS)
-    del sep_graph
-    # the same four calls with the batch-invariant decode FFN
     inv_graph = capture_many(torch, lambda i: db.step_invariant(i % NSETS), NSETS)
-    time_graphs(torch, [inv_graph], 2)
-    t_inv = time_graphs(torch, [inv_graph], sep_reps) / (sep_reps * NSETS)
-    del inv_graph
+    for g in (sep_graph, inv_graph):
+        time_graphs(torch, [g], 2)
+    ab = interleaved(torch, {"layer": rep, "separate_calls": sep_graph, "invariant_separate_calls": inv_graph},
+                     NSETS, 20 if series else 1)
+    t_sep = ab["separate_calls"]["median_us"] * 1e-6
+    t_inv = ab["invariant_separate_calls"]["median_us"] * 1e-6
+    del sep_graph, inv_graph, rep
     # the gate/up kernel alone, then the down kernel alone: one graph of 64
     # back-to-back launches over the 64 routings, replayed; HIP events on the
     # replay stream bracket the whole timed region
@@ -258,18 +401,27 @@ def decode_section(args, torch, m, gd, gi):
     t_gu = time_graphs(torch, [gu_graph], reps) / (reps * NSETS)
     time_graphs(torch, [dn_graph], 2)
     t_dn = time_graphs(torch, [dn_graph], reps) / (reps * NSETS)
+    gu_rep = stats_us(replay_series(torch, gu_graph, NSETS, REPLAYS if series else 3))
+    del gu_graph, dn_graph
+    clock_after = clk.read()
     # algorithmic bytes of each half: the k experts' weights, x or h, the logits, h, and the output
     gu_bytes = (cfg.k * (2 * cfg.I * (cfg.H // 2 + cfg.H // 32)) + cfg.H * 2 + cfg.E * 4
                 + cfg.k * cfg.I * 4)
     dn_bytes = cfg.k * (cfg.H * (cfg.I // 2 + cfg.I // 32)) + cfg.k * cfg.I * 4 + cfg.H * 2
     res = dict(seconds=t, gbps=gbps, ms_per_step=t / args.steps * 1e3, touched_mean=sum(touched) / NSETS,
                gateup_us=t_gu * 1e6, gateup_bytes=gu_bytes, down_us=t_dn * 1e6, down_bytes=dn_bytes,
-               separate_us=t_sep * 1e6, invariant_us=t_inv * 1e6, graph_per_step_us=t_launch * 1e6, db=db)
-    log(f"decode1: {res['ms_per_step'] * 1e3:.1f} us/step, {gbps:.0f} GB/s (separate calls: {t_sep * 1e6:.1f} us; "
-        f"separate calls, batch-invariant FFN: {t_inv * 1e6:.1f} us; "
-        f"one graph launch per step: {t_launch * 1e6:.1f} us); "
-        f"route+gate/up {t_gu * 1e6:.1f} us ({gu_bytes / t_gu / 1e9:.0f} GB/s), down+combine {t_dn * 1e6:.1f} us "
-        f"({dn_bytes / t_dn / 1e9:.0f} GB/s)")
+               separate_us=t_sep * 1e6, invariant_us=t_inv * 1e6, graph_per_step_us=t_launch * 1e6,
+               replays=dict(replays, GBps_at_median=round(mean_bytes / (replays["median_us"] * 1e-6) / 1e9, 1)),
+               cold=dict(cold, GBps_at_median=round(mean_bytes / (cold["median_us"] * 1e-6) / 1e9, 1),
+                         flush_bytes=FLUSH_BYTES),
+               interleaved=ab, gateup_replays=gu_rep, clocks=dict(before=clock_before, after=clock_after), db=db)
+    log(f"decode1: {res['ms_per_step'] * 1e3:.1f} us/step, {gbps:.0f} GB/s; per replay of 64 steps median "
+        f"{replays['median_us']:.1f} min {replays['min_us']:.1f} us/step; cold (LLC flushed) median "
+        f"{cold['median_us']:.1f} us; interleaved medians: layer {ab['layer']['median_us']:.1f}, separate calls "
+        f"{t_sep * 1e6:.1f}, batch-invariant separate calls {t_inv * 1e6:.1f} us; one graph launch per step "
+        f"{t_launch * 1e6:.1f} us; route+gate/up {t_gu * 1e6:.1f} us ({gu_bytes / t_gu / 1e9:.0f} GB/s), "
+        f"down+combine {t_dn * 1e6:.1f} us ({dn_bytes / t_dn / 1e9:.0f} GB/s); sclk "
+        f"{clock_before['probe_sclk_mhz_median']:.0f} -> {clock_after['probe_sclk_mhz_median']:.0f} MHz")
     return res
 
 
@@ -315,9 +467,15 @@ def verify_section(args, torch, m, gd, gi):
     torch.cuda.synchronize()
     touched = db.touched()
     steps = max(NSETS, min(args.steps, 512))
+    clk = Clock(torch, gd)
+    clock_before = clk.read()
     g = capture_many(torch, lambda i: db.step(i % NSETS), steps)  # back to back, as in decode1
     time_graphs(torch, [g], 1)
     t = time_graphs(torch, [g], 1)
+    del g
+    g = capture_many(torch, lambda i: db.step(i % NSETS), NSETS)
+    replay_series(torch, g, NSETS, 2)
+    replays = stats_us(replay_series(torch, g, NSETS, REPLAYS if not args.no_series else 3))
     del g
     nbytes = sum(layer_bytes(cfg, touched[i % NSETS], cfg.T) for i in range(steps))
     per = t / steps
@@ -329,10 +487,13 @@ def verify_section(args, torch, m, gd, gi):
         time_graphs(torch, [g], 1)
         extra[key] = time_graphs(torch, [g], 2) / (2 * NSETS) * 1e6
         del g
+    clock_after = clk.read()
     log(f"verify16: separate calls {extra['separate_calls_us_per_step']:.1f} us/step, expert FFN in two waves "
-        f"{extra['two_wave_us_per_step']:.1f} us/step (same bytes)")
+        f"{extra['two_wave_us_per_step']:.1f} us/step (same bytes); per replay of 64 steps median "
+        f"{replays['median_us']:.1f} min {replays['min_us']:.1f} us/step")
     return dict(us_per_step=per * 1e6, tokens_per_s=cfg.T / per, gbps=nbytes / t / 1e9,
-                frac_of_peak_hbm=nbytes / t / PEAK_HBM, experts_touched_mean=sum(touched) / NSETS, **extra)
+                frac_of_peak_hbm=nbytes / t / PEAK_HBM, experts_touched_mean=sum(touched) / NSETS, **extra,
+                replays=replays, clocks=dict(before=clock_before, after=clock_after))
 
 
 def read_ceiling(torch, gd) -> dict:
@@ -395,21 +556,37 @@ def prefill_section(args, torch, m, gd, gi):
     except m.MoeError as exc:
         log(f"prefill4096 skipped: {exc}")
         return None
+    clk = Clock(torch, gd)
+    clock_before = clk.read()
     graphs = capture(torch, step, 1)
     time_graphs(torch, graphs, 3)
     t = time_graphs(torch, graphs, args.prefill_steps)
     per = t / args.prefill_steps
+    series = not args.no_series
+    replays = stats_us(replay_series(torch, graphs[0], 1, max(REPLAYS, args.prefill_steps) if series else 3))
+    flush = make_flush(torch, gd)
+    cold = stats_us(replay_series(torch, graphs[0], 1, 20 if series else 3, flush))
+    clock_after = clk.read()
+    del graphs
     flops = 6.0 * cfg.H * cfg.I * T * k
     touched = int((torch.diff(off) > 0).sum().item())
     wbytes = touched * cfg.expert_bytes
     binding = max(flops / PEAK_MXFP4, wbytes / PEAK_HBM)  # seconds at the binding roofline
     log(f"prefill4096: {per * 1e3:.3f} ms/layer, {T / per / 1e6:.2f} M tok/s, {touched} experts, "
         f"{wbytes / per / 1e9:.0f} GB/s of expert weights")
+    log(f"prefill4096: per replay median {replays['median_us'] / 1e3:.3f} min {replays['min_us'] / 1e3:.3f} ms; "
+        f"cold median {cold['median_us'] / 1e3:.3f} ms; sclk {clock_before['probe_sclk_mhz_median']:.0f} -> "
+        f"{clock_after['probe_sclk_mhz_median']:.0f} MHz")
     return dict(ms_per_layer=per * 1e3, tokens_per_s=T / per, tflops=flops / per / 1e12,
                 frac_of_mxfp4_peak=flops / per / PEAK_MXFP4,
                 experts_touched=touched, weight_bytes=wbytes,
                 weight_GBps=wbytes / per / 1e9, frac_of_peak_hbm_weights=wbytes / per / PEAK_HBM,
-                frac_of_binding_roofline=binding / per, frac_of_measured_mfma=flops / per / MFMA_MEASURED)
+                frac_of_binding_roofline=binding / per, frac_of_measured_mfma=flops / per / MFMA_MEASURED,
+                replays=replays, cold=dict(cold, flush_bytes=FLUSH_BYTES),
+                clocks=dict(before=clock_before, after=clock_after),
+                mfma_busy=profile_fields(MFMA_FILE, PREFILL_SRC, ("gateup_tile_busy", "down_tile_busy",
+                                                                  "gateup_skinny_busy", "down_skinny_busy")),
+                _dev=dict(x=x, logits=logits, ids=ids, out=out))
 
 
 def router_gate_section(args, torch, m, gd, gi):
@@ -474,10 +651,14 @@ def chain_section(args, torch, m, gd, gi):
             m.moe_decode_layer_rmsnorm(logits[layer], xs[layer], k, stores[layer], 1e-6, e2s[layer], m.MOE_OUT_BF16,
                                        xs[layer + 1], ids[layer], w[layer], ws)
 
+    clk = Clock(torch, gd)
+    clock_before = clk.read()
     graphs = capture(torch, token, 1)
     time_graphs(torch, graphs, 3)
     t = time_graphs(torch, graphs, args.chain_steps)
     per = t / args.chain_steps
+    replays = stats_us(replay_series(torch, graphs[0], 1, REPLAYS))
+    clock_after = clk.read()
     idn = ids.cpu().numpy()
     nbytes = sum(layer_bytes(cfg, len(set(idn[layer].reshape(-1).tolist())), T) + T * H * 2 * 2
                  for layer in range(cfg.layers))
@@ -485,41 +666,124 @@ def chain_section(args, torch, m, gd, gi):
     finite = bool(torch.isfinite(fin).all().item())
     log(f"chain40: {per * 1e3:.3f} ms/token, {nbytes / per / 1e9:.0f} GB/s, finite={finite}")
     return dict(ms_per_token=per * 1e3, tokens_per_s=1.0 / per, gbps=nbytes / per / 1e9,
-                frac_of_peak_hbm=nbytes / per / PEAK_HBM, bytes_per_token=nbytes, output_finite=finite)
+                frac_of_peak_hbm=nbytes / per / PEAK_HBM, bytes_per_token=nbytes, output_finite=finite,
+                replays=replays, clocks=dict(before=clock_before, after=clock_after))
 
 
-def cpu_baseline(db, gi) -> dict:
-    """The fp64 oracle on a bounded sample of the decode workload (3 routings)."""
+def cpu_baseline(db, gi, prefill=None) -> dict:
+    """The fp64 numpy oracle timed on bounded samples of the workloads, on the
+    host's cores: decode1 tokens with every BLAS thread and with one, one
+    verify16 step, two tokens of the prefill4096 chunk (MXFP6 activations, the
+    prefill reference), and one layer of the 40-layer chain.  Generating the
+    weights is outside every timed region.  For the prefill tokens the GPU
+    layer's output rows are compared with the oracle's (the prefill reference
+    and the unquantised definition)."""
     import numpy as np
     from oracle import moe_oracle as o
+    from threadpoolctl import threadpool_info, threadpool_limits
+    blas = max([p_.get("num_threads", 1) for p_ in threadpool_info()] + [1])
+    nproc = os.cpu_count() or 1
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = nproc
+    arms = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    # C1: decode1, one token per call
     cfg = db.cfg
     hw = gi.HostWeights(cfg)
-    n_tok, total_bytes, total_t = 10, 0, 0.0
-    for s in range(n_tok):
-        ids, _ = o.route(db.logit_sets[s], cfg.k)
-        for e in set(ids.reshape(-1).tolist()):
+    for name, n_tok, limit in (("decode1_all_threads", 4, None), ("decode1_one_thread", 3, 1)):
+        tot_t, tot_b = 0.0, 0
+        for i in range(n_tok):
+            s_ = 8 + i if limit else i
+            ids, _ = o.route(db.logit_sets[s_], cfg.k)
+            for e in set(ids.reshape(-1).tolist()):
+                for mat in range(3):
+                    hw.matrix(int(e), mat)
+            if limit:
+                with threadpool_limits(limit):
+                    _, dt = timed(lambda: o.moe_layer(db.hi.x_bf16, db.logit_sets[s_], hw.matrix, cfg.k, cfg.H))
+            else:
+                _, dt = timed(lambda: o.moe_layer(db.hi.x_bf16, db.logit_sets[s_], hw.matrix, cfg.k, cfg.H))
+            tot_t += dt
+            tot_b += layer_bytes(cfg, len(set(ids.reshape(-1).tolist())), cfg.T)
+            hw.drop()
+        arms[name] = dict(tokens=n_tok, seconds=round(tot_t, 2), GBps=round(tot_b / tot_t / 1e9, 4),
+                          tokens_per_s=round(n_tok / tot_t, 3), blas_threads=limit or blas,
+                          logit_sets=f"{8 if limit else 0}-{(8 if limit else 0) + n_tok - 1}")
+    # C2: one verify16 step (16 tokens, Zipf-biased routing)
+    c16 = gi.CONFIGS["verify16"]
+    hi16 = gi.host_inputs(c16)
+    lg16 = gi.logit_sets(c16, hi16.bias, 1)[0]
+    ids16, _ = o.route(lg16, c16.k)
+    hw16 = gi.HostWeights(c16)
+    for e in set(ids16.reshape(-1).tolist()):
+        for mat in range(3):
+            hw16.matrix(int(e), mat)
+    _, dt = timed(lambda: o.moe_layer(hi16.x_bf16, lg16, hw16.matrix, c16.k, c16.H))
+    hw16.drop()
+    arms["verify16_step"] = dict(tokens=c16.T, seconds=round(dt, 2), tokens_per_s=round(c16.T / dt, 3),
+                                 experts=len(set(ids16.reshape(-1).tolist())), blas_threads=blas)
+    # C4: two tokens of the prefill chunk through the prefill reference
+    if prefill is not None:
+        cp = gi.CONFIGS["prefill4096"]
+        hip_ = gi.host_inputs(cp)
+        toks = [0, cp.T // 2]
+        x_s, lg_s = hip_.x_bf16[toks], hip_.logits[0][toks]
+        idsp, _ = o.route(lg_s, cp.k)
+        hwp = gi.HostWeights(cp)
+        for e in set(idsp.reshape(-1).tolist()):
             for mat in range(3):
-                hw.matrix(int(e), mat)      # generate the inputs outside the timed region
-        t0 = time.perf_counter()
-        o.moe_layer(db.hi.x_bf16, db.logit_sets[s], hw.matrix, cfg.k, cfg.H)
-        total_t += time.perf_counter() - t0
-        total_bytes += layer_bytes(cfg, len(set(ids.reshape(-1).tolist())), cfg.T)
-        hw.drop()
-    log(f"cpu oracle: {total_t:.1f} s for {n_tok} decode tokens")
-    return dict(value=total_bytes / total_t / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
-                sample=f"{n_tok} single-token decode layers of the same workload (logit sets 0-{n_tok - 1}), "
-                       f"fp64 numpy oracle, weight generation excluded; {total_t:.1f} s",
-                tokens_per_s=n_tok / total_t)
+                hwp.matrix(int(e), mat)
+        ref, dt = timed(lambda: o.moe_layer(x_s, lg_s, hwp.matrix, cp.k, cp.H, mode="a6"))
+        ref16 = o.moe_layer(x_s, lg_s, hwp.matrix, cp.k, cp.H, mode="a16")
+        hwp.drop()
+        dev = prefill["_dev"]
+        gpu_ids = dev["ids"][toks].cpu().numpy()
+        gpu_out = dev["out"][toks].float().cpu().numpy().astype(np.float64)  # bf16 -> fp32 is exact
+        scale = np.max(np.abs(ref["out"]))
+        arms["prefill4096_sample"] = dict(
+            tokens=len(toks), token_ids=toks, seconds=round(dt, 2), tokens_per_s=round(len(toks) / dt, 3),
+            blas_threads=blas, gpu_ids_equal=bool(np.array_equal(gpu_ids, ref["ids"])),
+            gpu_out_rel_vs_prefill_reference=float(np.max(np.abs(gpu_out - ref["out"])) / scale),
+            gpu_out_rel_vs_unquantised=float(np.max(np.abs(gpu_out - ref16["out"])) / np.max(np.abs(ref16["out"]))))
+    # C5: the first layer of the 40-layer chain (154 of 384 experts resident)
+    c40 = gi.CONFIGS["chain40"]
+    hi40 = gi.host_inputs(c40)
+    hw40 = gi.HostWeights(c40, 0)
+    e2s = hi40.expert_to_slot[0]
+    ids40, _ = o.route(hi40.logits[0], c40.k, e2s)
+    for e in set(ids40.reshape(-1).tolist()):
+        if e2s[e] >= 0:
+            for mat in range(3):
+                hw40.matrix(int(e), mat)
+    _, dt = timed(lambda: o.chain_layer(hi40.x_bf16, hi40.logits[0], hw40.matrix, c40.k, c40.H, e2s))
+    hw40.drop()
+    arms["chain40_one_layer"] = dict(layers=1, seconds=round(dt, 2), blas_threads=blas,
+                                     ms_per_token_40_layers=round(40 * dt * 1e3, 1))
+    head = arms["decode1_all_threads"]
+    total = sum(a_["seconds"] for a_ in arms.values())
+    log(f"cpu oracle: {total:.1f} s over {len(arms)} arms; decode1 {head['tokens_per_s']:.2f} tok/s "
+        f"({head['GBps']:.3f} GB/s), one thread {arms['decode1_one_thread']['tokens_per_s']:.2f} tok/s")
+    return dict(value=head["GBps"], unit="GB/s", cores=int(blas), kind="oracle",
+                sample=f"decode1: {head['tokens']} single-token layers (logit sets {head['logit_sets']}) of the "
+                       f"same workload, fp64 numpy oracle, weight generation excluded; numpy's elementwise work "
+                       f"runs on one thread, only the matrix products use the {blas} BLAS threads",
+                nproc=nproc, affinity_cpus=affinity, tokens_per_s=head["tokens_per_s"], arms=arms,
+                seconds_total=round(total, 1))
 
 
-def calibrate(torch) -> dict:
-    """Plain device copy of 4 GiB (torch's copy kernel): a measured streaming
-    ceiling and the known-size kernel the HBM byte counters are scaled by."""
+def calibrate(torch, gd) -> dict:
+    """Two kernels of known traffic that the HBM byte counters are scaled by:
+    a plain device copy of 4 GiB (torch's copy kernel: 4 GiB read and 4 GiB
+    written) and the streaming-read probe over 4 GiB (4 GiB read, nothing
+    written).  Both are also measured streaming ceilings."""
+    probe = read_ceiling(torch, gd)
     n = 4 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     b = torch.empty_like(a)
@@ -534,7 +798,9 @@ def calibrate(torch) -> dict:
     e1.record()
     torch.cuda.synchronize()
     t = e0.elapsed_time(e1) / 1e3 / reps
-    res = dict(bytes_read=n, bytes_written=n, us=t * 1e6, copy_GBps=2 * n / t / 1e9)
+    res = dict(copy=dict(bytes_read=n, bytes_written=n, us=t * 1e6, copy_GBps=2 * n / t / 1e9),
+               read_probe=dict(bytes_read=probe["bytes"], bytes_written=0, us=probe["us"],
+                               read_GBps=probe["read_GBps"]))
     log(f"calibration copy: {t * 1e6:.0f} us per 4 GiB copy, {2 * n / t / 1e9:.0f} GB/s read+write")
     return res
 
@@ -546,14 +812,16 @@ def main() -> int:
         print("bench.py: only --gpus 1 is supported (the path is built and measured on one GPU)",
               file=sys.stderr)
         return 2
+    prov = provenance()  # before the GPU is touched: the git query is a child process
     import torch
     import fp4_routed_expert_mxfp4_amd as m
     from gen import device as gd
     from gen import inputs as gi
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    prov.update(torch=torch.__version__, hip=torch.version.hip, device=torch.cuda.get_device_name(0))
     m.lib()
     if args.calibrate:
-        print(json.dumps({"calibration": calibrate(torch)}), flush=True)
+        print(json.dumps({"calibration": calibrate(torch, gd)}), flush=True)
         return 0
 
     if args.only:
@@ -562,6 +830,7 @@ def main() -> int:
         res = fn(args, torch, m, gd, gi)
         if isinstance(res, dict):
             res.pop("db", None)
+            res.pop("_dev", None)
         print(json.dumps({"section": args.only, "result": res}), flush=True)
         return 0
 
@@ -573,7 +842,9 @@ def main() -> int:
     chain = None if args.no_chain else chain_section(args, torch, m, gd, gi)
     router = None if args.no_router_gate else router_gate_section(args, torch, m, gd, gi)
     cb3 = None if args.no_cb3 else cb3_section(args, torch, m, gd, gi, dec["db"])
-    cpu = None if args.no_cpu_baseline else cpu_baseline(dec["db"], gi)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(dec["db"], gi, prefill)
+    if prefill is not None:
+        prefill.pop("_dev", None)
 
     gu_achieved = dec["gateup_bytes"] / (dec["gateup_us"] * 1e-6)
     result = {
@@ -587,13 +858,19 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "mxfp4 (e2m1 codes, ue8m0 per 32) x bf16, fp32 accumulation",
         "data": "synthetic",
         "config": {"workload": "decode1: single-layer MoE FFN decode, batch 1, hidden 5120, expert width 2304, "
                                "384 MXFP4 experts resident, top-8, 64 rotating routings",
                    "hidden": cfg.H, "expert_width": cfg.I, "experts": cfg.E, "top_k": cfg.k, "tokens": cfg.T,
                    "weights": "e2m1 + UE8M0/32", "activations": "bf16"},
         "frac_of_peak_hbm": round(dec["gbps"] * 1e9 / PEAK_HBM, 4),
+        "timing": {"value": f"one graph of {args.steps} back-to-back steps after {args.warmup} untimed ones, HIP "
+                            "events on the replay stream",
+                   "replays": dec["replays"], "cold_llc_flushed": dec["cold"],
+                   "interleaved_medians": dec["interleaved"], "gateup_replays": dec["gateup_replays"],
+                   "clocks": dec["clocks"]},
+        "provenance": prov,
         "separate_calls_us_per_step": round(dec["separate_us"], 2),
         "batch_invariant_separate_calls_us_per_step": round(dec["invariant_us"], 2),
         "graph_launch_per_step_us": round(dec["graph_per_step_us"], 2),

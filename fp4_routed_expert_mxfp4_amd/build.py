@@ -23,6 +23,7 @@ ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 LIB_MOE = os.path.join(PKG, "libmoe_fp4.so")
 LIB_GEN = os.path.join(ROOT, "gen", "libmoe_gen.so")
+BUILD_INFO = os.path.join(PKG, "build_info.json")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -65,7 +66,32 @@ def build(jobs: int = 8) -> list[str]:
         list(ex.map(lambda u: _compile(*u), units))
     _link([o for s, o in units if os.path.basename(o).startswith("moe_")], LIB_MOE)
     _link([o for s, o in units if os.path.basename(o).startswith("gen_")], LIB_GEN)
+    _write_build_info(moe_srcs + gen_srcs)
     return [LIB_MOE, LIB_GEN]
+
+
+def _write_build_info(srcs: list[str]) -> None:
+    """Records what the libraries were built from (the git commit when a
+    checkout is present, and a hash of every source) beside them."""
+    import hashlib
+    import json
+    h = hashlib.sha256()
+    for s in sorted(srcs) + sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))):
+        h.update(os.path.relpath(s, ROOT).encode())
+        with open(s, "rb") as f:
+            h.update(f.read())
+    info = {"sources_sha256": h.hexdigest(), "arch": ARCH}
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=20)
+        d = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"], capture_output=True,
+                           text=True, timeout=20)
+        if r.returncode == 0:
+            info["git_head"] = r.stdout.strip()
+            info["uncommitted_changes"] = bool(d.stdout.strip())
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f, indent=1)
 
 
 if __name__ == "__main__":

@@ -2,7 +2,8 @@
 // wavefront taking 16 consecutive KiB per step with one 16-byte load per lane
 // per KiB (all 16 in flight), so that the read rate measured with it is the
 // HBM ceiling that a well-coalesced streaming kernel can reach on this GPU.
-// Measurement only: nothing of the MoE arithmetic lives here.
+// Also a clock probe (the shader clock while the GPU is busy).  Measurement
+// only: nothing of the MoE arithmetic lives here.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,9 +28,32 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u4* __restrict__
   if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads; no byte pattern used here gives this value
 }
 
+// Shader clock against the constant 100 MHz clock: every workgroup (one
+// wavefront) reads both counters, runs `iters` dependent multiply-adds and
+// reads them again; out[2b] and out[2b + 1] receive workgroup b's two deltas.
+__global__ __launch_bounds__(64) void clock_probe_kernel(uint64_t* __restrict__ out, int iters) {
+  const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  float v = (float)threadIdx.x;
+  for (int i = 0; i < iters; ++i) v = __builtin_fmaf(v, 0.999999f, 0.5f);
+  const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = c1 - c0;
+    out[2 * blockIdx.x + 1] = r1 - r0;
+  }
+  if (v == -1.0f) out[0] = 0;  // keeps the loop; v stays positive
+}
+
 }  // namespace
 
 extern "C" {
+
+// Launches the clock probe: blocks workgroups of one wavefront; out holds
+// 2 * blocks words.  0 on success, 1 on bad arguments, 2 on a launch error.
+__attribute__((visibility("default"))) int gen_clock_probe(void* out, int blocks, int iters, hipStream_t stream) {
+  if (!out || blocks <= 0 || blocks > 4096 || iters <= 0) return 1;
+  hipLaunchKernelGGL(clock_probe_kernel, dim3(blocks), dim3(64), 0, stream, (uint64_t*)out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // Reads bytes (a multiple of 16 KiB) at src (16-byte aligned) once.  sink: a
 // device word the kernel may write.  0 on success, 1 on bad arguments, 2 on a
