@@ -138,6 +138,8 @@ class DecodeBench:
         self.lws = torch.empty(m.decode_layer_workspace_bytes(T, k, E, cfg.H, cfg.I), dtype=torch.uint8,
                                device=dev)
         self.out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+        self.iws = torch.empty(m.decode_layer_invariant_workspace_bytes(T, k, E, cfg.H, cfg.I), dtype=torch.uint8,
+                               device=dev)
         # the two waves of the expert-subset runs: even expert ids, then odd ones
         even = (torch.arange(E, device=dev) % 2 == 0).to(torch.uint8)
         self.waves = (even, 1 - even)
@@ -171,6 +173,13 @@ class DecodeBench:
         m.moe_ffn_fp4_decode_invariant(self.x, c.k, c.E, self.store, None, self.off[s], self.sp[s], self.y,
                                        self.ws)
         m.moe_combine(self.y, self.w[s], None, m.MOE_OUT_BF16, self.out)
+
+    def step_invariant_layer(self, s: int) -> None:
+        """The same layer on the batch-invariant arithmetic in one call
+        (moe_decode_layer_invariant)."""
+        m, c = self.m, self.cfg
+        m.moe_decode_layer_invariant(self.logits[s], self.x, c.k, self.store, None, None, m.MOE_OUT_BF16, self.out,
+                                     self.ids[s], self.w[s], self.iws)
 
     def step_two_wave(self, s: int) -> None:
         """The same layer with the expert FFN in two waves over complementary expert
@@ -384,13 +393,15 @@ def decode_section(args, torch, m, gd, gi):
     # interleaved with the one-call layer (A B C A B C ...)
     sep_graph = capture_many(torch, lambda i: db.step_separate(i % NSETS), NSETS)
     inv_graph = capture_many(torch, lambda i: db.step_invariant(i % NSETS), NSETS)
-    for g in (sep_graph, inv_graph):
+    invl_graph = capture_many(torch, lambda i: db.step_invariant_layer(i % NSETS), NSETS)
+    for g in (sep_graph, inv_graph, invl_graph):
         time_graphs(torch, [g], 2)
-    ab = interleaved(torch, {"layer": rep, "separate_calls": sep_graph, "invariant_separate_calls": inv_graph},
-                     NSETS, 20 if series else 1)
+    ab = interleaved(torch, {"layer": rep, "separate_calls": sep_graph, "invariant_separate_calls": inv_graph,
+                             "invariant_layer": invl_graph}, NSETS, 20 if series else 1)
     t_sep = ab["separate_calls"]["median_us"] * 1e-6
     t_inv = ab["invariant_separate_calls"]["median_us"] * 1e-6
-    del sep_graph, inv_graph, rep
+    t_invl = ab["invariant_layer"]["median_us"] * 1e-6
+    del sep_graph, inv_graph, invl_graph, rep
     # the gate/up kernel alone, then the down kernel alone: one graph of 64
     # back-to-back launches over the 64 routings, replayed; HIP events on the
     # replay stream bracket the whole timed region
@@ -410,7 +421,8 @@ def decode_section(args, torch, m, gd, gi):
     dn_bytes = cfg.k * (cfg.H * (cfg.I // 2 + cfg.I // 32)) + cfg.k * cfg.I * 4 + cfg.H * 2
     res = dict(seconds=t, gbps=gbps, ms_per_step=t / args.steps * 1e3, touched_mean=sum(touched) / NSETS,
                gateup_us=t_gu * 1e6, gateup_bytes=gu_bytes, down_us=t_dn * 1e6, down_bytes=dn_bytes,
-               separate_us=t_sep * 1e6, invariant_us=t_inv * 1e6, graph_per_step_us=t_launch * 1e6,
+               separate_us=t_sep * 1e6, invariant_us=t_inv * 1e6, invariant_layer_us=t_invl * 1e6,
+               graph_per_step_us=t_launch * 1e6,
                replays=dict(replays, GBps_at_median=round(mean_bytes / (replays["median_us"] * 1e-6) / 1e9, 1)),
                cold=dict(cold, GBps_at_median=round(mean_bytes / (cold["median_us"] * 1e-6) / 1e9, 1),
                          flush_bytes=FLUSH_BYTES),
@@ -418,7 +430,8 @@ def decode_section(args, torch, m, gd, gi):
     log(f"decode1: {res['ms_per_step'] * 1e3:.1f} us/step, {gbps:.0f} GB/s; per replay of 64 steps median "
         f"{replays['median_us']:.1f} min {replays['min_us']:.1f} us/step; cold (LLC flushed) median "
         f"{cold['median_us']:.1f} us; interleaved medians: layer {ab['layer']['median_us']:.1f}, separate calls "
-        f"{t_sep * 1e6:.1f}, batch-invariant separate calls {t_inv * 1e6:.1f} us; one graph launch per step "
+        f"{t_sep * 1e6:.1f}, batch-invariant separate calls {t_inv * 1e6:.1f}, batch-invariant layer "
+        f"{t_invl * 1e6:.1f} us; one graph launch per step "
         f"{t_launch * 1e6:.1f} us; route+gate/up {t_gu * 1e6:.1f} us ({gu_bytes / t_gu / 1e9:.0f} GB/s), "
         f"down+combine {t_dn * 1e6:.1f} us ({dn_bytes / t_dn / 1e9:.0f} GB/s); sclk "
         f"{clock_before['probe_sclk_mhz_median']:.0f} -> {clock_after['probe_sclk_mhz_median']:.0f} MHz")
@@ -873,6 +886,7 @@ def main() -> int:
         "provenance": prov,
         "separate_calls_us_per_step": round(dec["separate_us"], 2),
         "batch_invariant_separate_calls_us_per_step": round(dec["invariant_us"], 2),
+        "batch_invariant_layer_us_per_step": round(dec["invariant_layer_us"], 2),
         "graph_launch_per_step_us": round(dec["graph_per_step_us"], 2),
         "roofline": {"kernel": "decode route + gate/up + SwiGLU (fused_gateup_kernel, moe_decode_layer_gateup)",
                      "bound": "hbm",

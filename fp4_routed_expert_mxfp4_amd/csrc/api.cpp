@@ -358,6 +358,41 @@ MOE_FP4_API moe_status moe_decode_layer(const float* logits, const uint16_t* x_b
                       ws_bytes, 0, stream);
 }
 
+MOE_FP4_API size_t moe_decode_layer_invariant_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t hidden,
+                                                              int32_t inter) {
+  if (T < 1 || k < 1 || E < 1 || hidden < 1 || inter < 1) return 0;
+  if (T == 1) return moe::invariant_layer_workspace_bytes(k, hidden, inter);
+  return layer_ws_layout(T, k, E, hidden, inter, nullptr).total;
+}
+
+MOE_FP4_API moe_status moe_decode_layer_invariant(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E,
+                                                  int32_t k, const int32_t* expert_to_slot, const moe_fp4_experts* w,
+                                                  const uint16_t* residual_bf16, moe_out_dtype od, void* out,
+                                                  int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                                                  hipStream_t stream) {
+  size_t need = 0;
+  const moe_status st = check_decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out,
+                                           topk_ids, topk_w, false, 0.f, &need);
+  if (st != MOE_OK || T == 0) return st;
+  need = moe_decode_layer_invariant_workspace_bytes(T, k, E, w->hidden, w->inter);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (misaligned(ws, 256)) return MOE_ERR_ALIGN;
+  const moe::ExpertStore store = to_store(w);
+  const bool bf16 = od == MOE_OUT_BF16;
+  if (T == 1)
+    return launched(moe::launch_invariant_layer(logits, x_bf16, E, k, expert_to_slot, store, residual_bf16, bf16,
+                                                out, topk_ids, topk_w, ws, stream));
+  const LayerWs l = layer_ws_layout(T, k, E, w->hidden, w->inter, ws);
+  hipError_t e = moe::launch_route(logits, T, E, k, expert_to_slot, topk_ids, topk_w, stream);
+  if (e == hipSuccess)
+    e = moe::launch_permute(topk_ids, T * k, E, l.offsets, l.sorted_pair, l.pair_to_row, l.pws, stream);
+  if (e == hipSuccess)
+    e = moe::launch_decode_mt(x_bf16, T, k, E, store, expert_to_slot, l.offsets, l.sorted_pair, l.y, l.hws, 0,
+                              stream);
+  if (e == hipSuccess) e = moe::launch_combine(l.y, topk_w, T, k, w->hidden, residual_bf16, bf16, out, stream);
+  return launched(e);
+}
+
 MOE_FP4_API moe_status moe_decode_layer_noalloc(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E,
                                                 int32_t k, const int32_t* expert_to_slot, const moe_fp4_experts* w,
                                                 const uint16_t* residual_bf16, moe_out_dtype od, void* out,

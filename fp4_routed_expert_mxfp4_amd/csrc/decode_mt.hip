@@ -40,6 +40,7 @@
 // walk the units grid-stride.
 #include "common.cuh"
 #include "kernels.h"
+#include "route_core.cuh"
 
 namespace moe {
 
@@ -364,7 +365,197 @@ __global__ __launch_bounds__(kMtThreads, 2) void down_mt_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// The batch-invariant decode layer of one token in one call: route + gate/up,
+// then down, then the fixed-order combine.  Every output is computed by the
+// arithmetic of gateup_mt_kernel and down_mt_kernel (the same K quarters,
+// chunk order and MFMA sequence, the same partial-sum order), so the token's
+// rows are bit-identical to its rows in a batch; the routing runs in every
+// workgroup of the first kernel (as the fast one-token layer does), which
+// saves the route and permute launches and the plan of the buckets.
+// ---------------------------------------------------------------------------
+
+struct InvRoute {
+  int expert[kMaxTopK];  // bucket order: ascending expert id
+  int slot[kMaxTopK];    // storage slot of bucket b's expert (-1: none)
+  int pair[kMaxTopK];    // routing slot j of bucket b (its y_pair row)
+};
+
+// Wavefront 0 routes the token (route_token) and ranks the k picks by expert
+// id, the bucket order of moe_permute; workgroup 0 publishes the routing.
+// Ends on a barrier.
+template <int NPL>
+__device__ void inv_route(const float* __restrict__ logits, int E, int k, const int32_t* __restrict__ e2s,
+                          int num_slots, InvRoute& r, InvRoute* __restrict__ pub, int32_t* __restrict__ topk_ids,
+                          float* __restrict__ topk_w) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const RoutePick pick = route_token<NPL>(logits, E, k, e2s, lane);
+    int rank = 0;
+    for (int i = 0; i < k; ++i) {
+      const int ei = __builtin_amdgcn_readlane(pick.expert, i);
+      rank += (ei < pick.expert || (ei == pick.expert && i < lane)) ? 1 : 0;
+    }
+    if (lane < k) {
+      int sl = e2s ? e2s[pick.expert] : pick.expert;
+      if (sl >= num_slots) sl = -1;
+      r.expert[rank] = pick.expert;
+      r.slot[rank] = sl;
+      r.pair[rank] = lane;
+      if (blockIdx.x == 0) {
+        topk_ids[lane] = pick.expert;
+        topk_w[lane] = pick.weight;
+        pub->expert[rank] = pick.expert;
+        pub->slot[rank] = sl;
+        pub->pair[rank] = lane;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// gateup_mt_kernel for the one routed token: unit u = (bucket u / tiles,
+// column tile u % tiles); the token is row 0 of the unit's 16-row group.
+template <int NPL>
+__global__ __launch_bounds__(kMtThreads, 2) void inv_gateup_kernel(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x, int E, int k, const int32_t* __restrict__ e2s,
+    ExpertStore w, InvRoute* __restrict__ pub, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+    uint16_t* __restrict__ hpl) {
+  __shared__ InvRoute rt;
+  __shared__ uint32_t tabs[4][64 * kMtW];
+  inv_route<NPL>(logits, E, k, e2s, w.num_slots, rt, pub, topk_ids, topk_w);
+  const int H = w.H, I = w.I, NB = H / 32, tiles = I / 32, nch = H / 128;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, q16 = lane & 15, g = lane >> 4;
+  const int cb = wid * nch / 4, ce = (wid + 1) * nch / 4;
+  const uint32_t wrow = (uint32_t)H / 2u;
+  const size_t mat = (size_t)I * wrow, smat = (size_t)I * NB, lo_plane = (size_t)k * I;
+  const int units = k * tiles;
+  uint32_t* tab = tabs[wid];
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int b = u / tiles, q = u - b * tiles;
+    const int slot = rt.slot[b];
+    if (slot < 0) continue;  // the down kernel writes zero rows
+    MtSrc<1> src;
+    src.ra = make_rsrc(x, (uint32_t)H * 2u);
+    src.va = q16 == 0 ? 64u * g : kOob;
+    src.plane = 0;
+    const rsrc_t gr = make_rsrc(w.wg + (size_t)slot * mat, (uint32_t)mat);
+    const rsrc_t ur = make_rsrc(w.wu + (size_t)slot * mat, (uint32_t)mat);
+#pragma unroll
+    for (int f = 0; f < kMtFrags; ++f) {  // fragments 0, 1: gate rows; 2, 3: the same up rows
+      src.rb[f] = f < 2 ? gr : ur;
+      src.vb[f] = (uint32_t)(32 * q + 16 * (f & 1) + q16) * wrow + 16u * (uint32_t)g;
+    }
+    const rsrc_t sgr = make_rsrc(w.sg + (size_t)slot * smat, (uint32_t)smat);
+    const rsrc_t sur = make_rsrc(w.su + (size_t)slot * smat, (uint32_t)smat);
+    auto tables = [&](int cw0, ScaleRows<32, 64, kMtWin, kMtW> (&ts)[2]) {
+      ts[0].issue(sgr, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NB; });
+      ts[1].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NB; });
+    };
+    f4v acc[kMtFrags] = {};
+    mt_k_loop<2>(src, acc, cb, ce, tab, tables);
+    __builtin_amdgcn_wave_barrier();
+    mt_part_store(reinterpret_cast<float*>(tab), acc, lane);
+    __syncthreads();
+    // wavefront f < 2: h columns 32q + 16f + q16; the token is accumulator 0 of lanes 0-15
+    if (wid < 2 && g == 0) {
+      const float gv = mt_part_sum(tabs, wid, 0, lane), uv = mt_part_sum(tabs, wid + 2, 0, lane);
+      const float hv = swiglu_f32(gv, uv);
+      const uint16_t hi = f32_to_bf16_rne(hv);
+      const size_t o = (size_t)b * I + 32 * q + 16 * wid + q16;
+      hpl[o] = hi;
+      hpl[lo_plane + o] = bf16_lo_part(hv, hi);
+    }
+    __syncthreads();  // the partials are read before the next unit's tables overwrite them
+  }
+}
+
+// down_mt_kernel for the one routed token: unit u = (bucket u / tiles, 64
+// output columns u % tiles); y_pair row = the bucket's routing slot.
+__global__ __launch_bounds__(kMtThreads, 2) void inv_down_kernel(int k, ExpertStore w,
+                                                                 const InvRoute* __restrict__ pub,
+                                                                 const uint16_t* __restrict__ hpl,
+                                                                 float* __restrict__ y) {
+  __shared__ InvRoute rt;
+  __shared__ uint32_t tabs[4][64 * kMtW];
+  if (threadIdx.x < kMaxTopK) {
+    rt.expert[threadIdx.x] = pub->expert[threadIdx.x];
+    rt.slot[threadIdx.x] = pub->slot[threadIdx.x];
+    rt.pair[threadIdx.x] = pub->pair[threadIdx.x];
+  }
+  __syncthreads();
+  const int H = w.H, I = w.I, NB = I / 32, tiles = H / 64, nch = I / 128;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, q16 = lane & 15, g = lane >> 4;
+  const int cb = wid * nch / 4, ce = (wid + 1) * nch / 4;
+  const uint32_t wrow = (uint32_t)I / 2u;
+  const size_t mat = (size_t)H * wrow, smat = (size_t)H * NB;
+  const int units = k * tiles;
+  uint32_t* tab = tabs[wid];
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int b = u / tiles, q = u - b * tiles;
+    const int slot = rt.slot[b], n0 = 64 * q;
+    float* yrow = y + (size_t)rt.pair[b] * H;
+    if (slot < 0) {  // no stored expert: its row is zero
+      if (wid == 0) yrow[n0 + lane] = 0.f;
+      continue;
+    }
+    MtSrc<2> src;
+    src.ra = make_rsrc(hpl, (uint32_t)((size_t)k * I * 4));
+    src.va = q16 == 0 ? (uint32_t)b * (uint32_t)I * 2u + 64u * g : kOob;
+    src.plane = (uint32_t)((size_t)k * I * 2);
+    const rsrc_t rc = make_rsrc(w.wd + (size_t)slot * mat, (uint32_t)mat);
+#pragma unroll
+    for (int f = 0; f < kMtFrags; ++f) {
+      src.rb[f] = rc;
+      src.vb[f] = (uint32_t)(n0 + 16 * f + q16) * wrow + 16u * (uint32_t)g;
+    }
+    const rsrc_t sdr = make_rsrc(w.sd + (size_t)slot * smat, (uint32_t)smat);
+    auto tables = [&](int cw0, ScaleRows<32, 64, kMtWin, kMtW> (&ts)[2]) {
+      ts[0].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + r) * NB; });
+      ts[1].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + 32 + r) * NB; });
+    };
+    f4v acc[kMtFrags] = {};
+    mt_k_loop<1>(src, acc, cb, ce, tab, tables);
+    __builtin_amdgcn_wave_barrier();
+    mt_part_store(reinterpret_cast<float*>(tab), acc, lane);
+    __syncthreads();
+    // wavefront f: output columns n0 + 16f + q16; the token is accumulator 0 of lanes 0-15
+    if (g == 0) yrow[n0 + 16 * wid + q16] = mt_part_sum(tabs, wid, 0, lane);
+    __syncthreads();
+  }
+}
+
 }  // namespace
+
+size_t invariant_layer_workspace_bytes(int k, int H, int I) {
+  return 256 + (((size_t)k * I * 4 + 255) & ~(size_t)255) + (size_t)k * H * 4;
+}
+
+hipError_t launch_invariant_layer(const float* logits, const uint16_t* x, int E, int k, const int32_t* e2s,
+                                  const ExpertStore& w, const uint16_t* residual, bool bf16_out, void* out,
+                                  int32_t* topk_ids, float* topk_w, void* ws, hipStream_t s) {
+  InvRoute* pub = reinterpret_cast<InvRoute*>(ws);
+  uint16_t* hpl = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(ws) + 256);
+  float* y = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + 256 +
+                                      (((size_t)k * w.I * 4 + 255) & ~(size_t)255));
+  const int npl = (E + 63) / 64;
+  const dim3 g1(min(k * (w.I / 32), kMtGridGU)), b1(kMtThreads);
+#define MOE_INV_GU(NP) \
+  hipLaunchKernelGGL(inv_gateup_kernel<NP>, g1, b1, 0, s, logits, x, E, k, e2s, w, pub, topk_ids, topk_w, hpl)
+  if (npl <= 1) MOE_INV_GU(1);
+  else if (npl <= 2) MOE_INV_GU(2);
+  else if (npl <= 4) MOE_INV_GU(4);
+  else if (npl <= 8) MOE_INV_GU(8);
+  else MOE_INV_GU(16);
+#undef MOE_INV_GU
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(inv_down_kernel, dim3(min(k * (w.H / 64), kMtGridDN)), dim3(kMtThreads), 0, s, k, w, pub, hpl,
+                     y);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_combine(y, topk_w, 1, k, w.H, residual, bf16_out, out, s);
+}
 
 hipError_t launch_decode_mt(const uint16_t* x, int T, int k, int E, const ExpertStore& w, const int32_t* e2s,
                             const int32_t* offsets, const int32_t* sorted_pair, float* y_pair, void* ws, int phase,

@@ -46,6 +46,13 @@ hipError_t launch_decode_mt(const uint16_t* x, int T, int k, int E, const Expert
                             const int32_t* offsets, const int32_t* sorted_pair, float* y_pair, void* ws, int phase,
                             hipStream_t s, const uint8_t* run = nullptr);
 
+// The batch-invariant decode layer of one token in one call (route + gate/up,
+// down, combine) on the multi-token kernels' arithmetic.
+size_t invariant_layer_workspace_bytes(int k, int H, int I);
+hipError_t launch_invariant_layer(const float* logits, const uint16_t* x, int E, int k, const int32_t* e2s,
+                                  const ExpertStore& w, const uint16_t* residual, bool bf16_out, void* out,
+                                  int32_t* topk_ids, float* topk_w, void* ws, hipStream_t s);
+
 // Fused one-token decode layer (route + gate/up, then down + combine).
 bool fused_decode_supported(int T, int k, int E, int H, int I);
 size_t fused_decode_workspace_bytes(int k, int I);

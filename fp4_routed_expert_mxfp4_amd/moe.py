@@ -25,6 +25,7 @@ EXPORTED = ("moe_route", "moe_router_logits", "moe_route_x", "moe_ffn_cb3_decode
             "moe_ffn_fp4_decode_gateup", "moe_ffn_fp4_decode_down", "moe_ffn_fp4_decode_subset",
             "moe_ffn_fp4_decode_invariant",
             "moe_decode_layer_workspace_bytes", "moe_decode_layer", "moe_decode_layer_noalloc", "moe_decode_layer_gateup",
+            "moe_decode_layer_invariant_workspace_bytes", "moe_decode_layer_invariant",
             "moe_decode_layer_down", "moe_decode_layer_rmsnorm_workspace_bytes", "moe_decode_layer_rmsnorm",
             "moe_ffn_fp4_prefill_workspace_bytes", "moe_ffn_fp4_prefill", "moe_ffn_fp4_prefill_subset", "moe_combine",
             "moe_rmsnorm_bf16", "moe_status_string")
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
                                              vp],
             "moe_decode_layer_workspace_bytes": [i32, i32, i32, i32, i32],
             "moe_decode_layer": _LAYER_ARGS,
+            "moe_decode_layer_invariant_workspace_bytes": [i32, i32, i32, i32, i32],
+            "moe_decode_layer_invariant": _LAYER_ARGS,
             "moe_decode_layer_noalloc": [vp, vp, i32, i32, i32, vp, ctypes.POINTER(CExperts), vp, ctypes.c_int, vp,
                                          vp, vp, vp],
             "moe_decode_layer_gateup": _LAYER_ARGS,
@@ -105,6 +108,7 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_fp4_decode_workspace_bytes.restype = sz
         L.moe_ffn_fp4_prefill_workspace_bytes.restype = sz
         L.moe_decode_layer_workspace_bytes.restype = sz
+        L.moe_decode_layer_invariant_workspace_bytes.restype = sz
         L.moe_decode_layer_rmsnorm_workspace_bytes.restype = sz
         L.moe_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -439,6 +443,45 @@ def moe_decode_layer(logits: torch.Tensor, x: torch.Tensor, k: int, store: Exper
     cs = store.cstruct()
     name = ("moe_decode_layer", "moe_decode_layer_gateup", "moe_decode_layer_down")[phase]
     _check(name, getattr(lib(), name)(
+        _ptr(logits), _ptr(x), T, E, k, _ptr(expert_to_slot), ctypes.byref(cs), _ptr(residual), out_dtype,
+        _ptr(out), _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(), _stream(dev)))
+    return out, topk_ids, topk_w
+
+
+def decode_layer_invariant_workspace_bytes(T: int, k: int, E: int, hidden: int, inter: int) -> int:
+    return int(lib().moe_decode_layer_invariant_workspace_bytes(T, k, E, hidden, inter))
+
+
+def moe_decode_layer_invariant(logits: torch.Tensor, x: torch.Tensor, k: int, store: ExpertStore,
+                               expert_to_slot: torch.Tensor | None = None, residual: torch.Tensor | None = None,
+                               out_dtype: int = MOE_OUT_BF16, out: torch.Tensor | None = None,
+                               topk_ids: torch.Tensor | None = None, topk_w: torch.Tensor | None = None,
+                               ws: torch.Tensor | None = None):
+    """The batch-invariant decode layer in one call; returns (out, topk_ids, topk_w)."""
+    _want(logits, (torch.float32,), "logits")
+    _want(x, _BF16, "x")
+    T, E = logits.shape
+    H = x.shape[1]
+    dev = x.device
+    if expert_to_slot is not None:
+        _want(expert_to_slot, (torch.int32,), "expert_to_slot")
+    if residual is not None:
+        _want(residual, _BF16, "residual")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16 if out_dtype == MOE_OUT_BF16 else torch.float32, device=dev)
+    _want(out, _BF16 if out_dtype == MOE_OUT_BF16 else (torch.float32,), "out")
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _want(topk_ids, (torch.int32,), "topk_ids")
+    _want(topk_w, (torch.float32,), "topk_w")
+    if ws is None:
+        ws = torch.empty(max(decode_layer_invariant_workspace_bytes(T, k, E, store.hidden, store.inter), 256),
+                         dtype=torch.uint8, device=dev)
+    _want(ws, (torch.uint8,), "ws")
+    cs = store.cstruct()
+    _check("moe_decode_layer_invariant", lib().moe_decode_layer_invariant(
         _ptr(logits), _ptr(x), T, E, k, _ptr(expert_to_slot), ctypes.byref(cs), _ptr(residual), out_dtype,
         _ptr(out), _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(), _stream(dev)))
     return out, topk_ids, topk_w

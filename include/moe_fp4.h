@@ -275,6 +275,29 @@ MOE_FP4_API moe_status moe_decode_layer(const float* logits, const uint16_t* x_b
                                         moe_out_dtype od, void* out, int32_t* topk_ids, float* topk_w,
                                         void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_decode_layer_invariant -- one whole decode layer (route, bucketing,
+ * expert FFN, combine) in one call on the batch-invariant arithmetic of
+ * moe_ffn_fp4_decode_invariant: the output and topk_ids/topk_w are
+ * bit-identical to moe_route, moe_permute, moe_ffn_fp4_decode_invariant and
+ * moe_combine, so a token's row is the same whether the token is decoded
+ * alone or inside a batch (a verify round reproducing single-token decode bit
+ * for bit: "Fast single-box DeepSeek v4.1 Flash runtime", "Dependency order
+ * and swarm split" and "Document map").  For one token the routing runs
+ * inside the first kernel and the layer is three kernels (route + gate/up,
+ * down, the fixed-order combine); larger T runs the four steps with their
+ * intermediates in the workspace.
+ *   arguments as moe_decode_layer;
+ *   ws: moe_decode_layer_invariant_workspace_bytes(T, k, E, hidden, inter)
+ *       bytes, 256-byte aligned; contents on entry do not matter
+ * 1 <= T <= MOE_DECODE_MAX_TOKENS. */
+MOE_FP4_API size_t moe_decode_layer_invariant_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t hidden,
+                                                              int32_t inter);
+MOE_FP4_API moe_status moe_decode_layer_invariant(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E,
+                                                  int32_t k, const int32_t* expert_to_slot,
+                                                  const moe_fp4_experts* w, const uint16_t* residual_bf16,
+                                                  moe_out_dtype od, void* out, int32_t* topk_ids, float* topk_w,
+                                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* moe_decode_layer_noalloc -- moe_decode_layer for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): the same arguments and the same results

@@ -310,3 +310,31 @@ def test_noalloc_layer_validation():
     assert m.decode_layer_workspace_bytes(256, 8, 384, 5120, 2304) > m.NOALLOC_SCRATCH_BYTES
     assert m.decode_layer_workspace_bytes(128, 8, 384, 5120, 2304) <= m.NOALLOC_SCRATCH_BYTES
     assert call(T=256) == m.MOE_ERR_WORKSPACE
+
+
+def test_invariant_layer_validation():
+    """moe_decode_layer_invariant validates as moe_decode_layer, with its own
+    workspace size (one token: routing record, h planes and y_pair)."""
+    m = _lib()
+    L = m.lib()
+    # routing record, h planes, y_pair
+    assert m.decode_layer_invariant_workspace_bytes(1, 8, 384, 5120, 2304) == 256 + 8 * 2304 * 4 + 8 * 5120 * 4
+    assert m.decode_layer_invariant_workspace_bytes(16, 8, 384, 5120, 2304) == \
+        m.decode_layer_workspace_bytes(16, 8, 384, 5120, 2304)
+    assert m.decode_layer_invariant_workspace_bytes(0, 8, 384, 5120, 2304) == 0
+    st = _store(m, hidden=1024, inter=256, num_slots=8)
+    need = m.decode_layer_invariant_workspace_bytes(1, 2, 8, 1024, 256)
+
+    def call(logits=FAKE, x=FAKE, T=1, E=8, k=2, store=st, od=0, out=FAKE, ids=FAKE, ws=FAKE, ws_bytes=need):
+        return L.moe_decode_layer_invariant(logits, x, T, E, k, None, ctypes.byref(store), None, od, out, ids, FAKE,
+                                            ws, ws_bytes, None)
+    assert call(logits=None) == m.MOE_ERR_NULL
+    assert call(ids=None) == m.MOE_ERR_NULL
+    assert call(k=9) == m.MOE_ERR_SHAPE
+    assert call(T=300) == m.MOE_ERR_UNSUPPORTED
+    assert call(od=5) == m.MOE_ERR_UNSUPPORTED
+    assert call(x=MIS) == m.MOE_ERR_ALIGN
+    assert call(ws=None) == m.MOE_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == m.MOE_ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == m.MOE_ERR_ALIGN
+    assert call(T=0, logits=None, x=None, out=None, ids=None, ws=None) == m.MOE_OK
