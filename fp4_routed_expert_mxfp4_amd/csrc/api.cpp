@@ -2,6 +2,7 @@
 // Every check here runs before any HIP call, so a rejected call touches
 // neither the device nor the stream.
 #include <stdint.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -11,6 +12,16 @@
 namespace {
 
 inline bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+// The int a C caller passed for an enum argument, read without loading an
+// out-of-range value as the enum type; checked against the named values.
+template <typename Enum>
+int enum_bits(const Enum* e) {
+  static_assert(sizeof(Enum) == sizeof(int), "C enums are int-sized");
+  int v;
+  memcpy(&v, e, sizeof v);
+  return v;
+}
 
 moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
@@ -77,7 +88,7 @@ bool noalloc_scratch(void** out) {
 extern "C" {
 
 MOE_FP4_API const char* moe_status_string(moe_status s) {
-  switch (s) {
+  switch (enum_bits(&s)) {
     case MOE_OK: return "ok";
     case MOE_ERR_NULL: return "a required pointer is NULL";
     case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
@@ -162,7 +173,7 @@ MOE_FP4_API moe_status moe_ffn_cb3_decode(const uint16_t* x_bf16, int32_t T, int
 }
 
 MOE_FP4_API size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E) {
-  if (T < 0 || k < 1 || E < 1) return 0;
+  if (T < 0 || k < 1 || E < 1 || (int64_t)T * k > (1 << 24)) return 0;  // moe_permute rejects more pairs
   return moe::permute_workspace_bytes(T * k, E);
 }
 
@@ -255,24 +266,33 @@ struct LayerWs {
 
 size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Offsets are computed first and turned into pointers only for a real base
+// (a size query passes none: no arithmetic on a null pointer).
 LayerWs layer_ws_layout(int T, int k, int E, int H, int I, void* base) {
   const size_t P = (size_t)T * k;
-  uint8_t* p = reinterpret_cast<uint8_t*>(base);
-  LayerWs l;
-  size_t off = 0;
-  l.offsets = reinterpret_cast<int32_t*>(p + off);
-  off += up256((size_t)(E + 1) * 4);
-  l.sorted_pair = reinterpret_cast<int32_t*>(p + off);
+  const int Pi = P > (size_t)INT32_MAX ? INT32_MAX : (int)P;
+  size_t off = up256((size_t)(E + 1) * 4);
+  const size_t o_sp = off;
   off += up256(P * 4);
-  l.pair_to_row = reinterpret_cast<int32_t*>(p + off);
+  const size_t o_p2r = off;
   off += up256(P * 4);
-  l.pws = p + off;
-  off += up256(moe::permute_workspace_bytes((int)P, E));
-  l.hws = p + off;
+  const size_t o_pws = off;
+  off += up256(moe::permute_workspace_bytes(Pi, E));
+  const size_t o_hws = off;
   off += up256(moe::decode_workspace_bytes(T, k, I));
-  l.y = reinterpret_cast<float*>(p + off);
+  const size_t o_y = off;
   off += up256(P * H * 4);
+  LayerWs l{};
   l.total = off;
+  if (base) {
+    uint8_t* p = reinterpret_cast<uint8_t*>(base);
+    l.offsets = reinterpret_cast<int32_t*>(p);
+    l.sorted_pair = reinterpret_cast<int32_t*>(p + o_sp);
+    l.pair_to_row = reinterpret_cast<int32_t*>(p + o_p2r);
+    l.pws = p + o_pws;
+    l.hws = p + o_hws;
+    l.y = reinterpret_cast<float*>(p + o_y);
+  }
   return l;
 }
 
@@ -288,7 +308,7 @@ MOE_FP4_API size_t moe_decode_layer_workspace_bytes(int32_t T, int32_t k, int32_
 // workspace bytes the call takes.  MOE_OK with *need == 0 means T == 0 (nothing to do).
 static moe_status check_decode_layer(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E, int32_t k,
                                      const int32_t* expert_to_slot, const moe_fp4_experts* w,
-                                     const uint16_t* residual_bf16, moe_out_dtype od, const void* out,
+                                     const uint16_t* residual_bf16, int od, const void* out,
                                      const int32_t* topk_ids, const float* topk_w, bool norm, float eps,
                                      size_t* need) {
   *need = 0;
@@ -312,10 +332,10 @@ static moe_status check_decode_layer(const float* logits, const uint16_t* x_bf16
 // itself the residual (residual_bf16 is then ignored).
 static moe_status decode_layer(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t E, int32_t k,
                                const int32_t* expert_to_slot, const moe_fp4_experts* w, const uint16_t* residual_bf16,
-                               moe_out_dtype od, void* out, int32_t* topk_ids, float* topk_w, void* ws,
+                               int od, void* out, int32_t* topk_ids, float* topk_w, void* ws,
                                size_t ws_bytes, int phase, hipStream_t stream, bool norm = false, float eps = 0.f) {
   size_t need = 0;
-  const moe_status st = check_decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out,
+  const moe_status st = check_decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, enum_bits(&od), out,
                                            topk_ids, topk_w, norm, eps, &need);
   if (st != MOE_OK || T == 0) return st;
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
@@ -354,7 +374,7 @@ MOE_FP4_API moe_status moe_decode_layer(const float* logits, const uint16_t* x_b
                                         const uint16_t* residual_bf16, moe_out_dtype od, void* out,
                                         int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
                                         hipStream_t stream) {
-  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out, topk_ids, topk_w, ws,
+  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, enum_bits(&od), out, topk_ids, topk_w, ws,
                       ws_bytes, 0, stream);
 }
 
@@ -371,7 +391,7 @@ MOE_FP4_API moe_status moe_decode_layer_invariant(const float* logits, const uin
                                                   int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
                                                   hipStream_t stream) {
   size_t need = 0;
-  const moe_status st = check_decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out,
+  const moe_status st = check_decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, enum_bits(&od), out,
                                            topk_ids, topk_w, false, 0.f, &need);
   if (st != MOE_OK || T == 0) return st;
   need = moe_decode_layer_invariant_workspace_bytes(T, k, E, w->hidden, w->inter);
@@ -398,13 +418,13 @@ MOE_FP4_API moe_status moe_decode_layer_noalloc(const float* logits, const uint1
                                                 const uint16_t* residual_bf16, moe_out_dtype od, void* out,
                                                 int32_t* topk_ids, float* topk_w, hipStream_t stream) {
   size_t need = 0;
-  const moe_status st = check_decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out,
+  const moe_status st = check_decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, enum_bits(&od), out,
                                            topk_ids, topk_w, false, 0.f, &need);
   if (st != MOE_OK || T == 0) return st;
   if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
   void* ws = nullptr;
   if (!noalloc_scratch(&ws)) return MOE_ERR_LAUNCH;
-  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out, topk_ids, topk_w, ws,
+  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, enum_bits(&od), out, topk_ids, topk_w, ws,
                       MOE_NOALLOC_SCRATCH_BYTES, 0, stream);
 }
 
@@ -413,7 +433,7 @@ MOE_FP4_API moe_status moe_decode_layer_gateup(const float* logits, const uint16
                                                const uint16_t* residual_bf16, moe_out_dtype od, void* out,
                                                int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
                                                hipStream_t stream) {
-  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out, topk_ids, topk_w, ws,
+  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, enum_bits(&od), out, topk_ids, topk_w, ws,
                       ws_bytes, 1, stream);
 }
 
@@ -422,7 +442,7 @@ MOE_FP4_API moe_status moe_decode_layer_down(const float* logits, const uint16_t
                                              const uint16_t* residual_bf16, moe_out_dtype od, void* out,
                                              int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
                                              hipStream_t stream) {
-  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, od, out, topk_ids, topk_w, ws,
+  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, residual_bf16, enum_bits(&od), out, topk_ids, topk_w, ws,
                       ws_bytes, 2, stream);
 }
 
@@ -437,7 +457,7 @@ MOE_FP4_API moe_status moe_decode_layer_rmsnorm(const float* logits, const uint1
                                                 const moe_fp4_experts* w, moe_out_dtype od, void* out,
                                                 int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
                                                 hipStream_t stream) {
-  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, nullptr, od, out, topk_ids, topk_w, ws, ws_bytes,
+  return decode_layer(logits, x_bf16, T, E, k, expert_to_slot, w, nullptr, enum_bits(&od), out, topk_ids, topk_w, ws, ws_bytes,
                       0, stream, true, eps);
 }
 
@@ -448,7 +468,7 @@ MOE_FP4_API size_t moe_ffn_fp4_prefill_workspace_bytes(int32_t T, int32_t k, int
 
 static moe_status prefill_call(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E, const moe_fp4_experts* w,
                                const int32_t* expert_to_slot, const int32_t* expert_offsets,
-                               const int32_t* sorted_pair, moe_act_fmt act, float* y_pair, void* ws,
+                               const int32_t* sorted_pair, int act, float* y_pair, void* ws,
                                size_t ws_bytes, hipStream_t stream, const uint8_t* run) {
   if (act != MOE_ACT_MXFP6_E2M3) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)T * k > (1 << 22)) return MOE_ERR_SHAPE;
@@ -471,7 +491,7 @@ MOE_FP4_API moe_status moe_ffn_fp4_prefill(const uint16_t* x_bf16, int32_t T, in
                                            const int32_t* expert_offsets, const int32_t* sorted_pair,
                                            moe_act_fmt act, float* y_pair, void* ws, size_t ws_bytes,
                                            hipStream_t stream) {
-  return prefill_call(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, act, y_pair, ws, ws_bytes,
+  return prefill_call(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, enum_bits(&act), y_pair, ws, ws_bytes,
                       stream, nullptr);
 }
 
@@ -481,7 +501,7 @@ MOE_FP4_API moe_status moe_ffn_fp4_prefill_subset(const uint16_t* x_bf16, int32_
                                                   const uint8_t* run_mask, moe_act_fmt act, float* y_pair, void* ws,
                                                   size_t ws_bytes, hipStream_t stream) {
   if (!run_mask && T > 0) return MOE_ERR_NULL;
-  return prefill_call(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, act, y_pair, ws, ws_bytes,
+  return prefill_call(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, enum_bits(&act), y_pair, ws, ws_bytes,
                       stream, run_mask);
 }
 
@@ -489,13 +509,14 @@ MOE_FP4_API moe_status moe_combine(const float* y_pair, const float* topk_w, int
                                    const uint16_t* residual_bf16, moe_out_dtype od, void* out,
                                    hipStream_t stream) {
   if (T < 0 || k < 1 || k > MOE_MAX_TOPK || H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
-  if (od != MOE_OUT_BF16 && od != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
+  const int odv = enum_bits(&od);
+  if (odv != MOE_OUT_BF16 && odv != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!y_pair || !topk_w || !out) return MOE_ERR_NULL;
   if (misaligned(y_pair, 16) || misaligned(out, 16) || (residual_bf16 && misaligned(residual_bf16, 16)))
     return MOE_ERR_ALIGN;
   if (T > 65535) return MOE_ERR_UNSUPPORTED;
-  return launched(moe::launch_combine(y_pair, topk_w, T, k, H, residual_bf16, od == MOE_OUT_BF16, out, stream));
+  return launched(moe::launch_combine(y_pair, topk_w, T, k, H, residual_bf16, odv == MOE_OUT_BF16, out, stream));
 }
 
 MOE_FP4_API moe_status moe_rmsnorm_bf16(const uint16_t* x_bf16, int32_t T, int32_t H, float eps,
