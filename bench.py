@@ -821,7 +821,7 @@ def calibrate(torch, gd) -> dict:
 def main() -> int:
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the path runs on one GPU; --gpus must be 1"}))
         print("bench.py: only --gpus 1 is supported (the path is built and measured on one GPU)",
               file=sys.stderr)
         return 2

@@ -93,7 +93,7 @@ MOE_FP4_API const char* moe_status_string(moe_status s) {
     case MOE_ERR_NULL: return "a required pointer is NULL";
     case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
     case MOE_ERR_ALIGN: return "a pointer misses its required alignment";
-    case MOE_ERR_UNSUPPORTED: return "shape not supported by this build";
+    case MOE_ERR_UNSUPPORTED: return "shape not supported by this library";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_LAUNCH: return "kernel launch failed";
   }

@@ -68,7 +68,7 @@ typedef enum {
   MOE_ERR_NULL = 1,         /* a required pointer is NULL                         */
   MOE_ERR_SHAPE = 2,        /* a size is out of range or inconsistent             */
   MOE_ERR_ALIGN = 3,        /* a pointer misses the alignment stated for it       */
-  MOE_ERR_UNSUPPORTED = 4,  /* a valid shape this build has no kernel for         */
+  MOE_ERR_UNSUPPORTED = 4,  /* a valid shape this library has no kernel for       */
   MOE_ERR_WORKSPACE = 5,    /* workspace missing or smaller than the query says   */
   MOE_ERR_LAUNCH = 6        /* the HIP runtime rejected a kernel launch           */
 } moe_status;
@@ -96,7 +96,7 @@ typedef struct {
   const uint8_t *w_down, *s_down;
 } moe_fp4_experts;
 
-/* Limits of this build. */
+/* Limits of this library. */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 #define MOE_DECODE_MAX_TOKENS 256
