@@ -103,6 +103,8 @@ def parse():
                     help="skip the per-replay, cache-flushed and interleaved series (for counter runs)")
     ap.add_argument("--only", choices=("decode", "prefill", "chain", "verify", "router", "cb3"), default=None,
                     help="run one section only (for profiling); prints that section's numbers")
+    ap.add_argument("--load-probe", action="store_true",
+                    help="only measure the per-CU rate of the weight-tile load shapes (gen_load_probe)")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run the two HBM-bytes calibration kernels (a 4 GiB copy and a 4 GiB read)")
     return ap.parse_args()
@@ -818,6 +820,49 @@ def calibrate(torch, gd) -> dict:
     return res
 
 
+def load_probe(torch, gd) -> dict:
+    """Per-CU rate of the two shapes a weight tile can be loaded with (8 rows x
+    128 B per load, or 32 rows x 32 B, the MFMA operand order of a 32-row
+    fragment) against where the rows live: each XCD's 32 workgroups stream
+    512-row sets of their own region of 1.3 MB (stays in the XCD's L2), 16.8 MB
+    (memory-side cache) or 134 MB (HBM), with 4 or 8 wavefronts of 32 KiB of
+    loads in flight each.  HIP events on the stream the probe runs on."""
+    regions = (512, 6554, 52429)  # rows of 2560 B per XCD
+    buf = torch.ones(8 * regions[-1] * 2560, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L = gd.lib()
+    stream = torch.cuda.current_stream()
+    iters = 400
+    rows = []
+    for rr in regions:
+        for waves in (4, 8):
+            for pat in (0, 1):
+                def run():
+                    assert L.gen_load_probe(buf.data_ptr(), rr, pat, waves, iters, sink.data_ptr(),
+                                            stream.cuda_stream) == 0
+                run()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = 3
+                e0.record(stream)
+                for _ in range(reps):
+                    run()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t = e0.elapsed_time(e1) / 1e3 / reps
+                nbytes = 256 * waves * iters * 32 * 1024
+                row = dict(region_MB_per_xcd=round(rr * 2560 / 1e6, 1), waves_per_cu=waves,
+                           shape="8 rows x 128 B" if pat == 0 else "32 rows x 32 B (MFMA order)",
+                           us=round(t * 1e6, 1), TBps=round(nbytes / t / 1e12, 2),
+                           GBps_per_cu=round(nbytes / t / 1e9 / 256, 1))
+                log(f"load probe: {row['region_MB_per_xcd']:6.1f} MB per XCD, {waves} waves/CU, "
+                    f"{row['shape']:28s} {row['GBps_per_cu']:6.1f} GB/s per CU ({row['TBps']:.2f} TB/s)")
+                rows.append(row)
+    del buf
+    torch.cuda.empty_cache()
+    return dict(rows=rows)
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -835,6 +880,9 @@ def main() -> int:
     m.lib()
     if args.calibrate:
         print(json.dumps({"calibration": calibrate(torch, gd)}), flush=True)
+        return 0
+    if args.load_probe:
+        print(json.dumps({"load_probe": load_probe(torch, gd)}), flush=True)
         return 0
 
     if args.only:

@@ -29,6 +29,8 @@ def lib() -> ctypes.CDLL:
         L.gen_stream_read.restype = ctypes.c_int
         L.gen_clock_probe.argtypes = [vp, i32, i32, vp]
         L.gen_clock_probe.restype = ctypes.c_int
+        L.gen_load_probe.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+        L.gen_load_probe.restype = ctypes.c_int
         _lib = L
     return _lib
 

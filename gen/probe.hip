@@ -2,8 +2,9 @@
 // wavefront taking 16 consecutive KiB per step with one 16-byte load per lane
 // per KiB (all 16 in flight), so that the read rate measured with it is the
 // HBM ceiling that a well-coalesced streaming kernel can reach on this GPU.
-// Also a clock probe (the shader clock while the GPU is busy).  Measurement
-// only: nothing of the MoE arithmetic lives here.
+// Also a clock probe (the shader clock while the GPU is busy) and a probe of
+// the load shapes a weight tile can be read with.  Measurement only: nothing
+// of the MoE arithmetic lives here.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,9 +44,78 @@ __global__ __launch_bounds__(64) void clock_probe_kernel(uint64_t* __restrict__ 
   if (v == -1.0f) out[0] = 0;  // keeps the loop; v stays positive
 }
 
+// Weight-tile load probe: the rate at which one CU pulls a weight tile's rows
+// (512 rows x 2560 B, a gate/up tile's rows at hidden 5120) for the two load
+// shapes a GEMM kernel can use, against where the rows live.  Workgroup b
+// runs on XCD b % 8 and streams its own 512-row sets of that XCD's region
+// (region_rows rows, so a region of 1.3 MB stays in the XCD's L2 and larger
+// ones do not), NW wavefronts each with 32 loads of 1 KiB in flight per step:
+//   PAT 0: 8 rows x 128 B per load (lane l: row l / 8, bytes 16 (l % 8) of
+//          the row's 128-B chunk pair);
+//   PAT 1: 32 rows x 32 B per load, the MFMA operand order of a 32-row
+//          fragment (lane l: row l % 32, bytes 16 (l / 32) of the K-step).
+// Every address lies inside the workgroup's region (rows wrap modulo
+// region_rows, columns stay inside a 2560-B row), and the loads go through a
+// buffer resource bounded by the region.
+template <int PAT, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void weight_load_probe_kernel(const uint8_t* __restrict__ buf,
+                                                                       uint32_t region_rows, int iters,
+                                                                       unsigned* __restrict__ sink) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint32_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const size_t region_bytes = (size_t)region_rows * 2560u;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)(buf + xcd * region_bytes), (short)0,
+                                                                     (uint32_t)region_bytes, 0x00020000);
+  unsigned acc = 0;
+  for (int it = 0; it < iters; ++it) {
+    const uint32_t c4 = (uint32_t)((it * 4) % 40);  // four 64-B chunks of K per step, 40 per row
+    const uint32_t set = slot * (uint32_t)(NW / 4) + (uint32_t)(wid >> 2) + 32u * (NW / 4) * (uint32_t)(it / 10);
+    const uint32_t row0 = (set * 512u) % region_rows;
+    u4 v[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      uint32_t row, col;
+      if (PAT == 0) {
+        row = (uint32_t)(wid & 3) * 128u + (uint32_t)(j & 15) * 8u + (uint32_t)(lane >> 3);
+        col = (c4 + 2u * (uint32_t)(j >> 4)) * 64u + (uint32_t)(lane & 7) * 16u;
+      } else {
+        const uint32_t q = (uint32_t)(j & 7);
+        row = (uint32_t)(wid & 3) * 128u + (q >> 1) * 32u + (uint32_t)(lane & 31);
+        col = (c4 + (uint32_t)(j >> 3)) * 64u + (q & 1u) * 32u + (uint32_t)(lane >> 5) * 16u;
+      }
+      v[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, ((row0 + row) % region_rows) * 2560u + col,
+                                                                           0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc += v[j].x ^ (v[j].w * (unsigned)j);
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads
+}
+
 }  // namespace
 
 extern "C" {
+
+// Launches the weight-tile load probe over 256 workgroups: buf holds 8 regions
+// of region_rows rows of 2560 B; pattern 0 or 1; waves 4 or 8 per workgroup.
+// Bytes read: 256 * waves * iters * 32 KiB.  0 on success, 1 on bad
+// arguments, 2 on a launch error.
+__attribute__((visibility("default"))) int gen_load_probe(const void* buf, int region_rows, int pattern, int waves,
+                                                          int iters, void* sink, hipStream_t stream) {
+  if (!buf || !sink || region_rows < 512 || (size_t)region_rows * 2560u >= 0x80000000u || iters <= 0 ||
+      (pattern != 0 && pattern != 1) || (waves != 4 && waves != 8))
+    return 1;
+  const dim3 g(256), b(64 * waves);
+  const uint8_t* p = (const uint8_t*)buf;
+  unsigned* k = (unsigned*)sink;
+  const uint32_t rr = (uint32_t)region_rows;
+  if (pattern == 0 && waves == 4) hipLaunchKernelGGL((weight_load_probe_kernel<0, 4>), g, b, 0, stream, p, rr, iters, k);
+  if (pattern == 0 && waves == 8) hipLaunchKernelGGL((weight_load_probe_kernel<0, 8>), g, b, 0, stream, p, rr, iters, k);
+  if (pattern == 1 && waves == 4) hipLaunchKernelGGL((weight_load_probe_kernel<1, 4>), g, b, 0, stream, p, rr, iters, k);
+  if (pattern == 1 && waves == 8) hipLaunchKernelGGL((weight_load_probe_kernel<1, 8>), g, b, 0, stream, p, rr, iters, k);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
 
 // Launches the clock probe: blocks workgroups of one wavefront; out holds
 // 2 * blocks words.  0 on success, 1 on bad arguments, 2 on a launch error.
