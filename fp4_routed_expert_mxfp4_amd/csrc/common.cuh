@@ -213,6 +213,17 @@ struct ScaleRows {
       tab[row * STRIDE + wd] = v[i];
     }
   }
+  // The same words in chunk-major order for 128 rows: word wd of row r at
+  // (32 wd + r % 32) * 4 + r / 32, so one 16-byte read returns the words of
+  // rows r32, r32 + 32, r32 + 64 and r32 + 96 for one chunk.
+  __device__ __forceinline__ void store_cf(uint32_t* tab, int t) const {
+    static_assert(ROWS == 128, "four 32-row fragments");
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = t + NT * i, row = idx / WIN, wd = idx - row * WIN;
+      tab[(32 * wd + (row & 31)) * 4 + (row >> 5)] = v[i];
+    }
+  }
 };
 
 // Compact list of the non-empty buckets, built by wavefront 0 into LDS.  With

@@ -54,19 +54,10 @@ __device__ __forceinline__ uint32_t e2m3_rne(float t) {
   return sign | code;
 }
 
-// One 32-element block -> 24 packed bytes (code i at bits 6i..6i+5) + scale byte.
-// Block exponent X = floor(log2 amax) - 2 (+1 when the significand of amax
-// exceeds 1.875), clamped to [-127, 127]; amax == 0 gives scale 0, codes 0.
-__device__ __forceinline__ void q6_block(const float (&v)[32], uint32_t (&pk)[6], uint32_t& sbyte) {
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-  for (int w = 0; w < 6; ++w) pk[w] = 0u;
-  if (amax == 0.f) {
-    sbyte = 0u;
-    return;
-  }
+// Scale of a block whose largest magnitude is amax > 0: block exponent
+// X = floor(log2 amax) - 2 (+1 when the significand of amax exceeds 1.875),
+// clamped to [-127, 127].  Returns the scale byte X + 127; inv = 2^-X.
+__device__ __forceinline__ uint32_t q6_scale(float amax, float& inv) {
   const uint32_t ab = __float_as_uint(amax);
   int E;
   uint32_t mant;
@@ -81,7 +72,24 @@ __device__ __forceinline__ void q6_block(const float (&v)[32], uint32_t (&pk)[6]
   int X = E - 2 + (mant > 0x700000u ? 1 : 0);
   X = X < -127 ? -127 : (X > 127 ? 127 : X);
   const int ie = 127 - X;  // biased exponent of 2^-X, in [0, 254]
-  const float inv = ie == 0 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)ie << 23);
+  inv = ie == 0 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)ie << 23);
+  return (uint32_t)(X + 127);
+}
+
+// One 32-element block -> 24 packed bytes (code i at bits 6i..6i+5) + scale
+// byte (q6_scale); amax == 0 gives scale 0, codes 0.
+__device__ __forceinline__ void q6_block(const float (&v)[32], uint32_t (&pk)[6], uint32_t& sbyte) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int w = 0; w < 6; ++w) pk[w] = 0u;
+  if (amax == 0.f) {
+    sbyte = 0u;
+    return;
+  }
+  float inv;
+  sbyte = q6_scale(amax, inv);
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const uint32_t c = e2m3_rne(v[i] * inv);
@@ -89,7 +97,6 @@ __device__ __forceinline__ void q6_block(const float (&v)[32], uint32_t (&pk)[6]
     pk[w] |= c << sh;
     if (sh > 26) pk[w + 1] |= c >> (32 - sh);
   }
-  sbyte = (uint32_t)(X + 127);
 }
 
 // MXFP6 rows in the layout the GEMMs read.  Row p is a sorted (bucket-order)
@@ -320,47 +327,65 @@ constexpr uint32_t kOpenRange = 0x7FFFFFF0u;  // range of the activation buffers
 
 // ---- the grouped GEMM core ---------------------------------------------------------
 //
-// A tile is BM = 128 bucket rows x 4 * WN = 512 weight rows over all of K, in
-// chunks of 128 (four 32-blocks, two K-steps of V_MFMA_SCALE_F32_32X32X64).
-// Each wavefront owns WN = 128 weight rows (four 32-row B fragments) and all
-// 128 bucket rows (four A fragments): 16 MFMAs per K-step into 16 x 16 fp32
-// accumulators per lane.  Its weight rows are used by no other wavefront, so
-// they go from memory straight into its registers; the MXFP6 activations are
-// shared by the four wavefronts and staged once per chunk through a
-// three-stage LDS ring with one barrier per chunk.  With three stages the
-// first K-step of chunk c+1 is read from LDS while chunk c is multiplied (it
-// was stored before the previous barrier), and the stage refilled during
-// chunk c (with chunk c+2) was last read before that barrier.  The scale
-// bytes of the tile are read once per window of TWIN chunks into LDS tables
-// (row-contiguous loads: a per-chunk 4-byte load from every row would cost a
-// cache-line request per row).
+// A tile is BM = 128 bucket rows x 8 * WN = 512 weight rows over all of K, in
+// chunks of 128 (four 32-blocks, two K-steps of V_MFMA_SCALE_F32_32X32X64),
+// processed a pair of chunks at a time by eight wavefronts, two per SIMD.
+// Each wavefront owns WN = 64 weight rows (two 32-row fragments) and all 128
+// bucket rows (four fragments): 8 MFMAs per K-step into 4 x 2 accumulators of
+// 16 fp32 per lane (128 AGPRs), which leaves 128 VGPRs for everything else.
+//
+// Loads.  What a load costs is the number of distinct weight rows it touches
+// and what a CU keeps in flight, not its bytes: a load over the 32 rows of an
+// MFMA operand streams at ~38 GB/s per CU even from L2, one over 8 rows x
+// 128 B at up to ~100, and once the rows live beyond L2 the rate grows with
+// the loads in flight (two wavefronts per SIMD, 8-row loads: ~80 GB/s per CU
+// against ~30 for one).  So each wavefront loads its weight rows for a chunk
+// pair as 8 rows x 128 B per load (lane l: row 8 j + l / 8, bytes 16 (l % 8)
+// of the pair), writes them into a private LDS area and reads them back in
+// operand order; the next pair's loads go out as soon as the registers are
+// written.  The weights' scale bytes of a pair (8 per row) go straight to
+// registers.  The activations are shared by the eight wavefronts: each
+// chunk's 128 records are copied from memory into one of four LDS stages by
+// the buffer unit (buffer_load ... lds, no registers; two copies of 1 KB per
+// wavefront), a pair ahead, and read from there by every
+// wavefront; their scale words come from an LDS table filled once per window
+// of TWIN chunks.  One barrier per pair: before it, each wavefront waits for
+// its own copies of the next pair; the stages they fill were last read before
+// the previous one.
+//
+// The gate/up GEMM puts the weights in the MFMA's first operand, so an
+// accumulator holds one bucket row per lane (row l % 32 of its fragment) and
+// 16 weight rows per register set, 8 (r / 4) + 4 (l / 32) + r % 4 of the
+// fragment's 32: the gate and up rows of a wavefront are the same 32 h
+// columns, half of each MXFP6 block in one lane and half in its partner l ^ 32,
+// so the epilogue needs one lane swap per block and no LDS.  The down GEMM
+// puts the activations first, so a lane holds one output column of 16 rows
+// and a store writes 32 consecutive columns of a y_pair row.
 
 // A copy of v that the compiler cannot see through: per-lane index arithmetic
 // derived from it is recomputed where it is used instead of being hoisted out
-// of the persistent tile loop (hoisted, the table and epilogue addresses of a
-// tile would hold well over a hundred registers for the whole kernel).
+// of the persistent tile loop.
 __device__ __forceinline__ int opaque(int v) {
   asm volatile("" : "+v"(v));
   return v;
 }
 
-constexpr int WN = 128;             // weight rows per wavefront (four fragments)
-constexpr int NSTAGE = 3;           // A chunks held in LDS
-constexpr int A_HS = BM * 48 + 64;  // LDS bytes per K-half region of an A chunk
-constexpr int A_STAGE = 2 * A_HS;   // LDS bytes per A chunk
-constexpr int TWIN = 40;            // scale-table window in chunks (160 blocks)
-constexpr int TSW = TWIN + 1;       // words per table row (odd: a fragment's 32 rows hit 32 banks)
+constexpr int kTilePT = 512;        // threads of a tile workgroup: eight wavefronts
+constexpr int WN = 64;              // weight rows per wavefront (two fragments)
+constexpr int A_HS = BM * 48 + 64;  // LDS bytes per K-half region of an A stage
+constexpr int A_STAGE = 2 * A_HS;   // LDS bytes per A stage (one chunk)
+constexpr int TWIN = 40;            // scale-table window in chunks (even: whole pairs)
+constexpr int B_FRAG = 32 * 128;    // LDS bytes of one fragment's pair in operand order
+constexpr int B_SCR = 2 * B_FRAG;   // a wavefront's weight reorder area
 
-struct TileSmem {
-  union {
-    struct {
-      uint8_t a[NSTAGE][A_STAGE];
-      uint32_t sca[BM * TSW];     // A scale words of the tile's rows, [row][chunk of the window]
-      uint32_t scb[4][WN * TSW];  // B scale words of each wavefront's 128 weight rows
-    } k;
-    float stage[BM * (GU_N + 1)];  // gate/up epilogue: h of the tile, fp32
-  };
-  int rowtok[BM];
+// Table word of row r (of 128) and chunk wd of the window, chunk-major: a
+// lane's words of rows r32 + 32 f, f = 0..3, are one 16-byte read.  One chunk
+// column more than the window, read (never used) after its last chunk.
+__device__ __forceinline__ int cf_index(int row, int wd) { return (32 * wd + (row & 31)) * 4 + (row >> 5); }
+constexpr int TAB_WORDS = (TWIN + 1) * 128;
+
+struct TileTables {
+  uint32_t sca[TAB_WORDS];  // activation scale words of the tile's 128 rows
 };
 
 // Words [cw0, cw0 + WIN) of ROWS table rows from a chunk-major word array
@@ -385,73 +410,53 @@ struct ScaleCols {
       tab[row * STRIDE + wd] = v[i];
     }
   }
-};
-
-// Half (rows 64 HALF .. 64 HALF + 63) of the B scale table of one wavefront:
-// words [cw0, cw0 + TWIN) of those weight rows, read as 8-byte pairs (a row's
-// scale bytes are contiguous and 8-byte aligned: K is a multiple of 256).
-// Words past a row's end belong to the next row or lie past the resource's
-// range (zeros); they are never used.  row_off(r): byte offset of table row r.
-template <int HALF>
-struct BTable {
-  static constexpr int N = (WN / 2) * TWIN / 2 / 64;  // 8-byte loads per lane
-  uint2 v[N];
-  template <typename RowRes, typename RowOff>
-  __device__ __forceinline__ void issue(RowRes res, RowOff row_off, int cw0, int lane) {
+  // The same words in the chunk-major order of the tile tables (128 rows).
+  __device__ __forceinline__ void store_cf(uint32_t* tab, int t) const {
+    static_assert(ROWS == 128, "four 32-row fragments");
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int idx = lane + 64 * i, row = 64 * HALF + idx / (TWIN / 2), pr = idx % (TWIN / 2);
-      v[i] = bload8(res(row), row_off(row) + 4u * (uint32_t)(cw0 + 2 * pr));
-    }
-  }
-  __device__ __forceinline__ void store(uint32_t* tab, int lane) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = lane + 64 * i, row = 64 * HALF + idx / (TWIN / 2), pr = idx % (TWIN / 2);
-      tab[row * TSW + 2 * pr] = v[i].x;
-      tab[row * TSW + 2 * pr + 1] = v[i].y;
+      const int idx = t + NT * i, wd = idx / ROWS, row = idx - wd * ROWS;
+      tab[cf_index(row, wd)] = v[i];
     }
   }
 };
 
-// One A chunk in registers between its loads and its LDS store: the tile's two
-// record runs (K-half 0, then 1; 128 rows x 48 B each) as 768 pieces of 16 B,
-// piece t + 256 j in thread t.  Memory and LDS hold the runs in the same order.
-struct AStage {
-  uint4_t q[3];
-};
-
-struct ASrc {
+// The activation records of a tile's chunk: two runs (K-half 0, then 1) of 128
+// rows x 48 B, 12 KB, copied into an LDS stage as 12 pieces of 1 KB (64 lanes x
+// 16 B; a 12-byte copy into LDS leaves a lane 16 bytes).  Wavefront w copies
+// pieces w and w + 8; wavefronts 4-7, which have no second piece, copy their
+// first one again (the same bytes to the same place), so every wavefront
+// issues two copies per chunk.  Memory and the stage hold the runs in the same
+// order; the stage pads each run by 64 B.  Rows past the bucket read other
+// buckets' records (their outputs are never stored and their scale words are
+// zero); past the array's end they read zeros.
+struct ACopy {
   rsrc_t rc;
-  uint32_t vc[3];    // this thread's pieces of chunk 0
+  uint32_t vc[2];    // the lane's 16 B of each piece in chunk 0
   uint32_t cstride;  // bytes per chunk: both K-halves of all P rows
-  // Rows past the bucket read other buckets' records (their outputs are never
-  // stored and their scale words are zero); past the array's end they read zeros.
-  __device__ __forceinline__ void init(const uint8_t* base, uint32_t bytes, int tid, int row0, int P) {
+  int lo[2];         // LDS offset of each piece in a stage (the same in every lane)
+  __device__ __forceinline__ void init(const uint8_t* base, uint32_t bytes, int wid, int lane, int row0, int P) {
     rc = make_rsrc(base, bytes);
     cstride = 96u * (uint32_t)P;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const int i = tid + kPT * j, h = i / (BM * 3);
-      vc[j] = ((uint32_t)h * (uint32_t)P + (uint32_t)row0) * 48u + (uint32_t)(i - h * BM * 3) * 16u;
+    for (int j = 0; j < 2; ++j) {
+      const int i = j == 1 && wid + 8 < 12 ? wid + 8 : wid, h = i / 6, q = i - 6 * h;  // 6 pieces per run
+      vc[j] = ((uint32_t)h * (uint32_t)P + (uint32_t)row0) * 48u + (uint32_t)q * 1024u + (uint32_t)lane * 16u;
+      lo[j] = h * A_HS + q * 1024;
     }
   }
-  __device__ __forceinline__ void load(int c, AStage& r) const {
+  // Chunk c into stage st; c < 0 copies nothing useful (zeros).
+  __device__ __forceinline__ void copy(uint8_t* st, int c) const {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) r.q[j] = bload16(rc, vc[j] + (uint32_t)c * cstride);
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (__attribute__((address_space(3))) void*)(st + lo[j]), 16,
+                                               c < 0 ? kOob : vc[j] + (uint32_t)c * cstride, 0, 0, 0);
   }
 };
 
-__device__ __forceinline__ void store_a(uint8_t* st, const AStage& r, int tid) {
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int i = tid + kPT * j, h = i / (BM * 3);
-    *reinterpret_cast<uint4_t*>(st + h * A_HS + (i - h * BM * 3) * 16) = r.q[j];
-  }
-}
-
-// The lane's A operand of K-step S of fragment f: 24 bytes at offset 24 S of
-// the 48-byte record of row 32 f + r32 in K-half h (blocks 4c + h and 4c + 2 + h).
+// The lane's activation operand of K-step S of fragment f: 24 bytes at offset
+// 24 S of the 48-byte record of row 32 f + r32 in K-half h (blocks 4c + h and
+// 4c + 2 + h).
 template <int S>
 __device__ __forceinline__ i8v read_afrag(const uint8_t* st, int f, int r32, int h) {
   const uint8_t* p = st + h * A_HS + (32 * f + r32) * 48 + 24 * S;
@@ -466,112 +471,166 @@ __device__ __forceinline__ i8v read_afrag(const uint8_t* st, int f, int r32, int
   }
 }
 
-// One wavefront's weight rows for one chunk: each fragment's 32 rows as two
-// loads of 16 rows x 64 contiguous bytes (lane l: row 16 j + l % 16, block
-// l / 16 of the chunk); b_operands() moves them into MFMA order.
-struct BChunk {
-  uint4_t q[4][2];  // [fragment][row half]
+// One wavefront's weight rows for a chunk pair as loaded: fragment g's 32
+// rows x 128 B in four loads of 8 rows (q[g][j]: rows 8 j + l / 8, bytes
+// 16 (l % 8)).
+struct BRaw {
+  uint4_t q[2][4];
 };
 
 struct BSrc {
-  rsrc_t rc[4];    // codes of the matrix holding each fragment
-  uint32_t vc[4];  // fragment row (lane % 16) offset + 16 * (lane / 16)
-  uint32_t half;   // byte distance of fragment row 16 from row 0
-  __device__ __forceinline__ void load(int c, BChunk& r) const {
+  rsrc_t rc[2], rs[2];  // codes and scales of the matrix holding each fragment
+  uint32_t vc[2];       // the lane's code bytes in chunk 0: row l / 8 of the fragment, + 16 (l % 8)
+  uint32_t vs[2];       // the lane's scale bytes in chunk 0: row l % 32 of the fragment
+  uint32_t row8;        // bytes from a weight row to the row 8 below
+  // Fragment g of the pair starting at chunk c (even); c < 0 loads zeros.
+  // Past the row's last chunk the bytes belong to the next row (never used).
+  __device__ __forceinline__ void load(int g, int c, BRaw& r, uint2& ws) const {
+    const bool z = c < 0;
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) r.q[g][j] = bload16(rc[g], vc[g] + half * j + (uint32_t)c * 64u);
+    for (int j = 0; j < 4; ++j) r.q[g][j] = bload16(rc[g], z ? kOob : vc[g] + (uint32_t)j * row8 + (uint32_t)c * 64u);
+    ws = bload8(rs[g], z ? kOob : vs[g] + (uint32_t)c * 4u);
   }
 };
 
-// Chunk c of the tile (i = c - cw0 within the window): both K-steps, 32
-// MFMAs.  af holds the chunk's K-step 0 fragments on entry and the next
-// chunk's on return (read from stage nxt).  run == false multiplies nothing
-// (a chunk past the last one of a pair).
-__device__ __forceinline__ void tile_chunk(const TileSmem& sm, const uint8_t* cur, const uint8_t* nxt,
-                                           const BChunk& bc, i8v (&af)[4], f16v (&acc)[4][4], int i, int wid,
-                                           int r32, int h, bool run) {
-  uint32_t sa[4], sb[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) sa[f] = sm.k.sca[(32 * f + r32) * TSW + i] >> (8 * h);
-#pragma unroll
-  for (int g = 0; g < 4; ++g) sb[g] = sm.k.scb[wid][(32 * g + r32) * TSW + i] >> (8 * h);
-  i8v bop[4][2];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) b_operands(bc.q[g][0], bc.q[g][1], bop[g][0], bop[g][1]);
-  i8v af1[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) af1[f] = read_afrag<1>(cur, f, r32, h);
-  if (run) {
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[f], bop[g][0], acc[f][g], 2, 4, 0,
-                                                                     (int)sa[f], 0, (int)sb[g]);
-  }
-#pragma unroll
-  for (int f = 0; f < 4; ++f) af[f] = read_afrag<0>(nxt, f, r32, h);
-  if (run) {
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af1[f], bop[g][1], acc[f][g], 2, 4, 0,
-                                                                     (int)(sa[f] >> 16), 0, (int)(sb[g] >> 16));
-  }
+__device__ __forceinline__ i8v bop(const uint4_t& q) { return i8v{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0}; }
+
+// s_waitcnt with only the vector-memory count: every vector memory operation
+// but the n most recent has completed (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// All K of one tile.  B chunk c+1 is loaded while chunk c is multiplied (two
-// register sets, so the loop runs in pairs of chunks), A chunk c+2 is loaded
-// into registers at the start of chunk c and stored into its LDS stage at the
-// end.  Loads past the window's last chunk re-read it, so no load sits behind
-// a branch.  tables(cw0) issues and stores the scale tables of a window; the
-// barrier after the first A stages makes them visible.
-template <typename Tables>
-__device__ __forceinline__ void tile_k_loop(TileSmem& sm, f16v (&acc)[4][4], const ASrc& as, const BSrc& bs,
-                                            int nch, int tid, Tables tables) {
-  const int lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
+// s_waitcnt with only the LDS count: this wavefront's LDS operations have completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// Workgroup barrier without the release fence of __syncthreads(), which would
+// wait for every copy into LDS in flight: each caller first waits for what the
+// other wavefronts will read.  The acquire fence (no instructions at workgroup
+// scope) keeps the compiler from moving later LDS reads above the barrier.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Vector memory operations of a pair: four LDS copies (two chunks), then per
+// weight fragment four code loads and a scale load.
+constexpr int kPairWeightVm = 2 * 5;
+
+// A lane's scale words of chunk wd (rows r32 + 32 f of the table), shifted so
+// that byte 0 is the scale of its block 4c + h (K-step 0) and byte 2 that of
+// block 4c + 2 + h (K-step 1).
+__device__ __forceinline__ uint4_t scale_words(const uint32_t* tab, int wd, int r32, int h) {
+  const uint4_t w = *reinterpret_cast<const uint4_t*>(tab + (32 * wd + r32) * 4);
+  const int s = 8 * h;
+  return uint4_t{w.x >> s, w.y >> s, w.z >> s, w.w >> s};
+}
+
+__device__ __forceinline__ int word(const uint4_t& w, int f) {
+  return (int)(f == 0 ? w.x : f == 1 ? w.y : f == 2 ? w.z : w.w);
+}
+
+// One MFMA of the tile: weights W (fp4, scale byte opsel of sw) against
+// activations A (fp6, scale byte opsel of sa).  WFIRST: the weights are the
+// first operand (accumulators hold one bucket row per lane) or the second
+// (one output column per lane).
+template <bool WFIRST>
+__device__ __forceinline__ f16v tile_mfma(const i8v& W, const i8v& A, const f16v& c, int opsel, int sw, int sa) {
+  if (WFIRST) {
+    if (opsel == 0) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(W, A, c, 4, 2, 0, sw, 0, sa);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(W, A, c, 4, 2, 2, sw, 2, sa);
+  }
+  if (opsel == 0) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, W, c, 2, 4, 0, sa, 0, sw);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, W, c, 2, 4, 2, sa, 2, sw);
+}
+
+// Pair q of a window (chunks c0 = cw0 + 2q and c0 + 1, in stages 2 PJ and
+// 2 PJ + 1; raw and ws hold its weights as loaded).  The copies of the next
+// pair go out first, into the other two stages; then the fragments' rows are
+// written into the wavefront's LDS area in operand order (K-step S at
+// S * 1024, lane t's 16 B at slot t ^ 2 S, so both the writes and the reads
+// stay within two LDS banks per slot) and the registers reloaded with the
+// next pair; then the four K-steps: the activation fragments and the two
+// weight operands are read, 8 MFMAs.  run0 / run1: chunk c0 / c0 + 1 exists.
+template <int PJ, bool WFIRST>
+__device__ __forceinline__ void tile_pair(const TileTables& tb, uint8_t* const (&st)[4], uint8_t* scr,
+                                          const ACopy& as, const BSrc& bs, BRaw& raw, uint2 (&ws)[2],
+                                          f16v (&acc)[4][2], int cw0, int last, int q, int lane, int r32, int h,
+                                          bool run0, bool run1) {
+  const int c0 = cw0 + 2 * q, n0 = c0 + 2;
+  as.copy(st[2 - 2 * PJ], n0 <= last ? n0 : -1);
+  as.copy(st[3 - 2 * PJ], n0 + 1 <= last ? n0 + 1 : -1);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const int r8 = lane >> 3, s = lane & 7, S = s >> 1, hh = s & 1;
+    uint8_t* wr = scr + S * 1024 + ((r8 ^ (2 * S)) + 32 * hh) * 16;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4_t*>(wr + g * B_FRAG + j * 128) = raw.q[g][j];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint2 wsn[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) bs.load(g, n0 <= last ? n0 : -1, raw, wsn[g]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int S = 0; S < 4; ++S) {
+    if (S < 2 ? !run0 : !run1) continue;
+    const uint8_t* sta = st[2 * PJ + (S >> 1)];
+    const uint4_t sa = scale_words(tb.sca, c0 + (S >> 1) - cw0, r32, h);
+    i8v a[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) a[f] = (S & 1) ? read_afrag<1>(sta, f, r32, h) : read_afrag<0>(sta, f, r32, h);
+    uint4_t b[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      b[g] = *reinterpret_cast<const uint4_t*>(scr + g * B_FRAG + S * 1024 + ((lane ^ (2 * S)) * 16));
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int sw = (int)((S < 2 ? ws[g].x : ws[g].y) >> (8 * h));
+#pragma unroll
+      for (int f = 0; f < 4; ++f) acc[f][g] = tile_mfma<WFIRST>(bop(b[g]), a[f], acc[f][g], 2 * (S & 1), sw, word(sa, f));
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g) ws[g] = wsn[g];
+  wait_vm<kPairWeightVm>();  // this wavefront's copies of the next pair are done
+  wg_barrier();
+}
+
+// All K of one tile.  The first pair's copies go out before the window's
+// scale table and its weight loads after; the table's stores wait for every
+// load before them, so the copies are done, and the barrier publishes the
+// table and the first stages.  tables(cw0) issues and stores the scale table
+// of a window.
+template <bool WFIRST, typename Tables>
+__device__ __forceinline__ void tile_k_loop(TileTables& tb, uint8_t* const (&st)[4], uint8_t* scr,
+                                            f16v (&acc)[4][2], const ACopy& as, const BSrc& bs, int nch, int tid,
+                                            Tables tables) {
+  const int lane = tid & 63, r32 = lane & 31, h = lane >> 5;
   for (int cw0 = 0; cw0 < nch; cw0 += TWIN) {
     const int last = min(cw0 + TWIN, nch) - 1;
-    if (cw0 > 0) __syncthreads();  // every wavefront is done with the previous window
-    AStage a0, a1;
-    as.load(cw0, a0);
-    as.load(min(cw0 + 1, last), a1);
-    BChunk b0, b1;
-    bs.load(cw0, b0);
+    if (cw0 > 0) wg_barrier();  // every wavefront is done with the previous window
+    as.copy(st[0], cw0);
+    as.copy(st[1], cw0 + 1 <= last ? cw0 + 1 : -1);
     tables(cw0);
-    store_a(sm.k.a[0], a0, tid);
-    store_a(sm.k.a[1], a1, tid);
-    __syncthreads();
-    i8v af[4];
+    __builtin_amdgcn_sched_barrier(0);
+    BRaw raw;
+    uint2 ws[2];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) af[f] = read_afrag<0>(sm.k.a[0], f, r32, h);
-    int s0 = 0;  // LDS stage of chunk c
-    for (int c = cw0; c <= last; c += 2) {
-      const int s1 = s0 == 2 ? 0 : s0 + 1, s2 = s1 == 2 ? 0 : s1 + 1;
-      // The loads of each step are pinned ahead of its MFMAs (sched_barrier):
-      // left to itself the scheduler sinks them next to their first use.
-      {  // chunk c (always present)
-        AStage an;
-        as.load(min(c + 2, last), an);
-        bs.load(min(c + 1, last), b1);
-        __builtin_amdgcn_sched_barrier(0);
-        tile_chunk(sm, sm.k.a[s0], sm.k.a[s1], b0, af, acc, c - cw0, wid, r32, h, true);
-        store_a(sm.k.a[s2], an, tid);
-        __syncthreads();
-      }
-      {  // chunk c + 1 (past the last chunk of an odd window: loads and stores only)
-        AStage an;
-        as.load(min(c + 3, last), an);
-        bs.load(min(c + 2, last), b0);
-        __builtin_amdgcn_sched_barrier(0);
-        tile_chunk(sm, sm.k.a[s1], sm.k.a[s2], b1, af, acc, c + 1 - cw0, wid, r32, h, c + 1 <= last);
-        store_a(sm.k.a[s0], an, tid);
-        __syncthreads();
-      }
-      s0 = s2;
+    for (int g = 0; g < 2; ++g) bs.load(g, cw0, raw, ws[g]);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<kPairWeightVm>();  // all but the weight loads just issued
+    wait_lgkm0();              // the table stores
+    wg_barrier();
+    for (int q = 0; cw0 + 2 * q <= last; q += 2) {
+      const int c = cw0 + 2 * q;
+      tile_pair<0, WFIRST>(tb, st, scr, as, bs, raw, ws, acc, cw0, last, q, lane, r32, h, true, c + 1 <= last);
+      tile_pair<1, WFIRST>(tb, st, scr, as, bs, raw, ws, acc, cw0, last, q + 1, lane, r32, h, c + 2 <= last,
+                           c + 3 <= last);
     }
   }
 }
@@ -817,160 +876,165 @@ __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
 // last tile narrower than 256 columns (inter % 256 == 128) wavefronts 2 and 3
 // load zeros and store nothing.
 
-__global__ __launch_bounds__(kPT, 1) void gateup_tile_kernel(
+__global__ __launch_bounds__(kTilePT, 1) void gateup_tile_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, uint32_t xq_bytes, uint32_t xs_bytes, int P,
     ExpertStore w, const TileDesc* __restrict__ tiles, const int32_t* __restrict__ counts,
     uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
-  __shared__ TileSmem sm;
+  __shared__ TileTables tb;
+  __shared__ __attribute__((aligned(16))) uint8_t a0[A_STAGE], a1[A_STAGE], a2[A_STAGE], a3[A_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t bscr[8 * B_SCR];
+  uint8_t* const st[4] = {a0, a1, a2, a3};
   const int H = w.H, I = w.I, NBH = H / 32, NBI = I / 32;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
+  // wid in a scalar register: every address derived from it alone stays scalar
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6), r32 = lane & 31;
   const uint32_t wrow = (uint32_t)H / 2u;
   const size_t mat = (size_t)I * wrow, smat = (size_t)I * NBH;
   const int total = counts[0];
+  // Every K loop ends on a barrier after the last reads of the stages and the
+  // table, and the epilogue uses registers only, so a tile can start at once.
   for (TileWalk tw(total); tw.next < tw.end; tw.next += tw.step) {
     const TileDesc d = tiles[tw.next];
     if (d.slot < 0) continue;  // no stored expert: the down GEMM writes its rows as zeros
-    __syncthreads();           // the previous tile's epilogue is done with the LDS
     const int j0 = d.ntile * GU_N;
-    const int hc0 = j0 + 64 * wid;           // this wavefront's first h column
-    const bool live = hc0 < I;               // inter % 256 == 128: the last tile is half wide
-    ASrc as;
-    as.init(xq, xq_bytes, tid, d.row0, P);
+    const int hc0 = j0 + 32 * wid;  // this wavefront's 32 h columns: gate rows hc0.. (fragment 0), up rows (1)
+    const bool live = hc0 < I;      // inter % 256 == 128: the last tile is half wide
+    ACopy as;
+    as.init(xq, xq_bytes, wid, lane, d.row0, P);
     BSrc bs;
-    const rsrc_t rg = make_rsrc(w.wg + (size_t)d.slot * mat, (uint32_t)mat);
-    const rsrc_t ru = make_rsrc(w.wu + (size_t)d.slot * mat, (uint32_t)mat);
-    const uint32_t lrow = (uint32_t)(lane & 15) * wrow + 16u * (uint32_t)(lane >> 4);
+    bs.rc[0] = make_rsrc(w.wg + (size_t)d.slot * mat, (uint32_t)mat);
+    bs.rc[1] = make_rsrc(w.wu + (size_t)d.slot * mat, (uint32_t)mat);
+    bs.rs[0] = make_rsrc(w.sg + (size_t)d.slot * smat, (uint32_t)smat);
+    bs.rs[1] = make_rsrc(w.su + (size_t)d.slot * smat, (uint32_t)smat);
+    bs.row8 = 8u * wrow;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bs.rc[g] = g < 2 ? rg : ru;
-      bs.vc[g] = live ? (uint32_t)(hc0 + 32 * (g & 1)) * wrow + lrow : kOob;
+    for (int g = 0; g < 2; ++g) {
+      bs.vc[g] = live ? ((uint32_t)hc0 + (uint32_t)(lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7) : kOob;
+      bs.vs[g] = live ? ((uint32_t)hc0 + (uint32_t)r32) * (uint32_t)NBH : kOob;
     }
-    bs.half = 16u * wrow;
     const rsrc_t xsr = make_rsrc(xs, xs_bytes);
-    const rsrc_t sgr = make_rsrc(w.sg + (size_t)d.slot * smat, (uint32_t)smat);
-    const rsrc_t sur = make_rsrc(w.su + (size_t)d.slot * smat, (uint32_t)smat);
     auto tables = [&](int cw0) {
-      const int t = opaque(tid), l = t & 63;
-      // table rows 0-63: gate rows hc0.., 64-127: the same up rows
-      const auto off = [&](int r) { return live ? (uint32_t)(hc0 + (r & 63)) * (uint32_t)NBH : kOob; };
-      ScaleCols<BM, kPT, TWIN, TSW> ta;
-      BTable<0> t0;
-      BTable<1> t1;
+      const int t = opaque(tid);
+      ScaleCols<BM, kTilePT, TWIN, TWIN + 1> ta;
       ta.issue(xsr, cw0, t, d.row0, d.mrows, P);
-      t0.issue([&](int) { return sgr; }, off, cw0, l);
-      ta.store(sm.k.sca, t);
-      t0.store(sm.k.scb[wid], l);
-      t1.issue([&](int) { return sur; }, off, cw0, l);
-      t1.store(sm.k.scb[wid], l);
+      ta.store_cf(tb.sca, t);
     };
-    f16v acc[4][4];
+    f16v acc[4][2];
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) acc[f][g] = f16v{};
-    tile_k_loop(sm, acc, as, bs, H / KC, tid, tables);  // ends on a barrier
-    // h = silu(g) * u into the staging buffer
-    {
+    for (int f = 0; f < 4; ++f) acc[f][0] = acc[f][1] = f16v{};
+    tile_k_loop<true>(tb, st, bscr + wid * B_SCR, acc, as, bs, H / KC, tid, tables);  // ends on a barrier
+    // h = silu(g) * u and its MXFP6 block, in registers.  Lane l holds row
+    // 32 f + l % 32 and columns 8 j + 4 (l / 32) + i of the wavefront's 32 in
+    // register 4 j + i: the block's largest magnitude and its packed codes are
+    // completed with the partner lane l ^ 32.
+    if (live) {
       const int t = opaque(tid), e32 = t & 31, eh = (t >> 5) & 1;
-      float* st = sm.stage + (eh * 4) * (GU_N + 1) + 64 * (t >> 6) + e32;
+      const int gblk = hc0 >> 5;
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
+      for (int f = 0; f < 4; ++f) {
+        const int row = 32 * f + e32;
+        float hv[16], amax = 0.f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int r = 0; r < 16; ++r) {
+          hv[r] = swiglu_fast(acc[f][0][r], acc[f][1][r]);
+          amax = fmaxf(amax, fabsf(hv[r]));
+        }
+        const auto mx = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax), false, false);
+        amax = fmaxf(__uint_as_float(mx[0]), __uint_as_float(mx[1]));
+        // G[j]: the four codes of columns 8 j + 4 eh .. + 3 (24 bits)
+        uint32_t G[4] = {0u, 0u, 0u, 0u}, sbyte = 0u;
+        if (amax != 0.f) {
+          float inv;
+          sbyte = q6_scale(amax, inv);
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            st[(32 * f + (r >> 2) * 8 + (r & 3)) * (GU_N + 1) + 32 * i] = swiglu_fast(acc[f][i][r], acc[f][2 + i][r]);
-    }
-    __syncthreads();
-    // MXFP6 of each (row, 32-block) of the tile, written in sorted-row order
-    const int nblk = min(GU_N, I - j0) / 32;
-    for (int item = opaque(tid); item < BM * (GU_N / 32); item += kPT) {
-      const int row = item % BM, blk = item / BM;
-      if (row < d.mrows && blk < nblk) {
-        float v[32];
+          for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = sm.stage[row * (GU_N + 1) + 32 * blk + i];
-        uint32_t pk[6], sb;
-        q6_block(v, pk, sb);
-        const size_t grow = (size_t)(d.row0 + row);
-        const int gblk = j0 / 32 + blk;
-        uint2* dst = reinterpret_cast<uint2*>(hq + q6_offset(d.row0 + row, gblk, P));
-        dst[0] = make_uint2(pk[0], pk[1]);
-        dst[1] = make_uint2(pk[2], pk[3]);
-        dst[2] = make_uint2(pk[4], pk[5]);
-        hs[grow * NBI + gblk] = (uint8_t)sb;
+            for (int i = 0; i < 4; ++i) G[j] |= e2m3_rne(hv[4 * j + i] * inv) << (6 * i);
+        }
+        // The record's 24 bytes: code m at bits 6m..6m+5, so columns 8j'..8j'+7
+        // are 48 bits, the lower lane's G[j'] then the upper lane's.  The lower
+        // lane writes bytes 0-11 (j' = 0, 1), the upper lane bytes 12-23.
+        const uint32_t s0 = eh ? G[0] : G[2], s1 = eh ? G[1] : G[3];
+        const auto x0 = __builtin_amdgcn_permlane32_swap(s0, s0, false, false);
+        const auto x1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
+        const uint32_t q0 = eh ? x0[0] : x0[1], q1 = eh ? x1[0] : x1[1];
+        const uint32_t lo0 = eh ? q0 : G[0], lo1 = eh ? q1 : G[1], hi0 = eh ? G[2] : q0, hi1 = eh ? G[3] : q1;
+        if (row < d.mrows) {
+          uint32_t* dst = reinterpret_cast<uint32_t*>(hq + q6_offset(d.row0 + row, gblk, P) + 12 * eh);
+          dst[0] = lo0 | (hi0 << 24);
+          dst[1] = (hi0 >> 8) | (lo1 << 16);
+          dst[2] = (lo1 >> 16) | (hi1 << 8);
+          if (eh == 0) hs[(size_t)(d.row0 + row) * NBI + gblk] = (uint8_t)sbyte;
+        }
       }
     }
   }
+  wait_vm<0>();  // no copy into LDS outlives the workgroup
 }
 
 // ---- P2: down GEMM -> y_pair ---------------------------------------------------------
 //
-// Wavefront w of a tile owns output columns n0 + 128 w .. + 127 (four
-// fragments of W_down rows); each lane stores its accumulators straight into
-// the y_pair rows of the tile's pairs (32 consecutive columns of two rows per
-// store).  In a last tile narrower than 512 columns (hidden % 512 == 256)
-// wavefronts 2 and 3 load zeros and store nothing.
+// Wavefront w of a tile owns output columns n0 + 64 w .. + 63 (two fragments
+// of W_down rows); each lane stores its accumulators straight into the y_pair
+// rows of the tile's pairs (32 consecutive columns of two rows per store).  In
+// a last tile narrower than 512 columns (hidden % 512 == 256) wavefronts 4-7
+// load zeros and store nothing.
 
-__global__ __launch_bounds__(kPT, 1) void down_tile_kernel(
+__global__ __launch_bounds__(kTilePT, 1) void down_tile_kernel(
     const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, uint32_t hq_bytes, uint32_t hs_bytes, int P,
     ExpertStore w, const int32_t* __restrict__ sorted_pair, const TileDesc* __restrict__ tiles,
     const int32_t* __restrict__ counts, float* __restrict__ y) {
-  __shared__ TileSmem sm;
+  __shared__ TileTables tb;
+  __shared__ __attribute__((aligned(16))) uint8_t a0[A_STAGE], a1[A_STAGE], a2[A_STAGE], a3[A_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t bscr[8 * B_SCR];
+  __shared__ int rowtok[BM];
+  uint8_t* const st[4] = {a0, a1, a2, a3};
   const int H = w.H, I = w.I, NBI = I / 32;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6), r32 = lane & 31;
   const uint32_t wrow = (uint32_t)I / 2u;
   const size_t mat = (size_t)H * wrow, smat = (size_t)H * NBI;
   const int total = counts[1];
   for (TileWalk tw(total); tw.next < tw.end; tw.next += tw.step) {
     const TileDesc d = tiles[tw.next];
-    __syncthreads();
-    if (tid < BM) sm.rowtok[tid] = tid < d.mrows ? sorted_pair[d.row0 + tid] : -1;
-    __syncthreads();
+    wg_barrier();  // the previous tile's epilogue has read rowtok
+    if (tid < BM) rowtok[tid] = tid < d.mrows ? sorted_pair[d.row0 + tid] : -1;
+    wait_lgkm0();
+    wg_barrier();
     const int n0 = d.ntile * DN_N;
     const int nc0 = n0 + WN * wid;  // this wavefront's first output column
     const bool live = nc0 < H;
     if (d.slot < 0) {
-      for (int i = tid; i < d.mrows * DN_N; i += kPT) {
+      for (int i = tid; i < d.mrows * DN_N; i += kTilePT) {
         const int row = i / DN_N, col = i % DN_N;
-        if (n0 + col < H) y[(size_t)sm.rowtok[row] * H + n0 + col] = 0.f;
+        if (n0 + col < H) y[(size_t)rowtok[row] * H + n0 + col] = 0.f;
       }
       continue;
     }
-    ASrc as;
-    as.init(hq, hq_bytes, tid, d.row0, P);
+    ACopy as;
+    as.init(hq, hq_bytes, wid, lane, d.row0, P);
     BSrc bs;
     const rsrc_t rd = make_rsrc(w.wd + (size_t)d.slot * mat, (uint32_t)mat);
-    const uint32_t lrow = (uint32_t)(lane & 15) * wrow + 16u * (uint32_t)(lane >> 4);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bs.rc[g] = rd;
-      bs.vc[g] = live ? (uint32_t)(nc0 + 32 * g) * wrow + lrow : kOob;
-    }
-    bs.half = 16u * wrow;
-    const rsrc_t hsr = make_rsrc(hs, hs_bytes);
     const rsrc_t sdr = make_rsrc(w.sd + (size_t)d.slot * smat, (uint32_t)smat);
+    bs.row8 = 8u * wrow;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const uint32_t row = (uint32_t)(nc0 + 32 * g);
+      bs.rc[g] = rd;
+      bs.rs[g] = sdr;
+      bs.vc[g] = live ? (row + (uint32_t)(lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7) : kOob;
+      bs.vs[g] = live ? (row + (uint32_t)r32) * (uint32_t)NBI : kOob;
+    }
+    const rsrc_t hsr = make_rsrc(hs, hs_bytes);
     auto tables = [&](int cw0) {
-      // A scales: hs is row-major [sorted row][I/32], so its words are read row by row
-      const int t = opaque(tid), l = t & 63;
-      const auto res = [&](int) { return sdr; };
-      const auto off = [&](int r) { return live ? (uint32_t)(nc0 + r) * (uint32_t)NBI : kOob; };
-      ScaleRows<BM, kPT, TWIN, TSW> ta;
-      BTable<0> t0;
-      BTable<1> t1;
+      // hs is row-major [sorted row][I/32], so its words are read row by row
+      const int t = opaque(tid);
+      ScaleRows<BM, kTilePT, TWIN, TWIN + 1> ta;
       ta.issue(hsr, cw0, t, [&](int r) { return r < d.mrows ? (uint32_t)(d.row0 + r) * (uint32_t)NBI : kOob; });
-      t0.issue(res, off, cw0, l);
-      ta.store(sm.k.sca, t);
-      t0.store(sm.k.scb[wid], l);
-      t1.issue(res, off, cw0, l);
-      t1.store(sm.k.scb[wid], l);
+      ta.store_cf(tb.sca, t);
     };
-    f16v acc[4][4];
+    f16v acc[4][2];
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) acc[f][g] = f16v{};
-    tile_k_loop(sm, acc, as, bs, I / KC, tid, tables);
+    for (int f = 0; f < 4; ++f) acc[f][0] = acc[f][1] = f16v{};
+    tile_k_loop<false>(tb, st, bscr + wid * B_SCR, acc, as, bs, I / KC, tid, tables);
     if (live) {
       const int t = opaque(tid), e32 = t & 31, eh = (t >> 5) & 1;
 #pragma unroll
@@ -980,14 +1044,15 @@ __global__ __launch_bounds__(kPT, 1) void down_tile_kernel(
         for (int r = 0; r < 16; ++r) {
           const int row = 32 * f + (r >> 2) * 8 + eh * 4 + (r & 3);
           if (row < d.mrows) {
-            float* yr = y + (size_t)sm.rowtok[row] * H + nc0 + e32;
+            float* yr = y + (size_t)rowtok[row] * H + nc0 + e32;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) yr[32 * g] = acc[f][g][r];
+            for (int g = 0; g < 2; ++g) yr[32 * g] = acc[f][g][r];
           }
         }
       }
     }
   }
+  wait_vm<0>();  // no copy into LDS outlives the workgroup
 }
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -1047,7 +1112,7 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
                      w, sorted_pair, sbk, counts, hq, hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(gateup_tile_kernel, dim3(kGrid), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, (int)P, w,
+  hipLaunchKernelGGL(gateup_tile_kernel, dim3(kGrid), dim3(kTilePT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, (int)P, w,
                      gu, counts, hq, hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -1055,7 +1120,7 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
                      sorted_pair, sbk, counts, y_pair);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(down_tile_kernel, dim3(kGrid), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, (int)P, w,
+  hipLaunchKernelGGL(down_tile_kernel, dim3(kGrid), dim3(kTilePT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, (int)P, w,
                      sorted_pair, dn, counts, y_pair);
   return hipGetLastError();
 }
