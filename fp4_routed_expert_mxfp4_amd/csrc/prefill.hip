@@ -656,12 +656,13 @@ __device__ __forceinline__ float swiglu_fast(float g, float u) {
 
 
 // Four K-steps (two 128-K chunks) of one wavefront: A block 2s+h of row r32
-// (24 B); each B fragment's rows as two halves of 16 rows x 64 B per chunk
-// (moved into MFMA order by b_operands when used); and the scale words of
-// those 8 blocks.
+// (24 B); each B fragment's 32 rows x 128 B of the two chunks as loaded, four
+// loads of 8 rows (b[g][j]: rows 8 j + l / 8, bytes 16 (l % 8)), moved into
+// MFMA order through the wavefront's LDS area when used (a load over the 16 or
+// 32 rows of an operand streams at about two thirds of this rate from memory).
 struct SkRegs {
   uint2 a[4][3];
-  uint4_t b[2][2][2];  // [chunk][fragment][row half]
+  uint4_t b[2][4];  // [fragment][load]
 };
 
 // Scale words come from a per-wavefront LDS table read once per window of
@@ -669,12 +670,13 @@ struct SkRegs {
 // fragments (whose scale bytes are contiguous).
 constexpr int SKWIN = 20;
 constexpr int SKW = SKWIN + 1;  // words per table row (odd: 32 rows hit 32 banks)
+constexpr int SK_SCR = 32 * 128;  // a wavefront's LDS area for one fragment's two chunks in MFMA order
 
 struct SkSrc {
   rsrc_t ra, rb[2];
-  uint32_t va, vb[2];  // va: the lane's record (row r32, K-half h) in chunk 0; vb: row (lane%16) + 16 * (lane/16)
+  uint32_t va, vb[2];  // va: the lane's record (row r32, K-half h) in chunk 0; vb: row l / 8 of the fragment, + 16 (l % 8)
   uint32_t cstride;    // bytes per chunk of the A records
-  uint32_t half;       // byte distance of fragment row 16 from row 0
+  uint32_t row8;       // bytes from a weight row to the row 8 below
   __device__ __forceinline__ void load(int n, SkRegs& r) const {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {  // K-step s: chunk 2n + s/2, block 2(s%2) + h = bytes 24(s%2).. of the record
@@ -682,24 +684,36 @@ struct SkSrc {
 #pragma unroll
       for (int j = 0; j < 3; ++j) r.a[s][j] = bload8(ra, o + 8u * j);
     }
-    // the two chunks' 64-B halves of each row's 128-B line back to back
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) r.b[m][g][j] = bload16(rb[g], vb[g] + half * j + (uint32_t)(2 * n + m) * 64u);
+      for (int j = 0; j < 4; ++j) r.b[g][j] = bload16(rb[g], vb[g] + (uint32_t)j * row8 + (uint32_t)n * 128u);
   }
 };
 
+// A fragment's four K-step operands from its loads (b: as SkRegs::b[g]): the
+// rows are written into the wavefront's LDS area in operand order (K-step S at
+// S * 1024, lane t's 16 B at slot t ^ 2 S, so both the writes and the reads
+// stay within two LDS banks per slot) and read back.  A wavefront's LDS
+// accesses complete in order, so the area serves one fragment after another.
+__device__ __forceinline__ void sk_operands(const uint4_t (&b)[4], uint8_t* scr, i8v (&op)[4]) {
+  const int lane = __lane_id(), r8 = lane >> 3, s = lane & 7, S = s >> 1, hh = s & 1;
+  uint8_t* wr = scr + S * 1024 + ((r8 ^ (2 * S)) + 32 * hh) * 16;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4_t*>(wr + j * 128) = b[j];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint4_t q = *reinterpret_cast<const uint4_t*>(scr + k * 1024 + ((lane ^ (2 * k)) * 16));
+    op[k] = i8v{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+  }
+}
+
 __device__ __forceinline__ void sk_mma(const SkRegs& r, f16v (&acc)[2], int nks, int h, const uint32_t* tab,
-                                       int cw) {  // cw: the batch's first chunk within the window
+                                       int cw, uint8_t* scr) {  // cw: the batch's first chunk within the window
   const int r32 = __lane_id() & 31;
   i8v bop[2][4];  // [fragment][K-step]
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int g = 0; g < 2; ++g) b_operands(r.b[m][g][0], r.b[m][g][1], bop[g][2 * m], bop[g][2 * m + 1]);
+  for (int g = 0; g < 2; ++g) sk_operands(r.b[g], scr, bop[g]);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     if (s < nks) {
@@ -730,7 +744,7 @@ struct SkTables {
 // tables(cw0, ts) issues the scale-table loads of the window starting at chunk cw0.
 template <typename TS, typename Tables>
 __device__ __forceinline__ void sk_k_loop(const SkSrc& src, f16v (&acc)[2], int K, int h, uint32_t* tab,
-                                          Tables tables) {
+                                          uint8_t* scr, Tables tables) {
   const int nks_total = K / 64, nchunks = K / KC;
   const int lane = __lane_id();
   for (int cw0 = 0; cw0 < nchunks; cw0 += SKWIN) {
@@ -745,9 +759,9 @@ __device__ __forceinline__ void sk_k_loop(const SkSrc& src, f16v (&acc)[2], int 
     __builtin_amdgcn_wave_barrier();  // a wavefront's LDS accesses complete in order
     for (int n = b0; n <= last; n += 2) {
       src.load(min(n + 1, last), r1);
-      sk_mma(r0, acc, min(4, nks_total - 4 * n), h, tab, 2 * (n - b0));
+      sk_mma(r0, acc, min(4, nks_total - 4 * n), h, tab, 2 * (n - b0), scr);
       src.load(min(n + 2, last), r0);
-      sk_mma(r1, acc, n + 1 > last ? 0 : min(4, nks_total - 4 * (n + 1)), h, tab, 2 * (n + 1 - b0));
+      sk_mma(r1, acc, n + 1 > last ? 0 : min(4, nks_total - 4 * (n + 1)), h, tab, 2 * (n + 1 - b0), scr);
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -763,6 +777,7 @@ __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
     const int32_t* __restrict__ counts, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
   __shared__ float stage[4][32 * 33];
   __shared__ uint32_t sktab[4][96 * SKW];
+  __shared__ __attribute__((aligned(16))) uint8_t skscr[4][SK_SCR];
   const int H = w.H, I = w.I, NBH = H / 32, NBI = I / 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
   const uint32_t wrow = (uint32_t)H / 2u;
@@ -779,8 +794,8 @@ __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
     src.cstride = 96u * (uint32_t)P;
     src.rb[0] = make_rsrc(w.wg + (size_t)bk.slot * mat, (uint32_t)mat);
     src.rb[1] = make_rsrc(w.wu + (size_t)bk.slot * mat, (uint32_t)mat);
-    src.vb[0] = src.vb[1] = (uint32_t)(32 * q + (lane & 15)) * wrow + 16u * (uint32_t)(lane >> 4);
-    src.half = 16u * wrow;
+    src.vb[0] = src.vb[1] = (uint32_t)(32 * q + (lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7);
+    src.row8 = 8u * wrow;
     const rsrc_t xsr = make_rsrc(xs, xs_bytes);
     const rsrc_t sgr = make_rsrc(w.sg + (size_t)bk.slot * smat, (uint32_t)smat);
     const rsrc_t sur = make_rsrc(w.su + (size_t)bk.slot * smat, (uint32_t)smat);
@@ -791,7 +806,7 @@ __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
       ts.b[1].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NBH; });
     };
     f16v acc[2] = {f16v{}, f16v{}};
-    sk_k_loop<TS>(src, acc, H, h, sktab[wid], tables);
+    sk_k_loop<TS>(src, acc, H, h, sktab[wid], skscr[wid], tables);
     // h = silu(g) * u: rows of the bucket x this unit's 32 h columns (one MXFP6 block per row)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -821,6 +836,7 @@ __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
     ExpertStore w, const int32_t* __restrict__ sorted_pair, const SkBucket* __restrict__ sbk,
     const int32_t* __restrict__ counts, float* __restrict__ y) {
   __shared__ uint32_t sktab[4][96 * SKW];
+  __shared__ __attribute__((aligned(16))) uint8_t skscr[4][SK_SCR];
   const int H = w.H, I = w.I, NBI = I / 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, r32 = lane & 31, h = lane >> 5;
   const uint32_t wrow = (uint32_t)I / 2u;
@@ -842,9 +858,9 @@ __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       src.rb[g] = rc;
-      src.vb[g] = (uint32_t)(n0 + 32 * g + (lane & 15)) * wrow + 16u * (uint32_t)(lane >> 4);
+      src.vb[g] = (uint32_t)(n0 + 32 * g + (lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7);
     }
-    src.half = 16u * wrow;
+    src.row8 = 8u * wrow;
     const rsrc_t hsr = make_rsrc(hs, hs_bytes);
     const rsrc_t sdr = make_rsrc(w.sd + (size_t)bk.slot * smat, (uint32_t)smat);
     using TS = SkTables<ScaleRows<32, 64, SKWIN, SKW>>;
@@ -854,7 +870,7 @@ __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
       ts.b[1].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + 32 + r) * NBI; });
     };
     f16v acc[2] = {f16v{}, f16v{}};
-    sk_k_loop<TS>(src, acc, I, h, sktab[wid], tables);
+    sk_k_loop<TS>(src, acc, I, h, sktab[wid], skscr[wid], tables);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = (i >> 2) * 8 + h * 4 + (i & 3);
