@@ -30,14 +30,18 @@
 // therefore one fixed fp32 expression of its own inputs: bit-identical
 // whichever other rows share its bucket and batch.
 //
-// K runs in chunks of 128 (four 32-blocks).  A B fragment is one 16-byte load
-// per lane -- lane l: block 4c + l/16 of row l%16, so 16 rows x 64 contiguous
-// bytes -- which is already the MFMA's operand order: K-step t takes dword t
-// (codes 8t..8t+7) of that block, and A's lane the same 8 values of x (or h)
-// of its row.  The scale bytes of a window of chunks are read once per
-// wavefront into an LDS table (contiguous row reads); the next chunk's loads
-// are in flight while one is multiplied.  The workgroups are persistent and
-// walk the units grid-stride.
+// K runs in chunks of 128 (four 32-blocks).  In the MFMA's operand order a B
+// fragment's chunk is lane l: block 4c + l/16 of row l%16 (16 rows x 64
+// contiguous bytes); K-step t takes dword t (codes 8t..8t+7) of that block, and
+// A's lane the same 8 values of x (or h) of its row.  The down kernels load B
+// in that order, one chunk at a time.  The gate/up kernels take chunk pairs
+// and load each fragment's pair as two loads of 8 rows x 128 bytes (lane l:
+// row 8j + l/8, bytes 16 (l%8) of the pair), a shape the memory pipeline
+// streams faster than 16 half lines, and move the pieces into operand order
+// through the wavefront's own LDS area.  The scale bytes of a window of chunks
+// are read once per wavefront into an LDS table (contiguous row reads); the
+// next chunks' loads are in flight while the current ones are multiplied.  The
+// workgroups are persistent and walk the units grid-stride.
 #include "common.cuh"
 #include "kernels.h"
 #include "route_core.cuh"
@@ -56,6 +60,7 @@ constexpr int kMtWin = 20;        // chunks per scale window (80 blocks; even: w
 constexpr int kMtW = kMtWin + 1;  // words per table row (odd: 16 rows hit 16 banks)
 constexpr int kMtRows = 16;       // bucket rows per unit (the MFMA's M)
 constexpr int kMtFrags = 4;       // 16-row weight fragments per unit
+constexpr int kMtScr = kMtFrags * 2048;  // a wavefront's LDS area: the fragments' chunk pair in operand order
 
 // The bucket list and, per bucket, the prefix of its groups of kMtRows rows: bucket b
 // owns units [tiles * G[b], tiles * G[b+1]), its groups of one column tile
@@ -123,14 +128,14 @@ __device__ __forceinline__ bf16x8_t dq8(uint32_t w, float s) {
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // CH consecutive chunks of one unit (one or two): A (per chunk and plane the
-// lane's 64 B of block 4c+g) and the four B fragments (lane: 16 B = block
-// 4c+g of row l%16).  With CH = 2 a fragment row's two chunks are the two
-// halves of one 128-byte line and their loads go out back to back, which
-// keeps the line's two requests together in the memory pipeline.
+// lane's 64 B of block 4c+g) and the four B fragments.  CH = 1: b[0][f] is
+// fragment f in operand order (lane: 16 B = block 4c+g of row l%16).  CH = 2:
+// b[j][f] is the j-th 8-row load of fragment f's chunk pair (lane l: row
+// 8j + l/8, bytes 16 (l%8) of the pair), put in operand order by mt_operands.
 template <int PLANES, int CH>
 struct MtRegs {
   uint4_t a[CH][PLANES][4];  // [chunk][plane][K-step]
-  uint4_t b[CH][kMtFrags];   // [chunk][fragment]
+  uint4_t b[CH][kMtFrags];   // CH = 1: [0][fragment]; CH = 2: [load][fragment]
 };
 
 template <int PLANES>
@@ -138,17 +143,24 @@ struct MtSrc {
   rsrc_t ra, rb[kMtFrags];
   uint32_t va;              // the lane's A row + 64 * g (kOob past the bucket's end)
   uint32_t plane;           // byte distance of the A planes
-  uint32_t vb[kMtFrags];    // fragment row (lane%16) + 16 * g
+  uint32_t vb[kMtFrags];    // CH = 1: fragment row l%16, + 16 g; CH = 2: fragment row l/8, + 16 (l%8)
+  uint32_t row8;            // CH = 2: bytes from a weight row to the row 8 below
   // chunks c .. c+CH-1, those at or past `end` read as zeros (every offset past its range)
   template <int CH>
   __device__ __forceinline__ void load(int c, int end, MtRegs<PLANES, CH>& r) const {
     uint32_t off[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) off[i] = c + i < end ? 0u : kOob;  // real offsets stay below 2^31
+    if constexpr (CH == 1) {
 #pragma unroll
-    for (int f = 0; f < kMtFrags; ++f)
+      for (int f = 0; f < kMtFrags; ++f) r.b[0][f] = bload16(rb[f], (vb[f] + (uint32_t)c * 64u) | off[0]);
+    } else {
+      const uint32_t ob = off[(__lane_id() >> 2) & 1];  // the lane's 16 B lie in chunk c + (l%8)/4
 #pragma unroll
-      for (int i = 0; i < CH; ++i) r.b[i][f] = bload16(rb[f], (vb[f] + (uint32_t)(c + i) * 64u) | off[i]);
+      for (int f = 0; f < kMtFrags; ++f)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) r.b[j][f] = bload16(rb[f], (vb[f] + (uint32_t)j * row8 + (uint32_t)c * 64u) | ob);
+    }
 #pragma unroll
     for (int i = 0; i < CH; ++i)
 #pragma unroll
@@ -163,9 +175,42 @@ struct MtSrc {
 // lane's scale is byte g of its row's table word for the chunk (cw: the first
 // chunk's table column; a chunk past the window's last column cwl reads zeros
 // and takes the scale of column cwl, a loaded one).
+// The chunk pair of the four fragments (b: MtRegs<., 2>::b) in operand order,
+// bq[i][f] = chunk i of fragment f.  Each fragment has 2 KB of the
+// wavefront's LDS area scr: chunk i at 1024 i, the 16 B of operand lane t at
+// slot t ^ (4i + t/16) ^ 8 (t & 1).  The swizzle keeps the 16 lanes of a
+// write (two rows, all eight pieces) and of a read (16 rows) on 16 distinct
+// 16-byte bank groups.  A wavefront's LDS accesses complete in order, so the
+// area is reused by the next pair without a wait.
+__device__ __forceinline__ void mt_operands(const uint4_t (&b)[2][kMtFrags], uint8_t* scr,
+                                            uint4_t (&bq)[2][kMtFrags]) {
+  const int lane = __lane_id(), rr = lane >> 3, p = lane & 7, i = p >> 2, g = p & 3;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int slot = ((8 * j + rr + 16 * g) ^ p) ^ (8 * (rr & 1));
+#pragma unroll
+    for (int f = 0; f < kMtFrags; ++f)
+      *reinterpret_cast<uint4_t*>(scr + f * 2048 + i * 1024 + slot * 16) = b[j][f];
+  }
+  const int tg = lane >> 4, odd = 8 * (lane & 1);
+#pragma unroll
+  for (int ci = 0; ci < 2; ++ci)
+#pragma unroll
+    for (int f = 0; f < kMtFrags; ++f)
+      bq[ci][f] = *reinterpret_cast<const uint4_t*>(scr + f * 2048 + ci * 1024 +
+                                                    ((lane ^ (4 * ci + tg)) ^ odd) * 16);
+}
+
 template <int PLANES, int CH>
 __device__ __forceinline__ void mt_mma(const MtRegs<PLANES, CH>& r, f4v (&acc)[kMtFrags], const uint32_t* tab,
-                                       int cw, int cwl, int q16, int g) {
+                                       int cw, int cwl, int q16, int g, uint8_t* scr) {
+  uint4_t bq[CH][kMtFrags];
+  if constexpr (CH == 2) {
+    mt_operands(r.b, scr, bq);
+  } else {
+#pragma unroll
+    for (int f = 0; f < kMtFrags; ++f) bq[0][f] = r.b[0][f];
+  }
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int col = min(cw + i, cwl);
@@ -177,7 +222,7 @@ __device__ __forceinline__ void mt_mma(const MtRegs<PLANES, CH>& r, f4v (&acc)[k
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int f = 0; f < kMtFrags; ++f) {
-        const bf16x8_t bw = dq8(r.b[i][f][t], sc[f]);
+        const bf16x8_t bw = dq8(bq[i][f][t], sc[f]);
 #pragma unroll
         for (int p = 0; p < PLANES; ++p)
           acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.a[i][p][t]), bw, acc[f], 0, 0, 0);
@@ -194,7 +239,7 @@ __device__ __forceinline__ void mt_mma(const MtRegs<PLANES, CH>& r, f4v (&acc)[k
 // (table row 16f + r: row r of fragment f).
 template <int CH, int PLANES, typename Tables>
 __device__ __forceinline__ void mt_k_loop(const MtSrc<PLANES>& src, f4v (&acc)[kMtFrags], int cb, int ce,
-                                          uint32_t* tab, Tables tables) {
+                                          uint32_t* tab, uint8_t* scr, Tables tables) {
   static_assert(kMtWin % CH == 0, "whole chunk sets per window");
   const int lane = __lane_id(), q16 = lane & 15, g = lane >> 4;
   for (int cw0 = cb; cw0 < ce; cw0 += kMtWin) {
@@ -209,10 +254,10 @@ __device__ __forceinline__ void mt_k_loop(const MtSrc<PLANES>& src, f4v (&acc)[k
     for (int c = cw0; c < end; c += 2 * CH) {
       src.load(min(c + CH, last), c + CH < end ? end : 0, r1);
       __builtin_amdgcn_sched_barrier(0);  // the next set's loads go out before these MFMAs
-      mt_mma(r0, acc, tab, c - cw0, last - cw0, q16, g);
+      mt_mma(r0, acc, tab, c - cw0, last - cw0, q16, g, scr);
       src.load(min(c + 2 * CH, last), c + 2 * CH < end ? end : 0, r0);
       __builtin_amdgcn_sched_barrier(0);
-      if (c + CH < end) mt_mma(r1, acc, tab, c + CH - cw0, last - cw0, q16, g);
+      if (c + CH < end) mt_mma(r1, acc, tab, c + CH - cw0, last - cw0, q16, g, scr);
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -250,6 +295,7 @@ __global__ __launch_bounds__(kMtThreads, 2) void gateup_mt_kernel(
     uint16_t* __restrict__ hpl, int P) {
   __shared__ MtPlan pl;
   __shared__ uint32_t tabs[4][64 * kMtW];
+  __shared__ __attribute__((aligned(16))) uint8_t mtscr[4][kMtScr];
   pl.build(offsets, E, run);
   const int H = w.H, I = w.I, NB = H / 32, tiles = I / 32, nch = H / 128;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, q16 = lane & 15, g = lane >> 4;
@@ -275,8 +321,9 @@ __global__ __launch_bounds__(kMtThreads, 2) void gateup_mt_kernel(
 #pragma unroll
     for (int f = 0; f < kMtFrags; ++f) {  // fragments 0, 1: gate rows; 2, 3: the same up rows
       src.rb[f] = f < 2 ? gr : ur;
-      src.vb[f] = (uint32_t)(32 * q + 16 * (f & 1) + q16) * wrow + 16u * (uint32_t)g;
+      src.vb[f] = (uint32_t)(32 * q + 16 * (f & 1) + (lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7);
     }
+    src.row8 = 8u * wrow;
     const rsrc_t sgr = make_rsrc(w.sg + (size_t)slot * smat, (uint32_t)smat);
     const rsrc_t sur = make_rsrc(w.su + (size_t)slot * smat, (uint32_t)smat);
     auto tables = [&](int cw0, ScaleRows<32, 64, kMtWin, kMtW> (&ts)[2]) {
@@ -284,7 +331,7 @@ __global__ __launch_bounds__(kMtThreads, 2) void gateup_mt_kernel(
       ts[1].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NB; });
     };
     f4v acc[kMtFrags] = {};
-    mt_k_loop<2>(src, acc, cb, ce, tab, tables);
+    mt_k_loop<2>(src, acc, cb, ce, tab, mtscr[wid], tables);
     __builtin_amdgcn_wave_barrier();
     mt_part_store(reinterpret_cast<float*>(tab), acc, lane);
     __syncthreads();
@@ -344,13 +391,14 @@ __global__ __launch_bounds__(kMtThreads, 2) void down_mt_kernel(
       src.rb[f] = rc;
       src.vb[f] = (uint32_t)(n0 + 16 * f + q16) * wrow + 16u * (uint32_t)g;
     }
+    src.row8 = 0;
     const rsrc_t sdr = make_rsrc(w.sd + (size_t)slot * smat, (uint32_t)smat);
     auto tables = [&](int cw0, ScaleRows<32, 64, kMtWin, kMtW> (&ts)[2]) {
       ts[0].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + r) * NB; });
       ts[1].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + 32 + r) * NB; });
     };
     f4v acc[kMtFrags] = {};
-    mt_k_loop<1>(src, acc, cb, ce, tab, tables);
+    mt_k_loop<1>(src, acc, cb, ce, tab, nullptr, tables);
     __builtin_amdgcn_wave_barrier();
     mt_part_store(reinterpret_cast<float*>(tab), acc, lane);
     __syncthreads();
@@ -423,6 +471,7 @@ __global__ __launch_bounds__(kMtThreads, 2) void inv_gateup_kernel(
     uint16_t* __restrict__ hpl) {
   __shared__ InvRoute rt;
   __shared__ uint32_t tabs[4][64 * kMtW];
+  __shared__ __attribute__((aligned(16))) uint8_t mtscr[4][kMtScr];
   inv_route<NPL>(logits, E, k, e2s, w.num_slots, rt, pub, topk_ids, topk_w);
   const int H = w.H, I = w.I, NB = H / 32, tiles = I / 32, nch = H / 128;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, q16 = lane & 15, g = lane >> 4;
@@ -444,8 +493,9 @@ __global__ __launch_bounds__(kMtThreads, 2) void inv_gateup_kernel(
 #pragma unroll
     for (int f = 0; f < kMtFrags; ++f) {  // fragments 0, 1: gate rows; 2, 3: the same up rows
       src.rb[f] = f < 2 ? gr : ur;
-      src.vb[f] = (uint32_t)(32 * q + 16 * (f & 1) + q16) * wrow + 16u * (uint32_t)g;
+      src.vb[f] = (uint32_t)(32 * q + 16 * (f & 1) + (lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7);
     }
+    src.row8 = 8u * wrow;
     const rsrc_t sgr = make_rsrc(w.sg + (size_t)slot * smat, (uint32_t)smat);
     const rsrc_t sur = make_rsrc(w.su + (size_t)slot * smat, (uint32_t)smat);
     auto tables = [&](int cw0, ScaleRows<32, 64, kMtWin, kMtW> (&ts)[2]) {
@@ -453,7 +503,7 @@ __global__ __launch_bounds__(kMtThreads, 2) void inv_gateup_kernel(
       ts[1].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NB; });
     };
     f4v acc[kMtFrags] = {};
-    mt_k_loop<2>(src, acc, cb, ce, tab, tables);
+    mt_k_loop<2>(src, acc, cb, ce, tab, mtscr[wid], tables);
     __builtin_amdgcn_wave_barrier();
     mt_part_store(reinterpret_cast<float*>(tab), acc, lane);
     __syncthreads();
@@ -509,13 +559,14 @@ __global__ __launch_bounds__(kMtThreads, 2) void inv_down_kernel(int k, ExpertSt
       src.rb[f] = rc;
       src.vb[f] = (uint32_t)(n0 + 16 * f + q16) * wrow + 16u * (uint32_t)g;
     }
+    src.row8 = 0;
     const rsrc_t sdr = make_rsrc(w.sd + (size_t)slot * smat, (uint32_t)smat);
     auto tables = [&](int cw0, ScaleRows<32, 64, kMtWin, kMtW> (&ts)[2]) {
       ts[0].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + r) * NB; });
       ts[1].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + 32 + r) * NB; });
     };
     f4v acc[kMtFrags] = {};
-    mt_k_loop<1>(src, acc, cb, ce, tab, tables);
+    mt_k_loop<1>(src, acc, cb, ce, tab, nullptr, tables);
     __builtin_amdgcn_wave_barrier();
     mt_part_store(reinterpret_cast<float*>(tab), acc, lane);
     __syncthreads();
