@@ -60,7 +60,6 @@ constexpr int kMtWin = 20;        // chunks per scale window (80 blocks; even: w
 constexpr int kMtW = kMtWin + 1;  // words per table row (odd: 16 rows hit 16 banks)
 constexpr int kMtRows = 16;       // bucket rows per unit (the MFMA's M)
 constexpr int kMtFrags = 4;       // 16-row weight fragments per unit
-constexpr int kMtScr = kMtFrags * 2048;  // a wavefront's LDS area: the fragments' chunk pair in operand order
 
 // The bucket list and, per bucket, the prefix of its groups of kMtRows rows: bucket b
 // owns units [tiles * G[b], tiles * G[b+1]), its groups of one column tile
@@ -128,136 +127,201 @@ __device__ __forceinline__ bf16x8_t dq8(uint32_t w, float s) {
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // CH consecutive chunks of one unit (one or two): A (per chunk and plane the
-// lane's 64 B of block 4c+g) and the four B fragments.  CH = 1: b[0][f] is
-// fragment f in operand order (lane: 16 B = block 4c+g of row l%16).  CH = 2:
-// b[j][f] is the j-th 8-row load of fragment f's chunk pair (lane l: row
-// 8j + l/8, bytes 16 (l%8) of the pair), put in operand order by mt_operands.
-template <int PLANES, int CH>
+// lane's 64 B of block 4c+g) and the unit's NF B fragments.  CH = 1 (down):
+// b[0][f] is fragment f in operand order (lane: 16 B = block 4c+g of row
+// l%16).  CH = 2 (gate/up): b[j][f] is the j-th 8-row load of fragment f's
+// chunk pair (lane l: row 8j + l/8, bytes 16 (l%8) of the pair), put in
+// operand order through LDS (mt_stage, mt_fetch).
+template <int PLANES, int CH, int NF>
 struct MtRegs {
   uint4_t a[CH][PLANES][4];  // [chunk][plane][K-step]
-  uint4_t b[CH][kMtFrags];   // CH = 1: [0][fragment]; CH = 2: [load][fragment]
+  uint4_t b[CH][NF];         // CH = 1: [0][fragment]; CH = 2: [load][fragment]
 };
 
-template <int PLANES>
+// A chunk at or past `end` reads as zeros: its offsets get kOob, past every
+// range (real offsets stay below 2^31).
+template <int PLANES, int NF>
 struct MtSrc {
-  rsrc_t ra, rb[kMtFrags];
-  uint32_t va;              // the lane's A row + 64 * g (kOob past the bucket's end)
-  uint32_t plane;           // byte distance of the A planes
-  uint32_t vb[kMtFrags];    // CH = 1: fragment row l%16, + 16 g; CH = 2: fragment row l/8, + 16 (l%8)
-  uint32_t row8;            // CH = 2: bytes from a weight row to the row 8 below
-  // chunks c .. c+CH-1, those at or past `end` read as zeros (every offset past its range)
+  rsrc_t ra, rb[NF];
+  uint32_t va;        // the lane's A row + 64 * g (kOob past the bucket's end)
+  uint32_t plane;     // byte distance of the A planes
+  uint32_t vb[NF];    // CH = 1: fragment row l%16, + 16 g; CH = 2: fragment row l/8, + 16 (l%8)
+  uint32_t row8;      // CH = 2: bytes from a weight row to the row 8 below
+  // A of chunks c .. c+CH-1
   template <int CH>
-  __device__ __forceinline__ void load(int c, int end, MtRegs<PLANES, CH>& r) const {
-    uint32_t off[CH];
+  __device__ __forceinline__ void load_a(int c, int end, MtRegs<PLANES, CH, NF>& r) const {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) off[i] = c + i < end ? 0u : kOob;  // real offsets stay below 2^31
-    if constexpr (CH == 1) {
-#pragma unroll
-      for (int f = 0; f < kMtFrags; ++f) r.b[0][f] = bload16(rb[f], (vb[f] + (uint32_t)c * 64u) | off[0]);
-    } else {
-      const uint32_t ob = off[(__lane_id() >> 2) & 1];  // the lane's 16 B lie in chunk c + (l%8)/4
-#pragma unroll
-      for (int f = 0; f < kMtFrags; ++f)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) r.b[j][f] = bload16(rb[f], (vb[f] + (uint32_t)j * row8 + (uint32_t)c * 64u) | ob);
-    }
-#pragma unroll
-    for (int i = 0; i < CH; ++i)
+    for (int i = 0; i < CH; ++i) {
+      const uint32_t off = c + i < end ? 0u : kOob;
 #pragma unroll
       for (int p = 0; p < PLANES; ++p)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          r.a[i][p][t] = bload16(ra, (va + p * plane + (uint32_t)(c + i) * 256u + 16u * t) | off[i]);
+          r.a[i][p][t] = bload16(ra, (va + p * plane + (uint32_t)(c + i) * 256u + 16u * t) | off);
+    }
+  }
+  // B of chunk c in operand order (CH = 1)
+  __device__ __forceinline__ void load_b1(int c, int end, MtRegs<PLANES, 1, NF>& r) const {
+    const uint32_t off = c < end ? 0u : kOob;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) r.b[0][f] = bload16(rb[f], (vb[f] + (uint32_t)c * 64u) | off);
+  }
+  // B of chunks c, c+1 in 8-row loads (CH = 2); the lane's 16 B lie in chunk c + (l%8)/4
+  __device__ __forceinline__ void load_b2(int c, int end, MtRegs<PLANES, 2, NF>& r) const {
+    const uint32_t ob = c + ((__lane_id() >> 2) & 1) < end ? 0u : kOob;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) r.b[j][f] = bload16(rb[f], (vb[f] + (uint32_t)j * row8 + (uint32_t)c * 64u) | ob);
   }
 };
 
-// The MFMAs of the CH chunks: per chunk 4 K-steps x 4 fragments x PLANES.  The
-// lane's scale is byte g of its row's table word for the chunk (cw: the first
-// chunk's table column; a chunk past the window's last column cwl reads zeros
-// and takes the scale of column cwl, a loaded one).
-// The chunk pair of the four fragments (b: MtRegs<., 2>::b) in operand order,
-// bq[i][f] = chunk i of fragment f.  Each fragment has 2 KB of the
-// wavefront's LDS area scr: chunk i at 1024 i, the 16 B of operand lane t at
-// slot t ^ (4i + t/16) ^ 8 (t & 1).  The swizzle keeps the 16 lanes of a
-// write (two rows, all eight pieces) and of a read (16 rows) on 16 distinct
-// 16-byte bank groups.  A wavefront's LDS accesses complete in order, so the
-// area is reused by the next pair without a wait.
-__device__ __forceinline__ void mt_operands(const uint4_t (&b)[2][kMtFrags], uint8_t* scr,
-                                            uint4_t (&bq)[2][kMtFrags]) {
+// The chunk pair of the NF fragments (b: MtRegs<., 2, NF>::b) is written to
+// the wavefront's LDS area scr (NF * 2 KB) and read back in operand order,
+// chunk by chunk.  Fragment f has 2 KB at 2048 f: chunk i at 1024 i, the 16 B
+// of operand lane t at slot t ^ (4i + t/16) ^ 8 (t & 1).  The swizzle keeps
+// the 16 lanes of a write (two rows, all eight pieces) and of a read (16 rows)
+// on 16 distinct 16-byte bank groups.  A wavefront's LDS accesses complete in
+// order, so the area is reused by the next pair without a wait.
+template <int NF>
+__device__ __forceinline__ void mt_stage(const uint4_t (&b)[2][NF], uint8_t* scr) {
   const int lane = __lane_id(), rr = lane >> 3, p = lane & 7, i = p >> 2, g = p & 3;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int slot = ((8 * j + rr + 16 * g) ^ p) ^ (8 * (rr & 1));
 #pragma unroll
-    for (int f = 0; f < kMtFrags; ++f)
-      *reinterpret_cast<uint4_t*>(scr + f * 2048 + i * 1024 + slot * 16) = b[j][f];
-  }
-  const int tg = lane >> 4, odd = 8 * (lane & 1);
-#pragma unroll
-  for (int ci = 0; ci < 2; ++ci)
-#pragma unroll
-    for (int f = 0; f < kMtFrags; ++f)
-      bq[ci][f] = *reinterpret_cast<const uint4_t*>(scr + f * 2048 + ci * 1024 +
-                                                    ((lane ^ (4 * ci + tg)) ^ odd) * 16);
-}
-
-template <int PLANES, int CH>
-__device__ __forceinline__ void mt_mma(const MtRegs<PLANES, CH>& r, f4v (&acc)[kMtFrags], const uint32_t* tab,
-                                       int cw, int cwl, int q16, int g, uint8_t* scr) {
-  uint4_t bq[CH][kMtFrags];
-  if constexpr (CH == 2) {
-    mt_operands(r.b, scr, bq);
-  } else {
-#pragma unroll
-    for (int f = 0; f < kMtFrags; ++f) bq[0][f] = r.b[0][f];
-  }
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int col = min(cw + i, cwl);
-    float sc[kMtFrags];
-#pragma unroll
-    for (int f = 0; f < kMtFrags; ++f)
-      sc[f] = ue8m0_to_f32((tab[(16 * f + q16) * kMtW + col] >> (8 * g)) & 0xFFu);
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int f = 0; f < kMtFrags; ++f) {
-        const bf16x8_t bw = dq8(bq[i][f][t], sc[f]);
-#pragma unroll
-        for (int p = 0; p < PLANES; ++p)
-          acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.a[i][p][t]), bw, acc[f], 0, 0, 0);
-      }
+    for (int f = 0; f < NF; ++f) *reinterpret_cast<uint4_t*>(scr + f * 2048 + i * 1024 + slot * 16) = b[j][f];
   }
 }
 
-// The chunks [cb, ce) of one unit: windows of kMtWin chunks; in a window the
-// next CH chunks' loads are in flight while CH chunks are multiplied, the two
-// register sets alternating.  A chunk past the window's end reads zeros and
-// is multiplied like the others (a set wholly past the end is skipped); the
-// loads are unconditional and pinned ahead of the MFMAs they overlap.
-// tables(cw0, ts) issues the scale loads of the window starting at chunk cw0
-// (table row 16f + r: row r of fragment f).
-template <int CH, int PLANES, typename Tables>
-__device__ __forceinline__ void mt_k_loop(const MtSrc<PLANES>& src, f4v (&acc)[kMtFrags], int cb, int ce,
-                                          uint32_t* tab, uint8_t* scr, Tables tables) {
-  static_assert(kMtWin % CH == 0, "whole chunk sets per window");
+// chunk ci of the staged pair: bq[f] = fragment f in operand order
+template <int NF>
+__device__ __forceinline__ void mt_fetch(const uint8_t* scr, int ci, uint4_t (&bq)[NF]) {
+  const int lane = __lane_id(), tg = lane >> 4, odd = 8 * (lane & 1);
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+    bq[f] = *reinterpret_cast<const uint4_t*>(scr + f * 2048 + ci * 1024 + ((lane ^ (4 * ci + tg)) ^ odd) * 16);
+}
+
+// The MFMAs of one chunk: 4 K-steps x NF fragments x PLANES, B (bq) in operand
+// order.  The lane's scale is byte g of its row's table word in column col.
+// Every output column's sum depends only on its own fragment.
+template <int PLANES, int NF>
+__device__ __forceinline__ void mt_mma_chunk(const uint4_t (&a)[PLANES][4], const uint4_t (&bq)[NF],
+                                             f4v (&acc)[NF], const uint32_t* tab, int col, int q16, int g) {
+  float sc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) sc[f] = ue8m0_to_f32((tab[(16 * f + q16) * kMtW + col] >> (8 * g)) & 0xFFu);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const bf16x8_t bw = dq8(bq[f][t], sc[f]);
+#pragma unroll
+      for (int p = 0; p < PLANES; ++p)
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[p][t]), bw, acc[f], 0, 0, 0);
+    }
+}
+
+// Scale tables of a unit's window (table row 16 f + r: row r of fragment f).
+// Gate/up: the gate rows' table then the up rows' (8 NF rows each); down: one
+// table of 16 NF rows.
+template <int NF>
+struct MtTabGU {
+  ScaleRows<8 * NF, 64, kMtWin, kMtW> t[2];
+  __device__ __forceinline__ void store(uint32_t* tab, int lane) const {
+    t[0].store(tab, lane);
+    t[1].store(tab + 8 * NF * kMtW, lane);
+  }
+};
+template <int NF>
+struct MtTabDN {
+  ScaleRows<16 * NF, 64, kMtWin, kMtW> t;
+  __device__ __forceinline__ void store(uint32_t* tab, int lane) const { t.store(tab, lane); }
+};
+
+// The chunks [cb, ce) of one unit (down): windows of kMtWin chunks; in a
+// window two register sets of one chunk alternate, the next chunk's loads in
+// flight while one is multiplied.  A chunk past the window's end is skipped;
+// the loads are unconditional (past the end they read zeros) and pinned ahead
+// of the MFMAs they overlap.  tables(cw0, ts) issues the scale loads of the
+// window starting at chunk cw0.
+template <typename TS, int PLANES, int NF, typename Tables>
+__device__ __forceinline__ void mt_k_loop(const MtSrc<PLANES, NF>& src, f4v (&acc)[NF], int cb, int ce,
+                                          uint32_t* tab, Tables tables) {
   const int lane = __lane_id(), q16 = lane & 15, g = lane >> 4;
   for (int cw0 = cb; cw0 < ce; cw0 += kMtWin) {
     const int end = min(cw0 + kMtWin, ce), last = end - 1;
-    ScaleRows<32, 64, kMtWin, kMtW> ts[2];
+    TS ts;
     tables(cw0, ts);
-    MtRegs<PLANES, CH> r0, r1;
-    src.load(cw0, end, r0);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) ts[t].store(tab + 32 * t * kMtW, lane);
+    MtRegs<PLANES, 1, NF> r[2];
+    auto load = [&](int c, MtRegs<PLANES, 1, NF>& dst) {
+      src.load_b1(min(c, last), c < end ? end : 0, dst);
+      src.template load_a<1>(min(c, last), c < end ? end : 0, dst);
+    };
+    load(cw0, r[0]);
+    ts.store(tab, lane);
     __builtin_amdgcn_wave_barrier();  // a wavefront's LDS accesses complete in order
-    for (int c = cw0; c < end; c += 2 * CH) {
-      src.load(min(c + CH, last), c + CH < end ? end : 0, r1);
-      __builtin_amdgcn_sched_barrier(0);  // the next set's loads go out before these MFMAs
-      mt_mma(r0, acc, tab, c - cw0, last - cw0, q16, g, scr);
-      src.load(min(c + 2 * CH, last), c + 2 * CH < end ? end : 0, r0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (c + CH < end) mt_mma(r1, acc, tab, c + CH - cw0, last - cw0, q16, g, scr);
+    for (int c0 = cw0; c0 < end; c0 += 2) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = c0 + j;
+        load(c + 1, r[j ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads go out before these MFMAs
+        if (j == 0 || c < end) mt_mma_chunk(r[j].a[0], r[j].b[0], acc, tab, c - cw0, q16, g);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// The chunks [cb, ce) of one unit in chunk pairs (gate/up), B two pairs ahead
+// and A one pair ahead: sets n = chunks cw0 + 2n, +1 of a window.  Issue
+// order: A(0), B(0), B(1), then per set n, once B(n) is staged in LDS:
+// A(n+1), B(n+2).  Loads complete in order, so set n waits for A(n) and B(n)
+// only, with B(n+1) still in flight, and the MFMAs of set n overlap two sets'
+// weight loads.  Every load and staging is unconditional (past the window's
+// end they read zeros) so each wait covers one set; a set wholly past the end
+// is not multiplied, the zero second chunk of a set that straddles it is.
+template <typename TS, int PLANES, int NF, typename Tables>
+__device__ __forceinline__ void mt_k_loop_deep(const MtSrc<PLANES, NF>& src, f4v (&acc)[NF], int cb, int ce,
+                                               uint32_t* tab, uint8_t* scr, Tables tables) {
+  const int lane = __lane_id(), q16 = lane & 15, g = lane >> 4;
+  for (int cw0 = cb; cw0 < ce; cw0 += kMtWin) {
+    const int end = min(cw0 + kMtWin, ce), last = end - 1;
+    TS ts;
+    tables(cw0, ts);
+    MtRegs<PLANES, 2, NF> r[2];  // r[i].a: A of set n (n % 2 == i); r[i].b: raw B of set n, then n + 2
+    auto load_a = [&](int n, MtRegs<PLANES, 2, NF>& dst) {
+      const int c = cw0 + 2 * n;
+      src.template load_a<2>(min(c, last), c < end ? end : 0, dst);
+    };
+    auto load_b = [&](int n, MtRegs<PLANES, 2, NF>& dst) {
+      const int c = cw0 + 2 * n;
+      src.load_b2(min(c, last), c < end ? end : 0, dst);
+    };
+    load_a(0, r[0]);
+    load_b(0, r[0]);
+    load_b(1, r[1]);
+    ts.store(tab, lane);
+    __builtin_amdgcn_wave_barrier();  // a wavefront's LDS accesses complete in order
+    for (int n0 = 0; cw0 + 2 * n0 < end; n0 += 2) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + j, c = cw0 + 2 * n;
+        mt_stage<NF>(r[j].b, scr);
+        load_a(n + 1, r[j ^ 1]);
+        load_b(n + 2, r[j]);
+        __builtin_amdgcn_sched_barrier(0);  // the next loads go out before these MFMAs
+        if (j == 0 || c < end) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {  // a chunk past the window's end takes column `last`'s scales
+            uint4_t bq[NF];
+            mt_fetch<NF>(scr, i, bq);
+            mt_mma_chunk(r[j].a[i], bq, acc, tab, min(c + i, last) - cw0, q16, g);
+          }
+        }
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -268,15 +332,17 @@ __device__ __forceinline__ void mt_k_loop(const MtSrc<PLANES>& src, f4v (&acc)[k
 // added in wavefront order, so every output is the same fp32 expression
 // whatever the batch around it.  part: the wavefront's own table area, free
 // once its K loop is done.
-__device__ __forceinline__ void mt_part_store(float* part, const f4v (&acc)[kMtFrags], int lane) {
+template <int NF>
+__device__ __forceinline__ void mt_part_store(float* part, const f4v (&acc)[NF], int lane) {
 #pragma unroll
-  for (int f = 0; f < kMtFrags; ++f)
+  for (int f = 0; f < NF; ++f)
 #pragma unroll
     for (int v = 0; v < 4; ++v) part[(4 * f + v) * 64 + lane] = acc[f][v];
 }
 
 // fragment f, accumulator v of the whole unit: partial 0 + 1 + 2 + 3
-__device__ __forceinline__ float mt_part_sum(const uint32_t (*tabs)[64 * kMtW], int f, int v, int lane) {
+template <int NF>
+__device__ __forceinline__ float mt_part_sum(const uint32_t (*tabs)[16 * NF * kMtW], int f, int v, int lane) {
   const int i = (4 * f + v) * 64 + lane;
   float s = __uint_as_float(tabs[0][i]);
 #pragma unroll
@@ -293,11 +359,12 @@ __global__ __launch_bounds__(kMtThreads, 2) void gateup_mt_kernel(
     const uint16_t* __restrict__ x, uint32_t x_bytes, int k, int E, ExpertStore w, const int32_t* __restrict__ e2s,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, const uint8_t* __restrict__ run,
     uint16_t* __restrict__ hpl, int P) {
+  constexpr int NF = kMtFrags, NG = NF / 2;
   __shared__ MtPlan pl;
-  __shared__ uint32_t tabs[4][64 * kMtW];
-  __shared__ __attribute__((aligned(16))) uint8_t mtscr[4][kMtScr];
+  __shared__ uint32_t tabs[4][16 * NF * kMtW];
+  __shared__ __attribute__((aligned(16))) uint8_t mtscr[4][NF * 2048];
   pl.build(offsets, E, run);
-  const int H = w.H, I = w.I, NB = H / 32, tiles = I / 32, nch = H / 128;
+  const int H = w.H, I = w.I, NB = H / 32, tiles = I / (8 * NF), nch = H / 128;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, q16 = lane & 15, g = lane >> 4;
   const int cb = wid * nch / 4, ce = (wid + 1) * nch / 4;
   const uint32_t wrow = (uint32_t)H / 2u;
@@ -312,40 +379,40 @@ __global__ __launch_bounds__(kMtThreads, 2) void gateup_mt_kernel(
     if (slot < 0 || slot >= w.num_slots) continue;  // the down kernel writes zero rows
     const int rr = kMtRows * mg + q16;
     const int tok = rr < cnt ? sorted_pair[row0 + rr] / k : -1;
-    MtSrc<1> src;
+    MtSrc<1, NF> src;
     src.ra = make_rsrc(x, x_bytes);
     src.va = tok >= 0 ? (uint32_t)tok * (uint32_t)H * 2u + 64u * g : kOob;
     src.plane = 0;
     const rsrc_t gr = make_rsrc(w.wg + (size_t)slot * mat, (uint32_t)mat);
     const rsrc_t ur = make_rsrc(w.wu + (size_t)slot * mat, (uint32_t)mat);
 #pragma unroll
-    for (int f = 0; f < kMtFrags; ++f) {  // fragments 0, 1: gate rows; 2, 3: the same up rows
-      src.rb[f] = f < 2 ? gr : ur;
-      src.vb[f] = (uint32_t)(32 * q + 16 * (f & 1) + (lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7);
+    for (int f = 0; f < NF; ++f) {  // fragments 0 .. NG-1: gate rows; NG .. NF-1: the same up rows
+      src.rb[f] = f < NG ? gr : ur;
+      src.vb[f] = (uint32_t)(8 * NF * q + 16 * (f % NG) + (lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7);
     }
     src.row8 = 8u * wrow;
     const rsrc_t sgr = make_rsrc(w.sg + (size_t)slot * smat, (uint32_t)smat);
     const rsrc_t sur = make_rsrc(w.su + (size_t)slot * smat, (uint32_t)smat);
-    auto tables = [&](int cw0, ScaleRows<32, 64, kMtWin, kMtW> (&ts)[2]) {
-      ts[0].issue(sgr, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NB; });
-      ts[1].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NB; });
+    auto tables = [&](int cw0, MtTabGU<NF>& ts) {
+      ts.t[0].issue(sgr, cw0, lane, [&](int r) { return (uint32_t)(8 * NF * q + r) * NB; });
+      ts.t[1].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(8 * NF * q + r) * NB; });
     };
-    f4v acc[kMtFrags] = {};
-    mt_k_loop<2>(src, acc, cb, ce, tab, mtscr[wid], tables);
+    f4v acc[NF] = {};
+    mt_k_loop_deep<MtTabGU<NF>>(src, acc, cb, ce, tab, mtscr[wid], tables);
     __builtin_amdgcn_wave_barrier();
-    mt_part_store(reinterpret_cast<float*>(tab), acc, lane);
+    mt_part_store<NF>(reinterpret_cast<float*>(tab), acc, lane);
     __syncthreads();
-    // wavefront f < 2: h columns 32q + 16f + q16 (gate fragment f, up fragment f + 2);
+    // wavefront f < NG: h columns 8 NF q + 16f + q16 (gate fragment f, up fragment f + NG);
     // accumulator v: bucket row 16mg + 4g + v
-    if (wid < 2) {
+    if (wid < NG) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = kMtRows * mg + 4 * g + v;
-        const float gv = mt_part_sum(tabs, wid, v, lane), uv = mt_part_sum(tabs, wid + 2, v, lane);
+        const float gv = mt_part_sum<NF>(tabs, wid, v, lane), uv = mt_part_sum<NF>(tabs, wid + NG, v, lane);
         if (row < cnt) {
           const float hv = swiglu_f32(gv, uv);
           const uint16_t hi = f32_to_bf16_rne(hv);
-          const size_t o = (size_t)(row0 + row) * I + 32 * q + 16 * wid + q16;
+          const size_t o = (size_t)(row0 + row) * I + 8 * NF * q + 16 * wid + q16;
           hpl[o] = hi;
           hpl[lo_plane + o] = bf16_lo_part(hv, hi);
         }
@@ -359,10 +426,11 @@ __global__ __launch_bounds__(kMtThreads, 2) void down_mt_kernel(
     const uint16_t* __restrict__ hpl, int P, int E, ExpertStore w, const int32_t* __restrict__ e2s,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair, const uint8_t* __restrict__ run,
     float* __restrict__ y) {
+  constexpr int NF = kMtFrags;
   __shared__ MtPlan pl;
-  __shared__ uint32_t tabs[4][64 * kMtW];
+  __shared__ uint32_t tabs[4][16 * NF * kMtW];
   pl.build(offsets, E, run);
-  const int H = w.H, I = w.I, NB = I / 32, tiles = H / 64, nch = I / 128;
+  const int H = w.H, I = w.I, NB = I / 32, tiles = H / (16 * NF), nch = I / 128;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, q16 = lane & 15, g = lane >> 4;
   const int cb = wid * nch / 4, ce = (wid + 1) * nch / 4;
   const uint32_t wrow = (uint32_t)I / 2u;
@@ -374,40 +442,41 @@ __global__ __launch_bounds__(kMtThreads, 2) void down_mt_kernel(
     pl.locate(u, tiles, b, mg, q);
     const int expert = pl.bk.expert[b], row0 = pl.bk.row0[b], cnt = pl.bk.cnt[b];
     const int slot = e2s ? e2s[expert] : expert;
-    const int n0 = 64 * q;
+    const int n0 = 16 * NF * q;
     if (slot < 0 || slot >= w.num_slots) {  // no stored expert: its rows are zero
       for (int r = kMtRows * mg + wid; r < min(cnt, kMtRows * (mg + 1)); r += 4)
-        y[(size_t)sorted_pair[row0 + r] * H + n0 + lane] = 0.f;
+        for (int c = lane; c < 16 * NF; c += 64) y[(size_t)sorted_pair[row0 + r] * H + n0 + c] = 0.f;
       continue;
     }
     const int rr = kMtRows * mg + q16;
-    MtSrc<2> src;
+    MtSrc<2, NF> src;
     src.ra = make_rsrc(hpl, (uint32_t)((size_t)P * I * 4));
     src.va = rr < cnt ? (uint32_t)(row0 + rr) * (uint32_t)I * 2u + 64u * g : kOob;
     src.plane = (uint32_t)((size_t)P * I * 2);
     const rsrc_t rc = make_rsrc(w.wd + (size_t)slot * mat, (uint32_t)mat);
 #pragma unroll
-    for (int f = 0; f < kMtFrags; ++f) {
+    for (int f = 0; f < NF; ++f) {
       src.rb[f] = rc;
       src.vb[f] = (uint32_t)(n0 + 16 * f + q16) * wrow + 16u * (uint32_t)g;
     }
     src.row8 = 0;
     const rsrc_t sdr = make_rsrc(w.sd + (size_t)slot * smat, (uint32_t)smat);
-    auto tables = [&](int cw0, ScaleRows<32, 64, kMtWin, kMtW> (&ts)[2]) {
-      ts[0].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + r) * NB; });
-      ts[1].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + 32 + r) * NB; });
+    auto tables = [&](int cw0, MtTabDN<NF>& ts) {
+      ts.t.issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + r) * NB; });
     };
-    f4v acc[kMtFrags] = {};
-    mt_k_loop<1>(src, acc, cb, ce, tab, nullptr, tables);
+    f4v acc[NF] = {};
+    mt_k_loop<MtTabDN<NF>>(src, acc, cb, ce, tab, tables);
     __builtin_amdgcn_wave_barrier();
-    mt_part_store(reinterpret_cast<float*>(tab), acc, lane);
+    mt_part_store<NF>(reinterpret_cast<float*>(tab), acc, lane);
     __syncthreads();
-    // wavefront f: output columns n0 + 16f + q16; accumulator v: bucket row 16mg + 4g + v
+    // fragment f (wavefront f % 4): output columns n0 + 16f + q16; accumulator v: bucket row 16mg + 4g + v
+    for (int f = wid; f < NF; f += 4) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = kMtRows * mg + 4 * g + v;
-      const float yv = mt_part_sum(tabs, wid, v, lane);
-      if (row < cnt) y[(size_t)sorted_pair[row0 + row] * H + n0 + 16 * wid + q16] = yv;
+      for (int v = 0; v < 4; ++v) {
+        const int row = kMtRows * mg + 4 * g + v;
+        const float yv = mt_part_sum<NF>(tabs, f, v, lane);
+        if (row < cnt) y[(size_t)sorted_pair[row0 + row] * H + n0 + 16 * f + q16] = yv;
+      }
     }
     __syncthreads();
   }
@@ -469,11 +538,12 @@ __global__ __launch_bounds__(kMtThreads, 2) void inv_gateup_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ x, int E, int k, const int32_t* __restrict__ e2s,
     ExpertStore w, InvRoute* __restrict__ pub, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
     uint16_t* __restrict__ hpl) {
+  constexpr int NF = kMtFrags, NG = NF / 2;
   __shared__ InvRoute rt;
-  __shared__ uint32_t tabs[4][64 * kMtW];
-  __shared__ __attribute__((aligned(16))) uint8_t mtscr[4][kMtScr];
+  __shared__ uint32_t tabs[4][16 * NF * kMtW];
+  __shared__ __attribute__((aligned(16))) uint8_t mtscr[4][NF * 2048];
   inv_route<NPL>(logits, E, k, e2s, w.num_slots, rt, pub, topk_ids, topk_w);
-  const int H = w.H, I = w.I, NB = H / 32, tiles = I / 32, nch = H / 128;
+  const int H = w.H, I = w.I, NB = H / 32, tiles = I / (8 * NF), nch = H / 128;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, q16 = lane & 15, g = lane >> 4;
   const int cb = wid * nch / 4, ce = (wid + 1) * nch / 4;
   const uint32_t wrow = (uint32_t)H / 2u;
@@ -484,35 +554,35 @@ __global__ __launch_bounds__(kMtThreads, 2) void inv_gateup_kernel(
     const int b = u / tiles, q = u - b * tiles;
     const int slot = rt.slot[b];
     if (slot < 0) continue;  // the down kernel writes zero rows
-    MtSrc<1> src;
+    MtSrc<1, NF> src;
     src.ra = make_rsrc(x, (uint32_t)H * 2u);
     src.va = q16 == 0 ? 64u * g : kOob;
     src.plane = 0;
     const rsrc_t gr = make_rsrc(w.wg + (size_t)slot * mat, (uint32_t)mat);
     const rsrc_t ur = make_rsrc(w.wu + (size_t)slot * mat, (uint32_t)mat);
 #pragma unroll
-    for (int f = 0; f < kMtFrags; ++f) {  // fragments 0, 1: gate rows; 2, 3: the same up rows
-      src.rb[f] = f < 2 ? gr : ur;
-      src.vb[f] = (uint32_t)(32 * q + 16 * (f & 1) + (lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7);
+    for (int f = 0; f < NF; ++f) {  // fragments 0 .. NG-1: gate rows; NG .. NF-1: the same up rows
+      src.rb[f] = f < NG ? gr : ur;
+      src.vb[f] = (uint32_t)(8 * NF * q + 16 * (f % NG) + (lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7);
     }
     src.row8 = 8u * wrow;
     const rsrc_t sgr = make_rsrc(w.sg + (size_t)slot * smat, (uint32_t)smat);
     const rsrc_t sur = make_rsrc(w.su + (size_t)slot * smat, (uint32_t)smat);
-    auto tables = [&](int cw0, ScaleRows<32, 64, kMtWin, kMtW> (&ts)[2]) {
-      ts[0].issue(sgr, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NB; });
-      ts[1].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NB; });
+    auto tables = [&](int cw0, MtTabGU<NF>& ts) {
+      ts.t[0].issue(sgr, cw0, lane, [&](int r) { return (uint32_t)(8 * NF * q + r) * NB; });
+      ts.t[1].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(8 * NF * q + r) * NB; });
     };
-    f4v acc[kMtFrags] = {};
-    mt_k_loop<2>(src, acc, cb, ce, tab, mtscr[wid], tables);
+    f4v acc[NF] = {};
+    mt_k_loop_deep<MtTabGU<NF>>(src, acc, cb, ce, tab, mtscr[wid], tables);
     __builtin_amdgcn_wave_barrier();
-    mt_part_store(reinterpret_cast<float*>(tab), acc, lane);
+    mt_part_store<NF>(reinterpret_cast<float*>(tab), acc, lane);
     __syncthreads();
-    // wavefront f < 2: h columns 32q + 16f + q16; the token is accumulator 0 of lanes 0-15
-    if (wid < 2 && g == 0) {
-      const float gv = mt_part_sum(tabs, wid, 0, lane), uv = mt_part_sum(tabs, wid + 2, 0, lane);
+    // wavefront f < NG: h columns 8 NF q + 16f + q16; the token is accumulator 0 of lanes 0-15
+    if (wid < NG && g == 0) {
+      const float gv = mt_part_sum<NF>(tabs, wid, 0, lane), uv = mt_part_sum<NF>(tabs, wid + NG, 0, lane);
       const float hv = swiglu_f32(gv, uv);
       const uint16_t hi = f32_to_bf16_rne(hv);
-      const size_t o = (size_t)b * I + 32 * q + 16 * wid + q16;
+      const size_t o = (size_t)b * I + 8 * NF * q + 16 * wid + q16;
       hpl[o] = hi;
       hpl[lo_plane + o] = bf16_lo_part(hv, hi);
     }
@@ -520,21 +590,22 @@ __global__ __launch_bounds__(kMtThreads, 2) void inv_gateup_kernel(
   }
 }
 
-// down_mt_kernel for the one routed token: unit u = (bucket u / tiles, 64
+// down_mt_kernel for the one routed token: unit u = (bucket u / tiles, 16 NF
 // output columns u % tiles); y_pair row = the bucket's routing slot.
 __global__ __launch_bounds__(kMtThreads, 2) void inv_down_kernel(int k, ExpertStore w,
                                                                  const InvRoute* __restrict__ pub,
                                                                  const uint16_t* __restrict__ hpl,
                                                                  float* __restrict__ y) {
+  constexpr int NF = kMtFrags;
   __shared__ InvRoute rt;
-  __shared__ uint32_t tabs[4][64 * kMtW];
+  __shared__ uint32_t tabs[4][16 * NF * kMtW];
   if (threadIdx.x < kMaxTopK) {
     rt.expert[threadIdx.x] = pub->expert[threadIdx.x];
     rt.slot[threadIdx.x] = pub->slot[threadIdx.x];
     rt.pair[threadIdx.x] = pub->pair[threadIdx.x];
   }
   __syncthreads();
-  const int H = w.H, I = w.I, NB = I / 32, tiles = H / 64, nch = I / 128;
+  const int H = w.H, I = w.I, NB = I / 32, tiles = H / (16 * NF), nch = I / 128;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, q16 = lane & 15, g = lane >> 4;
   const int cb = wid * nch / 4, ce = (wid + 1) * nch / 4;
   const uint32_t wrow = (uint32_t)I / 2u;
@@ -543,35 +614,36 @@ __global__ __launch_bounds__(kMtThreads, 2) void inv_down_kernel(int k, ExpertSt
   uint32_t* tab = tabs[wid];
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
     const int b = u / tiles, q = u - b * tiles;
-    const int slot = rt.slot[b], n0 = 64 * q;
+    const int slot = rt.slot[b], n0 = 16 * NF * q;
     float* yrow = y + (size_t)rt.pair[b] * H;
     if (slot < 0) {  // no stored expert: its row is zero
-      if (wid == 0) yrow[n0 + lane] = 0.f;
+      if (wid == 0)
+        for (int c = lane; c < 16 * NF; c += 64) yrow[n0 + c] = 0.f;
       continue;
     }
-    MtSrc<2> src;
+    MtSrc<2, NF> src;
     src.ra = make_rsrc(hpl, (uint32_t)((size_t)k * I * 4));
     src.va = q16 == 0 ? (uint32_t)b * (uint32_t)I * 2u + 64u * g : kOob;
     src.plane = (uint32_t)((size_t)k * I * 2);
     const rsrc_t rc = make_rsrc(w.wd + (size_t)slot * mat, (uint32_t)mat);
 #pragma unroll
-    for (int f = 0; f < kMtFrags; ++f) {
+    for (int f = 0; f < NF; ++f) {
       src.rb[f] = rc;
       src.vb[f] = (uint32_t)(n0 + 16 * f + q16) * wrow + 16u * (uint32_t)g;
     }
     src.row8 = 0;
     const rsrc_t sdr = make_rsrc(w.sd + (size_t)slot * smat, (uint32_t)smat);
-    auto tables = [&](int cw0, ScaleRows<32, 64, kMtWin, kMtW> (&ts)[2]) {
-      ts[0].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + r) * NB; });
-      ts[1].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + 32 + r) * NB; });
+    auto tables = [&](int cw0, MtTabDN<NF>& ts) {
+      ts.t.issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + r) * NB; });
     };
-    f4v acc[kMtFrags] = {};
-    mt_k_loop<1>(src, acc, cb, ce, tab, nullptr, tables);
+    f4v acc[NF] = {};
+    mt_k_loop<MtTabDN<NF>>(src, acc, cb, ce, tab, tables);
     __builtin_amdgcn_wave_barrier();
-    mt_part_store(reinterpret_cast<float*>(tab), acc, lane);
+    mt_part_store<NF>(reinterpret_cast<float*>(tab), acc, lane);
     __syncthreads();
-    // wavefront f: output columns n0 + 16f + q16; the token is accumulator 0 of lanes 0-15
-    if (g == 0) yrow[n0 + 16 * wid + q16] = mt_part_sum(tabs, wid, 0, lane);
+    // fragment f (wavefront f % 4): output columns n0 + 16f + q16; the token is accumulator 0 of lanes 0-15
+    if (g == 0)
+      for (int f = wid; f < NF; f += 4) yrow[n0 + 16 * f + q16] = mt_part_sum<NF>(tabs, f, 0, lane);
     __syncthreads();
   }
 }
@@ -590,7 +662,7 @@ hipError_t launch_invariant_layer(const float* logits, const uint16_t* x, int E,
   float* y = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + 256 +
                                       (((size_t)k * w.I * 4 + 255) & ~(size_t)255));
   const int npl = (E + 63) / 64;
-  const dim3 g1(min(k * (w.I / 32), kMtGridGU)), b1(kMtThreads);
+  const dim3 g1(min(k * (w.I / (8 * kMtFrags)), kMtGridGU)), b1(kMtThreads);
 #define MOE_INV_GU(NP) \
   hipLaunchKernelGGL(inv_gateup_kernel<NP>, g1, b1, 0, s, logits, x, E, k, e2s, w, pub, topk_ids, topk_w, hpl)
   if (npl <= 1) MOE_INV_GU(1);
@@ -601,8 +673,8 @@ hipError_t launch_invariant_layer(const float* logits, const uint16_t* x, int E,
 #undef MOE_INV_GU
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(inv_down_kernel, dim3(min(k * (w.H / 64), kMtGridDN)), dim3(kMtThreads), 0, s, k, w, pub, hpl,
-                     y);
+  hipLaunchKernelGGL(inv_down_kernel, dim3(min(k * (w.H / (16 * kMtFrags)), kMtGridDN)), dim3(kMtThreads), 0, s, k,
+                     w, pub, hpl, y);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_combine(y, topk_w, 1, k, w.H, residual, bf16_out, out, s);
