@@ -17,11 +17,10 @@
 //                 h = silu(g)*u, h -> MXFP6 into hq/hs (sorted-row order)
 //   P2  down:     per tile: y = W_down.h (MFMA, fp32) -> y_pair row p
 //
-// A GEMM tile is 128 bucket rows x 256 weight rows over all of K, in chunks of
-// 256 (eight 32-blocks, four MFMA K-steps).  The weights, the large operand,
-// stream from memory straight into the registers of the one wavefront that
-// uses them; the activations are staged once per chunk through LDS and read
-// by all four wavefronts.  Workgroups are persistent: the tile list (bucket,
+// Buckets of more than 32 rows run as GEMM tiles of 128 bucket rows x 512
+// weight rows over all of K (the grouped GEMM core below); smaller buckets,
+// whose experts are read once for a handful of rows, as a weight stream (the
+// streaming path).  The tile workgroups are persistent: the tile list (bucket,
 // weight tile, row tile -- row tiles of one weight tile adjacent, so they
 // share that weight tile in L2) is split into eight contiguous ranges, one
 // per XCD.
@@ -139,40 +138,66 @@ __global__ __launch_bounds__(kPT) void quant_x_kernel(const uint16_t* __restrict
   xs[g] = (uint8_t)sb;
 }
 
-// The token-major blocks copied into the sorted chunk-major layout: one
-// thread per (chunk c, sorted row p) reads its token's 96 B and scale word of
-// the chunk and writes the two 48-byte records (consecutive threads write
-// consecutive records) and the chunk's scale word.  Only the rows that the
-// bucketing filled are read: sorted rows at or past offsets[E] (pairs whose
-// expert id was out of range are in no bucket) hold no pair index, and a
-// pair index outside [0, T*k) is skipped as well.
+// The token-major blocks copied into the sorted chunk-major layout.  One
+// wavefront per (chunk c, 64 consecutive sorted rows): each lane reads its
+// row's 96 B of the chunk (the four blocks of its token) into the wavefront's
+// LDS area as the row's two 48-byte records, then the wavefront writes each
+// K-half's 64 records, 3 KB contiguous in xq, with three 16-byte stores per
+// lane (every store instruction one contiguous 1 KB), and the chunk's scale
+// words.  Only the rows that the bucketing filled are written: sorted rows at
+// or past offsets[E] (pairs whose expert id was out of range are in no
+// bucket) hold no pair index, and a pair index outside [0, T*k) is skipped
+// as well.
 __global__ __launch_bounds__(kPT) void sort_x_kernel(const uint8_t* __restrict__ xq_t,
                                                      const uint8_t* __restrict__ xs_t, int H, int k, int P,
                                                      const int32_t* __restrict__ offsets, int E,
                                                      const int32_t* __restrict__ sorted_pair,
                                                      uint8_t* __restrict__ xq, uint32_t* __restrict__ xs) {
-  const int g = blockIdx.x * kPT + threadIdx.x;
-  const int nch = H / 128;
-  if (g >= P * nch) return;
-  const int c = g / P, p = g - c * P;
-  if (p >= offsets[E]) return;
-  const int pair = sorted_pair[p];
-  if (pair < 0 || pair >= P) return;
-  const size_t t = (size_t)(pair / k);
-  const uint2* src = reinterpret_cast<const uint2*>(xq_t + (t * (H / 32) + 4 * c) * 24);
-  uint2 w[12];  // block b of the chunk = w[3b .. 3b+2]
+  __shared__ __attribute__((aligned(16))) uint8_t rec[kPT / 64][2][64 * 48];
+  __shared__ uint8_t ok[kPT / 64][64];
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nch = H / 128, ngrp = (P + 63) / 64, gw = blockIdx.x * (kPT / 64) + wid;
+  if (gw >= nch * ngrp) return;
+  const int c = gw / ngrp, p0 = (gw - c * ngrp) * 64, p = p0 + lane, nvalid = offsets[E];
+  if (p0 >= nvalid) return;
+  const int pair = p < nvalid ? sorted_pair[p] : -1;
+  const bool valid = pair >= 0 && pair < P;
+  const size_t t = valid ? (size_t)(pair / k) : 0;
+  uint32_t u[24] = {};  // block b of the chunk = u[6b .. 6b+5]
+  if (valid) {
+    const uint4* src = reinterpret_cast<const uint4*>(xq_t + (t * (H / 32) + 4 * c) * 24);
 #pragma unroll
-  for (int i = 0; i < 12; ++i) w[i] = src[i];
+    for (int i = 0; i < 6; ++i) {
+      const uint4 v = src[i];
+      u[4 * i] = v.x, u[4 * i + 1] = v.y, u[4 * i + 2] = v.z, u[4 * i + 3] = v.w;
+    }
+    xs[(size_t)c * P + p] = *reinterpret_cast<const uint32_t*>(xs_t + t * (H / 32) + 4 * c);
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {  // record of K-half h: block h, then block 2+h
-    uint2* dst = reinterpret_cast<uint2*>(xq + q6_offset(p, 4 * c + h, P));
+    uint32_t* r = reinterpret_cast<uint32_t*>(rec[wid][h] + lane * 48);
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      dst[i] = w[3 * h + i];
-      dst[3 + i] = w[3 * (2 + h) + i];
+    for (int i = 0; i < 6; ++i) {
+      r[i] = u[6 * h + i];
+      r[6 + i] = u[6 * (2 + h) + i];
     }
   }
-  xs[(size_t)c * P + p] = *reinterpret_cast<const uint32_t*>(xs_t + t * (H / 32) + 4 * c);
+  ok[wid][lane] = valid ? 1 : 0;
+  // other lanes' records are read next: wavefront-scope fences keep the
+  // compiler's order (a wavefront's LDS accesses complete in order)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint8_t* dst = xq + ((size_t)(2 * c + h) * P + p0) * 48;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int off = 1024 * j + 16 * lane, r = off / 48;  // a 16-byte piece lies in one record
+      if (p0 + r < nvalid && ok[wid][r])
+        *reinterpret_cast<uint4*>(dst + off) = *reinterpret_cast<const uint4*>(rec[wid][h] + off);
+    }
+  }
 }
 
 // ---- tile plan -----------------------------------------------------------------
@@ -650,9 +675,10 @@ __device__ __forceinline__ float swiglu_fast(float g, float u) {
 // spread thinly over the routed experts) is a weight stream, not a GEMM: its
 // expert is read once for a handful of rows.  One wavefront per (bucket, 32
 // weight rows of each of two matrices): its A fragment (the bucket's rows,
-// rows past the end read as zeros) and its two B fragments come straight from
-// memory into registers in MFMA order, in batches of four K-steps with the next
-// batch in flight, and many wavefronts per CU keep the HBM stream full.
+// rows past the end read as zeros) comes from memory into registers in MFMA
+// order and its two B fragments in 8-row loads, in batches of four K-steps
+// with the next batch in flight, and many wavefronts per CU keep the HBM
+// stream full.
 
 
 // Four K-steps (two 128-K chunks) of one wavefront: A block 2s+h of row r32
@@ -1110,11 +1136,11 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
                                                align256(kMaxExperts * sizeof(SkBucket)));
   uint8_t* xq_t = reinterpret_cast<uint8_t*>(counts) + 256;  // token-major x blocks, then their scales
   uint8_t* xs_t = xq_t + align256((size_t)T * H / 32 * 24);
-  const int nblk = T * (H / 32), nq = (int)P * (H / 128);
+  const int nblk = T * (H / 32), nsw = (H / 128) * (int)((P + 63) / 64);  // sort_x: wavefronts
   hipLaunchKernelGGL(quant_x_kernel, dim3((nblk + kPT - 1) / kPT), dim3(kPT), 0, s, x, nblk, xq_t, xs_t);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(sort_x_kernel, dim3((nq + kPT - 1) / kPT), dim3(kPT), 0, s, xq_t, xs_t, H, k, (int)P,
+  hipLaunchKernelGGL(sort_x_kernel, dim3((nsw + kPT / 64 - 1) / (kPT / 64)), dim3(kPT), 0, s, xq_t, xs_t, H, k, (int)P,
                      offsets, E, sorted_pair, xq, reinterpret_cast<uint32_t*>(xs));
   err = hipGetLastError();
   if (err != hipSuccess) return err;
