@@ -511,10 +511,11 @@ def verify_section(args, torch, m, gd, gi):
                 replays=replays, clocks=dict(before=clock_before, after=clock_after))
 
 
-def read_ceiling(torch, gd) -> dict:
+def read_ceiling(torch, gd, lds: bool = False) -> dict:
     """The measured streaming-read ceiling: the harness's probe kernel (every
-    wavefront 16 KiB contiguous per step, all loads in flight) over 4 GiB
-    resident in HBM, HIP events on its stream."""
+    wavefront 16 KiB contiguous per step, all loads in flight; with lds the
+    loads are copies into LDS by the buffer unit) over 4 GiB resident in HBM,
+    HIP events on its stream."""
     n = 4 << 30
     a = torch.ones(n, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -522,7 +523,8 @@ def read_ceiling(torch, gd) -> dict:
     stream = torch.cuda.current_stream()
 
     def run():
-        assert L.gen_stream_read(a.data_ptr(), n, sink.data_ptr(), stream.cuda_stream) == 0
+        fn = L.gen_stream_read_lds if lds else L.gen_stream_read
+        assert fn(a.data_ptr(), n, sink.data_ptr(), stream.cuda_stream) == 0
 
     for _ in range(2):
         run()
@@ -537,7 +539,7 @@ def read_ceiling(torch, gd) -> dict:
     t = e0.elapsed_time(e1) / 1e3 / reps
     del a
     torch.cuda.empty_cache()
-    log(f"read ceiling: {n / t / 1e9:.0f} GB/s (streaming-read probe over 4 GiB)")
+    log(f"read ceiling: {n / t / 1e9:.0f} GB/s (streaming-read probe over 4 GiB{', copies into LDS' if lds else ''})")
     return dict(bytes=n, us=t * 1e6, read_GBps=n / t / 1e9)
 
 
@@ -821,12 +823,14 @@ def calibrate(torch, gd) -> dict:
 
 
 def load_probe(torch, gd) -> dict:
-    """Per-CU rate of the two shapes a weight tile can be loaded with (8 rows x
-    128 B per load, or 32 rows x 32 B, the MFMA operand order of a 32-row
-    fragment) against where the rows live: each XCD's 32 workgroups stream
-    512-row sets of their own region of 1.3 MB (stays in the XCD's L2), 16.8 MB
-    (memory-side cache) or 134 MB (HBM), with 4 or 8 wavefronts of 32 KiB of
-    loads in flight each.  HIP events on the stream the probe runs on."""
+    """Per-CU rate of the shapes a weight tile can be loaded with (8 rows x 128
+    B per load with the lanes along a row or across rows, 32 rows x 32 B (the
+    MFMA operand order of a 32-row fragment), and the 8-row shapes copied into
+    LDS by the buffer unit) against where the rows live: each XCD's 32
+    workgroups stream 512-row sets of their own region of 1.3 MB (stays in the
+    XCD's L2), 16.8 MB (memory-side cache) or 134 MB (HBM), with 4 or 8
+    wavefronts of 32 KiB of loads in flight each (the LDS copies: 128 KiB per
+    workgroup).  HIP events on the stream the probe runs on."""
     regions = (512, 6554, 52429)  # rows of 2560 B per XCD
     buf = torch.ones(8 * regions[-1] * 2560, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -836,7 +840,7 @@ def load_probe(torch, gd) -> dict:
     rows = []
     for rr in regions:
         for waves in (4, 8):
-            for pat in (0, 1):
+            for pat in (0, 1, 2, 3, 4, 5, 6, 7, 8):
                 def run():
                     assert L.gen_load_probe(buf.data_ptr(), rr, pat, waves, iters, sink.data_ptr(),
                                             stream.cuda_stream) == 0
@@ -850,13 +854,18 @@ def load_probe(torch, gd) -> dict:
                 e1.record(stream)
                 torch.cuda.synchronize()
                 t = e0.elapsed_time(e1) / 1e3 / reps
-                nbytes = 256 * waves * iters * 32 * 1024
-                row = dict(region_MB_per_xcd=round(rr * 2560 / 1e6, 1), waves_per_cu=waves,
-                           shape="8 rows x 128 B" if pat == 0 else "32 rows x 32 B (MFMA order)",
+                nbytes = 256 * iters * 1024 * (128 if 3 <= pat <= 5 else 64 if pat == 7 else
+                                               waves * 8 if pat == 8 else waves * 32)
+                shape = ("8 rows x 128 B, lanes along rows", "32 rows x 32 B (MFMA order)",
+                         "8 rows x 128 B, lanes across rows", "8 rows x 128 B across rows, into LDS",
+                         "8 rows x 128 B along rows, into LDS", "8 rows along rows rotated, into LDS",
+                         "8 rows along rows rotated", "8 rows rotated, into LDS, half in flight",
+                         "8 rows x 128 B, 8 loads in flight")[pat]
+                row = dict(region_MB_per_xcd=round(rr * 2560 / 1e6, 1), waves_per_cu=waves, shape=shape,
                            us=round(t * 1e6, 1), TBps=round(nbytes / t / 1e12, 2),
                            GBps_per_cu=round(nbytes / t / 1e9 / 256, 1))
                 log(f"load probe: {row['region_MB_per_xcd']:6.1f} MB per XCD, {waves} waves/CU, "
-                    f"{row['shape']:28s} {row['GBps_per_cu']:6.1f} GB/s per CU ({row['TBps']:.2f} TB/s)")
+                    f"{row['shape']:38s} {row['GBps_per_cu']:6.1f} GB/s per CU ({row['TBps']:.2f} TB/s)")
                 rows.append(row)
     del buf
     torch.cuda.empty_cache()
@@ -882,7 +891,10 @@ def main() -> int:
         print(json.dumps({"calibration": calibrate(torch, gd)}), flush=True)
         return 0
     if args.load_probe:
-        print(json.dumps({"load_probe": load_probe(torch, gd)}), flush=True)
+        res = load_probe(torch, gd)
+        res["stream_read"] = read_ceiling(torch, gd)
+        res["stream_read_lds"] = read_ceiling(torch, gd, lds=True)
+        print(json.dumps({"load_probe": res}), flush=True)
         return 0
 
     if args.only:

@@ -27,6 +27,8 @@ def lib() -> ctypes.CDLL:
         L.gen_fill_codes.restype = L.gen_fill_scales.restype = ctypes.c_int
         L.gen_stream_read.argtypes = [vp, i64, vp, vp]
         L.gen_stream_read.restype = ctypes.c_int
+        L.gen_stream_read_lds.argtypes = [vp, i64, vp, vp]
+        L.gen_stream_read_lds.restype = ctypes.c_int
         L.gen_clock_probe.argtypes = [vp, i32, i32, vp]
         L.gen_clock_probe.restype = ctypes.c_int
         L.gen_load_probe.argtypes = [vp, i32, i32, i32, i32, vp, vp]

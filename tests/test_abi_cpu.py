@@ -44,7 +44,8 @@ def test_gen_library_exports():
     if not os.path.exists(gd.LIB_PATH):
         pytest.skip("libmoe_gen.so not built")
     L = ctypes.CDLL(gd.LIB_PATH)
-    for name in ("gen_fill_codes", "gen_fill_scales", "gen_stream_read", "gen_clock_probe", "gen_load_probe"):
+    for name in ("gen_fill_codes", "gen_fill_scales", "gen_stream_read", "gen_stream_read_lds", "gen_clock_probe",
+                 "gen_load_probe"):
         assert hasattr(L, name), name
 
 
@@ -56,7 +57,8 @@ def test_gen_load_probe_rejects_bad_arguments():
         pytest.skip("libmoe_gen.so not built")
     L = gd.lib()
     good = dict(region_rows=512, pattern=0, waves=4, iters=1)
-    for bad in (dict(region_rows=511), dict(region_rows=1 << 20), dict(pattern=2), dict(waves=6), dict(iters=0)):
+    for bad in (dict(region_rows=511), dict(region_rows=1 << 20), dict(pattern=9), dict(pattern=-1), dict(waves=6),
+                dict(iters=0)):
         a = dict(good, **bad)
         assert L.gen_load_probe(FAKE, a["region_rows"], a["pattern"], a["waves"], a["iters"], FAKE, None) == 1, bad
     assert L.gen_load_probe(None, 512, 0, 4, 1, FAKE, None) == 1
