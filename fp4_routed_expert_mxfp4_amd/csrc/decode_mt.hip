@@ -46,6 +46,8 @@
 #include "kernels.h"
 #include "route_core.cuh"
 
+#include <type_traits>
+
 namespace moe {
 
 namespace {
@@ -125,6 +127,14 @@ __device__ __forceinline__ bf16x8_t dq8(uint32_t w, float s) {
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// A copy of v the compiler cannot see through: per-lane addresses derived from
+// it are recomputed where used instead of being hoisted out of a persistent
+// loop, where they would hold registers for its whole length.
+__device__ __forceinline__ int opaque_lane(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 // CH consecutive chunks of one unit (one or two): A (per chunk and plane the
 // lane's 64 B of block 4c+g) and the unit's NF B fragments.  CH = 1 (down):
@@ -327,6 +337,123 @@ __device__ __forceinline__ void mt_k_loop_deep(const MtSrc<PLANES, NF>& src, f4v
   }
 }
 
+// A workgroup's gate/up units as one stream (units whose K quarter fits one
+// scale window): the loads that mt_k_loop_deep issues past a unit's end (its
+// sets nsets, nsets + 1) are the next unit's first sets instead, and the next
+// unit's scale table is loaded before this unit's epilogue, so the next
+// unit's first weights arrive while this one's partial sums are added.  The
+// chunks, their order and the MFMA sequence of every unit are those of
+// mt_k_loop_deep.
+template <int NF>
+struct GuUnit {
+  int live;            // a unit to compute (otherwise every load reads zeros)
+  int u;               // its index
+  rsrc_t rg, ru;       // its gate and up codes
+  rsrc_t sg, su;       // and their scale bytes
+  uint32_t boff;       // byte offset of its first weight row (8 NF q rows)
+  uint32_t srow;       // its first weight row
+  int pair;            // the lane's A row as make() found it (its A offset is taken at first use)
+  int info[5];         // what the epilogue needs
+};
+
+// make(u, U): the first live unit at or after u (stepping by stride), or
+// U.live = 0; va_of(U.pair): the lane's A offset (row + 64 g, kOob for none),
+// taken where the first A loads go out so that a row index make() loaded is
+// not waited for earlier; epi(U, acc): the unit's epilogue.  x: the A rows'
+// resource.
+// vb0[f]: the lane's byte offset in the fragment-row pattern (row f*16 % 8NF/2
+// + l/8, + 16 (l%8)) without the unit's offset.
+template <int NF, typename Make, typename VaOf, typename Epi>
+__device__ __forceinline__ void mt_gu_stream(int u0, int stride, int cb, int ce, int NB, uint32_t row8, rsrc_t x,
+                                             uint32_t* tab, uint8_t* scr, Make make, VaOf va_of, Epi epi) {
+  constexpr int NG = NF / 2;
+  const int lane = __lane_id(), q16 = lane & 15, g = lane >> 4;
+  // sets of the quarter, padded to an even count (a padded set reads zeros and
+  // is not multiplied) so that every unit starts in register set 0
+  const int nreal = (ce - cb + 1) >> 1, nsets = (nreal + 1) & ~1, last = ce - 1;
+  const uint32_t half = ((uint32_t)lane >> 2) & 1u;  // the lane's 16 B of a pair lie in chunk c + half
+  uint32_t vb0[NG];
+#pragma unroll
+  for (int f = 0; f < NG; ++f) vb0[f] = (uint32_t)(16 * f + (lane >> 3)) * (row8 / 8u) + 16u * (uint32_t)(lane & 7);
+  auto tables = [&](const GuUnit<NF>& U, MtTabGU<NF>& ts) {
+    const int t = opaque_lane(lane);
+    ts.t[0].issue(U.sg, cb, t, [&](int r) { return U.live ? (U.srow + (uint32_t)r) * (uint32_t)NB : kOob; });
+    ts.t[1].issue(U.su, cb, t, [&](int r) { return U.live ? (U.srow + (uint32_t)r) * (uint32_t)NB : kOob; });
+  };
+  // A of set n (chunks cb + 2n, +1) from row offset va (kOob: zeros)
+  auto load_a = [&](uint32_t va, int n, MtRegs<1, 2, NF>& dst) {
+    const int c = cb + 2 * n;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t off = c + i < ce ? 0u : kOob;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dst.a[i][0][t] = bload16(x, (va + (uint32_t)(c + i) * 256u + 16u * t) | off);
+    }
+  };
+  // B of set n of the unit with codes rg, ru at boff (live == 0: zeros)
+  auto load_b = [&](rsrc_t rg, rsrc_t ru, uint32_t boff, int live, int n, MtRegs<1, 2, NF>& dst) {
+    const int c = cb + 2 * n;
+    const uint32_t ob = live && c + (int)half < ce ? 0u : kOob;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        dst.b[j][f] = bload16(f < NG ? rg : ru, (vb0[f % NG] + boff + (uint32_t)j * row8 + (uint32_t)c * 64u) | ob);
+  };
+  GuUnit<NF> U, N;
+  make(u0, U);
+  if (!U.live) return;
+  MtTabGU<NF> ts;
+  tables(U, ts);
+  MtRegs<1, 2, NF> r[2];
+  load_a(va_of(U.pair), 0, r[0]);
+  load_b(U.rg, U.ru, U.boff, 1, 0, r[0]);
+  load_b(U.rg, U.ru, U.boff, 1, 1, r[1]);
+  for (;;) {
+    ts.store(tab, opaque_lane(lane));  // waits for the table's loads, issued after this unit's first sets
+    __builtin_amdgcn_wave_barrier();  // a wavefront's LDS accesses complete in order
+    make(U.u + stride, N);  // after the wait: its row-index load is not waited for here
+    const uint32_t uva = va_of(U.pair);
+    f4v acc[NF] = {};
+    // set n: B(n) staged, A(n + 1) and B(n + 2) issued (this unit's, or with
+    // NEXT the next unit's first sets), then the MFMAs of set n
+    auto step = [&](auto J, auto NA, auto NB, int n) {
+      constexpr int j = decltype(J)::value;
+      constexpr bool na = decltype(NA)::value, nb = decltype(NB)::value;
+      const int c = cb + 2 * n;
+      mt_stage<NF>(r[j].b, scr);
+      if constexpr (na) load_a(va_of(N.pair), n + 1 - nsets, r[j ^ 1]);
+      else load_a(uva, n + 1, r[j ^ 1]);
+      if constexpr (nb) load_b(N.rg, N.ru, N.boff, N.live, n + 2 - nsets, r[j]);
+      else load_b(U.rg, U.ru, U.boff, 1, n + 2, r[j]);
+      __builtin_amdgcn_sched_barrier(0);  // the next loads go out before these MFMAs
+      if (n < nreal) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {  // a chunk past the quarter's end takes column `last`'s scales
+          uint4_t bq[NF];
+          mt_fetch<NF>(scr, i, bq);
+          mt_mma_chunk(r[j].a[i], bq, acc, tab, min(c + i, last) - cb, q16, g);
+        }
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using F = std::false_type;
+    using T = std::true_type;
+    for (int n = 0; n + 2 < nsets; n += 2) {
+      step(I0{}, F{}, F{}, n);
+      step(I1{}, F{}, F{}, n + 1);
+    }
+    step(I0{}, F{}, T{}, nsets - 2);  // B of the next unit's set 0
+    step(I1{}, T{}, T{}, nsets - 1);  // its A of set 0 and B of set 1
+    __builtin_amdgcn_sched_barrier(0);  // the table's loads after the last MFMAs (their registers)
+    tables(N, ts);
+    epi(U, acc);
+    if (!N.live) break;
+    U = N;
+  }
+}
+
 // The four wavefronts of a workgroup take fixed quarters of a unit's K
 // (chunks [w*nch/4, (w+1)*nch/4)); their partial sums meet in LDS and are
 // added in wavefront order, so every output is the same fp32 expression
@@ -371,6 +498,61 @@ __global__ __launch_bounds__(kMtThreads, 2) void gateup_mt_kernel(
   const size_t mat = (size_t)I * wrow, smat = (size_t)I * NB, lo_plane = (size_t)P * I;
   const int units = tiles * pl.groups();
   uint32_t* tab = tabs[wid];
+  // the gate/up epilogue of unit (b, mg, q): wavefront f < NG takes h columns
+  // 8 NF q + 16f + q16 (gate fragment f, up fragment f + NG); accumulator v:
+  // bucket row 16mg + 4g + v
+  auto epilogue = [&](int mg, int q, int row0, int cnt, const f4v (&acc)[NF]) {
+    __builtin_amdgcn_wave_barrier();
+    mt_part_store<NF>(reinterpret_cast<float*>(tab), acc, lane);
+    __syncthreads();
+    if (wid < NG) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = kMtRows * mg + 4 * g + v;
+        const float gv = mt_part_sum<NF>(tabs, wid, v, lane), uv = mt_part_sum<NF>(tabs, wid + NG, v, lane);
+        if (row < cnt) {
+          const float hv = swiglu_f32(gv, uv);
+          const uint16_t hi = f32_to_bf16_rne(hv);
+          const size_t o = (size_t)(row0 + row) * I + 8 * NF * q + 16 * wid + q16;
+          hpl[o] = hi;
+          hpl[lo_plane + o] = bf16_lo_part(hv, hi);
+        }
+      }
+    }
+    __syncthreads();  // the partials are read before the next unit's tables overwrite them
+  };
+  if ((nch + 3) / 4 <= kMtWin && nch / 4 >= 3) {  // every quarter one scale window of at least two sets
+    auto make = [&](int u, GuUnit<NF>& U) {
+      int b = 0, mg = 0, q = 0, slot = 0;
+      for (; u < units; u += gridDim.x) {
+        pl.locate(u, tiles, b, mg, q);
+        const int expert = pl.bk.expert[b];
+        slot = e2s ? e2s[expert] : expert;
+        if (slot >= 0 && slot < w.num_slots) break;  // units of experts not stored: the down kernel writes zeros
+      }
+      U.u = u;
+      U.live = u < units;
+      const size_t sl = U.live ? (size_t)slot : 0;
+      U.rg = make_rsrc(w.wg + sl * mat, (uint32_t)mat);
+      U.ru = make_rsrc(w.wu + sl * mat, (uint32_t)mat);
+      U.sg = make_rsrc(w.sg + sl * smat, (uint32_t)smat);
+      U.su = make_rsrc(w.su + sl * smat, (uint32_t)smat);
+      U.srow = (uint32_t)(8 * NF * q);
+      U.boff = U.srow * wrow;
+      const int row0 = U.live ? pl.bk.row0[b] : 0, cnt = U.live ? pl.bk.cnt[b] : 0;
+      const int rr = kMtRows * mg + q16;
+      U.pair = rr < cnt ? sorted_pair[row0 + rr] : -1;
+      U.info[0] = mg, U.info[1] = q, U.info[2] = row0, U.info[3] = cnt;
+    };
+    auto va_of = [&](int pair) {
+      return pair >= 0 ? (uint32_t)(pair / k) * (uint32_t)H * 2u + 64u * (uint32_t)g : kOob;
+    };
+    mt_gu_stream<NF>(blockIdx.x, gridDim.x, cb, ce, NB, 8u * wrow, make_rsrc(x, x_bytes), tab, mtscr[wid], make,
+                     va_of, [&](const GuUnit<NF>& U, const f4v (&acc)[NF]) {
+                       epilogue(U.info[0], U.info[1], U.info[2], U.info[3], acc);
+                     });
+    return;
+  }
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
     int b, mg, q;
     pl.locate(u, tiles, b, mg, q);
@@ -399,26 +581,7 @@ __global__ __launch_bounds__(kMtThreads, 2) void gateup_mt_kernel(
     };
     f4v acc[NF] = {};
     mt_k_loop_deep<MtTabGU<NF>>(src, acc, cb, ce, tab, mtscr[wid], tables);
-    __builtin_amdgcn_wave_barrier();
-    mt_part_store<NF>(reinterpret_cast<float*>(tab), acc, lane);
-    __syncthreads();
-    // wavefront f < NG: h columns 8 NF q + 16f + q16 (gate fragment f, up fragment f + NG);
-    // accumulator v: bucket row 16mg + 4g + v
-    if (wid < NG) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = kMtRows * mg + 4 * g + v;
-        const float gv = mt_part_sum<NF>(tabs, wid, v, lane), uv = mt_part_sum<NF>(tabs, wid + NG, v, lane);
-        if (row < cnt) {
-          const float hv = swiglu_f32(gv, uv);
-          const uint16_t hi = f32_to_bf16_rne(hv);
-          const size_t o = (size_t)(row0 + row) * I + 8 * NF * q + 16 * wid + q16;
-          hpl[o] = hi;
-          hpl[lo_plane + o] = bf16_lo_part(hv, hi);
-        }
-      }
-    }
-    __syncthreads();  // the partials are read before the next unit's tables overwrite them
+    epilogue(mg, q, row0, cnt, acc);
   }
 }
 
@@ -550,6 +713,46 @@ __global__ __launch_bounds__(kMtThreads, 2) void inv_gateup_kernel(
   const size_t mat = (size_t)I * wrow, smat = (size_t)I * NB, lo_plane = (size_t)k * I;
   const int units = k * tiles;
   uint32_t* tab = tabs[wid];
+  // wavefront f < NG: h columns 8 NF q + 16f + q16; the token is accumulator 0 of lanes 0-15
+  auto epilogue = [&](int b, int q, const f4v (&acc)[NF]) {
+    __builtin_amdgcn_wave_barrier();
+    mt_part_store<NF>(reinterpret_cast<float*>(tab), acc, lane);
+    __syncthreads();
+    if (wid < NG && g == 0) {
+      const float gv = mt_part_sum<NF>(tabs, wid, 0, lane), uv = mt_part_sum<NF>(tabs, wid + NG, 0, lane);
+      const float hv = swiglu_f32(gv, uv);
+      const uint16_t hi = f32_to_bf16_rne(hv);
+      const size_t o = (size_t)b * I + 8 * NF * q + 16 * wid + q16;
+      hpl[o] = hi;
+      hpl[lo_plane + o] = bf16_lo_part(hv, hi);
+    }
+    __syncthreads();  // the partials are read before the next unit's tables overwrite them
+  };
+  if ((nch + 3) / 4 <= kMtWin && nch / 4 >= 3) {  // every quarter one scale window of at least two sets
+    auto make = [&](int u, GuUnit<NF>& U) {
+      int slot = -1;
+      for (; u < units; u += gridDim.x) {
+        slot = rt.slot[u / tiles];
+        if (slot >= 0) break;  // buckets of experts not stored: the down kernel writes zero rows
+      }
+      U.u = u;
+      U.live = u < units;
+      const int b = U.live ? u / tiles : 0, q = U.live ? u - b * tiles : 0;
+      const size_t sl = U.live ? (size_t)slot : 0;
+      U.rg = make_rsrc(w.wg + sl * mat, (uint32_t)mat);
+      U.ru = make_rsrc(w.wu + sl * mat, (uint32_t)mat);
+      U.sg = make_rsrc(w.sg + sl * smat, (uint32_t)smat);
+      U.su = make_rsrc(w.su + sl * smat, (uint32_t)smat);
+      U.srow = (uint32_t)(8 * NF * q);
+      U.boff = U.srow * wrow;
+      U.pair = 0;
+      U.info[0] = b, U.info[1] = q;
+    };
+    auto va_of = [&](int) { return q16 == 0 ? 64u * (uint32_t)g : kOob; };
+    mt_gu_stream<NF>(blockIdx.x, gridDim.x, cb, ce, NB, 8u * wrow, make_rsrc(x, (uint32_t)H * 2u), tab, mtscr[wid],
+                     make, va_of, [&](const GuUnit<NF>& U, const f4v (&acc)[NF]) { epilogue(U.info[0], U.info[1], acc); });
+    return;
+  }
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
     const int b = u / tiles, q = u - b * tiles;
     const int slot = rt.slot[b];
@@ -574,19 +777,7 @@ __global__ __launch_bounds__(kMtThreads, 2) void inv_gateup_kernel(
     };
     f4v acc[NF] = {};
     mt_k_loop_deep<MtTabGU<NF>>(src, acc, cb, ce, tab, mtscr[wid], tables);
-    __builtin_amdgcn_wave_barrier();
-    mt_part_store<NF>(reinterpret_cast<float*>(tab), acc, lane);
-    __syncthreads();
-    // wavefront f < NG: h columns 8 NF q + 16f + q16; the token is accumulator 0 of lanes 0-15
-    if (wid < NG && g == 0) {
-      const float gv = mt_part_sum<NF>(tabs, wid, 0, lane), uv = mt_part_sum<NF>(tabs, wid + NG, 0, lane);
-      const float hv = swiglu_f32(gv, uv);
-      const uint16_t hi = f32_to_bf16_rne(hv);
-      const size_t o = (size_t)b * I + 8 * NF * q + 16 * wid + q16;
-      hpl[o] = hi;
-      hpl[lo_plane + o] = bf16_lo_part(hv, hi);
-    }
-    __syncthreads();  // the partials are read before the next unit's tables overwrite them
+    epilogue(b, q, acc);
   }
 }
 
