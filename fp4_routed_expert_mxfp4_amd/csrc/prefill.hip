@@ -676,18 +676,19 @@ __device__ __forceinline__ float swiglu_fast(float g, float u) {
 // expert is read once for a handful of rows.  One wavefront per (bucket, 32
 // weight rows of each of two matrices): its A fragment (the bucket's rows,
 // rows past the end read as zeros) comes from memory into registers in MFMA
-// order and its two B fragments in 8-row loads, in batches of four K-steps
-// with the next batch in flight, and many wavefronts per CU keep the HBM
-// stream full.
+// order and its two B fragments in 8-row loads, in batches of four K-steps,
+// and many wavefronts per CU keep the HBM stream full.
 
 
-// Four K-steps (two 128-K chunks) of one wavefront: A block 2s+h of row r32
-// (24 B); each B fragment's 32 rows x 128 B of the two chunks as loaded, four
-// loads of 8 rows (b[g][j]: rows 8 j + l / 8, bytes 16 (l % 8)), moved into
-// MFMA order through the wavefront's LDS area when used (a load over the 16 or
-// 32 rows of an operand streams at about two thirds of this rate from memory).
+// Four K-steps (two 128-K chunks) of one wavefront: A, the lane's 48-byte
+// record (row r32, K-half h) of each chunk in three 16-byte loads (K-step 2c
+// takes its bytes 0-23, block 2c... of the record, K-step 2c+1 bytes 24-47);
+// each B fragment's 32 rows x 128 B of the two chunks as loaded, four loads of
+// 8 rows (b[g][j]: rows 8 j + l / 8, bytes 16 (l % 8)), moved into MFMA order
+// through the wavefront's LDS area when used (a load over the 16 or 32 rows of
+// an operand streams at about two thirds of this rate from memory).
 struct SkRegs {
-  uint2 a[4][3];
+  uint4_t a[2][3];  // [chunk][16 B of the lane's 48-byte record]: K-step 2c bytes 0-23, 2c+1 bytes 24-47
   uint4_t b[2][4];  // [fragment][load]
 };
 
@@ -705,10 +706,10 @@ struct SkSrc {
   uint32_t row8;       // bytes from a weight row to the row 8 below
   __device__ __forceinline__ void load(int n, SkRegs& r) const {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {  // K-step s: chunk 2n + s/2, block 2(s%2) + h = bytes 24(s%2).. of the record
-      const uint32_t o = va + (uint32_t)(2 * n + (s >> 1)) * cstride + 24u * (uint32_t)(s & 1);
+    for (int c = 0; c < 2; ++c) {  // chunk 2n + c: the lane's whole record (records are 48 B, 16-B aligned)
+      const uint32_t o = va + (uint32_t)(2 * n + c) * cstride;
 #pragma unroll
-      for (int j = 0; j < 3; ++j) r.a[s][j] = bload8(ra, o + 8u * j);
+      for (int j = 0; j < 3; ++j) r.a[c][j] = bload16(ra, o + 16u * j);
     }
 #pragma unroll
     for (int g = 0; g < 2; ++g)
@@ -743,8 +744,10 @@ __device__ __forceinline__ void sk_mma(const SkRegs& r, f16v (&acc)[2], int nks,
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     if (s < nks) {
-      const i8v a = i8v{(int)r.a[s][0].x, (int)r.a[s][0].y, (int)r.a[s][1].x, (int)r.a[s][1].y,
-                        (int)r.a[s][2].x, (int)r.a[s][2].y, 0, 0};
+      // K-step s: block 2(s%2) + h = bytes 24 (s%2) .. of the record of chunk 2n + s/2
+      const uint4_t* q = r.a[s >> 1];
+      const i8v a = (s & 1) ? i8v{(int)q[1].z, (int)q[1].w, (int)q[2].x, (int)q[2].y, (int)q[2].z, (int)q[2].w, 0, 0}
+                            : i8v{(int)q[0].x, (int)q[0].y, (int)q[0].z, (int)q[0].w, (int)q[1].x, (int)q[1].y, 0, 0};
       // low byte: the scale of block 2s+h
       const int sa = (int)((tab[r32 * SKW + cw + (s >> 1)] >> (8 * h)) >> (16 * (s & 1)));
 #pragma unroll
@@ -764,10 +767,13 @@ struct SkTables {
   ScaleRows<32, 64, SKWIN, SKW> b[2];
 };
 
-// All K of one unit: batches of four K-steps, the next batch's loads in flight
-// while one is multiplied; pairs of batches alternate the two register sets.
-// Loads past the last batch re-read it (never used): no load behind a branch.
-// tables(cw0, ts) issues the scale-table loads of the window starting at chunk cw0.
+// All K of one unit: batches of four K-steps, each batch's loads issued once
+// the previous batch's MFMAs have read their registers.  One batch in flight
+// per wavefront streams faster than two once the rows live beyond L2 (fewer
+// loads queued per wavefront), and the eight wavefronts of a CU cover each
+// other's waits.  The load after the last batch re-reads it (never used): no
+// load behind a branch.  tables(cw0, ts) issues the scale-table loads of the
+// window starting at chunk cw0.
 template <typename TS, typename Tables>
 __device__ __forceinline__ void sk_k_loop(const SkSrc& src, f16v (&acc)[2], int K, int h, uint32_t* tab,
                                           uint8_t* scr, Tables tables) {
@@ -777,17 +783,15 @@ __device__ __forceinline__ void sk_k_loop(const SkSrc& src, f16v (&acc)[2], int 
     const int b0 = cw0 / 2, last = (min(cw0 + SKWIN, nchunks) + 1) / 2 - 1;  // batches of this window
     TS ts;
     tables(cw0, ts);
-    SkRegs r0, r1;
+    SkRegs r0;
     src.load(b0, r0);
     ts.a.store(tab, lane);
     ts.b[0].store(tab + 32 * SKW, lane);
     ts.b[1].store(tab + 64 * SKW, lane);
     __builtin_amdgcn_wave_barrier();  // a wavefront's LDS accesses complete in order
-    for (int n = b0; n <= last; n += 2) {
-      src.load(min(n + 1, last), r1);
+    for (int n = b0; n <= last; ++n) {
       sk_mma(r0, acc, min(4, nks_total - 4 * n), h, tab, 2 * (n - b0), scr);
-      src.load(min(n + 2, last), r0);
-      sk_mma(r1, acc, n + 1 > last ? 0 : min(4, nks_total - 4 * (n + 1)), h, tab, 2 * (n + 1 - b0), scr);
+      src.load(min(n + 1, last), r0);
     }
     __builtin_amdgcn_wave_barrier();
   }
