@@ -475,23 +475,16 @@ __device__ __forceinline__ void fused_gateup_rows(const FusedRoute& fr, const ui
   (void)units;
   const int nslot = k * nbat;
   if (gw >= nslot) return;
-  Where wa, wb;
-  GateUpBatch<J, R> A, Bn;
-  where(gw, wa);
-  gu_load(A, wa.cp, wa.sp, wa.n0, rowbytes, NB);
-  for (int q = gw; q < nslot; q += 2 * total_waves) {
-    const int q1 = q + total_waves, q2 = q + 2 * total_waves;
-    const bool has1 = q1 < nslot;
-    if (has1) {
-      where(q1, wb);
-      gu_load(Bn, wb.cp, wb.sp, wb.n0, rowbytes, NB);
-    }
+  // One batch in flight per wavefront: the next batch's loads go out once this
+  // one is reduced (with two in flight the step measured 0.25 us slower: fewer
+  // loads queued per wavefront stream faster, and the CU's eight wavefronts
+  // cover each other's waits).
+  Where wa;
+  GateUpBatch<J, R> A;
+  for (int q = gw; q < nslot; q += total_waves) {
+    where(q, wa);
+    gu_load(A, wa.cp, wa.sp, wa.n0, rowbytes, NB);
     if (wa.store) gu_finish(A, xr, lane, wa.hrow, wa.n0);
-    if (q2 < nslot) {
-      where(q2, wa);
-      gu_load(A, wa.cp, wa.sp, wa.n0, rowbytes, NB);
-    }
-    if (has1 && wb.store) gu_finish(Bn, xr, lane, wb.hrow, wb.n0);
   }
 }
 
