@@ -368,8 +368,11 @@ constexpr uint32_t kOpenRange = 0x7FFFFFF0u;  // range of the activation buffers
 // pair as 8 rows x 128 B per load (lane l: row 8 j + l / 8, bytes 16 (l % 8)
 // of the pair), writes them into a private LDS area and reads them back in
 // operand order; the next pair's loads go out as soon as the registers are
-// written.  The weights' scale bytes of a pair (8 per row) go straight to
-// registers.  The activations are shared by the eight wavefronts: each
+// written.  The weights' scale bytes go to registers two pairs at a time: a
+// scale load touches one line per row whatever its width, so each lane loads
+// one pair's 8 bytes of its row (lane l: pair l / 32) and swaps them with its
+// partner l ^ 32, half the loads and lines of one load per pair (removing
+// the scale loads altogether sped the GEMMs up by 10-14%).  The activations are shared by the eight wavefronts: each
 // chunk's 128 records are copied from memory into one of four LDS stages by
 // the buffer unit (buffer_load ... lds, no registers; two copies of 1 KB per
 // wavefront), a pair ahead, and read from there by every
@@ -506,17 +509,35 @@ struct BRaw {
 struct BSrc {
   rsrc_t rc[2], rs[2];  // codes and scales of the matrix holding each fragment
   uint32_t vc[2];       // the lane's code bytes in chunk 0: row l / 8 of the fragment, + 16 (l % 8)
-  uint32_t vs[2];       // the lane's scale bytes in chunk 0: row l % 32 of the fragment
+  uint32_t vs[2];       // the lane's scale bytes in group 0: row l % 32 of the fragment, pair l / 32
   uint32_t row8;        // bytes from a weight row to the row 8 below
-  // Fragment g of the pair starting at chunk c (even); c < 0 loads zeros.
+  // Codes of fragment g of the pair starting at chunk c (even); c < 0 loads zeros.
   // Past the row's last chunk the bytes belong to the next row (never used).
-  __device__ __forceinline__ void load(int g, int c, BRaw& r, uint2& ws) const {
+  __device__ __forceinline__ void load(int g, int c, BRaw& r) const {
     const bool z = c < 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) r.q[g][j] = bload16(rc[g], z ? kOob : vc[g] + (uint32_t)j * row8 + (uint32_t)c * 64u);
-    ws = bload8(rs[g], z ? kOob : vs[g] + (uint32_t)c * 4u);
+  }
+  // Scale bytes of fragment g for the two pairs starting at chunk c (c % 4 == 0):
+  // the lane gets those of pair l / 32 (8 bytes); c < 0 loads zeros.
+  __device__ __forceinline__ uint2 load_scales(int g, int c) const {
+    return bload8(rs[g], c < 0 ? kOob : vs[g] + (uint32_t)c * 4u);
   }
 };
+
+// A lane's weight scale words of the two pairs of a group, from the 8 bytes of
+// its row that it loaded (pair h = l / 32) and the 8 its partner lane l ^ 32
+// loaded: word p holds bytes h and 2 + h of chunk 2p's scale word, then of
+// chunk 2p + 1's, so byte S is the scale of K-step S of pair p.
+__device__ __forceinline__ void group_words(const uint2& own, int h, uint32_t (&pk)[2]) {
+  const auto x0 = __builtin_amdgcn_permlane32_swap(own.x, own.x, false, false);
+  const auto x1 = __builtin_amdgcn_permlane32_swap(own.y, own.y, false, false);
+  const uint32_t o0 = h ? x0[0] : x0[1], o1 = h ? x1[0] : x1[1];  // the partner's pair
+  const uint32_t sel = 0x06040200u + 0x01010101u * (uint32_t)h;
+  const uint32_t mine = __builtin_amdgcn_perm(own.y, own.x, sel), other = __builtin_amdgcn_perm(o1, o0, sel);
+  pk[0] = h ? other : mine;
+  pk[1] = h ? mine : other;
+}
 
 __device__ __forceinline__ i8v bop(const uint4_t& q) { return i8v{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0}; }
 
@@ -541,8 +562,8 @@ __device__ __forceinline__ void wg_barrier() {
 }
 
 // Vector memory operations of a pair: four LDS copies (two chunks), then per
-// weight fragment four code loads and a scale load.
-constexpr int kPairWeightVm = 2 * 5;
+// weight fragment four code loads (and a scale load in a group's first pair).
+constexpr int kPairCodeVm = 2 * 4;
 
 // A lane's scale words of chunk wd (rows r32 + 32 f of the table), shifted so
 // that byte 0 is the scale of its block 4c + h (K-step 0) and byte 2 that of
@@ -561,14 +582,10 @@ __device__ __forceinline__ int word(const uint4_t& w, int f) {
 // activations A (fp6, scale byte opsel of sa).  WFIRST: the weights are the
 // first operand (accumulators hold one bucket row per lane) or the second
 // (one output column per lane).
-template <bool WFIRST>
-__device__ __forceinline__ f16v tile_mfma(const i8v& W, const i8v& A, const f16v& c, int opsel, int sw, int sa) {
-  if (WFIRST) {
-    if (opsel == 0) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(W, A, c, 4, 2, 0, sw, 0, sa);
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(W, A, c, 4, 2, 2, sw, 2, sa);
-  }
-  if (opsel == 0) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, W, c, 2, 4, 0, sa, 0, sw);
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, W, c, 2, 4, 2, sa, 2, sw);
+template <bool WFIRST, int OW, int OA>
+__device__ __forceinline__ f16v tile_mfma(const i8v& W, const i8v& A, const f16v& c, int sw, int sa) {
+  if (WFIRST) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(W, A, c, 4, 2, OW, sw, OA, sa);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, W, c, 2, 4, OA, sa, OW, sw);
 }
 
 // Pair q of a window (chunks c0 = cw0 + 2q and c0 + 1, in stages 2 PJ and
@@ -581,10 +598,14 @@ __device__ __forceinline__ f16v tile_mfma(const i8v& W, const i8v& A, const f16v
 // weight operands are read, 8 MFMAs.  run0 / run1: chunk c0 / c0 + 1 exists.
 template <int PJ, bool WFIRST>
 __device__ __forceinline__ void tile_pair(const TileTables& tb, uint8_t* const (&st)[4], uint8_t* scr,
-                                          const ACopy& as, const BSrc& bs, BRaw& raw, uint2 (&ws)[2],
-                                          f16v (&acc)[4][2], int cw0, int last, int q, int lane, int r32, int h,
-                                          bool run0, bool run1) {
+                                          const ACopy& as, const BSrc& bs, BRaw& raw, uint2 (&sraw)[2],
+                                          uint32_t (&pk)[2][2], f16v (&acc)[4][2], int cw0, int last, int q,
+                                          int lane, int r32, int h, bool run0, bool run1) {
   const int c0 = cw0 + 2 * q, n0 = c0 + 2;
+  if (PJ == 0) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) group_words(sraw[g], h, pk[g]);
+  }
   as.copy(st[2 - 2 * PJ], n0 <= last ? n0 : -1);
   as.copy(st[3 - 2 * PJ], n0 + 1 <= last ? n0 + 1 : -1);
   __builtin_amdgcn_sched_barrier(0);
@@ -597,9 +618,13 @@ __device__ __forceinline__ void tile_pair(const TileTables& tb, uint8_t* const (
       for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4_t*>(wr + g * B_FRAG + j * 128) = raw.q[g][j];
   }
   __builtin_amdgcn_sched_barrier(0);
-  uint2 wsn[2];
+  if (PJ == 0) {
+    const int cn = c0 + 4;  // the next group
 #pragma unroll
-  for (int g = 0; g < 2; ++g) bs.load(g, n0 <= last ? n0 : -1, raw, wsn[g]);
+    for (int g = 0; g < 2; ++g) sraw[g] = bs.load_scales(g, cn <= last ? cn : -1);
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g) bs.load(g, n0 <= last ? n0 : -1, raw);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int S = 0; S < 4; ++S) {
@@ -615,14 +640,18 @@ __device__ __forceinline__ void tile_pair(const TileTables& tb, uint8_t* const (
       b[g] = *reinterpret_cast<const uint4_t*>(scr + g * B_FRAG + S * 1024 + ((lane ^ (2 * S)) * 16));
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const int sw = (int)((S < 2 ? ws[g].x : ws[g].y) >> (8 * h));
+      const int sw = (int)pk[g][PJ];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) acc[f][g] = tile_mfma<WFIRST>(bop(b[g]), a[f], acc[f][g], 2 * (S & 1), sw, word(sa, f));
+      for (int f = 0; f < 4; ++f) {
+        if (S == 0) acc[f][g] = tile_mfma<WFIRST, 0, 0>(bop(b[g]), a[f], acc[f][g], sw, word(sa, f));
+        if (S == 1) acc[f][g] = tile_mfma<WFIRST, 1, 2>(bop(b[g]), a[f], acc[f][g], sw, word(sa, f));
+        if (S == 2) acc[f][g] = tile_mfma<WFIRST, 2, 0>(bop(b[g]), a[f], acc[f][g], sw, word(sa, f));
+        if (S == 3) acc[f][g] = tile_mfma<WFIRST, 3, 2>(bop(b[g]), a[f], acc[f][g], sw, word(sa, f));
+      }
     }
   }
-#pragma unroll
-  for (int g = 0; g < 2; ++g) ws[g] = wsn[g];
-  wait_vm<kPairWeightVm>();  // this wavefront's copies of the next pair are done
+  if (PJ == 0) wait_vm<kPairCodeVm + 2>();  // this wavefront's copies of the next pair are done
+  else wait_vm<kPairCodeVm>();
   wg_barrier();
 }
 
@@ -644,17 +673,20 @@ __device__ __forceinline__ void tile_k_loop(TileTables& tb, uint8_t* const (&st)
     tables(cw0);
     __builtin_amdgcn_sched_barrier(0);
     BRaw raw;
-    uint2 ws[2];
+    uint2 sraw[2];
+    uint32_t pk[2][2];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) bs.load(g, cw0, raw, ws[g]);
+    for (int g = 0; g < 2; ++g) sraw[g] = bs.load_scales(g, cw0);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) bs.load(g, cw0, raw);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<kPairWeightVm>();  // all but the weight loads just issued
-    wait_lgkm0();              // the table stores
+    wait_vm<kPairCodeVm>();  // all but the code loads just issued
+    wait_lgkm0();            // the table stores
     wg_barrier();
     for (int q = 0; cw0 + 2 * q <= last; q += 2) {
       const int c = cw0 + 2 * q;
-      tile_pair<0, WFIRST>(tb, st, scr, as, bs, raw, ws, acc, cw0, last, q, lane, r32, h, true, c + 1 <= last);
-      tile_pair<1, WFIRST>(tb, st, scr, as, bs, raw, ws, acc, cw0, last, q + 1, lane, r32, h, c + 2 <= last,
+      tile_pair<0, WFIRST>(tb, st, scr, as, bs, raw, sraw, pk, acc, cw0, last, q, lane, r32, h, true, c + 1 <= last);
+      tile_pair<1, WFIRST>(tb, st, scr, as, bs, raw, sraw, pk, acc, cw0, last, q + 1, lane, r32, h, c + 2 <= last,
                            c + 3 <= last);
     }
   }
@@ -955,7 +987,7 @@ __global__ __launch_bounds__(kTilePT, 1) void gateup_tile_kernel(
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       bs.vc[g] = live ? ((uint32_t)hc0 + (uint32_t)(lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7) : kOob;
-      bs.vs[g] = live ? ((uint32_t)hc0 + (uint32_t)r32) * (uint32_t)NBH : kOob;
+      bs.vs[g] = live ? ((uint32_t)hc0 + (uint32_t)r32) * (uint32_t)NBH + 8u * (uint32_t)(lane >> 5) : kOob;
     }
     const rsrc_t xsr = make_rsrc(xs, xs_bytes);
     auto tables = [&](int cw0) {
@@ -1067,7 +1099,7 @@ __global__ __launch_bounds__(kTilePT, 1) void down_tile_kernel(
       bs.rc[g] = rd;
       bs.rs[g] = sdr;
       bs.vc[g] = live ? (row + (uint32_t)(lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7) : kOob;
-      bs.vs[g] = live ? (row + (uint32_t)r32) * (uint32_t)NBI : kOob;
+      bs.vs[g] = live ? (row + (uint32_t)r32) * (uint32_t)NBI + 8u * (uint32_t)(lane >> 5) : kOob;
     }
     const rsrc_t hsr = make_rsrc(hs, hs_bytes);
     auto tables = [&](int cw0) {
