@@ -560,13 +560,26 @@ def prefill_section(args, torch, m, gd, gi):
     ws = torch.empty(m.prefill_workspace_bytes(T, k, cfg.H, cfg.I), dtype=torch.uint8, device=dev)
     pws = torch.empty(max(m.permute_workspace_bytes(T, k, E), 256), dtype=torch.uint8, device=dev)
     out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+    # the experts' copy in MFMA operand order for the tiled GEMMs, made once when the
+    # experts are loaded (outside the timed step, like the experts themselves)
+    packed = torch.empty(m.prefill_packed_bytes(store.num_slots, cfg.H, cfg.I), dtype=torch.uint8, device=dev)
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record()
+    m.moe_prefill_pack_weights(store, packed)
+    p1.record()
+    torch.cuda.synchronize()
+    pack_ms = p0.elapsed_time(p1)
 
-    def step(_i):
-        m.moe_route(logits, k, None, ids, w)
-        m.moe_permute(ids, E, off, sp, p2r, pws)
-        m.moe_ffn_fp4_prefill(x, k, E, store, None, off, sp, y, ws)
-        m.moe_combine(y, w, None, m.MOE_OUT_BF16, out)
+    def step_with(ffn):
+        def step(_i):
+            m.moe_route(logits, k, None, ids, w)
+            m.moe_permute(ids, E, off, sp, p2r, pws)
+            ffn()
+            m.moe_combine(y, w, None, m.MOE_OUT_BF16, out)
+        return step
 
+    step = step_with(lambda: m.moe_ffn_fp4_prefill_packed(x, k, E, store, packed, None, off, sp, y, ws))
+    step_rm = step_with(lambda: m.moe_ffn_fp4_prefill(x, k, E, store, None, off, sp, y, ws))
     try:
         step(0)
         torch.cuda.synchronize()
@@ -585,12 +598,18 @@ def prefill_section(args, torch, m, gd, gi):
     cold = stats_us(replay_series(torch, graphs[0], 1, 20 if series else 3, flush))
     clock_after = clk.read()
     del graphs
+    # the same step with the tiled GEMMs on the row-major store (no packed copy)
+    graphs_rm = capture(torch, step_rm, 1)
+    time_graphs(torch, graphs_rm, 3)
+    per_rm = time_graphs(torch, graphs_rm, max(3, args.prefill_steps // 3)) / max(3, args.prefill_steps // 3)
+    del graphs_rm
     flops = 6.0 * cfg.H * cfg.I * T * k
     touched = int((torch.diff(off) > 0).sum().item())
     wbytes = touched * cfg.expert_bytes
     binding = max(flops / PEAK_MXFP4, wbytes / PEAK_HBM)  # seconds at the binding roofline
     log(f"prefill4096: {per * 1e3:.3f} ms/layer, {T / per / 1e6:.2f} M tok/s, {touched} experts, "
-        f"{wbytes / per / 1e9:.0f} GB/s of expert weights")
+        f"{wbytes / per / 1e9:.0f} GB/s of expert weights (row-major store: {per_rm * 1e3:.3f} ms; "
+        f"packing the copy: {pack_ms:.1f} ms once)")
     log(f"prefill4096: per replay median {replays['median_us'] / 1e3:.3f} min {replays['min_us'] / 1e3:.3f} ms; "
         f"cold median {cold['median_us'] / 1e3:.3f} ms; sclk {clock_before['probe_sclk_mhz_median']:.0f} -> "
         f"{clock_after['probe_sclk_mhz_median']:.0f} MHz")
@@ -601,6 +620,8 @@ def prefill_section(args, torch, m, gd, gi):
                 frac_of_binding_roofline=binding / per, frac_of_measured_mfma=flops / per / MFMA_MEASURED,
                 replays=replays, cold=dict(cold, flush_bytes=FLUSH_BYTES),
                 clocks=dict(before=clock_before, after=clock_after),
+                weights="operand-order copy for the tiled GEMMs (moe_ffn_fp4_prefill_packed)",
+                pack_ms=pack_ms, packed_bytes=packed.numel(), row_major_ms_per_layer=per_rm * 1e3,
                 mfma_busy=profile_fields(MFMA_FILE, PREFILL_SRC, ("gateup_tile_busy", "down_tile_busy",
                                                                   "gateup_skinny_busy", "down_skinny_busy")),
                 _dev=dict(x=x, logits=logits, ids=ids, out=out))

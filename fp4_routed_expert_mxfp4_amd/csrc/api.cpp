@@ -469,7 +469,8 @@ MOE_FP4_API size_t moe_ffn_fp4_prefill_workspace_bytes(int32_t T, int32_t k, int
 static moe_status prefill_call(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E, const moe_fp4_experts* w,
                                const int32_t* expert_to_slot, const int32_t* expert_offsets,
                                const int32_t* sorted_pair, int act, float* y_pair, void* ws,
-                               size_t ws_bytes, hipStream_t stream, const uint8_t* run) {
+                               size_t ws_bytes, hipStream_t stream, const uint8_t* run,
+                               const uint8_t* packed = nullptr) {
   if (act != MOE_ACT_MXFP6_E2M3) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)T * k > (1 << 22)) return MOE_ERR_SHAPE;
   // the MXFP6 activations (x once per sorted row, and h) are addressed with 31-bit buffer offsets
@@ -483,7 +484,7 @@ static moe_status prefill_call(const uint16_t* x_bf16, int32_t T, int32_t k, int
                                    ws, ws_bytes, need);
   if (st != MOE_OK || T == 0) return st;
   return launched(moe::launch_prefill(x_bf16, T, k, E, to_store(w), expert_to_slot, expert_offsets,
-                                      sorted_pair, y_pair, ws, stream, run));
+                                      sorted_pair, y_pair, ws, stream, run, packed));
 }
 
 MOE_FP4_API moe_status moe_ffn_fp4_prefill(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
@@ -493,6 +494,41 @@ MOE_FP4_API moe_status moe_ffn_fp4_prefill(const uint16_t* x_bf16, int32_t T, in
                                            hipStream_t stream) {
   return prefill_call(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, enum_bits(&act), y_pair, ws, ws_bytes,
                       stream, nullptr);
+}
+
+MOE_FP4_API size_t moe_prefill_packed_bytes(int32_t num_slots, int32_t hidden, int32_t inter) {
+  if (num_slots < 1 || hidden < 256 || hidden % 256 != 0 || inter < 128 || inter % 128 != 0) return 0;
+  return moe::prefill_packed_bytes(num_slots, hidden, inter);
+}
+
+MOE_FP4_API moe_status moe_prefill_pack_weights(const moe_fp4_experts* w, void* packed, size_t packed_bytes,
+                                                hipStream_t stream) {
+  moe_status st = check_store(w);
+  if (st != MOE_OK) return st;
+  if (!packed) return MOE_ERR_NULL;
+  if (w->hidden % 256 != 0 || w->inter % 128 != 0) return MOE_ERR_SHAPE;
+  if (misaligned(packed, 256)) return MOE_ERR_ALIGN;
+  if (packed_bytes < moe::prefill_packed_bytes(w->num_slots, w->hidden, w->inter)) return MOE_ERR_WORKSPACE;
+  // a slot's blocks are addressed with 32-bit offsets
+  if (moe_prefill_packed_bytes(1, w->hidden, w->inter) >= ((size_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  return launched(moe::launch_pack_weights(to_store(w), static_cast<uint8_t*>(packed), stream));
+}
+
+MOE_FP4_API moe_status moe_ffn_fp4_prefill_packed(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                                  const moe_fp4_experts* w, const void* packed, size_t packed_bytes,
+                                                  const int32_t* expert_to_slot, const int32_t* expert_offsets,
+                                                  const int32_t* sorted_pair, moe_act_fmt act, float* y_pair,
+                                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (T > 0) {
+    if (!packed) return MOE_ERR_NULL;
+    if (!w) return MOE_ERR_NULL;
+    if (misaligned(packed, 256)) return MOE_ERR_ALIGN;
+    if (w->num_slots > 0 && packed_bytes < moe::prefill_packed_bytes(w->num_slots, w->hidden, w->inter))
+      return MOE_ERR_WORKSPACE;
+    if (moe::prefill_packed_bytes(1, w->hidden, w->inter) >= ((size_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  }
+  return prefill_call(x_bf16, T, k, E, w, expert_to_slot, expert_offsets, sorted_pair, enum_bits(&act), y_pair, ws, ws_bytes,
+                      stream, nullptr, static_cast<const uint8_t*>(packed));
 }
 
 MOE_FP4_API moe_status moe_ffn_fp4_prefill_subset(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,

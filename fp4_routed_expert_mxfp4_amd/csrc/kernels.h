@@ -63,11 +63,16 @@ hipError_t launch_decode_fused(const float* logits, const uint16_t* x, int E, in
                                int32_t* topk_ids, float* topk_w, void* ws, int phase, hipStream_t s,
                                bool norm = false, float eps = 0.f);
 
-// Prefill FFN on block-scaled MFMA with MXFP6 activations.
+// Prefill FFN on block-scaled MFMA with MXFP6 activations.  packed: the
+// experts' copy in MFMA operand order (launch_pack_weights) for the tiled
+// GEMMs, or null to read the row-major store.
 size_t prefill_workspace_bytes(int T, int k, int H, int I);
 hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertStore& w,
                           const int32_t* e2s, const int32_t* offsets, const int32_t* sorted_pair,
-                          float* y_pair, void* ws, hipStream_t s, const uint8_t* run = nullptr);
+                          float* y_pair, void* ws, hipStream_t s, const uint8_t* run = nullptr,
+                          const uint8_t* packed = nullptr);
+size_t prefill_packed_bytes(int num_slots, int H, int I);
+hipError_t launch_pack_weights(const ExpertStore& w, uint8_t* dst, hipStream_t s);
 
 // Decode FFN over experts in the 3-bit per-row codebook format: index bytes
 // [S][rows][K*3/8], codebooks [S][rows][8] bf16; h fp32 in ws as for launch_decode.

@@ -564,6 +564,8 @@ __device__ __forceinline__ void wg_barrier() {
 // Vector memory operations of a pair: four LDS copies (two chunks), then per
 // weight fragment four code loads (and a scale load in a group's first pair).
 constexpr int kPairCodeVm = 2 * 4;
+// The same with operand-order weights: per fragment four operand loads and a scale load.
+constexpr int kPairPkVm = 2 * 5;
 
 // A lane's scale words of chunk wd (rows r32 + 32 f of the table), shifted so
 // that byte 0 is the scale of its block 4c + h (K-step 0) and byte 2 that of
@@ -688,6 +690,132 @@ __device__ __forceinline__ void tile_k_loop(TileTables& tb, uint8_t* const (&st)
       tile_pair<0, WFIRST>(tb, st, scr, as, bs, raw, sraw, pk, acc, cw0, last, q, lane, r32, h, true, c + 1 <= last);
       tile_pair<1, WFIRST>(tb, st, scr, as, bs, raw, sraw, pk, acc, cw0, last, q + 1, lane, r32, h, c + 2 <= last,
                            c + 3 <= last);
+    }
+  }
+}
+
+// ---- weights in operand order -------------------------------------------------------
+//
+// The packed copy of the experts (moe_prefill_pack_weights) holds each matrix
+// as blocks of 32 rows x one chunk pair: four K-steps of 64 lanes x 16 code
+// bytes (lane l: row l % 32, bytes 16 (l / 32) of the K-step's 32), then 64
+// lanes x 4 scale bytes (byte S: the scale of block 2 S + l / 32 of the pair).
+// A wavefront then loads each fragment's K-step operand as one contiguous
+// 1 KB straight into the register the MFMA reads and its scale word in one
+// 256-byte load: no trip through LDS, no reordering, and two lines of scales
+// per fragment and pair instead of 32.
+
+constexpr int kPkBlock = 4096 + 256;  // bytes of a (32-row block, chunk pair) of the packed copy
+
+__host__ __device__ inline int pk_pairs(int K) { return (K + 255) / 256; }
+// Bytes of one slot of the packed copy: gate, up (I rows of H), then down (H rows of I).
+__host__ __device__ inline size_t pk_slot_bytes(int H, int I) {
+  return ((size_t)2 * (I / 32) * pk_pairs(H) + (size_t)(H / 32) * pk_pairs(I)) * kPkBlock;
+}
+
+struct BSrcPk {
+  rsrc_t r;        // the slot's packed blocks
+  uint32_t fb[2];  // the lane's code bytes in fragment g's first block, kOob past the matrix
+  uint32_t sb[2];  // the lane's scale word in that block
+  __device__ __forceinline__ void init(rsrc_t rr, uint32_t base0, uint32_t base1, bool live0, bool live1, int lane) {
+    r = rr;
+    fb[0] = live0 ? base0 + 16u * (uint32_t)lane : kOob;
+    fb[1] = live1 ? base1 + 16u * (uint32_t)lane : kOob;
+    sb[0] = live0 ? base0 + 4096u + 4u * (uint32_t)lane : kOob;
+    sb[1] = live1 ? base1 + 4096u + 4u * (uint32_t)lane : kOob;
+  }
+  // Fragment g's operand of K-step S of pair pq; pq < 0 loads zeros.
+  __device__ __forceinline__ uint4_t step(int g, int pq, int S) const {
+    return bload16(r, pq < 0 || fb[g] == kOob ? kOob : fb[g] + (uint32_t)pq * kPkBlock + (uint32_t)S * 1024u);
+  }
+  // Fragment g's scale word of pair pq (byte S: K-step S).
+  __device__ __forceinline__ uint32_t scales(int g, int pq) const {
+    return bload4(r, pq < 0 || sb[g] == kOob ? kOob : sb[g] + (uint32_t)pq * kPkBlock);
+  }
+};
+
+// Pair q of a window with operand-order weights.  Loads: the activation
+// copies of the next pair go out first; then each K-step's registers are
+// reloaded with the next pair's operand as soon as its MFMAs are issued, and
+// the next pair's scale words go out with the first of them, so each K-step
+// waits only for its own operands.  One barrier per pair, for the activation
+// stages.
+template <int PJ, bool WFIRST>
+__device__ __forceinline__ void tile_pair_pk(const TileTables& tb, uint8_t* const (&st)[4], const ACopy& as,
+                                             const BSrcPk& bs, uint4_t (&bq)[2][4], uint32_t (&ws)[2],
+                                             f16v (&acc)[4][2], int cw0, int last, int q, int r32, int h, bool run0,
+                                             bool run1) {
+  const int c0 = cw0 + 2 * q, n0 = c0 + 2;
+  const int pqn = n0 <= last ? n0 / 2 : -1;
+  as.copy(st[2 - 2 * PJ], n0 <= last ? n0 : -1);
+  as.copy(st[3 - 2 * PJ], n0 + 1 <= last ? n0 + 1 : -1);
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t wsn[2];
+#pragma unroll
+  for (int S = 0; S < 4; ++S) {
+    if (S < 2 ? run0 : run1) {
+      const uint8_t* sta = st[2 * PJ + (S >> 1)];
+      const uint4_t sa = scale_words(tb.sca, c0 + (S >> 1) - cw0, r32, h);
+      i8v a[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) a[f] = (S & 1) ? read_afrag<1>(sta, f, r32, h) : read_afrag<0>(sta, f, r32, h);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int sw = (int)ws[g];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          if (S == 0) acc[f][g] = tile_mfma<WFIRST, 0, 0>(bop(bq[g][S]), a[f], acc[f][g], sw, word(sa, f));
+          if (S == 1) acc[f][g] = tile_mfma<WFIRST, 1, 2>(bop(bq[g][S]), a[f], acc[f][g], sw, word(sa, f));
+          if (S == 2) acc[f][g] = tile_mfma<WFIRST, 2, 0>(bop(bq[g][S]), a[f], acc[f][g], sw, word(sa, f));
+          if (S == 3) acc[f][g] = tile_mfma<WFIRST, 3, 2>(bop(bq[g][S]), a[f], acc[f][g], sw, word(sa, f));
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (S == 0) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) wsn[g] = bs.scales(g, pqn);
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) bq[g][S] = bs.step(g, pqn, S);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g) ws[g] = wsn[g];
+  wait_vm<kPairPkVm>();  // this wavefront's copies of the next pair are done
+  wg_barrier();
+}
+
+// All K of one tile with operand-order weights (see tile_k_loop).  The first
+// pair's scale words are loaded before its operands, as in every later pair,
+// so that each K-step's wait counts the same loads.
+template <bool WFIRST, typename Tables>
+__device__ __forceinline__ void tile_k_loop_pk(TileTables& tb, uint8_t* const (&st)[4], f16v (&acc)[4][2],
+                                               const ACopy& as, const BSrcPk& bs, int nch, int tid, Tables tables) {
+  const int lane = tid & 63, r32 = lane & 31, h = lane >> 5;
+  for (int cw0 = 0; cw0 < nch; cw0 += TWIN) {
+    const int last = min(cw0 + TWIN, nch) - 1;
+    if (cw0 > 0) wg_barrier();  // every wavefront is done with the previous window
+    as.copy(st[0], cw0);
+    as.copy(st[1], cw0 + 1 <= last ? cw0 + 1 : -1);
+    tables(cw0);
+    __builtin_amdgcn_sched_barrier(0);
+    uint4_t bq[2][4];
+    uint32_t ws[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) ws[g] = bs.scales(g, cw0 / 2);
+#pragma unroll
+    for (int S = 0; S < 4; ++S)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) bq[g][S] = bs.step(g, cw0 / 2, S);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<kPairPkVm>();  // all but the weight loads just issued
+    wait_lgkm0();          // the table stores
+    wg_barrier();
+    for (int q = 0; cw0 + 2 * q <= last; q += 2) {
+      const int c = cw0 + 2 * q;
+      tile_pair_pk<0, WFIRST>(tb, st, as, bs, bq, ws, acc, cw0, last, q, r32, h, true, c + 1 <= last);
+      tile_pair_pk<1, WFIRST>(tb, st, as, bs, bq, ws, acc, cw0, last, q + 1, r32, h, c + 2 <= last, c + 3 <= last);
     }
   }
 }
@@ -954,13 +1082,14 @@ __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
 // last tile narrower than 256 columns (inter % 256 == 128) wavefronts 2 and 3
 // load zeros and store nothing.
 
+template <bool PK>  // PK: weights from the packed copy pk (operand order), else the row-major store
 __global__ __launch_bounds__(kTilePT, 1) void gateup_tile_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, uint32_t xq_bytes, uint32_t xs_bytes, int P,
-    ExpertStore w, const TileDesc* __restrict__ tiles, const int32_t* __restrict__ counts,
-    uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
+    ExpertStore w, const uint8_t* __restrict__ pk, const TileDesc* __restrict__ tiles,
+    const int32_t* __restrict__ counts, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
   __shared__ TileTables tb;
   __shared__ __attribute__((aligned(16))) uint8_t a0[A_STAGE], a1[A_STAGE], a2[A_STAGE], a3[A_STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t bscr[8 * B_SCR];
+  __shared__ __attribute__((aligned(16))) uint8_t bscr[PK ? 16 : 8 * B_SCR];
   uint8_t* const st[4] = {a0, a1, a2, a3};
   const int H = w.H, I = w.I, NBH = H / 32, NBI = I / 32;
   // wid in a scalar register: every address derived from it alone stays scalar
@@ -979,15 +1108,24 @@ __global__ __launch_bounds__(kTilePT, 1) void gateup_tile_kernel(
     ACopy as;
     as.init(xq, xq_bytes, wid, lane, d.row0, P);
     BSrc bs;
-    bs.rc[0] = make_rsrc(w.wg + (size_t)d.slot * mat, (uint32_t)mat);
-    bs.rc[1] = make_rsrc(w.wu + (size_t)d.slot * mat, (uint32_t)mat);
-    bs.rs[0] = make_rsrc(w.sg + (size_t)d.slot * smat, (uint32_t)smat);
-    bs.rs[1] = make_rsrc(w.su + (size_t)d.slot * smat, (uint32_t)smat);
-    bs.row8 = 8u * wrow;
+    BSrcPk bp;
+    if constexpr (PK) {
+      const size_t sbytes = pk_slot_bytes(H, I);
+      const uint32_t np = (uint32_t)pk_pairs(H), rb = (uint32_t)hc0 / 32u;
+      const uint32_t up0 = (uint32_t)(I / 32) * np * (uint32_t)kPkBlock;  // the up matrix's first block
+      bp.init(make_rsrc(pk + (size_t)d.slot * sbytes, (uint32_t)sbytes), rb * np * (uint32_t)kPkBlock,
+              up0 + rb * np * (uint32_t)kPkBlock, live, live, lane);
+    } else {
+      bs.rc[0] = make_rsrc(w.wg + (size_t)d.slot * mat, (uint32_t)mat);
+      bs.rc[1] = make_rsrc(w.wu + (size_t)d.slot * mat, (uint32_t)mat);
+      bs.rs[0] = make_rsrc(w.sg + (size_t)d.slot * smat, (uint32_t)smat);
+      bs.rs[1] = make_rsrc(w.su + (size_t)d.slot * smat, (uint32_t)smat);
+      bs.row8 = 8u * wrow;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      bs.vc[g] = live ? ((uint32_t)hc0 + (uint32_t)(lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7) : kOob;
-      bs.vs[g] = live ? ((uint32_t)hc0 + (uint32_t)r32) * (uint32_t)NBH + 8u * (uint32_t)(lane >> 5) : kOob;
+      for (int g = 0; g < 2; ++g) {
+        bs.vc[g] = live ? ((uint32_t)hc0 + (uint32_t)(lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7) : kOob;
+        bs.vs[g] = live ? ((uint32_t)hc0 + (uint32_t)r32) * (uint32_t)NBH + 8u * (uint32_t)(lane >> 5) : kOob;
+      }
     }
     const rsrc_t xsr = make_rsrc(xs, xs_bytes);
     auto tables = [&](int cw0) {
@@ -999,7 +1137,8 @@ __global__ __launch_bounds__(kTilePT, 1) void gateup_tile_kernel(
     f16v acc[4][2];
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[f][0] = acc[f][1] = f16v{};
-    tile_k_loop<true>(tb, st, bscr + wid * B_SCR, acc, as, bs, H / KC, tid, tables);  // ends on a barrier
+    if constexpr (PK) tile_k_loop_pk<true>(tb, st, acc, as, bp, H / KC, tid, tables);  // ends on a barrier
+    else tile_k_loop<true>(tb, st, bscr + wid * B_SCR, acc, as, bs, H / KC, tid, tables);
     // h = silu(g) * u and its MXFP6 block, in registers.  Lane l holds row
     // 32 f + l % 32 and columns 8 j + 4 (l / 32) + i of the wavefront's 32 in
     // register 4 j + i: the block's largest magnitude and its packed codes are
@@ -1057,13 +1196,14 @@ __global__ __launch_bounds__(kTilePT, 1) void gateup_tile_kernel(
 // a last tile narrower than 512 columns (hidden % 512 == 256) wavefronts 4-7
 // load zeros and store nothing.
 
+template <bool PK>
 __global__ __launch_bounds__(kTilePT, 1) void down_tile_kernel(
     const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, uint32_t hq_bytes, uint32_t hs_bytes, int P,
-    ExpertStore w, const int32_t* __restrict__ sorted_pair, const TileDesc* __restrict__ tiles,
-    const int32_t* __restrict__ counts, float* __restrict__ y) {
+    ExpertStore w, const uint8_t* __restrict__ pk, const int32_t* __restrict__ sorted_pair,
+    const TileDesc* __restrict__ tiles, const int32_t* __restrict__ counts, float* __restrict__ y) {
   __shared__ TileTables tb;
   __shared__ __attribute__((aligned(16))) uint8_t a0[A_STAGE], a1[A_STAGE], a2[A_STAGE], a3[A_STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t bscr[8 * B_SCR];
+  __shared__ __attribute__((aligned(16))) uint8_t bscr[PK ? 16 : 8 * B_SCR];
   __shared__ int rowtok[BM];
   uint8_t* const st[4] = {a0, a1, a2, a3};
   const int H = w.H, I = w.I, NBI = I / 32;
@@ -1090,16 +1230,25 @@ __global__ __launch_bounds__(kTilePT, 1) void down_tile_kernel(
     ACopy as;
     as.init(hq, hq_bytes, wid, lane, d.row0, P);
     BSrc bs;
-    const rsrc_t rd = make_rsrc(w.wd + (size_t)d.slot * mat, (uint32_t)mat);
-    const rsrc_t sdr = make_rsrc(w.sd + (size_t)d.slot * smat, (uint32_t)smat);
-    bs.row8 = 8u * wrow;
+    BSrcPk bp;
+    if constexpr (PK) {
+      const size_t sbytes = pk_slot_bytes(H, I);
+      const uint32_t np = (uint32_t)pk_pairs(I), rb = (uint32_t)nc0 / 32u;
+      const uint32_t dn0 = 2u * (uint32_t)(I / 32) * (uint32_t)pk_pairs(H) * (uint32_t)kPkBlock;  // first down block
+      bp.init(make_rsrc(pk + (size_t)d.slot * sbytes, (uint32_t)sbytes), dn0 + rb * np * (uint32_t)kPkBlock,
+              dn0 + (rb + 1u) * np * (uint32_t)kPkBlock, live, live, lane);
+    } else {
+      const rsrc_t rd = make_rsrc(w.wd + (size_t)d.slot * mat, (uint32_t)mat);
+      const rsrc_t sdr = make_rsrc(w.sd + (size_t)d.slot * smat, (uint32_t)smat);
+      bs.row8 = 8u * wrow;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const uint32_t row = (uint32_t)(nc0 + 32 * g);
-      bs.rc[g] = rd;
-      bs.rs[g] = sdr;
-      bs.vc[g] = live ? (row + (uint32_t)(lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7) : kOob;
-      bs.vs[g] = live ? (row + (uint32_t)r32) * (uint32_t)NBI + 8u * (uint32_t)(lane >> 5) : kOob;
+      for (int g = 0; g < 2; ++g) {
+        const uint32_t row = (uint32_t)(nc0 + 32 * g);
+        bs.rc[g] = rd;
+        bs.rs[g] = sdr;
+        bs.vc[g] = live ? (row + (uint32_t)(lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7) : kOob;
+        bs.vs[g] = live ? (row + (uint32_t)r32) * (uint32_t)NBI + 8u * (uint32_t)(lane >> 5) : kOob;
+      }
     }
     const rsrc_t hsr = make_rsrc(hs, hs_bytes);
     auto tables = [&](int cw0) {
@@ -1112,7 +1261,8 @@ __global__ __launch_bounds__(kTilePT, 1) void down_tile_kernel(
     f16v acc[4][2];
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[f][0] = acc[f][1] = f16v{};
-    tile_k_loop<false>(tb, st, bscr + wid * B_SCR, acc, as, bs, I / KC, tid, tables);
+    if constexpr (PK) tile_k_loop_pk<false>(tb, st, acc, as, bp, I / KC, tid, tables);
+    else tile_k_loop<false>(tb, st, bscr + wid * B_SCR, acc, as, bs, I / KC, tid, tables);
     if (live) {
       const int t = opaque(tid), e32 = t & 31, eh = (t >> 5) & 1;
 #pragma unroll
@@ -1133,6 +1283,58 @@ __global__ __launch_bounds__(kTilePT, 1) void down_tile_kernel(
   wait_vm<0>();  // no copy into LDS outlives the workgroup
 }
 
+// ---- the packed copy ------------------------------------------------------------------
+//
+// One thread per (slot, matrix, 32-row block, chunk pair, lane): it gathers
+// the lane's 16 code bytes of each K-step and its four scale bytes from the
+// row-major store (zeros past K) and writes them where the operand-order
+// loads read them, 1 KB per K-step and wavefront.
+__global__ __launch_bounds__(256) void pack_weights_kernel(ExpertStore w, uint8_t* __restrict__ dst) {
+  const int H = w.H, I = w.I, slot = blockIdx.y;
+  const long u = (long)blockIdx.x * 256 + threadIdx.x;
+  const int npg = pk_pairs(H), npd = pk_pairs(I);
+  const long ngu = (long)(I / 32) * npg, ndn = (long)(H / 32) * npd;
+  const long blk = u >> 6;
+  if (blk >= 2 * ngu + ndn) return;
+  const int t = (int)(u & 63), r32 = t & 31, h = t >> 5;
+  int K, np;
+  long b;
+  const uint8_t *codes, *scales;
+  if (blk < 2 * ngu) {
+    const int m = blk < ngu ? 0 : 1;
+    b = blk - m * ngu;
+    K = H;
+    np = npg;
+    codes = (m ? w.wu : w.wg) + (size_t)slot * I * (H / 2);
+    scales = (m ? w.su : w.sg) + (size_t)slot * I * (H / 32);
+  } else {
+    b = blk - 2 * ngu;
+    K = I;
+    np = npd;
+    codes = w.wd + (size_t)slot * H * (I / 2);
+    scales = w.sd + (size_t)slot * H * (I / 32);
+  }
+  const long rb = b / np;
+  const int pq = (int)(b - rb * np);
+  const long row = rb * 32 + r32;
+  const int KB = K / 2, NB = K / 32;
+  uint8_t* o = dst + (size_t)slot * pk_slot_bytes(H, I) + (size_t)blk * kPkBlock;
+#pragma unroll
+  for (int S = 0; S < 4; ++S) {
+    const int off = 128 * pq + 32 * S + 16 * h;  // the lane's code bytes of K-step S within the row
+    uint4_t v = {0u, 0u, 0u, 0u};
+    if (off < KB) v = *reinterpret_cast<const uint4_t*>(codes + (size_t)row * KB + off);
+    *reinterpret_cast<uint4_t*>(o + S * 1024 + 16 * t) = v;
+  }
+  uint32_t word = 0u;
+#pragma unroll
+  for (int S = 0; S < 4; ++S) {
+    const int blkk = 8 * pq + 2 * S + h;  // scale block of K-step S for this lane
+    if (blkk < NB) word |= (uint32_t)scales[(size_t)row * NB + blkk] << (8 * S);
+  }
+  *reinterpret_cast<uint32_t*>(o + 4096 + 4 * t) = word;
+}
+
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Upper bound of the row tiles of a call: one ragged tile per non-empty bucket.
@@ -1148,9 +1350,19 @@ size_t prefill_workspace_bytes(int T, int k, int H, int I) {
          align256((size_t)T * H / 32 * 24) + align256((size_t)T * H / 32);
 }
 
+size_t prefill_packed_bytes(int num_slots, int H, int I) { return (size_t)num_slots * pk_slot_bytes(H, I); }
+
+hipError_t launch_pack_weights(const ExpertStore& w, uint8_t* dst, hipStream_t s) {
+  if (w.num_slots <= 0) return hipSuccess;
+  const long threads = 64L * (2L * (w.I / 32) * pk_pairs(w.H) + (long)(w.H / 32) * pk_pairs(w.I));
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((threads + 255) / 256), (unsigned)w.num_slots), dim3(256), 0, s,
+                     w, dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertStore& w, const int32_t* e2s,
                           const int32_t* offsets, const int32_t* sorted_pair, float* y_pair, void* ws,
-                          hipStream_t s, const uint8_t* run) {
+                          hipStream_t s, const uint8_t* run, const uint8_t* packed) {
   const int H = w.H, I = w.I;
   if (H % 256 != 0 || I % 128 != 0) return hipErrorInvalidValue;
   const int ntw_gu = (I + GU_N - 1) / GU_N, ntw_dn = (H + DN_N - 1) / DN_N;
@@ -1190,16 +1402,24 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
                      w, sorted_pair, sbk, counts, hq, hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(gateup_tile_kernel, dim3(kGrid), dim3(kTilePT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, (int)P, w,
-                     gu, counts, hq, hs);
+  if (packed)
+    hipLaunchKernelGGL(gateup_tile_kernel<true>, dim3(kGrid), dim3(kTilePT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b,
+                       (int)P, w, packed, gu, counts, hq, hs);
+  else
+    hipLaunchKernelGGL(gateup_tile_kernel<false>, dim3(kGrid), dim3(kTilePT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b,
+                       (int)P, w, packed, gu, counts, hq, hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(down_skinny_kernel, dim3(dn_grid), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, (int)P, w,
                      sorted_pair, sbk, counts, y_pair);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(down_tile_kernel, dim3(kGrid), dim3(kTilePT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, (int)P, w,
-                     sorted_pair, dn, counts, y_pair);
+  if (packed)
+    hipLaunchKernelGGL(down_tile_kernel<true>, dim3(kGrid), dim3(kTilePT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b,
+                       (int)P, w, packed, sorted_pair, dn, counts, y_pair);
+  else
+    hipLaunchKernelGGL(down_tile_kernel<false>, dim3(kGrid), dim3(kTilePT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b,
+                       (int)P, w, packed, sorted_pair, dn, counts, y_pair);
   return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@ EXPORTED = ("moe_route", "moe_router_logits", "moe_route_x", "moe_ffn_cb3_decode
             "moe_decode_layer_workspace_bytes", "moe_decode_layer", "moe_decode_layer_noalloc", "moe_decode_layer_gateup",
             "moe_decode_layer_invariant_workspace_bytes", "moe_decode_layer_invariant",
             "moe_decode_layer_down", "moe_decode_layer_rmsnorm_workspace_bytes", "moe_decode_layer_rmsnorm",
-            "moe_ffn_fp4_prefill_workspace_bytes", "moe_ffn_fp4_prefill", "moe_ffn_fp4_prefill_subset", "moe_combine",
+            "moe_ffn_fp4_prefill_workspace_bytes", "moe_ffn_fp4_prefill", "moe_ffn_fp4_prefill_subset",
+            "moe_prefill_packed_bytes", "moe_prefill_pack_weights", "moe_ffn_fp4_prefill_packed", "moe_combine",
             "moe_rmsnorm_bf16", "moe_status_string")
 
 
@@ -95,6 +96,10 @@ def lib() -> ctypes.CDLL:
                                     vp, vp, sz, vp],
             "moe_ffn_fp4_prefill_subset": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, vp, vp, vp,
                                            ctypes.c_int, vp, vp, sz, vp],
+            "moe_prefill_packed_bytes": [i32, i32, i32],
+            "moe_prefill_pack_weights": [ctypes.POINTER(CExperts), vp, sz, vp],
+            "moe_ffn_fp4_prefill_packed": [vp, i32, i32, i32, ctypes.POINTER(CExperts), vp, sz, vp, vp, vp,
+                                           ctypes.c_int, vp, vp, sz, vp],
             "moe_combine": [vp, vp, i32, i32, i32, vp, ctypes.c_int, vp, vp],
             "moe_rmsnorm_bf16": [vp, i32, i32, f32, vp, vp],
             "moe_status_string": [ctypes.c_int],
@@ -107,6 +112,7 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_cb3_decode_workspace_bytes.restype = sz
         L.moe_ffn_fp4_decode_workspace_bytes.restype = sz
         L.moe_ffn_fp4_prefill_workspace_bytes.restype = sz
+        L.moe_prefill_packed_bytes.restype = sz
         L.moe_decode_layer_workspace_bytes.restype = sz
         L.moe_decode_layer_invariant_workspace_bytes.restype = sz
         L.moe_decode_layer_rmsnorm_workspace_bytes.restype = sz
@@ -570,6 +576,42 @@ def moe_ffn_fp4_prefill(x: torch.Tensor, k: int, E: int, store: ExpertStore,
     _check("moe_ffn_fp4_prefill", lib().moe_ffn_fp4_prefill(
         _ptr(x), T, k, E, ctypes.byref(cs), _ptr(expert_to_slot), _ptr(expert_offsets), _ptr(sorted_pair),
         act, _ptr(y_pair), _ptr(ws), ws.numel(), _stream(x.device)))
+    return y_pair
+
+
+def prefill_packed_bytes(num_slots: int, hidden: int, inter: int) -> int:
+    """Bytes of the experts' copy in MFMA operand order (0: unsupported shape)."""
+    return int(lib().moe_prefill_packed_bytes(num_slots, hidden, inter))
+
+
+def moe_prefill_pack_weights(store: ExpertStore, packed: torch.Tensor | None = None) -> torch.Tensor:
+    """Write the copy of ``store`` that moe_ffn_fp4_prefill_packed's tiled GEMMs read."""
+    need = prefill_packed_bytes(store.num_slots, store.hidden, store.inter)
+    dev = store.w_gate.device
+    if packed is None:
+        packed = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _want(packed, (torch.uint8,), "packed")
+    cs = store.cstruct()
+    _check("moe_prefill_pack_weights", lib().moe_prefill_pack_weights(
+        ctypes.byref(cs), _ptr(packed), packed.numel(), _stream(dev)))
+    return packed
+
+
+def moe_ffn_fp4_prefill_packed(x: torch.Tensor, k: int, E: int, store: ExpertStore, packed: torch.Tensor,
+                               expert_to_slot: torch.Tensor | None, expert_offsets: torch.Tensor,
+                               sorted_pair: torch.Tensor, y_pair: torch.Tensor | None = None,
+                               ws: torch.Tensor | None = None, act: int = MOE_ACT_MXFP6_E2M3) -> torch.Tensor:
+    """moe_ffn_fp4_prefill with the tiled GEMMs on ``packed`` (moe_prefill_pack_weights of the same store)."""
+    T, y_pair = _ffn_args(x, k, store, expert_to_slot, expert_offsets, sorted_pair, y_pair)
+    need = prefill_workspace_bytes(T, k, store.hidden, store.inter)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _want(ws, (torch.uint8,), "ws")
+    _want(packed, (torch.uint8,), "packed")
+    cs = store.cstruct()
+    _check("moe_ffn_fp4_prefill_packed", lib().moe_ffn_fp4_prefill_packed(
+        _ptr(x), T, k, E, ctypes.byref(cs), _ptr(packed), packed.numel(), _ptr(expert_to_slot),
+        _ptr(expert_offsets), _ptr(sorted_pair), act, _ptr(y_pair), _ptr(ws), ws.numel(), _stream(x.device)))
     return y_pair
 
 

@@ -389,6 +389,43 @@ MOE_FP4_API moe_status moe_ffn_fp4_prefill(const uint16_t* x_bf16, int32_t T, in
                                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_prefill_pack_weights, moe_ffn_fp4_prefill_packed -- moe_ffn_fp4_prefill
+ * with its tiled GEMMs reading a second copy of the experts laid out in the
+ * block-scaled MFMA's operand order.  Prefill re-reads each touched expert
+ * once per tile of its tokens and is bound by how fast the weights reach the
+ * matrix cores ("DeepSeek V4.1 Flash Q4 / 27 September 2026", "30 September
+ * follow-up: prefill"); the copy is made once, when the experts are loaded.
+ * Layout of the copy: for each slot, the gate, up and down matrices in turn
+ * (gate and up: inter rows of hidden; down: hidden rows of inter), each as
+ * blocks of 32 rows x 256 K elements, ordered by row block then K; a block is
+ * 4 K-steps x 64 lanes x 16 code bytes (lane l: row l % 32, code bytes
+ * 16 (l / 32) .. +15 of the K-step's 32 bytes of that row), then 64 lanes x
+ * 4 scale bytes (byte S of lane l: the UE8M0 byte of the row's 32-block
+ * 8 j + 2 S + l / 32, j the block's index along K).  Past K (inter % 256 ==
+ * 128) codes and scales are zero.
+ *   moe_prefill_packed_bytes(num_slots, hidden, inter): bytes of the copy
+ *     (0 for an unsupported shape: hidden % 256 or inter % 128 nonzero)
+ *   moe_prefill_pack_weights: writes the copy of every slot of w into
+ *     packed (device, 256-byte aligned, packed_bytes at least the size above;
+ *     MOE_ERR_WORKSPACE otherwise); asynchronous on stream
+ *   moe_ffn_fp4_prefill_packed: arguments as moe_ffn_fp4_prefill, plus the
+ *     copy of the same w.  The result is bit-identical to moe_ffn_fp4_prefill:
+ *     the same MFMAs in the same order, only the weights' path differs.  The
+ *     small-bucket kernels still stream w itself.  A copy that does not
+ *     match w gives wrong results; a NULL or short copy with T >= 1 is
+ *     MOE_ERR_NULL / MOE_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------- */
+MOE_FP4_API size_t moe_prefill_packed_bytes(int32_t num_slots, int32_t hidden, int32_t inter);
+MOE_FP4_API moe_status moe_prefill_pack_weights(const moe_fp4_experts* w, void* packed, size_t packed_bytes,
+                                                hipStream_t stream);
+MOE_FP4_API moe_status moe_ffn_fp4_prefill_packed(const uint16_t* x_bf16, int32_t T, int32_t k, int32_t E,
+                                                  const moe_fp4_experts* w, const void* packed,
+                                                  size_t packed_bytes, const int32_t* expert_to_slot,
+                                                  const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                                  moe_act_fmt act, float* y_pair, void* ws, size_t ws_bytes,
+                                                  hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_ffn_fp4_decode_subset, moe_ffn_fp4_prefill_subset -- the expert FFN
  * over a subset of the experts: the two-wave routed MoE of the M5 Max page
  * ("DeepSeek V4.1 Flash Q4 / 27 September 2026", "30 September follow-up:

@@ -156,6 +156,34 @@ def test_subset_validation():
     assert pre(T=0, mask=None) == m.MOE_OK
 
 
+def test_packed_prefill_validation():
+    """The operand-order copy of the experts: its size, and the pack and packed
+    prefill calls' argument checks (no launch is reached)."""
+    m = _lib()
+    L = m.lib()
+    st = _store(m)
+    # hidden 256, inter 128: gate and up 4 row blocks x 1 pair, down 8 row blocks x 1 (half-empty) pair
+    assert L.moe_prefill_packed_bytes(8, 256, 128) == 8 * 16 * 4352
+    # hidden 5120, inter 2304: 2 x 72 x 20 + 160 x 9 blocks of 4352 bytes per slot
+    assert L.moe_prefill_packed_bytes(384, 5120, 2304) == 384 * (2 * 72 * 20 + 160 * 9) * 4352
+    assert L.moe_prefill_packed_bytes(8, 320, 128) == 0
+    assert L.moe_prefill_packed_bytes(8, 256, 96) == 0
+    assert L.moe_prefill_packed_bytes(0, 256, 128) == 0
+    need = L.moe_prefill_packed_bytes(8, 256, 128)
+    assert L.moe_prefill_pack_weights(None, FAKE, need, None) == m.MOE_ERR_NULL
+    assert L.moe_prefill_pack_weights(ctypes.byref(st), None, need, None) == m.MOE_ERR_NULL
+    assert L.moe_prefill_pack_weights(ctypes.byref(st), MIS, need, None) == m.MOE_ERR_ALIGN
+    assert L.moe_prefill_pack_weights(ctypes.byref(st), FAKE, need - 1, None) == m.MOE_ERR_WORKSPACE
+    pre = lambda packed=FAKE, pbytes=need, T=4, x=FAKE, ws_bytes=1 << 30: L.moe_ffn_fp4_prefill_packed(
+        x, T, 2, 8, ctypes.byref(st), packed, pbytes, None, FAKE, FAKE, 0, FAKE, FAKE, ws_bytes, None)
+    assert pre(packed=None) == m.MOE_ERR_NULL
+    assert pre(packed=MIS) == m.MOE_ERR_ALIGN
+    assert pre(pbytes=need - 1) == m.MOE_ERR_WORKSPACE
+    assert pre(x=None) == m.MOE_ERR_NULL
+    assert pre(ws_bytes=0) == m.MOE_ERR_WORKSPACE
+    assert pre(T=0, packed=None) == m.MOE_OK
+
+
 def test_prefill_and_combine_validation():
     m = _lib()
     L = m.lib()
