@@ -703,7 +703,9 @@ __device__ __forceinline__ void tile_k_loop(TileTables& tb, uint8_t* const (&st)
 // A wavefront then loads each fragment's K-step operand as one contiguous
 // 1 KB straight into the register the MFMA reads and its scale word in one
 // 256-byte load: no trip through LDS, no reordering, and two lines of scales
-// per fragment and pair instead of 32.
+// per fragment and pair instead of 32.  The small-bucket kernels read the
+// same blocks (a unit's 32 gate and 32 up rows, or 64 down rows, are whole
+// row blocks).
 
 constexpr int kPkBlock = 4096 + 256;  // bytes of a (32-row block, chunk pair) of the packed copy
 
@@ -849,7 +851,8 @@ __device__ __forceinline__ float swiglu_fast(float g, float u) {
 // an operand streams at about two thirds of this rate from memory).
 struct SkRegs {
   uint4_t a[2][3];  // [chunk][16 B of the lane's 48-byte record]: K-step 2c bytes 0-23, 2c+1 bytes 24-47
-  uint4_t b[2][4];  // [fragment][load]
+  uint4_t b[2][4];  // [fragment][load] (packed weights: [fragment][K-step], in operand order)
+  uint32_t ws[2];   // packed weights: each fragment's scale word of the pair (byte S: K-step S)
 };
 
 // Scale words come from a per-wavefront LDS table read once per window of
@@ -864,6 +867,9 @@ struct SkSrc {
   uint32_t va, vb[2];  // va: the lane's record (row r32, K-half h) in chunk 0; vb: row l / 8 of the fragment, + 16 (l % 8)
   uint32_t cstride;    // bytes per chunk of the A records
   uint32_t row8;       // bytes from a weight row to the row 8 below
+  rsrc_t rp;           // packed weights: the slot's blocks
+  uint32_t pb[2];      // packed weights: the lane's code bytes in fragment g's first block
+  template <bool PK>
   __device__ __forceinline__ void load(int n, SkRegs& r) const {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {  // chunk 2n + c: the lane's whole record (records are 48 B, 16-B aligned)
@@ -871,10 +877,21 @@ struct SkSrc {
 #pragma unroll
       for (int j = 0; j < 3; ++j) r.a[c][j] = bload16(ra, o + 16u * j);
     }
+    if constexpr (PK) {
+      // the pair's scale words first, then its four K-step operands per fragment
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+      for (int g = 0; g < 2; ++g)
+        r.ws[g] = bload4(rp, pb[g] + (uint32_t)n * kPkBlock + 4096u - 12u * (uint32_t)(__lane_id()));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r.b[g][j] = bload16(rb[g], vb[g] + (uint32_t)j * row8 + (uint32_t)n * 128u);
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int S = 0; S < 4; ++S) r.b[g][S] = bload16(rp, pb[g] + (uint32_t)n * kPkBlock + (uint32_t)S * 1024u);
+    } else {
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r.b[g][j] = bload16(rb[g], vb[g] + (uint32_t)j * row8 + (uint32_t)n * 128u);
+    }
   }
 };
 
@@ -895,12 +912,20 @@ __device__ __forceinline__ void sk_operands(const uint4_t (&b)[4], uint8_t* scr,
   }
 }
 
+template <bool PK>
 __device__ __forceinline__ void sk_mma(const SkRegs& r, f16v (&acc)[2], int nks, int h, const uint32_t* tab,
                                        int cw, uint8_t* scr) {  // cw: the batch's first chunk within the window
   const int r32 = __lane_id() & 31;
   i8v bop[2][4];  // [fragment][K-step]
+  if constexpr (PK) {
 #pragma unroll
-  for (int g = 0; g < 2; ++g) sk_operands(r.b[g], scr, bop[g]);
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bop[g][k] = i8v{(int)r.b[g][k].x, (int)r.b[g][k].y, (int)r.b[g][k].z, (int)r.b[g][k].w, 0, 0, 0, 0};
+  } else {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) sk_operands(r.b[g], scr, bop[g]);
+  }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     if (s < nks) {
@@ -912,8 +937,16 @@ __device__ __forceinline__ void sk_mma(const SkRegs& r, f16v (&acc)[2], int nks,
       const int sa = (int)((tab[r32 * SKW + cw + (s >> 1)] >> (8 * h)) >> (16 * (s & 1)));
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const int sb = (int)((tab[(32 + 32 * g + r32) * SKW + cw + (s >> 1)] >> (8 * h)) >> (16 * (s & 1)));
-        acc[g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop[g][s], acc[g], 2, 4, 0, sa, 0, sb);
+        if constexpr (PK) {
+          const int sb = (int)r.ws[g];  // byte s: K-step s
+          if (s == 0) acc[g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop[g][s], acc[g], 2, 4, 0, sa, 0, sb);
+          if (s == 1) acc[g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop[g][s], acc[g], 2, 4, 0, sa, 1, sb);
+          if (s == 2) acc[g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop[g][s], acc[g], 2, 4, 0, sa, 2, sb);
+          if (s == 3) acc[g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop[g][s], acc[g], 2, 4, 0, sa, 3, sb);
+        } else {
+          const int sb = (int)((tab[(32 + 32 * g + r32) * SKW + cw + (s >> 1)] >> (8 * h)) >> (16 * (s & 1)));
+          acc[g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop[g][s], acc[g], 2, 4, 0, sa, 0, sb);
+        }
       }
     }
   }
@@ -934,7 +967,7 @@ struct SkTables {
 // other's waits.  The load after the last batch re-reads it (never used): no
 // load behind a branch.  tables(cw0, ts) issues the scale-table loads of the
 // window starting at chunk cw0.
-template <typename TS, typename Tables>
+template <typename TS, bool PK, typename Tables>
 __device__ __forceinline__ void sk_k_loop(const SkSrc& src, f16v (&acc)[2], int K, int h, uint32_t* tab,
                                           uint8_t* scr, Tables tables) {
   const int nks_total = K / 64, nchunks = K / KC;
@@ -944,14 +977,16 @@ __device__ __forceinline__ void sk_k_loop(const SkSrc& src, f16v (&acc)[2], int 
     TS ts;
     tables(cw0, ts);
     SkRegs r0;
-    src.load(b0, r0);
+    src.load<PK>(b0, r0);
     ts.a.store(tab, lane);
-    ts.b[0].store(tab + 32 * SKW, lane);
-    ts.b[1].store(tab + 64 * SKW, lane);
+    if constexpr (!PK) {
+      ts.b[0].store(tab + 32 * SKW, lane);
+      ts.b[1].store(tab + 64 * SKW, lane);
+    }
     __builtin_amdgcn_wave_barrier();  // a wavefront's LDS accesses complete in order
     for (int n = b0; n <= last; ++n) {
-      sk_mma(r0, acc, min(4, nks_total - 4 * n), h, tab, 2 * (n - b0), scr);
-      src.load(min(n + 1, last), r0);
+      sk_mma<PK>(r0, acc, min(4, nks_total - 4 * n), h, tab, 2 * (n - b0), scr);
+      src.load<PK>(min(n + 1, last), r0);
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -961,9 +996,10 @@ __device__ __forceinline__ void sk_k_loop(const SkSrc& src, f16v (&acc)[2], int 
 // workgroup); those past the plan's unit count exit at once, and the hardware
 // dispatcher balances the rest.
 
+template <bool PK>  // PK: weights from the packed copy pk (operand order), else the row-major store
 __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, uint32_t xq_bytes, uint32_t xs_bytes, int P,
-    ExpertStore w, const int32_t* __restrict__ sorted_pair, const SkBucket* __restrict__ sbk,
+    ExpertStore w, const uint8_t* __restrict__ pk, const int32_t* __restrict__ sorted_pair, const SkBucket* __restrict__ sbk,
     const int32_t* __restrict__ counts, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
   __shared__ float stage[4][32 * 33];
   __shared__ uint32_t sktab[4][96 * SKW];
@@ -986,17 +1022,26 @@ __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
     src.rb[1] = make_rsrc(w.wu + (size_t)bk.slot * mat, (uint32_t)mat);
     src.vb[0] = src.vb[1] = (uint32_t)(32 * q + (lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7);
     src.row8 = 8u * wrow;
+    if constexpr (PK) {
+      const size_t sbytes = pk_slot_bytes(H, I);
+      const uint32_t np = (uint32_t)pk_pairs(H);
+      src.rp = make_rsrc(pk + (size_t)bk.slot * sbytes, (uint32_t)sbytes);
+      src.pb[0] = (uint32_t)q * np * (uint32_t)kPkBlock + 16u * (uint32_t)lane;
+      src.pb[1] = src.pb[0] + (uint32_t)(I / 32) * np * (uint32_t)kPkBlock;  // the up matrix
+    }
     const rsrc_t xsr = make_rsrc(xs, xs_bytes);
     const rsrc_t sgr = make_rsrc(w.sg + (size_t)bk.slot * smat, (uint32_t)smat);
     const rsrc_t sur = make_rsrc(w.su + (size_t)bk.slot * smat, (uint32_t)smat);
     using TS = SkTables<ScaleCols<32, 64, SKWIN, SKW>>;
     auto tables = [&](int cw0, TS& ts) {
       ts.a.issue(xsr, cw0, lane, bk.row0, bk.cnt, P);
-      ts.b[0].issue(sgr, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NBH; });
-      ts.b[1].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NBH; });
+      if constexpr (!PK) {
+        ts.b[0].issue(sgr, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NBH; });
+        ts.b[1].issue(sur, cw0, lane, [&](int r) { return (uint32_t)(32 * q + r) * NBH; });
+      }
     };
     f16v acc[2] = {f16v{}, f16v{}};
-    sk_k_loop<TS>(src, acc, H, h, sktab[wid], skscr[wid], tables);
+    sk_k_loop<TS, PK>(src, acc, H, h, sktab[wid], skscr[wid], tables);
     // h = silu(g) * u: rows of the bucket x this unit's 32 h columns (one MXFP6 block per row)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -1021,9 +1066,10 @@ __global__ __launch_bounds__(kPT, 2) void gateup_skinny_kernel(
   }
 }
 
+template <bool PK>
 __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
     const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, uint32_t hq_bytes, uint32_t hs_bytes, int P,
-    ExpertStore w, const int32_t* __restrict__ sorted_pair, const SkBucket* __restrict__ sbk,
+    ExpertStore w, const uint8_t* __restrict__ pk, const int32_t* __restrict__ sorted_pair, const SkBucket* __restrict__ sbk,
     const int32_t* __restrict__ counts, float* __restrict__ y) {
   __shared__ uint32_t sktab[4][96 * SKW];
   __shared__ __attribute__((aligned(16))) uint8_t skscr[4][SK_SCR];
@@ -1051,16 +1097,26 @@ __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
       src.vb[g] = (uint32_t)(n0 + 32 * g + (lane >> 3)) * wrow + 16u * (uint32_t)(lane & 7);
     }
     src.row8 = 8u * wrow;
+    if constexpr (PK) {
+      const size_t sbytes = pk_slot_bytes(H, I);
+      const uint32_t np = (uint32_t)pk_pairs(I), rb = (uint32_t)n0 / 32u;
+      const uint32_t dn0 = 2u * (uint32_t)(I / 32) * (uint32_t)pk_pairs(H) * (uint32_t)kPkBlock;  // first down block
+      src.rp = make_rsrc(pk + (size_t)bk.slot * sbytes, (uint32_t)sbytes);
+      src.pb[0] = dn0 + rb * np * (uint32_t)kPkBlock + 16u * (uint32_t)lane;
+      src.pb[1] = src.pb[0] + np * (uint32_t)kPkBlock;
+    }
     const rsrc_t hsr = make_rsrc(hs, hs_bytes);
     const rsrc_t sdr = make_rsrc(w.sd + (size_t)bk.slot * smat, (uint32_t)smat);
     using TS = SkTables<ScaleRows<32, 64, SKWIN, SKW>>;
     auto tables = [&](int cw0, TS& ts) {
       ts.a.issue(hsr, cw0, lane, [&](int r) { return r < bk.cnt ? (uint32_t)(bk.row0 + r) * NBI : kOob; });
-      ts.b[0].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + r) * NBI; });
-      ts.b[1].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + 32 + r) * NBI; });
+      if constexpr (!PK) {
+        ts.b[0].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + r) * NBI; });
+        ts.b[1].issue(sdr, cw0, lane, [&](int r) { return (uint32_t)(n0 + 32 + r) * NBI; });
+      }
     };
     f16v acc[2] = {f16v{}, f16v{}};
-    sk_k_loop<TS>(src, acc, I, h, sktab[wid], skscr[wid], tables);
+    sk_k_loop<TS, PK>(src, acc, I, h, sktab[wid], skscr[wid], tables);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = (i >> 2) * 8 + h * 4 + (i & 3);
@@ -1398,8 +1454,12 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
   if (err != hipSuccess) return err;
   const size_t nsk = min((size_t)E, P);  // small buckets at most
   const int gu_grid = (int)((nsk * (size_t)(I / 32) + 3) / 4), dn_grid = (int)((nsk * (size_t)(H / 64) + 3) / 4);
-  hipLaunchKernelGGL(gateup_skinny_kernel, dim3(gu_grid), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b, (int)P,
-                     w, sorted_pair, sbk, counts, hq, hs);
+  if (packed)
+    hipLaunchKernelGGL(gateup_skinny_kernel<true>, dim3(gu_grid), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b,
+                       (int)P, w, packed, sorted_pair, sbk, counts, hq, hs);
+  else
+    hipLaunchKernelGGL(gateup_skinny_kernel<false>, dim3(gu_grid), dim3(kPT), 0, s, xq, xs, (uint32_t)xq_b, (uint32_t)xs_b,
+                       (int)P, w, packed, sorted_pair, sbk, counts, hq, hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (packed)
@@ -1410,8 +1470,12 @@ hipError_t launch_prefill(const uint16_t* x, int T, int k, int E, const ExpertSt
                        (int)P, w, packed, gu, counts, hq, hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(down_skinny_kernel, dim3(dn_grid), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b, (int)P, w,
-                     sorted_pair, sbk, counts, y_pair);
+  if (packed)
+    hipLaunchKernelGGL(down_skinny_kernel<true>, dim3(dn_grid), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b,
+                       (int)P, w, packed, sorted_pair, sbk, counts, y_pair);
+  else
+    hipLaunchKernelGGL(down_skinny_kernel<false>, dim3(dn_grid), dim3(kPT), 0, s, hq, hs, (uint32_t)hq_b, (uint32_t)hs_b,
+                       (int)P, w, packed, sorted_pair, sbk, counts, y_pair);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (packed)

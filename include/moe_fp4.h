@@ -410,10 +410,11 @@ MOE_FP4_API moe_status moe_ffn_fp4_prefill(const uint16_t* x_bf16, int32_t T, in
  *     MOE_ERR_WORKSPACE otherwise); asynchronous on stream
  *   moe_ffn_fp4_prefill_packed: arguments as moe_ffn_fp4_prefill, plus the
  *     copy of the same w.  The result is bit-identical to moe_ffn_fp4_prefill:
- *     the same MFMAs in the same order, only the weights' path differs.  The
- *     small-bucket kernels still stream w itself.  A copy that does not
- *     match w gives wrong results; a NULL or short copy with T >= 1 is
- *     MOE_ERR_NULL / MOE_ERR_WORKSPACE.
+ *     the same MFMAs in the same order, only the weights' path differs.  Both
+ *     the tiled GEMMs and the small-bucket kernels read the copy; w gives the
+ *     shape and the slot count.  A copy that does not match w gives wrong
+ *     results; a NULL or short copy with T >= 1 is MOE_ERR_NULL /
+ *     MOE_ERR_WORKSPACE.
  * ------------------------------------------------------------------------- */
 MOE_FP4_API size_t moe_prefill_packed_bytes(int32_t num_slots, int32_t hidden, int32_t inter);
 MOE_FP4_API moe_status moe_prefill_pack_weights(const moe_fp4_experts* w, void* packed, size_t packed_bytes,

@@ -1,5 +1,6 @@
 """The prefill FFN on the experts' copy in MFMA operand order
-(moe_prefill_pack_weights, moe_ffn_fp4_prefill_packed), through the C ABI:
+(moe_prefill_pack_weights, moe_ffn_fp4_prefill_packed: tiled and small-bucket
+kernels both read the copy), through the C ABI:
 the copy's layout against its definition in the header, and the packed call
 bit-identical to moe_ffn_fp4_prefill (which the prefill parity tests compare
 with the oracle), plus a direct oracle comparison."""
