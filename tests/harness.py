@@ -61,15 +61,19 @@ class GpuLayer:
         self.weights = gi.HostWeights(cfg, layer)
 
     def run(self, path: str = "decode", x=None, logits=None, residual=None, out_dtype=None):
-        """route -> permute -> FFN (decode or prefill) -> combine, all on the device."""
+        """route -> permute -> FFN (decode, prefill or prefill_packed) -> combine, all on the device."""
         import fp4_routed_expert_mxfp4_amd as m
         cfg = self.cfg
         x = self.x if x is None else x
         logits = self.logits if logits is None else logits
         ids, w = m.moe_route(logits, cfg.k, self.e2s)
         off, sp, p2r = m.moe_permute(ids, cfg.E)
-        ffn = m.moe_ffn_fp4_decode if path == "decode" else m.moe_ffn_fp4_prefill
-        y = ffn(x, cfg.k, cfg.E, self.store, self.e2s, off, sp)
+        if path == "prefill_packed":  # the prefill FFN on the experts' operand-order copy
+            packed = m.moe_prefill_pack_weights(self.store)
+            y = m.moe_ffn_fp4_prefill_packed(x, cfg.k, cfg.E, self.store, packed, self.e2s, off, sp)
+        else:
+            ffn = m.moe_ffn_fp4_decode if path == "decode" else m.moe_ffn_fp4_prefill
+            y = ffn(x, cfg.k, cfg.E, self.store, self.e2s, off, sp)
         out32 = m.moe_combine(y, w, residual, m.MOE_OUT_F32)
         out16 = m.moe_combine(y, w, residual, m.MOE_OUT_BF16)
         torch.cuda.synchronize()
