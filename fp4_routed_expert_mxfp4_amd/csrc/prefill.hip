@@ -24,6 +24,13 @@
 // weight tile, row tile -- row tiles of one weight tile adjacent, so they
 // share that weight tile in L2) is split into eight contiguous ranges, one
 // per XCD.
+//
+// The weights come either from the row-major expert store (each load covers
+// 8 rows x 128 B and is reordered through LDS into operand order) or from a
+// copy of the experts in operand order (pack_weights_kernel, made once when
+// the experts are loaded), from which each K-step's operand is one
+// contiguous 1 KB load straight into the MFMA's register.  Both give the
+// same bytes to the same MFMAs in the same order.
 #include "common.cuh"
 #include "kernels.h"
 
