@@ -1129,8 +1129,8 @@ __global__ __launch_bounds__(kPT, 2) void down_skinny_kernel(
       const int row = (i >> 2) * 8 + h * 4 + (i & 3);
       if (row < bk.cnt) {
         float* yr = y + (size_t)sorted_pair[bk.row0 + row] * H + n0 + r32;
-        yr[0] = acc[0][i];
-        yr[32] = acc[1][i];
+        __builtin_nontemporal_store(acc[0][i], yr);  // streaming stores, as in the tiled down GEMM
+        __builtin_nontemporal_store(acc[1][i], yr + 32);
       }
     }
   }
@@ -1336,8 +1336,10 @@ __global__ __launch_bounds__(kTilePT, 1) void down_tile_kernel(
           const int row = 32 * f + (r >> 2) * 8 + eh * 4 + (r & 3);
           if (row < d.mrows) {
             float* yr = y + (size_t)rowtok[row] * H + nc0 + e32;
+            // streaming stores: the rows are read once, by the combine, after the whole
+            // GEMM (671 MB at 4096 tokens), so caching them only leaves dirty lines to evict
 #pragma unroll
-            for (int g = 0; g < 2; ++g) yr[32 * g] = acc[f][g][r];
+            for (int g = 0; g < 2; ++g) __builtin_nontemporal_store(acc[f][g][r], yr + 32 * g);
           }
         }
       }
