@@ -30,7 +30,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int j = min(j0 + i, k - 1);
-      v[i] = *reinterpret_cast<const float4_t*>(yt + (size_t)j * H);
+      // streaming loads: each row is read once (at 4096 tokens 671 MB, far past the caches)
+      v[i] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(yt + (size_t)j * H));
       wj[i] = wt[j];
     }
 #pragma unroll
