@@ -159,6 +159,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ uint4_t bload16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+// The same with the non-temporal cache policy, for bytes read once per call.
+__device__ __forceinline__ uint4_t bload16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
 __device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }

@@ -31,7 +31,13 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
 
-__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+// Weight rows are streamed once per call: non-temporal loads (measured 26.6 -> 25.0 us for
+// the one-token route + gate/up kernel, whose 100 MB stream would otherwise churn the caches).
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ uint32_t comp(const uint4& v, int q) {
   return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
@@ -563,14 +569,14 @@ __device__ __forceinline__ void dn_load_rows(DownBatch<M, TAIL>& B, rsrc_t rc, r
     const uint32_t oc = v ? (uint32_t)(m0 + i) * rowbytes : kOob, os = v ? (uint32_t)((m0 + i) * NB) : kOob;
 #pragma unroll
     for (int mm = 0; mm < M; ++mm) {
-      B.c[i][mm] = as_uint4(bload16(rc, oc + (uint32_t)(64 * mm + lane) * 16u));
+      B.c[i][mm] = as_uint4(bload16_nt(rc, oc + (uint32_t)(64 * mm + lane) * 16u));
       B.s[i][mm] = bload1(rs, os + (uint32_t)(64 * mm + lane));
     }
   }
   if (TAIL) {
     const int r = lane >> 3, blk = 64 * M + (lane & 7);
     const bool v = on && r < nvalid;
-    B.ct = as_uint4(bload16(rc, v ? (uint32_t)(m0 + r) * rowbytes + (uint32_t)blk * 16u : kOob));
+    B.ct = as_uint4(bload16_nt(rc, v ? (uint32_t)(m0 + r) * rowbytes + (uint32_t)blk * 16u : kOob));
     B.st = bload1(rs, v ? (uint32_t)((m0 + r) * NB + blk) : kOob);
   }
 }
